@@ -1,0 +1,14 @@
+"""MI355X-native GQA decode attention: RoPE + KV-cache append + split-K
+flash-decoding, hand-written HIP for gfx950 behind a C ABI (libkvdecode.so).
+
+The compute entry points are imported lazily from ``_binding`` so that the
+workload generators and the sizing helpers import without the native library.
+"""
+__all__ = ["rope_append_kv", "gqa_decode_attn", "workspace_size", "library_path"]
+
+
+def __getattr__(name):
+    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer"):
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

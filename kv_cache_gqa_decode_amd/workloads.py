@@ -1,0 +1,217 @@
+"""Seeded synthetic decode workloads, shared by the tests, the smoke check and
+the benchmark.
+
+This module only draws random numbers and lays them out; it contains no part
+of the decode computation (no rotation, no attention, no rounding beyond the
+cast of the drawn values to the storage dtype), so the GPU path and the CPU
+oracle can both consume its output without sharing any of the method.
+
+Recipe (every array is a pure function of the workload name, n_kv_heads and
+the overrides; see ``Spec``):
+
+* ``rng = np.random.default_rng([cfg_id, n_kv_heads, stream])``; the streams
+  are 0 (lengths), 1 (q), 2 (k_new), 3 (v_new), 4 (block permutation) and
+  ``1000 + b`` (the cached history of sequence b, K then V).
+* Values ~ N(0, 1) * value_scale drawn in float32, then cast to the storage
+  dtype (bf16 round-to-nearest-even through torch's cast).  q is multiplied by
+  ``q_gain`` before the cast (the "peaked" variants use 32).
+* Sequence b holds ``L_b = positions[b] + 1`` tokens after the append: the
+  history occupies slots 0 .. L_b - 2, the new token goes to slot
+  ``positions[b] = L_b - 1``.
+* Every slot that the attention must not read -- the append slot before the
+  append, all slots >= L_b, every pool block no table row references, and the
+  tail of each sequence's last block -- holds NaN when ``poison`` is set
+  (zero otherwise), so a read outside the valid range shows up in the output.
+* Paged pools: a seeded permutation of all physical blocks, sequence b owning
+  ``perm[b * max_blocks_per_seq : (b + 1) * max_blocks_per_seq]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass
+class Spec:
+    name: str
+    cfg_id: int
+    dtype: str                  # "f32" | "bf16"
+    batch: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    len_lo: int                 # L_b drawn uniformly from [len_lo, len_hi]
+    len_hi: int
+    max_seq_len: int            # contiguous S_max (ignored when paged)
+    value_scale: float = 1.0
+    block_size: int = 0         # 0 = contiguous, 16 = paged
+    num_blocks: int = 0
+    max_blocks_per_seq: int = 0
+    q_gain: float = 1.0
+    poison: bool = True
+    rope_base: float = 10000.0
+
+    @property
+    def n_rep(self) -> int:
+        return self.n_heads // self.n_kv_heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def replace(self, **kw) -> "Spec":
+        return dataclasses.replace(self, **kw)
+
+
+def spec(name: str, n_kv_heads: Optional[int] = None, **overrides) -> Spec:
+    """The five workloads, by name.
+
+    c1  fp32 B1 H8 G2 D64, 255 cached + 1 new token, S_max 256, N(0,1)
+    c2  bf16 B1 H32 G8 D128, context 1024, N(0,1)/sqrt(128)
+    c3  bf16 B64 H32 G8 D128, contexts U[512, 8192], padded S_max 8192
+    c4  bf16 paged (16-token blocks, 65536-block pool), B32 H32 G8 D128,
+        contexts U[1024, 32768], tables from a seeded block permutation
+    c5  bf16 B1 H32 D128, context 131072, G in {32, 8, 1}
+    """
+    s128 = 1.0 / math.sqrt(128.0)
+    table = {
+        "c1": Spec("c1", 1, "f32", 1, 8, 2, 64, 256, 256, 256, 1.0),
+        "c2": Spec("c2", 2, "bf16", 1, 32, 8, 128, 1024, 1024, 1024, s128),
+        "c3": Spec("c3", 3, "bf16", 64, 32, 8, 128, 512, 8192, 8192, s128),
+        "c4": Spec("c4", 4, "bf16", 32, 32, 8, 128, 1024, 32768, 32768, s128,
+                   block_size=16, num_blocks=65536, max_blocks_per_seq=2048),
+        "c5": Spec("c5", 5, "bf16", 1, 32, 8, 128, 131072, 131072, 131072, s128),
+    }
+    s = table[name]
+    if n_kv_heads is not None:
+        s = s.replace(n_kv_heads=n_kv_heads)
+    if overrides:
+        s = s.replace(**overrides)
+    if s.block_size:
+        s = s.replace(max_seq_len=s.max_blocks_per_seq * s.block_size)
+    return s
+
+
+@dataclasses.dataclass
+class Problem:
+    spec: Spec
+    q: np.ndarray               # [B, H, D] storage dtype
+    k_new: np.ndarray           # [B, G, D]
+    v_new: np.ndarray           # [B, G, D]
+    k_cache: np.ndarray         # [B, S_max, G, D] or [NB, 16, G, D]
+    v_cache: np.ndarray
+    positions: np.ndarray       # [B] int32
+    seq_lens: np.ndarray        # [B] int32 = positions + 1
+    block_table: Optional[np.ndarray]  # [B, max_blocks_per_seq] int32
+
+    @property
+    def max_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+
+def _rng(s: Spec, stream: int) -> np.random.Generator:
+    return np.random.default_rng([s.cfg_id, s.n_kv_heads, stream])
+
+
+def _to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _fill_value(s: Spec):
+    if s.dtype == "f32":
+        return np.float32(np.nan) if s.poison else np.float32(0)
+    return BF16_NAN if s.poison else np.uint16(0)
+
+
+def draw_lengths(s: Spec) -> np.ndarray:
+    rng = _rng(s, 0)
+    return rng.integers(s.len_lo, s.len_hi, size=s.batch, endpoint=True).astype(np.int32)
+
+
+def draw_history(s: Spec, b: int, n_tokens: int):
+    """Cached (already rotated) K and V of sequence b: two [n, G, D] arrays."""
+    rng = _rng(s, 1000 + b)
+    shape = (n_tokens, s.n_kv_heads, s.head_dim)
+    k = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
+    v = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
+    return _to_storage(k, s.dtype), _to_storage(v, s.dtype)
+
+
+def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
+    """Draw every input of one decode step of workload ``s``."""
+    B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
+    L = draw_lengths(s) if lengths is None else np.asarray(lengths, np.int32).copy()
+    if L.shape != (B,):
+        raise ValueError("lengths must have shape [batch]")
+    if (L < 1).any() or (L > s.max_seq_len).any():
+        raise ValueError("every length must lie in [1, max_seq_len]")
+    sc = np.float32(s.value_scale)
+    q = _rng(s, 1).standard_normal((B, H, D), dtype=np.float32) * sc * np.float32(s.q_gain)
+    k_new = _rng(s, 2).standard_normal((B, G, D), dtype=np.float32) * sc
+    v_new = _rng(s, 3).standard_normal((B, G, D), dtype=np.float32) * sc
+    store = np.float32 if s.dtype == "f32" else np.uint16
+    fill = _fill_value(s)
+    table = None
+    if s.block_size:
+        bs = s.block_size
+        if B * s.max_blocks_per_seq > s.num_blocks:
+            raise ValueError("pool too small for disjoint tables")
+        perm = _rng(s, 4).permutation(s.num_blocks).astype(np.int32)
+        table = np.ascontiguousarray(
+            perm[: B * s.max_blocks_per_seq].reshape(B, s.max_blocks_per_seq))
+        k_cache = np.full((s.num_blocks, bs, G, D), fill, dtype=store)
+        v_cache = np.full((s.num_blocks, bs, G, D), fill, dtype=store)
+        for b in range(B):
+            n_hist = int(L[b]) - 1
+            if n_hist == 0:
+                continue
+            kh, vh = draw_history(s, b, n_hist)
+            nblk = -(-n_hist // bs)
+            pad = nblk * bs - n_hist
+            if pad:
+                kh = np.concatenate([kh, np.full((pad, G, D), fill, store)])
+                vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
+            ids = table[b, :nblk]
+            k_cache[ids] = kh.reshape(nblk, bs, G, D)
+            v_cache[ids] = vh.reshape(nblk, bs, G, D)
+    else:
+        k_cache = np.full((B, s.max_seq_len, G, D), fill, dtype=store)
+        v_cache = np.full((B, s.max_seq_len, G, D), fill, dtype=store)
+        for b in range(B):
+            n_hist = int(L[b]) - 1
+            if n_hist:
+                kh, vh = draw_history(s, b, n_hist)
+                k_cache[b, :n_hist] = kh
+                v_cache[b, :n_hist] = vh
+    return Problem(spec=s, q=_to_storage(q, s.dtype), k_new=_to_storage(k_new, s.dtype),
+                   v_new=_to_storage(v_new, s.dtype), k_cache=k_cache, v_cache=v_cache,
+                   positions=(L - 1).astype(np.int32), seq_lens=L.astype(np.int32),
+                   block_table=table)
+
+
+def as_torch(a: np.ndarray, device=None):
+    """A torch tensor holding the same bits (uint16 arrays become bfloat16)."""
+    import torch
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device) if device is not None else t
+
+
+def from_torch(t) -> np.ndarray:
+    """Host numpy copy with the same bits (bfloat16 becomes uint16)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()

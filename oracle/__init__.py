@@ -1,0 +1,248 @@
+"""fp64 CPU oracle for the GQA decode step (RoPE, KV-cache append, attention).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It never
+imports the GPU package and the GPU package never imports it; the two share
+no code.  Inputs reach both sides from the seeded workload generators, which
+hold no arithmetic of the method.
+
+Contents
+--------
+* ``liboracle.so`` (from ``kvoracle.c``): the decode step in plain C loops,
+  fp64 throughout -- RoPE rotation, append at the slot given by the position,
+  textbook two-pass softmax attention with the GQA head mapping g = h / n_rep.
+* ``full_causal``: an independently written NumPy recompute of causal
+  attention from scratch (RoPE through complex multiplication), used to pin
+  the decode loop.
+* ``merge``: the log-sum-exp merge of attention over disjoint token sets.
+
+Arrays: bf16 data are passed as ``uint16`` bit patterns; fp32 as ``float32``;
+fp64 as ``float64``.  Pages cited by title:
+  [KVGR] "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践"
+  [SA4]  "4. 自注意力机制推理：单步计算、KV Cache的引入与原理"
+  [OPT]  "Transformer架构优化实战2026：注意力机制、KV Cache与推理加速完整指南"
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+F64, F32, BF16 = 0, 1, 2
+INTERLEAVED, HALF = 0, 1
+
+_DTYPE_CODE = {"f64": F64, "f32": F32, "bf16": BF16}
+_NP_STORAGE = {F64: np.float64, F32: np.float32, BF16: np.uint16}
+_STYLE_CODE = {"interleaved": INTERLEAVED, "half": HALF}
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_heads", "n_kv_heads", "head_dim", "dtype", "block_size",
+        "max_seq_len", "num_blocks", "max_blocks_per_seq")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        lib.kvo_round_to_bf16.restype = ctypes.c_double
+        lib.kvo_round_to_bf16.argtypes = [ctypes.c_double]
+        lib.kvo_bf16_bits.restype = ctypes.c_uint16
+        lib.kvo_bf16_bits.argtypes = [ctypes.c_double]
+        lib.kvo_theta.restype = ctypes.c_double
+        lib.kvo_theta.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double]
+        lib.kvo_rope_rotate.restype = None
+        lib.kvo_rope_rotate.argtypes = [P, P, ctypes.c_int, ctypes.c_double,
+                                        ctypes.c_double, ctypes.c_int]
+        lib.kvo_rope_append.restype = ctypes.c_int
+        lib.kvo_rope_append.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P,
+                                        P, P, ctypes.c_double, ctypes.c_int]
+        lib.kvo_decode_attn.restype = ctypes.c_int
+        lib.kvo_decode_attn.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P,
+                                        ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.kvo_decode_attn_units.restype = ctypes.c_int
+        lib.kvo_decode_attn_units.argtypes = [ctypes.POINTER(_Shape), P, P, P, P,
+                                              P, ctypes.c_double, P, P,
+                                              ctypes.c_int64, P, P, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _need(a, dtype, name, shape=None):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"{name}: expected a C-contiguous {np.dtype(dtype).name} array")
+    if shape is not None and tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {a.shape} != {shape}")
+    return a
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+class Geometry:
+    """Shape of one decode problem, as the oracle sees it.
+
+    Contiguous caches are ``[B, S_max, G, D]``; paged pools are
+    ``[num_blocks, block_size, G, D]`` with an int32 table
+    ``[B, max_blocks_per_seq]`` ([OPT] §四 PagedKVCache; [KVGR] §4.1).
+    """
+
+    def __init__(self, batch, n_heads, n_kv_heads, head_dim, dtype="bf16",
+                 max_seq_len=None, block_size=0, num_blocks=0, max_blocks_per_seq=0):
+        if n_heads % n_kv_heads:
+            raise ValueError("n_heads must be a multiple of n_kv_heads")  # [OPT] §六 assert
+        self.batch, self.n_heads, self.n_kv_heads, self.head_dim = batch, n_heads, n_kv_heads, head_dim
+        self.dtype = dtype
+        self.block_size, self.num_blocks = block_size, num_blocks
+        self.max_blocks_per_seq = max_blocks_per_seq
+        if block_size:
+            max_seq_len = max_blocks_per_seq * block_size
+        self.max_seq_len = max_seq_len
+
+    @property
+    def code(self):
+        return _DTYPE_CODE[self.dtype]
+
+    @property
+    def storage(self):
+        return _NP_STORAGE[self.code]
+
+    def cache_shape(self):
+        if self.block_size:
+            return (self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim)
+        return (self.batch, self.max_seq_len, self.n_kv_heads, self.head_dim)
+
+    def _c(self):
+        return _Shape(self.batch, self.n_heads, self.n_kv_heads, self.head_dim,
+                      self.code, self.block_size, self.max_seq_len, self.num_blocks,
+                      self.max_blocks_per_seq)
+
+
+def theta(i: int, head_dim: int, base: float = 10000.0) -> float:
+    """theta_i = base^(-2i/D) ([KVGR] §3)."""
+    return _load().kvo_theta(i, head_dim, base)
+
+
+def round_to_bf16(x: float) -> float:
+    """Nearest bf16 value of the fp64 number x, ties to even, one rounding."""
+    return _load().kvo_round_to_bf16(float(x))
+
+
+def bf16_bits(x: float) -> int:
+    return int(_load().kvo_bf16_bits(float(x)))
+
+
+def rope_rotate(x, pos, base=10000.0, style="interleaved"):
+    """R_pos x for every row of an fp64 array [..., D] ([KVGR] §3)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    out = np.empty_like(flat)
+    lib = _load()
+    for r in range(flat.shape[0]):
+        lib.kvo_rope_rotate(_ptr(flat[r]), _ptr(out[r]), D, float(pos), float(base),
+                            _STYLE_CODE[style])
+    return out.reshape(x.shape)
+
+
+def rope_append(geom: Geometry, q, k_new, v_new, k_cache, v_cache, positions,
+                block_table=None, base=10000.0, style="interleaved"):
+    """Rotate q and k_new at positions[b] and write k_rot, v_new into the caches.
+
+    The caches are modified in place.  Returns q_rot [B, H, D] fp64.
+    Raises ValueError if a position or block id does not exist.
+    """
+    B, H, G, D = geom.batch, geom.n_heads, geom.n_kv_heads, geom.head_dim
+    st = geom.storage
+    if q is not None:
+        _need(q, st, "q", (B, H, D))
+    _need(k_new, st, "k_new", (B, G, D))
+    _need(v_new, st, "v_new", (B, G, D))
+    _need(k_cache, st, "k_cache", geom.cache_shape())
+    _need(v_cache, st, "v_cache", geom.cache_shape())
+    _need(positions, np.int32, "positions", (B,))
+    if geom.block_size:
+        _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    q_rot = np.zeros((B, H, D), np.float64)
+    sh = geom._c()
+    rc = _load().kvo_rope_append(ctypes.byref(sh), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                 _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(positions), _ptr(block_table), float(base),
+                                 _STYLE_CODE[style])
+    if rc != 0:
+        raise ValueError("position or block id out of range")
+    return q_rot
+
+
+def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=None,
+                scale=None, want_probs=False, n_threads=None):
+    """fp64 attention of every (b, h) query over its first seq_lens[b] tokens.
+
+    Returns (out [B,H,D], lse [B,H]) and, with want_probs, the weights
+    [B, H, max_seq_len] (zero past seq_lens[b]).
+    """
+    B, H, D = geom.batch, geom.n_heads, geom.head_dim
+    _need(q_rot, np.float64, "q_rot", (B, H, D))
+    _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
+    _need(v_cache, geom.storage, "v_cache", geom.cache_shape())
+    _need(seq_lens, np.int32, "seq_lens", (B,))
+    if geom.block_size:
+        _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)  # default 1/sqrt(d_k), d_k = per-head dim ([KVGR] §2.1)
+    out = np.zeros((B, H, D), np.float64)
+    lse = np.zeros((B, H), np.float64)
+    probs = np.zeros((B, H, geom.max_seq_len), np.float64) if want_probs else None
+    sh = geom._c()
+    rc = _load().kvo_decode_attn(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_lens), _ptr(block_table), float(scale), _ptr(out),
+                                 _ptr(lse), _ptr(probs), n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("a referenced cache slot does not exist")
+    return (out, lse, probs) if want_probs else (out, lse)
+
+
+def decode_attn_units(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, units,
+                      block_table=None, scale=None, n_threads=None):
+    """As decode_attn, for the listed (b, h) pairs only: returns out [n, D], lse [n]."""
+    B, H, D = geom.batch, geom.n_heads, geom.head_dim
+    _need(q_rot, np.float64, "q_rot", (B, H, D))
+    _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
+    _need(v_cache, geom.storage, "v_cache", geom.cache_shape())
+    _need(seq_lens, np.int32, "seq_lens", (B,))
+    if geom.block_size:
+        _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    units = np.asarray(units, dtype=np.int32).reshape(-1, 2)
+    ub = np.ascontiguousarray(units[:, 0])
+    uh = np.ascontiguousarray(units[:, 1])
+    if ((ub < 0) | (ub >= B) | (uh < 0) | (uh >= H)).any():
+        raise ValueError("unit out of range")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    n = units.shape[0]
+    out = np.zeros((n, D), np.float64)
+    lse = np.zeros((n,), np.float64)
+    sh = geom._c()
+    rc = _load().kvo_decode_attn_units(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
+                                       float(scale), _ptr(ub), _ptr(uh), n, _ptr(out),
+                                       _ptr(lse), n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("a referenced cache slot does not exist")
+    return out, lse
