@@ -1,0 +1,255 @@
+"""Decode-step benchmark on one MI355X.
+
+One step = rope_append_kv + gqa_decode_attn (RoPE on q and the new k, the
+KV-cache append, split-K GQA attention and the cross-split merge) for one
+layer over a batch of synthetic sequences whose inputs are already resident
+in HBM.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
+decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
+
+Prints ONE JSON line:
+  value      KV HBM GB/s of the whole step = KV bytes / step time, where
+             KV bytes = sum_b L_b * G * D * 2 (K and V) * 2 bytes
+  roofline   the split-K attention kernel alone: KV bytes / its mean
+             duration (HIP events recorded on its stream around every launch
+             in the timed region) against the 8 TB/s HBM peak; `traffic`
+             is the HBM bytes per launch from the committed rocprofv3
+             counter summary of this kernel and workload (null when missing
+             or taken from a different kernel source)
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload, in the same unit (a reported baseline only)
+
+Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
+                       [--kv-heads G] [--kernel auto|valu|mfma] [--split N]
+                       [--no-cpu-baseline] [--flush]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "kv_cache_gqa_decode_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_name(s) -> str:
+    return {"c1": "c1 fp32 single step B1 H8 G2 D64 L256",
+            "c2": "c2 bf16 Llama-3-8B-shaped B1 H32 G8 D128 L1024",
+            "c3": "c3 bf16 batched varlen B64 H32 G8 D128 L~U[512,8192]",
+            "c4": "c4 bf16 paged(16) B32 H32 G8 D128 L~U[1024,32768] pool 65536 blocks",
+            "c5": f"c5 bf16 long context B1 H32 G{s.n_kv_heads} D128 L131072"}[s.name]
+
+
+def load_traffic(key: str, src_hash: str):
+    """HBM traffic per launch from profiles/<key>.json when it was measured
+    on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{key}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(s, p, budget_s: float):
+    """Time the oracle (RoPE + append + attention, fp64, all host threads) on
+    the first n sequences of the workload, n grown until ~budget_s of work."""
+    import numpy as np
+    import oracle
+    from kv_cache_gqa_decode_amd import sizing
+
+    threads = oracle.default_threads()
+    g_all = oracle.Geometry(s.batch, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
+                            max_seq_len=s.max_seq_len, block_size=s.block_size,
+                            num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
+
+    def run(n):
+        idx = np.arange(n)
+        kc, vc = p.k_cache, p.v_cache          # the oracle writes only the appended slots
+        if s.block_size:
+            g = oracle.Geometry(n, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
+                                block_size=16, num_blocks=s.num_blocks,
+                                max_blocks_per_seq=s.max_blocks_per_seq)
+            tab = np.ascontiguousarray(p.block_table[idx])
+        else:
+            g = oracle.Geometry(n, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
+                                max_seq_len=s.max_seq_len)
+            kc = np.ascontiguousarray(p.k_cache[idx])
+            vc = np.ascontiguousarray(p.v_cache[idx])
+            tab = None
+        args = [np.ascontiguousarray(a[idx]) for a in (p.q, p.k_new, p.v_new)]
+        pos = np.ascontiguousarray(p.positions[idx])
+        lens = np.ascontiguousarray(p.seq_lens[idx])
+        t0 = time.perf_counter()
+        q_rot = oracle.rope_append(g, *args, kc, vc, pos, tab, base=s.rope_base)
+        oracle.decode_attn(g, q_rot, kc, vc, lens, tab, n_threads=threads)
+        return time.perf_counter() - t0, lens
+
+    del g_all
+    n = 1
+    dt, lens = run(n)
+    while dt < budget_s / 4 and n < s.batch:
+        n = min(s.batch, max(n + 1, int(n * budget_s / 2 / max(dt, 1e-3))))
+        dt, lens = run(n)
+    reps = [dt]
+    while sum(reps) < budget_s / 2 and len(reps) < 5:   # small workloads: repeat, take the median
+        reps.append(run(n)[0])
+    dt = float(sorted(reps)[len(reps) // 2])
+    kvb = sizing.decode_kv_read_bytes(lens, s.n_kv_heads, s.head_dim, s.elem_bytes)
+    return {"value": kvb / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {s.batch} sequences, all {s.n_heads} heads, one step "
+                      f"(RoPE + append + attention), median of {len(reps)} runs: {dt:.3f} s, "
+                      f"{n / dt:.3g} seq-steps/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--kv-heads", type=int, default=None)
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--flush", action="store_true",
+                    help="also time each step after evicting the 256 MB MALL")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step "
+              "shards across GPUs by batch, heads or sequence with no change to the kernels, "
+              "but this build measures one GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_gqa_decode_amd as kvd
+    from kv_cache_gqa_decode_amd import sizing
+    from kv_cache_gqa_decode_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
+    t_gen = time.perf_counter()
+    p = W.make_problem(s)
+    print(f"# generated {s.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    t = {k: W.as_torch(getattr(p, k), dev) for k in
+         ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
+    table = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    max_len = p.max_len
+    kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split)
+    B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
+    q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    plan = kvd.get_plan(B, H, t["k_cache"], table, max_len)
+
+    def step():
+        kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                           t["positions"], table, base=s.rope_base, q_rot=q_rot)
+        kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
+                            max_seq_len=max_len, out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with kvd.kernel_timer(args.steps) as kt:
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kv_bytes = sizing.decode_kv_read_bytes(p.seq_lens, G, D, s.elem_bytes)
+    aux = sizing.decode_aux_bytes(B, H, G, D, s.elem_bytes,
+                                  int(sum(-(-int(L) // 16) for L in p.seq_lens)) if table is not None else 0)
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_ms = kt.mean_ms
+    achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+
+    flushed = None
+    if args.flush:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(min(args.steps, 20)):
+            scratch.fill_(1)
+            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(); step(); b2.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b2))
+        flushed = float(np.median(times))
+        del scratch
+
+    key = f"{s.name}" + (f"_g{G}" if s.name == "c5" else "")
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(key, src_hash)
+    result = {
+        "metric": "decode-attention KV HBM GB/s (% of peak) and seq-steps/sec at 1 MI355X",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) values, seeded lengths; no datasets or weights)",
+        "config": {"workload": workload_name(s), "batch": B, "n_heads": H, "n_kv_heads": G,
+                   "head_dim": D, "kv_dtype": s.dtype, "accumulate": "f32",
+                   "block_size": s.block_size, "total_context_tokens": int(p.seq_lens.sum()),
+                   "max_context": max_len, "kv_bytes_per_step": kv_bytes,
+                   "aux_bytes_per_step": aux, "split_tokens": plan["split_tokens"],
+                   "n_splits": plan["n_splits"], "kernel": plan["kernel"],
+                   "parallelism": "single GPU"},
+        "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode split-K attention",
+                     "kernel_ms": round(kern_ms, 5), "launches_timed": kt.count,
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "kernel_source_hash": src_hash},
+    }
+    if flushed is not None:
+        result["mall_flushed_ms_per_step"] = round(flushed, 5)
+        result["mall_flushed_gbs"] = round(kv_bytes / (flushed * 1e-3) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(s, p, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

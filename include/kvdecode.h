@@ -1,0 +1,211 @@
+/*
+ * kvdecode.h -- C ABI of libkvdecode.so: one autoregressive decode step of
+ * grouped-query attention on an AMD Instinct MI355X (gfx950).
+ *
+ * The step is the one the pages below describe for inference with a KV cache:
+ *   1. rope_append_kv: rotate the new query and key with RoPE at the token's
+ *      position and write the rotated key and the value into a preallocated
+ *      KV cache at that position;
+ *   2. gqa_decode_attn: softmax(q K^T * scale) V of that single query over all
+ *      cached tokens, each KV head shared by n_heads / n_kv_heads query heads.
+ *
+ * Pages (cited by title and section):
+ *   [KVGR] "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践"
+ *   [SA4]  "4. 自注意力机制推理：单步计算、KV Cache的引入与原理"
+ *   [OPT]  "Transformer架构优化实战2026：注意力机制、KV Cache与推理加速完整指南"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers to tensors are DEVICE pointers (hipMalloc'd or torch CUDA
+ *   tensors) unless stated otherwise; `shape` is a HOST pointer.
+ * - Every tensor is dense and row-major in the layout given per argument.
+ * - The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises inside these calls; work is enqueued on `stream` (a
+ *   hipStream_t; NULL = the legacy default stream) and KVD_OK means
+ *   "validated and enqueued".
+ * - Host-checkable argument errors return a status and enqueue nothing.
+ *   Launch failures return KVD_EHIP.
+ * - Values that live on the device (positions, seq_lens, block-table
+ *   entries) cannot be checked on the host.  The kernels never read or write
+ *   outside the buffers the shape describes: an out-of-range position or
+ *   block id skips that append; a length above max_seq_len_host is clamped
+ *   to it; a block id outside [0, num_blocks) contributes nothing.  Outputs
+ *   for such inputs are unspecified.
+ * - Calls on different streams are independent; the library keeps only a
+ *   per-device property cache and the optional tuning / timing state below.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVD_OK = 0,
+  KVD_EINVAL = 1,        /* null pointer, inconsistent shape, aliasing */
+  KVD_EUNSUPPORTED = 2,  /* head_dim, dtype or block_size not supported */
+  KVD_ERANGE = 3,        /* max_seq_len_host outside [0, max_seq_len] */
+  KVD_EWORKSPACE = 4,    /* workspace missing or smaller than required */
+  KVD_EHIP = 5           /* a HIP runtime call or launch failed */
+} kvd_status;
+
+typedef enum {
+  KVD_FP32 = 0,          /* IEEE binary32 */
+  KVD_BF16 = 1           /* bfloat16 (upper half of a binary32) */
+} kvd_dtype;
+
+typedef enum {
+  /* Pair (2i, 2i+1) is (real, imag) of the i-th complex number: the pages'
+   * reading of RoPE as interleaved real/imaginary parts ([KVGR] §3). */
+  KVD_ROPE_INTERLEAVED = 0,
+  /* Pair (i, i + D/2): the "rotate half" arrangement. */
+  KVD_ROPE_HALF = 1
+} kvd_rope_style;
+
+/*
+ * Geometry of the decode problem.
+ *   batch       B >= 0 sequences (B == 0: the calls validate and do nothing)
+ *   n_heads     H >= 1 query heads
+ *   n_kv_heads  G >= 1 KV heads; H % G == 0 ([OPT] §六 asserts it); query head
+ *               h reads KV head h / (H / G) ([KVGR] §2.2, repeat_interleave)
+ *   head_dim    D in {64, 128}
+ *   kv_dtype    kvd_dtype of q, k_new, v_new, k_cache and v_cache
+ *   block_size  0  = contiguous cache  [B, max_seq_len, G, D]
+ *                    ([OPT] §四 KVCache: (batch, seq, heads, head_dim));
+ *               16 = paged pool [num_blocks, 16, G, D] with an int32 block
+ *                    table [B, max_blocks_per_seq]: token p of sequence b is
+ *                    row p % 16 of block table[b][p / 16] ([OPT] §四
+ *                    PagedKVCache; [KVGR] §4.1, 16-token blocks)
+ *   max_seq_len contiguous: S_max, the row capacity per sequence;
+ *               paged: must equal max_blocks_per_seq * 16
+ *   num_blocks  paged: pool size (>= 1); contiguous: ignored
+ *   max_blocks_per_seq  paged: table row stride (>= 1); contiguous: ignored
+ */
+typedef struct kvd_shape {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;
+  int32_t block_size;
+  int32_t max_seq_len;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+} kvd_shape;
+
+/*
+ * rope_append_kv -- RoPE on q and the new k, then the cache append.
+ *
+ * For every sequence b with P = positions[b]:
+ *   theta_i = rope_base^(-2i/D), angle_i = P * theta_i  ([KVGR] §3);
+ *   every pair (a, c) of q[b,h,:] and k_new[b,g,:] becomes
+ *   (a cos - c sin, a sin + c cos), i.e. multiplication by cos + i sin;
+ *   q_rot[b,h,:] = rotated q (fp32);
+ *   K cache slot (b, P, g) = rotated k_new, rounded once (nearest-even) from
+ *   the exact rotation to kv_dtype; V slot (b, P, g) = v_new, bit copy
+ *   ([SA4] §4.5: preallocated cache written at index `step`; [OPT] §四
+ *   KVCache.update).  The cache stores rotated keys, so history is never
+ *   rotated again ([KVGR] §3).  V is not rotated.
+ *
+ *   q          [B, H, D] kv_dtype, or NULL to rotate and append k/v only
+ *   k_new      [B, G, D] kv_dtype, not yet rotated
+ *   v_new      [B, G, D] kv_dtype
+ *   q_rot      [B, H, D] fp32 output (ignored when q == NULL); must not
+ *              overlap q, k_new, v_new or the caches
+ *   k_cache, v_cache   cache tensors as described by `shape`; modified in
+ *              place at the B appended slots only
+ *   positions  [B] int32, 0 <= positions[b] < max_seq_len (the number of
+ *              tokens already cached for sequence b)
+ *   block_table  [B, max_blocks_per_seq] int32 when paged, NULL otherwise;
+ *              the block that receives an append must belong to that
+ *              sequence alone
+ *   rope_base  > 0 (10000 in the pages; some models use 1e6)
+ *   rope_style kvd_rope_style
+ * Errors: EINVAL (null pointer, H % G != 0, B < 0, table given for a
+ * contiguous cache or missing for a paged one, q_rot == q, base <= 0),
+ * EUNSUPPORTED (head_dim, kv_dtype, block_size, rope_style), EHIP.
+ */
+kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_new,
+                          const void* v_new, float* q_rot, void* k_cache, void* v_cache,
+                          const int32_t* positions, const int32_t* block_table,
+                          double rope_base, int32_t rope_style, void* stream);
+
+/*
+ * gqa_decode_attn -- one query per (b, h) attending over its sequence.
+ *
+ *   s_j = scale * <q_rot[b,h,:], K[b, j, h / (H/G), :]>   for j < L_b,
+ *   out[b,h,:] = sum_j softmax(s)_j * V[b, j, h / (H/G), :],
+ *   lse[b,h]   = ln(sum_j exp(s_j))
+ * with L_b = seq_lens[b] ([KVGR] §2.1 and §4.2; [SA4] §4.1, §4.5: attend
+ * over cache[:step+1]).  Tokens j >= L_b are never read (the causal bound
+ * of the last position, [KVGR] §5.1).  The work is split along the sequence
+ * in chunks that are multiples of 16 tokens; partial results are merged by
+ * log-sum-exp in a second kernel when more than one chunk is needed.
+ *
+ *   q_rot      [B, H, D] fp32 (already rotated, e.g. by rope_append_kv)
+ *   k_cache, v_cache   as described by `shape` (read only)
+ *   seq_lens   [B] int32, 0 <= seq_lens[b] <= max_seq_len_host
+ *              (seq_lens[b] == 0 gives out = 0 and lse = -inf)
+ *   block_table  as in rope_append_kv
+ *   max_seq_len_host  host-side upper bound of seq_lens, used to plan the
+ *              grid; 0 <= max_seq_len_host <= shape->max_seq_len
+ *   scale      softmax scale, normally 1/sqrt(D) ([KVGR] §2.1: d_k is the
+ *              per-head dimension; [OPT] §三: the default 1/sqrt(d_k))
+ *   out        [B, H, D] fp32 output
+ *   lse        [B, H] fp32 output (natural log), or NULL
+ *   workspace  device scratch of at least gqa_decode_workspace_size(shape,
+ *              max_seq_len_host) bytes, 256-byte aligned, or NULL when that
+ *              size is 0; contents on entry are ignored
+ * Errors: EINVAL (null pointers, inconsistent shape, out overlapping q_rot),
+ * EUNSUPPORTED, ERANGE (max_seq_len_host), EWORKSPACE, EHIP.
+ */
+kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const void* k_cache,
+                           const void* v_cache, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t max_seq_len_host,
+                           float scale, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gqa_decode_attn needs for this shape and length bound
+ * on the current device under the current tuning (0 when no split merge is
+ * needed).  Returns 0 for an invalid shape as well; gqa_decode_attn then
+ * reports the shape error. */
+size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kvd_status_string(int32_t status);
+
+/*
+ * Plan inspection and tuning (process-wide; set before issuing work).
+ *
+ * kvd_get_plan reports how gqa_decode_attn would run: plan[0] = tokens per
+ * split (a multiple of 16), plan[1] = number of splits, plan[2] = kernel
+ * (0 = VALU dot products, 1 = MFMA), plan[3] = workgroups launched by the
+ * split kernel.  `plan` is a host array of 4 int32.
+ *
+ * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU) or
+ * 1 (MFMA, bf16 only); split_tokens = 0 (automatic) or a positive multiple
+ * of 16.  EUNSUPPORTED if the override cannot run; the override applies to
+ * later calls in the whole process.
+ */
+kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan);
+kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens);
+
+/*
+ * Kernel timing for measurement.  kvd_timer_begin(n) makes the next n calls
+ * of gqa_decode_attn record a pair of HIP events on their stream around the
+ * split-K kernel's launch (n <= 4096).  kvd_timer_end waits for those events
+ * and returns the summed kernel time in milliseconds and the number of
+ * launches timed, then disables timing.  Host pointers.
+ */
+kvd_status kvd_timer_begin(int32_t n_launches);
+kvd_status kvd_timer_end(double* total_ms, int32_t* n_timed);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

@@ -1,0 +1,288 @@
+"""ctypes binding of libkvdecode.so (argument marshalling only).
+
+Every step of the decode computation runs in the HIP kernels behind the C
+ABI (include/kvdecode.h).  This module checks tensor devices, dtypes and
+shapes, allocates outputs and the split workspace with torch, passes raw
+pointers and the current HIP stream, and turns status codes into
+exceptions.  There is no fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
+
+KVD_FP32, KVD_BF16 = 0, 1
+_STYLES = {"interleaved": 0, "half": 1}
+_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1}
+
+
+class KvdError(ValueError):
+    """A non-OK status from libkvdecode.so."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_heads", "n_kv_heads", "head_dim", "kv_dtype", "block_size",
+        "max_seq_len", "num_blocks", "max_blocks_per_seq")]
+
+
+EXPORTED = ("rope_append_kv", "gqa_decode_attn", "gqa_decode_workspace_size",
+            "kvd_status_string", "kvd_get_plan", "kvd_set_tuning", "kvd_timer_begin",
+            "kvd_timer_end")
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libkvdecode.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m "
+                "kv_cache_gqa_decode_amd.build` (or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        SP = ctypes.POINTER(Shape)
+        lib.rope_append_kv.restype = I32
+        lib.rope_append_kv.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_double, I32, P]
+        lib.gqa_decode_attn.restype = I32
+        lib.gqa_decode_attn.argtypes = [SP, P, P, P, P, P, I32, ctypes.c_float, P, P, P,
+                                        ctypes.c_size_t, P]
+        lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
+        lib.gqa_decode_workspace_size.argtypes = [SP, I32]
+        lib.kvd_status_string.restype = ctypes.c_char_p
+        lib.kvd_status_string.argtypes = [I32]
+        lib.kvd_get_plan.restype = I32
+        lib.kvd_get_plan.argtypes = [SP, I32, ctypes.POINTER(I32)]
+        lib.kvd_set_tuning.restype = I32
+        lib.kvd_set_tuning.argtypes = [I32, I32]
+        lib.kvd_timer_begin.restype = I32
+        lib.kvd_timer_begin.argtypes = [I32]
+        lib.kvd_timer_end.restype = I32
+        lib.kvd_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().kvd_status_string(status).decode()
+        raise KvdError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return KVD_FP32
+    if dt == torch.bfloat16:
+        return KVD_BF16
+    raise ValueError(f"unsupported KV dtype {dt}: float32 or bfloat16")
+
+
+def _need(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_shape(batch: int, n_heads: int, k_cache: torch.Tensor,
+               block_table: Optional[torch.Tensor]) -> Shape:
+    """kvd_shape from the cache tensor: contiguous [B, S_max, G, D] or paged
+    pool [num_blocks, 16, G, D] with table [B, max_blocks_per_seq]."""
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be 4-D")
+    G, D = int(k_cache.shape[2]), int(k_cache.shape[3])
+    code = _dtype_code(k_cache.dtype)
+    if block_table is None:
+        if int(k_cache.shape[0]) != batch:
+            raise ValueError("contiguous cache batch dimension does not match q")
+        return Shape(batch, n_heads, G, D, code, 0, int(k_cache.shape[1]), 0, 0)
+    if int(k_cache.shape[1]) != 16:
+        raise ValueError("paged pool must have 16-token blocks")
+    if block_table.dim() != 2 or int(block_table.shape[0]) != batch:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    mbps = int(block_table.shape[1])
+    return Shape(batch, n_heads, G, D, code, 16, mbps * 16, int(k_cache.shape[0]), mbps)
+
+
+def rope_append_kv(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+                   block_table: Optional[torch.Tensor] = None, base: float = 10000.0,
+                   style: str = "interleaved",
+                   q_rot: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """RoPE on q and k_new at ``positions`` and the append of k_rot / v_new into
+    the caches (in place).  Returns q_rot [B, H, D] float32 (None if q is None)."""
+    lib = load_library()
+    dev = k_cache.device
+    B, G, D = int(k_new.shape[0]), int(k_new.shape[1]), int(k_new.shape[2])
+    H = int(q.shape[1]) if q is not None else G
+    shape = make_shape(B, H, k_cache, block_table)
+    dt = k_cache.dtype
+    if q is not None:
+        _need(q, "q", dev, dt, (B, H, D))
+    _need(k_new, "k_new", dev, dt, (B, G, D))
+    _need(v_new, "v_new", dev, dt, (B, G, D))
+    _need(k_cache, "k_cache", dev, dt)
+    _need(v_cache, "v_cache", dev, dt, tuple(k_cache.shape))
+    _need(positions, "positions", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if style not in _STYLES:
+        raise ValueError(f"style must be one of {sorted(_STYLES)}")
+    if q is not None and q_rot is None:
+        q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _check(lib.rope_append_kv(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                              _ptr(q_rot) if q is not None else None, _ptr(k_cache),
+                              _ptr(v_cache), _ptr(positions), _ptr(block_table),
+                              float(base), _STYLES[style], _stream(dev)))
+    return q_rot if q is not None else None
+
+
+_ws_cache = {}
+
+
+def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def workspace_size(q_rot: torch.Tensor, k_cache: torch.Tensor,
+                   block_table: Optional[torch.Tensor] = None,
+                   max_seq_len: Optional[int] = None) -> int:
+    lib = load_library()
+    B, H = int(q_rot.shape[0]), int(q_rot.shape[1])
+    shape = make_shape(B, H, k_cache, block_table)
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    return int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+
+
+def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """softmax(q K^T * scale) V per (b, h) over the first seq_lens[b] cached
+    tokens.  Returns (out [B, H, D] float32, lse [B, H] float32 natural log).
+
+    ``max_seq_len`` is the host-side bound on seq_lens used to plan the grid
+    (default: the cache capacity)."""
+    lib = load_library()
+    dev = k_cache.device
+    B, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _need(k_cache, "k_cache", dev)
+    _need(v_cache, "v_cache", dev, k_cache.dtype, tuple(k_cache.shape))
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if int(k_cache.shape[3]) != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dev, torch.float32, (B, H))
+    nbytes = int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_attn(ctypes.byref(shape), _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(seq_lens), _ptr(block_table), msl, float(scale), _ptr(out),
+                               _ptr(lse), _ptr(workspace), wbytes, _stream(dev)))
+    return out, lse
+
+
+def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0) -> None:
+    """Process-wide override of the kernel ("valu", "mfma" or None for
+    automatic) and of the tokens per split (0 = automatic)."""
+    _check(load_library().kvd_set_tuning(_KERNELS[kernel], int(split_tokens)))
+
+
+def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
+             block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None):
+    """{'split_tokens', 'n_splits', 'kernel', 'workgroups'} the library would use."""
+    shape = make_shape(batch, n_heads, k_cache, block_table)
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    arr = (ctypes.c_int32 * 4)()
+    _check(load_library().kvd_get_plan(ctypes.byref(shape), msl, arr))
+    return {"split_tokens": arr[0], "n_splits": arr[1],
+            "kernel": "mfma" if arr[2] == 1 else "valu", "workgroups": arr[3]}
+
+
+class kernel_timer:
+    """Time the split-K attention kernel of the next ``n`` gqa_decode_attn
+    calls with HIP events recorded on their stream around that launch.
+
+        with kernel_timer(100) as t:
+            ...  # 100 calls
+        t.total_ms, t.count, t.mean_ms
+    """
+
+    def __init__(self, n: int):
+        self.n = int(n)
+        self.total_ms = 0.0
+        self.count = 0
+
+    def __enter__(self):
+        _check(load_library().kvd_timer_begin(self.n))
+        return self
+
+    def __exit__(self, *exc):
+        ms = ctypes.c_double(0)
+        cnt = ctypes.c_int32(0)
+        _check(load_library().kvd_timer_end(ctypes.byref(ms), ctypes.byref(cnt)))
+        self.total_ms, self.count = ms.value, cnt.value
+        return False
+
+    @property
+    def mean_ms(self) -> float:
+        return self.total_ms / self.count if self.count else float("nan")

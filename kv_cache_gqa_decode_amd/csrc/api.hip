@@ -1,0 +1,295 @@
+// Host side of libkvdecode.so: the C ABI declared in include/kvdecode.h.
+//
+// Validation happens entirely on the host before any HIP call, so an invalid
+// call returns its status with nothing enqueued.  Planning turns the shape
+// and the host bound on sequence lengths into a split size (tokens per
+// workgroup, a multiple of 16 so paged and contiguous caches split at the
+// same token boundaries) and a grid that fills the device's compute units.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "kvd_internal.h"
+
+using namespace kvd;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
+
+std::atomic<int> g_kernel_override{-1};     // -1 auto, 0 VALU, 1 MFMA
+std::atomic<int> g_split_override{0};       // 0 auto
+
+struct Timer {
+  std::mutex mu;
+  std::vector<hipEvent_t> start, stop;
+  int capacity = 0;
+  int limit = 0;
+  int used = 0;
+  bool active = false;
+};
+Timer g_timer;
+
+int device_cu_count(int* cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev < 0 || dev >= kMaxDevices) return -1;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      return -1;
+    g_cu_count[dev].store(v, std::memory_order_relaxed);
+  }
+  *cu = v;
+  return 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvd_status check_shape(const kvd_shape* s) {
+  if (!s) return KVD_EINVAL;
+  if (s->batch < 0 || s->batch > 65535) return KVD_EINVAL;
+  if (s->n_heads < 1 || s->n_kv_heads < 1 || s->n_heads > 4096) return KVD_EINVAL;
+  if (s->n_heads % s->n_kv_heads != 0) return KVD_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return KVD_EUNSUPPORTED;
+  if (s->kv_dtype != KVD_FP32 && s->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+  if (s->block_size != 0 && s->block_size != 16) return KVD_EUNSUPPORTED;
+  if (s->max_seq_len < 1) return KVD_EINVAL;
+  if (s->block_size == 16) {
+    if (s->num_blocks < 1 || s->max_blocks_per_seq < 1) return KVD_EINVAL;
+    if (static_cast<int64_t>(s->max_blocks_per_seq) * 16 != s->max_seq_len) return KVD_EINVAL;
+  }
+  return KVD_OK;
+}
+
+struct Plan {
+  int chunk = 0;        // tokens per split
+  int n_splits = 0;
+  int kernel = 0;       // 0 VALU, 1 MFMA
+  int head_groups = 1;  // VALU: query-head groups per KV head
+  int rb = 1;           // VALU: heads per pass
+  int64_t wgs = 0;
+  size_t workspace = 0;
+};
+
+int round_up(int64_t x, int64_t m) { return static_cast<int>((x + m - 1) / m * m); }
+
+kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl) {
+  const int R = s->n_heads / s->n_kv_heads;
+  int kernel = g_kernel_override.load();
+  if (kernel < 0) kernel = 0;
+  if (kernel == 1) return KVD_EUNSUPPORTED;   // MFMA path not built in this library
+  pl->kernel = kernel;
+  pl->rb = valu_heads_per_pass(R);
+  pl->head_groups = (R + pl->rb - 1) / pl->rb;
+  if (max_len_host <= 0 || s->batch == 0) {
+    pl->chunk = 16; pl->n_splits = 0; pl->wgs = 0; pl->workspace = 0;
+    return KVD_OK;
+  }
+  int chunk = g_split_override.load();
+  if (chunk <= 0) {
+    // Aim for ~8 workgroups per CU over the whole (b, kv head, head group)
+    // grid, each streaming at least 64 tokens.
+    const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
+                         static_cast<int64_t>(max_len_host);
+    const int64_t target = static_cast<int64_t>(cu) * 8;
+    chunk = round_up((rows + target - 1) / target, 64);
+    if (chunk < 64) chunk = 64;
+    if (chunk > 8192) chunk = 8192;
+  }
+  if (chunk > round_up(max_len_host, 16)) chunk = round_up(max_len_host, 16);
+  pl->chunk = chunk;
+  pl->n_splits = (max_len_host + chunk - 1) / chunk;
+  pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
+  if (pl->n_splits > 1) {
+    const size_t rows = static_cast<size_t>(s->batch) * s->n_heads * pl->n_splits;
+    size_t o_bytes = rows * s->head_dim * sizeof(float);
+    o_bytes = (o_bytes + 255) / 256 * 256;
+    pl->workspace = o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+  } else {
+    pl->workspace = 0;
+  }
+  return KVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvd_status_string(int32_t status) {
+  switch (status) {
+    case KVD_OK: return "ok";
+    case KVD_EINVAL: return "invalid argument (null pointer, inconsistent shape or aliasing)";
+    case KVD_EUNSUPPORTED: return "unsupported head_dim, dtype, block_size, rope style or kernel";
+    case KVD_ERANGE: return "max_seq_len_host outside [0, max_seq_len]";
+    case KVD_EWORKSPACE: return "workspace missing or too small";
+    case KVD_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens) {
+  if (kernel < -1 || kernel > 1) return KVD_EINVAL;
+  if (kernel == 1) return KVD_EUNSUPPORTED;
+  if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
+  g_kernel_override.store(kernel);
+  g_split_override.store(split_tokens);
+  return KVD_OK;
+}
+
+kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (!plan) return KVD_EINVAL;
+  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  Plan pl;
+  st = make_plan(shape, max_seq_len_host, cu, &pl);
+  if (st != KVD_OK) return st;
+  plan[0] = pl.chunk;
+  plan[1] = pl.n_splits;
+  plan[2] = pl.kernel;
+  plan[3] = static_cast<int32_t>(pl.wgs);
+  return KVD_OK;
+}
+
+size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host) {
+  if (check_shape(shape) != KVD_OK) return 0;
+  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return 0;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return 0;
+  Plan pl;
+  if (make_plan(shape, max_seq_len_host, cu, &pl) != KVD_OK) return 0;
+  return pl.workspace;
+}
+
+kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_new,
+                          const void* v_new, float* q_rot, void* k_cache, void* v_cache,
+                          const int32_t* positions, const int32_t* block_table,
+                          double rope_base, int32_t rope_style, void* stream) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
+  if (!k_new || !v_new || !k_cache || !v_cache || !positions) return KVD_EINVAL;
+  if (q && !q_rot) return KVD_EINVAL;
+  if (q && static_cast<const void*>(q_rot) == q) return KVD_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return KVD_EINVAL;
+  const bool paged = shape->block_size == 16;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  if (shape->batch == 0) return KVD_OK;
+  RopeParams p;
+  p.q = q; p.k_new = k_new; p.v_new = v_new; p.q_rot = q ? q_rot : nullptr;
+  p.k_cache = k_cache; p.v_cache = v_cache; p.positions = positions; p.table = block_table;
+  p.base = rope_base; p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads;
+  p.D = shape->head_dim; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  if (launch_rope_append(p, shape->kv_dtype, paged, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVD_EHIP;
+  return KVD_OK;
+}
+
+kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const void* k_cache,
+                           const void* v_cache, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t max_seq_len_host, float scale,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
+  if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
+  if (!std::isfinite(scale)) return KVD_EINVAL;
+  const bool paged = shape->block_size == 16;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (shape->batch == 0) return KVD_OK;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  Plan pl;
+  st = make_plan(shape, max_seq_len_host, cu, &pl);
+  if (st != KVD_OK) return st;
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
+  if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G;
+  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.chunk = pl.chunk; p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
+  p.qscale = scale * 1.4426950408889634f;
+  p.direct = pl.n_splits <= 1 ? 1 : 0;
+  if (pl.workspace > 0) {
+    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
+    size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  } else {
+    p.part_o = nullptr; p.part_lse = nullptr;
+  }
+
+  if (pl.n_splits == 0) {
+    // no sequence can hold a token: the merge kernel writes zeros and -inf
+    p.chunk = 16; p.n_splits = 1;
+    return launch_lse_reduce(p, s) == hipSuccess ? KVD_OK : KVD_EHIP;
+  }
+
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.active && g_timer.used < g_timer.limit) {
+      ev_start = g_timer.start[g_timer.used];
+      ev_stop = g_timer.stop[g_timer.used];
+      ++g_timer.used;
+    }
+  }
+  if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
+  if (launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s) != hipSuccess) return KVD_EHIP;
+  if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
+  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
+  return KVD_OK;
+}
+
+kvd_status kvd_timer_begin(int32_t n_launches) {
+  if (n_launches < 1 || n_launches > 4096) return KVD_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  while (g_timer.capacity < n_launches) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return KVD_EHIP;
+    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return KVD_EHIP; }
+    g_timer.start.push_back(a);
+    g_timer.stop.push_back(b);
+    ++g_timer.capacity;
+  }
+  g_timer.used = 0;
+  g_timer.limit = n_launches;
+  g_timer.active = true;
+  return KVD_OK;
+}
+
+kvd_status kvd_timer_end(double* total_ms, int32_t* n_timed) {
+  if (!total_ms || !n_timed) return KVD_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  double sum = 0.0;
+  for (int i = 0; i < g_timer.used; ++i) {
+    if (hipEventSynchronize(g_timer.stop[i]) != hipSuccess) return KVD_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess) return KVD_EHIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *n_timed = g_timer.used;
+  g_timer.active = false;
+  g_timer.used = 0;
+  return KVD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the HIP sources of libkvdecode.so.
+// Nothing here is part of the C ABI (include/kvdecode.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvdecode.h"
+
+namespace kvd {
+
+// Everything a decode-attention launch needs, passed by value.
+struct DecodeParams {
+  const float* q_rot;       // [B, H, D] fp32
+  const void* k;            // cache or pool
+  const void* v;
+  const int32_t* seq_lens;  // [B]
+  const int32_t* table;     // [B, max_blocks_per_seq] or null
+  float* out;               // [B, H, D]
+  float* lse;               // [B, H] or null
+  float* part_o;            // [B * H, n_splits, D]  (split results, normalised)
+  float* part_lse;          // [B * H, n_splits]     (log2 of the split's exp-sum)
+  int32_t B, H, G, D, R;    // R = H / G
+  int32_t max_seq_len;      // contiguous S_max, or max_blocks_per_seq * 16
+  int32_t max_len_host;     // lengths are clamped to this
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t chunk;            // tokens per split, multiple of 16
+  int32_t n_splits;
+  int32_t head_groups;      // query-head groups per KV head (VALU kernel)
+  float qscale;             // softmax scale * log2(e)
+  int32_t direct;           // 1: one split, write out / lse directly
+};
+
+struct RopeParams {
+  const void* q;            // [B, H, D] or null
+  const void* k_new;        // [B, G, D]
+  const void* v_new;        // [B, G, D]
+  float* q_rot;             // [B, H, D]
+  void* k_cache;
+  void* v_cache;
+  const int32_t* positions;
+  const int32_t* table;
+  double base;
+  int32_t B, H, G, D;
+  int32_t style;
+  int32_t max_seq_len;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+};
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
+                              hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
+                              int rb, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
+hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
+
+// Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).
+int valu_heads_per_pass(int n_rep);
+// Workgroups and tokens per workgroup-iteration of the MFMA kernel.
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
+
+// ------------------------------------------------------------ device helpers
+
+// bf16 pair in a 32-bit word -> two floats (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_float(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+}  // namespace kvd

@@ -1,0 +1,93 @@
+// Cross-split log-sum-exp merge.
+//
+// Attention over the union of disjoint token chunks is the combination of
+// the per-chunk results weighted by exp(lse_s - lse): with M = max_s lse_s,
+// w_s = 2^(lse_s - M) (lse kept in log2 units), out = sum_s w_s o_s / sum_s
+// w_s and lse = M + log2(sum_s w_s).  This is the exact blockwise-softmax
+// algebra behind the tiled attention of "Transformer推理核心：KV Cache、GQA与
+// RoPE原理与工程实践" §4.2 applied across workgroups.
+//
+// One 256-thread workgroup per (b, h).  D/4 threads read one partial row as
+// float4s, so 256 / (D/4) partials are combined concurrently; the thread
+// groups then merge through LDS.  Only the ceil(L_b / chunk) splits that
+// hold tokens are read.
+#include "kvd_internal.h"
+
+namespace kvd {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D>
+__global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
+  constexpr int TPR = D / 4;          // threads per partial row
+  constexpr int SP = 256 / TPR;       // partials in flight per pass
+  __shared__ float sm_red[256];
+  __shared__ float4 sm_acc[SP][TPR];
+  __shared__ float sm_w[SP];
+
+  const int bh = blockIdx.x;
+  const int b = bh / p.H;
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int ns = (L + p.chunk - 1) / p.chunk;
+  const int tid = threadIdx.x;
+  float* out = p.out + static_cast<int64_t>(bh) * D;
+  if (ns == 0) {
+    if (tid < D) out[tid] = 0.f;
+    if (tid == 0 && p.lse) p.lse[bh] = kNegInf;
+    return;
+  }
+  const float* plse = p.part_lse + static_cast<int64_t>(bh) * p.n_splits;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o + static_cast<int64_t>(bh) * p.n_splits * D);
+
+  // 1) M = max over splits
+  float M = kNegInf;
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, plse[s]);
+  sm_red[tid] = M;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + w]);
+    __syncthreads();
+  }
+  M = sm_red[0];
+  const float ref = M == kNegInf ? 0.f : M;
+
+  // 2) weighted sums, SP partial rows at a time
+  const int sr = tid / TPR, c4 = tid - sr * TPR;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  for (int s = sr; s < ns; s += SP) {
+    const float w = exp2f(plse[s] - ref);
+    const float4 o = po[static_cast<int64_t>(s) * TPR + c4];
+    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    wsum += w;
+  }
+  sm_acc[sr][c4] = acc;
+  if (c4 == 0) sm_w[sr] = wsum;
+  __syncthreads();
+  if (tid < TPR) {
+    float4 a = sm_acc[0][tid];
+    float ws = sm_w[0];
+#pragma unroll
+    for (int r = 1; r < SP; ++r) {
+      const float4 x = sm_acc[r][tid];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      ws += sm_w[r];
+    }
+    const float inv = 1.f / ws;
+    reinterpret_cast<float4*>(out)[tid] = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    if (tid == 0 && p.lse) p.lse[bh] = (ref + log2f(ws)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.B * p.H);
+  if (p.D == 64) lse_reduce_kernel<64><<<grid, 256, 0, stream>>>(p);
+  else lse_reduce_kernel<128><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace kvd

@@ -1,0 +1,142 @@
+// Fused RoPE + KV-cache append (one launch per decode step).
+//
+// "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践" §3: theta_i =
+// base^(-2i/d), angle = position * theta_i, each (real, imag) pair of q and k
+// multiplied by cos + i sin; only the new token is rotated, the cache keeps
+// rotated keys.  "4. 自注意力机制推理" §4.5 and "Transformer架构优化实战2026"
+// §四: the new K/V go into a preallocated cache at the step's position
+// (contiguous, or through a 16-token block table).
+//
+// One thread per rotated pair of q or k, or per copied element of v.  The
+// rotation runs in fp64 and the stored key is rounded once to the cache
+// dtype, so the appended row is bit-identical to the exact rotation rounded
+// to nearest-even.  The work is B * ((H + G) * D / 2 + G * D) threads: a few
+// microseconds at most, dominated by the launch.
+#include "kvd_internal.h"
+
+namespace kvd {
+namespace {
+
+// Nearest-even bf16 of a double, in one rounding (no detour through fp32,
+// which would round twice).  Works on the binary64 fields directly.
+__device__ uint16_t double_to_bf16_rne(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
+  const int e = static_cast<int>((u >> 52) & 0x7ff);
+  const uint64_t frac = u & ((1ull << 52) - 1);
+  if (e == 0x7ff) return static_cast<uint16_t>(sign | (frac ? 0x7fc0u : 0x7f80u));
+  if (e == 0) return static_cast<uint16_t>(sign);          // |x| < 2^-1022 rounds to 0
+  int E = e - 1023;
+  if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
+  const uint64_t sig = (1ull << 52) | frac;                 // 53-bit significand
+  if (E >= -126) {                                          // bf16 normal range
+    uint64_t keep = sig >> 45;                              // 8 significant bits
+    const uint64_t rem = sig & ((1ull << 45) - 1);
+    const uint64_t halfway = 1ull << 44;
+    if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
+    if (keep == 256) { keep = 128; ++E; }
+    if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
+    return static_cast<uint16_t>(sign | (static_cast<uint32_t>(E + 127) << 7) |
+                                 static_cast<uint32_t>(keep & 0x7f));
+  }
+  // bf16 subnormal: value = sig * 2^(E-52), unit 2^-133 -> sig >> (-(E + 81))
+  const int shift = -(E + 81);                              // > 45 here
+  if (shift > 54) return static_cast<uint16_t>(sign);       // below half a unit
+  uint64_t keep = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t halfway = 1ull << (shift - 1);
+  if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
+  return static_cast<uint16_t>(sign | static_cast<uint32_t>(keep));  // 128 -> min normal
+}
+
+template <typename T> __device__ __forceinline__ double load_d(const void* p, int64_t i);
+template <> __device__ __forceinline__ double load_d<float>(const void* p, int64_t i) {
+  return static_cast<double>(static_cast<const float*>(p)[i]);
+}
+template <> __device__ __forceinline__ double load_d<uint16_t>(const void* p, int64_t i) {
+  return static_cast<double>(bf16_to_float(static_cast<const uint16_t*>(p)[i]));
+}
+
+template <typename T> __device__ __forceinline__ void store_rounded(void* p, int64_t i, double x);
+template <> __device__ __forceinline__ void store_rounded<float>(void* p, int64_t i, double x) {
+  static_cast<float*>(p)[i] = static_cast<float>(x);       // v_cvt_f32_f64: nearest-even
+}
+template <> __device__ __forceinline__ void store_rounded<uint16_t>(void* p, int64_t i, double x) {
+  static_cast<uint16_t*>(p)[i] = double_to_bf16_rne(x);
+}
+
+// Row (in units of D elements) of slot `pos` of sequence b, KV head g, or -1.
+template <bool PAGED>
+__device__ __forceinline__ int64_t slot_row(const RopeParams& p, int b, int pos, int g) {
+  if (pos < 0 || pos >= p.max_seq_len) return -1;
+  if (!PAGED) return (static_cast<int64_t>(b) * p.max_seq_len + pos) * p.G + g;
+  const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (pos >> 4)];
+  if (blk < 0 || blk >= p.num_blocks) return -1;
+  return (static_cast<int64_t>(blk) * 16 + (pos & 15)) * p.G + g;
+}
+
+template <typename T, bool PAGED>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int half = p.D >> 1;
+  const int nq = p.q ? p.H * half : 0;
+  const int nk = p.G * half;
+  const int nv = p.G * p.D;
+  if (i >= nq + nk + nv) return;
+  const int pos = p.positions[b];
+
+  if (i < nq + nk) {
+    const bool is_q = i < nq;
+    const int j = is_q ? i : i - nq;
+    const int head = j / half, pi = j - head * half;
+    const int ia = p.style == KVD_ROPE_HALF ? pi : 2 * pi;
+    const int ib = p.style == KVD_ROPE_HALF ? pi + half : 2 * pi + 1;
+    const double theta = pow(p.base, -2.0 * pi / p.D);
+    double sn, cs;
+    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+    const int heads = is_q ? p.H : p.G;
+    const int64_t src = (static_cast<int64_t>(b) * heads + head) * p.D;
+    const void* x = is_q ? p.q : p.k_new;
+    const double a = load_d<T>(x, src + ia), c = load_d<T>(x, src + ib);
+    const double ra = a * cs - c * sn;      // (a + ic)(cos + i sin)
+    const double rb = a * sn + c * cs;
+    if (is_q) {
+      p.q_rot[src + ia] = static_cast<float>(ra);
+      p.q_rot[src + ib] = static_cast<float>(rb);
+    } else {
+      const int64_t row = slot_row<PAGED>(p, b, pos, head);
+      if (row >= 0) {
+        store_rounded<T>(p.k_cache, row * p.D + ia, ra);
+        store_rounded<T>(p.k_cache, row * p.D + ib, rb);
+      }
+    }
+  } else {
+    const int j = i - nq - nk;
+    const int g = j / p.D, d = j - g * p.D;
+    const int64_t row = slot_row<PAGED>(p, b, pos, g);
+    if (row >= 0) {
+      const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
+      static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
+                              hipStream_t stream) {
+  const int half = p.D / 2;
+  const int work = (p.q ? p.H * half : 0) + p.G * half + p.G * p.D;
+  const dim3 grid((work + 255) / 256, p.B);
+  if (kv_dtype == KVD_FP32) {
+    if (paged) rope_append_kernel<float, true><<<grid, 256, 0, stream>>>(p);
+    else rope_append_kernel<float, false><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (paged) rope_append_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(p);
+    else rope_append_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvd

@@ -1,0 +1,71 @@
+"""Shared pieces of the GPU parity tests: run one decode step through the
+C ABI and the same step through the oracle, on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_gqa_decode_amd as kvd
+from kv_cache_gqa_decode_amd import workloads as W
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU")
+    return torch.device("cuda", 0)
+
+
+def geom(s: W.Spec) -> oracle.Geometry:
+    return oracle.Geometry(s.batch, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
+                           max_seq_len=s.max_seq_len, block_size=s.block_size,
+                           num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
+
+
+def upload(p: W.Problem, dev):
+    t = {k: W.as_torch(getattr(p, k), dev) for k in
+         ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
+    t["block_table"] = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    return t
+
+
+def gpu_step(t, s: W.Spec, max_len: int, style="interleaved", scale=None, sync=True):
+    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                               t["positions"], t["block_table"], base=s.rope_base, style=style)
+    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
+                                   t["block_table"], scale=scale, max_seq_len=max_len)
+    if sync:
+        torch.cuda.synchronize()
+    return q_rot, out, lse
+
+
+def oracle_step(p: W.Problem, style="interleaved", units=None, scale=None):
+    """Returns (q_rot fp64, out, lse, k_cache, v_cache) computed by the oracle
+    on host copies of the inputs.  With ``units`` only those (b, h) rows."""
+    s = p.spec
+    g = geom(s)
+    kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, p.block_table,
+                               base=s.rope_base, style=style)
+    if units is None:
+        out, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, p.block_table, scale=scale)
+    else:
+        out, lse = oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, units, p.block_table,
+                                            scale=scale)
+    return q_rot, out, lse, kc, vc
+
+
+def appended_rows(p: W.Problem):
+    """Index tuples of the B * G appended (row, head) slots in the cache array."""
+    s = p.spec
+    rows = []
+    for b in range(s.batch):
+        pos = int(p.positions[b])
+        if s.block_size:
+            rows.append((int(p.block_table[b, pos // 16]), pos % 16))
+        else:
+            rows.append((b, pos))
+    return rows
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)

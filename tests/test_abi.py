@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before any HIP
+call (nothing is enqueued, so these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_gqa_decode_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvdecode.h")
+
+OK, EINVAL, EUNSUPPORTED, ERANGE, EWORKSPACE, EHIP = range(6)
+FAKE = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.kvd_status_string(code)
+    assert b"unknown" in lib.kvd_status_string(99)
+
+
+def shape(**kw):
+    base = dict(batch=2, n_heads=8, n_kv_heads=2, head_dim=64, kv_dtype=1, block_size=0,
+                max_seq_len=64, num_blocks=0, max_blocks_per_seq=0)
+    base.update(kw)
+    return B.Shape(*base.values())
+
+
+def attn(lib, sh, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000),
+         scale=0.125):
+    return lib.gqa_decode_attn(ctypes.byref(sh) if sh is not None else None, q, k, v, lens, table,
+                               msl, scale, out, None, None, 0, None)
+
+
+def rope(lib, sh, q=FAKE, qr=ctypes.c_void_p(0x3000), table=None, base=10000.0, style=0):
+    return lib.rope_append_kv(ctypes.byref(sh) if sh is not None else None, q, FAKE, FAKE, qr,
+                              FAKE, FAKE, FAKE, table, base, style, None)
+
+
+def test_attn_rejects_bad_arguments(lib):
+    assert attn(lib, None) == EINVAL
+    assert attn(lib, shape(n_heads=6, n_kv_heads=4)) == EINVAL          # H % G
+    assert attn(lib, shape(head_dim=96)) == EUNSUPPORTED
+    assert attn(lib, shape(head_dim=63)) == EUNSUPPORTED
+    assert attn(lib, shape(kv_dtype=7)) == EUNSUPPORTED
+    assert attn(lib, shape(block_size=32)) == EUNSUPPORTED
+    assert attn(lib, shape(batch=-1)) == EINVAL
+    assert attn(lib, shape(max_seq_len=0)) == EINVAL
+    assert attn(lib, shape(), q=None) == EINVAL
+    assert attn(lib, shape(), lens=None) == EINVAL
+    assert attn(lib, shape(), out=None) == EINVAL
+    assert attn(lib, shape(), out=FAKE) == EINVAL                        # out aliases q_rot
+    assert attn(lib, shape(), k=ctypes.c_void_p(0x1004)) == EINVAL       # misaligned
+    assert attn(lib, shape(), scale=float("nan")) == EINVAL
+    assert attn(lib, shape(), msl=65) == ERANGE
+    assert attn(lib, shape(), msl=-1) == ERANGE
+    assert attn(lib, shape(), table=FAKE) == EINVAL                      # table for contiguous
+    paged = shape(block_size=16, max_seq_len=64, num_blocks=10, max_blocks_per_seq=4)
+    assert attn(lib, paged) == EINVAL                                    # missing table
+    assert attn(lib, shape(block_size=16, max_seq_len=60, num_blocks=10,
+                           max_blocks_per_seq=4), table=FAKE) == EINVAL  # 60 != 4 * 16
+    assert attn(lib, shape(block_size=16, max_seq_len=64, num_blocks=0,
+                           max_blocks_per_seq=4), table=FAKE) == EINVAL
+    assert attn(lib, shape(batch=0)) == OK                               # nothing to do
+
+
+def test_rope_rejects_bad_arguments(lib):
+    assert rope(lib, None) == EINVAL
+    assert rope(lib, shape(head_dim=80)) == EUNSUPPORTED
+    assert rope(lib, shape(), style=2) == EUNSUPPORTED
+    assert rope(lib, shape(), qr=None) == EINVAL
+    assert rope(lib, shape(), qr=FAKE) == EINVAL                         # q_rot aliases q
+    assert rope(lib, shape(), base=0.0) == EINVAL
+    assert rope(lib, shape(), base=float("inf")) == EINVAL
+    assert rope(lib, shape(), table=FAKE) == EINVAL
+    assert rope(lib, shape(block_size=16, max_seq_len=64, num_blocks=4,
+                           max_blocks_per_seq=4)) == EINVAL
+    assert rope(lib, shape(batch=0)) == OK
+
+
+def test_tuning_and_timer_validation(lib):
+    assert lib.kvd_set_tuning(-2, 0) == EINVAL
+    assert lib.kvd_set_tuning(0, 24) == EINVAL           # not a multiple of 16
+    assert lib.kvd_set_tuning(0, -16) == EINVAL
+    assert lib.kvd_set_tuning(-1, 0) == OK
+    assert lib.kvd_timer_begin(0) == EINVAL
+    assert lib.kvd_timer_begin(5000) == EINVAL
+    assert lib.kvd_timer_end(None, None) == EINVAL
+    plan = (ctypes.c_int32 * 4)()
+    assert lib.kvd_get_plan(None, 0, plan) == EINVAL
+    assert lib.kvd_get_plan(ctypes.byref(shape()), 100, plan) == ERANGE
+    assert lib.gqa_decode_workspace_size(ctypes.byref(shape(head_dim=48)), 10) == 0
+
+
+def test_binding_raises_without_compute(lib):
+    import torch
+    cpu = torch.zeros((2, 8, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        B._dtype_code(torch.float16)
+    with pytest.raises(ValueError):
+        B.make_shape(2, 8, torch.zeros((2, 64, 2)), None)
+    with pytest.raises(KeyError):
+        B.set_tuning("triton")
+    assert cpu.shape == (2, 8, 64)

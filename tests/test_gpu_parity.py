@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Gates (tests/gates.py): fp32 normwise relative error <= 1e-5; bf16 KV max
+absolute error <= 1e-2 and normwise <= 1e-3; lse within 1e-5 / 1e-4
+relative; the cache append bit-exact.  Small cases compare every element;
+full-size workloads compare sampled (b, h) rows (the oracle computes them
+one by one) plus every appended cache row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_gqa_decode_amd as kvd
+from kv_cache_gqa_decode_amd import workloads as W
+from tests import gates
+from tests.gpu_helpers import (appended_rows, bits, device, gpu_step, oracle_step, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_tuning():
+    kvd.set_tuning(None, 0)
+    yield
+    kvd.set_tuning(None, 0)
+
+
+def check_full(p: W.Problem, kernel=None, split=0, style="interleaved", what=""):
+    """Every output element and every cache element against the oracle."""
+    dev = device()
+    s = p.spec
+    kvd.set_tuning(kernel, split)
+    t = upload(p, dev)
+    q_rot, out, lse = gpu_step(t, s, p.max_len, style=style)
+    oq, oo, ol, okc, ovc = oracle_step(p, style=style)
+    kc, vc = W.from_torch(t["k_cache"]), W.from_torch(t["v_cache"])
+    assert np.array_equal(bits(kc), bits(okc)), f"{what}: K cache differs from the oracle's"
+    assert np.array_equal(bits(vc), bits(ovc)), f"{what}: V cache differs from the oracle's"
+    qr = q_rot.cpu().numpy()
+    ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
+    assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+    e = gates.assert_out(out.cpu().numpy(), oo, s.dtype, what)
+    gates.assert_lse(lse.cpu().numpy(), ol, s.dtype, what)
+    return e
+
+
+# ------------------------------------------------------- the small workloads
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+def test_c1_fp32_single_step(style):
+    p = W.make_problem(W.spec("c1"))
+    check_full(p, style=style, what=f"c1 {style}")
+
+
+@pytest.mark.parametrize("q_gain", [1.0, 32.0])
+def test_c2_bf16_llama_shape(q_gain):
+    p = W.make_problem(W.spec("c2", q_gain=q_gain))
+    check_full(p, what=f"c2 q_gain={q_gain}")
+
+
+# --------------------------------------------- ragged, split and paged cases
+
+RAGGED = np.array([1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 1023, 1024], np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("split", [0, 16, 64, 208])
+def test_varlen_contiguous(dtype, split):
+    s = W.spec("c3", batch=RAGGED.size, max_seq_len=1024, dtype=dtype, q_gain=8.0)
+    p = W.make_problem(s, lengths=RAGGED)
+    check_full(p, kernel="valu", split=split, what=f"varlen {dtype} split={split}")
+
+
+@pytest.mark.parametrize("split", [0, 16, 48, 256])
+def test_paged_small(split):
+    s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
+    p = W.make_problem(s, lengths=RAGGED)
+    check_full(p, split=split, what=f"paged split={split}")
+
+
+@pytest.mark.parametrize("split", [0, 32])
+def test_paged_equals_contiguous_bitwise(split):
+    """The same logical cache, paged or contiguous, gives identical bits."""
+    dev = device()
+    kvd.set_tuning(None, split)
+    L = np.array([5, 16, 333, 1024, 700], np.int32)
+    sp = W.spec("c4", batch=5, num_blocks=500, max_blocks_per_seq=64)
+    sc = W.spec("c3", batch=5, max_seq_len=1024).replace(cfg_id=sp.cfg_id)
+    res = []
+    for s in (sp, sc):
+        p = W.make_problem(s, lengths=L)
+        t = upload(p, dev)
+        q_rot, out, lse = gpu_step(t, s, 1024)
+        res.append((q_rot.cpu(), out.cpu(), lse.cpu()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16, 32])
+def test_gqa_ratios(D, dtype, n_rep):
+    H = 32
+    G = H // n_rep
+    L = np.array([700, 129, 1], np.int32)
+    s = W.spec("c3", batch=3, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=768,
+               dtype=dtype, q_gain=4.0, value_scale=D ** -0.5 if dtype == "bf16" else 1.0)
+    p = W.make_problem(s, lengths=L)
+    check_full(p, what=f"D={D} {dtype} n_rep={n_rep}")
+
+
+def test_zero_lengths_and_empty_bound():
+    dev = device()
+    s = W.spec("c3", batch=3, max_seq_len=64)
+    p = W.make_problem(s, lengths=np.array([3, 10, 64], np.int32))
+    t = upload(p, dev)
+    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                               t["positions"])
+    lens = torch.tensor([0, 10, 0], dtype=torch.int32, device=dev)
+    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens, max_seq_len=64)
+    torch.cuda.synchronize()
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    assert torch.isinf(lse[0]).all() and (lse[0] < 0).all()
+    assert torch.isfinite(out[1]).all()
+    # a zero host bound: nothing can be attended
+    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens * 0, max_seq_len=0)
+    torch.cuda.synchronize()
+    assert (out == 0).all() and torch.isinf(lse).all()
+
+
+def test_out_of_range_positions_skip_the_append():
+    """Positions the host cannot check (device-resident): the kernel leaves
+    the cache untouched instead of writing out of bounds."""
+    dev = device()
+    s = W.spec("c3", batch=3, max_seq_len=64)
+    p = W.make_problem(s, lengths=np.array([3, 10, 64], np.int32))
+    t = upload(p, dev)
+    before = t["k_cache"].clone()
+    bad = torch.tensor([-1, 64, 1 << 30], dtype=torch.int32, device=dev)
+    kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], bad)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), t["k_cache"].view(torch.int16))
+
+
+def test_split_counts_agree():
+    """Different split sizes reduce in different orders: results agree to
+    rounding and every one matches the oracle."""
+    s = W.spec("c3", batch=2, max_seq_len=4096, q_gain=16.0)
+    p = W.make_problem(s, lengths=np.array([4096, 2500], np.int32))
+    for split in (16, 128, 1024, 4096):
+        check_full(p, split=split, what=f"split={split}")
+
+
+def test_workspace_too_small_is_reported():
+    dev = device()
+    s = W.spec("c3", batch=2, max_seq_len=2048)
+    p = W.make_problem(s, lengths=np.array([2048, 100], np.int32))
+    t = upload(p, dev)
+    kvd.set_tuning(None, 64)
+    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                               t["positions"])
+    need = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=2048)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(kvd.KvdError) as ei:
+        kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], max_seq_len=2048,
+                            workspace=small)
+    assert ei.value.status == 4
+
+
+def test_repeated_steps_are_idempotent():
+    """Re-running the step at the same positions rewrites the same bits and
+    gives the same outputs (what the benchmark's timed loop relies on)."""
+    dev = device()
+    s = W.spec("c3", batch=4, max_seq_len=512)
+    p = W.make_problem(s, lengths=np.array([512, 77, 300, 1], np.int32))
+    t = upload(p, dev)
+    first = [x.clone() for x in gpu_step(t, s, 512)]
+    k1 = t["k_cache"].clone()
+    for _ in range(3):
+        again = gpu_step(t, s, 512)
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
+    assert torch.equal(k1.view(torch.int16), t["k_cache"].view(torch.int16))
