@@ -69,6 +69,33 @@ def load_traffic(key: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def read_ceiling(dev, kvd, gib: int = 4):
+    """Best streaming-read bandwidth of the read probe over a few launch
+    shapes (GB/s), the practical roof beside the nominal peak."""
+    import torch
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = (0.0, None)
+    for per_cu in (4, 8, 16):
+        for unroll in (4, 8):
+            nwg = cu * per_cu
+            sink = kvd.read_probe(buf, nwg, unroll)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                kvd.read_probe(buf, nwg, unroll, sink)
+            b.record()
+            torch.cuda.synchronize()
+            gbs = 5 * buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, f"{per_cu} workgroups/CU x 256 threads, {unroll} x 16 B in flight")
+    del buf
+    return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
+            "shape": best[1], "buffer_gib": gib}
+
+
 def cpu_baseline(s, p, budget_s: float):
     """Time the oracle (RoPE + append + attention, fp64, all host threads) on
     the first n sequences of the workload, n grown until ~budget_s of work."""
@@ -133,6 +160,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--flush", action="store_true",
                     help="also time each step after evicting the 256 MB MALL")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the streaming-read ceiling and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
                          "(reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -161,6 +190,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
+        return
+    if args.read_ceiling:
+        print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd)}))
         return
     s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
     t_gen = time.perf_counter()

@@ -8,7 +8,7 @@ __all__ = ["rope_append_kv", "gqa_decode_attn", "workspace_size", "library_path"
 
 
 def __getattr__(name):
-    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer"):
+    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer", "read_probe"):
         from . import _binding
         return getattr(_binding, name)
     raise AttributeError(name)

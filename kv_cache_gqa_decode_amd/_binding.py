@@ -17,7 +17,10 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
+# KVD_LIBRARY_PATH may point at another build of the same library (for A/B
+# measurements of build variants); by default the in-tree build is used.
+LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
 
 KVD_FP32, KVD_BF16 = 0, 1
 _STYLES = {"interleaved": 0, "half": 1}
@@ -40,7 +43,7 @@ class Shape(ctypes.Structure):
 
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "gqa_decode_workspace_size",
             "kvd_status_string", "kvd_get_plan", "kvd_set_tuning", "kvd_timer_begin",
-            "kvd_timer_end")
+            "kvd_timer_end", "kvd_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -80,6 +83,8 @@ def load_library():
         lib.kvd_timer_begin.argtypes = [I32]
         lib.kvd_timer_end.restype = I32
         lib.kvd_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
+        lib.kvd_read_probe.restype = I32
+        lib.kvd_read_probe.argtypes = [P, ctypes.c_size_t, P, I32, I32, P]
         _lib = lib
         return lib
 
@@ -256,6 +261,18 @@ def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
     _check(load_library().kvd_get_plan(ctypes.byref(shape), msl, arr))
     return {"split_tokens": arr[0], "n_splits": arr[1],
             "kernel": "mfma" if arr[2] == 1 else "valu", "workgroups": arr[3]}
+
+
+def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8,
+               sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Launch the streaming-read probe over all bytes of ``buf`` (measurement
+    only); returns the sink tensor."""
+    if sink is None or sink.numel() < n_workgroups:
+        sink = torch.empty(n_workgroups, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().kvd_read_probe(_ptr(buf), nbytes, _ptr(sink), int(n_workgroups),
+                                         int(unroll), _stream(buf.device)))
+    return sink
 
 
 class kernel_timer:

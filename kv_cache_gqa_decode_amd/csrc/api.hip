@@ -79,12 +79,21 @@ int round_up(int64_t x, int64_t m) { return static_cast<int>((x + m - 1) / m * m
 
 kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl) {
   const int R = s->n_heads / s->n_kv_heads;
+  // matrix cores for bf16 caches with up to 32 query heads per KV head
+  const bool mfma_ok = s->kv_dtype == KVD_BF16 && R <= 32;
   int kernel = g_kernel_override.load();
-  if (kernel < 0) kernel = 0;
-  if (kernel == 1) return KVD_EUNSUPPORTED;   // MFMA path not built in this library
+  if (kernel < 0) kernel = mfma_ok ? 1 : 0;
+  if (kernel == 1 && !mfma_ok) return KVD_EUNSUPPORTED;
   pl->kernel = kernel;
-  pl->rb = valu_heads_per_pass(R);
-  pl->head_groups = (R + pl->rb - 1) / pl->rb;
+  if (kernel == 1) {
+    pl->rb = R;
+    pl->head_groups = 1;
+  } else {
+    pl->rb = valu_heads_per_pass(R);
+    pl->head_groups = (R + pl->rb - 1) / pl->rb;
+  }
+  // a workgroup advances kWaves tiles of kMfmaTileTokens tokens (MFMA) per step
+  const int granule = kernel == 1 ? kMfmaWaves * kMfmaTileTokens : 64;
   if (max_len_host <= 0 || s->batch == 0) {
     pl->chunk = 16; pl->n_splits = 0; pl->wgs = 0; pl->workspace = 0;
     return KVD_OK;
@@ -96,10 +105,10 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t target = static_cast<int64_t>(cu) * 8;
-    chunk = round_up((rows + target - 1) / target, 64);
-    if (chunk < 64) chunk = 64;
-    if (chunk > 8192) chunk = 8192;
+    chunk = round_up((rows + target - 1) / target, granule);
+    if (chunk < granule) chunk = granule;
   }
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   if (chunk > round_up(max_len_host, 16)) chunk = round_up(max_len_host, 16);
   pl->chunk = chunk;
   pl->n_splits = (max_len_host + chunk - 1) / chunk;
@@ -133,7 +142,6 @@ const char* kvd_status_string(int32_t status) {
 
 kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens) {
   if (kernel < -1 || kernel > 1) return KVD_EINVAL;
-  if (kernel == 1) return KVD_EUNSUPPORTED;
   if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
   g_kernel_override.store(kernel);
   g_split_override.store(split_tokens);
@@ -252,7 +260,9 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
     }
   }
   if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
-  if (launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s) != hipSuccess) return KVD_EHIP;
+  const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)
+                                      : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
+  if (e != hipSuccess) return KVD_EHIP;
   if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
   if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int g = blockIdx.y / p.head_groups;
   const int hg = blockIdx.y - g * p.head_groups;
   const int b = blockIdx.z;
-  int L = p.seq_lens[b];
+  int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int h0 = g * p.R + hg * RB;
   const int nh = min(RB, p.R - hg * RB);
@@ -109,13 +109,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = lane / LPR, c = lane - rg * LPR;
 
+  // unconditional vector loads from a valid head, then a select (a load under
+  // a per-lane branch would serialise into one round trip per element)
   float q[RB][EPL];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const bool live = r < nh;
     const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + h0 + (live ? r : 0)) * D + c * EPL;
+    const float qs = live ? p.qscale : 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) q[r][e] = live ? src[e] * p.qscale : 0.f;
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + e);
+      q[r][e] = x.x * qs; q[r][e + 1] = x.y * qs; q[r][e + 2] = x.z * qs; q[r][e + 3] = x.w * qs;
+    }
   }
 
   float m[RB], l[RB], acc[RB][EPL];

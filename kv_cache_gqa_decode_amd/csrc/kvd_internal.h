@@ -62,6 +62,8 @@ int valu_heads_per_pass(int n_rep);
 // Workgroups and tokens per workgroup-iteration of the MFMA kernel.
 constexpr int kMfmaWaves = 4;
 constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
+constexpr int kMaxChunk = 8192;       // tokens per split, upper bound
+constexpr int kMfmaMaxChunk = kMaxChunk;
 
 // ------------------------------------------------------------ device helpers
 

@@ -64,26 +64,43 @@ def test_c2_bf16_llama_shape(q_gain):
 RAGGED = np.array([1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 1023, 1024], np.int32)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+KERNELS = [("f32", "valu"), ("bf16", "valu"), ("bf16", "mfma")]
+
+
+@pytest.mark.parametrize("dtype,kernel", KERNELS)
 @pytest.mark.parametrize("split", [0, 16, 64, 208])
-def test_varlen_contiguous(dtype, split):
+def test_varlen_contiguous(dtype, kernel, split):
     s = W.spec("c3", batch=RAGGED.size, max_seq_len=1024, dtype=dtype, q_gain=8.0)
     p = W.make_problem(s, lengths=RAGGED)
-    check_full(p, kernel="valu", split=split, what=f"varlen {dtype} split={split}")
+    check_full(p, kernel=kernel, split=split, what=f"varlen {dtype} {kernel} split={split}")
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 16, 48, 256])
-def test_paged_small(split):
+def test_paged_small(kernel, split):
     s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
     p = W.make_problem(s, lengths=RAGGED)
-    check_full(p, split=split, what=f"paged split={split}")
+    check_full(p, kernel=kernel, split=split, what=f"paged {kernel} split={split}")
 
 
+def test_auto_plan_picks_matrix_cores_for_bf16():
+    dev = device()
+    k = torch.empty((4, 64, 8, 128), dtype=torch.bfloat16, device=dev)
+    assert kvd.get_plan(4, 32, k)["kernel"] == "mfma"
+    assert kvd.get_plan(4, 8 * 64, k)["kernel"] == "valu"          # n_rep 64
+    k32 = torch.empty((4, 64, 8, 128), dtype=torch.float32, device=dev)
+    assert kvd.get_plan(4, 32, k32)["kernel"] == "valu"
+    with pytest.raises(kvd.KvdError):
+        kvd.set_tuning("mfma", 0)
+        kvd.get_plan(4, 32, k32)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 32])
-def test_paged_equals_contiguous_bitwise(split):
+def test_paged_equals_contiguous_bitwise(kernel, split):
     """The same logical cache, paged or contiguous, gives identical bits."""
     dev = device()
-    kvd.set_tuning(None, split)
+    kvd.set_tuning(kernel, split)
     L = np.array([5, 16, 333, 1024, 700], np.int32)
     sp = W.spec("c4", batch=5, num_blocks=500, max_blocks_per_seq=64)
     sc = W.spec("c3", batch=5, max_seq_len=1024).replace(cfg_id=sp.cfg_id)
@@ -98,16 +115,16 @@ def test_paged_equals_contiguous_bitwise(split):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,kernel", KERNELS)
 @pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16, 32])
-def test_gqa_ratios(D, dtype, n_rep):
+def test_gqa_ratios(D, dtype, kernel, n_rep):
     H = 32
     G = H // n_rep
     L = np.array([700, 129, 1], np.int32)
     s = W.spec("c3", batch=3, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=768,
                dtype=dtype, q_gain=4.0, value_scale=D ** -0.5 if dtype == "bf16" else 1.0)
     p = W.make_problem(s, lengths=L)
-    check_full(p, what=f"D={D} {dtype} n_rep={n_rep}")
+    check_full(p, kernel=kernel, what=f"D={D} {dtype} {kernel} n_rep={n_rep}")
 
 
 def test_zero_lengths_and_empty_bound():
@@ -143,13 +160,14 @@ def test_out_of_range_positions_skip_the_append():
     assert torch.equal(before.view(torch.int16), t["k_cache"].view(torch.int16))
 
 
-def test_split_counts_agree():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_split_counts_agree(kernel):
     """Different split sizes reduce in different orders: results agree to
     rounding and every one matches the oracle."""
     s = W.spec("c3", batch=2, max_seq_len=4096, q_gain=16.0)
     p = W.make_problem(s, lengths=np.array([4096, 2500], np.int32))
     for split in (16, 128, 1024, 4096):
-        check_full(p, split=split, what=f"split={split}")
+        check_full(p, kernel=kernel, split=split, what=f"{kernel} split={split}")
 
 
 def test_workspace_too_small_is_reported():
