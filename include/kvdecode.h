@@ -207,15 +207,17 @@ kvd_status kvd_timer_end(double* total_ms, int32_t* n_timed);
 /*
  * kvd_read_probe -- measurement utility, not part of the decode step: reads
  * `bytes` (a multiple of 16) of the 16-byte-aligned device buffer `buf` with
- * coalesced 16-byte loads (`unroll` in {1, 4, 8} loads in flight per thread,
- * `n_workgroups` workgroups of 256 threads in a grid-stride loop) and writes
- * one XOR word per workgroup to `sink` (device, n_workgroups uint32).  Its
- * duration gives the device's practical streaming-read bandwidth, the roof
- * the decode kernels are compared with beside the nominal HBM peak.
+ * coalesced 16-byte loads (`unroll` in {1, 4, 8, 16} loads in flight per
+ * thread, `n_workgroups` workgroups of 256 threads; chunked = 0: the grid
+ * strides over the buffer together, chunked = 1: each workgroup streams one
+ * contiguous 1/n_workgroups of it) and writes one XOR word per workgroup to
+ * `sink` (device, n_workgroups uint32).  Its duration gives the device's
+ * practical streaming-read bandwidth, the roof the decode kernels are
+ * compared with beside the nominal HBM peak.
  * Errors: EINVAL, EUNSUPPORTED (unroll), EHIP.
  */
 kvd_status kvd_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
-                          int32_t unroll, void* stream);
+                          int32_t unroll, int32_t chunked, void* stream);
 
 #ifdef __cplusplus
 }

@@ -84,7 +84,7 @@ def load_library():
         lib.kvd_timer_end.restype = I32
         lib.kvd_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
         lib.kvd_read_probe.restype = I32
-        lib.kvd_read_probe.argtypes = [P, ctypes.c_size_t, P, I32, I32, P]
+        lib.kvd_read_probe.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
         _lib = lib
         return lib
 
@@ -263,7 +263,7 @@ def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
             "kernel": "mfma" if arr[2] == 1 else "valu", "workgroups": arr[3]}
 
 
-def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8,
+def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8, chunked: bool = False,
                sink: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Launch the streaming-read probe over all bytes of ``buf`` (measurement
     only); returns the sink tensor."""
@@ -271,7 +271,7 @@ def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8,
         sink = torch.empty(n_workgroups, dtype=torch.int32, device=buf.device)
     nbytes = buf.numel() * buf.element_size()
     _check(load_library().kvd_read_probe(_ptr(buf), nbytes, _ptr(sink), int(n_workgroups),
-                                         int(unroll), _stream(buf.device)))
+                                         int(unroll), int(bool(chunked)), _stream(buf.device)))
     return sink
 
 

@@ -69,6 +69,7 @@ struct Plan {
   int chunk = 0;        // tokens per split
   int n_splits = 0;
   int kernel = 0;       // 0 VALU, 1 MFMA
+  int grid_order = 0;   // MFMA dispatch order (DecodeParams::grid_order)
   int head_groups = 1;  // VALU: query-head groups per KV head
   int rb = 1;           // VALU: heads per pass
   int64_t wgs = 0;
@@ -100,18 +101,30 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   }
   int chunk = g_split_override.load();
   if (chunk <= 0) {
-    // Aim for ~8 workgroups per CU over the whole (b, kv head, head group)
-    // grid, each streaming at least 64 tokens.
+    // Resident workgroups: two per CU (one for more than 16 heads per KV head,
+    // whose workgroups need twice the registers) for the MFMA kernel, four
+    // for the VALU kernel.  Aim for about two rounds of them over the
+    // (sequence, KV head) pairs at the host bound on lengths -- one round
+    // with more than 16 heads, whose merge epilogue is heavier -- and no
+    // more than 2048 tokens per split.
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
-    const int64_t target = static_cast<int64_t>(cu) * 8;
-    chunk = round_up((rows + target - 1) / target, granule);
+    const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (R > 16 ? 1 : 2));
+    const int64_t rounds = (kernel == 1 && R > 16) ? 1 : 2;
+    chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
+    if (chunk > 2048) chunk = 2048;
   }
   if (chunk > kMaxChunk) chunk = kMaxChunk;
+  // the split index is a grid dimension: at most 65535 splits
+  if ((max_len_host + chunk - 1) / chunk > 65535) chunk = round_up((max_len_host + 65534) / 65535, 16);
   if (chunk > round_up(max_len_host, 16)) chunk = round_up(max_len_host, 16);
   pl->chunk = chunk;
   pl->n_splits = (max_len_host + chunk - 1) / chunk;
+  // one sequence: consecutive splits of one head side by side; several
+  // sequences: the heads of one token range side by side, sequence by
+  // sequence for paged pools, first chunks first for contiguous caches
+  pl->grid_order = s->batch == 1 ? 0 : (s->block_size == 16 ? 2 : 1);
   pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
   if (pl->n_splits > 1) {
     const size_t rows = static_cast<size_t>(s->batch) * s->n_heads * pl->n_splits;
@@ -235,6 +248,7 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
   p.chunk = pl.chunk; p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
   p.qscale = scale * 1.4426950408889634f;
   p.direct = pl.n_splits <= 1 ? 1 : 0;
+  p.grid_order = pl.grid_order;
   if (pl.workspace > 0) {
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
     size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;

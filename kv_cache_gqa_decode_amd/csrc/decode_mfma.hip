@@ -122,9 +122,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   // q_hi / q_lo as B operands: [nb][kb][hi, lo][lane] x 16 bytes
   __shared__ __align__(16) uint4 sm_q[NB * KB * 2 * 64];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // grid order (chosen by the planner): which of (sequence, KV head, split)
+  // varies fastest in dispatch order decides how the workgroups reading the
+  // same DRAM rows (the heads of one token range) and the longest chunks are
+  // spread in time and across the XCDs
+  int b, g, split;
+  if (p.grid_order == 0) { split = blockIdx.x; g = blockIdx.y; b = blockIdx.z; }
+  else if (p.grid_order == 1) { g = blockIdx.x; b = blockIdx.y; split = blockIdx.z; }
+  else { g = blockIdx.x; split = blockIdx.y; b = blockIdx.z; }
   const int R = p.R;
   const int hbase = g * R;            // first query head of this KV head
   int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
@@ -402,7 +407,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
-  const dim3 grid(p.n_splits, p.G, p.B);
+  const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
+                  : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
+                                      : dim3(p.G, p.n_splits, p.B);
   if (paged) decode_mfma_kernel<D, NB, true><<<grid, 256, 0, s>>>(p);
   else decode_mfma_kernel<D, NB, false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();

@@ -85,10 +85,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   __shared__ float sm_m[kWaves][RB];
   __shared__ float sm_l[kWaves][RB];
 
-  const int split = blockIdx.x;
+  // grid (B, G * head_groups, n_splits): first chunks are dispatched first
+  const int b = blockIdx.x;
   const int g = blockIdx.y / p.head_groups;
   const int hg = blockIdx.y - g * p.head_groups;
-  const int b = blockIdx.z;
+  const int split = blockIdx.z;
   int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int h0 = g * p.R + hg * RB;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 
 template <typename T, int D, bool PAGED>
 hipError_t launch_t(const DecodeParams& p, int rb, hipStream_t s) {
-  const dim3 grid(p.n_splits, p.G * p.head_groups, p.B);
+  const dim3 grid(p.B, p.G * p.head_groups, p.n_splits);
   switch (rb) {
     case 1: decode_valu_kernel<T, D, 1, PAGED><<<grid, 256, 0, s>>>(p); break;
     case 2: decode_valu_kernel<T, D, 2, PAGED><<<grid, 256, 0, s>>>(p); break;

@@ -30,6 +30,7 @@ struct DecodeParams {
   int32_t head_groups;      // query-head groups per KV head (VALU kernel)
   float qscale;             // softmax scale * log2(e)
   int32_t direct;           // 1: one split, write out / lse directly
+  int32_t grid_order;       // MFMA kernel: 0 (split, G, B), 1 (G, B, split), 2 (G, split, B)
 };
 
 struct RopeParams {

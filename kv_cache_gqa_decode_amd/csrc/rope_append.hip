@@ -7,11 +7,11 @@
 // §四: the new K/V go into a preallocated cache at the step's position
 // (contiguous, or through a 16-token block table).
 //
-// One thread per rotated pair of q or k, or per copied element of v.  The
-// rotation runs in fp64 and the stored key is rounded once to the cache
-// dtype, so the appended row is bit-identical to the exact rotation rounded
-// to nearest-even.  The work is B * ((H + G) * D / 2 + G * D) threads: a few
-// microseconds at most, dominated by the launch.
+// Workgroup (sequence, slice): the sequence's D/2 rotation factors are
+// computed in fp64 into LDS, then each thread rotates one pair of q or k or
+// copies one element of v.  The rotation runs in fp64 and the stored key is
+// rounded once to the cache dtype, so the appended row is bit-identical to
+// the exact rotation rounded to nearest-even.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -77,47 +77,53 @@ __device__ __forceinline__ int64_t slot_row(const RopeParams& p, int b, int pos,
 
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  // workgroup (sequence, slice of 256 items): the D/2 rotation factors of the
+  // sequence's position are computed once per workgroup (fp64) and shared by
+  // its threads through LDS
+  __shared__ double cs[64], sn[64];
+  const int b = blockIdx.x;
   const int half = p.D >> 1;
+  const int pos = p.positions[b];
+  for (int i = threadIdx.x; i < half; i += 256) {
+    const double theta = pow(p.base, -2.0 * i / p.D);
+    sincos(static_cast<double>(pos) * theta, &sn[i], &cs[i]);
+  }
+  __syncthreads();
   const int nq = p.q ? p.H * half : 0;
   const int nk = p.G * half;
   const int nv = p.G * p.D;
-  if (i >= nq + nk + nv) return;
-  const int pos = p.positions[b];
-
-  if (i < nq + nk) {
-    const bool is_q = i < nq;
-    const int j = is_q ? i : i - nq;
-    const int head = j / half, pi = j - head * half;
-    const int ia = p.style == KVD_ROPE_HALF ? pi : 2 * pi;
-    const int ib = p.style == KVD_ROPE_HALF ? pi + half : 2 * pi + 1;
-    const double theta = pow(p.base, -2.0 * pi / p.D);
-    double sn, cs;
-    sincos(static_cast<double>(pos) * theta, &sn, &cs);
-    const int heads = is_q ? p.H : p.G;
-    const int64_t src = (static_cast<int64_t>(b) * heads + head) * p.D;
-    const void* x = is_q ? p.q : p.k_new;
-    const double a = load_d<T>(x, src + ia), c = load_d<T>(x, src + ib);
-    const double ra = a * cs - c * sn;      // (a + ic)(cos + i sin)
-    const double rb = a * sn + c * cs;
-    if (is_q) {
-      p.q_rot[src + ia] = static_cast<float>(ra);
-      p.q_rot[src + ib] = static_cast<float>(rb);
-    } else {
-      const int64_t row = slot_row<PAGED>(p, b, pos, head);
-      if (row >= 0) {
-        store_rounded<T>(p.k_cache, row * p.D + ia, ra);
-        store_rounded<T>(p.k_cache, row * p.D + ib, rb);
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i < nq + nk + nv) {
+    if (i < nq + nk) {
+      const bool is_q = i < nq;
+      const int j = is_q ? i : i - nq;
+      const int head = j / half, pi = j - head * half;
+      const int ia = p.style == KVD_ROPE_HALF ? pi : 2 * pi;
+      const int ib = p.style == KVD_ROPE_HALF ? pi + half : 2 * pi + 1;
+      const int heads = is_q ? p.H : p.G;
+      const int64_t src = (static_cast<int64_t>(b) * heads + head) * p.D;
+      const void* x = is_q ? p.q : p.k_new;
+      const double a = load_d<T>(x, src + ia), c = load_d<T>(x, src + ib);
+      const double ra = a * cs[pi] - c * sn[pi];    // (a + ic)(cos + i sin)
+      const double rb = a * sn[pi] + c * cs[pi];
+      if (is_q) {
+        p.q_rot[src + ia] = static_cast<float>(ra);
+        p.q_rot[src + ib] = static_cast<float>(rb);
+      } else {
+        const int64_t row = slot_row<PAGED>(p, b, pos, head);
+        if (row >= 0) {
+          store_rounded<T>(p.k_cache, row * p.D + ia, ra);
+          store_rounded<T>(p.k_cache, row * p.D + ib, rb);
+        }
       }
-    }
-  } else {
-    const int j = i - nq - nk;
-    const int g = j / p.D, d = j - g * p.D;
-    const int64_t row = slot_row<PAGED>(p, b, pos, g);
-    if (row >= 0) {
-      const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
-      static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];
+    } else {
+      const int j = i - nq - nk;
+      const int g = j / p.D, d = j - g * p.D;
+      const int64_t row = slot_row<PAGED>(p, b, pos, g);
+      if (row >= 0) {
+        const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
+        static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];
+      }
     }
   }
 }
@@ -126,9 +132,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
 
 hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream) {
-  const int half = p.D / 2;
-  const int work = (p.q ? p.H * half : 0) + p.G * half + p.G * p.D;
-  const dim3 grid((work + 255) / 256, p.B);
+  const int work = (p.q ? p.H : 0) * (p.D / 2) + p.G * (p.D / 2) + p.G * p.D;
+  const dim3 grid(p.B, (work + 255) / 256);
   if (kv_dtype == KVD_FP32) {
     if (paged) rope_append_kernel<float, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<float, false><<<grid, 256, 0, stream>>>(p);
