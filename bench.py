@@ -156,8 +156,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kv-heads", type=int, default=None)
-    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "persist", "wave"])
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--tail-split", type=int, default=0,
+                    help="tokens per split over the last --tail-span positions (0 = automatic)")
+    ap.add_argument("--tail-span", type=int, default=-1)
+    ap.add_argument("--order", type=int, default=-1, help="MFMA dispatch order 0/1/2 (-1 automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--flush", action="store_true",
@@ -205,13 +209,15 @@ def main():
          ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
     table = None if p.block_table is None else W.as_torch(p.block_table, dev)
     max_len = p.max_len
-    kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split)
+    kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split, args.tail_split,
+                   args.tail_span, None if args.order < 0 else args.order)
     B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
     q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    # zeroed: its first 256 bytes are work counters that each call leaves at zero
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len)
 
     def step():

@@ -23,6 +23,10 @@ FLAGS = [
     "-ffp-contract=fast", "-munsafe-fp-atomics",
     # no packed-fp32 instructions (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics as written: the wave kernel claims its next
+    # work item ahead of time, and the atomic optimizer's wave-wide rewrite
+    # would wait for the returned value on the spot
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
@@ -49,7 +53,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # --no-undefined: a kernel whose host launch stub was not emitted fails
+    # here rather than when the library is loaded
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

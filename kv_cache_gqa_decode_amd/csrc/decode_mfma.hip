@@ -14,23 +14,29 @@
 //           q is fp32; it enters the bf16 product as q_hi + q_lo, two bf16
 //           numbers whose sum is q to ~2^-17, as two MFMAs into one
 //           accumulator, so scores keep near-fp32 accuracy while K is exact.
+//           The q operands stay in registers for the whole split.
 //   softmax the score output puts head h in lane h % 16 with tokens
 //           16*tb + 4*(lane/16) + j; running max and sum per head live in
 //           that lane, the tile max crosses the 4 lane groups with two
-//           shuffles, and the accumulators are rescaled only when some
-//           running max actually moved.
+//           shuffles.  The running max is only moved (and the accumulators
+//           rescaled) when a tile's max exceeds it by more than 2^8: until
+//           then probabilities are taken against the stale max, which the
+//           final normalisation by the sum cancels exactly.
 //   P V     computed transposed, O^T[d][h] += sum_t V[t][d] P[h][t]: the B
 //           operand P^T needs exactly the probabilities the lane holds (the
 //           token order inside the contraction is free and chosen to match
 //           the score layout), and each head's accumulators stay in its
 //           lanes, so the rescale moves no data.  P is split hi + lo like q.
 //           V^T is the A operand.  V rows travel HBM -> LDS directly
-//           (global_load_lds, 16 bytes per lane, no registers): each
+//           (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): each
 //           instruction lands 64 lanes x 16 bytes contiguously, rows in
 //           order, and consecutive instructions are 32 bytes apart, so the
 //           four lane groups' 2-byte column reads fall in disjoint banks.
-//           Rows past the end of the sequence are zeroed in LDS after the
-//           copy (padding may hold NaN and 0 * NaN is NaN).
+//           The column reads are ds_read_u16, packed in pairs.  Rows past
+//           the end of the sequence
+//           or in an invalid block are read out of range, and are also
+//           zeroed in LDS after the copy in the tiles that have them (stale
+//           LDS may hold NaN and 0 * NaN is NaN).
 //
 // Software pipeline: while tile i is computed, tile i+1 is in flight -- its V
 // rows into the second of two LDS buffers from the start of tile i, its K
@@ -38,103 +44,51 @@
 // so a wave keeps up to 16 KB of loads outstanding while it works.
 // Vector-memory loads complete in issue order, so "at most N outstanding"
 // (s_waitcnt vmcnt(N), N = the loads of one tile) says tile i has landed.
-// Paged block ids are staged in LDS once per workgroup, so no table load
-// sits between two tiles' loads.  Waves of a workgroup take interleaved
-// tiles of the split and merge their (m, l, O) through LDS at the end.
-#include "kvd_internal.h"
+// The LDS reads and writes of the staged tiles are issued from inline
+// assembly on purpose: the compiler cannot tell that they do not touch the
+// buffer an HBM -> LDS copy is still filling, and would otherwise wait for
+// every outstanding copy before each of them, which serialises the pipeline.
+// Their ordering against the copies is the explicit vmcnt wait above.
+// The copies are MUBUF (buffer) loads rather than global ones: the compiler
+// treats a pending global HBM -> LDS copy like a FLAT access and then turns
+// its own wait for the K registers into a wait for everything.
+// Paged block ids are held in registers (lane j = j-th block this wave
+// visits) and broadcast with readlane, so no table or LDS load sits between
+// two tiles' loads.  Waves of a workgroup take interleaved tiles of the
+// split and merge their (m, l, O) through LDS at the end.
+#include "mfma_tile.h"
 
 namespace kvd {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
+using namespace mt;
 
-constexpr float kNegInf = -__builtin_inff();
-constexpr int kMaxChunkBlocks = kMfmaMaxChunk / 16;
+// block ids per wave held in registers: 64 per VGPR
+constexpr int kBlkRegs = (kMfmaMaxChunk / 16 / kMfmaWaves + 63) / 64;
 
-// bf16 bits of a finite float, nearest-even.
-__device__ __forceinline__ unsigned short bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<unsigned short>(u >> 16);
-}
-__device__ __forceinline__ float bf16_value(unsigned short h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-// x ~= hi + lo with both bf16 (the residual x - hi is exact in fp32)
-__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
-  hi = bf16_bits(x);
-  lo = bf16_bits(x - bf16_value(hi));
-}
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Completes this wave's outstanding LDS accesses and keeps the compiler
-// from moving memory accesses across: the wave-private staging tiles are
-// written by some lanes and read by others.
-__device__ __forceinline__ void lds_fence() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-// At most N of this wave's vector-memory loads (HBM -> LDS copies included)
-// are still outstanding; loads complete in issue order.
-template <int N>
-__device__ __forceinline__ void vmem_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
+// LDS of a workgroup: two staged V tiles per wave, reused for the merge
 template <int D>
-struct Geo {
-  static constexpr int KB = D / 32;          // 32-dim blocks of the score contraction
-  static constexpr int CB = D / 16;          // 16-dim blocks of the output
-  static constexpr int TT = kMfmaTileTokens; // 32 tokens per wave tile
-  static constexpr int LPR = D / 8;          // lanes per V row (16 bytes each)
-  static constexpr int RPI = 64 / LPR;       // V rows per load instruction
-  static constexpr int NVL = TT / RPI;       // V load instructions per tile
-  static constexpr int NLOADS = 2 * KB + NVL;  // vector-memory loads per tile
-  // every V copy instruction writes 1 KiB; instruction blocks are padded by
-  // 32 bytes so the transposed column reads of the four lane groups fall in
-  // different banks
-  static constexpr int BLOCK = 1024 + 32;
-  static constexpr int kTileBytes = NVL * BLOCK;
-  // byte offset of (token row r, byte c within the row) in a staged tile
-  __device__ __forceinline__ static int at(int r, int c) {
-    return (r / RPI) * BLOCK + (r % RPI) * (2 * D) + c;
-  }
-};
+constexpr int smem_bytes() {
+  constexpr int stage = kMfmaWaves * 2 * Geo<D>::kTileBytes;
+  constexpr int merge = (kMfmaWaves * 16 * D + 2 * kMfmaWaves * 16) * 4;
+  return stage > merge ? stage : merge;
+}
 
+// One (sequence b, KV head g, split) unit computed by the whole workgroup:
+// the waves take interleaved tiles of the split, merge through LDS and
+// write the split's normalised output and log-sum-exp (or the final output
+// when there is a single split).
 template <int D, int NB, bool PAGED>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
+__device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int b, int g, int split) {
   using G = Geo<D>;
   constexpr int KB = G::KB, CB = G::CB, TT = G::TT, LPR = G::LPR, RPI = G::RPI, NVL = G::NVL;
   constexpr int kWaves = kMfmaWaves;
-  constexpr int kStageBytes = kWaves * 2 * G::kTileBytes;         // two V buffers per wave
-  constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;
-  constexpr int kSmem = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
   static_assert(TT == 32 && NB >= 1 && NB <= 2, "tile shape");
-  __shared__ __align__(16) char smem[kSmem];
-  __shared__ int sm_blk[PAGED ? kMaxChunkBlocks : 1];
-  // q_hi / q_lo as B operands: [nb][kb][hi, lo][lane] x 16 bytes
-  __shared__ __align__(16) uint4 sm_q[NB * KB * 2 * 64];
-
-  // grid order (chosen by the planner): which of (sequence, KV head, split)
-  // varies fastest in dispatch order decides how the workgroups reading the
-  // same DRAM rows (the heads of one token range) and the longest chunks are
-  // spread in time and across the XCDs
-  int b, g, split;
-  if (p.grid_order == 0) { split = blockIdx.x; g = blockIdx.y; b = blockIdx.z; }
-  else if (p.grid_order == 1) { g = blockIdx.x; b = blockIdx.y; split = blockIdx.z; }
-  else { g = blockIdx.x; split = blockIdx.y; b = blockIdx.z; }
   const int R = p.R;
   const int hbase = g * R;            // first query head of this KV head
-  int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+  int L = scalar_load_i32(p.seq_lens + b);
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
-  const int t0 = split * p.chunk;
+  const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
       for (int idx = threadIdx.x; idx < R * D; idx += 256) {
@@ -145,88 +99,152 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
     }
     return;
   }
-  const int t1 = min(t0 + p.chunk, L);
+  const int t1 = min(t0 + split_size(p, split), L);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  const char* kbase = static_cast<const char*>(p.k);
-  const char* vbase = static_cast<const char*>(p.v);
+  // bytes between consecutive tokens of one KV head, and the start of this
+  // (sequence, KV head) -- of KV head g of the pool when paged
+  const int64_t rs = static_cast<int64_t>(p.G) * (2 * D);
+  const int64_t head0 = (PAGED ? 0 : static_cast<int64_t>(b) * p.max_seq_len * rs) +
+                        static_cast<int64_t>(g) * (2 * D);
+  const char* kbase = static_cast<const char*>(p.k) + head0;
+  const char* vbase = static_cast<const char*>(p.v) + head0;
 
-  if (PAGED) {
-    // this split's block ids (an id outside the pool is replaced by -1)
-    const int nblk = (t1 - t0 + 15) >> 4;
-    for (int i = threadIdx.x; i < nblk; i += 256) {
-      const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (t0 >> 4) + i];
-      sm_blk[i] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
-    }
-    __syncthreads();
-  }
-  // row (in units of D elements) of token t of this sequence and KV head; a
-  // token in a bad block reads block 0 and is masked out
-  auto row_of = [&](int t) -> int64_t {
-    if (!PAGED) return (static_cast<int64_t>(b) * p.max_seq_len + t) * p.G + g;
-    int blk = sm_blk[(t - t0) >> 4];
-    blk = blk < 0 ? 0 : blk;
-    return (static_cast<int64_t>(blk) * 16 + (t & 15)) * p.G + g;
-  };
-  auto block_ok = [&](int t) -> bool { return !PAGED || sm_blk[(t - t0) >> 4] >= 0; };
-
-  // K rows in the A-operand layout: token tbase + 16*tb + n, 16 bytes at dims kb*32 + grp*8
-  auto issue_k = [&](int tbase, uint4 (&k)[2][KB]) {
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      int t = tbase + 16 * tb + n;
-      t = t < t1 ? t : t0;
-      const char* rp = kbase + row_of(t) * (2 * D) + grp * 16;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) k[tb][kb] = *reinterpret_cast<const uint4*>(rp + kb * 64);
-    }
-  };
-  // V rows, coalesced, HBM -> LDS: instruction jj covers rows jj*RPI .. +RPI-1
-  auto issue_v = [&](int tbase, char* buf) {
-#pragma unroll
-    for (int jj = 0; jj < NVL; ++jj) {
-      int t = tbase + jj * RPI + lane / LPR;
-      t = t < t1 ? t : t0;
-      const char* src = vbase + row_of(t) * (2 * D) + (lane % LPR) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + jj * G::BLOCK), 16, 0, 0);
-    }
-  };
-
-  char* vbuf[2] = {smem + (2 * wave) * G::kTileBytes, smem + (2 * wave + 1) * G::kTileBytes};
-  uint4 kr[2][KB];
-  int base = t0 + wave * TT;
-  if (base < t1) {                    // tile 0 is requested before q
-    issue_k(base, kr);
-    issue_v(base, vbuf[0]);
-  }
-
-  // q as the B operand of the scores, staged once per workgroup in LDS: the
-  // operand of lane (n, grp) for block (nb, kb) is dims kb*32 + grp*8 .. +7 of
-  // head nb*16 + n, split into hi and lo.  Unconditional vector loads from a
+  // q operands, requested first: lane (n, grp) of block (nb, kb) holds dims
+  // kb*32 + grp*8 .. +7 of head nb*16 + n.  Unconditional vector loads from a
   // valid head, then a select (a load under a per-lane branch would
   // serialise into one round trip per element).
-  for (int idx = threadIdx.x; idx < NB * KB * 64; idx += 256) {
-    const int ql_ = idx & 63, nbkb = idx >> 6;
-    const int nb = nbkb / KB, kb = nbkb - nb * KB;
-    const int h = nb * 16 + (ql_ & 15), gq = ql_ >> 4;
-    const bool live = h < R;
-    const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + hbase + (live ? h : 0)) * D;
-    const float qs = live ? p.qscale : 0.f;
-    const float4 x0 = *reinterpret_cast<const float4*>(src + kb * 32 + gq * 8);
-    const float4 x1 = *reinterpret_cast<const float4*>(src + kb * 32 + gq * 8 + 4);
-    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    u16x8 hi, lo;
+  float4 qraw[NB][KB][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      unsigned short a, c;
-      split_bf16(xv[j] * qs, a, c);
-      hi[j] = a; lo[j] = c;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int h = nb * 16 + n;
+    const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + hbase + (h < R ? h : 0)) * D + grp * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qraw[nb][kb][0] = *reinterpret_cast<const float4*>(src + kb * 32);
+      qraw[nb][kb][1] = *reinterpret_cast<const float4*>(src + kb * 32 + 4);
     }
-    sm_q[(nbkb * 2 + 0) * 64 + ql_] = __builtin_bit_cast(uint4, hi);
-    sm_q[(nbkb * 2 + 1) * 64 + ql_] = __builtin_bit_cast(uint4, lo);
   }
-  __syncthreads();
+
+  // paged: the ids of the blocks this wave visits, lane j of register c =
+  // the wave's (64c + j)-th block = split block 8*(i/2) + 2*wave + i%2 with
+  // i = 64c + j (tile i/2 of the wave, half i%2); ids outside the pool
+  // become -1
+  int blkv[PAGED ? kBlkRegs : 1];
+  if (PAGED) {
+    const int nblk = (t1 - t0 + 15) >> 4;
+    const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks_per_seq + (t0 >> 4);
+#pragma unroll
+    for (int c = 0; c < kBlkRegs; ++c) {
+      const int i = c * 64 + lane;
+      int sb = 8 * (i >> 1) + 2 * wave + (i & 1);
+      sb = sb < nblk ? sb : nblk - 1;
+      const int blk = trow[sb];
+      blkv[c] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+    }
+  }
+  // block ids (wave-uniform) of the two 16-token halves of the wave's tile kt
+  auto tile_blocks = [&](int kt, int (&blk)[2]) {
+    if (!PAGED) { blk[0] = blk[1] = 0; return; }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int i = 2 * kt + tb;
+      int v = blkv[0];
+#pragma unroll
+      for (int c = 1; c < kBlkRegs; ++c) v = (i >> 6) == c ? blkv[c] : v;
+      blk[tb] = __builtin_amdgcn_readlane(v, i & 63);
+    }
+  };
+
+  // Each 16-token half of a tile is read through two buffer descriptors
+  // (K and V) that start at the half's first token row and end at the last
+  // valid one: tokens at or past the end of the split, and every token of an
+  // invalid block, are out of range and read as zeros without touching
+  // memory (the last tile may reach past S_max).  Per-lane offsets are then
+  // the same for every tile.
+  struct TileSrc { rsrc_t k[2], v[2]; };
+  auto tile_src = [&](int tbase, const int (&blk)[2]) {
+    TileSrc ts;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lo = tbase + 16 * h;
+      int rows = t1 - lo;
+      rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+      int64_t off;
+      if (PAGED) {
+        if (blk[h] < 0) rows = 0;
+        off = static_cast<int64_t>(blk[h] < 0 ? 0 : blk[h]) * 16 * rs;
+      } else {
+        off = static_cast<int64_t>(lo) * rs;
+      }
+      // wave-uniform by construction; readfirstlane keeps the descriptor in
+      // scalar registers (a VALU clamp would otherwise make it look divergent)
+      rows = __builtin_amdgcn_readfirstlane(rows);
+      const uint32_t bytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(rs);
+      ts.k[h] = make_rsrc(kbase + off, bytes);
+      ts.v[h] = make_rsrc(vbase + off, bytes);
+    }
+    return ts;
+  };
+  // K rows in the A-operand layout: row n of half tb, 16 bytes at dims
+  // kb*32 + grp*8
+  const uint32_t koff = static_cast<uint32_t>(n * rs + grp * 16);
+  auto issue_k = [&](const TileSrc& ts, uint4 (&k)[2][KB]) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        k[tb][kb] = load16(ts.k[tb], koff + kb * 64);
+  };
+  // V rows, coalesced, HBM -> LDS: instruction jj covers tile rows
+  // jj*RPI .. +RPI-1, i.e. rows (jj*RPI) % 16 + lane/LPR of half jj*RPI/16
+  const uint32_t vlane = static_cast<uint32_t>((lane / LPR) * rs + (lane % LPR) * 16);
+  auto issue_v = [&](const TileSrc& ts, lds_char* buf) {
+#pragma unroll
+    for (int jj = 0; jj < NVL; ++jj) {
+      const uint32_t off = vlane + static_cast<uint32_t>(((jj * RPI) % 16) * rs);
+      copy16_to_lds(ts.v[(jj * RPI) / 16], buf + jj * G::BLOCK, off);
+    }
+  };
+
+  lds_char* const stage = (lds_char*)(smem);
+  lds_char* vbuf[2] = {stage + (2 * wave) * G::kTileBytes, stage + (2 * wave + 1) * G::kTileBytes};
+  // this lane's P V column-read base in each buffer
+  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(4 * grp, 2 * n),
+                           lds_addr(vbuf[1]) + G::at(4 * grp, 2 * n)};
+  uint4 kr[2][KB];
+  int blk_cur[2];
+  int base = t0 + wave * TT;
+  tile_blocks(0, blk_cur);
+  {
+    // issued on every path (a wave without tiles gets empty descriptors and
+    // reads nothing), so the wait for the q loads above stays partial
+    const TileSrc ts = tile_src(base, blk_cur);
+    issue_k(ts, kr);
+    issue_v(ts, vbuf[0]);
+  }
+
+  // q * scale * log2(e) as bf16 hi + lo (heads >= n_rep get zeros)
+  bf16x8 qh[NB][KB], ql[NB][KB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float qs = nb * 16 + n < R ? p.qscale : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const float4 x0 = qraw[nb][kb][0], x1 = qraw[nb][kb][1];
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      u16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        unsigned short a, c;
+        split_bf16(xv[j] * qs, a, c);
+        hi[j] = a; lo[j] = c;
+      }
+      qh[nb][kb] = __builtin_bit_cast(bf16x8, hi);
+      ql[nb][kb] = __builtin_bit_cast(bf16x8, lo);
+    }
+  }
 
   f32x4 acc[NB][CB];
   float m[NB], l[NB];
@@ -237,19 +255,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One tile: `kr` holds its K rows, `vt` its V rows (being copied).  The
-  // next tile's V copies go out first, into the other buffer; its K rows go
-  // out right after this tile's score MFMAs have consumed `kr`.
-  auto compute = [&](int tbase, uint4 (&kr)[2][KB], char* vt, char* vnext) {
+  // One tile (the wave's kt-th): `kr` holds its K rows, buffer `cur` its V
+  // rows (being copied), `blk` its block ids.  The next tile's V copies go
+  // out first, into the other buffer; its K rows go out right after this
+  // tile's score MFMAs have consumed `kr`.  `more` (a constant at each call)
+  // says whether there is a next tile: the loads are then issued on every
+  // path, so the compiler's own wait for `kr` counts them and stays partial.
+  auto compute = [&](int kt, int tbase, int (&blk)[2], int cur, const bool more) {
     const int nbase = tbase + kWaves * TT;
-    const bool more = nbase < t1;
-    if (more) issue_v(nbase, vnext);
-    const bool full = tbase + TT <= t1;
-    bool blk_ok[2] = {true, true};
-    if (PAGED) {
-      blk_ok[0] = block_ok(tbase);
-      blk_ok[1] = tbase + 16 < t1 ? block_ok(tbase + 16) : true;
+    int blk_next[2];
+    tile_blocks(kt + 1, blk_next);
+    const TileSrc ns = tile_src(nbase, blk_next);
+    if (more) {
+      issue_v(ns, vbuf[cur ^ 1]);
+      // keep the copies ahead of the score MFMAs, whose wait for `kr` may
+      // then leave them outstanding
+      __builtin_amdgcn_sched_barrier(0);
     }
+    const bool full = tbase + TT <= t1;
+    const bool ok0 = !PAGED || blk[0] >= 0;
+    const bool ok1 = !PAGED || blk[1] >= 0;
+    const bool masked = !full || !ok0 || !ok1;      // wave-uniform
     // scores of the two 16-token halves
     f32x4 s[NB][2];
 #pragma unroll
@@ -260,14 +286,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, kr[h2][kb]);
-          const bf16x8 qh = __builtin_bit_cast(bf16x8, sm_q[((nb * KB + kb) * 2 + 0) * 64 + lane]);
-          const bf16x8 ql = __builtin_bit_cast(bf16x8, sm_q[((nb * KB + kb) * 2 + 1) * 64 + lane]);
-          c = mfma(a, qh, c);
-          c = mfma(a, ql, c);
+          c = mfma(a, qh[nb][kb], c);
+          c = mfma(a, ql[nb][kb], c);
         }
         s[nb][h2] = c;
       }
-    if (more) issue_k(nbase, kr);        // K rows of the next tile, into the same registers
+    if (more) issue_k(ns, kr);          // K rows of the next tile, into the same registers
 
     bf16x8 ph[NB], pl[NB];
 #pragma unroll
@@ -276,29 +300,36 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = tbase + 16 * h2 + 4 * grp + j;
-          sv[h2 * 4 + j] = (t < t1 && blk_ok[h2]) ? s[nb][h2][j] : kNegInf;
-        }
+        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j];
+      if (masked) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = tbase + 16 * h2 + 4 * grp + j;
+            const bool ok = h2 == 0 ? ok0 : ok1;
+            if (!(t < t1 && ok)) sv[h2 * 4 + j] = kNegInf;
+          }
+      }
       float mt = sv[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[nb], mt);
-      const float ref = mn == kNegInf ? 0.f : mn;
-      if (__any(mn > m[nb])) {           // a running max moved: rescale
-        const float alpha = exp2f(m[nb] - ref);
+      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves: rescale
+        const float mn = fmaxf(m[nb], mt);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         l[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
+        m[nb] = mn;
       }
-      m[nb] = mn;
+      const float ref = m[nb] == kNegInf ? 0.f : m[nb];
       u16x8 hi, lo;
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pj = exp2f(sv[j] - ref);
+        const float pj = __builtin_amdgcn_exp2f(sv[j] - ref);
         ps += pj;
         unsigned short a, c;
         split_bf16(pj, a, c);
@@ -313,43 +344,41 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
     // then K rows) may still be outstanding
     if (more) vmem_wait<G::NLOADS>();
     else vmem_wait<0>();
-    if (!full || PAGED) {                // rows past the end or in a bad block become zeros
+    if (masked) {                        // rows past the end or in a bad block become zeros
+      const uint32_t vt = lds_addr(vbuf[cur]);
 #pragma unroll
       for (int jj = 0; jj < NVL; ++jj) {
         const int r = jj * RPI + lane / LPR;
-        const int t = tbase + r;
-        if (!(t < t1 && blk_ok[r >> 4]))
-          *reinterpret_cast<uint4*>(vt + G::at(r, (lane % LPR) * 16)) = make_uint4(0, 0, 0, 0);
+        const bool ok = (jj * RPI) / 16 == 0 ? ok0 : ok1;
+        if (!(tbase + r < t1 && ok)) lds_zero16(vt + jj * G::BLOCK + lane * 16);
       }
     }
-    lds_fence();                         // the tile is visible to the whole wave
 
     // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens 16*(j/4) + 4*grp + j%4
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      u16x8 a;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = 16 * (j >> 2) + 4 * grp + (j & 3);
-        a[j] = *reinterpret_cast<const unsigned short*>(vt + G::at(tok, (16 * cb + n) * 2));
-      }
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+      const bf16x8 av = gather_v<D>(vrd[cur] + cb * 32);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         acc[nb][cb] = mfma(av, ph[nb], acc[nb][cb]);
         acc[nb][cb] = mfma(av, pl[nb], acc[nb][cb]);
       }
     }
-    lds_fence();                         // reads done before this buffer is refilled
+    blk[0] = blk_next[0];
+    blk[1] = blk_next[1];
   };
 
-  // the two V buffers alternate; K lives in one register set
-  while (base < t1) {
-    compute(base, kr, vbuf[0], vbuf[1]);
-    base += kWaves * TT;
-    if (base >= t1) break;
-    compute(base, kr, vbuf[1], vbuf[0]);
-    base += kWaves * TT;
+  // the two V buffers alternate; K lives in one register set; the wave's
+  // last tile is peeled off (no next tile to request)
+  if (base < t1) {
+    int kt = 0, cur = 0;
+    while (base + kWaves * TT < t1) {
+      compute(kt, base, blk_cur, cur, true);
+      base += kWaves * TT;
+      ++kt;
+      cur ^= 1;
+    }
+    compute(kt, base, blk_cur, cur, false);
   }
 
   // per-wave sums: the four lane groups of a head hold partial sums under one max
@@ -391,8 +420,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
         sum += sm_l[w * 16 + r] * a;
       }
       const int h = hbase + hb + r;
-      const float val = o / sum;
-      const float lse2 = ref + log2f(sum);
+      // every token of the split masked (invalid blocks): empty softmax
+      const float val = sum > 0.f ? o / sum : 0.f;
+      const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
       if (p.direct) {
         p.out[(static_cast<int64_t>(b) * p.H + h) * D + d] = val;
         if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + h] = lse2 * 0.69314718055994531f;
@@ -405,8 +435,83 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
+// One workgroup per unit, dispatched by the hardware in the planner's order.
+template <int D, int NB, bool PAGED>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
+  __shared__ __align__(16) char smem[smem_bytes<D>()];
+  const Unit u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
+}
+
+// 32-bit LDS accesses of the unit hand-off slots, from inline assembly for
+// the reason given at gather_v (each waits for itself)
+__device__ __forceinline__ void lds_write_u32(uint32_t addr, int v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ int lds_read_u32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+// Persistent workgroups: a grid sized to what the device holds at once keeps
+// taking the next unit number from an atomic counter in the workspace (in
+// the same order as the dispatch order above) until the units run out, so
+// workgroups that stream faster take more units and no last round of
+// workgroups leaves the device half idle.  Wave 0 claims the unit after the
+// current one when the current one starts and hands it to the other waves
+// through a double-buffered LDS slot at the barrier that closes each unit
+// (that barrier also keeps the next unit's V copies out of the merge area
+// until every wave has read it).  The last workgroup to leave puts both
+// counters back to zero.  Unit numbers compare unsigned: counters that do
+// not start at zero (a workspace the caller did not clear) can only make
+// workgroups leave early, never index outside the batch.
+template <int D, int NB, bool PAGED>
+__global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeParams p) {
+  __shared__ __align__(16) char smem[smem_bytes<D>()];
+  __shared__ int sm_next[2];
+  typedef __attribute__((address_space(1))) uint32_t global_u32;
+  global_u32* const ctr = (global_u32*)(p.counters);
+  const bool leader = threadIdx.x == 0;
+  const uint32_t slot0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(sm_next)));
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (leader) v = static_cast<int>(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return v;
+  };
+
+  int par = 0;
+  {
+    const int first = claim();
+    if (leader) lds_write_u32(slot0, first);
+    __builtin_amdgcn_s_barrier();
+  }
+  int item = __builtin_amdgcn_readfirstlane(lds_read_u32(slot0));
+  while (static_cast<uint32_t>(item) < static_cast<uint32_t>(p.n_items)) {
+    const int next_v = claim();
+    const Unit u = unit_of_item(p, item);
+    run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
+    par ^= 1;
+    if (leader) lds_write_u32(slot0 + 4 * par, next_v);
+    __builtin_amdgcn_s_barrier();
+    item = __builtin_amdgcn_readfirstlane(lds_read_u32(slot0 + 4 * par));
+  }
+  if (leader) {
+    const uint32_t done = __hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == static_cast<uint32_t>(p.n_workers) - 1u) {
+      __hip_atomic_exchange(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_exchange(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 template <int D, int NB>
-hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
+hipError_t launch_nb(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
+  if (persistent_wg > 0) {
+    if (paged) decode_mfma_persistent_kernel<D, NB, true><<<persistent_wg, 256, 0, s>>>(p);
+    else decode_mfma_persistent_kernel<D, NB, false><<<persistent_wg, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
   const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
                   : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
                                       : dim3(p.G, p.n_splits, p.B);
@@ -416,15 +521,39 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
-  return p.R <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
+hipError_t launch_d(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
+  return p.R <= 16 ? launch_nb<D, 1>(p, paged, persistent_wg, s)
+                   : launch_nb<D, 2>(p, paged, persistent_wg, s);
+}
+
+template <int D, int NB, bool PAGED>
+const void* persistent_fn() {
+  return reinterpret_cast<const void*>(&decode_mfma_persistent_kernel<D, NB, PAGED>);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
-  if (p.chunk > kMfmaMaxChunk) return hipErrorInvalidValue;
-  return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
+  if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
+      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits)
+    return hipErrorInvalidValue;
+  if (persistent_wg > 0 && (!p.counters || p.n_workers != persistent_wg)) return hipErrorInvalidValue;
+  return p.D == 64 ? launch_d<64>(p, paged, persistent_wg, s) : launch_d<128>(p, paged, persistent_wg, s);
+}
+
+int decode_mfma_persistent_occupancy(int D, int R, bool paged) {
+  const bool nb2 = R > 16;
+  const void* fn;
+  if (D == 64) {
+    fn = nb2 ? (paged ? persistent_fn<64, 2, true>() : persistent_fn<64, 2, false>())
+             : (paged ? persistent_fn<64, 1, true>() : persistent_fn<64, 1, false>());
+  } else {
+    fn = nb2 ? (paged ? persistent_fn<128, 2, true>() : persistent_fn<128, 2, false>())
+             : (paged ? persistent_fn<128, 1, true>() : persistent_fn<128, 1, false>());
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess) return 0;
+  return n;
 }
 
 }  // namespace kvd

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int h0 = g * p.R + hg * RB;
   const int nh = min(RB, p.R - hg * RB);
-  const int t0 = split * p.chunk;
+  const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {      // empty sequence: out = 0, lse = -inf
       for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
     }
     return;
   }
-  const int t1 = min(t0 + p.chunk, L);
+  const int t1 = min(t0 + split_size(p, split), L);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rg = lane / LPR, c = lane - rg * LPR;

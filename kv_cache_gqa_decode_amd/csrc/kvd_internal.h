@@ -25,12 +25,22 @@ struct DecodeParams {
   int32_t max_len_host;     // lengths are clamped to this
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
-  int32_t chunk;            // tokens per split, multiple of 16
+  // Splits of a sequence: n_big splits of `chunk` tokens, then splits of
+  // `chunk2` tokens (both multiples of 16; n_big == n_splits: all equal).
+  // Small last splits keep the units that are dispatched last short.
+  int32_t chunk;
+  int32_t chunk2;
+  int32_t n_big;
   int32_t n_splits;
   int32_t head_groups;      // query-head groups per KV head (VALU kernel)
   float qscale;             // softmax scale * log2(e)
   int32_t direct;           // 1: one split, write out / lse directly
   int32_t grid_order;       // MFMA kernel: 0 (split, G, B), 1 (G, B, split), 2 (G, split, B)
+  // persistent MFMA kernel: units (sequence, KV head, split) handed out by an
+  // atomic counter; counters[0] = next unit, counters[1] = workgroups done
+  uint32_t* counters;
+  int32_t n_items;          // B * G * n_splits
+  int32_t n_workers;        // workgroups launched
 };
 
 struct RopeParams {
@@ -55,8 +65,18 @@ hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
                               int rb, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
+// persistent_wg > 0: that many persistent workgroups taking units from
+// p.counters; 0: one workgroup per unit.
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, int persistent_wg,
+                              hipStream_t stream);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
+// Resident workgroups per CU of the persistent MFMA kernel for (D, n_rep,
+// paged), or 0.
+int decode_mfma_persistent_occupancy(int D, int R, bool paged);
+// Persistent wave kernel: `n_wg` workgroups of 4 waves, each wave taking
+// (sequence, KV head, split) units from p.counters (p.n_workers = waves).
+hipError_t launch_decode_wave(const DecodeParams& p, bool paged, int n_wg, hipStream_t stream);
+int decode_wave_occupancy(int D, int R, bool paged);
 
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).
 int valu_heads_per_pass(int n_rep);
@@ -65,8 +85,23 @@ constexpr int kMfmaWaves = 4;
 constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
 constexpr int kMaxChunk = 8192;       // tokens per split, upper bound
 constexpr int kMfmaMaxChunk = kMaxChunk;
+constexpr int kCounterBytes = 256;    // work counters at the start of the workspace
+constexpr int kWaveMaxChunk = 4096;   // tokens per unit of the persistent wave kernel
 
 // ------------------------------------------------------------ device helpers
+
+// first token, size and count of the splits of a sequence (see DecodeParams)
+__host__ __device__ __forceinline__ int split_start(const DecodeParams& p, int s) {
+  return s < p.n_big ? s * p.chunk : p.n_big * p.chunk + (s - p.n_big) * p.chunk2;
+}
+__host__ __device__ __forceinline__ int split_size(const DecodeParams& p, int s) {
+  return s < p.n_big ? p.chunk : p.chunk2;
+}
+// splits holding at least one of L tokens
+__host__ __device__ __forceinline__ int split_count(const DecodeParams& p, int L) {
+  const int big = p.n_big * p.chunk;
+  return L <= big ? (L + p.chunk - 1) / p.chunk : p.n_big + (L - big + p.chunk2 - 1) / p.chunk2;
+}
 
 // bf16 pair in a 32-bit word -> two floats (exact).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -7,7 +7,7 @@
 // algebra behind the tiled attention of "Transformer推理核心：KV Cache、GQA与
 // RoPE原理与工程实践" §4.2 applied across workgroups.
 //
-// Only the ceil(L_b / chunk) splits that hold tokens are read.
+// Only the splits that hold tokens of the sequence are read.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   const int b = bh / p.H;
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
-  const int ns = (L + p.chunk - 1) / p.chunk;
+  const int ns = split_count(p, L);
   const int tid = threadIdx.x;
   float* out = p.out + static_cast<int64_t>(bh) * D + d0;
   if (ns == 0) {
@@ -76,9 +76,11 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
       a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
       ws += sm_w[r];
     }
-    const float inv = 1.f / ws;
+    // no split saw a valid token (every block invalid): empty softmax
+    const float inv = ws > 0.f ? 1.f / ws : 0.f;
     reinterpret_cast<float4*>(out)[tid] = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-    if (tid == 0 && blockIdx.y == 0 && p.lse) p.lse[bh] = (ref + log2f(ws)) * 0.69314718055994531f;
+    if (tid == 0 && blockIdx.y == 0 && p.lse)
+      p.lse[bh] = ws > 0.f ? (ref + log2f(ws)) * 0.69314718055994531f : kNegInf;
   }
 }
 

@@ -1,0 +1,180 @@
+// Device helpers shared by the two matrix-core decode kernels (bf16 KV):
+// operand types, the bf16 hi/lo split, buffer descriptors for the K/V
+// reads, the staged V-tile geometry in LDS and the inline-assembly LDS
+// accesses of that tile.  Not part of the C ABI.
+#pragma once
+
+#include "kvd_internal.h"
+
+namespace kvd {
+namespace mt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr float kNegInf = -__builtin_inff();
+// the running max moves only when a tile's max exceeds it by more than this
+// (log2 units): probabilities stay below 2^8, far inside fp32 / bf16 range
+constexpr float kRescaleSlack = 8.f;
+
+// bf16 bits of a finite float, nearest-even.
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<unsigned short>(u >> 16);
+}
+__device__ __forceinline__ float bf16_value(unsigned short h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// x ~= hi + lo with both bf16 (the residual x - hi is exact in fp32)
+__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - bf16_value(hi));
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// At most N of this wave's vector-memory loads (HBM -> LDS copies included)
+// are still outstanding; loads complete in issue order.
+template <int N>
+__device__ __forceinline__ void vmem_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// A 64-bit value made wave-uniform (readfirstlane of both halves).  The
+// builtin returns a signed int: each half goes back through uint32_t so the
+// low half is zero-extended, not sign-extended, when the halves are joined.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0: byte
+// offsets; word 3 = the gfx9-family default format).  A load at an offset
+// >= bytes is out of range: it touches no memory and returns zeros.  Both
+// arguments are wave-uniform by construction; readfirstlane keeps the
+// descriptor in scalar registers even where the compiler cannot prove it
+// (a descriptor it believes divergent costs a loop around every load).
+__device__ __forceinline__ rsrc_t make_rsrc(const char* base, uint32_t bytes) {
+  char* ub = reinterpret_cast<char*>(uniform_u64(reinterpret_cast<uint64_t>(base)));
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, n, 0x00020000);
+}
+// 16 bytes per lane from `r` at byte offset `off` into LDS at dst + 16*lane
+// (MUBUF rather than global: the compiler treats a pending global HBM -> LDS
+// copy like a FLAT access and then turns its own waits for unrelated
+// register loads into waits for everything)
+__device__ __forceinline__ void copy16_to_lds(rsrc_t r, lds_char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// A wave-uniform 32-bit read through the scalar cache (as constant memory:
+// only for data the kernel does not write).  Counted apart
+// from vector-memory loads, so waiting for it leaves those -- and an atomic
+// issued by one lane under a branch, whose place in their order the
+// compiler cannot pin down -- outstanding.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  return *reinterpret_cast<const_i32*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+template <int D>
+struct Geo {
+  static constexpr int KB = D / 32;          // 32-dim blocks of the score contraction
+  static constexpr int CB = D / 16;          // 16-dim blocks of the output
+  static constexpr int TT = kMfmaTileTokens; // 32 tokens per wave tile
+  static constexpr int LPR = D / 8;          // lanes per V row (16 bytes each)
+  static constexpr int RPI = 64 / LPR;       // V rows per load instruction
+  static constexpr int NVL = TT / RPI;       // V load instructions per tile
+  static constexpr int NLOADS = 2 * KB + NVL;  // vector-memory loads per tile
+  // every V copy instruction writes 1 KiB; instruction blocks are padded by
+  // 32 bytes so the transposed column reads of the four lane groups fall in
+  // different banks
+  static constexpr int BLOCK = 1024 + 32;
+  static constexpr int kTileBytes = NVL * BLOCK;
+  // byte offset of (token row r, byte c within the row) in a staged tile
+  __device__ __forceinline__ static constexpr int at(int r, int c) {
+    return (r / RPI) * BLOCK + (r % RPI) * (2 * D) + c;
+  }
+  // The P V A operand of lane (n, grp) is column n of token rows
+  // 16*(j/4) + 4*grp + j%4, j = 0..7: at(4*grp, 2n) plus this offset.
+  static constexpr int voff(int j) { return (16 * (j >> 2) / RPI) * BLOCK + (j & 3) * (2 * D); }
+};
+
+// Eight bf16 of one V column, from the staged tile at `addr` (+ voff(j)),
+// packed two per register; waits for its own LDS reads.  Issued from inline
+// assembly on purpose: the compiler cannot tell that these reads do not
+// touch the buffer an HBM -> LDS copy is still filling, and would otherwise
+// wait for every outstanding copy first, which serialises the pipeline.
+// Each value is read zero-extended and the pairs are packed with shifts:
+// with SRAM ECC on, a 16-bit "d16" load does not keep the other half of its
+// register.
+template <int D>
+__device__ __forceinline__ bf16x8 gather_v(uint32_t addr) {
+  using G = Geo<D>;
+  u32x4 r;
+  uint32_t r0, r1, r2, r3, x0, x1, x2, x3, x4, x5, x6, x7;
+  asm volatile(
+      "ds_read_u16 %4, %12 offset:%13\n\t"
+      "ds_read_u16 %5, %12 offset:%14\n\t"
+      "ds_read_u16 %6, %12 offset:%15\n\t"
+      "ds_read_u16 %7, %12 offset:%16\n\t"
+      "ds_read_u16 %8, %12 offset:%17\n\t"
+      "ds_read_u16 %9, %12 offset:%18\n\t"
+      "ds_read_u16 %10, %12 offset:%19\n\t"
+      "ds_read_u16 %11, %12 offset:%20\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_lshl_or_b32 %0, %5, 16, %4\n\t"
+      "v_lshl_or_b32 %1, %7, 16, %6\n\t"
+      "v_lshl_or_b32 %2, %9, 16, %8\n\t"
+      "v_lshl_or_b32 %3, %11, 16, %10"
+      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3),
+        "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
+      : "v"(addr), "i"(G::voff(0)), "i"(G::voff(1)), "i"(G::voff(2)), "i"(G::voff(3)),
+        "i"(G::voff(4)), "i"(G::voff(5)), "i"(G::voff(6)), "i"(G::voff(7)));
+  r[0] = r0; r[1] = r1; r[2] = r2; r[3] = r3;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 16 zero bytes at LDS address `addr` (inline assembly for the same reason
+// as gather_v; ordered after the copies by an explicit vmcnt wait)
+__device__ __forceinline__ void lds_zero16(uint32_t addr) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(z) : "memory");
+}
+
+// The dispatch order (chosen by the planner) of the (sequence, KV head,
+// split) units, slot x fastest: which of them run side by side decides how
+// the workgroups reading the same DRAM rows (the heads of one token range)
+// and the longest chunks are spread in time and across the XCDs.
+struct Unit { int b, g, split; };
+__device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int z) {
+  const int o = p.grid_order;
+  return Unit{o == 1 ? y : z, o == 0 ? y : x, o == 0 ? x : (o == 1 ? z : y)};
+}
+// the same order for a linear unit number
+__device__ __forceinline__ Unit unit_of_item(const DecodeParams& p, int item) {
+  const int o = p.grid_order;
+  const int nx = o == 0 ? p.n_splits : p.G;
+  const int ny = o == 0 ? p.G : (o == 1 ? p.B : p.n_splits);
+  const int yz = item / nx;
+  return unit_of(p, item - yz * nx, yz % ny, yz / ny);
+}
+
+}  // namespace mt
+}  // namespace kvd
