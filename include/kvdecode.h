@@ -159,13 +159,9 @@ kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_n
  *   lse        [B, H] fp32 output (natural log), or NULL
  *   workspace  device scratch of at least gqa_decode_workspace_size(shape,
  *              max_seq_len_host) bytes, 256-byte aligned, or NULL when that
- *              size is 0.  With the persistent kernel (the default for bf16
- *              caches) its first 256 bytes are work counters that MUST
- *              be zero before the first call that uses the workspace
- *              (allocate it zeroed, or clear it once); every call leaves them
- *              zero again.  The rest is scratch whose contents on entry are
- *              ignored.  Calls that may run at the same time (other streams)
- *              need separate workspaces.
+ *              size is 0; contents on entry are ignored.  Calls that may
+ *              run at the same time (other streams) need separate
+ *              workspaces.
  * Errors: EINVAL (null pointers, inconsistent shape, out overlapping q_rot),
  * EUNSUPPORTED, ERANGE (max_seq_len_host), EWORKSPACE, EHIP.
  */
@@ -189,13 +185,11 @@ const char* kvd_status_string(int32_t status);
  *
  * kvd_get_plan reports how gqa_decode_attn would run: plan[0] = tokens per
  * split (a multiple of 16), plan[1] = number of splits, plan[2] = kernel
- * (0 = VALU dot products, 1 = MFMA with one workgroup per split, 2 = MFMA
- * with persistent workgroups taking splits from a work counter),
- * plan[3] = workgroups launched by the split kernel.  `plan` is a host array
- * of 4 int32.
+ * (0 = VALU dot products, 1 = MFMA), plan[3] = workgroups launched by the
+ * split kernel.  `plan` is a host array of 4 int32.
  *
- * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU), 1 or
- * 2 (MFMA, bf16 only, up to 32 query heads per KV head); split_tokens = 0
+ * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU) or
+ * 1 (MFMA, bf16 only, up to 32 query heads per KV head); split_tokens = 0
  * (automatic) or a positive multiple of 16.  EUNSUPPORTED if the override
  * cannot run; the override applies to later calls in the whole process.
  */

@@ -24,7 +24,7 @@ LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(
 
 KVD_FP32, KVD_BF16 = 0, 1
 _STYLES = {"interleaved": 0, "half": 1}
-_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1, "persist": 2, "wave": 3}
+_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1}
 
 
 class KvdError(ValueError):
@@ -191,9 +191,7 @@ def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
     key = dev.index if dev.index is not None else torch.cuda.current_device()
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        # zeroed: the first 256 bytes are the wave kernel's work counters,
-        # which every call leaves at zero
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 
@@ -253,7 +251,7 @@ def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
 
 def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_tokens: int = 0,
                tail_span_tokens: int = -1, dispatch_order: Optional[int] = None) -> None:
-    """Process-wide override of the kernel ("valu", "mfma", "persist", "wave" or None
+    """Process-wide override of the kernel ("valu", "mfma" or None
     for automatic), the tokens per split (0 = automatic), the shorter splits
     covering the last ``tail_span_tokens`` positions (0 / -1 = automatic) and
     the MFMA dispatch order (0, 1, 2 or None for automatic)."""
@@ -270,7 +268,7 @@ def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
     arr = (ctypes.c_int32 * 4)()
     _check(load_library().kvd_get_plan(ctypes.byref(shape), msl, arr))
     return {"split_tokens": arr[0], "n_splits": arr[1],
-            "kernel": {0: "valu", 1: "mfma", 2: "persist", 3: "wave"}[arr[2]], "workgroups": arr[3]}
+            "kernel": {0: "valu", 1: "mfma"}[arr[2]], "workgroups": arr[3]}
 
 
 def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8, chunked: bool = False,

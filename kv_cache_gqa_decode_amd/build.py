@@ -23,10 +23,6 @@ FLAGS = [
     "-ffp-contract=fast", "-munsafe-fp-atomics",
     # no packed-fp32 instructions (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep single-lane atomics as written: the wave kernel claims its next
-    # work item ahead of time, and the atomic optimizer's wave-wide rewrite
-    # would wait for the returned value on the spot
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

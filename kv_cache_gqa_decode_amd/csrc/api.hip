@@ -20,12 +20,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
 
-// -1 auto, 0 VALU, 1 MFMA one workgroup per unit, 2 MFMA persistent
-// workgroups, 3 MFMA persistent waves
-std::atomic<int> g_kernel_override{-1};
-// resident workgroups per CU of the persistent MFMA kernels, per device,
-// kernel and (head_dim 128, n_rep > 16, paged); 0 = not yet queried
-std::atomic<int> g_persist_occ[kMaxDevices][2][2][2][2];
+std::atomic<int> g_kernel_override{-1};     // -1 auto, 0 VALU, 1 MFMA
 std::atomic<int> g_split_override{0};       // 0 auto
 std::atomic<int> g_tail_split_override{0};  // tokens per split near the end: 0 auto
 std::atomic<int> g_tail_span_override{-1};  // tokens covered by those splits: -1 auto
@@ -55,20 +50,6 @@ int device_cu_count(int* cu) {
   return 0;
 }
 
-int persistent_occupancy(bool waves, int D, int R, bool paged, int* occ) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
-  std::atomic<int>& slot = g_persist_occ[dev][waves][D == 128][R > 16][paged];
-  int v = slot.load(std::memory_order_relaxed);
-  if (v == 0) {
-    v = waves ? decode_wave_occupancy(D, R, paged) : decode_mfma_persistent_occupancy(D, R, paged);
-    if (v <= 0) return -1;
-    slot.store(v, std::memory_order_relaxed);
-  }
-  *occ = v;
-  return 0;
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kvd_status check_shape(const kvd_shape* s) {
@@ -92,8 +73,7 @@ struct Plan {
   int chunk2 = 0;       // tokens per split after those
   int n_big = 0;
   int n_splits = 0;
-  int kernel = 0;       // 0 VALU, 1 MFMA workgroup per unit, 2 MFMA persistent workgroups
-  int64_t n_items = 0;  // persistent kernel: B * G * n_splits units
+  int kernel = 0;       // 0 VALU, 1 MFMA
   int grid_order = 0;   // MFMA dispatch order (DecodeParams::grid_order)
   int head_groups = 1;  // VALU: query-head groups per KV head
   int rb = 1;           // VALU: heads per pass
@@ -102,42 +82,6 @@ struct Plan {
 };
 
 int round_up(int64_t x, int64_t m) { return static_cast<int>((x + m - 1) / m * m); }
-
-// Persistent wave kernel: tokens per unit.  Each wave should get several
-// units (about six at the host bound on lengths, so that faster waves take
-// more of them), but a unit's partial result (n_rep rows of D floats,
-// written and read back by the merge) should stay small next to its K/V
-// bytes: at least 64 tokens per query head, unless that would leave waves
-// without any unit.
-int wave_chunk(int64_t tokens, int64_t waves, int R, int max_len_host) {
-  const int64_t t_bal = (tokens + waves * 6 - 1) / (waves * 6);
-  const int64_t t_par = (tokens + waves - 1) / waves;
-  const int64_t t_ovh = 64 * static_cast<int64_t>(R);
-  const int64_t lo = t_ovh < t_par ? t_ovh : t_par;
-  int64_t t = t_bal > lo ? t_bal : lo;
-  t = (t + kMfmaTileTokens - 1) / kMfmaTileTokens * kMfmaTileTokens;
-  if (t < kMfmaTileTokens) t = kMfmaTileTokens;
-  if (t > kWaveMaxChunk) t = kWaveMaxChunk;
-  const int64_t cap = (static_cast<int64_t>(max_len_host) + 15) / 16 * 16;
-  if (t > cap) t = cap;
-  return static_cast<int>(t);
-}
-
-// Persistent MFMA kernel: tokens per (sequence, KV head, split) unit, a
-// multiple of the 128 tokens the four waves advance per step.  About
-// `per_wg` units per resident workgroup at the host bound on lengths, so
-// that faster workgroups can take more of them while each unit still
-// amortises its start (q, first tiles) and its merge.
-int persistent_chunk(int64_t tokens, int64_t max_wg, int per_wg, int max_len_host) {
-  const int64_t granule = kMfmaWaves * kMfmaTileTokens;
-  int64_t t = (tokens + max_wg * per_wg - 1) / (max_wg * per_wg);
-  t = (t + granule - 1) / granule * granule;
-  if (t < 2 * granule) t = 2 * granule;
-  if (t > 2048) t = 2048;
-  const int64_t cap = (static_cast<int64_t>(max_len_host) + 15) / 16 * 16;
-  if (t > cap) t = cap;
-  return static_cast<int>(t);
-}
 
 // Splits of [0, max_len): `chunk` tokens each, except that the last
 // `tail span` tokens (tuning; none by default) are cut into splits of
@@ -161,48 +105,8 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   const bool mfma_ok = s->kv_dtype == KVD_BF16 && R <= 32;
   int kernel = g_kernel_override.load();
   if (kernel < 0) kernel = mfma_ok ? 1 : 0;
-  if (kernel >= 1 && !mfma_ok) return KVD_EUNSUPPORTED;
+  if (kernel == 1 && !mfma_ok) return KVD_EUNSUPPORTED;
   pl->kernel = kernel;
-  if (kernel >= 2) {
-    const bool waves = kernel == 3;
-    const bool paged = s->block_size == 16;
-    int occ = 0;
-    if (persistent_occupancy(waves, s->head_dim, R, paged, &occ) != 0) return KVD_EHIP;
-    const int64_t max_wg = static_cast<int64_t>(cu) * occ;
-    const int64_t workers_per_wg = waves ? kMfmaWaves : 1;
-    const int max_chunk = waves ? kWaveMaxChunk : kMfmaMaxChunk;
-    pl->rb = R;
-    pl->head_groups = 1;
-    pl->workspace = kCounterBytes;
-    pl->grid_order = s->batch == 1 ? 0 : (s->block_size == 16 ? 2 : 1);
-    if (max_len_host <= 0 || s->batch == 0) {
-      pl->chunk = 16; pl->n_splits = 0; pl->wgs = 0; pl->n_items = 0;
-      return KVD_OK;
-    }
-    const int64_t bg = static_cast<int64_t>(s->batch) * s->n_kv_heads;
-    int chunk = g_split_override.load();
-    if (chunk <= 0)
-      chunk = waves ? wave_chunk(bg * max_len_host, max_wg * kMfmaWaves, R, max_len_host)
-                    : persistent_chunk(bg * max_len_host, max_wg, 6, max_len_host);
-    if (chunk > max_chunk) chunk = max_chunk;
-    if (chunk > round_up(max_len_host, 16)) chunk = round_up(max_len_host, 16);
-    // unit numbers are int32
-    while (bg * ((max_len_host + chunk - 1) / chunk) > (int64_t{1} << 30) && chunk < max_chunk)
-      chunk *= 2;
-    if (chunk > max_chunk) chunk = max_chunk;
-    set_splits(pl, chunk, max_len_host);
-    if (g_order_override.load() >= 0) pl->grid_order = g_order_override.load();
-    pl->n_items = bg * pl->n_splits;
-    if (pl->n_items > (int64_t{1} << 30)) return KVD_EUNSUPPORTED;
-    const int64_t want = (pl->n_items + workers_per_wg - 1) / workers_per_wg;
-    pl->wgs = want < max_wg ? want : max_wg;
-    if (pl->n_splits > 1) {
-      const size_t rows = static_cast<size_t>(s->batch) * s->n_heads * pl->n_splits;
-      const size_t o_bytes = (rows * s->head_dim * sizeof(float) + 255) / 256 * 256;
-      pl->workspace += o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
-    }
-    return KVD_OK;
-  }
   if (kernel == 1) {
     pl->rb = R;
     pl->head_groups = 1;
@@ -220,17 +124,21 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   if (chunk <= 0) {
     // Resident workgroups: two per CU (one for more than 16 heads per KV head,
     // whose workgroups need twice the registers) for the MFMA kernel, four
-    // for the VALU kernel.  Aim for about two rounds of them over the
-    // (sequence, KV head) pairs at the host bound on lengths -- one round
-    // with more than 16 heads, whose merge epilogue is heavier -- and no
-    // more than 2048 tokens per split.
+    // for the VALU kernel.  The MFMA kernel aims for about four rounds of
+    // them over the (sequence, KV head) pairs at the host bound on lengths
+    // (one round with more than 16 heads, whose merge epilogue is heavier)
+    // and at most 1024 tokens per split: the workgroups that share a CU run
+    // at different speeds (the older one is served first), and smaller
+    // units let the dispatcher even that out at a small cost in merges.
+    // The VALU kernel aims for two rounds of at most 2048 tokens.
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (R > 16 ? 1 : 2));
-    const int64_t rounds = (kernel == 1 && R > 16) ? 1 : 2;
+    const int64_t rounds = kernel == 0 ? 2 : (R > 16 ? 1 : 4);
+    const int cap = kernel == 0 ? 2048 : 1024;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
-    if (chunk > 2048) chunk = 2048;
+    if (chunk > cap) chunk = cap;
   }
   if (chunk > kMaxChunk) chunk = kMaxChunk;
   // the split index is a grid dimension: at most 65535 splits
@@ -249,13 +157,10 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   if (g_order_override.load() >= 0) pl->grid_order = g_order_override.load();
   pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
   if (pl->n_splits > 1) {
-    // same layout as for the persistent kernel: the counter bytes stay reserved
-    // (and untouched), so a workspace shared by calls of both kernels keeps
-    // its counters at zero
     const size_t rows = static_cast<size_t>(s->batch) * s->n_heads * pl->n_splits;
     size_t o_bytes = rows * s->head_dim * sizeof(float);
     o_bytes = (o_bytes + 255) / 256 * 256;
-    pl->workspace = kCounterBytes + o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
+    pl->workspace = o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
   } else {
     pl->workspace = 0;
   }
@@ -280,7 +185,7 @@ const char* kvd_status_string(int32_t status) {
 
 kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
                              int32_t tail_span_tokens, int32_t dispatch_order) {
-  if (kernel < -1 || kernel > 3) return KVD_EINVAL;
+  if (kernel < -1 || kernel > 1) return KVD_EINVAL;
   if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
   if (tail_split_tokens < 0 || tail_split_tokens % 16 != 0) return KVD_EINVAL;
   if (tail_span_tokens < -1 || dispatch_order < -1 || dispatch_order > 2) return KVD_EINVAL;
@@ -385,20 +290,14 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
   p.qscale = scale * 1.4426950408889634f;
   p.direct = pl.n_splits <= 1 ? 1 : 0;
   p.grid_order = pl.grid_order;
-  p.counters = nullptr; p.n_items = 0; p.n_workers = 0;
+  // workspace layout: [partial O][partial lse]
   p.part_o = nullptr; p.part_lse = nullptr;
-  // workspace layout for every kernel: [work counters][partial O][partial lse]
-  char* ws = static_cast<char*>(workspace);
-  if (pl.kernel >= 2) {
-    p.counters = reinterpret_cast<uint32_t*>(ws);
-    p.n_items = static_cast<int32_t>(pl.n_items);
-    p.n_workers = static_cast<int32_t>(pl.wgs) * (pl.kernel == 3 ? kMfmaWaves : 1);
-  }
   if (pl.n_splits > 1) {
+    char* ws = static_cast<char*>(workspace);
     const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
     const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
-    p.part_o = reinterpret_cast<float*>(ws + kCounterBytes);
-    p.part_lse = reinterpret_cast<float*>(ws + kCounterBytes + o_bytes);
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
   }
 
   if (pl.n_splits == 0) {
@@ -417,11 +316,8 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
     }
   }
   if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
-  const hipError_t e =
-      pl.kernel == 3 ? launch_decode_wave(p, paged, static_cast<int>(pl.wgs), s)
-    : pl.kernel == 2 ? launch_decode_mfma(p, paged, static_cast<int>(pl.wgs), s)
-    : pl.kernel == 1 ? launch_decode_mfma(p, paged, 0, s)
-                     : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
+  const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)
+                                      : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
   if (e != hipSuccess) return KVD_EHIP;
   if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
   if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;

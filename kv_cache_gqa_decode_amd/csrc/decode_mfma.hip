@@ -443,75 +443,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
 }
 
-// 32-bit LDS accesses of the unit hand-off slots, from inline assembly for
-// the reason given at gather_v (each waits for itself)
-__device__ __forceinline__ void lds_write_u32(uint32_t addr, int v) {
-  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
-}
-__device__ __forceinline__ int lds_read_u32(uint32_t addr) {
-  int v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-
-// Persistent workgroups: a grid sized to what the device holds at once keeps
-// taking the next unit number from an atomic counter in the workspace (in
-// the same order as the dispatch order above) until the units run out, so
-// workgroups that stream faster take more units and no last round of
-// workgroups leaves the device half idle.  Wave 0 claims the unit after the
-// current one when the current one starts and hands it to the other waves
-// through a double-buffered LDS slot at the barrier that closes each unit
-// (that barrier also keeps the next unit's V copies out of the merge area
-// until every wave has read it).  The last workgroup to leave puts both
-// counters back to zero.  Unit numbers compare unsigned: counters that do
-// not start at zero (a workspace the caller did not clear) can only make
-// workgroups leave early, never index outside the batch.
-template <int D, int NB, bool PAGED>
-__global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeParams p) {
-  __shared__ __align__(16) char smem[smem_bytes<D>()];
-  __shared__ int sm_next[2];
-  typedef __attribute__((address_space(1))) uint32_t global_u32;
-  global_u32* const ctr = (global_u32*)(p.counters);
-  const bool leader = threadIdx.x == 0;
-  const uint32_t slot0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(sm_next)));
-  auto claim = [&]() -> int {
-    int v = 0;
-    if (leader) v = static_cast<int>(__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    return v;
-  };
-
-  int par = 0;
-  {
-    const int first = claim();
-    if (leader) lds_write_u32(slot0, first);
-    __builtin_amdgcn_s_barrier();
-  }
-  int item = __builtin_amdgcn_readfirstlane(lds_read_u32(slot0));
-  while (static_cast<uint32_t>(item) < static_cast<uint32_t>(p.n_items)) {
-    const int next_v = claim();
-    const Unit u = unit_of_item(p, item);
-    run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
-    par ^= 1;
-    if (leader) lds_write_u32(slot0 + 4 * par, next_v);
-    __builtin_amdgcn_s_barrier();
-    item = __builtin_amdgcn_readfirstlane(lds_read_u32(slot0 + 4 * par));
-  }
-  if (leader) {
-    const uint32_t done = __hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == static_cast<uint32_t>(p.n_workers) - 1u) {
-      __hip_atomic_exchange(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_exchange(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
 template <int D, int NB>
-hipError_t launch_nb(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
-  if (persistent_wg > 0) {
-    if (paged) decode_mfma_persistent_kernel<D, NB, true><<<persistent_wg, 256, 0, s>>>(p);
-    else decode_mfma_persistent_kernel<D, NB, false><<<persistent_wg, 256, 0, s>>>(p);
-    return hipGetLastError();
-  }
+hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
   const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
                   : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
                                       : dim3(p.G, p.n_splits, p.B);
@@ -521,39 +454,17 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, int persistent_wg, hipSt
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
-  return p.R <= 16 ? launch_nb<D, 1>(p, paged, persistent_wg, s)
-                   : launch_nb<D, 2>(p, paged, persistent_wg, s);
-}
-
-template <int D, int NB, bool PAGED>
-const void* persistent_fn() {
-  return reinterpret_cast<const void*>(&decode_mfma_persistent_kernel<D, NB, PAGED>);
+hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
+  return p.R <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, int persistent_wg, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
   if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits)
     return hipErrorInvalidValue;
-  if (persistent_wg > 0 && (!p.counters || p.n_workers != persistent_wg)) return hipErrorInvalidValue;
-  return p.D == 64 ? launch_d<64>(p, paged, persistent_wg, s) : launch_d<128>(p, paged, persistent_wg, s);
-}
-
-int decode_mfma_persistent_occupancy(int D, int R, bool paged) {
-  const bool nb2 = R > 16;
-  const void* fn;
-  if (D == 64) {
-    fn = nb2 ? (paged ? persistent_fn<64, 2, true>() : persistent_fn<64, 2, false>())
-             : (paged ? persistent_fn<64, 1, true>() : persistent_fn<64, 1, false>());
-  } else {
-    fn = nb2 ? (paged ? persistent_fn<128, 2, true>() : persistent_fn<128, 2, false>())
-             : (paged ? persistent_fn<128, 1, true>() : persistent_fn<128, 1, false>());
-  }
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess) return 0;
-  return n;
+  return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);
 }
 
 }  // namespace kvd

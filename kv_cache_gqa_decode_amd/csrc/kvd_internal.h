@@ -36,11 +36,6 @@ struct DecodeParams {
   float qscale;             // softmax scale * log2(e)
   int32_t direct;           // 1: one split, write out / lse directly
   int32_t grid_order;       // MFMA kernel: 0 (split, G, B), 1 (G, B, split), 2 (G, split, B)
-  // persistent MFMA kernel: units (sequence, KV head, split) handed out by an
-  // atomic counter; counters[0] = next unit, counters[1] = workgroups done
-  uint32_t* counters;
-  int32_t n_items;          // B * G * n_splits
-  int32_t n_workers;        // workgroups launched
 };
 
 struct RopeParams {
@@ -65,19 +60,8 @@ hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
                               int rb, hipStream_t stream);
-// persistent_wg > 0: that many persistent workgroups taking units from
-// p.counters; 0: one workgroup per unit.
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, int persistent_wg,
-                              hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
-// Resident workgroups per CU of the persistent MFMA kernel for (D, n_rep,
-// paged), or 0.
-int decode_mfma_persistent_occupancy(int D, int R, bool paged);
-// Persistent wave kernel: `n_wg` workgroups of 4 waves, each wave taking
-// (sequence, KV head, split) units from p.counters (p.n_workers = waves).
-hipError_t launch_decode_wave(const DecodeParams& p, bool paged, int n_wg, hipStream_t stream);
-int decode_wave_occupancy(int D, int R, bool paged);
-
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).
 int valu_heads_per_pass(int n_rep);
 // Workgroups and tokens per workgroup-iteration of the MFMA kernel.
@@ -85,8 +69,6 @@ constexpr int kMfmaWaves = 4;
 constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
 constexpr int kMaxChunk = 8192;       // tokens per split, upper bound
 constexpr int kMfmaMaxChunk = kMaxChunk;
-constexpr int kCounterBytes = 256;    // work counters at the start of the workspace
-constexpr int kWaveMaxChunk = 4096;   // tokens per unit of the persistent wave kernel
 
 // ------------------------------------------------------------ device helpers
 

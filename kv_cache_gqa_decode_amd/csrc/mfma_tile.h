@@ -68,12 +68,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char* base, uint32_t bytes) {
   const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
   return __builtin_amdgcn_make_buffer_rsrc(ub, 0, n, 0x00020000);
 }
+// Cache policy of the V copies: non-temporal.  Every V byte is read exactly
+// once and each copy instruction reads whole 128-byte lines, so keeping
+// them in the caches only displaces other traffic; marking them streaming
+// measured +15% (long single sequences) to +5% (batches) of bandwidth.  The
+// K loads keep the default policy: each K instruction reads half of a line
+// whose other half the next instruction reads, and a non-temporal first
+// half is fetched twice.
+constexpr int kCopyPolicyNT = 2;
 // 16 bytes per lane from `r` at byte offset `off` into LDS at dst + 16*lane
 // (MUBUF rather than global: the compiler treats a pending global HBM -> LDS
 // copy like a FLAT access and then turns its own waits for unrelated
 // register loads into waits for everything)
 __device__ __forceinline__ void copy16_to_lds(rsrc_t r, lds_char* dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, kCopyPolicyNT);
 }
 __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -167,14 +175,5 @@ __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int
   const int o = p.grid_order;
   return Unit{o == 1 ? y : z, o == 0 ? y : x, o == 0 ? x : (o == 1 ? z : y)};
 }
-// the same order for a linear unit number
-__device__ __forceinline__ Unit unit_of_item(const DecodeParams& p, int item) {
-  const int o = p.grid_order;
-  const int nx = o == 0 ? p.n_splits : p.G;
-  const int ny = o == 0 ? p.G : (o == 1 ? p.B : p.n_splits);
-  const int yz = item / nx;
-  return unit_of(p, item - yz * nx, yz % ny, yz / ny);
-}
-
 }  // namespace mt
 }  // namespace kvd

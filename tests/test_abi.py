@@ -105,7 +105,7 @@ def test_rope_rejects_bad_arguments(lib):
 
 def test_tuning_and_timer_validation(lib):
     assert lib.kvd_set_tuning(-2, 0) == EINVAL
-    assert lib.kvd_set_tuning(4, 0) == EINVAL
+    assert lib.kvd_set_tuning(2, 0) == EINVAL
     assert lib.kvd_set_tuning(0, 24) == EINVAL           # not a multiple of 16
     assert lib.kvd_set_tuning(0, -16) == EINVAL
     assert lib.kvd_set_tuning(-1, 0) == OK

@@ -65,7 +65,7 @@ def test_c2_bf16_llama_shape(q_gain):
 RAGGED = np.array([1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 1023, 1024], np.int32)
 
 
-KERNELS = [("f32", "valu"), ("bf16", "valu"), ("bf16", "mfma"), ("bf16", "persist"), ("bf16", "wave")]
+KERNELS = [("f32", "valu"), ("bf16", "valu"), ("bf16", "mfma")]
 
 
 @pytest.mark.parametrize("dtype,kernel", KERNELS)
@@ -76,7 +76,7 @@ def test_varlen_contiguous(dtype, kernel, split):
     check_full(p, kernel=kernel, split=split, what=f"varlen {dtype} {kernel} split={split}")
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma", "persist", "wave"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 16, 48, 256])
 def test_paged_small(kernel, split):
     s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
@@ -96,7 +96,7 @@ def test_auto_plan_picks_matrix_cores_for_bf16():
         kvd.get_plan(4, 32, k32)
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma", "persist", "wave"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 32])
 def test_paged_equals_contiguous_bitwise(kernel, split):
     """The same logical cache, paged or contiguous, gives identical bits."""
@@ -161,7 +161,7 @@ def test_out_of_range_positions_skip_the_append():
     assert torch.equal(before.view(torch.int16), t["k_cache"].view(torch.int16))
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma", "persist", "wave"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_split_counts_agree(kernel):
     """Different split sizes reduce in different orders: results agree to
     rounding and every one matches the oracle."""
@@ -204,57 +204,7 @@ def test_repeated_steps_are_idempotent():
     assert torch.equal(k1.view(torch.int16), t["k_cache"].view(torch.int16))
 
 
-@pytest.mark.parametrize("kernel", ["persist", "wave"])
-def test_persistent_counters_return_to_zero(kernel):
-    """The persistent kernel hands out work from two counters at the
-    start of the workspace; every call must leave them at zero, whatever the
-    shape, so the next call on the same workspace starts from item 0."""
-    dev = device()
-    kvd.set_tuning(kernel, 0)
-    ws = None
-    for lens, smax, split in (([700, 129, 1], 768, 0), ([5, 1, 3000], 4096, 64),
-                              ([17], 32, 0), ([4096, 2500], 4096, 4096)):
-        s = W.spec("c3", batch=len(lens), max_seq_len=smax, q_gain=4.0)
-        p = W.make_problem(s, lengths=np.array(lens, np.int32))
-        t = upload(p, dev)
-        kvd.set_tuning(kernel, split)
-        q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
-                                   t["positions"])
-        need = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=smax)
-        assert need >= 256
-        if ws is None or ws.numel() < need:
-            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-        out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
-                                       max_seq_len=smax, workspace=ws)
-        torch.cuda.synchronize()
-        assert int(ws[:8].view(torch.int32).abs().sum()) == 0
-        _, oo, ol, _, _ = oracle_step(p)
-        gates.assert_out(out.cpu().numpy(), oo, s.dtype, f"persistent counters {lens}")
-
-
-def test_kernels_share_a_workspace():
-    """Calls of the VALU or workgroup kernels and of the persistent kernel may use
-    the same workspace one after the other: the split partials of the former
-    never touch the persistent kernel's counters at the start of the workspace."""
-    dev = device()
-    s = W.spec("c3", batch=3, max_seq_len=1024, q_gain=4.0)
-    p = W.make_problem(s, lengths=np.array([1000, 333, 17], np.int32))
-    t = upload(p, dev)
-    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
-                               t["positions"])
-    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=dev)
-    _, oo, ol, _, _ = oracle_step(p)
-    for kernel, split in (("valu", 64), ("mfma", 128), ("persist", 128), ("wave", 64), ("valu", 16),
-                           ("wave", 0), ("persist", 0)):
-        kvd.set_tuning(kernel, split)
-        out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
-                                       max_seq_len=1024, workspace=ws)
-        torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, kernel
-        gates.assert_out(out.cpu().numpy(), oo, s.dtype, f"shared workspace {kernel} {split}")
-
-
-@pytest.mark.parametrize("kernel", ["valu", "mfma", "persist", "wave"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split,tail,span", [(256, 64, 400), (512, 128, 1024), (128, 16, 96),
                                              (1024, 1024, 500), (256, 32, 0)])
 @pytest.mark.parametrize("order", [None, 0, 1, 2])
@@ -270,7 +220,7 @@ def test_two_level_splits(kernel, split, tail, span, order):
                what=f"{kernel} split={split} tail={tail}/{span} order={order}")
 
 
-@pytest.mark.parametrize("kernel", ["mfma", "persist", "wave"])
+@pytest.mark.parametrize("kernel", ["mfma"])
 @pytest.mark.parametrize("order", [0, 1, 2])
 def test_two_level_splits_paged(kernel, order):
     s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
