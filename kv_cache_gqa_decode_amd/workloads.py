@@ -24,6 +24,14 @@ the overrides; see ``Spec``):
   (zero otherwise), so a read outside the valid range shows up in the output.
 * Paged pools: a seeded permutation of all physical blocks, sequence b owning
   ``perm[b * max_blocks_per_seq : (b + 1) * max_blocks_per_seq]``.
+* INT8 caches (dtype ``"i8"``): q, k_new and v_new as for bf16; the cached
+  history is drawn directly as codes, N(0, 40^2) clipped to [-127, 127] and
+  cast (truncating) to int8, i.e. data whose per-head absolute maximum sits
+  near 3.2 standard deviations; the per-head scales (stream 5) are
+  ``value_scale / 40 * U[0.75, 1.25]`` for K, then for V, in float32, so
+  dequantised values have about the spread of the bf16 workloads.  Poisoned
+  slots hold code 127.  V is laid out transposed inside every 16-token
+  group: ``[B, S_max/16, G, D, 16]`` or ``[num_blocks, G, D, 16]``.
 """
 from __future__ import annotations
 
@@ -40,7 +48,7 @@ BF16_NAN = np.uint16(0x7FC0)
 class Spec:
     name: str
     cfg_id: int
-    dtype: str                  # "f32" | "bf16"
+    dtype: str                  # "f32" | "bf16" | "i8" (bf16 inputs, INT8 cache)
     batch: int
     n_heads: int
     n_kv_heads: int
@@ -62,7 +70,13 @@ class Spec:
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        """Bytes per cached K or V element."""
+        return {"f32": 4, "bf16": 2, "i8": 1}[self.dtype]
+
+    @property
+    def input_dtype(self) -> str:
+        """dtype of q, k_new and v_new."""
+        return "bf16" if self.dtype == "i8" else self.dtype
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -108,6 +122,8 @@ class Problem:
     positions: np.ndarray       # [B] int32
     seq_lens: np.ndarray        # [B] int32 = positions + 1
     block_table: Optional[np.ndarray]  # [B, max_blocks_per_seq] int32
+    k_scale: Optional[np.ndarray] = None   # INT8 caches: [G] float32
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def max_len(self) -> int:
@@ -129,7 +145,32 @@ def _to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
 def _fill_value(s: Spec):
     if s.dtype == "f32":
         return np.float32(np.nan) if s.poison else np.float32(0)
+    if s.dtype == "i8":
+        return np.int8(127) if s.poison else np.int8(0)
     return BF16_NAN if s.poison else np.uint16(0)
+
+
+I8_CODE_STD = 40.0
+
+
+def _codes(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32) * np.float32(I8_CODE_STD)
+    return np.clip(x, -127, 127).astype(np.int8)
+
+
+def draw_scales(s: Spec):
+    """Per-KV-head scales of an INT8 cache: (k_scale, v_scale), [G] float32 each."""
+    rng = _rng(s, 5)
+    base = s.value_scale / I8_CODE_STD
+    k = (base * rng.uniform(0.75, 1.25, s.n_kv_heads)).astype(np.float32)
+    v = (base * rng.uniform(0.75, 1.25, s.n_kv_heads)).astype(np.float32)
+    return k, v
+
+
+def group_transpose(x: np.ndarray) -> np.ndarray:
+    """[n * 16, G, D] -> [n, G, D, 16]: V rows regrouped into the INT8 layout."""
+    n16, G, D = x.shape
+    return np.ascontiguousarray(x.reshape(n16 // 16, 16, G, D).transpose(0, 2, 3, 1))
 
 
 def draw_lengths(s: Spec) -> np.ndarray:
@@ -141,6 +182,9 @@ def draw_history(s: Spec, b: int, n_tokens: int):
     """Cached (already rotated) K and V of sequence b: two [n, G, D] arrays."""
     rng = _rng(s, 1000 + b)
     shape = (n_tokens, s.n_kv_heads, s.head_dim)
+    if s.dtype == "i8":
+        k = _codes(rng, shape)
+        return k, _codes(rng, shape)
     k = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
     v = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
     return _to_storage(k, s.dtype), _to_storage(v, s.dtype)
@@ -158,7 +202,10 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
     q = _rng(s, 1).standard_normal((B, H, D), dtype=np.float32) * sc * np.float32(s.q_gain)
     k_new = _rng(s, 2).standard_normal((B, G, D), dtype=np.float32) * sc
     v_new = _rng(s, 3).standard_normal((B, G, D), dtype=np.float32) * sc
-    store = np.float32 if s.dtype == "f32" else np.uint16
+    store = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[s.dtype]
+    i8 = s.dtype == "i8"
+    if i8 and (s.max_seq_len % 16 or s.block_size not in (0, 16)):
+        raise ValueError("INT8 caches group tokens by 16")
     fill = _fill_value(s)
     table = None
     if s.block_size:
@@ -169,7 +216,8 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
         table = np.ascontiguousarray(
             perm[: B * s.max_blocks_per_seq].reshape(B, s.max_blocks_per_seq))
         k_cache = np.full((s.num_blocks, bs, G, D), fill, dtype=store)
-        v_cache = np.full((s.num_blocks, bs, G, D), fill, dtype=store)
+        v_cache = np.full((s.num_blocks, G, D, bs) if i8 else (s.num_blocks, bs, G, D), fill,
+                          dtype=store)
         for b in range(B):
             n_hist = int(L[b]) - 1
             if n_hist == 0:
@@ -182,20 +230,30 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
                 vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
             ids = table[b, :nblk]
             k_cache[ids] = kh.reshape(nblk, bs, G, D)
-            v_cache[ids] = vh.reshape(nblk, bs, G, D)
+            v_cache[ids] = group_transpose(vh) if i8 else vh.reshape(nblk, bs, G, D)
     else:
-        k_cache = np.full((B, s.max_seq_len, G, D), fill, dtype=store)
-        v_cache = np.full((B, s.max_seq_len, G, D), fill, dtype=store)
+        S = s.max_seq_len
+        k_cache = np.full((B, S, G, D), fill, dtype=store)
+        v_cache = np.full((B, S // 16, G, D, 16) if i8 else (B, S, G, D), fill, dtype=store)
         for b in range(B):
             n_hist = int(L[b]) - 1
             if n_hist:
                 kh, vh = draw_history(s, b, n_hist)
                 k_cache[b, :n_hist] = kh
-                v_cache[b, :n_hist] = vh
-    return Problem(spec=s, q=_to_storage(q, s.dtype), k_new=_to_storage(k_new, s.dtype),
-                   v_new=_to_storage(v_new, s.dtype), k_cache=k_cache, v_cache=v_cache,
+                if i8:
+                    nblk = -(-n_hist // 16)
+                    pad = nblk * 16 - n_hist
+                    if pad:
+                        vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
+                    v_cache[b, :nblk] = group_transpose(vh)
+                else:
+                    v_cache[b, :n_hist] = vh
+    k_scale, v_scale = draw_scales(s) if i8 else (None, None)
+    idt = s.input_dtype
+    return Problem(spec=s, q=_to_storage(q, idt), k_new=_to_storage(k_new, idt),
+                   v_new=_to_storage(v_new, idt), k_cache=k_cache, v_cache=v_cache,
                    positions=(L - 1).astype(np.int32), seq_lens=L.astype(np.int32),
-                   block_table=table)
+                   block_table=table, k_scale=k_scale, v_scale=v_scale)
 
 
 def as_torch(a: np.ndarray, device=None):

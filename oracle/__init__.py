@@ -16,6 +16,14 @@ Contents
   the decode loop.
 * ``merge``: the log-sum-exp merge of attention over disjoint token sets.
 
+INT8 caches ([KVGR] §4.3: K and V stored as 8-bit integers with
+quantisation parameters calibrated per attention head): dtype ``"i8"``.  q,
+k_new and v_new are then bf16; the caches hold codes in [-127, 127] with one
+fp32 scale per KV head for K (``k_scale``) and one for V (``v_scale``).  A
+new element x is stored as the code nearest to x / scale (ties to even,
+saturating); attention reads scale * code.  V is transposed inside every
+16-token group (``Geometry.v_cache_shape``).
+
 Arrays: bf16 data are passed as ``uint16`` bit patterns; fp32 as ``float32``;
 fp64 as ``float64``.  Pages cited by title:
   [KVGR] "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践"
@@ -29,11 +37,12 @@ import numpy as np
 
 from .build import LIB, build
 
-F64, F32, BF16 = 0, 1, 2
+F64, F32, BF16, I8 = 0, 1, 2, 3
 INTERLEAVED, HALF = 0, 1
 
-_DTYPE_CODE = {"f64": F64, "f32": F32, "bf16": BF16}
-_NP_STORAGE = {F64: np.float64, F32: np.float32, BF16: np.uint16}
+_DTYPE_CODE = {"f64": F64, "f32": F32, "bf16": BF16, "i8": I8}
+_NP_STORAGE = {F64: np.float64, F32: np.float32, BF16: np.uint16, I8: np.int8}
+_NP_INPUT = {F64: np.float64, F32: np.float32, BF16: np.uint16, I8: np.uint16}
 _STYLE_CODE = {"interleaved": INTERLEAVED, "half": HALF}
 
 
@@ -57,6 +66,8 @@ def _load():
         lib.kvo_round_to_bf16.argtypes = [ctypes.c_double]
         lib.kvo_bf16_bits.restype = ctypes.c_uint16
         lib.kvo_bf16_bits.argtypes = [ctypes.c_double]
+        lib.kvo_quantize_i8.restype = ctypes.c_int
+        lib.kvo_quantize_i8.argtypes = [ctypes.c_double, ctypes.c_double]
         lib.kvo_theta.restype = ctypes.c_double
         lib.kvo_theta.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.kvo_rope_rotate.restype = None
@@ -65,6 +76,16 @@ def _load():
         lib.kvo_rope_append.restype = ctypes.c_int
         lib.kvo_rope_append.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P,
                                         P, P, ctypes.c_double, ctypes.c_int]
+        lib.kvo_rope_append_i8.restype = ctypes.c_int
+        lib.kvo_rope_append_i8.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P, P,
+                                           P, P, ctypes.c_double, ctypes.c_int]
+        lib.kvo_decode_attn_i8.restype = ctypes.c_int
+        lib.kvo_decode_attn_i8.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P, P,
+                                           ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.kvo_decode_attn_units_i8.restype = ctypes.c_int
+        lib.kvo_decode_attn_units_i8.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P,
+                                                 P, ctypes.c_double, P, P, ctypes.c_int64,
+                                                 P, P, ctypes.c_int]
         lib.kvo_decode_attn.restype = ctypes.c_int
         lib.kvo_decode_attn.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P,
                                         ctypes.c_double, P, P, P, ctypes.c_int]
@@ -101,6 +122,7 @@ class Geometry:
     Contiguous caches are ``[B, S_max, G, D]``; paged pools are
     ``[num_blocks, block_size, G, D]`` with an int32 table
     ``[B, max_blocks_per_seq]`` ([OPT] §四 PagedKVCache; [KVGR] §4.1).
+    INT8 V caches are ``[B, S_max/16, G, D, 16]`` or ``[num_blocks, G, D, 16]``.
     """
 
     def __init__(self, batch, n_heads, n_kv_heads, head_dim, dtype="bf16",
@@ -114,6 +136,8 @@ class Geometry:
         if block_size:
             max_seq_len = max_blocks_per_seq * block_size
         self.max_seq_len = max_seq_len
+        if dtype == "i8" and (max_seq_len % 16 or block_size not in (0, 16)):
+            raise ValueError("INT8 caches group tokens by 16")
 
     @property
     def code(self):
@@ -121,12 +145,26 @@ class Geometry:
 
     @property
     def storage(self):
+        """numpy dtype of the caches."""
         return _NP_STORAGE[self.code]
+
+    @property
+    def input_storage(self):
+        """numpy dtype of q, k_new and v_new."""
+        return _NP_INPUT[self.code]
 
     def cache_shape(self):
         if self.block_size:
             return (self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim)
         return (self.batch, self.max_seq_len, self.n_kv_heads, self.head_dim)
+
+    def v_cache_shape(self):
+        if self.dtype != "i8":
+            return self.cache_shape()
+        G, D = self.n_kv_heads, self.head_dim
+        if self.block_size:
+            return (self.num_blocks, G, D, 16)
+        return (self.batch, self.max_seq_len // 16, G, D, 16)
 
     def _c(self):
         return _Shape(self.batch, self.n_heads, self.n_kv_heads, self.head_dim,
@@ -148,6 +186,21 @@ def bf16_bits(x: float) -> int:
     return int(_load().kvo_bf16_bits(float(x)))
 
 
+def quantize_i8(x: float, s: float) -> int:
+    """INT8 code of x under scale s: nearest integer to x / s in [-127, 127]
+    (ties to even, fp64 quotient, saturating; NaN gives 0) ([KVGR] §4.3)."""
+    return int(_load().kvo_quantize_i8(float(x), float(s)))
+
+
+def _scales(geom, k_scale, v_scale):
+    if geom.dtype != "i8":
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("scales are only for INT8 caches")
+        return None, None
+    G = geom.n_kv_heads
+    return (_need(k_scale, np.float32, "k_scale", (G,)), _need(v_scale, np.float32, "v_scale", (G,)))
+
+
 def rope_rotate(x, pos, base=10000.0, style="interleaved"):
     """R_pos x for every row of an fp64 array [..., D] ([KVGR] §3)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
@@ -162,45 +215,56 @@ def rope_rotate(x, pos, base=10000.0, style="interleaved"):
 
 
 def rope_append(geom: Geometry, q, k_new, v_new, k_cache, v_cache, positions,
-                block_table=None, base=10000.0, style="interleaved"):
+                block_table=None, base=10000.0, style="interleaved", k_scale=None,
+                v_scale=None):
     """Rotate q and k_new at positions[b] and write k_rot, v_new into the caches.
 
     The caches are modified in place.  Returns q_rot [B, H, D] fp64.
+    INT8 caches take the per-head scales ``k_scale``, ``v_scale`` ([G] fp32).
     Raises ValueError if a position or block id does not exist.
     """
     B, H, G, D = geom.batch, geom.n_heads, geom.n_kv_heads, geom.head_dim
-    st = geom.storage
+    st, ist = geom.storage, geom.input_storage
     if q is not None:
-        _need(q, st, "q", (B, H, D))
-    _need(k_new, st, "k_new", (B, G, D))
-    _need(v_new, st, "v_new", (B, G, D))
+        _need(q, ist, "q", (B, H, D))
+    _need(k_new, ist, "k_new", (B, G, D))
+    _need(v_new, ist, "v_new", (B, G, D))
     _need(k_cache, st, "k_cache", geom.cache_shape())
-    _need(v_cache, st, "v_cache", geom.cache_shape())
+    _need(v_cache, st, "v_cache", geom.v_cache_shape())
     _need(positions, np.int32, "positions", (B,))
     if geom.block_size:
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    ks, vs = _scales(geom, k_scale, v_scale)
     q_rot = np.zeros((B, H, D), np.float64)
     sh = geom._c()
-    rc = _load().kvo_rope_append(ctypes.byref(sh), _ptr(q), _ptr(k_new), _ptr(v_new),
-                                 _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(positions), _ptr(block_table), float(base),
-                                 _STYLE_CODE[style])
+    if geom.dtype == "i8":
+        rc = _load().kvo_rope_append_i8(ctypes.byref(sh), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(ks),
+                                        _ptr(vs), _ptr(positions), _ptr(block_table),
+                                        float(base), _STYLE_CODE[style])
+    else:
+        rc = _load().kvo_rope_append(ctypes.byref(sh), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(positions), _ptr(block_table), float(base),
+                                     _STYLE_CODE[style])
     if rc != 0:
         raise ValueError("position or block id out of range")
     return q_rot
 
 
 def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=None,
-                scale=None, want_probs=False, n_threads=None):
+                scale=None, want_probs=False, n_threads=None, k_scale=None, v_scale=None):
     """fp64 attention of every (b, h) query over its first seq_lens[b] tokens.
 
     Returns (out [B,H,D], lse [B,H]) and, with want_probs, the weights
-    [B, H, max_seq_len] (zero past seq_lens[b]).
+    [B, H, max_seq_len] (zero past seq_lens[b]).  INT8 caches take their
+    per-head scales.
     """
     B, H, D = geom.batch, geom.n_heads, geom.head_dim
     _need(q_rot, np.float64, "q_rot", (B, H, D))
     _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
-    _need(v_cache, geom.storage, "v_cache", geom.cache_shape())
+    _need(v_cache, geom.storage, "v_cache", geom.v_cache_shape())
+    ks, vs = _scales(geom, k_scale, v_scale)
     _need(seq_lens, np.int32, "seq_lens", (B,))
     if geom.block_size:
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
@@ -210,21 +274,24 @@ def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=N
     lse = np.zeros((B, H), np.float64)
     probs = np.zeros((B, H, geom.max_seq_len), np.float64) if want_probs else None
     sh = geom._c()
-    rc = _load().kvo_decode_attn(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(seq_lens), _ptr(block_table), float(scale), _ptr(out),
-                                 _ptr(lse), _ptr(probs), n_threads or default_threads())
+    rc = _load().kvo_decode_attn_i8(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(ks), _ptr(vs), _ptr(seq_lens),
+                                    _ptr(block_table), float(scale), _ptr(out), _ptr(lse),
+                                    _ptr(probs), n_threads or default_threads())
     if rc != 0:
         raise ValueError("a referenced cache slot does not exist")
     return (out, lse, probs) if want_probs else (out, lse)
 
 
 def decode_attn_units(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, units,
-                      block_table=None, scale=None, n_threads=None):
+                      block_table=None, scale=None, n_threads=None, k_scale=None,
+                      v_scale=None):
     """As decode_attn, for the listed (b, h) pairs only: returns out [n, D], lse [n]."""
     B, H, D = geom.batch, geom.n_heads, geom.head_dim
     _need(q_rot, np.float64, "q_rot", (B, H, D))
     _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
-    _need(v_cache, geom.storage, "v_cache", geom.cache_shape())
+    _need(v_cache, geom.storage, "v_cache", geom.v_cache_shape())
+    ks, vs = _scales(geom, k_scale, v_scale)
     _need(seq_lens, np.int32, "seq_lens", (B,))
     if geom.block_size:
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
@@ -239,10 +306,11 @@ def decode_attn_units(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, units,
     out = np.zeros((n, D), np.float64)
     lse = np.zeros((n,), np.float64)
     sh = geom._c()
-    rc = _load().kvo_decode_attn_units(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
-                                       _ptr(v_cache), _ptr(seq_lens), _ptr(block_table),
-                                       float(scale), _ptr(ub), _ptr(uh), n, _ptr(out),
-                                       _ptr(lse), n_threads or default_threads())
+    rc = _load().kvo_decode_attn_units_i8(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
+                                          _ptr(v_cache), _ptr(ks), _ptr(vs), _ptr(seq_lens),
+                                          _ptr(block_table), float(scale), _ptr(ub), _ptr(uh),
+                                          n, _ptr(out), _ptr(lse),
+                                          n_threads or default_threads())
     if rc != 0:
         raise ValueError("a referenced cache slot does not exist")
     return out, lse

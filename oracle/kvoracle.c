@@ -35,6 +35,17 @@
  *
  * Storage dtypes: KVO_F64 (used by the pins' exact decode loop), KVO_F32 and
  * KVO_BF16 (raw 16-bit patterns; value = bits << 16 read as an IEEE float).
+ *
+ * KVO_I8: the INT8 cache of [KVGR] §4.3 (K and V held as 8-bit integers,
+ * quantisation parameters calibrated per attention head).  q, k_new and
+ * v_new are then bf16; each cache element is a code n in [-127, 127] whose
+ * value is scale[g] * n, with one fp32 scale per KV head for K and one for
+ * V.  A new element x is stored as the code nearest to x / scale (ties to
+ * even; x is the exact rotated key, or v_new as given).  Layout: K as the
+ * other dtypes ([.., 16, G, D] rows of D codes); V transposed inside each
+ * 16-token group: group r (contiguous: r = b * S_max/16 + pos/16; paged: the
+ * physical block) holds [G][D][16] codes, element (pos, g, d) at
+ * ((r * G + g) * D + d) * 16 + pos % 16.
  */
 #include <math.h>
 #include <pthread.h>
@@ -42,7 +53,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { KVO_F64 = 0, KVO_F32 = 1, KVO_BF16 = 2 };
+enum { KVO_F64 = 0, KVO_F32 = 1, KVO_BF16 = 2, KVO_I8 = 3 };
 enum { KVO_INTERLEAVED = 0, KVO_HALF = 1 };
 
 typedef struct {
@@ -86,6 +97,17 @@ uint16_t kvo_bf16_bits(double x) {
   return (uint16_t)(w >> 16);
 }
 
+/* INT8 code of x under scale s ([KVGR] §4.3): the integer in [-127, 127]
+ * nearest to x / s, ties to even, the quotient taken in fp64.  A NaN quotient
+ * gives 0; quotients beyond the range saturate at +-127. */
+int kvo_quantize_i8(double x, double s) {
+  double q = x / s;
+  if (isnan(q)) return 0;
+  if (q >= 127.0) return 127;
+  if (q <= -127.0) return -127;
+  return (int)nearbyint(q);   /* default rounding mode: nearest, ties to even */
+}
+
 static double load_elem(const void* p, int dtype, int64_t i) {
   switch (dtype) {
     case KVO_F64: return ((const double*)p)[i];
@@ -101,6 +123,9 @@ static void store_elem(void* p, int dtype, int64_t i, double v) {
     default:      ((uint16_t*)p)[i] = kvo_bf16_bits(v); break;
   }
 }
+
+/* dtype of q, k_new and v_new: bf16 in front of an INT8 cache */
+static int input_dtype(int dtype) { return dtype == KVO_I8 ? KVO_BF16 : dtype; }
 
 /* Copy one stored element without any arithmetic (the append of v). */
 static void copy_elem(void* dst, int64_t di, const void* src, int64_t si, int dtype) {
@@ -149,17 +174,34 @@ static int64_t cache_row(const kvo_shape* sh, const int32_t* table, int b, int64
   return ((int64_t)phys * sh->block_size + off) * sh->n_kv_heads + g;
 }
 
+/* INT8 caches: index of V element (pos, g, d) in the group-transposed
+ * layout; -1 when the slot does not exist.  `row` is cache_row's result for
+ * the same slot (it carries the block-table lookup). */
+static int64_t vt_index(const kvo_shape* sh, int b, int64_t pos, int g, int d, int64_t row) {
+  if (row < 0) return -1;
+  int64_t group;
+  if (sh->block_size == 0) {
+    group = (int64_t)b * (sh->max_seq_len / 16) + pos / 16;
+  } else {
+    group = row / ((int64_t)sh->block_size * sh->n_kv_heads);   /* physical block */
+  }
+  return ((group * sh->n_kv_heads + g) * sh->head_dim + d) * 16 + pos % 16;
+}
+
 /* ----------------------------------------------------- rope + cache append */
 
-/* q: [B,H,D], k_new/v_new: [B,G,D] in sh->dtype (q may be NULL).
+/* q: [B,H,D], k_new/v_new: [B,G,D] in the input dtype (q may be NULL).
  * q_rot: [B,H,D] fp64 out.  Caches are modified in place at slot positions[b].
+ * k_scale/v_scale: [G] per-head scales of an INT8 cache (NULL otherwise).
  * Returns 0, or -1 when a position or block id is out of range (that
  * sequence's append is then skipped). */
-int kvo_rope_append(const kvo_shape* sh, const void* q, const void* k_new,
-                    const void* v_new, double* q_rot, void* k_cache,
-                    void* v_cache, const int32_t* positions,
-                    const int32_t* block_table, double base, int style) {
+static int rope_append_impl(const kvo_shape* sh, const void* q, const void* k_new,
+                            const void* v_new, double* q_rot, void* k_cache,
+                            void* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* positions, const int32_t* block_table,
+                            double base, int style) {
   const int B = sh->batch, H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
+  const int in_dt = input_dtype(sh->dtype);
   int rc = 0;
   double* x = (double*)malloc(sizeof(double) * D);
   double* y = (double*)malloc(sizeof(double) * D);
@@ -168,7 +210,7 @@ int kvo_rope_append(const kvo_shape* sh, const void* q, const void* k_new,
     if (q != NULL) {
       for (int h = 0; h < H; ++h) {
         int64_t base_i = ((int64_t)b * H + h) * D;
-        for (int d = 0; d < D; ++d) x[d] = load_elem(q, sh->dtype, base_i + d);
+        for (int d = 0; d < D; ++d) x[d] = load_elem(q, in_dt, base_i + d);
         kvo_rope_rotate(x, y, D, pos, base, style);
         for (int d = 0; d < D; ++d) q_rot[base_i + d] = y[d];
       }
@@ -177,17 +219,44 @@ int kvo_rope_append(const kvo_shape* sh, const void* q, const void* k_new,
       int64_t row = cache_row(sh, block_table, b, positions[b], g);
       if (row < 0) { rc = -1; continue; }
       int64_t src = ((int64_t)b * G + g) * D;
-      for (int d = 0; d < D; ++d) x[d] = load_elem(k_new, sh->dtype, src + d);
+      for (int d = 0; d < D; ++d) x[d] = load_elem(k_new, in_dt, src + d);
       kvo_rope_rotate(x, y, D, pos, base, style);
       for (int d = 0; d < D; ++d) {
-        store_elem(k_cache, sh->dtype, row * D + d, y[d]);
-        copy_elem(v_cache, row * D + d, v_new, src + d, sh->dtype);
+        if (sh->dtype == KVO_I8) {
+          /* codes of the exact rotated key and of v_new ([KVGR] §4.3) */
+          ((int8_t*)k_cache)[row * D + d] = (int8_t)kvo_quantize_i8(y[d], k_scale[g]);
+          ((int8_t*)v_cache)[vt_index(sh, b, positions[b], g, d, row)] =
+              (int8_t)kvo_quantize_i8(load_elem(v_new, in_dt, src + d), v_scale[g]);
+        } else {
+          store_elem(k_cache, sh->dtype, row * D + d, y[d]);
+          copy_elem(v_cache, row * D + d, v_new, src + d, sh->dtype);
+        }
       }
     }
   }
   free(x);
   free(y);
   return rc;
+}
+
+int kvo_rope_append(const kvo_shape* sh, const void* q, const void* k_new,
+                    const void* v_new, double* q_rot, void* k_cache,
+                    void* v_cache, const int32_t* positions,
+                    const int32_t* block_table, double base, int style) {
+  if (sh->dtype == KVO_I8) return -2;   /* needs the scales */
+  return rope_append_impl(sh, q, k_new, v_new, q_rot, k_cache, v_cache, NULL, NULL,
+                          positions, block_table, base, style);
+}
+
+/* The append into an INT8 cache (sh->dtype == KVO_I8). */
+int kvo_rope_append_i8(const kvo_shape* sh, const void* q, const void* k_new,
+                       const void* v_new, double* q_rot, int8_t* k_cache,
+                       int8_t* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* positions, const int32_t* block_table,
+                       double base, int style) {
+  if (sh->dtype != KVO_I8) return -2;
+  return rope_append_impl(sh, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+                          positions, block_table, base, style);
 }
 
 /* ------------------------------------------------------------- attention */
@@ -200,6 +269,8 @@ typedef struct {
   const int32_t* seq_lens;
   const int32_t* table;
   double scale;
+  const float* k_scale;    /* INT8 caches: [G] per-head scales */
+  const float* v_scale;
   const int32_t* unit_b;   /* NULL: unit u is (u / H, u % H) */
   const int32_t* unit_h;
   int64_t n_units;
@@ -210,6 +281,23 @@ typedef struct {
   pthread_mutex_t mu;
   int bad;                 /* set when a referenced slot does not exist */
 } attn_job;
+
+/* Value of cached K / V element d of slot (b, j, g) whose row is `row`.
+ * INT8 caches dequantise exactly: scale[g] * code ([KVGR] §4.3). */
+static double key_at(const attn_job* job, int64_t row, int g, int d) {
+  const kvo_shape* sh = job->sh;
+  if (sh->dtype == KVO_I8)
+    return (double)job->k_scale[g] * (double)((const int8_t*)job->k_cache)[row * sh->head_dim + d];
+  return load_elem(job->k_cache, sh->dtype, row * sh->head_dim + d);
+}
+
+static double value_at(const attn_job* job, int b, int64_t j, int64_t row, int g, int d) {
+  const kvo_shape* sh = job->sh;
+  if (sh->dtype == KVO_I8)
+    return (double)job->v_scale[g] *
+           (double)((const int8_t*)job->v_cache)[vt_index(sh, b, j, g, d, row)];
+  return load_elem(job->v_cache, sh->dtype, row * sh->head_dim + d);
+}
 
 static void attn_unit(attn_job* job, int64_t u, double* s) {
   const kvo_shape* sh = job->sh;
@@ -233,7 +321,7 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
     int64_t row = cache_row(sh, job->table, b, j, g);
     if (row < 0) { job->bad = 1; s[j] = -INFINITY; continue; }
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += q[d] * load_elem(job->k_cache, sh->dtype, row * D + d);
+    for (int d = 0; d < D; ++d) dot += q[d] * key_at(job, row, g, d);
     s[j] = job->scale * dot;
     if (s[j] > m) m = s[j];
   }
@@ -249,7 +337,7 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
     if (job->probs) job->probs[u * sh->max_seq_len + j] = p;
     int64_t row = cache_row(sh, job->table, b, j, g);
     if (row < 0) continue;
-    for (int d = 0; d < D; ++d) o[d] += p * load_elem(job->v_cache, sh->dtype, row * D + d);
+    for (int d = 0; d < D; ++d) o[d] += p * value_at(job, b, j, row, g, d);
   }
   if (job->lse) job->lse[u] = m + log(l);
 }
@@ -286,32 +374,57 @@ static int run_attn(attn_job* job, int n_threads) {
 }
 
 /* Every (b, h): out [B,H,D], lse [B,H] (may be NULL), probs [B,H,max_seq_len]
- * (may be NULL).  seq_lens[b] tokens are attended. */
-int kvo_decode_attn(const kvo_shape* sh, const double* q_rot, const void* k_cache,
-                    const void* v_cache, const int32_t* seq_lens,
-                    const int32_t* block_table, double scale, double* out,
-                    double* lse, double* probs, int n_threads) {
+ * (may be NULL).  seq_lens[b] tokens are attended.  k_scale/v_scale: the
+ * per-head scales of an INT8 cache (NULL for the other dtypes). */
+int kvo_decode_attn_i8(const kvo_shape* sh, const double* q_rot, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* seq_lens, const int32_t* block_table, double scale,
+                       double* out, double* lse, double* probs, int n_threads) {
+  if ((sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
   attn_job job;
   memset(&job, 0, sizeof job);
   job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
+  job.k_scale = k_scale; job.v_scale = v_scale;
   job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
   job.n_units = (int64_t)sh->batch * sh->n_heads;
   job.out = out; job.lse = lse; job.probs = probs;
   return run_attn(&job, n_threads);
 }
 
+int kvo_decode_attn(const kvo_shape* sh, const double* q_rot, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens,
+                    const int32_t* block_table, double scale, double* out,
+                    double* lse, double* probs, int n_threads) {
+  return kvo_decode_attn_i8(sh, q_rot, k_cache, v_cache, NULL, NULL, seq_lens, block_table,
+                            scale, out, lse, probs, n_threads);
+}
+
 /* Only the listed (unit_b[u], unit_h[u]) pairs: out [n, D], lse [n]. */
+int kvo_decode_attn_units_i8(const kvo_shape* sh, const double* q_rot,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             double scale, const int32_t* unit_b,
+                             const int32_t* unit_h, int64_t n_units, double* out,
+                             double* lse, int n_threads) {
+  if ((sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
+  attn_job job;
+  memset(&job, 0, sizeof job);
+  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
+  job.k_scale = k_scale; job.v_scale = v_scale;
+  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
+  job.unit_b = unit_b; job.unit_h = unit_h; job.n_units = n_units;
+  job.out = out; job.lse = lse;
+  return run_attn(&job, n_threads);
+}
+
 int kvo_decode_attn_units(const kvo_shape* sh, const double* q_rot,
                           const void* k_cache, const void* v_cache,
                           const int32_t* seq_lens, const int32_t* block_table,
                           double scale, const int32_t* unit_b,
                           const int32_t* unit_h, int64_t n_units, double* out,
                           double* lse, int n_threads) {
-  attn_job job;
-  memset(&job, 0, sizeof job);
-  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
-  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
-  job.unit_b = unit_b; job.unit_h = unit_h; job.n_units = n_units;
-  job.out = out; job.lse = lse;
-  return run_attn(&job, n_threads);
+  return kvo_decode_attn_units_i8(sh, q_rot, k_cache, v_cache, NULL, NULL, seq_lens,
+                                  block_table, scale, unit_b, unit_h, n_units, out, lse,
+                                  n_threads);
 }
