@@ -55,7 +55,12 @@ typedef enum {
 
 typedef enum {
   KVD_FP32 = 0,          /* IEEE binary32 */
-  KVD_BF16 = 1           /* bfloat16 (upper half of a binary32) */
+  KVD_BF16 = 1,          /* bfloat16 (upper half of a binary32) */
+  /* INT8 cache ([KVGR] §4.3): K and V held as signed 8-bit codes with one
+   * fp32 scale per KV head for each; q, k_new and v_new are bfloat16.  Only
+   * the *_int8 calls below accept it.  Layout: K as for the other dtypes;
+   * V transposed inside every 16-token group (see rope_append_kv_int8). */
+  KVD_INT8 = 2
 } kvd_dtype;
 
 typedef enum {
@@ -73,15 +78,16 @@ typedef enum {
  *   n_kv_heads  G >= 1 KV heads; H % G == 0 ([OPT] §六 asserts it); query head
  *               h reads KV head h / (H / G) ([KVGR] §2.2, repeat_interleave)
  *   head_dim    D in {64, 128}
- *   kv_dtype    kvd_dtype of q, k_new, v_new, k_cache and v_cache
+ *   kv_dtype    kvd_dtype of q, k_new, v_new, k_cache and v_cache (KVD_INT8:
+ *               caches only, the rest bfloat16)
  *   block_size  0  = contiguous cache  [B, max_seq_len, G, D]
  *                    ([OPT] §四 KVCache: (batch, seq, heads, head_dim));
  *               16 = paged pool [num_blocks, 16, G, D] with an int32 block
  *                    table [B, max_blocks_per_seq]: token p of sequence b is
  *                    row p % 16 of block table[b][p / 16] ([OPT] §四
  *                    PagedKVCache; [KVGR] §4.1, 16-token blocks)
- *   max_seq_len contiguous: S_max, the row capacity per sequence;
- *               paged: must equal max_blocks_per_seq * 16
+ *   max_seq_len contiguous: S_max, the row capacity per sequence (a multiple
+ *               of 16 for KVD_INT8); paged: must equal max_blocks_per_seq * 16
  *   num_blocks  paged: pool size (>= 1); contiguous: ignored
  *   max_blocks_per_seq  paged: table row stride (>= 1); contiguous: ignored
  */
@@ -171,6 +177,55 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
                            float scale, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * rope_append_kv_int8 -- rope_append_kv for an INT8 cache
+ * (shape->kv_dtype == KVD_INT8).
+ *
+ * [KVGR] §4.3 stores the cached K and V as 8-bit integers instead of
+ * 16-bit floats, with quantisation parameters calibrated per attention
+ * head.  Here: a code n in [-127, 127] stands for scale[g] * n, with
+ * k_scale[g] for K and v_scale[g] for V (calibrated by the caller).  The
+ * rotation is as in rope_append_kv; the stored K code is the integer nearest
+ * to (exact rotated key) / k_scale[g] and the V code the one nearest to
+ * v_new / v_scale[g], the quotient taken in fp64, ties to even, saturating at
+ * +-127 (a NaN quotient stores 0).
+ *
+ *   q, k_new, v_new   bfloat16, shapes as in rope_append_kv
+ *   q_rot      [B, H, D] fp32 output (ignored when q == NULL)
+ *   k_cache    int8: contiguous [B, max_seq_len, G, D]; paged
+ *              [num_blocks, 16, G, D] (row of token p: as in rope_append_kv)
+ *   v_cache    int8, transposed inside each 16-token group: contiguous
+ *              [B, max_seq_len / 16, G, D, 16], paged [num_blocks, G, D, 16];
+ *              element (token p, head g, dim d) is [.., p / 16 or the block,
+ *              g, d, p % 16]
+ *   k_scale, v_scale  [G] fp32 device arrays, finite and > 0
+ *   positions, block_table, rope_base, rope_style   as in rope_append_kv
+ * Errors: as rope_append_kv; EUNSUPPORTED when kv_dtype is not KVD_INT8 (and
+ * rope_append_kv itself rejects KVD_INT8); EINVAL for null scales.
+ */
+kvd_status rope_append_kv_int8(const kvd_shape* shape, const void* q, const void* k_new,
+                               const void* v_new, float* q_rot, int8_t* k_cache,
+                               int8_t* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* positions, const int32_t* block_table,
+                               double rope_base, int32_t rope_style, void* stream);
+
+/*
+ * gqa_decode_attn_int8 -- gqa_decode_attn over an INT8 cache
+ * (shape->kv_dtype == KVD_INT8): the same result with K[.., g, :] =
+ * k_scale[g] * codes and V[.., g, :] = v_scale[g] * codes, layouts as in
+ * rope_append_kv_int8.  Up to 32 query heads per KV head.  Arguments,
+ * workspace and errors as gqa_decode_attn (workspace size from
+ * gqa_decode_workspace_size with the same shape); EUNSUPPORTED for more
+ * than 32 query heads per KV head or a non-INT8 shape (gqa_decode_attn
+ * itself rejects KVD_INT8); EINVAL for null scales.
+ */
+kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
+                                const int8_t* k_cache, const int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* seq_lens, const int32_t* block_table,
+                                int32_t max_seq_len_host, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace gqa_decode_attn needs for this shape and length bound
  * on the current device under the current tuning (0 when no split merge is
  * needed).  Returns 0 for an invalid shape as well; gqa_decode_attn then
@@ -185,11 +240,12 @@ const char* kvd_status_string(int32_t status);
  *
  * kvd_get_plan reports how gqa_decode_attn would run: plan[0] = tokens per
  * split (a multiple of 16), plan[1] = number of splits, plan[2] = kernel
- * (0 = VALU dot products, 1 = MFMA), plan[3] = workgroups launched by the
- * split kernel.  `plan` is a host array of 4 int32.
+ * (0 = VALU dot products, 1 = MFMA, 2 = INT8 MFMA), plan[3] = workgroups
+ * launched by the split kernel.  `plan` is a host array of 4 int32.
  *
- * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU) or
- * 1 (MFMA, bf16 only, up to 32 query heads per KV head); split_tokens = 0
+ * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU),
+ * 1 (MFMA, bf16 only, up to 32 query heads per KV head) or 2 (INT8 caches,
+ * their only kernel); split_tokens = 0
  * (automatic) or a positive multiple of 16.  EUNSUPPORTED if the override
  * cannot run; the override applies to later calls in the whole process.
  */

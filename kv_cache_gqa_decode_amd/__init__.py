@@ -4,11 +4,13 @@ flash-decoding, hand-written HIP for gfx950 behind a C ABI (libkvdecode.so).
 The compute entry points are imported lazily from ``_binding`` so that the
 workload generators and the sizing helpers import without the native library.
 """
-__all__ = ["rope_append_kv", "gqa_decode_attn", "workspace_size", "library_path"]
+__all__ = ["rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8", "gqa_decode_attn_int8",
+           "workspace_size", "library_path"]
 
 
 def __getattr__(name):
-    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer", "read_probe"):
+    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer", "read_probe",
+                                   "v_cache_shape_int8"):
         from . import _binding
         return getattr(_binding, name)
     raise AttributeError(name)

@@ -22,9 +22,10 @@ import torch
 LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
 
-KVD_FP32, KVD_BF16 = 0, 1
+KVD_FP32, KVD_BF16, KVD_INT8 = 0, 1, 2
 _STYLES = {"interleaved": 0, "half": 1}
-_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1}
+_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1, "int8": 2}
+_KERNEL_NAMES = {0: "valu", 1: "mfma", 2: "int8"}
 
 
 class KvdError(ValueError):
@@ -41,7 +42,8 @@ class Shape(ctypes.Structure):
         "max_seq_len", "num_blocks", "max_blocks_per_seq")]
 
 
-EXPORTED = ("rope_append_kv", "gqa_decode_attn", "gqa_decode_workspace_size",
+EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
+            "gqa_decode_attn_int8", "gqa_decode_workspace_size",
             "kvd_status_string", "kvd_get_plan", "kvd_set_tuning", "kvd_set_tuning_ex",
             "kvd_timer_begin",
             "kvd_timer_end", "kvd_read_probe")
@@ -72,6 +74,12 @@ def load_library():
         lib.gqa_decode_attn.restype = I32
         lib.gqa_decode_attn.argtypes = [SP, P, P, P, P, P, I32, ctypes.c_float, P, P, P,
                                         ctypes.c_size_t, P]
+        lib.rope_append_kv_int8.restype = I32
+        lib.rope_append_kv_int8.argtypes = [SP, P, P, P, P, P, P, P, P, P, P,
+                                            ctypes.c_double, I32, P]
+        lib.gqa_decode_attn_int8.restype = I32
+        lib.gqa_decode_attn_int8.argtypes = [SP, P, P, P, P, P, P, P, I32, ctypes.c_float, P,
+                                             P, P, ctypes.c_size_t, P]
         lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size.argtypes = [SP, I32]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -111,7 +119,9 @@ def _dtype_code(dt: torch.dtype) -> int:
         return KVD_FP32
     if dt == torch.bfloat16:
         return KVD_BF16
-    raise ValueError(f"unsupported KV dtype {dt}: float32 or bfloat16")
+    if dt == torch.int8:
+        return KVD_INT8
+    raise ValueError(f"unsupported KV dtype {dt}: float32, bfloat16 or int8")
 
 
 def _need(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None):
@@ -129,8 +139,9 @@ def _need(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=No
 
 def make_shape(batch: int, n_heads: int, k_cache: torch.Tensor,
                block_table: Optional[torch.Tensor]) -> Shape:
-    """kvd_shape from the cache tensor: contiguous [B, S_max, G, D] or paged
-    pool [num_blocks, 16, G, D] with table [B, max_blocks_per_seq]."""
+    """kvd_shape from the K cache tensor: contiguous [B, S_max, G, D] or paged
+    pool [num_blocks, 16, G, D] with table [B, max_blocks_per_seq] (an int8
+    K cache makes an INT8 shape)."""
     if k_cache.dim() != 4:
         raise ValueError("cache must be 4-D")
     G, D = int(k_cache.shape[2]), int(k_cache.shape[3])
@@ -249,9 +260,103 @@ def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     return out, lse
 
 
+def v_cache_shape_int8(k_cache: torch.Tensor, paged: bool) -> Tuple[int, ...]:
+    """Shape of the INT8 V cache that goes with an int8 K cache: V transposed
+    inside every 16-token group."""
+    if paged:
+        nb, _, G, D = (int(x) for x in k_cache.shape)
+        return (nb, G, D, 16)
+    B, S, G, D = (int(x) for x in k_cache.shape)
+    return (B, S // 16, G, D, 16)
+
+
+def _check_scales(k_scale, v_scale, G, dev):
+    _need(k_scale, "k_scale", dev, torch.float32, (G,))
+    _need(v_scale, "v_scale", dev, torch.float32, (G,))
+
+
+def rope_append_kv_int8(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                        v_scale: torch.Tensor, positions: torch.Tensor,
+                        block_table: Optional[torch.Tensor] = None, base: float = 10000.0,
+                        style: str = "interleaved",
+                        q_rot: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """rope_append_kv into an INT8 cache: bf16 q / k_new / v_new, int8 K cache
+    [B, S_max, G, D] (or pool [NB, 16, G, D]) and V cache
+    [B, S_max/16, G, D, 16] (or [NB, G, D, 16]), per-KV-head fp32 scales."""
+    lib = load_library()
+    dev = k_cache.device
+    B, G, D = int(k_new.shape[0]), int(k_new.shape[1]), int(k_new.shape[2])
+    H = int(q.shape[1]) if q is not None else G
+    shape = make_shape(B, H, k_cache, block_table)
+    if q is not None:
+        _need(q, "q", dev, torch.bfloat16, (B, H, D))
+    _need(k_new, "k_new", dev, torch.bfloat16, (B, G, D))
+    _need(v_new, "v_new", dev, torch.bfloat16, (B, G, D))
+    _need(k_cache, "k_cache", dev, torch.int8)
+    _need(v_cache, "v_cache", dev, torch.int8, v_cache_shape_int8(k_cache, block_table is not None))
+    _check_scales(k_scale, v_scale, G, dev)
+    _need(positions, "positions", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if style not in _STYLES:
+        raise ValueError(f"style must be one of {sorted(_STYLES)}")
+    if q is not None and q_rot is None:
+        q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _check(lib.rope_append_kv_int8(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(q_rot) if q is not None else None, _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(positions),
+                                   _ptr(block_table), float(base), _STYLES[style], _stream(dev)))
+    return q_rot if q is not None else None
+
+
+def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         k_scale: torch.Tensor, v_scale: torch.Tensor, seq_lens: torch.Tensor,
+                         block_table: Optional[torch.Tensor] = None,
+                         scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gqa_decode_attn over an INT8 cache (layouts as rope_append_kv_int8)."""
+    lib = load_library()
+    dev = k_cache.device
+    B, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _need(k_cache, "k_cache", dev, torch.int8)
+    _need(v_cache, "v_cache", dev, torch.int8, v_cache_shape_int8(k_cache, block_table is not None))
+    _check_scales(k_scale, v_scale, shape.n_kv_heads, dev)
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if int(k_cache.shape[3]) != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (B, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dev, torch.float32, (B, H))
+    nbytes = int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_attn_int8(ctypes.byref(shape), _ptr(q_rot), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+                                    _ptr(block_table), msl, float(scale), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), wbytes, _stream(dev)))
+    return out, lse
+
+
 def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_tokens: int = 0,
                tail_span_tokens: int = -1, dispatch_order: Optional[int] = None) -> None:
-    """Process-wide override of the kernel ("valu", "mfma" or None
+    """Process-wide override of the kernel ("valu", "mfma", "int8" or None
     for automatic), the tokens per split (0 = automatic), the shorter splits
     covering the last ``tail_span_tokens`` positions (0 / -1 = automatic) and
     the MFMA dispatch order (0, 1, 2 or None for automatic)."""
@@ -268,7 +373,7 @@ def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
     arr = (ctypes.c_int32 * 4)()
     _check(load_library().kvd_get_plan(ctypes.byref(shape), msl, arr))
     return {"split_tokens": arr[0], "n_splits": arr[1],
-            "kernel": {0: "valu", 1: "mfma"}[arr[2]], "workgroups": arr[3]}
+            "kernel": _KERNEL_NAMES[arr[2]], "workgroups": arr[3]}
 
 
 def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8, chunked: bool = False,

@@ -20,7 +20,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
 
-std::atomic<int> g_kernel_override{-1};     // -1 auto, 0 VALU, 1 MFMA
+std::atomic<int> g_kernel_override{-1};     // -1 auto, 0 VALU, 1 MFMA, 2 INT8 MFMA
 std::atomic<int> g_split_override{0};       // 0 auto
 std::atomic<int> g_tail_split_override{0};  // tokens per split near the end: 0 auto
 std::atomic<int> g_tail_span_override{-1};  // tokens covered by those splits: -1 auto
@@ -58,9 +58,12 @@ kvd_status check_shape(const kvd_shape* s) {
   if (s->n_heads < 1 || s->n_kv_heads < 1 || s->n_heads > 4096) return KVD_EINVAL;
   if (s->n_heads % s->n_kv_heads != 0) return KVD_EINVAL;
   if (s->head_dim != 64 && s->head_dim != 128) return KVD_EUNSUPPORTED;
-  if (s->kv_dtype != KVD_FP32 && s->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+  if (s->kv_dtype != KVD_FP32 && s->kv_dtype != KVD_BF16 && s->kv_dtype != KVD_INT8)
+    return KVD_EUNSUPPORTED;
   if (s->block_size != 0 && s->block_size != 16) return KVD_EUNSUPPORTED;
   if (s->max_seq_len < 1) return KVD_EINVAL;
+  // INT8 V is grouped by 16 tokens: a contiguous capacity of whole groups
+  if (s->kv_dtype == KVD_INT8 && s->max_seq_len % 16 != 0) return KVD_EUNSUPPORTED;
   if (s->block_size == 16) {
     if (s->num_blocks < 1 || s->max_blocks_per_seq < 1) return KVD_EINVAL;
     if (static_cast<int64_t>(s->max_blocks_per_seq) * 16 != s->max_seq_len) return KVD_EINVAL;
@@ -73,7 +76,7 @@ struct Plan {
   int chunk2 = 0;       // tokens per split after those
   int n_big = 0;
   int n_splits = 0;
-  int kernel = 0;       // 0 VALU, 1 MFMA
+  int kernel = 0;       // 0 VALU, 1 MFMA, 2 INT8 MFMA
   int grid_order = 0;   // MFMA dispatch order (DecodeParams::grid_order)
   int head_groups = 1;  // VALU: query-head groups per KV head
   int rb = 1;           // VALU: heads per pass
@@ -101,21 +104,30 @@ void set_splits(Plan* pl, int chunk, int max_len, bool tail = true) {
 
 kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl) {
   const int R = s->n_heads / s->n_kv_heads;
-  // matrix cores for bf16 caches with up to 32 query heads per KV head
-  const bool mfma_ok = s->kv_dtype == KVD_BF16 && R <= 32;
   int kernel = g_kernel_override.load();
-  if (kernel < 0) kernel = mfma_ok ? 1 : 0;
-  if (kernel == 1 && !mfma_ok) return KVD_EUNSUPPORTED;
+  if (s->kv_dtype == KVD_INT8) {
+    // INT8 caches: the INT8 matrix-core kernel, up to 32 query heads per KV head
+    if (R > 32) return KVD_EUNSUPPORTED;
+    if (kernel < 0) kernel = 2;
+    if (kernel != 2) return KVD_EUNSUPPORTED;
+  } else {
+    // matrix cores for bf16 caches with up to 32 query heads per KV head
+    const bool mfma_ok = s->kv_dtype == KVD_BF16 && R <= 32;
+    if (kernel < 0) kernel = mfma_ok ? 1 : 0;
+    if ((kernel == 1 && !mfma_ok) || kernel == 2) return KVD_EUNSUPPORTED;
+  }
   pl->kernel = kernel;
-  if (kernel == 1) {
+  if (kernel >= 1) {
     pl->rb = R;
     pl->head_groups = 1;
   } else {
     pl->rb = valu_heads_per_pass(R);
     pl->head_groups = (R + pl->rb - 1) / pl->rb;
   }
-  // a workgroup advances kWaves tiles of kMfmaTileTokens tokens (MFMA) per step
-  const int granule = kernel == 1 ? kMfmaWaves * kMfmaTileTokens : 64;
+  // a workgroup advances kWaves tiles of kMfmaTileTokens (MFMA) or
+  // kI8TileTokens (INT8) tokens per step
+  const int granule = kernel == 1 ? kMfmaWaves * kMfmaTileTokens
+                    : kernel == 2 ? kMfmaWaves * kI8TileTokens : 64;
   if (max_len_host <= 0 || s->batch == 0) {
     pl->chunk = 16; pl->n_splits = 0; pl->wgs = 0; pl->workspace = 0;
     return KVD_OK;
@@ -130,12 +142,14 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
     // and at most 1024 tokens per split: the workgroups that share a CU run
     // at different speeds (the older one is served first), and smaller
     // units let the dispatcher even that out at a small cost in merges.
-    // The VALU kernel aims for two rounds of at most 2048 tokens.
+    // The VALU kernel aims for two rounds of at most 2048 tokens.  The INT8
+    // kernel plans like the MFMA one with twice the tokens per split (the
+    // same bytes).
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (R > 16 ? 1 : 2));
     const int64_t rounds = kernel == 0 ? 2 : (R > 16 ? 1 : 4);
-    const int cap = kernel == 0 ? 2048 : 1024;
+    const int cap = kernel == 0 ? 2048 : (kernel == 2 ? 2048 : 1024);
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
     if (chunk > cap) chunk = cap;
@@ -185,7 +199,7 @@ const char* kvd_status_string(int32_t status) {
 
 kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
                              int32_t tail_span_tokens, int32_t dispatch_order) {
-  if (kernel < -1 || kernel > 1) return KVD_EINVAL;
+  if (kernel < -1 || kernel > 2) return KVD_EINVAL;
   if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
   if (tail_split_tokens < 0 || tail_split_tokens % 16 != 0) return KVD_EINVAL;
   if (tail_span_tokens < -1 || dispatch_order < -1 || dispatch_order > 2) return KVD_EINVAL;
@@ -228,10 +242,15 @@ size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_hos
   return pl.workspace;
 }
 
-kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_new,
-                          const void* v_new, float* q_rot, void* k_cache, void* v_cache,
-                          const int32_t* positions, const int32_t* block_table,
-                          double rope_base, int32_t rope_style, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
+                       const void* v_new, float* q_rot, void* k_cache, void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* positions,
+                       const int32_t* block_table, double rope_base, int32_t rope_style,
+                       void* stream) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
@@ -244,7 +263,8 @@ kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_n
   if (shape->batch == 0) return KVD_OK;
   RopeParams p;
   p.q = q; p.k_new = k_new; p.v_new = v_new; p.q_rot = q ? q_rot : nullptr;
-  p.k_cache = k_cache; p.v_cache = v_cache; p.positions = positions; p.table = block_table;
+  p.k_cache = k_cache; p.v_cache = v_cache; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.positions = positions; p.table = block_table;
   p.base = rope_base; p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads;
   p.D = shape->head_dim; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
@@ -253,11 +273,70 @@ kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_n
   return KVD_OK;
 }
 
+kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int32_t max_seq_len_host, float scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+}  // namespace
+
+extern "C" {
+
+kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_new,
+                          const void* v_new, float* q_rot, void* k_cache, void* v_cache,
+                          const int32_t* positions, const int32_t* block_table,
+                          double rope_base, int32_t rope_style, void* stream) {
+  // INT8 caches need their scales: rope_append_kv_int8
+  if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;
+  return append_impl(shape, q, k_new, v_new, q_rot, k_cache, v_cache, nullptr, nullptr,
+                     positions, block_table, rope_base, rope_style, stream);
+}
+
+kvd_status rope_append_kv_int8(const kvd_shape* shape, const void* q, const void* k_new,
+                               const void* v_new, float* q_rot, int8_t* k_cache, int8_t* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* positions, const int32_t* block_table,
+                               double rope_base, int32_t rope_style, void* stream) {
+  if (!shape) return KVD_EINVAL;
+  if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
+  if (!k_scale || !v_scale) return KVD_EINVAL;
+  return append_impl(shape, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+                     positions, block_table, rope_base, rope_style, stream);
+}
+
 kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const void* k_cache,
                            const void* v_cache, const int32_t* seq_lens,
                            const int32_t* block_table, int32_t max_seq_len_host, float scale,
                            float* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream) {
+  if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;
+  return decode_impl(shape, q_rot, k_cache, v_cache, nullptr, nullptr, seq_lens, block_table,
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
+                                const int8_t* k_cache, const int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* seq_lens, const int32_t* block_table,
+                                int32_t max_seq_len_host, float scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape) return KVD_EINVAL;
+  if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
+  if (!k_scale || !v_scale) return KVD_EINVAL;
+  return decode_impl(shape, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int32_t max_seq_len_host, float scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
@@ -280,6 +359,7 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeParams p;
   p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
+  p.k_scale = k_scale; p.v_scale = v_scale;
   p.out = out; p.lse = lse;
   p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
   p.R = p.H / p.G;
@@ -317,12 +397,17 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
   }
   if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
   const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)
+                     : pl.kernel == 2 ? launch_decode_i8(p, paged, s)
                                       : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
   if (e != hipSuccess) return KVD_EHIP;
   if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
   if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 kvd_status kvd_timer_begin(int32_t n_launches) {
   if (n_launches < 1 || n_launches > 4096) return KVD_EINVAL;

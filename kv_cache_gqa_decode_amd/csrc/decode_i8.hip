@@ -1,0 +1,480 @@
+// Split-K decode attention over an INT8 KV cache on the matrix cores
+// (D in {64, 128}, up to 32 query heads per KV head).
+//
+// The cache holds K and V as 8-bit codes n in [-127, 127] with one fp32
+// scale per KV head for each ("Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践"
+// §4.3: INT8 K/V with per-head quantisation parameters), so an element's
+// value is scale[g] * n and the result is softmax(q K^T * scale) V over those
+// values, as for the other dtypes (§2.1, §4.2 of the same page).  Half the
+// bytes of bf16 per token: the same HBM roof streams twice the tokens.
+//
+// Layout: K rows of D codes, token-major as for the other dtypes; V
+// transposed inside every 16-token group, [G][D][16] per group, so one
+// 16-byte load gives a lane sixteen tokens of one dimension -- the operand
+// layout of the P V product, with no transpose on the way.
+//
+// Per wave and 64-token tile (four 16-token groups):
+//   scores  v_mfma_i32_16x16x64_i8 on the codes themselves.  A = K rows
+//           (16 bytes of one token per lane, straight from HBM), B = q as
+//           three int8 limbs: q * (127 / max|q_h|) = a1 + a2/128 + a3/128^2
+//           up to 2^-15, each limb a separate exact int32 product.  The
+//           scores are sum_l S_l * 128^(1-l) * scale * k_scale * max|q_h|/127,
+//           relative accuracy ~2^-22 of the row -- the fp32 q enters exactly
+//           enough while K stays exact.  Rows of the score tile are permuted
+//           so that lane group c ends up holding the sixteen tokens of group
+//           c of the tile: half hb, row 4c + j is token 16c + 4hb + j.
+//   softmax running max / sum per head as in the bf16 kernel (lazy rescale by
+//           2^8 slack); probabilities are taken as 2^6 p so that their
+//           fp16 split stays in the normal range (the factor cancels in the
+//           normalisation; the stored max is lowered by 6 to match).
+//   P V     O^T[d][h] += sum_t V^T[d][t] P^T[t][h] with
+//           v_mfma_f32_16x16x32_f16: A = the V^T row of the lane's token
+//           group turned into fp16 exactly (c XOR 0x80 under the exponent
+//           byte 0x64 is the half 1152 + c, minus 1152), B = P split into
+//           fp16 hi + lo.  The final output is multiplied by v_scale.
+//
+// Pipeline: K rows of tile i+1 are requested as soon as tile i's score MFMAs
+// have read their registers, V rows of tile i+1 as soon as tile i's P V has
+// read them; a wave keeps up to one tile (8 KB of K, 8 KB of V at D = 128)
+// in flight.  Rows past the end of the split are read from the last group
+// that holds a token (always inside the cache) and masked out of the
+// softmax; codes are finite, so a masked token contributes exactly zero.
+#include "mfma_tile.h"
+
+namespace kvd {
+namespace {
+
+using namespace mt;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTT = kI8TileTokens;     // tokens per wave-tile
+constexpr int kLimbs = 3;
+constexpr float kPBias = 6.f;          // probabilities carried as 2^6 p
+constexpr int kBlkRegsI8 = (kMaxChunk / 16 / kMfmaWaves + 63) / 64;
+
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight codes (two words, token order) -> eight exact fp16 values.
+__device__ __forceinline__ f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
+  constexpr uint32_t kExp = 0x64646464u;            // fp16 exponent byte of 1024
+  const f16x2 off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;   // c + 128, unsigned
+  const f16x2 h0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x0, 0x04010400u)) + off;
+  const f16x2 h1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x0, 0x04030402u)) + off;
+  const f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x1, 0x04010400u)) + off;
+  const f16x2 h3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x1, 0x04030402u)) + off;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// fp16 hi + lo of two floats (hi truncated, lo the exact remainder truncated:
+// hi + lo within 2^-21 of x).
+__device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(a - static_cast<float>(h[0]),
+                                            b - static_cast<float>(h[1]));
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 255u) | ((static_cast<uint32_t>(b) & 255u) << 8) |
+         ((static_cast<uint32_t>(c) & 255u) << 16) | (static_cast<uint32_t>(d) << 24);
+}
+
+template <int D>
+constexpr int smem_bytes_i8() {
+  return (kMfmaWaves * 16 * D + 2 * kMfmaWaves * 16) * 4;
+}
+
+// One (sequence b, KV head g, split) unit computed by the whole workgroup.
+template <int D, int NB, bool PAGED>
+__device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, int b, int g,
+                                             int split) {
+  constexpr int KB = D / 64;          // 64-dim blocks of the score contraction
+  constexpr int CB = D / 16;          // 16-dim blocks of the output
+  constexpr int kWaves = kMfmaWaves;
+  static_assert(NB >= 1 && NB <= 2 && (D == 64 || D == 128), "tile shape");
+  const int R = p.R;
+  const int hbase = g * R;
+  int L = scalar_load_i32(p.seq_lens + b);
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int t0 = split_start(p, split);
+  if (t0 >= L) {
+    if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
+      for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+        const int r = idx / D, d = idx - r * D;
+        p.out[(static_cast<int64_t>(b) * p.H + hbase + r) * D + d] = 0.f;
+        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + hbase + r] = kNegInf;
+      }
+    }
+    return;
+  }
+  const int t1 = min(t0 + split_size(p, split), L);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  // bytes between consecutive tokens of a K head, and per 16-token group
+  // (of K rows, and of the V^T block of every head)
+  const int64_t rs = static_cast<int64_t>(p.G) * D;
+  const int64_t gs = rs * 16;
+  const int8_t* kbase = static_cast<const int8_t*>(p.k) + static_cast<int64_t>(g) * D;
+  const int8_t* vbase = static_cast<const int8_t*>(p.v) + static_cast<int64_t>(g) * D * 16;
+  if (!PAGED) {
+    kbase += static_cast<int64_t>(b) * p.max_seq_len * rs;
+    vbase += static_cast<int64_t>(b) * (p.max_seq_len >> 4) * gs;
+  }
+
+  // q rows, requested first: lane (n, grp) of block (nb, kb) holds dims
+  // kb*64 + grp*16 .. +15 of head nb*16 + n
+  float4 qraw[NB][KB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int h = nb * 16 + n;
+    const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + hbase + (h < R ? h : 0)) * D + grp * 16;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qraw[nb][kb][j] = *reinterpret_cast<const float4*>(src + kb * 64 + 4 * j);
+  }
+
+  // paged: the ids of the blocks this wave visits, lane j of register c =
+  // the wave's (64c + j)-th block = split block 16*(i/4) + 4*wave + i%4 with
+  // i = 64c + j (group i%4 of the wave's tile i/4); ids outside the pool
+  // become -1
+  int blkv[PAGED ? kBlkRegsI8 : 1];
+  const int last_grp = (t1 - 1) >> 4;         // last group holding a token of the split
+  if (PAGED) {
+    const int nblk = last_grp - (t0 >> 4) + 1;
+    const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks_per_seq + (t0 >> 4);
+#pragma unroll
+    for (int c = 0; c < kBlkRegsI8; ++c) {
+      const int i = c * 64 + lane;
+      int sb = 16 * (i >> 2) + 4 * wave + (i & 3);
+      sb = sb < nblk ? sb : nblk - 1;
+      const int blk = trow[sb];
+      blkv[c] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+    }
+  }
+
+  // Addresses of tile kt (first token tbase): the K lane reads rows of group
+  // n/4 of the tile, the V lane the V^T block of group grp; groups past the
+  // split's last one are replaced by it (in bounds; their tokens are masked)
+  struct TileAddr { const int8_t* k; const int8_t* v; bool vok; };
+  auto tile_addr = [&](int tbase, int kt) {
+    TileAddr ta;
+    int gk = (tbase >> 4) + (n >> 2), gv = (tbase >> 4) + grp;
+    gk = gk < last_grp ? gk : last_grp;
+    gv = gv < last_grp ? gv : last_grp;
+    int64_t kgo, vgo;
+    if (PAGED) {
+      int src = blkv[0];
+#pragma unroll
+      for (int c = 1; c < kBlkRegsI8; ++c) src = (kt >> 4) == c ? blkv[c] : src;
+      const int ik = __shfl(src, (4 * kt + (n >> 2)) & 63);
+      const int iv = __shfl(src, (4 * kt + grp) & 63);
+      kgo = ik < 0 ? 0 : ik;
+      vgo = iv < 0 ? 0 : iv;
+      ta.vok = iv >= 0;
+    } else {
+      kgo = gk;
+      vgo = gv;
+      ta.vok = true;
+    }
+    ta.k = kbase + kgo * gs + (n & 3) * rs + grp * 16;
+    ta.v = vbase + vgo * gs + n * 16;
+    return ta;
+  };
+  auto issue_k = [&](const int8_t* ka, i32x4 (&k)[4][KB]) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        k[hb][kb] = *reinterpret_cast<const i32x4*>(ka + hb * 4 * rs + kb * 64);
+  };
+  auto issue_v = [&](const int8_t* va, i32x4 (&v)[CB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) v[cb] = *reinterpret_cast<const i32x4*>(va + cb * 256);
+  };
+
+  i32x4 kr[4][KB];
+  i32x4 vr[CB];
+  int base = t0 + wave * kTT;
+  bool vok = true;
+  if (base < t1) {
+    const TileAddr ta = tile_addr(base, 0);
+    issue_k(ta.k, kr);
+    issue_v(ta.v, vr);
+    vok = ta.vok;
+  }
+
+  // q as three int8 limbs per head, and the per-head factors that turn the
+  // limbs' int32 products back into scores (log2 units)
+  i32x4 ql[kLimbs][NB][KB];
+  float mul[kLimbs][NB];
+  const float kscale = p.k_scale[g];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bool real = nb * 16 + n < R;
+    float amax = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = qraw[nb][kb][j];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float c = real && amax > 0.f ? 127.f / amax : 0.f;
+    const float m1 = real ? p.qscale * kscale * (amax / 127.f) : 0.f;
+    mul[0][nb] = m1;
+    mul[1][nb] = m1 * (1.f / 128.f);
+    mul[2][nb] = m1 * (1.f / 16384.f);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      int a[kLimbs][16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = qraw[nb][kb][j];
+        const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float y = xv[e] * c;
+          const float a1 = __builtin_rintf(y);
+          y = (y - a1) * 128.f;
+          const float a2 = __builtin_rintf(y);
+          y = (y - a2) * 128.f;
+          const float a3 = __builtin_rintf(y);
+          a[0][4 * j + e] = static_cast<int>(a1);
+          a[1][4 * j + e] = static_cast<int>(a2);
+          a[2][4 * j + e] = static_cast<int>(a3);
+        }
+      }
+#pragma unroll
+      for (int l = 0; l < kLimbs; ++l)
+        ql[l][nb][kb] = i32x4{static_cast<int>(pack4(a[l][0], a[l][1], a[l][2], a[l][3])),
+                              static_cast<int>(pack4(a[l][4], a[l][5], a[l][6], a[l][7])),
+                              static_cast<int>(pack4(a[l][8], a[l][9], a[l][10], a[l][11])),
+                              static_cast<int>(pack4(a[l][12], a[l][13], a[l][14], a[l][15]))};
+    }
+  }
+
+  f32x4 acc[NB][CB];
+  float m[NB], lsum[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf; lsum[nb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One tile: `kr` holds its K rows, `vr` its V^T rows (possibly still in
+  // flight), `vok` whether the lane's group is a valid block.  `more` (a
+  // constant at each call) says whether there is a next tile, whose loads
+  // then go out into the same registers once these are consumed.
+  auto compute = [&](int kt, int tbase, const bool more) {
+    TileAddr nx{};
+    if (more) nx = tile_addr(tbase + kWaves * kTT, kt + 1);
+    const bool full = tbase + kTT <= t1;
+    const bool masked = !full || (PAGED && !__all(vok));      // wave-uniform
+    // int32 score products of the three limbs, half hb = token rows
+    // 16c + 4hb + j of the tile's groups c
+    i32x4 S[kLimbs][NB][4];
+#pragma unroll
+    for (int l = 0; l < kLimbs; ++l)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          i32x4 c = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) c = mfma_i8(kr[hb][kb], ql[l][nb][kb], c);
+          S[l][nb][hb] = c;
+        }
+    if (more) issue_k(nx.k, kr);
+
+    f16x8 ph[NB][2], pl[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[16];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float s1 = static_cast<float>(S[0][nb][hb][j]);
+          const float s2 = static_cast<float>(S[1][nb][hb][j]);
+          const float s3 = static_cast<float>(S[2][nb][hb][j]);
+          sv[hb * 4 + j] = fmaf(s3, mul[2][nb], fmaf(s2, mul[1][nb], s1 * mul[0][nb]));
+        }
+      if (masked) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = tbase + 16 * grp + 4 * hb + j;
+            if (!(t < t1 && vok)) sv[hb * 4 + j] = kNegInf;
+          }
+      }
+      float mt = sv[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mt = fmaxf(mt, sv[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
+        const float mn = fmaxf(m[nb], mt);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
+        m[nb] = mn;
+      }
+      const float ref = (m[nb] == kNegInf ? 0.f : m[nb]) - kPBias;
+      float pv[16];
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        pv[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+        ps += pv[j];
+      }
+      lsum[nb] += ps;
+      // B operand of k-block kk: tokens 8kk .. 8kk+7 of the lane's group =
+      // halves 2kk (rows j) and 2kk+1
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t h[4], lo[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2)
+          split_f16(pv[8 * kk + 2 * q2], pv[8 * kk + 2 * q2 + 1], h[q2], lo[q2]);
+        ph[nb][kk] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
+        pl[nb][kk] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+      }
+    }
+
+    // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16cb + n, tokens of group grp
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const f16x8 a0 = codes_to_f16(static_cast<uint32_t>(vr[cb][0]), static_cast<uint32_t>(vr[cb][1]));
+      const f16x8 a1 = codes_to_f16(static_cast<uint32_t>(vr[cb][2]), static_cast<uint32_t>(vr[cb][3]));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[nb][cb] = mfma_f16(a0, ph[nb][0], acc[nb][cb]);
+        acc[nb][cb] = mfma_f16(a0, pl[nb][0], acc[nb][cb]);
+        acc[nb][cb] = mfma_f16(a1, ph[nb][1], acc[nb][cb]);
+        acc[nb][cb] = mfma_f16(a1, pl[nb][1], acc[nb][cb]);
+      }
+    }
+    if (more) {
+      issue_v(nx.v, vr);
+      vok = nx.vok;
+    }
+  };
+
+  if (base < t1) {
+    int kt = 0;
+    while (base + kWaves * kTT < t1) {
+      compute(kt, base, true);
+      base += kWaves * kTT;
+      ++kt;
+    }
+    compute(kt, base, false);
+  }
+
+  // per-wave sums: the four lane groups of a head hold partial sums under one max
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    lsum[nb] += __shfl_xor(lsum[nb], 16);
+    lsum[nb] += __shfl_xor(lsum[nb], 32);
+  }
+
+  // merge the waves through LDS, 16 heads at a time; each wave's (max, sum,
+  // O) is stated against max - 6, the scale its probabilities carry
+  float* so = reinterpret_cast<float*>(smem);       // [kWaves][16][D]
+  float* sm_m = so + kWaves * 16 * D;               // [kWaves][16]
+  float* sm_l = sm_m + kWaves * 16;                 // [kWaves][16]
+  const float vscale = p.v_scale[g];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int hb = nb * 16;
+    const int nh = min(16, R - hb);
+    if (nh <= 0) break;
+    __syncthreads();
+    if (n < nh) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) so[(wave * 16 + n) * D + 16 * cb + 4 * grp + j] = acc[nb][cb][j];
+      if (grp == 0) {
+        sm_m[wave * 16 + n] = m[nb] == kNegInf ? kNegInf : m[nb] - kPBias;
+        sm_l[wave * 16 + n] = lsum[nb];
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
+      const int r = idx / D, d = idx - r * D;
+      float M = sm_m[r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
+      const float ref = M == kNegInf ? 0.f : M;
+      float o = 0.f, sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float a = exp2f(sm_m[w * 16 + r] - ref);
+        o += so[(w * 16 + r) * D + d] * a;
+        sum += sm_l[w * 16 + r] * a;
+      }
+      const int h = hbase + hb + r;
+      const float val = sum > 0.f ? o / sum * vscale : 0.f;
+      const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
+      if (p.direct) {
+        p.out[(static_cast<int64_t>(b) * p.H + h) * D + d] = val;
+        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + h] = lse2 * 0.69314718055994531f;
+      } else {
+        const int64_t pr = (static_cast<int64_t>(b) * p.H + h) * p.n_splits + split;
+        p.part_o[pr * D + d] = val;
+        if (d == 0) p.part_lse[pr] = lse2;
+      }
+    }
+  }
+}
+
+template <int D, int NB, bool PAGED>
+__global__ __launch_bounds__(256) void decode_i8_kernel(DecodeParams p) {
+  __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
+  const Unit u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  run_split_i8<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
+}
+
+template <int D, int NB>
+hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
+  const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
+                  : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
+                                      : dim3(p.G, p.n_splits, p.B);
+  if (paged) decode_i8_kernel<D, NB, true><<<grid, 256, 0, s>>>(p);
+  else decode_i8_kernel<D, NB, false><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
+  return p.R <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t s) {
+  if (p.chunk > kMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
+      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.R > 32 ||
+      !p.k_scale || !p.v_scale || (!paged && p.max_seq_len % 16 != 0))
+    return hipErrorInvalidValue;
+  return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);
+}
+
+}  // namespace kvd

@@ -14,6 +14,8 @@ struct DecodeParams {
   const float* q_rot;       // [B, H, D] fp32
   const void* k;            // cache or pool
   const void* v;
+  const float* k_scale;     // INT8 caches: [G] per-head scales, else null
+  const float* v_scale;
   const int32_t* seq_lens;  // [B]
   const int32_t* table;     // [B, max_blocks_per_seq] or null
   float* out;               // [B, H, D]
@@ -45,6 +47,8 @@ struct RopeParams {
   float* q_rot;             // [B, H, D]
   void* k_cache;
   void* v_cache;
+  const float* k_scale;     // INT8 caches: [G] per-head scales, else null
+  const float* v_scale;
   const int32_t* positions;
   const int32_t* table;
   double base;
@@ -61,12 +65,14 @@ hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
                               int rb, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
+hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).
 int valu_heads_per_pass(int n_rep);
 // Workgroups and tokens per workgroup-iteration of the MFMA kernel.
 constexpr int kMfmaWaves = 4;
 constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
+constexpr int kI8TileTokens = 64;     // INT8 kernel: tokens per wave per iteration
 constexpr int kMaxChunk = 8192;       // tokens per split, upper bound
 constexpr int kMfmaMaxChunk = kMaxChunk;
 

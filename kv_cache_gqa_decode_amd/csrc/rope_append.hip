@@ -12,6 +12,15 @@
 // copies one element of v.  The rotation runs in fp64 and the stored key is
 // rounded once to the cache dtype, so the appended row is bit-identical to
 // the exact rotation rounded to nearest-even.
+//
+// INT8 caches (same page, §4.3: 8-bit K and V with per-head quantisation
+// parameters): the inputs are bf16 and each stored element is the code in
+// [-127, 127] nearest to x / scale[g], the quotient taken in fp64 from the
+// exact rotated key (or v_new), ties to even, saturating.  V codes go to the
+// group-transposed layout: element (pos, g, d) of group r at
+// ((r * G + g) * D + d) * 16 + pos % 16.
+#include <type_traits>
+
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -49,12 +58,26 @@ __device__ uint16_t double_to_bf16_rne(double x) {
   return static_cast<uint16_t>(sign | static_cast<uint32_t>(keep));  // 128 -> min normal
 }
 
+// INT8 code of x under scale s: nearest integer to the fp64 quotient, ties
+// to even (v_rndne_f64), saturating at +-127; a NaN quotient gives 0.
+__device__ __forceinline__ int8_t quantize_i8(double x, float s) {
+  const double q = x / static_cast<double>(s);
+  if (q != q) return 0;
+  if (q >= 127.0) return 127;
+  if (q <= -127.0) return -127;
+  return static_cast<int8_t>(static_cast<int>(__builtin_rint(q)));
+}
+
+// T = cache element type; int8_t stands for an INT8 cache fed with bf16
 template <typename T> __device__ __forceinline__ double load_d(const void* p, int64_t i);
 template <> __device__ __forceinline__ double load_d<float>(const void* p, int64_t i) {
   return static_cast<double>(static_cast<const float*>(p)[i]);
 }
 template <> __device__ __forceinline__ double load_d<uint16_t>(const void* p, int64_t i) {
   return static_cast<double>(bf16_to_float(static_cast<const uint16_t*>(p)[i]));
+}
+template <> __device__ __forceinline__ double load_d<int8_t>(const void* p, int64_t i) {
+  return load_d<uint16_t>(p, i);
 }
 
 template <typename T> __device__ __forceinline__ void store_rounded(void* p, int64_t i, double x);
@@ -112,8 +135,15 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       } else {
         const int64_t row = slot_row<PAGED>(p, b, pos, head);
         if (row >= 0) {
-          store_rounded<T>(p.k_cache, row * p.D + ia, ra);
-          store_rounded<T>(p.k_cache, row * p.D + ib, rb);
+          if constexpr (std::is_same<T, int8_t>::value) {
+            int8_t* kc = static_cast<int8_t*>(p.k_cache);
+            const float ks = p.k_scale[head];
+            kc[row * p.D + ia] = quantize_i8(ra, ks);
+            kc[row * p.D + ib] = quantize_i8(rb, ks);
+          } else {
+            store_rounded<T>(p.k_cache, row * p.D + ia, ra);
+            store_rounded<T>(p.k_cache, row * p.D + ib, rb);
+          }
         }
       }
     } else {
@@ -122,7 +152,15 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       const int64_t row = slot_row<PAGED>(p, b, pos, g);
       if (row >= 0) {
         const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
-        static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];
+        if constexpr (std::is_same<T, int8_t>::value) {
+          // group of the slot: the physical block, or 16-token group of the row
+          const int64_t grp = PAGED ? row / (16 * p.G)
+                                    : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (pos >> 4);
+          const int64_t vi = ((grp * p.G + g) * p.D + d) * 16 + (pos & 15);
+          static_cast<int8_t*>(p.v_cache)[vi] = quantize_i8(load_d<int8_t>(p.v_new, src), p.v_scale[g]);
+        } else {
+          static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];
+        }
       }
     }
   }
@@ -137,6 +175,9 @@ hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
   if (kv_dtype == KVD_FP32) {
     if (paged) rope_append_kernel<float, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<float, false><<<grid, 256, 0, stream>>>(p);
+  } else if (kv_dtype == KVD_INT8) {
+    if (paged) rope_append_kernel<int8_t, true><<<grid, 256, 0, stream>>>(p);
+    else rope_append_kernel<int8_t, false><<<grid, 256, 0, stream>>>(p);
   } else {
     if (paged) rope_append_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(p);

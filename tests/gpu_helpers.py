@@ -25,10 +25,23 @@ def upload(p: W.Problem, dev):
     t = {k: W.as_torch(getattr(p, k), dev) for k in
          ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
     t["block_table"] = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    for k in ("k_scale", "v_scale"):
+        a = getattr(p, k)
+        t[k] = None if a is None else W.as_torch(a, dev)
     return t
 
 
 def gpu_step(t, s: W.Spec, max_len: int, style="interleaved", scale=None, sync=True):
+    if s.dtype == "i8":
+        q_rot = kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"],
+                                        t["v_cache"], t["k_scale"], t["v_scale"], t["positions"],
+                                        t["block_table"], base=s.rope_base, style=style)
+        out, lse = kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
+                                            t["v_scale"], t["seq_lens"], t["block_table"],
+                                            scale=scale, max_seq_len=max_len)
+        if sync:
+            torch.cuda.synchronize()
+        return q_rot, out, lse
     q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                t["positions"], t["block_table"], base=s.rope_base, style=style)
     out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
@@ -44,13 +57,15 @@ def oracle_step(p: W.Problem, style="interleaved", units=None, scale=None):
     s = p.spec
     g = geom(s)
     kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if s.dtype == "i8" else {}
     q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, p.block_table,
-                               base=s.rope_base, style=style)
+                               base=s.rope_base, style=style, **sc)
     if units is None:
-        out, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, p.block_table, scale=scale)
+        out, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, p.block_table, scale=scale,
+                                      **sc)
     else:
         out, lse = oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, units, p.block_table,
-                                            scale=scale)
+                                            scale=scale, **sc)
     return q_rot, out, lse, kc, vc
 
 
@@ -68,4 +83,6 @@ def appended_rows(p: W.Problem):
 
 
 def bits(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.int8:
+        return a
     return a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)

@@ -103,9 +103,41 @@ def test_rope_rejects_bad_arguments(lib):
     assert rope(lib, shape(batch=0)) == OK
 
 
+def rope8(lib, sh, ks=FAKE, vs=FAKE, table=None):
+    return lib.rope_append_kv_int8(ctypes.byref(sh) if sh is not None else None, FAKE, FAKE,
+                                   FAKE, ctypes.c_void_p(0x3000), FAKE, FAKE, ks, vs, FAKE, table,
+                                   10000.0, 0, None)
+
+
+def attn8(lib, sh, ks=FAKE, vs=FAKE, msl=32):
+    return lib.gqa_decode_attn_int8(ctypes.byref(sh) if sh is not None else None, FAKE, FAKE,
+                                    FAKE, ks, vs, FAKE, None, msl, 0.125,
+                                    ctypes.c_void_p(0x2000), None, None, 0, None)
+
+
+def test_int8_calls_validate(lib):
+    i8 = shape(kv_dtype=2)
+    # the bf16/fp32 calls reject INT8 caches (they carry no scales) and the
+    # INT8 calls reject the other dtypes
+    assert rope(lib, i8) == EUNSUPPORTED
+    assert attn(lib, i8) == EUNSUPPORTED
+    assert rope8(lib, shape()) == EUNSUPPORTED
+    assert attn8(lib, shape()) == EUNSUPPORTED
+    assert rope8(lib, None) == EINVAL and attn8(lib, None) == EINVAL
+    assert rope8(lib, i8, ks=None) == EINVAL and rope8(lib, i8, vs=None) == EINVAL
+    assert attn8(lib, i8, ks=None) == EINVAL and attn8(lib, i8, vs=None) == EINVAL
+    # contiguous INT8 capacity must be whole 16-token groups
+    assert rope8(lib, shape(kv_dtype=2, max_seq_len=40)) == EUNSUPPORTED
+    assert attn8(lib, shape(kv_dtype=2, max_seq_len=40)) == EUNSUPPORTED
+    assert attn8(lib, i8, msl=65) == ERANGE
+    assert rope8(lib, i8, table=FAKE) == EINVAL
+    assert rope8(lib, shape(kv_dtype=2, batch=0)) == OK
+    assert attn8(lib, shape(kv_dtype=2, batch=0)) == OK
+
+
 def test_tuning_and_timer_validation(lib):
     assert lib.kvd_set_tuning(-2, 0) == EINVAL
-    assert lib.kvd_set_tuning(2, 0) == EINVAL
+    assert lib.kvd_set_tuning(3, 0) == EINVAL
     assert lib.kvd_set_tuning(0, 24) == EINVAL           # not a multiple of 16
     assert lib.kvd_set_tuning(0, -16) == EINVAL
     assert lib.kvd_set_tuning(-1, 0) == OK
