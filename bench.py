@@ -18,8 +18,13 @@ Prints ONE JSON line:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload, in the same unit (a reported baseline only)
 
+With --kv int8 the same workload runs on an INT8 cache (per-KV-head
+scales, rope_append_kv_int8 + gqa_decode_attn_int8); KV bytes then count one
+byte per element.
+
 Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
-                       [--kv-heads G] [--kernel auto|valu|mfma] [--split N]
+                       [--kv-heads G] [--kv native|int8]
+                       [--kernel auto|valu|mfma] [--split N]
                        [--no-cpu-baseline] [--flush]
 """
 import argparse
@@ -47,11 +52,14 @@ def kernel_source_hash() -> str:
 
 
 def workload_name(s) -> str:
-    return {"c1": "c1 fp32 single step B1 H8 G2 D64 L256",
+    name = {"c1": "c1 fp32 single step B1 H8 G2 D64 L256",
             "c2": "c2 bf16 Llama-3-8B-shaped B1 H32 G8 D128 L1024",
             "c3": "c3 bf16 batched varlen B64 H32 G8 D128 L~U[512,8192]",
             "c4": "c4 bf16 paged(16) B32 H32 G8 D128 L~U[1024,32768] pool 65536 blocks",
             "c5": f"c5 bf16 long context B1 H32 G{s.n_kv_heads} D128 L131072"}[s.name]
+    if s.dtype == "i8":
+        name = name.replace(" bf16 ", " INT8-KV (bf16 q, per-head scales) ", 1)
+    return name
 
 
 def load_traffic(key: str, src_hash: str):
@@ -110,6 +118,8 @@ def cpu_baseline(s, p, budget_s: float):
                             max_seq_len=s.max_seq_len, block_size=s.block_size,
                             num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
 
+    sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if s.dtype == "i8" else {}
+
     def run(n):
         idx = np.arange(n)
         kc, vc = p.k_cache, p.v_cache          # the oracle writes only the appended slots
@@ -128,8 +138,8 @@ def cpu_baseline(s, p, budget_s: float):
         pos = np.ascontiguousarray(p.positions[idx])
         lens = np.ascontiguousarray(p.seq_lens[idx])
         t0 = time.perf_counter()
-        q_rot = oracle.rope_append(g, *args, kc, vc, pos, tab, base=s.rope_base)
-        oracle.decode_attn(g, q_rot, kc, vc, lens, tab, n_threads=threads)
+        q_rot = oracle.rope_append(g, *args, kc, vc, pos, tab, base=s.rope_base, **sc)
+        oracle.decode_attn(g, q_rot, kc, vc, lens, tab, n_threads=threads, **sc)
         return time.perf_counter() - t0, lens
 
     del g_all
@@ -158,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kv-heads", type=int, default=None)
+    ap.add_argument("--kv", default="native", choices=["native", "int8"],
+                    help="cache dtype: the workload's own (bf16 / fp32) or INT8 with per-head scales")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--tail-split", type=int, default=0,
@@ -203,6 +215,11 @@ def main():
         print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd)}))
         return
     s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
+    if args.kv == "int8":
+        if s.dtype != "bf16":
+            print("--kv int8 applies to the bf16 workloads (c2..c5)", file=sys.stderr)
+            sys.exit(2)
+        s = s.replace(dtype="i8")
     t_gen = time.perf_counter()
     p = W.make_problem(s)
     print(f"# generated {s.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
@@ -210,6 +227,10 @@ def main():
     t = {k: W.as_torch(getattr(p, k), dev) for k in
          ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
     table = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    int8 = s.dtype == "i8"
+    if int8:
+        t["k_scale"] = W.as_torch(p.k_scale, dev)
+        t["v_scale"] = W.as_torch(p.v_scale, dev)
     max_len = p.max_len
     kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split, args.tail_split,
                    args.tail_span, None if args.order < 0 else args.order)
@@ -222,6 +243,14 @@ def main():
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len)
 
     def step():
+        if int8:
+            kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                    t["k_scale"], t["v_scale"], t["positions"], table,
+                                    base=s.rope_base, q_rot=q_rot)
+            kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
+                                     t["v_scale"], t["seq_lens"], table, max_seq_len=max_len,
+                                     out=out, lse=lse, workspace=ws)
+            return
         kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                            t["positions"], table, base=s.rope_base, q_rot=q_rot)
         kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
@@ -268,7 +297,7 @@ def main():
         flushed = float(np.median(times))
         del scratch
 
-    key = f"{s.name}" + (f"_g{G}" if s.name == "c5" else "")
+    key = f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "")
     src_hash = kernel_source_hash()
     traffic = load_traffic(key, src_hash)
     result = {
@@ -282,10 +311,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if s.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1)/sqrt(128) values, seeded lengths; no datasets or weights)",
+        "dtype": {"bf16": "bf16", "f32": "f32", "i8": "i8"}[s.dtype],
+        "data": ("synthetic (seeded INT8 codes ~ clipped N(0, 40^2), per-head scales, seeded "
+                 "lengths; no datasets or weights)" if int8 else
+                 "synthetic (seeded N(0,1)/sqrt(128) values, seeded lengths; no datasets or weights)"),
         "config": {"workload": workload_name(s), "batch": B, "n_heads": H, "n_kv_heads": G,
-                   "head_dim": D, "kv_dtype": s.dtype, "accumulate": "f32",
+                   "head_dim": D, "kv_dtype": s.dtype, "accumulate": "f32" if not int8 else
+                   "i32 (q K^T on int8 codes, 3 q limbs), f32 (P V in fp16 hi+lo)",
                    "block_size": s.block_size, "total_context_tokens": int(p.seq_lens.sum()),
                    "max_context": max_len, "kv_bytes_per_step": kv_bytes,
                    "aux_bytes_per_step": aux, "split_tokens": plan["split_tokens"],

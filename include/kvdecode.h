@@ -58,8 +58,9 @@ typedef enum {
   KVD_BF16 = 1,          /* bfloat16 (upper half of a binary32) */
   /* INT8 cache ([KVGR] §4.3): K and V held as signed 8-bit codes with one
    * fp32 scale per KV head for each; q, k_new and v_new are bfloat16.  Only
-   * the *_int8 calls below accept it.  Layout: K as for the other dtypes;
-   * V transposed inside every 16-token group (see rope_append_kv_int8). */
+   * the *_int8 calls below accept it.  Layout: tokens grouped by 16, each
+   * group holding per KV head its K rows and its V block transposed (see
+   * rope_append_kv_int8). */
   KVD_INT8 = 2
 } kvd_dtype;
 
@@ -192,12 +193,14 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
  *
  *   q, k_new, v_new   bfloat16, shapes as in rope_append_kv
  *   q_rot      [B, H, D] fp32 output (ignored when q == NULL)
- *   k_cache    int8: contiguous [B, max_seq_len, G, D]; paged
- *              [num_blocks, 16, G, D] (row of token p: as in rope_append_kv)
- *   v_cache    int8, transposed inside each 16-token group: contiguous
- *              [B, max_seq_len / 16, G, D, 16], paged [num_blocks, G, D, 16];
- *              element (token p, head g, dim d) is [.., p / 16 or the block,
- *              g, d, p % 16]
+ *   k_cache    int8, tokens grouped by 16 and each group by head:
+ *              contiguous [B, max_seq_len / 16, G, 16, D], paged
+ *              [num_blocks, G, 16, D]; element (token p, head g, dim d) is
+ *              [.., p / 16 (contiguous) or block table[b][p / 16] (paged), g,
+ *              p % 16, d]
+ *   v_cache    int8, the same grouping with each head's block transposed:
+ *              [B, max_seq_len / 16, G, D, 16] or [num_blocks, G, D, 16];
+ *              element (p, g, d) is [.., group or block, g, d, p % 16]
  *   k_scale, v_scale  [G] fp32 device arrays, finite and > 0
  *   positions, block_table, rope_base, rope_style   as in rope_append_kv
  * Errors: as rope_append_kv; EUNSUPPORTED when kv_dtype is not KVD_INT8 (and

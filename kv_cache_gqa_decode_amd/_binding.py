@@ -140,8 +140,24 @@ def _need(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=No
 def make_shape(batch: int, n_heads: int, k_cache: torch.Tensor,
                block_table: Optional[torch.Tensor]) -> Shape:
     """kvd_shape from the K cache tensor: contiguous [B, S_max, G, D] or paged
-    pool [num_blocks, 16, G, D] with table [B, max_blocks_per_seq] (an int8
-    K cache makes an INT8 shape)."""
+    pool [num_blocks, 16, G, D] with table [B, max_blocks_per_seq]; an int8
+    K cache is grouped by 16 tokens: [B, S_max/16, G, 16, D] or
+    [num_blocks, G, 16, D]."""
+    if k_cache.dtype == torch.int8:
+        if block_table is None:
+            if k_cache.dim() != 5 or int(k_cache.shape[3]) != 16:
+                raise ValueError("contiguous int8 K cache must be [B, S_max/16, G, 16, D]")
+            if int(k_cache.shape[0]) != batch:
+                raise ValueError("contiguous cache batch dimension does not match q")
+            return Shape(batch, n_heads, int(k_cache.shape[2]), int(k_cache.shape[4]), KVD_INT8,
+                         0, int(k_cache.shape[1]) * 16, 0, 0)
+        if k_cache.dim() != 4 or int(k_cache.shape[2]) != 16:
+            raise ValueError("paged int8 K pool must be [num_blocks, G, 16, D]")
+        if block_table.dim() != 2 or int(block_table.shape[0]) != batch:
+            raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+        mbps = int(block_table.shape[1])
+        return Shape(batch, n_heads, int(k_cache.shape[1]), int(k_cache.shape[3]), KVD_INT8, 16,
+                     mbps * 16, int(k_cache.shape[0]), mbps)
     if k_cache.dim() != 4:
         raise ValueError("cache must be 4-D")
     G, D = int(k_cache.shape[2]), int(k_cache.shape[3])
@@ -261,13 +277,13 @@ def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
 
 
 def v_cache_shape_int8(k_cache: torch.Tensor, paged: bool) -> Tuple[int, ...]:
-    """Shape of the INT8 V cache that goes with an int8 K cache: V transposed
-    inside every 16-token group."""
+    """Shape of the INT8 V cache that goes with an int8 K cache: per 16-token
+    group and head, V transposed ([.., G, D, 16] against K's [.., G, 16, D])."""
     if paged:
-        nb, _, G, D = (int(x) for x in k_cache.shape)
+        nb, G, _, D = (int(x) for x in k_cache.shape)
         return (nb, G, D, 16)
-    B, S, G, D = (int(x) for x in k_cache.shape)
-    return (B, S // 16, G, D, 16)
+    B, n, G, _, D = (int(x) for x in k_cache.shape)
+    return (B, n, G, D, 16)
 
 
 def _check_scales(k_scale, v_scale, G, dev):
@@ -282,7 +298,7 @@ def rope_append_kv_int8(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: t
                         style: str = "interleaved",
                         q_rot: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
     """rope_append_kv into an INT8 cache: bf16 q / k_new / v_new, int8 K cache
-    [B, S_max, G, D] (or pool [NB, 16, G, D]) and V cache
+    [B, S_max/16, G, 16, D] (or pool [NB, G, 16, D]) and V cache
     [B, S_max/16, G, D, 16] (or [NB, G, D, 16]), per-KV-head fp32 scales."""
     lib = load_library()
     dev = k_cache.device
@@ -331,7 +347,7 @@ def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
     if block_table is not None:
         _need(block_table, "block_table", dev, torch.int32)
-    if int(k_cache.shape[3]) != D:
+    if shape.head_dim != D:
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
     if scale is None:

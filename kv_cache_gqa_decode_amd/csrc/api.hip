@@ -143,12 +143,15 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
     // at different speeds (the older one is served first), and smaller
     // units let the dispatcher even that out at a small cost in merges.
     // The VALU kernel aims for two rounds of at most 2048 tokens.  The INT8
-    // kernel plans like the MFMA one with twice the tokens per split (the
-    // same bytes).
+    // kernel aims for a single round of at most 2048 tokens: its workgroups
+    // keep two 64-token tiles in flight per wave from the first tile on,
+    // and each one pays a full memory latency before its first tile, so
+    // fewer, longer units measured faster (a 128K sequence: 2048-token
+    // splits 46 us, 512-token splits 63 us).
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (R > 16 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (R > 16 ? 1 : 4);
+    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || R > 16 ? 1 : 4);
     const int cap = kernel == 0 ? 2048 : (kernel == 2 ? 2048 : 1024);
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;

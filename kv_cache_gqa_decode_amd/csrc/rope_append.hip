@@ -16,8 +16,10 @@
 // INT8 caches (same page, §4.3: 8-bit K and V with per-head quantisation
 // parameters): the inputs are bf16 and each stored element is the code in
 // [-127, 127] nearest to x / scale[g], the quotient taken in fp64 from the
-// exact rotated key (or v_new), ties to even, saturating.  V codes go to the
-// group-transposed layout: element (pos, g, d) of group r at
+// exact rotated key (or v_new), ties to even, saturating.  Tokens are grouped
+// by 16 (group r: the physical block, or b * S_max/16 + pos/16), each group
+// holding per KV head its 16 K rows and its V block transposed: K element
+// (pos, g, d) at ((r * G + g) * 16 + pos % 16) * D + d, V element at
 // ((r * G + g) * D + d) * 16 + pos % 16.
 #include <type_traits>
 
@@ -98,6 +100,18 @@ __device__ __forceinline__ int64_t slot_row(const RopeParams& p, int b, int pos,
   return (static_cast<int64_t>(blk) * 16 + (pos & 15)) * p.G + g;
 }
 
+// INT8 caches: the 16-token group of a slot whose token-major row is `row`
+// (the physical block, or group pos/16 of sequence b), and the slot's K row
+// in the group-major layout.
+template <bool PAGED>
+__device__ __forceinline__ int64_t i8_group(const RopeParams& p, int b, int pos, int64_t row) {
+  return PAGED ? row / (16 * p.G) : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (pos >> 4);
+}
+template <bool PAGED>
+__device__ __forceinline__ int64_t i8_krow(const RopeParams& p, int b, int pos, int g, int64_t row) {
+  return (i8_group<PAGED>(p, b, pos, row) * p.G + g) * 16 + (pos & 15);
+}
+
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
   // workgroup (sequence, slice of 256 items): the D/2 rotation factors of the
@@ -136,10 +150,10 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
         const int64_t row = slot_row<PAGED>(p, b, pos, head);
         if (row >= 0) {
           if constexpr (std::is_same<T, int8_t>::value) {
-            int8_t* kc = static_cast<int8_t*>(p.k_cache);
+            int8_t* kc = static_cast<int8_t*>(p.k_cache) + i8_krow<PAGED>(p, b, pos, head, row) * p.D;
             const float ks = p.k_scale[head];
-            kc[row * p.D + ia] = quantize_i8(ra, ks);
-            kc[row * p.D + ib] = quantize_i8(rb, ks);
+            kc[ia] = quantize_i8(ra, ks);
+            kc[ib] = quantize_i8(rb, ks);
           } else {
             store_rounded<T>(p.k_cache, row * p.D + ia, ra);
             store_rounded<T>(p.k_cache, row * p.D + ib, rb);
@@ -153,10 +167,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       if (row >= 0) {
         const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
         if constexpr (std::is_same<T, int8_t>::value) {
-          // group of the slot: the physical block, or 16-token group of the row
-          const int64_t grp = PAGED ? row / (16 * p.G)
-                                    : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (pos >> 4);
-          const int64_t vi = ((grp * p.G + g) * p.D + d) * 16 + (pos & 15);
+          const int64_t vi = ((i8_group<PAGED>(p, b, pos, row) * p.G + g) * p.D + d) * 16 + (pos & 15);
           static_cast<int8_t*>(p.v_cache)[vi] = quantize_i8(load_d<int8_t>(p.v_new, src), p.v_scale[g]);
         } else {
           static_cast<T*>(p.v_cache)[row * p.D + d] = static_cast<const T*>(p.v_new)[src];

@@ -30,8 +30,10 @@ the overrides; see ``Spec``):
   near 3.2 standard deviations; the per-head scales (stream 5) are
   ``value_scale / 40 * U[0.75, 1.25]`` for K, then for V, in float32, so
   dequantised values have about the spread of the bf16 workloads.  Poisoned
-  slots hold code 127.  V is laid out transposed inside every 16-token
-  group: ``[B, S_max/16, G, D, 16]`` or ``[num_blocks, G, D, 16]``.
+  slots hold code 127.  Tokens are grouped by 16, each group holding per KV
+  head its 16 K rows and its V block transposed: K ``[B, S_max/16, G, 16, D]``
+  or ``[num_blocks, G, 16, D]``, V ``[B, S_max/16, G, D, 16]`` or
+  ``[num_blocks, G, D, 16]``.
 """
 from __future__ import annotations
 
@@ -167,6 +169,12 @@ def draw_scales(s: Spec):
     return k, v
 
 
+def group_rows(x: np.ndarray) -> np.ndarray:
+    """[n * 16, G, D] -> [n, G, 16, D]: K rows regrouped into the INT8 layout."""
+    n16, G, D = x.shape
+    return np.ascontiguousarray(x.reshape(n16 // 16, 16, G, D).transpose(0, 2, 1, 3))
+
+
 def group_transpose(x: np.ndarray) -> np.ndarray:
     """[n * 16, G, D] -> [n, G, D, 16]: V rows regrouped into the INT8 layout."""
     n16, G, D = x.shape
@@ -215,7 +223,8 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
         perm = _rng(s, 4).permutation(s.num_blocks).astype(np.int32)
         table = np.ascontiguousarray(
             perm[: B * s.max_blocks_per_seq].reshape(B, s.max_blocks_per_seq))
-        k_cache = np.full((s.num_blocks, bs, G, D), fill, dtype=store)
+        k_cache = np.full((s.num_blocks, G, bs, D) if i8 else (s.num_blocks, bs, G, D), fill,
+                          dtype=store)
         v_cache = np.full((s.num_blocks, G, D, bs) if i8 else (s.num_blocks, bs, G, D), fill,
                           dtype=store)
         for b in range(B):
@@ -229,24 +238,26 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
                 kh = np.concatenate([kh, np.full((pad, G, D), fill, store)])
                 vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
             ids = table[b, :nblk]
-            k_cache[ids] = kh.reshape(nblk, bs, G, D)
+            k_cache[ids] = group_rows(kh) if i8 else kh.reshape(nblk, bs, G, D)
             v_cache[ids] = group_transpose(vh) if i8 else vh.reshape(nblk, bs, G, D)
     else:
         S = s.max_seq_len
-        k_cache = np.full((B, S, G, D), fill, dtype=store)
+        k_cache = np.full((B, S // 16, G, 16, D) if i8 else (B, S, G, D), fill, dtype=store)
         v_cache = np.full((B, S // 16, G, D, 16) if i8 else (B, S, G, D), fill, dtype=store)
         for b in range(B):
             n_hist = int(L[b]) - 1
             if n_hist:
                 kh, vh = draw_history(s, b, n_hist)
-                k_cache[b, :n_hist] = kh
                 if i8:
                     nblk = -(-n_hist // 16)
                     pad = nblk * 16 - n_hist
                     if pad:
+                        kh = np.concatenate([kh, np.full((pad, G, D), fill, store)])
                         vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
+                    k_cache[b, :nblk] = group_rows(kh)
                     v_cache[b, :nblk] = group_transpose(vh)
                 else:
+                    k_cache[b, :n_hist] = kh
                     v_cache[b, :n_hist] = vh
     k_scale, v_scale = draw_scales(s) if i8 else (None, None)
     idt = s.input_dtype

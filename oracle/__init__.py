@@ -21,8 +21,9 @@ quantisation parameters calibrated per attention head): dtype ``"i8"``.  q,
 k_new and v_new are then bf16; the caches hold codes in [-127, 127] with one
 fp32 scale per KV head for K (``k_scale``) and one for V (``v_scale``).  A
 new element x is stored as the code nearest to x / scale (ties to even,
-saturating); attention reads scale * code.  V is transposed inside every
-16-token group (``Geometry.v_cache_shape``).
+saturating); attention reads scale * code.  Tokens are grouped by 16 and
+each group holds, per KV head, the 16 K rows and the V block transposed
+(``Geometry.cache_shape`` / ``Geometry.v_cache_shape``).
 
 Arrays: bf16 data are passed as ``uint16`` bit patterns; fp32 as ``float32``;
 fp64 as ``float64``.  Pages cited by title:
@@ -122,7 +123,9 @@ class Geometry:
     Contiguous caches are ``[B, S_max, G, D]``; paged pools are
     ``[num_blocks, block_size, G, D]`` with an int32 table
     ``[B, max_blocks_per_seq]`` ([OPT] §四 PagedKVCache; [KVGR] §4.1).
-    INT8 V caches are ``[B, S_max/16, G, D, 16]`` or ``[num_blocks, G, D, 16]``.
+    INT8 caches are grouped by 16 tokens, per head: K ``[B, S_max/16, G, 16, D]``
+    or ``[num_blocks, G, 16, D]``, V ``[B, S_max/16, G, D, 16]`` or
+    ``[num_blocks, G, D, 16]``.
     """
 
     def __init__(self, batch, n_heads, n_kv_heads, head_dim, dtype="bf16",
@@ -154,9 +157,15 @@ class Geometry:
         return _NP_INPUT[self.code]
 
     def cache_shape(self):
+        """Shape of the K cache (and of V, except for INT8)."""
+        G, D = self.n_kv_heads, self.head_dim
+        if self.dtype == "i8":
+            if self.block_size:
+                return (self.num_blocks, G, 16, D)
+            return (self.batch, self.max_seq_len // 16, G, 16, D)
         if self.block_size:
-            return (self.num_blocks, self.block_size, self.n_kv_heads, self.head_dim)
-        return (self.batch, self.max_seq_len, self.n_kv_heads, self.head_dim)
+            return (self.num_blocks, self.block_size, G, D)
+        return (self.batch, self.max_seq_len, G, D)
 
     def v_cache_shape(self):
         if self.dtype != "i8":

@@ -41,11 +41,12 @@
  * v_new are then bf16; each cache element is a code n in [-127, 127] whose
  * value is scale[g] * n, with one fp32 scale per KV head for K and one for
  * V.  A new element x is stored as the code nearest to x / scale (ties to
- * even; x is the exact rotated key, or v_new as given).  Layout: K as the
- * other dtypes ([.., 16, G, D] rows of D codes); V transposed inside each
- * 16-token group: group r (contiguous: r = b * S_max/16 + pos/16; paged: the
- * physical block) holds [G][D][16] codes, element (pos, g, d) at
- * ((r * G + g) * D + d) * 16 + pos % 16.
+ * even; x is the exact rotated key, or v_new as given).  Layout: tokens are
+ * grouped by 16 (contiguous: group r = b * S_max/16 + pos/16; paged: the
+ * physical block), and each group holds, per KV head, the 16 K rows
+ * ([G][16][D]: element (pos, g, d) at ((r * G + g) * 16 + pos % 16) * D + d)
+ * and the V block transposed ([G][D][16]: at ((r * G + g) * D + d) * 16 +
+ * pos % 16).
  */
 #include <math.h>
 #include <pthread.h>
@@ -174,18 +175,27 @@ static int64_t cache_row(const kvo_shape* sh, const int32_t* table, int b, int64
   return ((int64_t)phys * sh->block_size + off) * sh->n_kv_heads + g;
 }
 
-/* INT8 caches: index of V element (pos, g, d) in the group-transposed
- * layout; -1 when the slot does not exist.  `row` is cache_row's result for
- * the same slot (it carries the block-table lookup). */
-static int64_t vt_index(const kvo_shape* sh, int b, int64_t pos, int g, int d, int64_t row) {
+/* INT8 caches: the 16-token group of slot (b, pos) whose row is `row`
+ * (cache_row's result, which carries the block-table lookup); -1 when the
+ * slot does not exist. */
+static int64_t i8_group(const kvo_shape* sh, int b, int64_t pos, int64_t row) {
   if (row < 0) return -1;
-  int64_t group;
-  if (sh->block_size == 0) {
-    group = (int64_t)b * (sh->max_seq_len / 16) + pos / 16;
-  } else {
-    group = row / ((int64_t)sh->block_size * sh->n_kv_heads);   /* physical block */
-  }
-  return ((group * sh->n_kv_heads + g) * sh->head_dim + d) * 16 + pos % 16;
+  if (sh->block_size == 0) return (int64_t)b * (sh->max_seq_len / 16) + pos / 16;
+  return row / ((int64_t)sh->block_size * sh->n_kv_heads);   /* physical block */
+}
+
+/* INT8 K element (pos, g, d): group-major, the head's 16 rows together */
+static int64_t kq_index(const kvo_shape* sh, int b, int64_t pos, int g, int d, int64_t row) {
+  int64_t r = i8_group(sh, b, pos, row);
+  if (r < 0) return -1;
+  return ((r * sh->n_kv_heads + g) * 16 + pos % 16) * sh->head_dim + d;
+}
+
+/* INT8 V element (pos, g, d): group-major, the head's block transposed */
+static int64_t vt_index(const kvo_shape* sh, int b, int64_t pos, int g, int d, int64_t row) {
+  int64_t r = i8_group(sh, b, pos, row);
+  if (r < 0) return -1;
+  return ((r * sh->n_kv_heads + g) * sh->head_dim + d) * 16 + pos % 16;
 }
 
 /* ----------------------------------------------------- rope + cache append */
@@ -224,7 +234,8 @@ static int rope_append_impl(const kvo_shape* sh, const void* q, const void* k_ne
       for (int d = 0; d < D; ++d) {
         if (sh->dtype == KVO_I8) {
           /* codes of the exact rotated key and of v_new ([KVGR] §4.3) */
-          ((int8_t*)k_cache)[row * D + d] = (int8_t)kvo_quantize_i8(y[d], k_scale[g]);
+          ((int8_t*)k_cache)[kq_index(sh, b, positions[b], g, d, row)] =
+              (int8_t)kvo_quantize_i8(y[d], k_scale[g]);
           ((int8_t*)v_cache)[vt_index(sh, b, positions[b], g, d, row)] =
               (int8_t)kvo_quantize_i8(load_elem(v_new, in_dt, src + d), v_scale[g]);
         } else {
@@ -284,10 +295,11 @@ typedef struct {
 
 /* Value of cached K / V element d of slot (b, j, g) whose row is `row`.
  * INT8 caches dequantise exactly: scale[g] * code ([KVGR] §4.3). */
-static double key_at(const attn_job* job, int64_t row, int g, int d) {
+static double key_at(const attn_job* job, int b, int64_t j, int64_t row, int g, int d) {
   const kvo_shape* sh = job->sh;
   if (sh->dtype == KVO_I8)
-    return (double)job->k_scale[g] * (double)((const int8_t*)job->k_cache)[row * sh->head_dim + d];
+    return (double)job->k_scale[g] *
+           (double)((const int8_t*)job->k_cache)[kq_index(sh, b, j, g, d, row)];
   return load_elem(job->k_cache, sh->dtype, row * sh->head_dim + d);
 }
 
@@ -321,7 +333,7 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
     int64_t row = cache_row(sh, job->table, b, j, g);
     if (row < 0) { job->bad = 1; s[j] = -INFINITY; continue; }
     double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += q[d] * key_at(job, row, g, d);
+    for (int d = 0; d < D; ++d) dot += q[d] * key_at(job, b, j, row, g, d);
     s[j] = job->scale * dot;
     if (s[j] > m) m = s[j];
   }

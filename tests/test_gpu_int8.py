@@ -149,14 +149,14 @@ def test_repeated_steps_are_idempotent():
 
 def test_plan_reports_the_int8_kernel():
     dev = device()
-    k = torch.empty((4, 64, 8, 128), dtype=torch.int8, device=dev)
+    k = torch.empty((4, 4, 8, 16, 128), dtype=torch.int8, device=dev)    # [B, S/16, G, 16, D]
     assert kvd.get_plan(4, 32, k)["kernel"] == "int8"
     with pytest.raises(kvd.KvdError):
         kvd.set_tuning("mfma", 0)
         kvd.get_plan(4, 32, k)
     kvd.set_tuning(None, 0)
     with pytest.raises(kvd.KvdError):
-        kvd.get_plan(1, 64, torch.empty((1, 64, 1, 128), dtype=torch.int8, device=dev))  # n_rep 64
+        kvd.get_plan(1, 64, torch.empty((1, 4, 1, 16, 128), dtype=torch.int8, device=dev))  # n_rep 64
 
 
 # ------------------------------------------------------------- full sizes

@@ -95,6 +95,14 @@ def _logical_v(s, v_cache):
     return np.ascontiguousarray(v_cache.transpose(0, 1, 4, 2, 3).reshape(B, n * 16, G, D))
 
 
+def _logical_k(s, k_cache):
+    """Token-major view [.., 16, G, D] of a group-major INT8 K cache."""
+    if s.block_size:
+        return np.ascontiguousarray(k_cache.transpose(0, 2, 1, 3))
+    B, n, G, _, D = k_cache.shape
+    return np.ascontiguousarray(k_cache.transpose(0, 1, 3, 2, 4).reshape(B, n * 16, G, D))
+
+
 def _slot(s, p, b):
     pos = int(p.positions[b])
     if s.block_size:
@@ -106,21 +114,21 @@ def _slot(s, p, b):
 def test_append_stores_nearest_codes_and_nothing_else(paged):
     s = _small_i8(paged)
     p = W.make_problem(s, lengths=np.array([1, 17, 70], np.int32))
-    k0, v0 = p.k_cache.copy(), _logical_v(s, p.v_cache)
+    k0, v0 = _logical_k(s, p.k_cache), _logical_v(s, p.v_cache)
     q_rot = oracle.rope_append(_geom(s), p.q, p.k_new, p.v_new, p.k_cache, p.v_cache,
                                p.positions, p.block_table, k_scale=p.k_scale, v_scale=p.v_scale)
-    vl = _logical_v(s, p.v_cache)
-    changed = np.zeros(p.k_cache.shape[:2], bool)
+    kl, vl = _logical_k(s, p.k_cache), _logical_v(s, p.v_cache)
+    changed = np.zeros(kl.shape[:2], bool)
     for b in range(s.batch):
         changed[_slot(s, p, b)] = True
-    assert np.array_equal(p.k_cache[~changed], k0[~changed])
+    assert np.array_equal(kl[~changed], k0[~changed])
     assert np.array_equal(vl[~changed], v0[~changed])
     for b in range(s.batch):
         sl = _slot(s, p, b)
         pos = int(p.positions[b])
         for g in range(s.n_kv_heads):
             k_rot = oracle.rope_rotate(_bf16_to64(p.k_new[b, g]), pos)
-            assert np.array_equal(p.k_cache[sl][g], _nearest_codes(k_rot, p.k_scale[g]))
+            assert np.array_equal(kl[sl][g], _nearest_codes(k_rot, p.k_scale[g]))
             v = _bf16_to64(p.v_new[b, g])
             assert np.array_equal(vl[sl][g], _nearest_codes(v, p.v_scale[g]))
     # q is rotated as for any other cache dtype
@@ -134,15 +142,15 @@ def test_append_saturates():
     neg = np.full_like(p.v_new, 0xC480)     # -1024.0
     oracle.rope_append(_geom(s), None, big, neg, p.k_cache, p.v_cache, p.positions,
                        k_scale=p.k_scale, v_scale=p.v_scale)
-    assert (p.k_cache[0, 0] == 127).all()   # position 0: no rotation
+    assert (_logical_k(s, p.k_cache)[0, 0] == 127).all()   # position 0: no rotation
     assert (_logical_v(s, p.v_cache)[0, 0] == -127).all()
 
 
 def _dequantised_f64(s, p):
-    """fp64 caches holding scale * code, V regrouped to token-major."""
+    """fp64 caches holding scale * code, K and V regrouped to token-major."""
     ks = p.k_scale.astype(np.float64)[:, None]
     vs = p.v_scale.astype(np.float64)[:, None]
-    k = np.ascontiguousarray(p.k_cache.astype(np.float64) * ks)
+    k = np.ascontiguousarray(_logical_k(s, p.k_cache).astype(np.float64) * ks)
     v = np.ascontiguousarray(_logical_v(s, p.v_cache).astype(np.float64) * vs)
     return k, v
 
@@ -174,7 +182,8 @@ def test_attention_equals_fp64_attention_on_dequantised_cache(paged, G):
 
 def test_scales_and_layout_matter():
     """Plausible mistakes change the result far beyond rounding: K and V
-    scales swapped, or V read token-major instead of group-transposed."""
+    scales swapped, V read token-major instead of group-transposed, or K
+    read token-major instead of group-major."""
     s = _small_i8(G=2)
     p = W.make_problem(s, lengths=np.array([40, 64, 70], np.int32))
     g8 = _geom(s)
@@ -190,6 +199,11 @@ def test_scales_and_layout_matter():
         p.v_scale.astype(np.float64)[:, None]
     g64 = oracle.Geometry(s.batch, s.n_heads, 2, s.head_dim, "f64", max_seq_len=s.max_seq_len)
     bad, _ = oracle.decode_attn(g64, q_rot, k64, np.ascontiguousarray(wrong_v), p.seq_lens)
+    assert np.abs(out - bad).max() > 1e-2 * np.abs(out).max()
+    _, v64 = _dequantised_f64(s, p)
+    wrong_k = p.k_cache.reshape(s.batch, s.max_seq_len, 2, s.head_dim).astype(np.float64) * \
+        p.k_scale.astype(np.float64)[:, None]
+    bad, _ = oracle.decode_attn(g64, q_rot, np.ascontiguousarray(wrong_k), v64, p.seq_lens)
     assert np.abs(out - bad).max() > 1e-2 * np.abs(out).max()
 
 
