@@ -42,12 +42,20 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kv_cache_gqa_decode_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+# the sources each split-K kernel is built from (a change to any of them
+# invalidates the traffic counters recorded for that kernel)
+KERNEL_SOURCES = {
+    "mfma": ("decode_mfma.hip", "mfma_tile.h", "kvd_internal.h"),
+    "int8": ("decode_i8.hip", "mfma_tile.h", "kvd_internal.h"),
+    "valu": ("decode_valu.hip", "kvd_internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str = "mfma") -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -298,7 +306,7 @@ def main():
         del scratch
 
     key = f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "")
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(plan["kernel"])
     traffic = load_traffic(key, src_hash)
     result = {
         "metric": "decode-attention KV HBM GB/s (% of peak) and seq-steps/sec at 1 MI355X",
