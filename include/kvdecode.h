@@ -263,7 +263,11 @@ kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens);
  * hardware dispatches last are short; dispatch_order sets which of (split,
  * KV head, sequence) varies fastest in the MFMA kernels' unit order: 0
  * (split, head, sequence), 1 (head, sequence, split), 2 (head, split,
- * sequence), -1 automatic.  EINVAL for values outside these ranges.
+ * sequence), 3 a work list of the (sequence, split) units that hold
+ * tokens, built on the device from seq_lens before the split kernel (full
+ * splits sequence by sequence, then the partial last splits longest first;
+ * ignored with a single split), -1 automatic (the work list for batches
+ * with more than one split).  EINVAL for values outside these ranges.
  */
 kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
                              int32_t tail_span_tokens, int32_t dispatch_order);

@@ -531,22 +531,22 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_i8_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
-  const Unit u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  Unit u;
+  if (!unit_at(p, u)) return;
   run_split_i8<D, 1, PAGED>(p, smem, u.b, u.g, u.split);
 }
 // 17 to 32 query heads per KV head: one workgroup per CU
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_i8_kernel_wide(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
-  const Unit u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  Unit u;
+  if (!unit_at(p, u)) return;
   run_split_i8<D, 2, PAGED>(p, smem, u.b, u.g, u.split);
 }
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
-  const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
-                  : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
-                                      : dim3(p.G, p.n_splits, p.B);
+  const dim3 grid = split_grid(p);
   if (NB == 1) {
     if (paged) decode_i8_kernel<D, true><<<grid, 256, 0, s>>>(p);
     else decode_i8_kernel<D, false><<<grid, 256, 0, s>>>(p);

@@ -439,15 +439,14 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 template <int D, int NB, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes<D>()];
-  const Unit u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  Unit u;
+  if (!unit_at(p, u)) return;
   run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
 }
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
-  const dim3 grid = p.grid_order == 0 ? dim3(p.n_splits, p.G, p.B)
-                  : p.grid_order == 1 ? dim3(p.G, p.B, p.n_splits)
-                                      : dim3(p.G, p.n_splits, p.B);
+  const dim3 grid = split_grid(p);
   if (paged) decode_mfma_kernel<D, NB, true><<<grid, 256, 0, s>>>(p);
   else decode_mfma_kernel<D, NB, false><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();

@@ -37,7 +37,10 @@ struct DecodeParams {
   int32_t head_groups;      // query-head groups per KV head (VALU kernel)
   float qscale;             // softmax scale * log2(e)
   int32_t direct;           // 1: one split, write out / lse directly
-  int32_t grid_order;       // MFMA kernel: 0 (split, G, B), 1 (G, B, split), 2 (G, split, B)
+  int32_t grid_order;       // matrix-core kernels: 0 (split, G, B), 1 (G, B, split),
+                            // 2 (G, split, B), 3 work list (heads fastest; units.hip)
+  int32_t* units;           // work list (grid_order 3): b | split << 16, in the workspace
+  int32_t* n_units;         // its length
 };
 
 struct RopeParams {
@@ -67,6 +70,7 @@ hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool page
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_build_units(const DecodeParams& p, hipStream_t stream);
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).
 int valu_heads_per_pass(int n_rep);
 // Workgroups and tokens per workgroup-iteration of the MFMA kernel.

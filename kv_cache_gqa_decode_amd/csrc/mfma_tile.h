@@ -167,13 +167,37 @@ __device__ __forceinline__ void lds_zero16(uint32_t addr) {
 }
 
 // The dispatch order (chosen by the planner) of the (sequence, KV head,
-// split) units, slot x fastest: which of them run side by side decides how
+// split) units, slot x fastest (orders 0-2; order 3 reads a work list): which of them run side by side decides how
 // the workgroups reading the same DRAM rows (the heads of one token range)
 // and the longest chunks are spread in time and across the XCDs.
 struct Unit { int b, g, split; };
 __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int z) {
   const int o = p.grid_order;
   return Unit{o == 1 ? y : z, o == 0 ? y : x, o == 0 ? x : (o == 1 ? z : y)};
+}
+// This workgroup's unit; false when it has none (order 3: past the end of
+// the work list, whose entries are b | split << 16 and whose KV heads are
+// the G consecutive workgroups of each entry).
+__device__ __forceinline__ bool unit_at(const DecodeParams& p, Unit& u) {
+  if (p.grid_order == 3) {
+    const int id = static_cast<int>(blockIdx.x);
+    const int k = id / p.G;
+    if (k >= scalar_load_i32(p.n_units)) return false;
+    const uint32_t e = static_cast<uint32_t>(scalar_load_i32(p.units + k));
+    u = Unit{static_cast<int>(e & 0xffffu), id - k * p.G, static_cast<int>(e >> 16)};
+    return true;
+  }
+  u = unit_of(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  return true;
+}
+// The split kernels' grid for the dispatch order.
+inline dim3 split_grid(const DecodeParams& p) {
+  switch (p.grid_order) {
+    case 0: return dim3(p.n_splits, p.G, p.B);
+    case 1: return dim3(p.G, p.B, p.n_splits);
+    case 2: return dim3(p.G, p.n_splits, p.B);
+    default: return dim3(static_cast<unsigned>(p.G) * p.B * p.n_splits);
+  }
 }
 }  // namespace mt
 }  // namespace kvd

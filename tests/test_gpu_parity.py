@@ -207,7 +207,7 @@ def test_repeated_steps_are_idempotent():
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split,tail,span", [(256, 64, 400), (512, 128, 1024), (128, 16, 96),
                                              (1024, 1024, 500), (256, 32, 0)])
-@pytest.mark.parametrize("order", [None, 0, 1, 2])
+@pytest.mark.parametrize("order", [None, 0, 1, 2, 3])
 def test_two_level_splits(kernel, split, tail, span, order):
     """Splits of `split` tokens, then of `tail` tokens over the last `span`
     positions of the bound, in every dispatch order: the merge sees the same
@@ -221,9 +221,36 @@ def test_two_level_splits(kernel, split, tail, span, order):
 
 
 @pytest.mark.parametrize("kernel", ["mfma"])
-@pytest.mark.parametrize("order", [0, 1, 2])
+@pytest.mark.parametrize("order", [0, 1, 2, 3])
 def test_two_level_splits_paged(kernel, order):
     s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
     p = W.make_problem(s, lengths=RAGGED)
     check_full(p, kernel=kernel, split=256, tail=(32, 300), order=order,
                what=f"paged {kernel} two-level order={order}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("order", [None, 1, 3])
+def test_empty_sequences_with_several_splits(kernel, order):
+    """Zero-length sequences among long ones with several splits: the work
+    list holds no unit for them, the merge still writes out = 0, lse = -inf,
+    and the others match the oracle."""
+    if kernel == "valu" and order is not None:
+        pytest.skip("the VALU kernel has one dispatch order")
+    dev = device()
+    s = W.spec("c3", batch=5, max_seq_len=1024, q_gain=8.0)
+    p = W.make_problem(s, lengths=np.array([1, 300, 1, 1024, 17], np.int32))
+    kvd.set_tuning(kernel, 64, 0, -1, order)
+    t = upload(p, dev)
+    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                               t["positions"])
+    lens = torch.tensor([0, 300, 0, 1024, 17], dtype=torch.int32, device=dev)
+    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens, max_seq_len=1024)
+    torch.cuda.synchronize()
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    assert torch.isinf(lse[0]).all() and torch.isinf(lse[2]).all()
+    p.seq_lens[:] = [0, 300, 0, 1024, 17]
+    oq, oo, ol, _, _ = oracle_step(p)
+    keep = [1, 3, 4]
+    gates.assert_out(out.cpu().numpy()[keep], oo[keep], "bf16", "empty sequences")
+    gates.assert_lse(lse.cpu().numpy()[keep], ol[keep], "bf16", "empty sequences")
