@@ -83,12 +83,19 @@ typedef enum {
  *               caches only, the rest bfloat16)
  *   block_size  0  = contiguous cache  [B, max_seq_len, G, D]
  *                    ([OPT] §四 KVCache: (batch, seq, heads, head_dim));
- *               16 = paged pool [num_blocks, 16, G, D] with an int32 block
- *                    table [B, max_blocks_per_seq]: token p of sequence b is
- *                    row p % 16 of block table[b][p / 16] ([OPT] §四
- *                    PagedKVCache; [KVGR] §4.1, 16-token blocks)
+ *               16 or 32 = paged pool [num_blocks, block_size, G, D] with an
+ *                    int32 block table [B, max_blocks_per_seq]: token p of
+ *                    sequence b is row p % block_size of block
+ *                    table[b][p / block_size] ([OPT] §四 PagedKVCache;
+ *                    [KVGR] §4.1, 16-token blocks; [OPT] §九 recommends 32
+ *                    for long sequences).  Several rows may name the same
+ *                    block (a shared prompt prefix, [OPT] §九 prefix
+ *                    caching), read only: a block that receives an append
+ *                    must belong to that sequence alone (copying a shared
+ *                    block before writing it is the caller's)
  *   max_seq_len contiguous: S_max, the row capacity per sequence (a multiple
- *               of 16 for KVD_INT8); paged: must equal max_blocks_per_seq * 16
+ *               of 16 for KVD_INT8); paged: must equal
+ *               max_blocks_per_seq * block_size
  *   num_blocks  paged: pool size (>= 1); contiguous: ignored
  *   max_blocks_per_seq  paged: table row stride (>= 1); contiguous: ignored
  */

@@ -151,13 +151,18 @@ def make_shape(batch: int, n_heads: int, k_cache: torch.Tensor,
                 raise ValueError("contiguous cache batch dimension does not match q")
             return Shape(batch, n_heads, int(k_cache.shape[2]), int(k_cache.shape[4]), KVD_INT8,
                          0, int(k_cache.shape[1]) * 16, 0, 0)
-        if k_cache.dim() != 4 or int(k_cache.shape[2]) != 16:
-            raise ValueError("paged int8 K pool must be [num_blocks, G, 16, D]")
+        # paged: [NB, G, 16, D] (16-token blocks) or [NB, m, G, 16, D] (16m-token blocks)
+        if k_cache.dim() == 4 and int(k_cache.shape[2]) == 16:
+            nb, m, G, D = int(k_cache.shape[0]), 1, int(k_cache.shape[1]), int(k_cache.shape[3])
+        elif k_cache.dim() == 5 and int(k_cache.shape[3]) == 16:
+            nb, m, G, D = (int(k_cache.shape[i]) for i in (0, 1, 2, 4))
+        else:
+            raise ValueError("paged int8 K pool must be [num_blocks, G, 16, D] or "
+                             "[num_blocks, block_size/16, G, 16, D]")
         if block_table.dim() != 2 or int(block_table.shape[0]) != batch:
             raise ValueError("block_table must be [batch, max_blocks_per_seq]")
         mbps = int(block_table.shape[1])
-        return Shape(batch, n_heads, int(k_cache.shape[1]), int(k_cache.shape[3]), KVD_INT8, 16,
-                     mbps * 16, int(k_cache.shape[0]), mbps)
+        return Shape(batch, n_heads, G, D, KVD_INT8, 16 * m, mbps * 16 * m, nb, mbps)
     if k_cache.dim() != 4:
         raise ValueError("cache must be 4-D")
     G, D = int(k_cache.shape[2]), int(k_cache.shape[3])
@@ -166,12 +171,13 @@ def make_shape(batch: int, n_heads: int, k_cache: torch.Tensor,
         if int(k_cache.shape[0]) != batch:
             raise ValueError("contiguous cache batch dimension does not match q")
         return Shape(batch, n_heads, G, D, code, 0, int(k_cache.shape[1]), 0, 0)
-    if int(k_cache.shape[1]) != 16:
-        raise ValueError("paged pool must have 16-token blocks")
+    bs = int(k_cache.shape[1])
+    if bs not in (16, 32):
+        raise ValueError("paged pool must have 16- or 32-token blocks")
     if block_table.dim() != 2 or int(block_table.shape[0]) != batch:
         raise ValueError("block_table must be [batch, max_blocks_per_seq]")
     mbps = int(block_table.shape[1])
-    return Shape(batch, n_heads, G, D, code, 16, mbps * 16, int(k_cache.shape[0]), mbps)
+    return Shape(batch, n_heads, G, D, code, bs, mbps * bs, int(k_cache.shape[0]), mbps)
 
 
 def rope_append_kv(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
@@ -279,11 +285,11 @@ def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
 def v_cache_shape_int8(k_cache: torch.Tensor, paged: bool) -> Tuple[int, ...]:
     """Shape of the INT8 V cache that goes with an int8 K cache: per 16-token
     group and head, V transposed ([.., G, D, 16] against K's [.., G, 16, D])."""
-    if paged:
+    if paged and k_cache.dim() == 4:
         nb, G, _, D = (int(x) for x in k_cache.shape)
         return (nb, G, D, 16)
-    B, n, G, _, D = (int(x) for x in k_cache.shape)
-    return (B, n, G, D, 16)
+    a, n, G, _, D = (int(x) for x in k_cache.shape)
+    return (a, n, G, D, 16)
 
 
 def _check_scales(k_scale, v_scale, G, dev):

@@ -60,13 +60,15 @@ kvd_status check_shape(const kvd_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return KVD_EUNSUPPORTED;
   if (s->kv_dtype != KVD_FP32 && s->kv_dtype != KVD_BF16 && s->kv_dtype != KVD_INT8)
     return KVD_EUNSUPPORTED;
-  if (s->block_size != 0 && s->block_size != 16) return KVD_EUNSUPPORTED;
+  if (s->block_size != 0 && s->block_size != 16 && s->block_size != 32) return KVD_EUNSUPPORTED;
   if (s->max_seq_len < 1) return KVD_EINVAL;
   // INT8 V is grouped by 16 tokens: a contiguous capacity of whole groups
   if (s->kv_dtype == KVD_INT8 && s->max_seq_len % 16 != 0) return KVD_EUNSUPPORTED;
-  if (s->block_size == 16) {
+  if (s->block_size != 0) {
     if (s->num_blocks < 1 || s->max_blocks_per_seq < 1) return KVD_EINVAL;
-    if (static_cast<int64_t>(s->max_blocks_per_seq) * 16 != s->max_seq_len) return KVD_EINVAL;
+    if (static_cast<int64_t>(s->max_blocks_per_seq) * s->block_size != s->max_seq_len) return KVD_EINVAL;
+    // the kernels address the pool in 16-token groups
+    if (static_cast<int64_t>(s->num_blocks) * (s->block_size / 16) > 0x7fffffff) return KVD_EINVAL;
   }
   return KVD_OK;
 }
@@ -180,7 +182,7 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   // then sequences, splits slowest (resp. sequences slowest).
   const int64_t list_wgs = static_cast<int64_t>(s->n_kv_heads) * s->batch * pl->n_splits;
   const bool list_ok = kernel >= 1 && pl->n_splits > 1 && list_wgs <= 0x7fffffff;
-  pl->grid_order = s->batch == 1 ? 0 : (list_ok ? 3 : (s->block_size == 16 ? 2 : 1));
+  pl->grid_order = s->batch == 1 ? 0 : (list_ok ? 3 : (s->block_size != 0 ? 2 : 1));
   const int ord = g_order_override.load();
   if (ord >= 0 && ord <= 2) pl->grid_order = ord;
   if (ord == 3 && list_ok) pl->grid_order = 3;   // a single split (or the VALU kernel): no list
@@ -279,7 +281,7 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
   if (q && !q_rot) return KVD_EINVAL;
   if (q && static_cast<const void*>(q_rot) == q) return KVD_EINVAL;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return KVD_EINVAL;
-  const bool paged = shape->block_size == 16;
+  const bool paged = shape->block_size != 0;
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (shape->batch == 0) return KVD_OK;
   RopeParams p;
@@ -289,6 +291,7 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
   p.base = rope_base; p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads;
   p.D = shape->head_dim; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
   if (launch_rope_append(p, shape->kv_dtype, paged, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVD_EHIP;
   return KVD_OK;
@@ -365,7 +368,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
     return KVD_EINVAL;
   if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
   if (!std::isfinite(scale)) return KVD_EINVAL;
-  const bool paged = shape->block_size == 16;
+  const bool paged = shape->block_size != 0;
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
   if (shape->batch == 0) return KVD_OK;
@@ -386,6 +389,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.R = p.H / p.G;
   p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
   p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
   p.qscale = scale * 1.4426950408889634f;

@@ -202,14 +202,12 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   const int last_grp = (t1 - 1) >> 4;         // last group holding a token of the split
   if (PAGED) {
     const int nblk = last_grp - (t0 >> 4) + 1;
-    const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks_per_seq + (t0 >> 4);
 #pragma unroll
     for (int c = 0; c < kBlkRegsI8; ++c) {
       const int i = c * 64 + lane;
       int sb = 16 * (i >> 2) + 4 * wave + (i & 3);
       sb = sb < nblk ? sb : nblk - 1;
-      const int blk = trow[sb];
-      blkv[c] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+      blkv[c] = paged_group(p, b, (t0 >> 4) + sb);
     }
   }
 

@@ -134,14 +134,12 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   int blkv[PAGED ? kBlkRegs : 1];
   if (PAGED) {
     const int nblk = (t1 - t0 + 15) >> 4;
-    const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks_per_seq + (t0 >> 4);
 #pragma unroll
     for (int c = 0; c < kBlkRegs; ++c) {
       const int i = c * 64 + lane;
       int sb = 8 * (i >> 1) + 2 * wave + (i & 1);
       sb = sb < nblk ? sb : nblk - 1;
-      const int blk = trow[sb];
-      blkv[c] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+      blkv[c] = paged_group(p, b, (t0 >> 4) + sb);
     }
   }
   // block ids (wave-uniform) of the two 16-token halves of the wave's tile kt

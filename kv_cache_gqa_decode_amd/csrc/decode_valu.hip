@@ -66,9 +66,9 @@ __device__ __forceinline__ float row_sum(float x) {
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_row(const DecodeParams& p, int b, int t, int g, bool& ok) {
   if (!PAGED) return (static_cast<int64_t>(b) * p.max_seq_len + t) * p.G + g;
-  int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (t >> 4)];
-  if (blk < 0 || blk >= p.num_blocks) { ok = false; blk = 0; }
-  return (static_cast<int64_t>(blk) * 16 + (t & 15)) * p.G + g;
+  int grp = paged_group(p, b, t >> 4);
+  if (grp < 0) { ok = false; grp = 0; }
+  return (static_cast<int64_t>(grp) * 16 + (t & 15)) * p.G + g;
 }
 
 template <typename T, int D, int RB, bool PAGED>

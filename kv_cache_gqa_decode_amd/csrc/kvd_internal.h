@@ -27,6 +27,7 @@ struct DecodeParams {
   int32_t max_len_host;     // lengths are clamped to this
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
+  int32_t block_shift;      // paged: log2(block_size / 16), 0 or 1
   // Splits of a sequence: n_big splits of `chunk` tokens, then splits of
   // `chunk2` tokens (both multiples of 16; n_big == n_splits: all equal).
   // Small last splits keep the units that are dispatched last short.
@@ -60,6 +61,7 @@ struct RopeParams {
   int32_t max_seq_len;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
+  int32_t block_shift;      // paged: log2(block_size / 16), 0 or 1
 };
 
 // Launchers (each returns the hipError_t of its launch).
@@ -93,6 +95,16 @@ __host__ __device__ __forceinline__ int split_size(const DecodeParams& p, int s)
 __host__ __device__ __forceinline__ int split_count(const DecodeParams& p, int L) {
   const int big = p.n_big * p.chunk;
   return L <= big ? (L + p.chunk - 1) / p.chunk : p.n_big + (L - big + p.chunk2 - 1) / p.chunk2;
+}
+
+// Paged caches: the pool's 16-token group that holds token group j (tokens
+// 16j .. 16j+15) of sequence b.  A block of block_size tokens is block_size/16
+// consecutive groups of the pool, so every kernel addresses the pool in
+// 16-token groups.  -1 when the table entry is outside the pool.
+__device__ __forceinline__ int paged_group(const DecodeParams& p, int b, int j) {
+  const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (j >> p.block_shift)];
+  if (blk < 0 || blk >= p.num_blocks) return -1;
+  return (blk << p.block_shift) | (j & ((1 << p.block_shift) - 1));
 }
 
 // bf16 pair in a 32-bit word -> two floats (exact).

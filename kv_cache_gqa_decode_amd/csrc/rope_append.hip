@@ -95,17 +95,20 @@ template <bool PAGED>
 __device__ __forceinline__ int64_t slot_row(const RopeParams& p, int b, int pos, int g) {
   if (pos < 0 || pos >= p.max_seq_len) return -1;
   if (!PAGED) return (static_cast<int64_t>(b) * p.max_seq_len + pos) * p.G + g;
-  const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (pos >> 4)];
+  const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (pos >> (4 + p.block_shift))];
   if (blk < 0 || blk >= p.num_blocks) return -1;
-  return (static_cast<int64_t>(blk) * 16 + (pos & 15)) * p.G + g;
+  // a block of 16 << shift tokens is that many consecutive rows
+  const int64_t tok = (static_cast<int64_t>(blk) << (4 + p.block_shift)) + (pos & ((16 << p.block_shift) - 1));
+  return tok * p.G + g;
 }
 
 // INT8 caches: the 16-token group of a slot whose token-major row is `row`
-// (the physical block, or group pos/16 of sequence b), and the slot's K row
-// in the group-major layout.
+// (paged: group row/G/16 of the pool, a block being block_size/16 groups;
+// contiguous: group pos/16 of sequence b), and the slot's K row in the
+// group-major layout.
 template <bool PAGED>
 __device__ __forceinline__ int64_t i8_group(const RopeParams& p, int b, int pos, int64_t row) {
-  return PAGED ? row / (16 * p.G) : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (pos >> 4);
+  return PAGED ? (row / p.G) >> 4 : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (pos >> 4);
 }
 template <bool PAGED>
 __device__ __forceinline__ int64_t i8_krow(const RopeParams& p, int b, int pos, int g, int64_t row) {

@@ -212,7 +212,7 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
     v_new = _rng(s, 3).standard_normal((B, G, D), dtype=np.float32) * sc
     store = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[s.dtype]
     i8 = s.dtype == "i8"
-    if i8 and (s.max_seq_len % 16 or s.block_size not in (0, 16)):
+    if i8 and (s.max_seq_len % 16 or s.block_size % 16):
         raise ValueError("INT8 caches group tokens by 16")
     fill = _fill_value(s)
     table = None
@@ -223,9 +223,12 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
         perm = _rng(s, 4).permutation(s.num_blocks).astype(np.int32)
         table = np.ascontiguousarray(
             perm[: B * s.max_blocks_per_seq].reshape(B, s.max_blocks_per_seq))
-        k_cache = np.full((s.num_blocks, G, bs, D) if i8 else (s.num_blocks, bs, G, D), fill,
+        m = bs // 16
+        gk = (G, 16, D) if m == 1 else (m, G, 16, D)
+        gv = (G, D, 16) if m == 1 else (m, G, D, 16)
+        k_cache = np.full((s.num_blocks, *gk) if i8 else (s.num_blocks, bs, G, D), fill,
                           dtype=store)
-        v_cache = np.full((s.num_blocks, G, D, bs) if i8 else (s.num_blocks, bs, G, D), fill,
+        v_cache = np.full((s.num_blocks, *gv) if i8 else (s.num_blocks, bs, G, D), fill,
                           dtype=store)
         for b in range(B):
             n_hist = int(L[b]) - 1
@@ -238,8 +241,12 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
                 kh = np.concatenate([kh, np.full((pad, G, D), fill, store)])
                 vh = np.concatenate([vh, np.full((pad, G, D), fill, store)])
             ids = table[b, :nblk]
-            k_cache[ids] = group_rows(kh) if i8 else kh.reshape(nblk, bs, G, D)
-            v_cache[ids] = group_transpose(vh) if i8 else vh.reshape(nblk, bs, G, D)
+            if i8:
+                k_cache[ids] = group_rows(kh).reshape(nblk, *gk)
+                v_cache[ids] = group_transpose(vh).reshape(nblk, *gv)
+            else:
+                k_cache[ids] = kh.reshape(nblk, bs, G, D)
+                v_cache[ids] = vh.reshape(nblk, bs, G, D)
     else:
         S = s.max_seq_len
         k_cache = np.full((B, S // 16, G, 16, D) if i8 else (B, S, G, D), fill, dtype=store)

@@ -125,7 +125,8 @@ class Geometry:
     ``[B, max_blocks_per_seq]`` ([OPT] §四 PagedKVCache; [KVGR] §4.1).
     INT8 caches are grouped by 16 tokens, per head: K ``[B, S_max/16, G, 16, D]``
     or ``[num_blocks, G, 16, D]``, V ``[B, S_max/16, G, D, 16]`` or
-    ``[num_blocks, G, D, 16]``.
+    ``[num_blocks, G, D, 16]``; 32-token blocks hold two groups
+    (``[num_blocks, 2, G, 16, D]``, ``[num_blocks, 2, G, D, 16]``).
     """
 
     def __init__(self, batch, n_heads, n_kv_heads, head_dim, dtype="bf16",
@@ -139,7 +140,7 @@ class Geometry:
         if block_size:
             max_seq_len = max_blocks_per_seq * block_size
         self.max_seq_len = max_seq_len
-        if dtype == "i8" and (max_seq_len % 16 or block_size not in (0, 16)):
+        if dtype == "i8" and (max_seq_len % 16 or block_size % 16):
             raise ValueError("INT8 caches group tokens by 16")
 
     @property
@@ -160,8 +161,11 @@ class Geometry:
         """Shape of the K cache (and of V, except for INT8)."""
         G, D = self.n_kv_heads, self.head_dim
         if self.dtype == "i8":
-            if self.block_size:
+            m = self.block_size // 16
+            if m == 1:
                 return (self.num_blocks, G, 16, D)
+            if m > 1:
+                return (self.num_blocks, m, G, 16, D)
             return (self.batch, self.max_seq_len // 16, G, 16, D)
         if self.block_size:
             return (self.num_blocks, self.block_size, G, D)
@@ -171,8 +175,11 @@ class Geometry:
         if self.dtype != "i8":
             return self.cache_shape()
         G, D = self.n_kv_heads, self.head_dim
-        if self.block_size:
+        m = self.block_size // 16
+        if m == 1:
             return (self.num_blocks, G, D, 16)
+        if m > 1:
+            return (self.num_blocks, m, G, D, 16)
         return (self.batch, self.max_seq_len // 16, G, D, 16)
 
     def _c(self):

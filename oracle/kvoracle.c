@@ -42,8 +42,10 @@
  * value is scale[g] * n, with one fp32 scale per KV head for K and one for
  * V.  A new element x is stored as the code nearest to x / scale (ties to
  * even; x is the exact rotated key, or v_new as given).  Layout: tokens are
- * grouped by 16 (contiguous: group r = b * S_max/16 + pos/16; paged: the
- * physical block), and each group holds, per KV head, the 16 K rows
+ * grouped by 16 (contiguous: group r = b * S_max/16 + pos/16; paged: group
+ * (block * block_size + pos % block_size) / 16 of the pool, a block being
+ * block_size / 16 consecutive groups), and each group holds, per KV head,
+ * the 16 K rows
  * ([G][16][D]: element (pos, g, d) at ((r * G + g) * 16 + pos % 16) * D + d)
  * and the V block transposed ([G][D][16]: at ((r * G + g) * D + d) * 16 +
  * pos % 16).
@@ -181,7 +183,8 @@ static int64_t cache_row(const kvo_shape* sh, const int32_t* table, int b, int64
 static int64_t i8_group(const kvo_shape* sh, int b, int64_t pos, int64_t row) {
   if (row < 0) return -1;
   if (sh->block_size == 0) return (int64_t)b * (sh->max_seq_len / 16) + pos / 16;
-  return row / ((int64_t)sh->block_size * sh->n_kv_heads);   /* physical block */
+  /* a physical block of block_size tokens is block_size / 16 groups */
+  return (row / sh->n_kv_heads) / 16;
 }
 
 /* INT8 K element (pos, g, d): group-major, the head's 16 rows together */

@@ -68,7 +68,10 @@ def test_attn_rejects_bad_arguments(lib):
     assert attn(lib, shape(head_dim=96)) == EUNSUPPORTED
     assert attn(lib, shape(head_dim=63)) == EUNSUPPORTED
     assert attn(lib, shape(kv_dtype=7)) == EUNSUPPORTED
-    assert attn(lib, shape(block_size=32)) == EUNSUPPORTED
+    assert attn(lib, shape(block_size=64)) == EUNSUPPORTED
+    assert attn(lib, shape(block_size=8)) == EUNSUPPORTED
+    assert attn(lib, shape(block_size=32, max_seq_len=64, num_blocks=10,
+                           max_blocks_per_seq=4), table=FAKE) == EINVAL  # 64 != 4 * 32
     assert attn(lib, shape(batch=-1)) == EINVAL
     assert attn(lib, shape(max_seq_len=0)) == EINVAL
     assert attn(lib, shape(), q=None) == EINVAL

@@ -17,6 +17,7 @@ from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
 from tests.gpu_helpers import device, gpu_step, oracle_step, upload
 from tests.test_gpu_full import sample_units
+from tests.test_gpu_parity import shared_prefix
 
 pytestmark = pytest.mark.gpu
 
@@ -71,9 +72,20 @@ def test_varlen_contiguous(split):
 
 
 @pytest.mark.parametrize("split", [0, 16, 48, 256])
-def test_paged_small(split):
-    s = i8("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
-    check_full(W.make_problem(s, lengths=RAGGED), split=split, what=f"int8 paged split={split}")
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_paged_small(split, block_size):
+    s = i8("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+           max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
+    check_full(W.make_problem(s, lengths=RAGGED), split=split,
+               what=f"int8 paged{block_size} split={split}")
+
+
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_shared_prefix_blocks(block_size):
+    s = i8("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+           max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
+    p = shared_prefix(W.make_problem(s, lengths=RAGGED), 128 // block_size)
+    check_full(p, split=48, what=f"int8 shared prefix {block_size}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -87,11 +99,13 @@ def test_gqa_ratios(D, n_rep):
 
 
 @pytest.mark.parametrize("split", [0, 32])
-def test_paged_equals_contiguous_bitwise(split):
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_paged_equals_contiguous_bitwise(split, block_size):
     dev = device()
     kvd.set_tuning(None, split)
     L = np.array([5, 16, 333, 1024, 700], np.int32)
-    sp = i8("c4", batch=5, num_blocks=500, max_blocks_per_seq=64)
+    sp = i8("c4", batch=5, num_blocks=8000 // block_size, max_blocks_per_seq=1024 // block_size,
+            block_size=block_size)
     sc = i8("c3", batch=5, max_seq_len=1024).replace(cfg_id=sp.cfg_id)
     res = []
     for s in (sp, sc):

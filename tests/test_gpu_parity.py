@@ -7,6 +7,8 @@ relative; the cache append bit-exact.  Small cases compare every element;
 full-size workloads compare sampled (b, h) rows (the oracle computes them
 one by one) plus every appended cache row.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -78,10 +80,35 @@ def test_varlen_contiguous(dtype, kernel, split):
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 16, 48, 256])
-def test_paged_small(kernel, split):
-    s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_paged_small(kernel, split, block_size):
+    s = W.spec("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+               max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
     p = W.make_problem(s, lengths=RAGGED)
-    check_full(p, kernel=kernel, split=split, what=f"paged {kernel} split={split}")
+    check_full(p, kernel=kernel, split=split, what=f"paged{block_size} {kernel} split={split}")
+
+
+def shared_prefix(p: W.Problem, n_shared: int) -> W.Problem:
+    """The rows of every sequence whose append lands past the first n_shared
+    blocks start with the first n_shared blocks of the longest sequence (a
+    shared prompt prefix, read only: appends stay in private blocks)."""
+    t = p.block_table.copy()
+    src = int(np.argmax(p.positions))
+    share = p.positions // p.spec.block_size >= n_shared
+    share[src] = False
+    t[share, :n_shared] = t[src, :n_shared]
+    assert share.sum() >= 2
+    return dataclasses.replace(p, block_table=t)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("split", [0, 48])
+def test_shared_prefix_blocks(kernel, block_size, split):
+    s = W.spec("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+               max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
+    p = shared_prefix(W.make_problem(s, lengths=RAGGED), 128 // block_size)
+    check_full(p, kernel=kernel, split=split, what=f"shared prefix {block_size} {kernel}")
 
 
 def test_auto_plan_picks_matrix_cores_for_bf16():
@@ -98,12 +125,14 @@ def test_auto_plan_picks_matrix_cores_for_bf16():
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split", [0, 32])
-def test_paged_equals_contiguous_bitwise(kernel, split):
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_paged_equals_contiguous_bitwise(kernel, split, block_size):
     """The same logical cache, paged or contiguous, gives identical bits."""
     dev = device()
     kvd.set_tuning(kernel, split)
     L = np.array([5, 16, 333, 1024, 700], np.int32)
-    sp = W.spec("c4", batch=5, num_blocks=500, max_blocks_per_seq=64)
+    sp = W.spec("c4", batch=5, num_blocks=8000 // block_size, max_blocks_per_seq=1024 // block_size,
+                block_size=block_size)
     sc = W.spec("c3", batch=5, max_seq_len=1024).replace(cfg_id=sp.cfg_id)
     res = []
     for s in (sp, sc):

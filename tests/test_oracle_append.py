@@ -19,10 +19,12 @@ def _geom(s):
                            num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
 
 
-def _small(dtype="bf16", paged=False, G=2, poison=True):
+def _small(dtype="bf16", paged=False, G=2, poison=True, block_size=16):
     if paged:
+        nb = 640 // block_size
         return W.spec("c4", batch=3, n_heads=4, n_kv_heads=G, head_dim=64, len_lo=1,
-                      len_hi=70, num_blocks=40, max_blocks_per_seq=8, poison=poison)
+                      len_hi=70, num_blocks=nb, max_blocks_per_seq=128 // block_size,
+                      block_size=block_size, poison=poison)
     s = W.spec("c3", batch=3, n_heads=4, n_kv_heads=G, head_dim=64, len_lo=1, len_hi=70,
                max_seq_len=80, poison=poison)
     return s.replace(dtype=dtype)
@@ -92,12 +94,13 @@ def test_stored_k_is_rotation_rounded_once(dtype):
         assert (np.abs(stored - exact) <= 0.5 * ulp).all()
 
 
-def test_paged_gather_equals_contiguous():
+@pytest.mark.parametrize("block_size", [16, 32])
+def test_paged_gather_equals_contiguous(block_size):
     """Gathering the paged pool through the table (the concatenation of a
     sequence's blocks) reproduces the contiguous cache, before and after the
-    append."""
+    append, for 16- and 32-token blocks."""
     G = 2
-    sp = _small("bf16", paged=True, G=G)
+    sp = _small("bf16", paged=True, G=G, block_size=block_size)
     sc = _small("bf16", paged=False, G=G).replace(cfg_id=sp.cfg_id, max_seq_len=128)
     L = np.array([3, 16, 70], np.int32)
     pp = W.make_problem(sp, lengths=L)
