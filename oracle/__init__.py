@@ -87,6 +87,16 @@ def _load():
         lib.kvo_decode_attn_units_i8.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P, P,
                                                  P, ctypes.c_double, P, P, ctypes.c_int64,
                                                  P, P, ctypes.c_int]
+        lib.kvo_rope_append_mq.restype = ctypes.c_int
+        lib.kvo_rope_append_mq.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P, P, P,
+                                           P, P, P, P, P, ctypes.c_double, ctypes.c_int]
+        lib.kvo_decode_attn_mq.restype = ctypes.c_int
+        lib.kvo_decode_attn_mq.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P, P, P,
+                                           P, P, ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.kvo_decode_attn_units_mq.restype = ctypes.c_int
+        lib.kvo_decode_attn_units_mq.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P,
+                                                 P, P, P, P, ctypes.c_double, P, P,
+                                                 ctypes.c_int64, P, P, ctypes.c_int]
         lib.kvo_decode_attn.restype = ctypes.c_int
         lib.kvo_decode_attn.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P,
                                         ctypes.c_double, P, P, P, ctypes.c_int]
@@ -232,28 +242,38 @@ def rope_rotate(x, pos, base=10000.0, style="interleaved"):
 
 def rope_append(geom: Geometry, q, k_new, v_new, k_cache, v_cache, positions,
                 block_table=None, base=10000.0, style="interleaved", k_scale=None,
-                v_scale=None):
+                v_scale=None, n_query=1):
     """Rotate q and k_new at positions[b] and write k_rot, v_new into the caches.
 
     The caches are modified in place.  Returns q_rot [B, H, D] fp64.
     INT8 caches take the per-head scales ``k_scale``, ``v_scale`` ([G] fp32).
+    With ``n_query`` = T > 1 each sequence brings T new tokens (q [B, T, H, D],
+    k_new / v_new [B, T, G, D]) for slots positions[b] .. positions[b] + T - 1
+    ([OPT] §五, the verification pass); q_rot is then [B, T, H, D].
     Raises ValueError if a position or block id does not exist.
     """
     B, H, G, D = geom.batch, geom.n_heads, geom.n_kv_heads, geom.head_dim
+    T = int(n_query)
     st, ist = geom.storage, geom.input_storage
+    lead = (B,) if T == 1 else (B, T)
     if q is not None:
-        _need(q, ist, "q", (B, H, D))
-    _need(k_new, ist, "k_new", (B, G, D))
-    _need(v_new, ist, "v_new", (B, G, D))
+        _need(q, ist, "q", (*lead, H, D))
+    _need(k_new, ist, "k_new", (*lead, G, D))
+    _need(v_new, ist, "v_new", (*lead, G, D))
     _need(k_cache, st, "k_cache", geom.cache_shape())
     _need(v_cache, st, "v_cache", geom.v_cache_shape())
     _need(positions, np.int32, "positions", (B,))
     if geom.block_size:
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
     ks, vs = _scales(geom, k_scale, v_scale)
-    q_rot = np.zeros((B, H, D), np.float64)
+    q_rot = np.zeros((*lead, H, D), np.float64)
     sh = geom._c()
-    if geom.dtype == "i8":
+    if T > 1:
+        rc = _load().kvo_rope_append_mq(ctypes.byref(sh), T, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        _ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(ks),
+                                        _ptr(vs), _ptr(positions), _ptr(block_table),
+                                        float(base), _STYLE_CODE[style])
+    elif geom.dtype == "i8":
         rc = _load().kvo_rope_append_i8(ctypes.byref(sh), _ptr(q), _ptr(k_new), _ptr(v_new),
                                         _ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(ks),
                                         _ptr(vs), _ptr(positions), _ptr(block_table),
@@ -269,15 +289,20 @@ def rope_append(geom: Geometry, q, k_new, v_new, k_cache, v_cache, positions,
 
 
 def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=None,
-                scale=None, want_probs=False, n_threads=None, k_scale=None, v_scale=None):
+                scale=None, want_probs=False, n_threads=None, k_scale=None, v_scale=None,
+                n_query=1):
     """fp64 attention of every (b, h) query over its first seq_lens[b] tokens.
 
     Returns (out [B,H,D], lse [B,H]) and, with want_probs, the weights
     [B, H, max_seq_len] (zero past seq_lens[b]).  INT8 caches take their
-    per-head scales.
+    per-head scales.  With ``n_query`` = T > 1, q_rot is [B, T, H, D] and
+    query t of sequence b attends the tokens j < seq_lens[b] - T + 1 + t;
+    out is [B, T, H, D], lse [B, T, H].
     """
     B, H, D = geom.batch, geom.n_heads, geom.head_dim
-    _need(q_rot, np.float64, "q_rot", (B, H, D))
+    T = int(n_query)
+    lead = (B,) if T == 1 else (B, T)
+    _need(q_rot, np.float64, "q_rot", (*lead, H, D))
     _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
     _need(v_cache, geom.storage, "v_cache", geom.v_cache_shape())
     ks, vs = _scales(geom, k_scale, v_scale)
@@ -286,11 +311,11 @@ def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=N
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
     if scale is None:
         scale = 1.0 / np.sqrt(D)  # default 1/sqrt(d_k), d_k = per-head dim ([KVGR] §2.1)
-    out = np.zeros((B, H, D), np.float64)
-    lse = np.zeros((B, H), np.float64)
-    probs = np.zeros((B, H, geom.max_seq_len), np.float64) if want_probs else None
+    out = np.zeros((*lead, H, D), np.float64)
+    lse = np.zeros((*lead, H), np.float64)
+    probs = np.zeros((*lead, H, geom.max_seq_len), np.float64) if want_probs else None
     sh = geom._c()
-    rc = _load().kvo_decode_attn_i8(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
+    rc = _load().kvo_decode_attn_mq(ctypes.byref(sh), T, _ptr(q_rot), _ptr(k_cache),
                                     _ptr(v_cache), _ptr(ks), _ptr(vs), _ptr(seq_lens),
                                     _ptr(block_table), float(scale), _ptr(out), _ptr(lse),
                                     _ptr(probs), n_threads or default_threads())
@@ -301,28 +326,39 @@ def decode_attn(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, block_table=N
 
 def decode_attn_units(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, units,
                       block_table=None, scale=None, n_threads=None, k_scale=None,
-                      v_scale=None):
-    """As decode_attn, for the listed (b, h) pairs only: returns out [n, D], lse [n]."""
+                      v_scale=None, n_query=1):
+    """As decode_attn, for the listed (b, h) pairs (T > 1: (b, t, h) triples)
+    only: returns out [n, D], lse [n]."""
     B, H, D = geom.batch, geom.n_heads, geom.head_dim
-    _need(q_rot, np.float64, "q_rot", (B, H, D))
+    T = int(n_query)
+    lead = (B,) if T == 1 else (B, T)
+    _need(q_rot, np.float64, "q_rot", (*lead, H, D))
     _need(k_cache, geom.storage, "k_cache", geom.cache_shape())
     _need(v_cache, geom.storage, "v_cache", geom.v_cache_shape())
     ks, vs = _scales(geom, k_scale, v_scale)
     _need(seq_lens, np.int32, "seq_lens", (B,))
     if geom.block_size:
         _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
-    units = np.asarray(units, dtype=np.int32).reshape(-1, 2)
-    ub = np.ascontiguousarray(units[:, 0])
-    uh = np.ascontiguousarray(units[:, 1])
-    if ((ub < 0) | (ub >= B) | (uh < 0) | (uh >= H)).any():
-        raise ValueError("unit out of range")
+    if T == 1:
+        units = np.asarray(units, dtype=np.int32).reshape(-1, 2)
+        ub = np.ascontiguousarray(units[:, 0])
+        uh = np.ascontiguousarray(units[:, 1])
+        if ((ub < 0) | (ub >= B) | (uh < 0) | (uh >= H)).any():
+            raise ValueError("unit out of range")
+    else:
+        units = np.asarray(units, dtype=np.int32).reshape(-1, 3)
+        if ((units[:, 0] < 0) | (units[:, 0] >= B) | (units[:, 1] < 0) | (units[:, 1] >= T) |
+                (units[:, 2] < 0) | (units[:, 2] >= H)).any():
+            raise ValueError("unit out of range")
+        ub = np.ascontiguousarray(units[:, 0])
+        uh = np.ascontiguousarray(units[:, 1] * H + units[:, 2])
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     n = units.shape[0]
     out = np.zeros((n, D), np.float64)
     lse = np.zeros((n,), np.float64)
     sh = geom._c()
-    rc = _load().kvo_decode_attn_units_i8(ctypes.byref(sh), _ptr(q_rot), _ptr(k_cache),
+    rc = _load().kvo_decode_attn_units_mq(ctypes.byref(sh), T, _ptr(q_rot), _ptr(k_cache),
                                           _ptr(v_cache), _ptr(ks), _ptr(vs), _ptr(seq_lens),
                                           _ptr(block_table), float(scale), _ptr(ub), _ptr(uh),
                                           n, _ptr(out), _ptr(lse),

@@ -32,6 +32,13 @@
  *   5. s_j = scale * <q_rot, K_j> for j < L (the causal bound of one query at
  *      the last position), textbook two-pass softmax, o = sum_j p_j V_j,
  *      lse = m + ln(sum_j e_j)         [KVGR] §2.1; [SA4] §4.1, §4.5.
+ *   6. Several new tokens per step (the *_mq functions, T = n_query): the
+ *      verification pass of speculative decoding, where the target model
+ *      processes the gamma draft tokens in one forward ([OPT] §五).  The T
+ *      new tokens of sequence b sit at positions P_b .. P_b + T - 1 and are
+ *      all appended; query t attends the tokens j <= P_b + t, i.e. j < L_b -
+ *      T + 1 + t with L_b = P_b + T (the causal mask inside the window,
+ *      [KVGR] §5.1 b.v).  T = 1 is the single-token step above.
  *
  * Storage dtypes: KVO_F64 (used by the pins' exact decode loop), KVO_F32 and
  * KVO_BF16 (raw 16-bit patterns; value = bits << 16 read as an IEEE float).
@@ -208,38 +215,41 @@ static int64_t vt_index(const kvo_shape* sh, int b, int64_t pos, int g, int d, i
  * k_scale/v_scale: [G] per-head scales of an INT8 cache (NULL otherwise).
  * Returns 0, or -1 when a position or block id is out of range (that
  * sequence's append is then skipped). */
-static int rope_append_impl(const kvo_shape* sh, const void* q, const void* k_new,
+static int rope_append_impl(const kvo_shape* sh, int T, const void* q, const void* k_new,
                             const void* v_new, double* q_rot, void* k_cache,
                             void* v_cache, const float* k_scale, const float* v_scale,
                             const int32_t* positions, const int32_t* block_table,
                             double base, int style) {
-  const int B = sh->batch, H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
+  const int H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
   const int in_dt = input_dtype(sh->dtype);
   int rc = 0;
   double* x = (double*)malloc(sizeof(double) * D);
   double* y = (double*)malloc(sizeof(double) * D);
-  for (int b = 0; b < B; ++b) {
-    double pos = (double)positions[b];
+  /* row bt = b * T + t holds new token t of sequence b, at position P_b + t */
+  for (int bt = 0; bt < sh->batch * T; ++bt) {
+    const int b = bt / T;
+    const int64_t slot = (int64_t)positions[b] + bt % T;
+    double pos = (double)slot;
     if (q != NULL) {
       for (int h = 0; h < H; ++h) {
-        int64_t base_i = ((int64_t)b * H + h) * D;
+        int64_t base_i = ((int64_t)bt * H + h) * D;
         for (int d = 0; d < D; ++d) x[d] = load_elem(q, in_dt, base_i + d);
         kvo_rope_rotate(x, y, D, pos, base, style);
         for (int d = 0; d < D; ++d) q_rot[base_i + d] = y[d];
       }
     }
     for (int g = 0; g < G; ++g) {
-      int64_t row = cache_row(sh, block_table, b, positions[b], g);
+      int64_t row = cache_row(sh, block_table, b, slot, g);
       if (row < 0) { rc = -1; continue; }
-      int64_t src = ((int64_t)b * G + g) * D;
+      int64_t src = ((int64_t)bt * G + g) * D;
       for (int d = 0; d < D; ++d) x[d] = load_elem(k_new, in_dt, src + d);
       kvo_rope_rotate(x, y, D, pos, base, style);
       for (int d = 0; d < D; ++d) {
         if (sh->dtype == KVO_I8) {
           /* codes of the exact rotated key and of v_new ([KVGR] §4.3) */
-          ((int8_t*)k_cache)[kq_index(sh, b, positions[b], g, d, row)] =
+          ((int8_t*)k_cache)[kq_index(sh, b, slot, g, d, row)] =
               (int8_t)kvo_quantize_i8(y[d], k_scale[g]);
-          ((int8_t*)v_cache)[vt_index(sh, b, positions[b], g, d, row)] =
+          ((int8_t*)v_cache)[vt_index(sh, b, slot, g, d, row)] =
               (int8_t)kvo_quantize_i8(load_elem(v_new, in_dt, src + d), v_scale[g]);
         } else {
           store_elem(k_cache, sh->dtype, row * D + d, y[d]);
@@ -258,7 +268,7 @@ int kvo_rope_append(const kvo_shape* sh, const void* q, const void* k_new,
                     void* v_cache, const int32_t* positions,
                     const int32_t* block_table, double base, int style) {
   if (sh->dtype == KVO_I8) return -2;   /* needs the scales */
-  return rope_append_impl(sh, q, k_new, v_new, q_rot, k_cache, v_cache, NULL, NULL,
+  return rope_append_impl(sh, 1, q, k_new, v_new, q_rot, k_cache, v_cache, NULL, NULL,
                           positions, block_table, base, style);
 }
 
@@ -269,7 +279,19 @@ int kvo_rope_append_i8(const kvo_shape* sh, const void* q, const void* k_new,
                        const int32_t* positions, const int32_t* block_table,
                        double base, int style) {
   if (sh->dtype != KVO_I8) return -2;
-  return rope_append_impl(sh, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+  return rope_append_impl(sh, 1, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+                          positions, block_table, base, style);
+}
+
+/* T new tokens per sequence (q [B,T,H,D], k_new/v_new [B,T,G,D], q_rot
+ * [B,T,H,D]); token t of sequence b goes to slot positions[b] + t.  Scales
+ * only for an INT8 cache. */
+int kvo_rope_append_mq(const kvo_shape* sh, int T, const void* q, const void* k_new,
+                       const void* v_new, double* q_rot, void* k_cache, void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* positions,
+                       const int32_t* block_table, double base, int style) {
+  if (T < 1 || (sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
+  return rope_append_impl(sh, T, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
                           positions, block_table, base, style);
 }
 
@@ -285,8 +307,9 @@ typedef struct {
   double scale;
   const float* k_scale;    /* INT8 caches: [G] per-head scales */
   const float* v_scale;
-  const int32_t* unit_b;   /* NULL: unit u is (u / H, u % H) */
-  const int32_t* unit_h;
+  int n_query;             /* T new tokens (queries) per sequence */
+  const int32_t* unit_b;   /* NULL: unit u is (u / (T H), u % (T H)) */
+  const int32_t* unit_h;   /* query row t * H + h of its sequence */
   int64_t n_units;
   double* out;             /* [n_units, D] */
   double* lse;             /* [n_units] or NULL */
@@ -318,14 +341,17 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
   const kvo_shape* sh = job->sh;
   const int H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
   const int n_rep = H / G;
-  int b = job->unit_b ? job->unit_b[u] : (int)(u / H);
-  int h = job->unit_h ? job->unit_h[u] : (int)(u % H);
+  const int T = job->n_query, TH = T * H;
+  int b = job->unit_b ? job->unit_b[u] : (int)(u / TH);
+  int th = job->unit_h ? job->unit_h[u] : (int)(u % TH);
+  int t = th / H, h = th % H;
   int g = h / n_rep;
   int64_t L = job->seq_lens[b];
-  const double* q = job->q_rot + ((int64_t)b * H + h) * D;
+  const double* q = job->q_rot + ((int64_t)b * TH + th) * D;
   double* o = job->out + u * D;
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (L > sh->max_seq_len) { job->bad = 1; L = sh->max_seq_len; }
+  L = L - T + 1 + t;                 /* query t sees the tokens up to its own */
   if (L <= 0) {
     if (job->lse) job->lse[u] = -INFINITY;
     return;
@@ -391,19 +417,27 @@ static int run_attn(attn_job* job, int n_threads) {
 /* Every (b, h): out [B,H,D], lse [B,H] (may be NULL), probs [B,H,max_seq_len]
  * (may be NULL).  seq_lens[b] tokens are attended.  k_scale/v_scale: the
  * per-head scales of an INT8 cache (NULL for the other dtypes). */
+int kvo_decode_attn_mq(const kvo_shape* sh, int T, const double* q_rot, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* seq_lens, const int32_t* block_table, double scale,
+                       double* out, double* lse, double* probs, int n_threads) {
+  if (T < 1 || (sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
+  attn_job job;
+  memset(&job, 0, sizeof job);
+  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
+  job.k_scale = k_scale; job.v_scale = v_scale; job.n_query = T;
+  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
+  job.n_units = (int64_t)sh->batch * T * sh->n_heads;
+  job.out = out; job.lse = lse; job.probs = probs;
+  return run_attn(&job, n_threads);
+}
+
 int kvo_decode_attn_i8(const kvo_shape* sh, const double* q_rot, const void* k_cache,
                        const void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* seq_lens, const int32_t* block_table, double scale,
                        double* out, double* lse, double* probs, int n_threads) {
-  if ((sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
-  attn_job job;
-  memset(&job, 0, sizeof job);
-  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
-  job.k_scale = k_scale; job.v_scale = v_scale;
-  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
-  job.n_units = (int64_t)sh->batch * sh->n_heads;
-  job.out = out; job.lse = lse; job.probs = probs;
-  return run_attn(&job, n_threads);
+  return kvo_decode_attn_mq(sh, 1, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens,
+                            block_table, scale, out, lse, probs, n_threads);
 }
 
 int kvo_decode_attn(const kvo_shape* sh, const double* q_rot, const void* k_cache,
@@ -415,6 +449,24 @@ int kvo_decode_attn(const kvo_shape* sh, const double* q_rot, const void* k_cach
 }
 
 /* Only the listed (unit_b[u], unit_h[u]) pairs: out [n, D], lse [n]. */
+int kvo_decode_attn_units_mq(const kvo_shape* sh, int T, const double* q_rot,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* seq_lens, const int32_t* block_table,
+                             double scale, const int32_t* unit_b,
+                             const int32_t* unit_h, int64_t n_units, double* out,
+                             double* lse, int n_threads) {
+  if (T < 1 || (sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
+  attn_job job;
+  memset(&job, 0, sizeof job);
+  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
+  job.k_scale = k_scale; job.v_scale = v_scale; job.n_query = T;
+  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
+  job.unit_b = unit_b; job.unit_h = unit_h; job.n_units = n_units;
+  job.out = out; job.lse = lse;
+  return run_attn(&job, n_threads);
+}
+
 int kvo_decode_attn_units_i8(const kvo_shape* sh, const double* q_rot,
                              const void* k_cache, const void* v_cache,
                              const float* k_scale, const float* v_scale,
@@ -422,15 +474,9 @@ int kvo_decode_attn_units_i8(const kvo_shape* sh, const double* q_rot,
                              double scale, const int32_t* unit_b,
                              const int32_t* unit_h, int64_t n_units, double* out,
                              double* lse, int n_threads) {
-  if ((sh->dtype == KVO_I8) != (k_scale != NULL && v_scale != NULL)) return -2;
-  attn_job job;
-  memset(&job, 0, sizeof job);
-  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
-  job.k_scale = k_scale; job.v_scale = v_scale;
-  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
-  job.unit_b = unit_b; job.unit_h = unit_h; job.n_units = n_units;
-  job.out = out; job.lse = lse;
-  return run_attn(&job, n_threads);
+  return kvo_decode_attn_units_mq(sh, 1, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens,
+                                  block_table, scale, unit_b, unit_h, n_units, out, lse,
+                                  n_threads);
 }
 
 int kvo_decode_attn_units(const kvo_shape* sh, const double* q_rot,
