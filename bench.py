@@ -22,8 +22,13 @@ With --kv int8 the same workload runs on an INT8 cache (per-KV-head
 scales, rope_append_kv_int8 + gqa_decode_attn_int8); KV bytes then count one
 byte per element.
 
+With --n-query T each sequence brings T new tokens (the verification pass of
+speculative decoding: rope_append_kv_multi + gqa_decode_attn_multi); the KV
+bytes are unchanged (the T queries of a KV head share each tile), the step
+processes B * T tokens.
+
 Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
-                       [--kv-heads G] [--kv native|int8]
+                       [--kv-heads G] [--kv native|int8] [--n-query T]
                        [--kernel auto|valu|mfma] [--split N]
                        [--no-cpu-baseline] [--flush]
 """
@@ -63,7 +68,8 @@ def workload_name(s) -> str:
     name = {"c1": "c1 fp32 single step B1 H8 G2 D64 L256",
             "c2": "c2 bf16 Llama-3-8B-shaped B1 H32 G8 D128 L1024",
             "c3": "c3 bf16 batched varlen B64 H32 G8 D128 L~U[512,8192]",
-            "c4": "c4 bf16 paged(16) B32 H32 G8 D128 L~U[1024,32768] pool 65536 blocks",
+            "c4": f"c4 bf16 paged({s.block_size}) B32 H32 G8 D128 L~U[1024,32768] pool "
+                  f"{s.num_blocks} blocks",
             "c5": f"c5 bf16 long context B1 H32 G{s.n_kv_heads} D128 L131072"}[s.name]
     if s.dtype == "i8":
         name = name.replace(" bf16 ", " INT8-KV (bf16 q, per-head scales) ", 1)
@@ -127,13 +133,16 @@ def cpu_baseline(s, p, budget_s: float):
                             num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
 
     sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if s.dtype == "i8" else {}
+    T = p.n_query
+    if T > 1:
+        sc["n_query"] = T
 
     def run(n):
         idx = np.arange(n)
         kc, vc = p.k_cache, p.v_cache          # the oracle writes only the appended slots
         if s.block_size:
             g = oracle.Geometry(n, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
-                                block_size=16, num_blocks=s.num_blocks,
+                                block_size=s.block_size, num_blocks=s.num_blocks,
                                 max_blocks_per_seq=s.max_blocks_per_seq)
             tab = np.ascontiguousarray(p.block_table[idx])
         else:
@@ -164,7 +173,8 @@ def cpu_baseline(s, p, budget_s: float):
     dt = float(sorted(reps)[len(reps) // 2])
     kvb = sizing.decode_kv_read_bytes(lens, s.n_kv_heads, s.head_dim, s.elem_bytes)
     return {"value": kvb / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {s.batch} sequences, all {s.n_heads} heads, one step "
+            "sample": f"first {n} of {s.batch} sequences, all {s.n_heads} heads, "
+                      f"{T} new token{'s' if T > 1 else ''} each, one step "
                       f"(RoPE + append + attention), median of {len(reps)} runs: {dt:.3f} s, "
                       f"{n / dt:.3g} seq-steps/s"}
 
@@ -176,8 +186,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--kv-heads", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None, choices=[16, 32],
+                    help="paged workload (c4) with 16- or 32-token blocks (same pool bytes)")
     ap.add_argument("--kv", default="native", choices=["native", "int8"],
                     help="cache dtype: the workload's own (bf16 / fp32) or INT8 with per-head scales")
+    ap.add_argument("--n-query", type=int, default=1,
+                    help="new tokens per sequence (T > 1: the multi-token verification step)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--tail-split", type=int, default=0,
@@ -223,13 +237,21 @@ def main():
         print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd)}))
         return
     s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
+    if args.block_size is not None:
+        if not s.block_size:
+            print("--block-size applies to the paged workload (c4)", file=sys.stderr)
+            sys.exit(2)
+        s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False, block_size=args.block_size,
+                   num_blocks=s.num_blocks * s.block_size // args.block_size,
+                   max_blocks_per_seq=s.max_blocks_per_seq * s.block_size // args.block_size)
     if args.kv == "int8":
         if s.dtype != "bf16":
             print("--kv int8 applies to the bf16 workloads (c2..c5)", file=sys.stderr)
             sys.exit(2)
         s = s.replace(dtype="i8")
     t_gen = time.perf_counter()
-    p = W.make_problem(s)
+    T = args.n_query
+    p = W.make_problem(s) if T == 1 else W.make_window(s, T)
     print(f"# generated {s.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
     t = {k: W.as_torch(getattr(p, k), dev) for k in
@@ -243,14 +265,22 @@ def main():
     kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split, args.tail_split,
                    args.tail_span, None if args.order < 0 else args.order)
     B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
-    q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len)
+    lead = (B,) if T == 1 else (B, T)
+    q_rot = torch.empty((*lead, H, D), dtype=torch.float32, device=dev)
+    out = torch.empty((*lead, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((*lead, H), dtype=torch.float32, device=dev)
+    ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len, n_query=T)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    plan = kvd.get_plan(B, H, t["k_cache"], table, max_len)
+    plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T)
+    sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
 
     def step():
+        if T > 1:
+            kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                     t["positions"], table, base=s.rope_base, q_rot=q_rot, **sc)
+            kvd.gqa_decode_attn_multi(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
+                                      max_seq_len=max_len, out=out, lse=lse, workspace=ws, **sc)
+            return
         if int8:
             kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                     t["k_scale"], t["v_scale"], t["positions"], table,
@@ -287,7 +317,7 @@ def main():
         torch.cuda.synchronize()
     kv_bytes = sizing.decode_kv_read_bytes(p.seq_lens, G, D, s.elem_bytes)
     aux = sizing.decode_aux_bytes(B, H, G, D, s.elem_bytes,
-                                  int(sum(-(-int(L) // 16) for L in p.seq_lens)) if table is not None else 0)
+                                  int(sum(-(-int(L) // s.block_size) for L in p.seq_lens)) if table is not None else 0)
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kern_ms = kt.mean_ms
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
@@ -305,7 +335,9 @@ def main():
         flushed = float(np.median(times))
         del scratch
 
-    key = f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "")
+    key = (f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "") +
+           (f"_bs{s.block_size}" if s.block_size not in (0, 16) else "") +
+           (f"_t{T}" if T > 1 else ""))
     src_hash = kernel_source_hash(plan["kernel"])
     traffic = load_traffic(key, src_hash)
     result = {
@@ -326,12 +358,14 @@ def main():
         "config": {"workload": workload_name(s), "batch": B, "n_heads": H, "n_kv_heads": G,
                    "head_dim": D, "kv_dtype": s.dtype, "accumulate": "f32" if not int8 else
                    "i32 (q K^T on int8 codes, 3 q limbs), f32 (P V in fp16 hi+lo)",
-                   "block_size": s.block_size, "total_context_tokens": int(p.seq_lens.sum()),
+                   "block_size": s.block_size, "new_tokens_per_seq": T,
+                   "total_context_tokens": int(p.seq_lens.sum()),
                    "max_context": max_len, "kv_bytes_per_step": kv_bytes,
                    "aux_bytes_per_step": aux, "split_tokens": plan["split_tokens"],
                    "n_splits": plan["n_splits"], "kernel": plan["kernel"],
                    "parallelism": "single GPU"},
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -202,12 +202,13 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
  *   q_rot      [B, H, D] fp32 output (ignored when q == NULL)
  *   k_cache    int8, tokens grouped by 16 and each group by head:
  *              contiguous [B, max_seq_len / 16, G, 16, D], paged
- *              [num_blocks, G, 16, D]; element (token p, head g, dim d) is
- *              [.., p / 16 (contiguous) or block table[b][p / 16] (paged), g,
- *              p % 16, d]
+ *              [num_blocks, block_size / 16, G, 16, D]; element (token p,
+ *              head g, dim d) is [b, p / 16, g, p % 16, d] (contiguous) or
+ *              [table[b][p / block_size], (p % block_size) / 16, g, p % 16, d]
  *   v_cache    int8, the same grouping with each head's block transposed:
- *              [B, max_seq_len / 16, G, D, 16] or [num_blocks, G, D, 16];
- *              element (p, g, d) is [.., group or block, g, d, p % 16]
+ *              [B, max_seq_len / 16, G, D, 16] or [num_blocks,
+ *              block_size / 16, G, D, 16]; element (p, g, d) is [.., group,
+ *              g, d, p % 16]
  *   k_scale, v_scale  [G] fp32 device arrays, finite and > 0
  *   positions, block_table, rope_base, rope_style   as in rope_append_kv
  * Errors: as rope_append_kv; EUNSUPPORTED when kv_dtype is not KVD_INT8 (and
@@ -242,6 +243,58 @@ kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
  * reports the shape error. */
 size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host);
 
+/*
+ * Several new tokens per sequence in one step: the verification pass of
+ * speculative decoding, in which the target model scores all gamma draft
+ * tokens in a single forward ("Transformer架构优化实战2026" §五), i.e.
+ * n_query = gamma + 1 queries per sequence under the causal mask of [KVGR]
+ * §5.1 inside the window.  With n_query = 1 these are the calls above.
+ *
+ * rope_append_kv_multi: token t (0 <= t < n_query) of sequence b is at
+ * position P + t with P = positions[b]; it is rotated at that position and
+ * appended at slot P + t, exactly as rope_append_kv does for one token.
+ *   q          [B, n_query, H, D], or NULL (k/v only)
+ *   k_new, v_new   [B, n_query, G, D]
+ *   q_rot      [B, n_query, H, D] fp32 output
+ *   k_scale, v_scale  [G] fp32 for an INT8 cache (as rope_append_kv_int8),
+ *              NULL for the other dtypes
+ *   input dtypes, caches, block_table, rope_base, rope_style as in
+ *   rope_append_kv (bf16 inputs for INT8 caches); every slot P + t must be
+ *   below max_seq_len and, when paged, in a block of sequence b's own
+ *
+ * gqa_decode_attn_multi: with L_b = seq_lens[b] counting the new tokens
+ * (L_b = P + n_query after the append), query t of sequence b attends the
+ * tokens j < L_b - n_query + 1 + t, its own and those before it:
+ *   out[b, t, h, :], lse[b, t, h] as gqa_decode_attn over those tokens
+ *   (a query that sees no token gets out = 0, lse = -inf)
+ *   q_rot      [B, n_query, H, D] fp32; out [B, n_query, H, D]; lse
+ *              [B, n_query, H] or NULL
+ *   k_scale, v_scale  as in rope_append_kv_multi
+ *   workspace  gqa_decode_workspace_size_multi(shape, n_query, ..) bytes
+ * The matrix-core kernels take the n_query * H / G query rows of a KV head
+ * together: at most 32 of them (bf16 and INT8 caches).  fp32 caches take
+ * n_query = 1 only.
+ * Errors: as the single-token calls; EUNSUPPORTED for n_query outside
+ * [1, 32], more than 32 query rows per KV head, or fp32 with n_query > 1;
+ * EINVAL when scales are given for a non-INT8 cache or missing for an INT8
+ * one.
+ */
+kvd_status rope_append_kv_multi(const kvd_shape* shape, int32_t n_query, const void* q,
+                                const void* k_new, const void* v_new, float* q_rot,
+                                void* k_cache, void* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* positions,
+                                const int32_t* block_table, double rope_base, int32_t rope_style,
+                                void* stream);
+kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+/* Workspace bytes of gqa_decode_attn_multi (0 also for an invalid shape). */
+size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,
+                                       int32_t max_seq_len_host);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kvd_status_string(int32_t status);
 
@@ -260,6 +313,9 @@ const char* kvd_status_string(int32_t status);
  * cannot run; the override applies to later calls in the whole process.
  */
 kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan);
+/* The plan of gqa_decode_attn_multi with n_query new tokens per sequence. */
+kvd_status kvd_get_plan_multi(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len_host,
+                              int32_t* plan);
 kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens);
 
 /*

@@ -43,8 +43,9 @@ class Shape(ctypes.Structure):
 
 
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
-            "gqa_decode_attn_int8", "gqa_decode_workspace_size",
-            "kvd_status_string", "kvd_get_plan", "kvd_set_tuning", "kvd_set_tuning_ex",
+            "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
+            "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi",
+            "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_set_tuning", "kvd_set_tuning_ex",
             "kvd_timer_begin",
             "kvd_timer_end", "kvd_read_probe")
 
@@ -82,10 +83,20 @@ def load_library():
                                              P, P, ctypes.c_size_t, P]
         lib.gqa_decode_workspace_size.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size.argtypes = [SP, I32]
+        lib.rope_append_kv_multi.restype = I32
+        lib.rope_append_kv_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P, P,
+                                             ctypes.c_double, I32, P]
+        lib.gqa_decode_attn_multi.restype = I32
+        lib.gqa_decode_attn_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_float,
+                                              P, P, P, ctypes.c_size_t, P]
+        lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
+        lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32]
         lib.kvd_status_string.restype = ctypes.c_char_p
         lib.kvd_status_string.argtypes = [I32]
         lib.kvd_get_plan.restype = I32
         lib.kvd_get_plan.argtypes = [SP, I32, ctypes.POINTER(I32)]
+        lib.kvd_get_plan_multi.restype = I32
+        lib.kvd_get_plan_multi.argtypes = [SP, I32, I32, ctypes.POINTER(I32)]
         lib.kvd_set_tuning.restype = I32
         lib.kvd_set_tuning.argtypes = [I32, I32]
         lib.kvd_set_tuning_ex.restype = I32
@@ -231,12 +242,14 @@ def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
 
 def workspace_size(q_rot: torch.Tensor, k_cache: torch.Tensor,
                    block_table: Optional[torch.Tensor] = None,
-                   max_seq_len: Optional[int] = None) -> int:
+                   max_seq_len: Optional[int] = None, n_query: int = 1) -> int:
+    """Workspace bytes of the decode call for q_rot [B, H, D] (n_query 1) or
+    [B, T, H, D] (n_query T)."""
     lib = load_library()
-    B, H = int(q_rot.shape[0]), int(q_rot.shape[1])
+    B, H = int(q_rot.shape[0]), int(q_rot.shape[-2])
     shape = make_shape(B, H, k_cache, block_table)
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    return int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+    return int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), int(n_query), msl))
 
 
 def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -376,6 +389,103 @@ def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     return out, lse
 
 
+def _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, paged):
+    """Input dtype of the multi-token calls; checks the caches and scales."""
+    if k_cache.dtype == torch.int8:
+        _need(k_cache, "k_cache", dev, torch.int8)
+        _need(v_cache, "v_cache", dev, torch.int8, v_cache_shape_int8(k_cache, paged))
+        if k_scale is None or v_scale is None:
+            raise ValueError("an int8 cache needs k_scale and v_scale")
+        _check_scales(k_scale, v_scale, G, dev)
+        return torch.bfloat16
+    if k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale belong to int8 caches only")
+    _need(k_cache, "k_cache", dev)
+    _need(v_cache, "v_cache", dev, k_cache.dtype, tuple(k_cache.shape))
+    return k_cache.dtype
+
+
+def rope_append_kv_multi(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+                         block_table: Optional[torch.Tensor] = None,
+                         k_scale: Optional[torch.Tensor] = None,
+                         v_scale: Optional[torch.Tensor] = None, base: float = 10000.0,
+                         style: str = "interleaved",
+                         q_rot: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """T new tokens per sequence: q [B, T, H, D], k_new / v_new [B, T, G, D];
+    token t of sequence b is rotated at positions[b] + t and appended there.
+    Returns q_rot [B, T, H, D] float32 (None if q is None).  int8 caches take
+    bf16 inputs and their per-head scales, other caches inputs of their dtype."""
+    lib = load_library()
+    dev = k_cache.device
+    B, T, G, D = (int(x) for x in k_new.shape)
+    H = int(q.shape[2]) if q is not None else G
+    shape = make_shape(B, H, k_cache, block_table)
+    dt = _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, block_table is not None)
+    if q is not None:
+        _need(q, "q", dev, dt, (B, T, H, D))
+    _need(k_new, "k_new", dev, dt, (B, T, G, D))
+    _need(v_new, "v_new", dev, dt, (B, T, G, D))
+    _need(positions, "positions", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if style not in _STYLES:
+        raise ValueError(f"style must be one of {sorted(_STYLES)}")
+    if q is not None and q_rot is None:
+        q_rot = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dev, torch.float32, (B, T, H, D))
+    _check(lib.rope_append_kv_multi(ctypes.byref(shape), T, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                    _ptr(q_rot) if q is not None else None, _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(positions),
+                                    _ptr(block_table), float(base), _STYLES[style], _stream(dev)))
+    return q_rot if q is not None else None
+
+
+def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                          k_scale: Optional[torch.Tensor] = None,
+                          v_scale: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of T new tokens per sequence, q_rot [B, T, H, D]: with
+    L = seq_lens[b] (the new tokens included), query t attends the tokens
+    j < L - T + 1 + t.  Returns (out [B, T, H, D], lse [B, T, H])."""
+    lib = load_library()
+    dev = k_cache.device
+    B, T, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, T, H, D))
+    _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, shape.n_kv_heads, dev,
+                        block_table is not None)
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if shape.head_dim != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (B, T, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dev, torch.float32, (B, T, H))
+    nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), T, msl))
+    if workspace is None:
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_attn_multi(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+                                     _ptr(block_table), msl, float(scale), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), wbytes, _stream(dev)))
+    return out, lse
+
+
 def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_tokens: int = 0,
                tail_span_tokens: int = -1, dispatch_order: Optional[int] = None) -> None:
     """Process-wide override of the kernel ("valu", "mfma", "int8" or None
@@ -388,12 +498,13 @@ def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_t
 
 
 def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
-             block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None):
+             block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None,
+             n_query: int = 1):
     """{'split_tokens', 'n_splits', 'kernel', 'workgroups'} the library would use."""
     shape = make_shape(batch, n_heads, k_cache, block_table)
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
     arr = (ctypes.c_int32 * 4)()
-    _check(load_library().kvd_get_plan(ctypes.byref(shape), msl, arr))
+    _check(load_library().kvd_get_plan_multi(ctypes.byref(shape), int(n_query), msl, arr))
     return {"split_tokens": arr[0], "n_splits": arr[1],
             "kernel": _KERNEL_NAMES[arr[2]], "workgroups": arr[3]}
 

@@ -105,19 +105,25 @@ void set_splits(Plan* pl, int chunk, int max_len, bool tail = true) {
   pl->n_splits = n_big + (rest + t2 - 1) / t2;
 }
 
-kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl) {
+// T new tokens (queries) per sequence: the matrix-core kernels take the
+// R * T query rows of a KV head as the columns of one tile.
+kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl, int T = 1) {
   const int R = s->n_heads / s->n_kv_heads;
+  if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
+  const int RT = R * T;
   int kernel = g_kernel_override.load();
   if (s->kv_dtype == KVD_INT8) {
-    // INT8 caches: the INT8 matrix-core kernel, up to 32 query heads per KV head
-    if (R > 32) return KVD_EUNSUPPORTED;
+    // INT8 caches: the INT8 matrix-core kernel, up to 32 query rows per KV head
+    if (RT > 32) return KVD_EUNSUPPORTED;
     if (kernel < 0) kernel = 2;
     if (kernel != 2) return KVD_EUNSUPPORTED;
   } else {
-    // matrix cores for bf16 caches with up to 32 query heads per KV head
-    const bool mfma_ok = s->kv_dtype == KVD_BF16 && R <= 32;
+    // matrix cores for bf16 caches with up to 32 query rows per KV head; the
+    // VALU kernel takes one new token per sequence
+    const bool mfma_ok = s->kv_dtype == KVD_BF16 && RT <= 32;
     if (kernel < 0) kernel = mfma_ok ? 1 : 0;
     if ((kernel == 1 && !mfma_ok) || kernel == 2) return KVD_EUNSUPPORTED;
+    if (kernel == 0 && T > 1) return KVD_EUNSUPPORTED;
   }
   pl->kernel = kernel;
   if (kernel >= 1) {
@@ -153,8 +159,8 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
     // splits 46 us, 512-token splits 63 us).
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
-    const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (R > 16 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || R > 16 ? 1 : 4);
+    const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (RT > 16 ? 1 : 2));
+    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 16 ? 1 : 4);
     const int cap = kernel == 0 ? 2048 : (kernel == 2 ? 2048 : 1024);
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
@@ -188,7 +194,7 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl)
   if (ord == 3 && list_ok) pl->grid_order = 3;   // a single split (or the VALU kernel): no list
   pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
   if (pl->n_splits > 1) {
-    const size_t rows = static_cast<size_t>(s->batch) * s->n_heads * pl->n_splits;
+    const size_t rows = static_cast<size_t>(s->batch) * T * s->n_heads * pl->n_splits;
     size_t o_bytes = rows * s->head_dim * sizeof(float);
     o_bytes = (o_bytes + 255) / 256 * 256;
     pl->workspace = o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
@@ -220,6 +226,10 @@ const char* kvd_status_string(int32_t status) {
   }
 }
 
+kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan) {
+  return kvd_get_plan_multi(shape, 1, max_seq_len_host, plan);
+}
+
 kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
                              int32_t tail_span_tokens, int32_t dispatch_order) {
   if (kernel < -1 || kernel > 2) return KVD_EINVAL;
@@ -238,15 +248,17 @@ kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens) {
   return kvd_set_tuning_ex(kernel, split_tokens, 0, -1, -1);
 }
 
-kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan) {
+kvd_status kvd_get_plan_multi(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len_host,
+                              int32_t* plan) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (!plan) return KVD_EINVAL;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (n_query < 1 || n_query > 32) return KVD_EUNSUPPORTED;
   int cu = 0;
   if (device_cu_count(&cu) != 0) return KVD_EHIP;
   Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, &pl);
+  st = make_plan(shape, max_seq_len_host, cu, &pl, n_query);
   if (st != KVD_OK) return st;
   plan[0] = pl.chunk;
   plan[1] = pl.n_splits;
@@ -255,14 +267,19 @@ kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_
   return KVD_OK;
 }
 
-size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host) {
+size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,
+                                       int32_t max_seq_len_host) {
   if (check_shape(shape) != KVD_OK) return 0;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return 0;
   int cu = 0;
   if (device_cu_count(&cu) != 0) return 0;
   Plan pl;
-  if (make_plan(shape, max_seq_len_host, cu, &pl) != KVD_OK) return 0;
+  if (make_plan(shape, max_seq_len_host, cu, &pl, n_query) != KVD_OK) return 0;
   return pl.workspace;
+}
+
+size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host) {
+  return gqa_decode_workspace_size_multi(shape, 1, max_seq_len_host);
 }
 
 }  // extern "C"
@@ -273,9 +290,10 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
                        const void* v_new, float* q_rot, void* k_cache, void* v_cache,
                        const float* k_scale, const float* v_scale, const int32_t* positions,
                        const int32_t* block_table, double rope_base, int32_t rope_style,
-                       void* stream) {
+                       void* stream, int32_t T = 1) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
+  if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
   if (!k_new || !v_new || !k_cache || !v_cache || !positions) return KVD_EINVAL;
   if (q && !q_rot) return KVD_EINVAL;
@@ -289,7 +307,7 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
   p.k_cache = k_cache; p.v_cache = v_cache; p.k_scale = k_scale; p.v_scale = v_scale;
   p.positions = positions; p.table = block_table;
   p.base = rope_base; p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads;
-  p.D = shape->head_dim; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
+  p.D = shape->head_dim; p.T = T; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   if (launch_rope_append(p, shape->kv_dtype, paged, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -301,7 +319,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
                        const void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* seq_lens, const int32_t* block_table,
                        int32_t max_seq_len_host, float scale, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream, int32_t T = 1);
 
 }  // namespace
 
@@ -352,6 +370,34 @@ kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
                      max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+kvd_status rope_append_kv_multi(const kvd_shape* shape, int32_t n_query, const void* q,
+                                const void* k_new, const void* v_new, float* q_rot,
+                                void* k_cache, void* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* positions,
+                                const int32_t* block_table, double rope_base, int32_t rope_style,
+                                void* stream) {
+  if (!shape) return KVD_EINVAL;
+  // INT8 caches take their scales, the others none
+  const bool i8 = shape->kv_dtype == KVD_INT8;
+  if (i8 != (k_scale != nullptr) || i8 != (v_scale != nullptr)) return KVD_EINVAL;
+  return append_impl(shape, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+                     positions, block_table, rope_base, rope_style, stream, n_query);
+}
+
+kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!shape) return KVD_EINVAL;
+  const bool i8 = shape->kv_dtype == KVD_INT8;
+  if (i8 != (k_scale != nullptr) || i8 != (v_scale != nullptr)) return KVD_EINVAL;
+  return decode_impl(shape, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream,
+                     n_query);
+}
+
 }  // extern "C"
 
 namespace {
@@ -360,7 +406,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
                        const void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* seq_lens, const int32_t* block_table,
                        int32_t max_seq_len_host, float scale, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream, int32_t T) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
@@ -371,11 +417,12 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   const bool paged = shape->block_size != 0;
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
   if (shape->batch == 0) return KVD_OK;
   int cu = 0;
   if (device_cu_count(&cu) != 0) return KVD_EHIP;
   Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, &pl);
+  st = make_plan(shape, max_seq_len_host, cu, &pl, T);
   if (st != KVD_OK) return st;
   if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
   if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
@@ -386,7 +433,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.k_scale = k_scale; p.v_scale = v_scale;
   p.out = out; p.lse = lse;
   p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
-  p.R = p.H / p.G;
+  p.R = p.H / p.G; p.T = T;
   p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
@@ -400,7 +447,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.part_o = nullptr; p.part_lse = nullptr;
   if (pl.n_splits > 1) {
     char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
+    const size_t rows = static_cast<size_t>(p.B) * p.T * p.H * p.n_splits;
     const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
     p.part_o = reinterpret_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(ws + o_bytes);

@@ -153,21 +153,31 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   constexpr int NV = kTileBytes / 1024;   // V^T copy instructions per tile
   static_assert(NB >= 1 && NB <= 2 && (D == 64 || D == 128), "tile shape");
   const int R = p.R;
-  const int hbase = g * R;
+  const int RT = R * p.T;             // tile columns: the query rows of this KV head
   int L = scalar_load_i32(p.seq_lens + b);
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
-      for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+      for (int idx = threadIdx.x; idx < RT * D; idx += 256) {
         const int r = idx / D, d = idx - r * D;
-        p.out[(static_cast<int64_t>(b) * p.H + hbase + r) * D + d] = 0.f;
-        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + hbase + r] = kNegInf;
+        const int64_t row = query_row(p, b, g, r);
+        p.out[row * D + d] = 0.f;
+        if (d == 0 && p.lse) p.lse[row] = kNegInf;
       }
     }
     return;
   }
   const int t1 = min(t0 + split_size(p, split), L);
+  // several new tokens: column c (token c / R) sees the tokens below
+  // L - T + 1 + c / R; tiles reaching past win need the per-column bound
+  const int win = L - p.T + 1;
+  int cbound[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = nb * 16 + (threadIdx.x & 15);
+    cbound[nb] = c < RT ? win + c / R : L;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -187,7 +197,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int h = nb * 16 + n;
-    const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + hbase + (h < R ? h : 0)) * D + grp * 16;
+    const float* src = p.q_rot + query_row(p, b, g, h < RT ? h : 0) * D + grp * 16;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -287,7 +297,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   const float kscale = p.k_scale[g];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const bool real = nb * 16 + n < R;
+    const bool real = nb * 16 + n < RT;
     float amax = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -359,7 +369,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
       vmem_wait<0>();
     }
     const bool full = tbase + kTT <= t1;
-    const bool masked = !full || (PAGED && !__all(vokc));      // wave-uniform
+    const bool masked = !full || (PAGED && !__all(vokc)) || tbase + kTT > win;   // wave-uniform
     // int32 score products of the three limbs, half hb = token rows
     // 16c + 4hb + j of the tile's groups c
     i32x4 S[kLimbs][NB][4];
@@ -394,7 +404,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int t = tbase + 16 * grp + 4 * hb + j;
-            if (!(t < t1 && vokc)) sv[hb * 4 + j] = kNegInf;
+            if (!(t < t1 && vokc && t < cbound[nb])) sv[hb * 4 + j] = kNegInf;
           }
       }
       float mt = sv[0];
@@ -481,7 +491,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int hb = nb * 16;
-    const int nh = min(16, R - hb);
+    const int nh = min(16, RT - hb);
     if (nh <= 0) break;
     __syncthreads();
     if (n < nh) {
@@ -508,14 +518,14 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
         o += so[(w * 16 + r) * D + d] * a;
         sum += sm_l[w * 16 + r] * a;
       }
-      const int h = hbase + hb + r;
+      const int64_t h = query_row(p, b, g, hb + r);
       const float val = sum > 0.f ? o / sum * vscale : 0.f;
       const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
       if (p.direct) {
-        p.out[(static_cast<int64_t>(b) * p.H + h) * D + d] = val;
-        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + h] = lse2 * 0.69314718055994531f;
+        p.out[h * D + d] = val;
+        if (d == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
       } else {
-        const int64_t pr = (static_cast<int64_t>(b) * p.H + h) * p.n_splits + split;
+        const int64_t pr = h * p.n_splits + split;
         p.part_o[pr * D + d] = val;
         if (d == 0) p.part_lse[pr] = lse2;
       }
@@ -557,14 +567,14 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
-  return p.R <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
+  return p.R * p.T <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t s) {
   if (p.chunk > kMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
-      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.R > 32 ||
+      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
       !p.k_scale || !p.v_scale || (!paged && p.max_seq_len % 16 != 0))
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);

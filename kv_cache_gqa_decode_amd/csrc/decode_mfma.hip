@@ -85,21 +85,31 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   constexpr int kWaves = kMfmaWaves;
   static_assert(TT == 32 && NB >= 1 && NB <= 2, "tile shape");
   const int R = p.R;
-  const int hbase = g * R;            // first query head of this KV head
+  const int RT = R * p.T;             // tile columns: the query rows of this KV head
   int L = scalar_load_i32(p.seq_lens + b);
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
-      for (int idx = threadIdx.x; idx < R * D; idx += 256) {
+      for (int idx = threadIdx.x; idx < RT * D; idx += 256) {
         const int r = idx / D, d = idx - r * D;
-        p.out[(static_cast<int64_t>(b) * p.H + hbase + r) * D + d] = 0.f;
-        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + hbase + r] = kNegInf;
+        const int64_t row = query_row(p, b, g, r);
+        p.out[row * D + d] = 0.f;
+        if (d == 0 && p.lse) p.lse[row] = kNegInf;
       }
     }
     return;
   }
   const int t1 = min(t0 + split_size(p, split), L);
+  // several new tokens: column c (token c / R) sees the tokens below
+  // L - T + 1 + c / R; tiles reaching past win need the per-column bound
+  const int win = L - p.T + 1;
+  int cbound[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = nb * 16 + (threadIdx.x & 15);
+    cbound[nb] = c < RT ? win + c / R : L;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -119,7 +129,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int h = nb * 16 + n;
-    const float* src = p.q_rot + (static_cast<int64_t>(b) * p.H + hbase + (h < R ? h : 0)) * D + grp * 8;
+    const float* src = p.q_rot + query_row(p, b, g, h < RT ? h : 0) * D + grp * 8;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       qraw[nb][kb][0] = *reinterpret_cast<const float4*>(src + kb * 32);
@@ -227,7 +237,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   bf16x8 qh[NB][KB], ql[NB][KB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float qs = nb * 16 + n < R ? p.qscale : 0.f;
+    const float qs = nb * 16 + n < RT ? p.qscale : 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const float4 x0 = qraw[nb][kb][0], x1 = qraw[nb][kb][1];
@@ -273,7 +283,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     const bool full = tbase + TT <= t1;
     const bool ok0 = !PAGED || blk[0] >= 0;
     const bool ok1 = !PAGED || blk[1] >= 0;
-    const bool masked = !full || !ok0 || !ok1;      // wave-uniform
+    const bool masked = !full || !ok0 || !ok1 || tbase + TT > win;      // wave-uniform
     // scores of the two 16-token halves
     f32x4 s[NB][2];
 #pragma unroll
@@ -306,7 +316,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
           for (int j = 0; j < 4; ++j) {
             const int t = tbase + 16 * h2 + 4 * grp + j;
             const bool ok = h2 == 0 ? ok0 : ok1;
-            if (!(t < t1 && ok)) sv[h2 * 4 + j] = kNegInf;
+            if (!(t < t1 && ok && t < cbound[nb])) sv[h2 * 4 + j] = kNegInf;
           }
       }
       float mt = sv[0];
@@ -393,7 +403,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int hb = nb * 16;
-    const int nh = min(16, R - hb);
+    const int nh = min(16, RT - hb);
     if (nh <= 0) break;
     __syncthreads();                   // staging tiles / previous pass no longer read
     if (n < nh) {
@@ -417,15 +427,15 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
         o += so[(w * 16 + r) * D + d] * a;
         sum += sm_l[w * 16 + r] * a;
       }
-      const int h = hbase + hb + r;
+      const int64_t h = query_row(p, b, g, hb + r);
       // every token of the split masked (invalid blocks): empty softmax
       const float val = sum > 0.f ? o / sum : 0.f;
       const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
       if (p.direct) {
-        p.out[(static_cast<int64_t>(b) * p.H + h) * D + d] = val;
-        if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + h] = lse2 * 0.69314718055994531f;
+        p.out[h * D + d] = val;
+        if (d == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
       } else {
-        const int64_t pr = (static_cast<int64_t>(b) * p.H + h) * p.n_splits + split;
+        const int64_t pr = h * p.n_splits + split;
         p.part_o[pr * D + d] = val;
         if (d == 0) p.part_lse[pr] = lse2;
       }
@@ -452,14 +462,14 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
-  return p.R <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
+  return p.R * p.T <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
   if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
-      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits)
+      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32)
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);
 }

@@ -285,6 +285,7 @@ int valu_heads_per_pass(int n_rep) {
 
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged, int rb,
                               hipStream_t s) {
+  if (p.T != 1) return hipErrorInvalidValue;    // one new token per sequence
   if (kv_dtype == KVD_FP32) {
     return p.D == 64 ? launch_d<float, 64>(p, paged, rb, s) : launch_d<float, 128>(p, paged, rb, s);
   }

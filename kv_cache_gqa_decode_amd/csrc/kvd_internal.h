@@ -23,6 +23,8 @@ struct DecodeParams {
   float* part_o;            // [B * H, n_splits, D]  (split results, normalised)
   float* part_lse;          // [B * H, n_splits]     (log2 of the split's exp-sum)
   int32_t B, H, G, D, R;    // R = H / G
+  int32_t T;                // new tokens (queries) per sequence; query t of
+                            // sequence b attends the tokens j < L_b - T + 1 + t
   int32_t max_seq_len;      // contiguous S_max, or max_blocks_per_seq * 16
   int32_t max_len_host;     // lengths are clamped to this
   int32_t num_blocks;
@@ -53,10 +55,11 @@ struct RopeParams {
   void* v_cache;
   const float* k_scale;     // INT8 caches: [G] per-head scales, else null
   const float* v_scale;
-  const int32_t* positions;
+  const int32_t* positions; // [B] slot of each sequence's first new token
   const int32_t* table;
   double base;
   int32_t B, H, G, D;
+  int32_t T;                // new tokens per sequence (rows b * T + t of q / k_new / v_new)
   int32_t style;
   int32_t max_seq_len;
   int32_t num_blocks;
@@ -105,6 +108,14 @@ __device__ __forceinline__ int paged_group(const DecodeParams& p, int b, int j) 
   const int blk = p.table[static_cast<int64_t>(b) * p.max_blocks_per_seq + (j >> p.block_shift)];
   if (blk < 0 || blk >= p.num_blocks) return -1;
   return (blk << p.block_shift) | (j & ((1 << p.block_shift) - 1));
+}
+
+// Row of q_rot / out / lse / the split partials that column c of KV head g's
+// tile stands for: the columns are the n_rep query heads of each of the T new
+// tokens, c = t * R + r.  With T = 1 this is query head g * R + c.
+__host__ __device__ __forceinline__ int64_t query_row(const DecodeParams& p, int b, int g, int c) {
+  const int t = c / p.R, r = c - t * p.R;
+  return (static_cast<int64_t>(b) * p.T + t) * p.H + g * p.R + r;
 }
 
 // bf16 pair in a 32-bit word -> two floats (exact).

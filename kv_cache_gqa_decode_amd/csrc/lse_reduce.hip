@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
 
   const int bh = blockIdx.x;
   const int d0 = blockIdx.y * DT;
-  const int b = bh / p.H;
+  const int b = bh / (p.H * p.T);       // rows b * T * H + t * H + h
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
   const int ns = split_count(p, L);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
 
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream) {
   const bool wide = p.n_splits > 16;
-  const dim3 grid(p.B * p.H, wide ? p.D / 32 : 1);
+  const dim3 grid(p.B * p.H * p.T, wide ? p.D / 32 : 1);
   if (p.D == 64) {
     if (wide) lse_reduce_kernel<64, 32><<<grid, 256, 0, stream>>>(p);
     else lse_reduce_kernel<64, 64><<<grid, 256, 0, stream>>>(p);

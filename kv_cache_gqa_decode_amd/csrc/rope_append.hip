@@ -117,16 +117,19 @@ __device__ __forceinline__ int64_t i8_krow(const RopeParams& p, int b, int pos, 
 
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
-  // workgroup (sequence, slice of 256 items): the D/2 rotation factors of the
-  // sequence's position are computed once per workgroup (fp64) and shared by
-  // its threads through LDS
+  // workgroup (new token bt = b * T + t, slice of 256 items): the D/2
+  // rotation factors of the token's position are computed once per workgroup
+  // (fp64) and shared by its threads through LDS
   __shared__ double cs[64], sn[64];
-  const int b = blockIdx.x;
+  const int bt = blockIdx.x;
+  const int b = bt / p.T;
   const int half = p.D >> 1;
-  const int pos = p.positions[b];
+  const int64_t pos64 = static_cast<int64_t>(p.positions[b]) + (bt - b * p.T);
+  // a slot past any cache (the rotation still uses the true position)
+  const int pos = pos64 > 0x7fffffff ? -1 : static_cast<int>(pos64);
   for (int i = threadIdx.x; i < half; i += 256) {
     const double theta = pow(p.base, -2.0 * i / p.D);
-    sincos(static_cast<double>(pos) * theta, &sn[i], &cs[i]);
+    sincos(static_cast<double>(pos64) * theta, &sn[i], &cs[i]);
   }
   __syncthreads();
   const int nq = p.q ? p.H * half : 0;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       const int ia = p.style == KVD_ROPE_HALF ? pi : 2 * pi;
       const int ib = p.style == KVD_ROPE_HALF ? pi + half : 2 * pi + 1;
       const int heads = is_q ? p.H : p.G;
-      const int64_t src = (static_cast<int64_t>(b) * heads + head) * p.D;
+      const int64_t src = (static_cast<int64_t>(bt) * heads + head) * p.D;
       const void* x = is_q ? p.q : p.k_new;
       const double a = load_d<T>(x, src + ia), c = load_d<T>(x, src + ib);
       const double ra = a * cs[pi] - c * sn[pi];    // (a + ic)(cos + i sin)
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       const int g = j / p.D, d = j - g * p.D;
       const int64_t row = slot_row<PAGED>(p, b, pos, g);
       if (row >= 0) {
-        const int64_t src = (static_cast<int64_t>(b) * p.G + g) * p.D + d;
+        const int64_t src = (static_cast<int64_t>(bt) * p.G + g) * p.D + d;
         if constexpr (std::is_same<T, int8_t>::value) {
           const int64_t vi = ((i8_group<PAGED>(p, b, pos, row) * p.G + g) * p.D + d) * 16 + (pos & 15);
           static_cast<int8_t*>(p.v_cache)[vi] = quantize_i8(load_d<int8_t>(p.v_new, src), p.v_scale[g]);
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
 hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream) {
   const int work = (p.q ? p.H : 0) * (p.D / 2) + p.G * (p.D / 2) + p.G * p.D;
-  const dim3 grid(p.B, (work + 255) / 256);
+  if (p.T < 1) return hipErrorInvalidValue;
+  const dim3 grid(p.B * p.T, (work + 255) / 256);
   if (kv_dtype == KVD_FP32) {
     if (paged) rope_append_kernel<float, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<float, false><<<grid, 256, 0, stream>>>(p);

@@ -24,6 +24,9 @@ the overrides; see ``Spec``):
   (zero otherwise), so a read outside the valid range shows up in the output.
 * Paged pools: a seeded permutation of all physical blocks, sequence b owning
   ``perm[b * max_blocks_per_seq : (b + 1) * max_blocks_per_seq]``.
+* Steps with T new tokens per sequence (``make_window``): the history of
+  L_b - T tokens as above, the new tokens from streams 6 (q), 7 (k_new) and 8
+  (v_new), ``positions[b] = L_b - T``.
 * INT8 caches (dtype ``"i8"``): q, k_new and v_new as for bf16; the cached
   history is drawn directly as codes, N(0, 40^2) clipped to [-127, 127] and
   cast (truncating) to int8, i.e. data whose per-head absolute maximum sits
@@ -126,6 +129,7 @@ class Problem:
     block_table: Optional[np.ndarray]  # [B, max_blocks_per_seq] int32
     k_scale: Optional[np.ndarray] = None   # INT8 caches: [G] float32
     v_scale: Optional[np.ndarray] = None
+    n_query: int = 1                       # new tokens per sequence (make_window)
 
     @property
     def max_len(self) -> int:
@@ -272,6 +276,33 @@ def make_problem(s: Spec, lengths: Optional[np.ndarray] = None) -> Problem:
                    v_new=_to_storage(v_new, idt), k_cache=k_cache, v_cache=v_cache,
                    positions=(L - 1).astype(np.int32), seq_lens=L.astype(np.int32),
                    block_table=table, k_scale=k_scale, v_scale=v_scale)
+
+
+def make_window(s: Spec, n_query: int, lengths: Optional[np.ndarray] = None) -> Problem:
+    """A step with ``n_query`` = T new tokens per sequence (the verification
+    pass of speculative decoding).  Sequence b holds L_b tokens after the
+    step (``lengths``, default the spec's draw clipped to at least T): the
+    history of L_b - T tokens is drawn exactly as by ``make_problem``, the T
+    new tokens go to slots ``positions[b] = L_b - T`` .. L_b - 1 (poisoned
+    before the append), and q [B, T, H, D], k_new / v_new [B, T, G, D] come
+    from streams 6, 7 and 8 with the distributions of streams 1, 2 and 3."""
+    T = int(n_query)
+    if T < 1:
+        raise ValueError("n_query must be >= 1")
+    L = draw_lengths(s) if lengths is None else np.asarray(lengths, np.int32).copy()
+    L = np.maximum(L, T).astype(np.int32)
+    if (L > s.max_seq_len).any():
+        raise ValueError("every length must lie in [n_query, max_seq_len]")
+    p = make_problem(s, lengths=L - T + 1)
+    B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
+    sc = np.float32(s.value_scale)
+    q = _rng(s, 6).standard_normal((B, T, H, D), dtype=np.float32) * sc * np.float32(s.q_gain)
+    k_new = _rng(s, 7).standard_normal((B, T, G, D), dtype=np.float32) * sc
+    v_new = _rng(s, 8).standard_normal((B, T, G, D), dtype=np.float32) * sc
+    idt = s.input_dtype
+    return dataclasses.replace(p, q=_to_storage(q, idt), k_new=_to_storage(k_new, idt),
+                               v_new=_to_storage(v_new, idt), positions=(L - T).astype(np.int32),
+                               seq_lens=L, n_query=T)
 
 
 def as_torch(a: np.ndarray, device=None):

@@ -138,6 +138,35 @@ def test_int8_calls_validate(lib):
     assert attn8(lib, shape(kv_dtype=2, batch=0)) == OK
 
 
+def rope_m(lib, sh, T, ks=None, vs=None):
+    return lib.rope_append_kv_multi(ctypes.byref(sh) if sh is not None else None, T, FAKE, FAKE,
+                                    FAKE, ctypes.c_void_p(0x3000), FAKE, FAKE, ks, vs, FAKE, None,
+                                    10000.0, 0, None)
+
+
+def attn_m(lib, sh, T, ks=None, vs=None, msl=32):
+    return lib.gqa_decode_attn_multi(ctypes.byref(sh) if sh is not None else None, T, FAKE, FAKE,
+                                     FAKE, ks, vs, FAKE, None, msl, 0.125,
+                                     ctypes.c_void_p(0x2000), None, None, 0, None)
+
+
+def test_multi_calls_validate(lib):
+    bf, i8 = shape(), shape(kv_dtype=2)
+    assert rope_m(lib, None, 2) == EINVAL and attn_m(lib, None, 2) == EINVAL
+    for T in (0, -1, 33):
+        assert rope_m(lib, bf, T) == EUNSUPPORTED
+        assert attn_m(lib, bf, T) == EUNSUPPORTED
+    # scales exactly for INT8 caches
+    assert rope_m(lib, bf, 2, ks=FAKE, vs=FAKE) == EINVAL
+    assert attn_m(lib, bf, 2, ks=FAKE) == EINVAL
+    assert rope_m(lib, i8, 2) == EINVAL and attn_m(lib, i8, 2, ks=FAKE) == EINVAL
+    assert attn_m(lib, bf, 2, msl=65) == ERANGE
+    assert rope_m(lib, shape(batch=0), 5) == OK
+    assert attn_m(lib, shape(batch=0), 5) == OK
+    assert attn_m(lib, shape(kv_dtype=2, batch=0), 5, ks=FAKE, vs=FAKE) == OK
+    assert lib.gqa_decode_workspace_size_multi(ctypes.byref(bf), 0, 10) == 0
+
+
 def test_tuning_and_timer_validation(lib):
     assert lib.kvd_set_tuning(-2, 0) == EINVAL
     assert lib.kvd_set_tuning(3, 0) == EINVAL
