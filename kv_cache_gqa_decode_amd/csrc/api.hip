@@ -143,16 +143,23 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
   }
   int chunk = g_split_override.load();
   if (chunk <= 0) {
-    // Resident workgroups: two per CU (one for more than 16 heads per KV head,
-    // whose workgroups need twice the registers) for the MFMA kernel, four
-    // for the VALU kernel.  The MFMA kernel aims for about four rounds of
-    // them over the (sequence, KV head) pairs at the host bound on lengths
-    // (one round with more than 16 heads, whose merge epilogue is heavier)
-    // and at most 1024 tokens per split: the workgroups that share a CU run
-    // at different speeds (the older one is served first), and smaller
-    // units let the dispatcher even that out at a small cost in merges.
-    // The VALU kernel aims for two rounds of at most 2048 tokens.  The INT8
-    // kernel aims for a single round of at most 2048 tokens: its workgroups
+    // Resident workgroups: two per CU for the MFMA kernel (also with two
+    // column blocks, held to 256 registers), four for the VALU kernel, two
+    // for the INT8 kernel (one with more than 16 query rows per KV head).
+    // The MFMA kernel aims for about four rounds of them over the
+    // (sequence, KV head) pairs at the host bound on lengths and at most
+    // 1024 tokens per split: the workgroups that share a CU run at
+    // different speeds (the older one is served first), and smaller units
+    // let the dispatcher even that out at a small cost in merges.  With
+    // more than 8 query rows per KV head (several new tokens, or n_rep
+    // above 8) each unit ends with a heavier merge of its waves and writes
+    // more partial rows: one round of splits of up to 2048 tokens then
+    // measured faster (c3 shape with 5 new tokens: 215 against 226 us),
+    // and with more than 16 rows, as long as one workgroup per CU would
+    // make them (a 128K MQA sequence: 512-token splits 20 us, 256-token
+    // 31 us).  The VALU kernel aims for two rounds of at most 2048 tokens.
+    // The INT8 kernel aims for a single round of at most 2048 tokens (4096
+    // with more than 16 query rows, one workgroup per CU): its workgroups
     // keep two 64-token tiles in flight per wave from the first tile on,
     // and each one pays a full memory latency before its first tile, so
     // fewer, longer units measured faster (a 128K sequence: 2048-token
@@ -160,8 +167,9 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (RT > 16 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 16 ? 1 : 4);
-    const int cap = kernel == 0 ? 2048 : (kernel == 2 ? 2048 : 1024);
+    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : 4);
+    const int cap = kernel == 0 ? 2048 : (kernel == 2 ? (RT > 16 ? 4096 : 2048)
+                                                      : (RT > 8 ? 2048 : 1024));
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
     if (chunk > cap) chunk = cap;

@@ -136,7 +136,7 @@ __device__ __forceinline__ void read_vt<4>(uint32_t addr, u32x4 (&v)[4]) {
 template <int D>
 constexpr int smem_bytes_i8() {
   constexpr int stage = kMfmaWaves * 2 * 64 * D;
-  constexpr int merge = (kMfmaWaves * 16 * D + 2 * kMfmaWaves * 16) * 4;
+  constexpr int merge = merge_bytes<D>();
   return stage > merge ? stage : merge;
 }
 
@@ -482,54 +482,16 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
     lsum[nb] += __shfl_xor(lsum[nb], 32);
   }
 
-  // merge the waves through LDS, 16 heads at a time; each wave's (max, sum,
-  // O) is stated against max - 6, the scale its probabilities carry
-  float* so = reinterpret_cast<float*>(smem);       // [kWaves][16][D]
-  float* sm_m = so + kWaves * 16 * D;               // [kWaves][16]
-  float* sm_l = sm_m + kWaves * 16;                 // [kWaves][16]
+  // merge the waves through LDS, 16 rows at a time; each wave's (max, sum,
+  // O) is stated against max - kPBias, the scale its probabilities carry,
+  // and O is in V codes (times v_scale)
   const float vscale = p.v_scale[g];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int hb = nb * 16;
-    const int nh = min(16, RT - hb);
+    const int nh = min(16, RT - nb * 16);
     if (nh <= 0) break;
-    __syncthreads();
-    if (n < nh) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) so[(wave * 16 + n) * D + 16 * cb + 4 * grp + j] = acc[nb][cb][j];
-      if (grp == 0) {
-        sm_m[wave * 16 + n] = m[nb] == kNegInf ? kNegInf : m[nb] - kPBias;
-        sm_l[wave * 16 + n] = lsum[nb];
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
-      const int r = idx / D, d = idx - r * D;
-      float M = sm_m[r];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
-      const float ref = M == kNegInf ? 0.f : M;
-      float o = 0.f, sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float a = exp2f(sm_m[w * 16 + r] - ref);
-        o += so[(w * 16 + r) * D + d] * a;
-        sum += sm_l[w * 16 + r] * a;
-      }
-      const int64_t h = query_row(p, b, g, hb + r);
-      const float val = sum > 0.f ? o / sum * vscale : 0.f;
-      const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
-      if (p.direct) {
-        p.out[h * D + d] = val;
-        if (d == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
-      } else {
-        const int64_t pr = h * p.n_splits + split;
-        p.part_o[pr * D + d] = val;
-        if (d == 0) p.part_lse[pr] = lse2;
-      }
-    }
+    merge_waves<D>(p, smem, b, g, split, nb * 16, nh, acc[nb],
+                   m[nb] == kNegInf ? kNegInf : m[nb] - kPBias, lsum[nb], vscale);
   }
 }
 
@@ -543,7 +505,10 @@ void decode_i8_kernel(DecodeParams p) {
   if (!unit_at(p, u)) return;
   run_split_i8<D, 1, PAGED>(p, smem, u.b, u.g, u.split);
 }
-// 17 to 32 query heads per KV head: one workgroup per CU
+// 17 to 32 query rows per KV head (two column blocks): at D = 128 the q
+// limbs, scores and accumulators of the second block do not fit beside the
+// double-buffered K registers within 256 per lane (held there, the compiler
+// spills), so one workgroup per CU
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_i8_kernel_wide(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];

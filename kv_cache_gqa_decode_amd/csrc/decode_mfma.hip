@@ -70,7 +70,7 @@ constexpr int kBlkRegs = (kMfmaMaxChunk / 16 / kMfmaWaves + 63) / 64;
 template <int D>
 constexpr int smem_bytes() {
   constexpr int stage = kMfmaWaves * 2 * Geo<D>::kTileBytes;
-  constexpr int merge = (kMfmaWaves * 16 * D + 2 * kMfmaWaves * 16) * 4;
+  constexpr int merge = merge_bytes<D>();
   return stage > merge ? stage : merge;
 }
 
@@ -396,67 +396,47 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     l[nb] += __shfl_xor(l[nb], 32);
   }
 
-  // merge the waves through LDS, 16 heads at a time
-  float* so = reinterpret_cast<float*>(smem);       // [kWaves][16][D]
-  float* sm_m = so + kWaves * 16 * D;               // [kWaves][16]
-  float* sm_l = sm_m + kWaves * 16;                 // [kWaves][16]
+  // merge the waves through LDS, 16 rows at a time
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int hb = nb * 16;
-    const int nh = min(16, RT - hb);
+    const int nh = min(16, RT - nb * 16);
     if (nh <= 0) break;
-    __syncthreads();                   // staging tiles / previous pass no longer read
-    if (n < nh) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) so[(wave * 16 + n) * D + 16 * cb + 4 * grp + j] = acc[nb][cb][j];
-      if (grp == 0) { sm_m[wave * 16 + n] = m[nb]; sm_l[wave * 16 + n] = l[nb]; }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
-      const int r = idx / D, d = idx - r * D;
-      float M = sm_m[r];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + r]);
-      const float ref = M == kNegInf ? 0.f : M;
-      float o = 0.f, sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float a = exp2f(sm_m[w * 16 + r] - ref);
-        o += so[(w * 16 + r) * D + d] * a;
-        sum += sm_l[w * 16 + r] * a;
-      }
-      const int64_t h = query_row(p, b, g, hb + r);
-      // every token of the split masked (invalid blocks): empty softmax
-      const float val = sum > 0.f ? o / sum : 0.f;
-      const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
-      if (p.direct) {
-        p.out[h * D + d] = val;
-        if (d == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
-      } else {
-        const int64_t pr = h * p.n_splits + split;
-        p.part_o[pr * D + d] = val;
-        if (d == 0) p.part_lse[pr] = lse2;
-      }
-    }
+    merge_waves<D>(p, smem, b, g, split, nb * 16, nh, acc[nb], m[nb], l[nb], 1.f);
   }
 }
 
 // One workgroup per unit, dispatched by the hardware in the planner's order.
-template <int D, int NB, bool PAGED>
+// Up to 16 query rows per KV head:
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes<D>()];
   Unit u;
   if (!unit_at(p, u)) return;
-  run_split<D, NB, PAGED>(p, smem, u.b, u.g, u.split);
+  run_split<D, 1, PAGED>(p, smem, u.b, u.g, u.split);
+}
+// 17 to 32 query rows per KV head (two column blocks): left to itself the
+// compiler splits the accumulators into AGPRs and needs 295 registers per
+// lane at D = 128, one workgroup per CU; held to 256 it fits them in VGPRs
+// without spilling, and two workgroups share a CU.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel_wide(DecodeParams p) {
+  __shared__ __align__(16) char smem[smem_bytes<D>()];
+  Unit u;
+  if (!unit_at(p, u)) return;
+  run_split<D, 2, PAGED>(p, smem, u.b, u.g, u.split);
 }
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
   const dim3 grid = split_grid(p);
-  if (paged) decode_mfma_kernel<D, NB, true><<<grid, 256, 0, s>>>(p);
-  else decode_mfma_kernel<D, NB, false><<<grid, 256, 0, s>>>(p);
+  if (NB == 1) {
+    if (paged) decode_mfma_kernel<D, true><<<grid, 256, 0, s>>>(p);
+    else decode_mfma_kernel<D, false><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (paged) decode_mfma_kernel_wide<D, true><<<grid, 256, 0, s>>>(p);
+    else decode_mfma_kernel_wide<D, false><<<grid, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -199,5 +199,89 @@ inline dim3 split_grid(const DecodeParams& p) {
     default: return dim3(static_cast<unsigned>(p.G) * p.B * p.n_splits);
   }
 }
+
+// The waves of a split workgroup each hold (acc, m, l) for the same 16 query
+// rows over different tiles: the column block's accumulator acc[cb] (rows
+// 16 cb + 4 grp + j of lane column n), its running max m (log2 units) and
+// its exp-sum l.  They are combined through LDS with the log-sum-exp weights
+// and the split's normalised rows (times out_scale) and log2-sum-exp written
+// -- as the final output when the split is the whole sequence.
+//
+// LDS rows are padded by 16 bytes so that the 16 lanes of a lane group,
+// which write rows 528 bytes apart, fall into different banks; each thread
+// then reduces one row over D / 16 consecutive dims, with the row's weights
+// computed once.
+template <int D>
+constexpr int merge_row_floats() { return D + 4; }
+template <int D>
+constexpr int merge_bytes() {
+  return (kMfmaWaves * 16 * merge_row_floats<D>() + 2 * kMfmaWaves * 16) * 4;
+}
+
+template <int D>
+__device__ __forceinline__ void merge_waves(const DecodeParams& p, char* smem, int b, int g,
+                                            int split, int hb, int nh,
+                                            const f32x4 (&acc)[D / 16], float m, float l,
+                                            float out_scale) {
+  constexpr int CB = D / 16, SD = merge_row_floats<D>();
+  constexpr int TPR = 16, DPT = D / TPR;    // threads per row, dims per thread
+  static_assert(DPT % 4 == 0, "float4 columns");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  float* so = reinterpret_cast<float*>(smem);           // [waves][16][SD]
+  float* sm_m = so + kMfmaWaves * 16 * SD;              // [waves][16]
+  float* sm_l = sm_m + kMfmaWaves * 16;                 // [waves][16]
+  __syncthreads();                  // staging tiles / previous pass no longer read
+  if (n < nh) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      *reinterpret_cast<f32x4*>(so + (wave * 16 + n) * SD + 16 * cb + 4 * grp) = acc[cb];
+    if (grp == 0) { sm_m[wave * 16 + n] = m; sm_l[wave * 16 + n] = l; }
+  }
+  __syncthreads();
+  const int r = threadIdx.x / TPR, c = threadIdx.x - r * TPR;
+  if (r >= nh) return;
+  float mw[kMfmaWaves];
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kMfmaWaves; ++w) {
+    mw[w] = sm_m[w * 16 + r];
+    M = fmaxf(M, mw[w]);
+  }
+  const float ref = M == kNegInf ? 0.f : M;
+  float a[kMfmaWaves];
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMfmaWaves; ++w) {
+    a[w] = exp2f(mw[w] - ref);
+    sum += sm_l[w * 16 + r] * a[w];
+  }
+  // every token of the split masked (invalid blocks, the window's bound):
+  // an empty softmax
+  const float inv = sum > 0.f ? out_scale / sum : 0.f;
+  const float lse2 = sum > 0.f ? ref + log2f(sum) : kNegInf;
+  f32x4 o[DPT / 4];
+#pragma unroll
+  for (int k = 0; k < DPT / 4; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kMfmaWaves; ++w)
+#pragma unroll
+    for (int k = 0; k < DPT / 4; ++k)
+      o[k] += *reinterpret_cast<const f32x4*>(so + (w * 16 + r) * SD + c * DPT + 4 * k) * a[w];
+  const int64_t h = query_row(p, b, g, hb + r);
+  float* dst;
+  if (p.direct) {
+    dst = p.out + h * D;
+    if (c == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
+  } else {
+    const int64_t pr = h * p.n_splits + split;
+    dst = p.part_o + pr * D;
+    if (c == 0) p.part_lse[pr] = lse2;
+  }
+#pragma unroll
+  for (int k = 0; k < DPT / 4; ++k)
+    *reinterpret_cast<f32x4*>(dst + c * DPT + 4 * k) = o[k] * inv;
+}
+
 }  // namespace mt
 }  // namespace kvd
