@@ -1,0 +1,383 @@
+// Causal prefill attention on the matrix cores: T new tokens per sequence (a
+// prompt, or one chunk of it appended after a cached history), query t
+// attending the tokens j < L_b - T + 1 + t.
+//
+// "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践" §4.2 describes the
+// tiled attention that keeps score blocks on chip and carries an online
+// softmax across key blocks; §5.1 b.v the causal mask.  Unlike the decode
+// step, prefill is a dense contraction (every query row meets every key
+// tile below its bound), so this kernel is organised for the MFMA pipe:
+//
+//  * a workgroup owns 128 query rows of one KV head -- the n_rep query heads
+//    of 128 / n_rep consecutive new tokens -- and walks the key tiles below
+//    their bounds, 32 tokens at a time;
+//  * each key tile is copied HBM -> LDS once (every wave issues a quarter of
+//    the copies, double-buffered, one barrier per tile) and read by all four
+//    waves, each of which owns 32 of the rows: the GQA group shares every
+//    tile, and no merge across waves is needed at the end;
+//  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
+//    A = K rows from LDS, B = the wave's q rows held in registers), so that
+//    each query row's scores and accumulators live in one lane column and
+//    the online softmax needs only two cross-lane shuffles;
+//  * O^T = V^T P^T with V^T gathered from the staged tile as in the decode
+//    kernel.
+//
+// Arithmetic: q (times scale * log2 e) and the probabilities enter the
+// matrix cores rounded once to bf16, accumulation is fp32, and the running
+// sum adds the rounded probabilities, so the output is an exact convex
+// combination of V rows with weights accurate to bf16.  This is the
+// precision of FlashAttention-2 in bf16; the decode kernels carry q and P
+// as bf16 hi + lo pairs instead, at twice the matrix-core work, which the
+// bandwidth-bound decode step does not notice but the compute-bound
+// prefill would.
+#include "mfma_tile.h"
+
+namespace kvd {
+namespace {
+
+using namespace mt;
+
+constexpr int kPfWaves = 4;
+constexpr int kPfCols = 32;                      // query rows per wave (two column blocks)
+constexpr int kPfRows = kPfWaves * kPfCols;      // query rows per workgroup
+constexpr int kPfTT = 32;                        // key tokens per tile
+
+template <int D>
+struct PfGeo {
+  static constexpr int KB = D / 32;              // 32-dim blocks of the score contraction
+  static constexpr int CB = D / 16;              // 16-dim blocks of the output
+  static constexpr int NDC = D / 8;              // 16-byte chunks of a K row
+  static constexpr int kKBytes = kPfTT * 2 * D;  // staged K tile
+  static constexpr int NKI = kKBytes / 1024;     // K copy instructions per tile
+  static constexpr int TPI = 64 / NDC;           // K rows per copy instruction
+  using VG = Geo<D>;                             // V tile: the decode kernel's layout
+  static constexpr int kVBytes = VG::kTileBytes;
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static_assert(NKI % kPfWaves == 0 && VG::NVL % kPfWaves == 0, "copies split over the waves");
+  // Chunk dc of K row t is stored at slot dc ^ swz(t) of the row: the 16
+  // rows one A-operand read touches then fall into 16 different bank
+  // groups (row t's chunk at t * 2D + 16 (dc ^ swz(t)) bytes).
+  __device__ __forceinline__ static int swz(int t) {
+    return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
+  }
+};
+
+// Four (D = 128) or two (D = 64) 16-byte K operands from LDS, waiting for
+// their own reads.  Inline assembly for the reason given at gather_v: a
+// compiler-visible LDS read would first wait for the next tile's copies.
+__device__ __forceinline__ void read_k(const uint32_t (&a)[4], bf16x8 (&k)[4]) {
+  u32x4 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  k[0] = __builtin_bit_cast(bf16x8, r0);
+  k[1] = __builtin_bit_cast(bf16x8, r1);
+  k[2] = __builtin_bit_cast(bf16x8, r2);
+  k[3] = __builtin_bit_cast(bf16x8, r3);
+}
+__device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
+  u32x4 r0, r1;
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a[0]), "v"(a[1]));
+  k[0] = __builtin_bit_cast(bf16x8, r0);
+  k[1] = __builtin_bit_cast(bf16x8, r1);
+}
+
+// Workgroup x: query-row tile nqt - 1 - x / (B G) (the tiles with the most
+// keys first), sequence and KV head from x mod B G.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
+  using PG = PfGeo<D>;
+  using VG = Geo<D>;
+  constexpr int KB = PG::KB, CB = PG::CB, NB = kPfCols / 16;
+  __shared__ __align__(16) char smem[2 * PG::kBufBytes];
+
+  const int R = p.R, T = p.T;
+  const int64_t ncols = static_cast<int64_t>(T) * R;
+  const int nqt = static_cast<int>((ncols + kPfRows - 1) / kPfRows);
+  const int bg = static_cast<int>(blockIdx.x % (p.B * p.G));
+  const int qt = nqt - 1 - static_cast<int>(blockIdx.x / (p.B * p.G));
+  const int g = bg % p.G, b = bg / p.G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+
+  int L = scalar_load_i32(p.seq_lens + b);
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int win = L - T + 1;                      // query t sees the tokens j < win + t
+  const int64_t c0 = static_cast<int64_t>(qt) * kPfRows;
+  const int64_t c_last = (c0 + kPfRows < ncols ? c0 + kPfRows : ncols) - 1;
+  // keys any row of the workgroup sees; the smallest bound of this wave's rows
+  int kmax = win + static_cast<int>(c_last / R);
+  kmax = kmax < L ? kmax : L;
+  const int64_t cw = c0 + wave * kPfCols;
+  const int wbound = win + static_cast<int>((cw < ncols ? cw : c_last) / R);
+
+  // the lane's query rows: column nb*16 + n of the wave
+  int cbound[NB];
+  int64_t qrow[NB];
+  bool real[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t c = cw + nb * 16 + n;
+    real[nb] = c < ncols;
+    const int t = static_cast<int>((real[nb] ? c : 0) / R);
+    const int r = static_cast<int>((real[nb] ? c : 0) - static_cast<int64_t>(t) * R);
+    cbound[nb] = real[nb] ? win + t : 0;
+    qrow[nb] = (static_cast<int64_t>(b) * T + t) * p.H + g * R + r;
+  }
+  // q * scale * log2(e) rounded to bf16: lane (n, grp) of block (nb, kb)
+  // holds dims kb*32 + grp*8 .. +7 of its row
+  bf16x8 qv[NB][KB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float* src = p.q_rot + qrow[nb] * D + grp * 8;
+    const float qs = real[nb] ? p.qscale : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const float4 x0 = *reinterpret_cast<const float4*>(src + kb * 32);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + kb * 32 + 4);
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      u16x8 h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = bf16_bits(xv[j] * qs);
+      qv[nb][kb] = __builtin_bit_cast(bf16x8, h);
+    }
+  }
+
+  // bytes between consecutive tokens of one KV head, and the start of this
+  // (sequence, KV head) -- of KV head g of the pool when paged
+  const int64_t rs = static_cast<int64_t>(p.G) * (2 * D);
+  const int64_t head0 = (PAGED ? 0 : static_cast<int64_t>(b) * p.max_seq_len * rs) +
+                        static_cast<int64_t>(g) * (2 * D);
+  const char* kbase = static_cast<const char*>(p.k) + head0;
+  const char* vbase = static_cast<const char*>(p.v) + head0;
+
+  // One descriptor per 16-token half of a tile and operand, spanning the
+  // valid rows (below kmax, in a valid block): other rows read as zeros
+  // without touching memory.
+  struct TileSrc { rsrc_t k[2], v[2]; bool ok[2]; };
+  auto tile_src = [&](int j0) {
+    TileSrc ts;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lo = j0 + 16 * h;
+      int rows = kmax - lo;
+      rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+      int64_t off;
+      ts.ok[h] = true;
+      if (PAGED) {
+        const int blk = rows > 0 ? paged_group(p, b, lo >> 4) : 0;
+        if (blk < 0) { rows = 0; ts.ok[h] = false; }
+        off = static_cast<int64_t>(blk < 0 ? 0 : blk) * 16 * rs;
+      } else {
+        off = static_cast<int64_t>(lo) * rs;
+      }
+      rows = __builtin_amdgcn_readfirstlane(rows);
+      const uint32_t bytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(rs);
+      ts.k[h] = make_rsrc(kbase + off, bytes);
+      ts.v[h] = make_rsrc(vbase + off, bytes);
+    }
+    return ts;
+  };
+  // this wave's quarter of a tile's copies: K instructions wave + 4 i (each
+  // 64 16-byte chunks, rows jj * TPI ..), V instructions likewise (rows
+  // jj * RPI .., the decode kernel's layout)
+  uint32_t koffc[PG::NKI / kPfWaves];
+#pragma unroll
+  for (int i = 0; i < PG::NKI / kPfWaves; ++i) {
+    const int jj = wave + kPfWaves * i;
+    const int u = jj * 64 + lane;
+    const int t = u / PG::NDC, slot = u % PG::NDC;
+    const int dc = slot ^ PG::swz(t);
+    koffc[i] = static_cast<uint32_t>((t & 15) * rs + dc * 16);
+  }
+  const uint32_t vlane = static_cast<uint32_t>((lane / VG::LPR) * rs + (lane % VG::LPR) * 16);
+  lds_char* const buf0 = (lds_char*)(smem);
+  auto issue = [&](const TileSrc& ts, int sel) {
+    lds_char* kb_ = buf0 + sel * PG::kBufBytes;
+#pragma unroll
+    for (int i = 0; i < PG::NKI / kPfWaves; ++i) {
+      const int jj = wave + kPfWaves * i;
+      const int h = (jj * PG::TPI) >> 4;
+      copy16_to_lds(h == 0 ? ts.k[0] : ts.k[1], kb_ + jj * 1024, koffc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VG::NVL / kPfWaves; ++i) {
+      const int jj = wave + kPfWaves * i;
+      const int h = (jj * VG::RPI) >> 4;
+      const uint32_t off = vlane + static_cast<uint32_t>(((jj * VG::RPI) & 15) * rs);
+      copy16_to_lds(h == 0 ? ts.v[0] : ts.v[1], kb_ + PG::kKBytes + jj * VG::BLOCK, off);
+    }
+  };
+  // V rows this wave copied that hold no valid token become zeros (an
+  // out-of-range copy leaves LDS as it was, and 0 * stale must stay 0)
+  auto zero_invalid_v = [&](const TileSrc& ts, int j0, int sel) {
+    const uint32_t vb = lds_addr(buf0 + sel * PG::kBufBytes + PG::kKBytes);
+#pragma unroll
+    for (int i = 0; i < VG::NVL / kPfWaves; ++i) {
+      const int jj = wave + kPfWaves * i;
+      const int r = jj * VG::RPI + lane / VG::LPR;
+      const bool ok = (jj * VG::RPI) >> 4 == 0 ? ts.ok[0] : ts.ok[1];
+      if (!(j0 + r < kmax && ok)) lds_zero16(vb + jj * VG::BLOCK + lane * 16);
+    }
+  };
+
+  // LDS read offsets of the lane's K operands: row 16 h2 + n, chunk kb*4 + grp
+  uint32_t koff[2][KB];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int t = 16 * h2 + n;
+      koff[h2][kb] = static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
+    }
+  const uint32_t vrd = static_cast<uint32_t>(VG::at(4 * grp, 2 * n));
+
+  f32x4 acc[NB][CB];
+  float m[NB], l[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf; l[nb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nkt = kmax > 0 ? (kmax + kPfTT - 1) / kPfTT : 0;
+  TileSrc cur;
+  if (nkt > 0) {
+    cur = tile_src(0);
+    issue(cur, 0);
+  }
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * kPfTT;
+    const int sel = kt & 1;
+    vmem_wait<0>();                    // this wave's copies of tile kt have landed
+    if (j0 + kPfTT > kmax || !cur.ok[0] || !cur.ok[1]) zero_invalid_v(cur, j0, sel);
+    __syncthreads();                   // every wave's copies of tile kt; tile kt - 1 no longer read
+    const TileSrc now = cur;
+    if (kt + 1 < nkt) {
+      cur = tile_src(j0 + kPfTT);
+      issue(cur, sel ^ 1);
+    }
+    const uint32_t kaddr = lds_addr(buf0 + sel * PG::kBufBytes);
+    const uint32_t vaddr = kaddr + PG::kKBytes + vrd;
+    const bool masked = j0 + kPfTT > wbound || !now.ok[0] || !now.ok[1];   // wave-uniform
+
+    // S^T: token rows 16 h2 + 4 grp + j, lane column n of block nb
+    f32x4 s[NB][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint32_t a[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[kb] = kaddr + koff[h2][kb];
+      bf16x8 ka[KB];
+      read_k(a, ka);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) c = mfma(ka[kb], qv[nb][kb], c);
+        s[nb][h2] = c;
+      }
+    }
+
+    bf16x8 pb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j];
+      if (masked) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = j0 + 16 * h2 + 4 * grp + j;
+            if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
+          }
+      }
+      float mt = sv[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
+        const float mn = fmaxf(m[nb], mt);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        l[nb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
+        m[nb] = mn;
+      }
+      const float ref = m[nb] == kNegInf ? 0.f : m[nb];
+      u16x8 h;
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[j] = bf16_bits(__builtin_amdgcn_exp2f(sv[j] - ref));
+        ps += bf16_value(h[j]);        // the sum of the weights P V uses
+      }
+      l[nb] += ps;
+      pb[nb] = __builtin_bit_cast(bf16x8, h);
+    }
+
+    // O^T[d][row] += V^T[d][t] P^T[t][row]
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const bf16x8 av = gather_v<D>(vaddr + cb * 32);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb][cb] = mfma(av, pb[nb], acc[nb][cb]);
+    }
+  }
+
+  // the four lane groups of a column hold partial sums under one max
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    l[nb] += __shfl_xor(l[nb], 16);
+    l[nb] += __shfl_xor(l[nb], 32);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (!real[nb]) continue;
+    const float inv = l[nb] > 0.f ? 1.f / l[nb] : 0.f;
+    float* dst = p.out + qrow[nb] * D + 4 * grp;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
+    if (grp == 0 && p.lse)
+      p.lse[qrow[nb]] = l[nb] > 0.f ? (m[nb] + log2f(l[nb])) * 0.69314718055994531f : kNegInf;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
+  if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  const int64_t ncols = static_cast<int64_t>(p.T) * p.R;
+  const int64_t nqt = (ncols + kPfRows - 1) / kPfRows;
+  const int64_t wgs = nqt * p.B * p.G;
+  if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  if (p.D == 64) {
+    if (paged) prefill_kernel<64, true><<<grid, 256, 0, s>>>(p);
+    else prefill_kernel<64, false><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (paged) prefill_kernel<128, true><<<grid, 256, 0, s>>>(p);
+    else prefill_kernel<128, false><<<grid, 256, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvd
