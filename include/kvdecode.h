@@ -275,9 +275,10 @@ size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_hos
  * together: at most 32 of them (bf16 and INT8 caches).  fp32 caches take
  * n_query = 1 only.
  * Errors: as the single-token calls; EUNSUPPORTED for n_query outside
- * [1, 32], more than 32 query rows per KV head, or fp32 with n_query > 1;
- * EINVAL when scales are given for a non-INT8 cache or missing for an INT8
- * one.
+ * [1, max_seq_len] (rope_append_kv_multi) or [1, 32] (gqa_decode_attn_multi),
+ * more than 32 query rows per KV head, or fp32 with n_query > 1; EINVAL when
+ * scales are given for a non-INT8 cache or missing for an INT8 one.  Longer
+ * windows (prompts, chunks of prompts) go through gqa_prefill_attn.
  */
 kvd_status rope_append_kv_multi(const kvd_shape* shape, int32_t n_query, const void* q,
                                 const void* k_new, const void* v_new, float* q_rot,
@@ -291,6 +292,35 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
                                  const int32_t* block_table, int32_t max_seq_len_host,
                                  float scale, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
+/*
+ * gqa_prefill_attn -- causal attention of a prompt, or of one chunk of a
+ * prompt appended after a cached history: n_query = T new tokens per
+ * sequence, already rotated and appended by rope_append_kv_multi, over a
+ * bf16 cache (contiguous or paged).  The result is that of
+ * gqa_decode_attn_multi for any T: with L_b = seq_lens[b] (the new tokens
+ * included), query t of sequence b attends the tokens j < L_b - T + 1 + t
+ * ([KVGR] §5.1 b.v causal mask; the tiled online-softmax attention of
+ * [KVGR] §4.2, here on the matrix cores).
+ *
+ * Arithmetic: q * scale and the softmax probabilities are rounded once to
+ * bf16 for the matrix cores, accumulation is fp32, and each row's weights
+ * are normalised by their own sum (the precision of FlashAttention-2 in
+ * bf16: about 1e-3 relative per output element, where gqa_decode_attn_multi
+ * keeps q and P to ~2^-17).  No workspace: each query row's output is
+ * finished by one workgroup.
+ *
+ *   q_rot      [B, T, H, D] fp32; out [B, T, H, D] fp32; lse [B, T, H] fp32
+ *              (natural log) or NULL
+ *   k_cache, v_cache, seq_lens, block_table, max_seq_len_host, scale
+ *              as in gqa_decode_attn
+ * Errors: EINVAL, ERANGE as gqa_decode_attn; EUNSUPPORTED for a cache dtype
+ * other than bf16 or n_query outside [1, max_seq_len]; EHIP.
+ */
+kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, int32_t max_seq_len_host, float scale,
+                            float* out, float* lse, void* stream);
+
 /* Workspace bytes of gqa_decode_attn_multi (0 also for an invalid shape). */
 size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,
                                        int32_t max_seq_len_host);

@@ -44,7 +44,7 @@ class Shape(ctypes.Structure):
 
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
-            "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi",
+            "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_set_tuning", "kvd_set_tuning_ex",
             "kvd_timer_begin",
             "kvd_timer_end", "kvd_read_probe")
@@ -89,6 +89,8 @@ def load_library():
         lib.gqa_decode_attn_multi.restype = I32
         lib.gqa_decode_attn_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_float,
                                               P, P, P, ctypes.c_size_t, P]
+        lib.gqa_prefill_attn.restype = I32
+        lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, P]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -483,6 +485,43 @@ def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                                      _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
                                      _ptr(block_table), msl, float(scale), _ptr(out), _ptr(lse),
                                      _ptr(workspace), wbytes, _stream(dev)))
+    return out, lse
+
+
+def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Causal attention of T new tokens per sequence (a prompt or a chunk of
+    one, already appended), q_rot [B, T, H, D], over a bf16 cache; query t
+    attends the tokens j < seq_lens[b] - T + 1 + t.  q and P enter the matrix
+    cores as bf16.  Returns (out [B, T, H, D], lse [B, T, H])."""
+    lib = load_library()
+    dev = k_cache.device
+    B, T, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, T, H, D))
+    _need(k_cache, "k_cache", dev, torch.bfloat16)
+    _need(v_cache, "v_cache", dev, torch.bfloat16, tuple(k_cache.shape))
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if shape.head_dim != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (B, T, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dev, torch.float32, (B, T, H))
+    _check(lib.gqa_prefill_attn(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(seq_lens), _ptr(block_table), msl, float(scale), _ptr(out),
+                                _ptr(lse), _stream(dev)))
     return out, lse
 
 

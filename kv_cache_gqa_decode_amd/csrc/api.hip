@@ -301,7 +301,7 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
                        void* stream, int32_t T = 1) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
-  if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
+  if (T < 1 || T > shape->max_seq_len) return KVD_EUNSUPPORTED;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
   if (!k_new || !v_new || !k_cache || !v_cache || !positions) return KVD_EINVAL;
   if (q && !q_rot) return KVD_EINVAL;
@@ -404,6 +404,36 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
   return decode_impl(shape, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
                      max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream,
                      n_query);
+}
+
+kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, int32_t max_seq_len_host, float scale,
+                            float* out, float* lse, void* stream) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (shape->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+  if (n_query < 1 || n_query > shape->max_seq_len) return KVD_EUNSUPPORTED;
+  if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
+  if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
+  if (!std::isfinite(scale)) return KVD_EINVAL;
+  const bool paged = shape->block_size != 0;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (shape->batch == 0) return KVD_OK;
+  DecodeParams p{};
+  p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G; p.T = n_query;
+  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
+  p.qscale = scale * 1.4426950408889634f;
+  return launch_prefill_mfma(p, paged, static_cast<hipStream_t>(stream)) == hipSuccess ? KVD_OK
+                                                                                      : KVD_EHIP;
 }
 
 }  // extern "C"

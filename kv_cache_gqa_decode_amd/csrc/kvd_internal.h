@@ -74,6 +74,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool page
                               int rb, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t stream);
+// causal prefill of p.T new tokens per sequence (p.qscale, no splits)
+hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_build_units(const DecodeParams& p, hipStream_t stream);
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).

@@ -23,13 +23,14 @@
 //    kernel.
 //
 // Arithmetic: q (times scale * log2 e) and the probabilities enter the
-// matrix cores rounded once to bf16, accumulation is fp32, and the running
-// sum adds the rounded probabilities, so the output is an exact convex
-// combination of V rows with weights accurate to bf16.  This is the
-// precision of FlashAttention-2 in bf16; the decode kernels carry q and P
-// as bf16 hi + lo pairs instead, at twice the matrix-core work, which the
-// bandwidth-bound decode step does not notice but the compute-bound
-// prefill would.
+// matrix cores rounded once to bf16, accumulation is fp32.  Two running
+// sums are kept: of the rounded probabilities, which normalises the output
+// (an exact convex combination of V rows, weights accurate to bf16), and of
+// the fp32 ones, which gives the log-sum-exp (off by the score rounding
+// only).  This is the precision of FlashAttention-2 in bf16; the decode
+// kernels carry q and P as bf16 hi + lo pairs instead, at twice the
+// matrix-core work, which the bandwidth-bound decode step does not notice
+// but the compute-bound prefill would.
 #include "mfma_tile.h"
 
 namespace kvd {
@@ -244,10 +245,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
   const uint32_t vrd = static_cast<uint32_t>(VG::at(4 * grp, 2 * n));
 
   f32x4 acc[NB][CB];
-  float m[NB], l[NB];
+  float m[NB], l[NB], lx[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = kNegInf; l[nb] = 0.f;
+    m[nb] = kNegInf; l[nb] = 0.f; lx[nb] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -317,19 +318,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
         const float mn = fmaxf(m[nb], mt);
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         l[nb] *= alpha;
+        lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
         m[nb] = mn;
       }
       const float ref = m[nb] == kNegInf ? 0.f : m[nb];
       u16x8 h;
-      float ps = 0.f;
+      float ps = 0.f, px = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        h[j] = bf16_bits(__builtin_amdgcn_exp2f(sv[j] - ref));
+        const float e = __builtin_amdgcn_exp2f(sv[j] - ref);
+        h[j] = bf16_bits(e);
         ps += bf16_value(h[j]);        // the sum of the weights P V uses
+        px += e;
       }
       l[nb] += ps;
+      lx[nb] += px;
       pb[nb] = __builtin_bit_cast(bf16x8, h);
     }
 
@@ -347,6 +352,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
   for (int nb = 0; nb < NB; ++nb) {
     l[nb] += __shfl_xor(l[nb], 16);
     l[nb] += __shfl_xor(l[nb], 32);
+    lx[nb] += __shfl_xor(lx[nb], 16);
+    lx[nb] += __shfl_xor(lx[nb], 32);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
     for (int cb = 0; cb < CB; ++cb)
       *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
     if (grp == 0 && p.lse)
-      p.lse[qrow[nb]] = l[nb] > 0.f ? (m[nb] + log2f(l[nb])) * 0.69314718055994531f : kNegInf;
+      p.lse[qrow[nb]] = lx[nb] > 0.f ? (m[nb] + log2f(lx[nb])) * 0.69314718055994531f : kNegInf;
   }
 }
 

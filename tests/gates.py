@@ -10,6 +10,17 @@
   scales, so the only difference is arithmetic (products of exact codes
   with q to ~2^-22 and p to ~2^-21, fp32 accumulation); quantisation error
   is not part of the comparison.
+* Causal prefill (gqa_prefill_attn, dtype "prefill"): q * scale and the
+  probabilities enter the matrix cores rounded once to bf16, as in
+  FlashAttention-2 in bf16.  Rounding each weight to bf16 perturbs it by up
+  to 2^-9 relative (1.1e-3 rms), and since the weights are normalised by
+  their own sum the output error is that perturbation averaged over V:
+  about 1e-3 relative per element.  lse comes from the sum of the unrounded
+  probabilities, so only the rounding of q moves it.  An fp64 emulation of
+  exactly these roundings (rows of 2 to 2000 tokens, q gain 1 to 32) gave
+  normwise output errors of 1.5e-3 to 3.0e-3 and lse errors up to 1.5e-3 *
+  max(1, |lse|) (2 tokens at q gain 32; 3e-4 otherwise).  Gates: max abs
+  <= 1e-2 (the bf16 gate), normwise <= 1e-2, lse <= 5e-3 * max(1, |r|).
 * lse (natural log): |g - r| <= tol_lse * max(1, |r|).
 * Cache append and block-table indexing: bit-exact.
 """
@@ -18,7 +29,8 @@ import numpy as np
 FP32_NORM_TOL = 1e-5
 BF16_ABS_TOL = 1e-2
 BF16_NORM_TOL = 1e-3
-LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "i8": 1e-4}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "i8": 1e-4, "prefill": 5e-3}
+PREFILL_NORM_TOL = 1e-2
 
 
 def normwise_rel_err(got, ref) -> float:
@@ -44,6 +56,8 @@ def out_ok(got, ref, dtype) -> bool:
         return False
     if dtype == "f32":
         return e["normwise"] <= FP32_NORM_TOL
+    if dtype == "prefill":
+        return e["max_abs"] <= BF16_ABS_TOL and e["normwise"] <= PREFILL_NORM_TOL
     return e["max_abs"] <= BF16_ABS_TOL and e["normwise"] <= BF16_NORM_TOL
 
 

@@ -153,8 +153,9 @@ def attn_m(lib, sh, T, ks=None, vs=None, msl=32):
 def test_multi_calls_validate(lib):
     bf, i8 = shape(), shape(kv_dtype=2)
     assert rope_m(lib, None, 2) == EINVAL and attn_m(lib, None, 2) == EINVAL
-    for T in (0, -1, 33):
+    for T in (0, -1, 65):                # the window must fit the cache (64 slots)
         assert rope_m(lib, bf, T) == EUNSUPPORTED
+    for T in (0, -1, 33):                # the decode kernels take up to 32 query rows
         assert attn_m(lib, bf, T) == EUNSUPPORTED
     # scales exactly for INT8 caches
     assert rope_m(lib, bf, 2, ks=FAKE, vs=FAKE) == EINVAL
@@ -165,6 +166,25 @@ def test_multi_calls_validate(lib):
     assert attn_m(lib, shape(batch=0), 5) == OK
     assert attn_m(lib, shape(kv_dtype=2, batch=0), 5, ks=FAKE, vs=FAKE) == OK
     assert lib.gqa_decode_workspace_size_multi(ctypes.byref(bf), 0, 10) == 0
+
+
+def prefill(lib, sh, T, q=FAKE, lens=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000)):
+    return lib.gqa_prefill_attn(ctypes.byref(sh) if sh is not None else None, T, q, FAKE, FAKE,
+                                lens, table, msl, 0.125, out, None, None)
+
+
+def test_prefill_validates(lib):
+    assert prefill(lib, None, 4) == EINVAL
+    assert prefill(lib, shape(kv_dtype=0), 4) == EUNSUPPORTED          # fp32 cache
+    assert prefill(lib, shape(kv_dtype=2), 4) == EUNSUPPORTED          # INT8 cache
+    for T in (0, -3, 65):
+        assert prefill(lib, shape(), T) == EUNSUPPORTED
+    assert prefill(lib, shape(), 4, q=None) == EINVAL
+    assert prefill(lib, shape(), 4, lens=None) == EINVAL
+    assert prefill(lib, shape(), 4, out=FAKE) == EINVAL                # out aliases q_rot
+    assert prefill(lib, shape(), 4, table=FAKE) == EINVAL
+    assert prefill(lib, shape(), 4, msl=65) == ERANGE
+    assert prefill(lib, shape(batch=0), 64) == OK
 
 
 def test_tuning_and_timer_validation(lib):

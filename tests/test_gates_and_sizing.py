@@ -88,3 +88,38 @@ def test_fp32_gate_rejects_bf16_level_error():
     ref = rng.standard_normal((8, 64))
     assert gates.out_ok(ref * (1 + 1e-7), ref, "f32")
     assert not gates.out_ok(ref + 2.0**-8 * np.abs(ref).max(), ref, "f32")
+
+
+def test_prefill_gate_rejects_planted_mistakes():
+    """The looser prefill gate (bf16 q and P) still rejects the mistakes a
+    causal prefill kernel can make: an off-by-one causal bound, a missing
+    mask inside the window, a dropped history and the h mod G mapping."""
+    T, B, H, G, D = 24, 2, 8, 2, 64
+    s = W.spec("c3", batch=B, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=256, q_gain=2.0)
+    L = np.array([T, 200], np.int32)
+    p = W.make_window(s, T, lengths=L)
+    g = oracle.Geometry(B, H, G, D, "bf16", max_seq_len=s.max_seq_len)
+    kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, n_query=T)
+    ref, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, n_query=T)
+    assert gates.out_ok(ref, ref, "prefill") and gates.lse_ok(lse, lse, "prefill")
+    # one token too few for every query (the bound taken exclusive of the query's own token)
+    short, sl = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens - 1, n_query=T)
+    short[0, 0] = 0.0                  # query 0 of an empty history then sees nothing
+    assert not gates.out_ok(short, ref, "prefill")
+    # no mask inside the window: every query sees all T new tokens
+    flat = oracle.Geometry(B * T, H, G, D, "bf16", max_seq_len=s.max_seq_len)
+    kk = np.repeat(kc, T, axis=0); vv = np.repeat(vc, T, axis=0)
+    unmasked, _ = oracle.decode_attn(flat, np.ascontiguousarray(q_rot.reshape(B * T, H, D)), kk,
+                                     vv, np.repeat(p.seq_lens, T))
+    assert not gates.out_ok(unmasked.reshape(ref.shape), ref, "prefill")
+    # the history of sequence 1 dropped (only the window attended)
+    kz, vz = kc.copy(), vc.copy()
+    kz[1, :200 - T] = 0; vz[1, :200 - T] = 0
+    nohist, _ = oracle.decode_attn(g, q_rot, kz, vz, p.seq_lens, n_query=T)
+    assert not gates.out_ok(nohist, ref, "prefill")
+    # GQA mapping h -> h mod G
+    perm = np.array([(h % G) * (H // G) + h // G for h in range(H)])
+    wrong, _ = oracle.decode_attn(g, np.ascontiguousarray(q_rot[:, :, perm]), kc, vc, p.seq_lens,
+                                  n_query=T)
+    assert not gates.out_ok(wrong[:, :, np.argsort(perm)], ref, "prefill")

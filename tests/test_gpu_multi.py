@@ -47,19 +47,27 @@ def gpu_window(t, s: W.Spec, max_len: int, style="interleaved"):
 
 
 def oracle_window(p: W.Problem, style="interleaved", units=None):
+    """The oracle's step on a window problem; arrays keep the T axis (also
+    for T = 1, which the oracle takes in the single-token layout)."""
     s = p.spec
     g = geom(s)
+    T = p.n_query
+    one = T == 1 and p.q.ndim == 4
+    sq = (lambda a: np.ascontiguousarray(a[:, 0])) if one else (lambda a: a)
     kc, vc = p.k_cache.copy(), p.v_cache.copy()
     sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if s.dtype == "i8" else {}
-    q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, p.block_table,
-                               base=s.rope_base, style=style, n_query=p.n_query, **sc)
+    q_rot = oracle.rope_append(g, sq(p.q), sq(p.k_new), sq(p.v_new), kc, vc, p.positions,
+                               p.block_table, base=s.rope_base, style=style, n_query=T, **sc)
     if units is None:
-        out, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, p.block_table,
-                                      n_query=p.n_query, **sc)
+        out, lse = oracle.decode_attn(g, q_rot, kc, vc, p.seq_lens, p.block_table, n_query=T,
+                                      **sc)
+        if one:
+            out, lse = out[:, None], lse[:, None]
     else:
-        out, lse = oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, units, p.block_table,
-                                            n_query=p.n_query, **sc)
-    return q_rot, out, lse, kc, vc
+        u = [(b, h) for b, _, h in units] if one else units
+        out, lse = oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, u, p.block_table,
+                                            n_query=T, **sc)
+    return (q_rot[:, None] if one else q_rot), out, lse, kc, vc
 
 
 def check_window(p: W.Problem, split=0, style="interleaved", what=""):

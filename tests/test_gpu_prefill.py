@@ -1,0 +1,157 @@
+"""GPU parity of the causal prefill (gqa_prefill_attn after
+rope_append_kv_multi) against the oracle's multi-token step on the same
+seeded inputs.
+
+A prompt is the window of T new tokens on an empty history; a chunk of a
+prompt is the same window after a cached history.  Query t attends the
+tokens j < L_b - T + 1 + t ([KVGR] §5.1 b.v inside the window; the tiled
+attention of [KVGR] §4.2).  The caches must match bit for bit; outputs and
+lse pass the prefill gates (bf16 q and probabilities on the matrix cores:
+max abs <= 1e-2, normwise <= 1e-2, lse <= 5e-3 relative).  Small cases
+compare every element; long prompts compare sampled (b, t, h) rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_gqa_decode_amd as kvd
+from kv_cache_gqa_decode_amd import workloads as W
+from tests import gates
+from tests.gpu_helpers import device, upload
+from tests.test_gpu_multi import oracle_window, _bits
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(t, s: W.Spec, max_len: int, style="interleaved"):
+    q_rot = kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                     t["positions"], t["block_table"], base=s.rope_base,
+                                     style=style)
+    out, lse = kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
+                                    t["block_table"], max_seq_len=max_len)
+    torch.cuda.synchronize()
+    return q_rot, out, lse
+
+
+def check_prefill(p: W.Problem, what="", units=None, style="interleaved"):
+    dev = device()
+    s = p.spec
+    print(f"[prefill] {what}", flush=True)
+    t = upload(p, dev)
+    q_rot, out, lse = gpu_prefill(t, s, p.max_len, style=style)
+    oq, oo, ol, okc, ovc = oracle_window(p, style=style, units=units)
+    assert torch.equal(_bits(t["k_cache"]), _bits(W.as_torch(okc, dev))), f"{what}: K cache"
+    assert torch.equal(_bits(t["v_cache"]), _bits(W.as_torch(ovc, dev))), f"{what}: V cache"
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    if units is not None:
+        ub, ut, uh = ([u[i] for u in units] for i in range(3))
+        go, gl = go[ub, ut, uh], gl[ub, ut, uh]
+    else:
+        qr = q_rot.cpu().numpy()
+        ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
+        assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+    e = gates.assert_out(go, oo, "prefill", what)
+    gates.assert_lse(gl, ol, "prefill", what)
+    print(f"[prefill] {what}: {e}", flush=True)
+    return e
+
+
+def _spec(B, H, G, D, S, paged=False, block_size=16, q_gain=2.0):
+    if paged:
+        s = W.spec("c4", batch=B, n_heads=H, n_kv_heads=G, head_dim=D,
+                   num_blocks=B * (S // block_size) + 8, max_blocks_per_seq=S // block_size,
+                   block_size=block_size, q_gain=q_gain)
+    else:
+        s = W.spec("c3", batch=B, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=S,
+                   q_gain=q_gain)
+    return s
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 100, 257])
+def test_prompt_from_empty(D, T):
+    """A whole prompt: no history, query t sees tokens 0 .. t."""
+    s = _spec(2, 8, 2, D, 512)
+    p = W.make_window(s, T, lengths=np.array([T, T], np.int32))
+    check_prefill(p, what=f"prompt D={D} T={T}")
+
+
+@pytest.mark.parametrize("T", [16, 64, 100])
+@pytest.mark.parametrize("paged,block_size", [(False, 16), (True, 16), (True, 32)])
+def test_chunk_after_history(T, paged, block_size):
+    """A chunk of T tokens after ragged cached histories (the shortest has
+    none)."""
+    lens = np.array([T, T + 1, T + 15, T + 300, 900, 1024], np.int32)
+    s = _spec(lens.size, 32, 8, 128, 1024, paged, block_size)
+    p = W.make_window(s, T, lengths=lens)
+    check_prefill(p, what=f"chunk T={T} paged={paged}/{block_size}")
+
+
+@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16, 32])
+def test_gqa_ratios(n_rep):
+    H = 32
+    s = _spec(2, H, H // n_rep, 128, 640)
+    p = W.make_window(s, 150, lengths=np.array([150, 600], np.int32))
+    check_prefill(p, what=f"n_rep={n_rep}")
+
+
+@pytest.mark.parametrize("q_gain", [1.0, 8.0, 32.0])
+def test_peaked_scores(q_gain):
+    s = _spec(2, 32, 8, 128, 1024, q_gain=q_gain)
+    p = W.make_window(s, 200, lengths=np.array([200, 1000], np.int32))
+    check_prefill(p, what=f"q_gain={q_gain}")
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+def test_rope_styles(style):
+    s = _spec(2, 16, 4, 128, 256)
+    p = W.make_window(s, 64, lengths=np.array([64, 256], np.int32))
+    check_prefill(p, style=style, what=f"rope {style}")
+
+
+def test_matches_decode_multi_within_gates():
+    """For windows the decode kernels take (n_rep * T <= 32) the prefill and
+    the decode kernel agree within the prefill gate."""
+    dev = device()
+    s = _spec(4, 32, 8, 128, 1024)
+    p = W.make_window(s, 5, lengths=np.array([5, 100, 640, 1024], np.int32))
+    t = upload(p, dev)
+    q_rot = kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                     t["positions"])
+    o1, l1 = kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"])
+    o2, l2 = kvd.gqa_decode_attn_multi(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"])
+    torch.cuda.synchronize()
+    gates.assert_out(o1.cpu().numpy(), o2.cpu().numpy(), "prefill", "prefill vs decode")
+    gates.assert_lse(l1.cpu().numpy(), l2.cpu().numpy(), "prefill", "prefill vs decode lse")
+
+
+def test_zero_and_short_lengths():
+    """seq_lens below T (queries that see nothing) give out = 0, lse = -inf
+    for those queries, and the others match the oracle's bounds."""
+    dev = device()
+    s = _spec(3, 8, 2, 64, 128)
+    T = 10
+    p = W.make_window(s, T, lengths=np.array([T, 50, 128], np.int32))
+    t = upload(p, dev)
+    q_rot = kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                     t["positions"])
+    lens = torch.tensor([0, 4, 128], dtype=torch.int32, device=dev)
+    out, lse = kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], lens, max_seq_len=128)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert (o[0] == 0).all() and np.isneginf(l[0]).all()
+    # length 4 with T = 10: queries 0 .. 5 see nothing, query t >= 6 sees t - 5 tokens
+    assert (o[1, :6] == 0).all() and np.isneginf(l[1, :6]).all()
+    assert np.isfinite(l[1, 6:]).all() and np.isfinite(o[2]).all()
+
+
+def test_long_prompt_sampled():
+    """An 8192-token prompt at the 128K workload's head shape (H 32, G 8,
+    D 128): sampled rows against the oracle, caches in full."""
+    T = 8192
+    s = W.spec("c5", max_seq_len=T, q_gain=2.0)
+    p = W.make_window(s, T, lengths=np.array([T], np.int32))
+    rng = np.random.default_rng(71)
+    ts = np.r_[0, 1, 31, 32, 127, 128, T - 1, rng.integers(0, T, 25)]
+    units = [(0, int(t), int(h)) for t, h in zip(ts, rng.integers(0, s.n_heads, ts.size))]
+    check_prefill(p, units=units, what="prompt 8192")
