@@ -22,13 +22,20 @@ With --kv int8 the same workload runs on an INT8 cache (per-KV-head
 scales, rope_append_kv_int8 + gqa_decode_attn_int8); KV bytes then count one
 byte per element.
 
+With --prefill T the bench times a causal prefill instead: T new tokens per
+sequence (a prompt from empty when the workload's lengths equal T, e.g.
+--config c5 --prefill 131072; a chunk after the cached history otherwise),
+rope_append_kv_multi + gqa_prefill_attn, reported in TFLOP/s of attention
+(4 * head_dim flops per query head and attended key) against the 2.5 PFLOP/s
+bf16 matrix-core peak.
+
 With --n-query T each sequence brings T new tokens (the verification pass of
 speculative decoding: rope_append_kv_multi + gqa_decode_attn_multi); the KV
 bytes are unchanged (the T queries of a KV head share each tile), the step
 processes B * T tokens.
 
 Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
-                       [--kv-heads G] [--kv native|int8] [--n-query T]
+                       [--kv-heads G] [--kv native|int8] [--n-query T] [--prefill T]
                        [--kernel auto|valu|mfma] [--split N]
                        [--no-cpu-baseline] [--flush]
 """
@@ -53,6 +60,7 @@ KERNEL_SOURCES = {
     "mfma": ("decode_mfma.hip", "mfma_tile.h", "kvd_internal.h"),
     "int8": ("decode_i8.hip", "mfma_tile.h", "kvd_internal.h"),
     "valu": ("decode_valu.hip", "kvd_internal.h"),
+    "prefill": ("prefill_mfma.hip", "mfma_tile.h", "kvd_internal.h"),
 }
 
 
@@ -179,6 +187,123 @@ def cpu_baseline(s, p, budget_s: float):
                       f"{n / dt:.3g} seq-steps/s"}
 
 
+def prefill_cpu_baseline(s, p, T, budget_s: float):
+    """The oracle on sampled query rows of the prefill step (all host
+    threads): flops of the sampled rows / time, in TFLOP/s."""
+    import numpy as np
+    import oracle
+    g = oracle.Geometry(s.batch, s.n_heads, s.n_kv_heads, s.head_dim, s.dtype,
+                        max_seq_len=s.max_seq_len, block_size=s.block_size,
+                        num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
+    kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, p.block_table,
+                               base=s.rope_base, n_query=T)
+    rng = np.random.default_rng(97)
+    threads = oracle.default_threads()
+
+    def run(n):
+        units = [(int(b), int(t), int(h)) for b, t, h in
+                 zip(rng.integers(0, s.batch, n), rng.integers(0, T, n),
+                     rng.integers(0, s.n_heads, n))]
+        keys = sum(max(0, min(int(p.seq_lens[b]), int(p.seq_lens[b]) - T + 1 + t))
+                   for b, t, _ in units)
+        t0 = time.perf_counter()
+        oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, units, p.block_table,
+                                 n_query=T, n_threads=threads)
+        return time.perf_counter() - t0, 4 * s.head_dim * keys
+
+    n = 8
+    dt, fl = run(n)
+    while dt < budget_s / 4 and n < 1 << 16:
+        n = max(n + 1, int(n * budget_s / 2 / max(dt, 1e-3)))
+        dt, fl = run(n)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly over (sequence, new token, head), "
+                      f"their attention over the causal bound in fp64: {dt:.3f} s"}
+
+
+def run_prefill(args, s, dev):
+    """Causal prefill of T new tokens per sequence: RoPE + append of the T
+    tokens, then gqa_prefill_attn.  Prints one JSON line in TFLOP/s."""
+    import numpy as np
+    import torch
+    import kv_cache_gqa_decode_amd as kvd
+    from kv_cache_gqa_decode_amd import sizing
+    from kv_cache_gqa_decode_amd import workloads as W
+    T = args.prefill
+    if s.dtype != "bf16":
+        print("--prefill runs on the bf16 workloads (c2..c5)", file=sys.stderr)
+        sys.exit(2)
+    if T > s.max_seq_len:
+        print(f"--prefill {T} exceeds the cache capacity {s.max_seq_len}", file=sys.stderr)
+        sys.exit(2)
+    t_gen = time.perf_counter()
+    p = W.make_window(s, T, lengths=np.clip(W.draw_lengths(s), T, s.max_seq_len))
+    print(f"# generated {s.name} prefill inputs in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    t = {k: W.as_torch(getattr(p, k), dev) for k in
+         ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
+    table = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
+    q_rot = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q_rot)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    max_len = p.max_len
+
+    def step():
+        kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                 t["positions"], table, base=s.rope_base, q_rot=q_rot)
+        kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
+                             max_seq_len=max_len, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    with kvd.kernel_timer(args.steps) as kt:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+    flops = sizing.window_attention_flops(p.seq_lens, T, H, D)
+    kern_ms = kt.mean_ms
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    result = {
+        "metric": "causal prefill attention TFLOP/s at 1 MI355X",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) values and lengths; no datasets or weights)",
+        "config": {"workload": workload_name(s) + f", prefill of {T} new tokens per sequence",
+                   "batch": B, "n_heads": H, "n_kv_heads": G, "head_dim": D,
+                   "new_tokens_per_seq": T, "total_context_tokens": int(p.seq_lens.sum()),
+                   "attended_keys": sizing.window_key_count(p.seq_lens, T),
+                   "flops_per_step": flops, "block_size": s.block_size,
+                   "arithmetic": "q and P rounded to bf16 on the matrix cores, fp32 accumulate",
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
+                     "kernel": "causal prefill attention", "kernel_ms": round(kern_ms, 4),
+                     "launches_timed": kt.count, "algorithmic_flops_per_launch": flops,
+                     "kernel_source_hash": kernel_source_hash("prefill")},
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = prefill_cpu_baseline(s, p, T, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,6 +317,9 @@ def main():
                     help="cache dtype: the workload's own (bf16 / fp32) or INT8 with per-head scales")
     ap.add_argument("--n-query", type=int, default=1,
                     help="new tokens per sequence (T > 1: the multi-token verification step)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="T > 0: time a causal prefill of T new tokens per sequence "
+                         "(rope_append_kv_multi + gqa_prefill_attn; bf16 workloads) instead")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--tail-split", type=int, default=0,
@@ -249,6 +377,9 @@ def main():
             print("--kv int8 applies to the bf16 workloads (c2..c5)", file=sys.stderr)
             sys.exit(2)
         s = s.replace(dtype="i8")
+    if args.prefill > 0:
+        run_prefill(args, s, dev)
+        return
     t_gen = time.perf_counter()
     T = args.n_query
     p = W.make_problem(s) if T == 1 else W.make_window(s, T)

@@ -367,8 +367,10 @@ kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_
 
 /*
  * Kernel timing for measurement.  kvd_timer_begin(n) makes the next n calls
- * of gqa_decode_attn record a pair of HIP events on their stream around the
- * split-K kernel's launch (n <= 4096).  kvd_timer_end waits for those events
+ * of the attention functions (gqa_decode_attn and its _int8 / _multi forms,
+ * gqa_prefill_attn) record a pair of HIP events on their stream around the
+ * launch of their main kernel -- the split-K kernel, the prefill kernel --
+ * (n <= 4096).  kvd_timer_end waits for those events
  * and returns the summed kernel time in milliseconds and the number of
  * launches timed, then disables timing.  Host pointers.
  */

@@ -36,6 +36,17 @@ struct Timer {
 };
 Timer g_timer;
 
+// The next pair of timing events while kvd_timer_begin is active (else the
+// pair stays null): recorded around the one timed kernel of a call.
+void timer_slot(hipEvent_t* start, hipEvent_t* stop) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.active && g_timer.used < g_timer.limit) {
+    *start = g_timer.start[g_timer.used];
+    *stop = g_timer.stop[g_timer.used];
+    ++g_timer.used;
+  }
+}
+
 int device_cu_count(int* cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -432,8 +443,13 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.qscale = scale * 1.4426950408889634f;
-  return launch_prefill_mfma(p, paged, static_cast<hipStream_t>(stream)) == hipSuccess ? KVD_OK
-                                                                                      : KVD_EHIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+  timer_slot(&ev_start, &ev_stop);
+  if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
+  if (launch_prefill_mfma(p, paged, s) != hipSuccess) return KVD_EHIP;
+  if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
+  return KVD_OK;
 }
 
 }  // extern "C"
@@ -502,14 +518,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   }
 
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_timer.mu);
-    if (g_timer.active && g_timer.used < g_timer.limit) {
-      ev_start = g_timer.start[g_timer.used];
-      ev_stop = g_timer.stop[g_timer.used];
-      ++g_timer.used;
-    }
-  }
+  timer_slot(&ev_start, &ev_stop);
   if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
   if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
   const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)

@@ -19,8 +19,8 @@
 //    A = K rows from LDS, B = the wave's q rows held in registers), so that
 //    each query row's scores and accumulators live in one lane column and
 //    the online softmax needs only two cross-lane shuffles;
-//  * O^T = V^T P^T with V^T gathered from the staged tile as in the decode
-//    kernel.
+//  * O^T = V^T P^T with V^T read from the staged tile (the decode kernel's
+//    V layout) by the transposing LDS reads of gfx950.
 //
 // Arithmetic: q (times scale * log2 e) and the probabilities enter the
 // matrix cores rounded once to bf16, accumulation is fp32.  Two running
@@ -93,10 +93,43 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
   k[1] = __builtin_bit_cast(bf16x8, r1);
 }
 
+// The V^T operand of lane (n, grp) for output dims 16 cb + n: tokens 4 grp
+// + s (s < 4) and 16 + 4 grp + s - 4 of the staged tile, from two
+// ds_read_b64_tr_b16.  That instruction hands lane i of each 16-lane group
+// 16-bit element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4,
+// k = 0..3 (measured on gfx950); so lane j of the group addresses token
+// row r0 + j / 4, dims 16 cb + 4 (j % 4) .. +3, and lane i receives dim
+// 16 cb + i of rows r0 .. r0 + 3.  `addr` is that address for r0 = 4 grp;
+// rows 16 + 4 grp lie `kHalf` bytes further.  Inline assembly for the
+// reason given at gather_v.
+template <int kHalf>
+__device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 a, b;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "i"(kHalf));
+  const u32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Two floats to packed bf16, nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
 // Workgroup x: query-row tile nqt - 1 - x / (B G) (the tiles with the most
-// keys first), sequence and KV head from x mod B G.
+// keys first), sequence and KV head from x mod B G.  Held to 168 registers,
+// three workgroups share a CU (measured 18% faster than two).
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_kernel(DecodeParams p) {
   using PG = PfGeo<D>;
   using VG = Geo<D>;
   constexpr int KB = PG::KB, CB = PG::CB, NB = kPfCols / 16;
@@ -148,9 +181,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
       const float4 x0 = *reinterpret_cast<const float4*>(src + kb * 32);
       const float4 x1 = *reinterpret_cast<const float4*>(src + kb * 32 + 4);
       const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      u16x8 h;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = bf16_bits(xv[j] * qs);
+      const u32x4 h = {pack_bf16(xv[0] * qs, xv[1] * qs), pack_bf16(xv[2] * qs, xv[3] * qs),
+                       pack_bf16(xv[4] * qs, xv[5] * qs), pack_bf16(xv[6] * qs, xv[7] * qs)};
       qv[nb][kb] = __builtin_bit_cast(bf16x8, h);
     }
   }
@@ -242,7 +274,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
       const int t = 16 * h2 + n;
       koff[h2][kb] = static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
     }
-  const uint32_t vrd = static_cast<uint32_t>(VG::at(4 * grp, 2 * n));
+  // the lane's address for read_vt_tr: row 4 grp + n / 4, dims 4 (n % 4) ..
+  const uint32_t vrd = static_cast<uint32_t>(VG::at(4 * grp + n / 4, 8 * (n % 4)));
+  constexpr int kVHalf = (16 / VG::RPI) * VG::BLOCK;     // rows r -> r + 16
 
   f32x4 acc[NB][CB];
   float m[NB], l[NB], lx[NB];
@@ -324,14 +358,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
         m[nb] = mn;
       }
       const float ref = m[nb] == kNegInf ? 0.f : m[nb];
-      u16x8 h;
+      float e[8];
       float ps = 0.f, px = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e = __builtin_amdgcn_exp2f(sv[j] - ref);
-        h[j] = bf16_bits(e);
-        ps += bf16_value(h[j]);        // the sum of the weights P V uses
-        px += e;
+        e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+        px += e[j];
+      }
+      u32x4 h;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = pack_bf16(e[2 * j], e[2 * j + 1]);
+        // the sum of the weights P V uses
+        ps += __uint_as_float(h[j] << 16) + __uint_as_float(h[j] & 0xffff0000u);
       }
       l[nb] += ps;
       lx[nb] += px;
@@ -341,7 +380,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(DecodeParams p) {
     // O^T[d][row] += V^T[d][t] P^T[t][row]
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const bf16x8 av = gather_v<D>(vaddr + cb * 32);
+      const bf16x8 av = read_vt_tr<kVHalf>(vaddr + cb * 32);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb][cb] = mfma(av, pb[nb], acc[nb][cb]);
     }

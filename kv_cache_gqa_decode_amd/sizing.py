@@ -34,3 +34,26 @@ def decode_aux_bytes(batch: int, n_heads: int, kv_heads: int, head_dim: int,
     out = batch * n_heads * (head_dim + 1) * 4
     ints = 2 * batch * 4 + 4 * n_table_entries
     return qkv_in + append + q_rot + out + ints
+
+
+def window_key_count(seq_lens, n_query: int) -> int:
+    """Keys attended by all queries of a step with T = n_query new tokens per
+    sequence (query t of sequence b sees the tokens j < L_b - T + 1 + t),
+    summed over queries and sequences.  A prompt from empty (L = T) gives
+    T (T + 1) / 2 per sequence."""
+    T = int(n_query)
+    total = 0
+    for L in np.asarray(seq_lens, dtype=np.int64):
+        a = int(L) - T + 1                       # keys of query 0
+        if a >= 1:
+            total += T * a + T * (T - 1) // 2
+        else:
+            top = a + T - 1                      # keys of the last query
+            total += top * (top + 1) // 2 if top > 0 else 0
+    return total
+
+
+def window_attention_flops(seq_lens, n_query: int, n_heads: int, head_dim: int) -> int:
+    """Multiply-adds of q K^T and P V, two flops each: 4 * head_dim per
+    (query head, attended key)."""
+    return 4 * head_dim * n_heads * window_key_count(seq_lens, n_query)

@@ -123,3 +123,13 @@ def test_prefill_gate_rejects_planted_mistakes():
     wrong, _ = oracle.decode_attn(g, np.ascontiguousarray(q_rot[:, :, perm]), kc, vc, p.seq_lens,
                                   n_query=T)
     assert not gates.out_ok(wrong[:, :, np.argsort(perm)], ref, "prefill")
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 17])
+def test_window_key_count_brute_force(T):
+    lens = np.array([0, 1, T - 1, T, T + 1, 40, 300], np.int64).clip(0)
+    brute = sum(max(0, min(int(L), int(L) - T + 1 + t)) for L in lens for t in range(T))
+    assert sizing.window_key_count(lens, T) == brute
+    # a prompt from empty: the causal triangle
+    assert sizing.window_key_count([T], T) == T * (T + 1) // 2
+    assert sizing.window_attention_flops([T], T, 32, 128) == 4 * 128 * 32 * T * (T + 1) // 2
