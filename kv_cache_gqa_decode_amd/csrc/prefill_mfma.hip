@@ -31,6 +31,8 @@
 // kernels carry q and P as bf16 hi + lo pairs instead, at twice the
 // matrix-core work, which the bandwidth-bound decode step does not notice
 // but the compute-bound prefill would.
+#include <type_traits>
+
 #include "mfma_tile.h"
 
 namespace kvd {
@@ -100,20 +102,29 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
 // k = 0..3 (measured on gfx950); so lane j of the group addresses token
 // row r0 + j / 4, dims 16 cb + 4 (j % 4) .. +3, and lane i receives dim
 // 16 cb + i of rows r0 .. r0 + 3.  `addr` is that address for r0 = 4 grp;
-// rows 16 + 4 grp lie `kHalf` bytes further.  Inline assembly for the
-// reason given at gather_v.
-template <int kHalf>
+// rows 16 + 4 grp lie `kHalf` bytes further; dims 16 cb .. at kOff = 32 cb.
+// Inline assembly for the reason given at gather_v.
+template <int kOff, int kHalf>
 __device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   u32x2 a, b;
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %2\n\t"
-      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(a), "=&v"(b)
-      : "v"(addr), "i"(kHalf));
+      : "v"(addr), "i"(kOff), "i"(kOff + kHalf));
   const u32x4 r = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 // Two floats to packed bf16, nearest-even (v_cvt_pk_bf16_f32).
@@ -293,7 +304,11 @@ void prefill_kernel(DecodeParams p) {
     cur = tile_src(0);
     issue(cur, 0);
   }
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One key tile: wait for its copies, request the next tile's, then scores,
+  // online softmax and P V.  MASK (a constant at each call) says whether the
+  // tile may reach past a row's bound or hold an invalid block.
+  auto tile = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int j0 = kt * kPfTT;
     const int sel = kt & 1;
     vmem_wait<0>();                    // this wave's copies of tile kt have landed
@@ -306,7 +321,8 @@ void prefill_kernel(DecodeParams p) {
     }
     const uint32_t kaddr = lds_addr(buf0 + sel * PG::kBufBytes);
     const uint32_t vaddr = kaddr + PG::kKBytes + vrd;
-    const bool masked = j0 + kPfTT > wbound || !now.ok[0] || !now.ok[1];   // wave-uniform
+    // wave-uniform; an invalid block (paged) masks its tokens on either path
+    const bool masked = (MASK && j0 + kPfTT > wbound) || (PAGED && !(now.ok[0] && now.ok[1]));
 
     // S^T: token rows 16 h2 + 4 grp + j, lane column n of block nb
     f32x4 s[NB][2];
@@ -378,13 +394,21 @@ void prefill_kernel(DecodeParams p) {
     }
 
     // O^T[d][row] += V^T[d][t] P^T[t][row]
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const bf16x8 av = read_vt_tr<kVHalf>(vaddr + cb * 32);
+    static_for<CB>([&](auto cbc) {
+      constexpr int cb = decltype(cbc)::value;
+      const bf16x8 av = read_vt_tr<32 * cb, kVHalf>(vaddr);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb][cb] = mfma(av, pb[nb], acc[nb][cb]);
-    }
-  }
+    });
+  };
+
+  // Tiles below the workgroup's smallest bound need no causal mask; the
+  // rest, at most two per wave, take the masked body.
+  const int wg_bound = win + static_cast<int>(c0 / R);
+  const int n_full = wg_bound >= kPfTT ? (wg_bound / kPfTT < nkt ? wg_bound / kPfTT : nkt) : 0;
+  int kt = 0;
+  for (; kt < n_full; ++kt) tile(kt, std::false_type{});
+  for (; kt < nkt; ++kt) tile(kt, std::true_type{});
 
   // the four lane groups of a column hold partial sums under one max
 #pragma unroll
