@@ -43,7 +43,7 @@
 // in flight and each tile's loads have a whole tile of compute to arrive.
 // One wait per tile ("at most one tile of loads outstanding") covers both.
 // The V^T reads from LDS are inline assembly for the reason given with
-// gather_v in mfma_tile.h (the compiler would otherwise wait for every
+// read_vt_tr in mfma_tile.h (the compiler would otherwise wait for every
 // outstanding copy first).  K rows past the end of the split are read from
 // the last group that holds a token (always inside the cache); V^T blocks
 // past it, or of an invalid block, are read out of range (zeros, no memory
@@ -100,7 +100,7 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 }
 
 // Sixteen bytes of each of this lane's CB V^T rows from LDS (row cb at
-// addr + 256 cb), waiting for its own reads.  Inline assembly: see gather_v.
+// addr + 256 cb), waiting for its own reads.  Inline assembly: see read_vt_tr.
 template <int CB>
 __device__ __forceinline__ void read_vt(uint32_t addr, u32x4 (&v)[CB]);
 template <>

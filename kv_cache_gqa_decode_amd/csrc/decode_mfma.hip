@@ -218,9 +218,10 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 
   lds_char* const stage = (lds_char*)(smem);
   lds_char* vbuf[2] = {stage + (2 * wave) * G::kTileBytes, stage + (2 * wave + 1) * G::kTileBytes};
-  // this lane's P V column-read base in each buffer
-  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(4 * grp, 2 * n),
-                           lds_addr(vbuf[1]) + G::at(4 * grp, 2 * n)};
+  // this lane's address for read_vt_tr: row 4 grp + n / 4, dims 4 (n % 4) ..
+  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(4 * grp + n / 4, 8 * (n % 4)),
+                           lds_addr(vbuf[1]) + G::at(4 * grp + n / 4, 8 * (n % 4))};
+  constexpr int kVHalf = (16 / RPI) * G::BLOCK;     // rows r -> r + 16
   uint4 kr[2][KB];
   int blk_cur[2];
   int base = t0 + wave * TT;
@@ -363,15 +364,16 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     }
 
     // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens 16*(j/4) + 4*grp + j%4
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const bf16x8 av = gather_v<D>(vrd[cur] + cb * 32);
+    // (transposing LDS reads)
+    static_for<CB>([&](auto cbc) {
+      constexpr int cb = decltype(cbc)::value;
+      const bf16x8 av = read_vt_tr<32 * cb, kVHalf>(vrd[cur]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         acc[nb][cb] = mfma(av, ph[nb], acc[nb][cb]);
         acc[nb][cb] = mfma(av, pl[nb], acc[nb][cb]);
       }
-    }
+    });
     blk[0] = blk_next[0];
     blk[1] = blk_next[1];
   };

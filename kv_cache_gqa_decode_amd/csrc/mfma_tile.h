@@ -1,8 +1,11 @@
-// Device helpers shared by the two matrix-core decode kernels (bf16 KV):
-// operand types, the bf16 hi/lo split, buffer descriptors for the K/V
-// reads, the staged V-tile geometry in LDS and the inline-assembly LDS
-// accesses of that tile.  Not part of the C ABI.
+// Device helpers shared by the matrix-core kernels (decode on bf16 and INT8
+// caches, prefill): operand types, the bf16 hi/lo split, buffer descriptors
+// for the K/V reads, the staged V-tile geometry in LDS, the inline-assembly
+// LDS accesses of that tile, the work-unit order and the merge of the
+// waves.  Not part of the C ABI.
 #pragma once
+
+#include <type_traits>
 
 #include "kvd_internal.h"
 
@@ -111,56 +114,61 @@ struct Geo {
   static constexpr int NVL = TT / RPI;       // V load instructions per tile
   static constexpr int NLOADS = 2 * KB + NVL;  // vector-memory loads per tile
   // every V copy instruction writes 1 KiB; instruction blocks are padded by
-  // 32 bytes so the transposed column reads of the four lane groups fall in
-  // different banks
+  // 32 bytes, so the four lane groups' transposing reads (rows 4 grp ..)
+  // start 8 banks apart
   static constexpr int BLOCK = 1024 + 32;
   static constexpr int kTileBytes = NVL * BLOCK;
   // byte offset of (token row r, byte c within the row) in a staged tile
   __device__ __forceinline__ static constexpr int at(int r, int c) {
     return (r / RPI) * BLOCK + (r % RPI) * (2 * D) + c;
   }
-  // The P V A operand of lane (n, grp) is column n of token rows
-  // 16*(j/4) + 4*grp + j%4, j = 0..7: at(4*grp, 2n) plus this offset.
-  static constexpr int voff(int j) { return (16 * (j >> 2) / RPI) * BLOCK + (j & 3) * (2 * D); }
 };
 
-// Eight bf16 of one V column, from the staged tile at `addr` (+ voff(j)),
-// packed two per register; waits for its own LDS reads.  Issued from inline
-// assembly on purpose: the compiler cannot tell that these reads do not
-// touch the buffer an HBM -> LDS copy is still filling, and would otherwise
-// wait for every outstanding copy first, which serialises the pipeline.
-// Each value is read zero-extended and the pairs are packed with shifts:
-// with SRAM ECC on, a 16-bit "d16" load does not keep the other half of its
-// register.
-template <int D>
-__device__ __forceinline__ bf16x8 gather_v(uint32_t addr) {
-  using G = Geo<D>;
-  u32x4 r;
-  uint32_t r0, r1, r2, r3, x0, x1, x2, x3, x4, x5, x6, x7;
+// The V^T operand of lane (n, grp) for output dims 16 cb + n: tokens 4 grp
+// + s (s < 4) and 16 + 4 grp + s - 4 of the staged tile, from two
+// ds_read_b64_tr_b16.  That instruction hands lane i of each 16-lane group
+// 16-bit element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4,
+// k = 0..3 (measured on gfx950); so lane j of the group addresses token
+// row r0 + j / 4, dims 16 cb + 4 (j % 4) .. +3, and lane i receives dim
+// 16 cb + i of rows r0 .. r0 + 3.  `addr` is that address for r0 = 4 grp;
+// rows 16 + 4 grp lie `kHalf` bytes further; dims 16 cb .. at kOff = 32 cb.
+// Issued from inline assembly on purpose: the compiler cannot tell that
+// these reads do not touch the buffer an HBM -> LDS copy is still filling,
+// and would otherwise wait for every outstanding copy first, which
+// serialises the pipeline.
+template <int kOff, int kHalf>
+__device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 a, b;
   asm volatile(
-      "ds_read_u16 %4, %12 offset:%13\n\t"
-      "ds_read_u16 %5, %12 offset:%14\n\t"
-      "ds_read_u16 %6, %12 offset:%15\n\t"
-      "ds_read_u16 %7, %12 offset:%16\n\t"
-      "ds_read_u16 %8, %12 offset:%17\n\t"
-      "ds_read_u16 %9, %12 offset:%18\n\t"
-      "ds_read_u16 %10, %12 offset:%19\n\t"
-      "ds_read_u16 %11, %12 offset:%20\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "v_lshl_or_b32 %0, %5, 16, %4\n\t"
-      "v_lshl_or_b32 %1, %7, 16, %6\n\t"
-      "v_lshl_or_b32 %2, %9, 16, %8\n\t"
-      "v_lshl_or_b32 %3, %11, 16, %10"
-      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3),
-        "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7)
-      : "v"(addr), "i"(G::voff(0)), "i"(G::voff(1)), "i"(G::voff(2)), "i"(G::voff(3)),
-        "i"(G::voff(4)), "i"(G::voff(5)), "i"(G::voff(6)), "i"(G::voff(7)));
-  r[0] = r0; r[1] = r1; r[2] = r2; r[3] = r3;
+      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "i"(kOff), "i"(kOff + kHalf));
+  const u32x4 r = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Two floats to packed bf16, nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
 // 16 zero bytes at LDS address `addr` (inline assembly for the same reason
-// as gather_v; ordered after the copies by an explicit vmcnt wait)
+// as read_vt_tr; ordered after the copies by an explicit vmcnt wait)
 __device__ __forceinline__ void lds_zero16(uint32_t addr) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(z) : "memory");

@@ -31,8 +31,6 @@
 // kernels carry q and P as bf16 hi + lo pairs instead, at twice the
 // matrix-core work, which the bandwidth-bound decode step does not notice
 // but the compute-bound prefill would.
-#include <type_traits>
-
 #include "mfma_tile.h"
 
 namespace kvd {
@@ -66,7 +64,7 @@ struct PfGeo {
 };
 
 // Four (D = 128) or two (D = 64) 16-byte K operands from LDS, waiting for
-// their own reads.  Inline assembly for the reason given at gather_v: a
+// their own reads.  Inline assembly for the reason given at read_vt_tr: a
 // compiler-visible LDS read would first wait for the next tile's copies.
 __device__ __forceinline__ void read_k(const uint32_t (&a)[4], bf16x8 (&k)[4]) {
   u32x4 r0, r1, r2, r3;
@@ -93,46 +91,6 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
       : "v"(a[0]), "v"(a[1]));
   k[0] = __builtin_bit_cast(bf16x8, r0);
   k[1] = __builtin_bit_cast(bf16x8, r1);
-}
-
-// The V^T operand of lane (n, grp) for output dims 16 cb + n: tokens 4 grp
-// + s (s < 4) and 16 + 4 grp + s - 4 of the staged tile, from two
-// ds_read_b64_tr_b16.  That instruction hands lane i of each 16-lane group
-// 16-bit element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4,
-// k = 0..3 (measured on gfx950); so lane j of the group addresses token
-// row r0 + j / 4, dims 16 cb + 4 (j % 4) .. +3, and lane i receives dim
-// 16 cb + i of rows r0 .. r0 + 3.  `addr` is that address for r0 = 4 grp;
-// rows 16 + 4 grp lie `kHalf` bytes further; dims 16 cb .. at kOff = 32 cb.
-// Inline assembly for the reason given at gather_v.
-template <int kOff, int kHalf>
-__device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 a, b;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
-      "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b)
-      : "v"(addr), "i"(kOff), "i"(kOff + kHalf));
-  const u32x4 r = {a[0], a[1], b[0], b[1]};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
-// Two floats to packed bf16, nearest-even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const f32x2 f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 // Workgroup x: query-row tile nqt - 1 - x / (B G) (the tiles with the most
