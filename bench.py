@@ -326,6 +326,9 @@ def main():
                     help="tokens per split over the last --tail-span positions (0 = automatic)")
     ap.add_argument("--tail-span", type=int, default=-1)
     ap.add_argument("--order", type=int, default=-1, help="MFMA dispatch order 0/1/2 (-1 automatic)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as one captured HIP graph in the timed region "
+                         "(the kernel-time region stays eager)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--flush", action="store_true",
@@ -428,13 +431,25 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the whole step (RoPE/append, work list, split kernel, merge) as one
+        # graph: the kernels and their arguments are those of the eager step
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
     # timed region 1: K whole steps, nothing else on the stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -494,6 +509,7 @@ def main():
                    "max_context": max_len, "kv_bytes_per_step": kv_bytes,
                    "aux_bytes_per_step": aux, "split_tokens": plan["split_tokens"],
                    "n_splits": plan["n_splits"], "kernel": plan["kernel"],
+                   "launch": "hip graph replay" if args.graph else "eager launches",
                    "parallelism": "single GPU"},
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
