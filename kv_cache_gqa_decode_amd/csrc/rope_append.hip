@@ -117,9 +117,9 @@ __device__ __forceinline__ int64_t i8_krow(const RopeParams& p, int b, int pos, 
 
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
-  // workgroup (new token bt = b * T + t, slice of 256 items): the D/2
-  // rotation factors of the token's position are computed once per workgroup
-  // (fp64) and shared by its threads through LDS
+  // workgroup (new token bt = b * T + t, slices y, y + gridDim.y, .. of 256
+  // items): the D/2 rotation factors of the token's position are computed
+  // once per workgroup (fp64) and shared by its threads through LDS
   __shared__ double cs[64], sn[64];
   const int bt = blockIdx.x;
   const int b = bt / p.T;
@@ -135,8 +135,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
   const int nq = p.q ? p.H * half : 0;
   const int nk = p.G * half;
   const int nv = p.G * p.D;
-  const int i = blockIdx.y * 256 + threadIdx.x;
-  if (i < nq + nk + nv) {
+  for (int i = blockIdx.y * 256 + threadIdx.x; i < nq + nk + nv; i += 256 * gridDim.y) {
     if (i < nq + nk) {
       const bool is_q = i < nq;
       const int j = is_q ? i : i - nq;
@@ -188,8 +187,13 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
 hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream) {
   const int work = (p.q ? p.H : 0) * (p.D / 2) + p.G * (p.D / 2) + p.G * p.D;
-  if (p.T < 1) return hipErrorInvalidValue;
-  const dim3 grid(p.B * p.T, (work + 255) / 256);
+  if (p.T < 1 || static_cast<int64_t>(p.B) * p.T > 0x7fffffff) return hipErrorInvalidValue;
+  // a few tokens (a decode step): one workgroup per 256 items, for
+  // parallelism; many (a prompt): one workgroup per token, so the rotation
+  // factors are computed once per token
+  const int tokens = p.B * p.T;
+  const int slices = tokens >= 4096 ? 1 : (work + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(tokens), slices);
   if (kv_dtype == KVD_FP32) {
     if (paged) rope_append_kernel<float, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<float, false><<<grid, 256, 0, stream>>>(p);
