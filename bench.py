@@ -325,7 +325,7 @@ def main():
     ap.add_argument("--tail-split", type=int, default=0,
                     help="tokens per split over the last --tail-span positions (0 = automatic)")
     ap.add_argument("--tail-span", type=int, default=-1)
-    ap.add_argument("--order", type=int, default=-1, help="MFMA dispatch order 0/1/2 (-1 automatic)")
+    ap.add_argument("--order", type=int, default=-1, help="MFMA dispatch order 0-4 (-1 automatic)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph in the timed region "
                          "(the kernel-time region stays eager)")

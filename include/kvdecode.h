@@ -359,8 +359,11 @@ kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens);
  * sequence), 3 a work list of the (sequence, split) units that hold
  * tokens, built on the device from seq_lens before the split kernel (full
  * splits sequence by sequence, then the partial last splits longest first;
- * ignored with a single split), -1 automatic (the work list for batches
- * with more than one split).  EINVAL for values outside these ranges.
+ * ignored with a single split), 4 the same list derived inside the split
+ * kernel, without the launch that builds it (batches of at most 64
+ * sequences; ignored otherwise), -1 automatic (order 4 for batches of 2 to
+ * 64 sequences with more than one split, order 3 above 64).  EINVAL for
+ * values outside these ranges.
  */
 kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
                              int32_t tail_span_tokens, int32_t dispatch_order);

@@ -530,7 +530,7 @@ def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_t
     """Process-wide override of the kernel ("valu", "mfma", "int8" or None
     for automatic), the tokens per split (0 = automatic), the shorter splits
     covering the last ``tail_span_tokens`` positions (0 / -1 = automatic) and
-    the MFMA dispatch order (0, 1, 2 or None for automatic)."""
+    the MFMA dispatch order (0-4 or None for automatic)."""
     _check(load_library().kvd_set_tuning_ex(
         _KERNELS[kernel], int(split_tokens), int(tail_split_tokens), int(tail_span_tokens),
         -1 if dispatch_order is None else int(dispatch_order)))

@@ -207,10 +207,16 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
   // then sequences, splits slowest (resp. sequences slowest).
   const int64_t list_wgs = static_cast<int64_t>(s->n_kv_heads) * s->batch * pl->n_splits;
   const bool list_ok = kernel >= 1 && pl->n_splits > 1 && list_wgs <= 0x7fffffff;
-  pl->grid_order = s->batch == 1 ? 0 : (list_ok ? 3 : (s->block_size != 0 ? 2 : 1));
+  // Up to 64 sequences the split kernel's waves derive the list themselves
+  // from the lengths (order 4, one sequence per lane): the same order
+  // without the launch that builds it.
+  const bool wave_list_ok = list_ok && s->batch <= 64;
+  pl->grid_order = s->batch == 1 ? 0
+                 : (wave_list_ok ? 4 : (list_ok ? 3 : (s->block_size != 0 ? 2 : 1)));
   const int ord = g_order_override.load();
   if (ord >= 0 && ord <= 2) pl->grid_order = ord;
   if (ord == 3 && list_ok) pl->grid_order = 3;   // a single split (or the VALU kernel): no list
+  if (ord == 4 && wave_list_ok) pl->grid_order = 4;
   pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
   if (pl->n_splits > 1) {
     const size_t rows = static_cast<size_t>(s->batch) * T * s->n_heads * pl->n_splits;
@@ -254,7 +260,7 @@ kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_
   if (kernel < -1 || kernel > 2) return KVD_EINVAL;
   if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
   if (tail_split_tokens < 0 || tail_split_tokens % 16 != 0) return KVD_EINVAL;
-  if (tail_span_tokens < -1 || dispatch_order < -1 || dispatch_order > 3) return KVD_EINVAL;
+  if (tail_span_tokens < -1 || dispatch_order < -1 || dispatch_order > 4) return KVD_EINVAL;
   g_kernel_override.store(kernel);
   g_split_override.store(split_tokens);
   g_tail_split_override.store(tail_split_tokens);

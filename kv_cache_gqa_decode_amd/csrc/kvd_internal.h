@@ -41,7 +41,8 @@ struct DecodeParams {
   float qscale;             // softmax scale * log2(e)
   int32_t direct;           // 1: one split, write out / lse directly
   int32_t grid_order;       // matrix-core kernels: 0 (split, G, B), 1 (G, B, split),
-                            // 2 (G, split, B), 3 work list (heads fastest; units.hip)
+                            // 2 (G, split, B), 3 work list (heads fastest; units.hip),
+                            // 4 the same list derived by each wave (B <= 64)
   int32_t* units;           // work list (grid_order 3): b | split << 16, in the workspace
   int32_t* n_units;         // its length
 };

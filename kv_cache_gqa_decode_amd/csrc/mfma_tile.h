@@ -175,7 +175,8 @@ __device__ __forceinline__ void lds_zero16(uint32_t addr) {
 }
 
 // The dispatch order (chosen by the planner) of the (sequence, KV head,
-// split) units, slot x fastest (orders 0-2; order 3 reads a work list): which of them run side by side decides how
+// split) units, slot x fastest (orders 0-2; orders 3 and 4 follow a work
+// list): which of them run side by side decides how
 // the workgroups reading the same DRAM rows (the heads of one token range)
 // and the longest chunks are spread in time and across the XCDs.
 struct Unit { int b, g, split; };
@@ -193,7 +194,65 @@ __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int
 // sequence) and then moves on.  Measured on the batched workload's split
 // kernel: fixed heads 198 us, rotation by k 195, by k / 2 187, by k / 16
 // 185; 64 uniform 8K sequences 373, 356, 343, 338 us.
+// Order 4, batches of at most 64 sequences: the order-3 list without its
+// launch.  Every wave derives its entry k = id / G from the lengths, one
+// sequence per lane: an inclusive scan of the full-split counts places the
+// full units (sequence by sequence); the partial last splits are ranked by
+// the key (16-token bucket of their length + 1) << 6 | (63 - b), unique per
+// lane, largest first -- longest bucket first, then by sequence -- and the
+// (k - n_full)-th largest is picked bit by bit with ballots (a radix
+// select: 16 steps of one compare and one popcount).
+__device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u) {
+  const int lane = threadIdx.x & 63;
+  const int id = static_cast<int>(blockIdx.x);
+  const int k = id / p.G;
+  int L = lane < p.B ? p.seq_lens[lane] : 0;
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int n = split_count(p, L);
+  int full = 0, part = 0;
+  if (n > 0) {
+    const int tail = L - split_start(p, n - 1);
+    if (tail == split_size(p, n - 1)) full = n;
+    else { full = n - 1; part = tail; }
+  }
+  int incl = full;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const int n_full = __builtin_amdgcn_readlane(incl, 63);
+  int b, split;
+  if (k < n_full) {
+    const uint64_t hit = __ballot(incl - full <= k && k < incl);
+    b = __builtin_ctzll(hit);
+    split = k - __builtin_amdgcn_readlane(incl - full, b);
+  } else {
+    // part <= kMaxChunk: the key fits in 16 bits
+    const int key = part > 0 ? ((((part - 1) >> 4) + 1) << 6) | (63 - lane) : 0;
+    uint64_t cand = __ballot(part > 0);
+    int j = k - n_full;
+    if (j >= __popcll(cand)) return false;
+#pragma unroll
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint64_t ones = cand & __ballot((key >> bit) & 1);
+      const int c1 = __popcll(ones);
+      if (j < c1) {
+        cand = ones;
+      } else {
+        j -= c1;
+        cand &= ~ones;
+      }
+    }
+    b = __builtin_ctzll(cand);
+    split = __builtin_amdgcn_readlane(full, b);
+  }
+  u = Unit{b, (id - k * p.G + (k >> 4)) % p.G, split};
+  return true;
+}
+
 __device__ __forceinline__ bool unit_at(const DecodeParams& p, Unit& u) {
+  if (p.grid_order == 4) return unit_from_lengths(p, u);
   if (p.grid_order == 3) {
     const int id = static_cast<int>(blockIdx.x);
     const int k = id / p.G;
@@ -212,7 +271,7 @@ inline dim3 split_grid(const DecodeParams& p) {
     case 0: return dim3(p.n_splits, p.G, p.B);
     case 1: return dim3(p.G, p.B, p.n_splits);
     case 2: return dim3(p.G, p.n_splits, p.B);
-    default: return dim3(static_cast<unsigned>(p.G) * p.B * p.n_splits);
+    default: return dim3(static_cast<unsigned>(p.G) * p.B * p.n_splits);   // orders 3, 4
   }
 }
 

@@ -124,7 +124,7 @@ def test_split_counts_agree():
 
 
 @pytest.mark.parametrize("split,tail,span", [(512, 128, 1024), (256, 32, 300)])
-@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
 def test_two_level_splits(split, tail, span, order):
     s = i8("c3", batch=RAGGED.size, max_seq_len=1024, q_gain=8.0)
     check_full(W.make_problem(s, lengths=RAGGED), split=split, tail=(tail, span), order=order,

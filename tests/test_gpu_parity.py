@@ -236,7 +236,7 @@ def test_repeated_steps_are_idempotent():
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("split,tail,span", [(256, 64, 400), (512, 128, 1024), (128, 16, 96),
                                              (1024, 1024, 500), (256, 32, 0)])
-@pytest.mark.parametrize("order", [None, 0, 1, 2, 3])
+@pytest.mark.parametrize("order", [None, 0, 1, 2, 3, 4])
 def test_two_level_splits(kernel, split, tail, span, order):
     """Splits of `split` tokens, then of `tail` tokens over the last `span`
     positions of the bound, in every dispatch order: the merge sees the same
@@ -250,7 +250,7 @@ def test_two_level_splits(kernel, split, tail, span, order):
 
 
 @pytest.mark.parametrize("kernel", ["mfma"])
-@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
 def test_two_level_splits_paged(kernel, order):
     s = W.spec("c4", batch=RAGGED.size, num_blocks=1000, max_blocks_per_seq=64, q_gain=8.0)
     p = W.make_problem(s, lengths=RAGGED)
@@ -259,7 +259,7 @@ def test_two_level_splits_paged(kernel, order):
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("order", [None, 1, 3])
+@pytest.mark.parametrize("order", [None, 1, 3, 4])
 def test_empty_sequences_with_several_splits(kernel, order):
     """Zero-length sequences among long ones with several splits: the work
     list holds no unit for them, the merge still writes out = 0, lse = -inf,
@@ -283,3 +283,54 @@ def test_empty_sequences_with_several_splits(kernel, order):
     keep = [1, 3, 4]
     gates.assert_out(out.cpu().numpy()[keep], oo[keep], "bf16", "empty sequences")
     gates.assert_lse(lse.cpu().numpy()[keep], ol[keep], "bf16", "empty sequences")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("batch", [64, 65, 2])
+def test_work_list_derived_in_kernel(dtype, batch):
+    """Dispatch order 4 (each wave derives its unit from the lengths, up to 64
+    sequences) against order 3 (the list built by its own launch): a batch
+    whose partial last splits tie in every 16-token bucket, with empty
+    sequences, lengths below one bucket and exact multiples of the split,
+    and a NaN-filled workspace, so a unit that no workgroup computed would
+    surface as NaN.  The two orders give the same bits, and the oracle's
+    result.  65 sequences exceed the lanes of a wave: order 4 then falls
+    back to order 3."""
+    dev = device()
+    rng = np.random.default_rng(batch)
+    base = np.array([0, 1, 5, 16, 17, 31, 32, 100, 111, 256, 257, 511, 512, 513, 700, 1024],
+                    np.int32)
+    lens = np.resize(base, batch).copy()
+    rng.shuffle(lens)
+    lens[lens == 0] = 1                      # the append needs a slot; emptied below
+    s = W.spec("c3", batch=batch, max_seq_len=1024, q_gain=8.0).replace(dtype=dtype)
+    p = W.make_problem(s, lengths=lens)
+    t = upload(p, dev)
+    q_rot = gpu_step(t, s, 1024)[0]
+    empty = np.flatnonzero(np.resize(base, batch) == 0)
+    run_lens = lens.copy()
+    run_lens[empty] = 0
+    lens_t = torch.tensor(run_lens, dtype=torch.int32, device=dev)
+    results = []
+    for order in (3, 4):
+        kvd.set_tuning(None, 128, 0, -1, order)
+        nbytes = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=1024)
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
+        if dtype == "i8":
+            out, lse = kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
+                                                t["v_scale"], lens_t, max_seq_len=1024,
+                                                workspace=ws)
+        else:
+            out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens_t,
+                                           max_seq_len=1024, workspace=ws)
+        torch.cuda.synchronize()
+        results.append((out.clone(), lse.clone()))
+    assert torch.equal(results[0][0], results[1][0]), "orders 3 and 4 differ"
+    assert torch.equal(results[0][1], results[1][1]), "orders 3 and 4 differ (lse)"
+    out, lse = (x.cpu().numpy() for x in results[1])
+    assert (out[empty] == 0).all() and np.isneginf(lse[empty]).all()
+    p.seq_lens[:] = run_lens
+    _, oo, ol, _, _ = oracle_step(p)
+    keep = np.flatnonzero(run_lens > 0)
+    gates.assert_out(out[keep], oo[keep], dtype, f"work list order 4, B={batch}")
+    gates.assert_lse(lse[keep], ol[keep], dtype, f"work list order 4, B={batch}")
