@@ -7,7 +7,13 @@
 // algebra behind the tiled attention of "Transformer推理核心：KV Cache、GQA与
 // RoPE原理与工程实践" §4.2 applied across workgroups.
 //
-// Only the splits that hold tokens of the sequence are read.
+// Only the splits that hold tokens of the sequence contribute.  The kernel
+// is a handful of microseconds of memory latency around a few MB of
+// partials, so it is written to wait for memory once: the sequence length
+// and every partial a thread merges are requested together (all reads stay
+// inside the workspace; the splits past the sequence's end are masked after
+// the loads land), each thread keeps its own running maximum, and the split
+// lanes are combined with wave shuffles and two barriers.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -15,86 +21,144 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// Workgroup (b*H + h, dim group): 256 threads = SL split lanes x DT/4 float4
-// columns merge DT output dims of one (b, h).  With few splits one
-// workgroup takes all D dims; with many, D/32 workgroups share a (b, h).
-template <int D, int DT>
+// Workgroup (b*T*H + t*H + h, dim group): 256 threads = SL split lanes x
+// DT/4 float4 columns merge DT output dims of one query row; split lane sl
+// takes splits sl, sl + SL, ... in batches of U whose loads are issued
+// together.  With few splits one workgroup takes all D dims; with many,
+// D/DT workgroups share a row.
+template <int D, int DT, int U>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   constexpr int C4 = DT / 4;          // float4 columns
   constexpr int SL = 256 / C4;        // split lanes
-  __shared__ float sm_red[256];
-  __shared__ float4 sm_acc[SL][C4];
-  __shared__ float sm_w[SL];
+  static_assert(C4 <= 32 && SL * C4 == 256, "columns within a wave");
+  __shared__ float4 sm_acc[4][C4];
+  __shared__ float sm_m[4], sm_w[4];
 
   const int bh = blockIdx.x;
   const int d0 = blockIdx.y * DT;
   const int b = bh / (p.H * p.T);       // rows b * T * H + t * H + h
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
-  const int ns = split_count(p, L);
   const int tid = threadIdx.x;
-  float* out = p.out + static_cast<int64_t>(bh) * D + d0;
-  if (ns == 0) {
-    if (tid < DT) out[tid] = 0.f;
-    if (tid == 0 && blockIdx.y == 0 && p.lse) p.lse[bh] = kNegInf;
-    return;
-  }
-  const float* plse = p.part_lse + static_cast<int64_t>(bh) * p.n_splits;
-  const float* po = p.part_o + static_cast<int64_t>(bh) * p.n_splits * D + d0;
-
-  // 1) M = max over splits
-  float M = kNegInf;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, plse[s]);
-  sm_red[tid] = M;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + w]);
-    __syncthreads();
-  }
-  M = sm_red[0];
-  const float ref = M == kNegInf ? 0.f : M;
-
-  // 2) weighted sums, SL partial rows at a time
   const int sl = tid / C4, c4 = tid - sl * C4;
+  // no workspace: no sequence can hold a token (the host planned no split)
+  const int n_splits = p.part_lse ? p.n_splits : 0;
+  const float* plse = p.part_lse + static_cast<int64_t>(bh) * p.n_splits;
+  const float* po = p.part_o + static_cast<int64_t>(bh) * p.n_splits * D + d0 + c4 * 4;
+
+  // the length through a vector-memory (buffer) load: a scalar load would
+  // be waited for before the partials below are requested
+  const __amdgpu_buffer_rsrc_t lens = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(p.seq_lens), 0, p.B * static_cast<int>(sizeof(int32_t)), 0x00020000);
+  const int L = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens, b * 4, 0, 0));
+  float m = kNegInf, wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  for (int s = sl; s < ns; s += SL) {
-    const float w = exp2f(plse[s] - ref);
-    const float4 o = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s) * D + c4 * 4);
-    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
-    wsum += w;
-  }
-  sm_acc[sl][c4] = acc;
-  if (c4 == 0) sm_w[sl] = wsum;
-  __syncthreads();
-  if (tid < C4) {
-    float4 a = sm_acc[0][tid];
-    float ws = sm_w[0];
+  float ls[U];
+  float4 o[U];
+  // request batch s0 (split lane sl's splits s0, s0 + SL, ..., in bounds)
+  auto request = [&](int s0) {
 #pragma unroll
-    for (int r = 1; r < SL; ++r) {
-      const float4 x = sm_acc[r][tid];
-      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-      ws += sm_w[r];
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SL;
+      const int sc = s < n_splits ? s : s0;          // in bounds; masked below
+      ls[u] = plse[sc];
+      o[u] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(sc) * D);
     }
-    // no split saw a valid token (every block invalid): empty softmax
-    const float inv = ws > 0.f ? 1.f / ws : 0.f;
-    reinterpret_cast<float4*>(out)[tid] = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
-    if (tid == 0 && blockIdx.y == 0 && p.lse)
-      p.lse[bh] = ws > 0.f ? (ref + log2f(ws)) * 0.69314718055994531f : kNegInf;
+  };
+  // fold the landed batch s0 into (m, wsum, acc); ns = splits holding tokens
+  auto fold = [&](int s0, int ns) {
+    float mt = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u * SL >= ns) ls[u] = kNegInf;       // never weighs in, even if NaN was read
+      mt = fmaxf(mt, ls[u]);
+    }
+    if (mt == kNegInf) return;
+    const float a = exp2f(m - mt);                  // m = -inf: 0
+    acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
+    wsum *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ls[u] == kNegInf) continue;               // masked, or a split without valid tokens
+      const float w = exp2f(ls[u] - mt);
+      acc.x += w * o[u].x; acc.y += w * o[u].y; acc.z += w * o[u].z; acc.w += w * o[u].w;
+      wsum += w;
+    }
+    m = mt;
+  };
+  // The first batch is requested before the length is used, in the same
+  // block, so that a single wait covers both; the rest (more than SL * U
+  // splits) follow one batch at a time.
+  if (sl < n_splits) {
+    request(sl);
+    // the splits holding tokens (the length clamped as in the split kernels)
+    const int Lc = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+    const int ns = split_count(p, Lc);
+    fold(sl, ns);
+    for (int s0 = sl + SL * U; s0 < n_splits; s0 += SL * U) {
+      request(s0);
+      fold(s0, ns);
+    }
   }
+  // Combine the split lanes: the workgroup's maximum (wave shuffles, then
+  // the 4 waves through LDS), each lane's sums rescaled to it, then summed
+  // over the split lanes of a column -- shuffles inside a wave (the lanes
+  // C4 apart hold the same column), the 4 waves through LDS.
+  constexpr int kW = 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  float M = m;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) sm_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  const float sc = m == kNegInf ? 0.f : exp2f(m - M);   // a lane without tokens adds 0
+  float4 a = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+  float ws = wsum * sc;
+#pragma unroll
+  for (int off = C4; off < 64; off <<= 1) {
+    a.x += __shfl_xor(a.x, off); a.y += __shfl_xor(a.y, off);
+    a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
+    ws += __shfl_xor(ws, off);
+  }
+  if (lane < C4) {
+    sm_acc[wave][lane] = a;
+    if (lane == 0) sm_w[wave] = ws;
+  }
+  __syncthreads();
+  if (tid >= C4) return;
+  a = sm_acc[0][tid];
+  ws = sm_w[0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) {
+    const float4 x = sm_acc[w][tid];
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    ws += sm_w[w];
+  }
+  // no split saw a valid token (an empty sequence, or every block invalid):
+  // an empty softmax, out = 0 and lse = -inf
+  const float inv = ws > 0.f ? 1.f / ws : 0.f;
+  float* out = p.out + static_cast<int64_t>(bh) * D + d0;
+  reinterpret_cast<float4*>(out)[tid] = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  if (tid == 0 && blockIdx.y == 0 && p.lse)
+    p.lse[bh] = ws > 0.f ? (M + log2f(ws)) * 0.69314718055994531f : kNegInf;
 }
 
 }  // namespace
 
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream) {
-  const bool wide = p.n_splits > 16;
-  const dim3 grid(p.B * p.H * p.T, wide ? p.D / 32 : 1);
+  // up to 8 splits: one workgroup per row, 8 split lanes x 32 columns; up to
+  // 64: 32-dim groups, 32 split lanes x 8 columns; more: 16-dim groups,
+  // 64 split lanes x 4 columns, 4 splits per lane per batch of loads
+  const int ns = p.n_splits;
+  const int groups = ns <= 8 ? 1 : (ns <= 64 ? p.D / 32 : p.D / 16);
+  const dim3 grid(p.B * p.H * p.T, groups);
   if (p.D == 64) {
-    if (wide) lse_reduce_kernel<64, 32><<<grid, 256, 0, stream>>>(p);
-    else lse_reduce_kernel<64, 64><<<grid, 256, 0, stream>>>(p);
+    if (ns <= 8) lse_reduce_kernel<64, 64, 1><<<grid, 256, 0, stream>>>(p);
+    else if (ns <= 64) lse_reduce_kernel<64, 32, 2><<<grid, 256, 0, stream>>>(p);
+    else lse_reduce_kernel<64, 16, 4><<<grid, 256, 0, stream>>>(p);
   } else {
-    if (wide) lse_reduce_kernel<128, 32><<<grid, 256, 0, stream>>>(p);
-    else lse_reduce_kernel<128, 128><<<grid, 256, 0, stream>>>(p);
+    if (ns <= 8) lse_reduce_kernel<128, 128, 1><<<grid, 256, 0, stream>>>(p);
+    else if (ns <= 64) lse_reduce_kernel<128, 32, 2><<<grid, 256, 0, stream>>>(p);
+    else lse_reduce_kernel<128, 16, 4><<<grid, 256, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
