@@ -158,8 +158,7 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
     // column blocks, held to 256 registers), four for the VALU kernel, two
     // for the INT8 kernel (one with more than 16 query rows per KV head).
     // The MFMA kernel aims for about four rounds of them over the
-    // (sequence, KV head) pairs at the host bound on lengths and at most
-    // 1024 tokens per split: the workgroups that share a CU run at
+    // (sequence, KV head) pairs and their tokens: the workgroups that share a CU run at
     // different speeds (the older one is served first), and smaller units
     // let the dispatcher even that out at a small cost in merges.  With
     // more than 8 query rows per KV head (several new tokens, or n_rep
@@ -175,12 +174,21 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
     // and each one pays a full memory latency before its first tile, so
     // fewer, longer units measured faster (a 128K sequence: 2048-token
     // splits 46 us, 512-token splits 63 us).
+    //
+    // The rounds are counted over the host bound on lengths.  For a batch
+    // the bound overstates the work: lengths spread over [0, bound] average
+    // about half of it.  The MFMA kernel with up to 8 rows therefore aims
+    // for eight rounds of the bound with several sequences (about four of
+    // the real work) and four with one, up to 2048 tokens per split
+    // (measured: the paged batch of contexts up to 32K, 2048-token splits
+    // 321 us against 328 us at 1024; the batch of contexts up to 8K, 1024
+    // tokens 179 us against 180 us at 2048; one 128K sequence, 512 tokens
+    // 79 us against 81 at 1024 and 83 at 256).
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          static_cast<int64_t>(max_len_host);
     const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (RT > 16 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : 4);
-    const int cap = kernel == 0 ? 2048 : (kernel == 2 ? (RT > 16 ? 4096 : 2048)
-                                                      : (RT > 8 ? 2048 : 1024));
+    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : (s->batch > 1 ? 8 : 4));
+    const int cap = kernel == 2 && RT > 16 ? 4096 : 2048;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
     if (chunk > cap) chunk = cap;
