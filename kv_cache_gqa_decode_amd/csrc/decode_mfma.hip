@@ -10,13 +10,14 @@
 //
 // Per wave and 32-token tile:
 //   scores  S[t][h] = sum_d K[t][d] q[h][d]: A = K rows straight from HBM in
-//           the A-operand layout (lane = token row, 8 dims per lane), B = q.
+//           the A-operand layout (lane n of a 16-token half = token row
+//           tile_row(n), 8 dims per lane), B = q.
 //           q is fp32; it enters the bf16 product as q_hi + q_lo, two bf16
 //           numbers whose sum is q to ~2^-17, as two MFMAs into one
 //           accumulator, so scores keep near-fp32 accuracy while K is exact.
 //           The q operands stay in registers for the whole split.
 //   softmax the score output puts head h in lane h % 16 with tokens
-//           16*tb + 4*(lane/16) + j; running max and sum per head live in
+//           16*tb + tile_row(4*(lane/16) + j); running max and sum per head live in
 //           that lane, the tile max crosses the 4 lane groups with two
 //           shuffles.  The running max is only moved (and the accumulators
 //           rescaled) when a tile's max exceeds it by more than 2^8: until
@@ -197,7 +198,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   };
   // K rows in the A-operand layout: row n of half tb, 16 bytes at dims
   // kb*32 + grp*8
-  const uint32_t koff = static_cast<uint32_t>(n * rs + grp * 16);
+  const uint32_t koff = static_cast<uint32_t>(tile_row(n) * rs + grp * 16);
   auto issue_k = [&](const TileSrc& ts, uint4 (&k)[2][KB]) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -218,9 +219,9 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 
   lds_char* const stage = (lds_char*)(smem);
   lds_char* vbuf[2] = {stage + (2 * wave) * G::kTileBytes, stage + (2 * wave + 1) * G::kTileBytes};
-  // this lane's address for read_vt_tr: row 4 grp + n / 4, dims 4 (n % 4) ..
-  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(4 * grp + n / 4, 8 * (n % 4)),
-                           lds_addr(vbuf[1]) + G::at(4 * grp + n / 4, 8 * (n % 4))};
+  // this lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
+  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(tile_row(4 * grp + n / 4), 8 * (n % 4)),
+                           lds_addr(vbuf[1]) + G::at(tile_row(4 * grp + n / 4), 8 * (n % 4))};
   constexpr int kVHalf = (16 / RPI) * G::BLOCK;     // rows r -> r + 16
   uint4 kr[2][KB];
   int blk_cur[2];
@@ -315,7 +316,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int t = tbase + 16 * h2 + 4 * grp + j;
+            const int t = tbase + 16 * h2 + tile_row(4 * grp + j);
             const bool ok = h2 == 0 ? ok0 : ok1;
             if (!(t < t1 && ok && t < cbound[nb])) sv[h2 * 4 + j] = kNegInf;
           }
@@ -363,7 +364,8 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       }
     }
 
-    // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens 16*(j/4) + 4*grp + j%4
+    // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens
+    // 16*(j/4) + tile_row(4*grp + j%4)
     // (transposing LDS reads)
     static_for<CB>([&](auto cbc) {
       constexpr int cb = decltype(cbc)::value;

@@ -124,14 +124,15 @@ struct Geo {
   }
 };
 
-// The V^T operand of lane (n, grp) for output dims 16 cb + n: tokens 4 grp
-// + s (s < 4) and 16 + 4 grp + s - 4 of the staged tile, from two
-// ds_read_b64_tr_b16.  That instruction hands lane i of each 16-lane group
-// 16-bit element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4,
-// k = 0..3 (measured on gfx950); so lane j of the group addresses token
-// row r0 + j / 4, dims 16 cb + 4 (j % 4) .. +3, and lane i receives dim
-// 16 cb + i of rows r0 .. r0 + 3.  `addr` is that address for r0 = 4 grp;
-// rows 16 + 4 grp lie `kHalf` bytes further; dims 16 cb .. at kOff = 32 cb.
+// The V^T operand of lane (n, grp) for output dims 16 cb + n: the tokens
+// the score left in lane group grp (tile_row(4 grp + s), s < 4, and the same
+// 16 tokens further) of the staged tile, from two ds_read_b64_tr_b16.  That
+// instruction hands lane i of each 16-lane group 16-bit element i % 4 of the
+// 8-byte rows addressed by lanes 4k + i / 4, k = 0..3 (measured on gfx950);
+// so lane j of the group addresses token row tile_row(4 grp + j / 4), dims
+// 16 cb + 4 (j % 4) .. +3, and lane i receives dim 16 cb + i of the four
+// rows.  `addr` is that address; the rows 16 further lie `kHalf` bytes
+// further; dims 16 cb .. at kOff = 32 cb.
 // Issued from inline assembly on purpose: the compiler cannot tell that
 // these reads do not touch the buffer an HBM -> LDS copy is still filling,
 // and would otherwise wait for every outstanding copy first, which
@@ -149,6 +150,17 @@ __device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
   const u32x4 r = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(bf16x8, r);
 }
+
+// The token of a 16-token half that row n of the score MFMA's A operand (K)
+// stands for: n = 4 g + s takes token 4 s + g.  The score then leaves lane
+// (n, grp) the tokens tile_row(4 grp + j) = 4 j + grp, and the V^T operand
+// must follow: each 16-lane group of a transposing read addresses the four
+// tokens 4 k + grp, k = 0..3, which lie in four different staged copy blocks
+// (1056 bytes apart, 8 banks) -- with the identity order they were four rows
+// of one block, 256 bytes apart, all in the same 8 banks: a 4-way conflict
+// on every V^T read (measured: 6.6 M conflict cycles per launch on the
+// batched workload, 4.5 per LDS instruction).
+__device__ __forceinline__ constexpr int tile_row(int n) { return 4 * (n & 3) + (n >> 2); }
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
 template <int N, int I = 0, typename F>

@@ -234,17 +234,17 @@ void prefill_kernel(DecodeParams p) {
     }
   };
 
-  // LDS read offsets of the lane's K operands: row 16 h2 + n, chunk kb*4 + grp
+  // LDS read offsets of the lane's K operands: row 16 h2 + tile_row(n), chunk kb*4 + grp
   uint32_t koff[2][KB];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int t = 16 * h2 + n;
+      const int t = 16 * h2 + tile_row(n);
       koff[h2][kb] = static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
     }
-  // the lane's address for read_vt_tr: row 4 grp + n / 4, dims 4 (n % 4) ..
-  const uint32_t vrd = static_cast<uint32_t>(VG::at(4 * grp + n / 4, 8 * (n % 4)));
+  // the lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
+  const uint32_t vrd = static_cast<uint32_t>(VG::at(tile_row(4 * grp + n / 4), 8 * (n % 4)));
   constexpr int kVHalf = (16 / VG::RPI) * VG::BLOCK;     // rows r -> r + 16
 
   f32x4 acc[NB][CB];
@@ -313,7 +313,7 @@ void prefill_kernel(DecodeParams p) {
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int t = j0 + 16 * h2 + 4 * grp + j;
+            const int t = j0 + 16 * h2 + tile_row(4 * grp + j);
             if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
           }
       }
