@@ -193,6 +193,11 @@ def test_tuning_and_timer_validation(lib):
     assert lib.kvd_set_tuning(0, 24) == EINVAL           # not a multiple of 16
     assert lib.kvd_set_tuning(0, -16) == EINVAL
     assert lib.kvd_set_tuning(-1, 0) == OK
+    # dispatch orders 0-4 (4: the work list derived inside the split kernel)
+    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, 5) == EINVAL
+    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, -2) == EINVAL
+    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, 4) == OK
+    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, -1) == OK
     assert lib.kvd_timer_begin(0) == EINVAL
     assert lib.kvd_timer_begin(5000) == EINVAL
     assert lib.kvd_timer_end(None, None) == EINVAL
