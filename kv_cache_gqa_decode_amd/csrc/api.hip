@@ -191,6 +191,20 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
     const int cap = kernel == 2 && RT > 16 ? 4096 : 2048;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
+    // Short units pay the workgroup's fixed cost (q loads, merge, partial
+    // rows) too often: the MFMA kernel with up to 8 rows takes no fewer than
+    // 512 tokens per split while that still makes a full round of units at
+    // the bound, else no fewer than 256 under the same condition (measured:
+    // 16 sequences of 8K, 256-token splits 74% of the peak, 512 83%, 1024
+    // 85%; 8 sequences of 2K, 128 tokens 38%, 256 47%).
+    if (kernel == 1 && RT <= 8) {
+      for (const int floor_tokens : {512, 256}) {
+        if (chunk < floor_tokens && rows / floor_tokens >= slots) {
+          chunk = floor_tokens;
+          break;
+        }
+      }
+    }
     if (chunk > cap) chunk = cap;
   }
   if (chunk > kMaxChunk) chunk = kMaxChunk;
