@@ -392,6 +392,9 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     }
     compute(kt, base, blk_cur, cur, false);
   }
+  // a wave without tiles still has its (empty) copies outstanding: they
+  // write zeros into its staging buffers, which the merge below reuses
+  vmem_wait<0>();
 
   // per-wave sums: the four lane groups of a head hold partial sums under one max
 #pragma unroll
