@@ -196,16 +196,6 @@ __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int
   const int o = p.grid_order;
   return Unit{o == 1 ? y : z, o == 0 ? y : x, o == 0 ? x : (o == 1 ? z : y)};
 }
-// This workgroup's unit; false when it has none (order 3: past the end of
-// the work list, whose entries are b | split << 16 and whose KV heads are
-// the G consecutive workgroups of each entry).  The hardware hands
-// workgroups to the 8 XCDs round-robin by id, so with the heads in a fixed
-// order every XCD would serve one KV head (G = 8) for the whole dispatch;
-// the heads of entries k are rotated by k / 16 instead, so each XCD stays
-// on one head for 16 consecutive entries (neighbouring token ranges of one
-// sequence) and then moves on.  Measured on the batched workload's split
-// kernel: fixed heads 198 us, rotation by k 195, by k / 2 187, by k / 16
-// 185; 64 uniform 8K sequences 373, 356, 343, 338 us.
 // Order 4, batches of at most 64 sequences: the order-3 list without its
 // launch.  Every wave derives its entry k = id / G from the lengths, one
 // sequence per lane: an inclusive scan of the full-split counts places the
@@ -213,7 +203,8 @@ __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int
 // the key (16-token bucket of their length + 1) << 6 | (63 - b), unique per
 // lane, largest first -- longest bucket first, then by sequence -- and the
 // (k - n_full)-th largest is picked bit by bit with ballots (a radix
-// select: 16 steps of one compare and one popcount).
+// select: 16 steps of one compare and one popcount).  The KV heads of an
+// entry are rotated across the XCDs as in order 3 (see unit_at).
 __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u) {
   const int lane = threadIdx.x & 63;
   const int id = static_cast<int>(blockIdx.x);
@@ -263,6 +254,17 @@ __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u
   return true;
 }
 
+// This workgroup's unit; false when it has none (orders 3 and 4: past the
+// end of the work list; order 3 reads entries b | split << 16 built by
+// units.hip, and the KV heads of an entry are its G consecutive
+// workgroups).  The hardware hands
+// workgroups to the 8 XCDs round-robin by id, so with the heads in a fixed
+// order every XCD would serve one KV head (G = 8) for the whole dispatch;
+// the heads of entries k are rotated by k / 16 instead, so each XCD stays
+// on one head for 16 consecutive entries (neighbouring token ranges of one
+// sequence) and then moves on.  Measured on the batched workload's split
+// kernel: fixed heads 198 us, rotation by k 195, by k / 2 187, by k / 16
+// 185; 64 uniform 8K sequences 373, 356, 343, 338 us.
 __device__ __forceinline__ bool unit_at(const DecodeParams& p, Unit& u) {
   if (p.grid_order == 4) return unit_from_lengths(p, u);
   if (p.grid_order == 3) {
