@@ -43,6 +43,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,11 +65,24 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_source_hash(kernel: str = "mfma") -> str:
+def code_text(src: str) -> str:
+    """C++ source without its comments and with whitespace collapsed: what
+    the compiler sees, so that an edit to a comment keeps the hash."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(kernel: str = "mfma", read=None) -> str:
+    """Hash of the code (comments aside) of the sources a kernel is built
+    from; ``read(name)`` supplies a file's text (default: the working tree)."""
+    if read is None:
+        def read(name):
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                return f.read()
     h = hashlib.sha256()
     for name in sorted(KERNEL_SOURCES[kernel]):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        h.update(name.encode() + b"\0" + code_text(read(name)).encode())
     return h.hexdigest()[:16]
 
 

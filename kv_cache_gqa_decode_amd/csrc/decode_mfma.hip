@@ -31,13 +31,14 @@
 //           V^T is the A operand.  V rows travel HBM -> LDS directly
 //           (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): each
 //           instruction lands 64 lanes x 16 bytes contiguously, rows in
-//           order, and consecutive instructions are 32 bytes apart, so the
-//           four lane groups' 2-byte column reads fall in disjoint banks.
-//           The column reads are ds_read_u16, packed in pairs.  Rows past
-//           the end of the sequence
-//           or in an invalid block are read out of range, and are also
-//           zeroed in LDS after the copy in the tiles that have them (stale
-//           LDS may hold NaN and 0 * NaN is NaN).
+//           order, and consecutive instructions are 32 bytes apart.  The
+//           operand is read with gfx950's transposing ds_read_b64_tr_b16
+//           (read_vt_tr), the tokens in tile_row order so that each 16-lane
+//           group reads rows of four different copy instructions (banks 8
+//           apart).  Rows past the end of the sequence or in an invalid
+//           block are read out of range, and are also zeroed in LDS after
+//           the copy in the tiles that have them (stale LDS may hold NaN and
+//           0 * NaN is NaN).
 //
 // Software pipeline: while tile i is computed, tile i+1 is in flight -- its V
 // rows into the second of two LDS buffers from the start of tile i, its K
