@@ -192,16 +192,23 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   }
 
   // q rows, requested first: lane (n, grp) of block (nb, kb) holds dims
-  // kb*64 + grp*16 .. +15 of head nb*16 + n
+  // kb*64 + grp*16 .. +15 of head nb*16 + n.  With two column blocks the
+  // rows are loaded once per workgroup and staged in LDS (QStage).
   float4 qraw[NB][KB][4];
+  QStage<D> qst;
+  if constexpr (NB == 2) {
+    qst.load(p, b, g, RT, wave, lane);
+  } else {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int h = nb * 16 + n;
-    const float* src = p.q_rot + query_row(p, b, g, h < RT ? h : 0) * D + grp * 16;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int h = nb * 16 + n;
+      const float* src = p.q_rot + query_row(p, b, g, h < RT ? h : 0) * D + grp * 16;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qraw[nb][kb][j] = *reinterpret_cast<const float4*>(src + kb * 64 + 4 * j);
+        for (int j = 0; j < 4; ++j)
+          qraw[nb][kb][j] = *reinterpret_cast<const float4*>(src + kb * 64 + 4 * j);
+    }
   }
 
   // paged: the ids of the blocks this wave visits, lane j of register c =
@@ -285,9 +292,27 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   i32x4 kr0[4][KB], kr1[4][KB];
   int base = t0 + wave * kTT;
   bool vok0 = true, vok1 = true;
-  if (base < t1) {
-    issue_v(base, 0, vb0);
-    issue_k(base, 0, kr0, vok0);
+  // issued on every path (a wave without tiles reads its split's last group
+  // of K, in bounds, and copies nothing: empty descriptors), so the
+  // compiler's wait for the q loads stays partial instead of also waiting
+  // for this tile
+  issue_v(base, 0, vb0);
+  issue_k(base, 0, kr0, vok0);
+
+  if constexpr (NB == 2) {
+    const uint32_t st = lds_addr(stage);
+    qst.publish(st, kTileBytes, wave, lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int h = nb * 16 + n;
+      const uint32_t a = QStage<D>::row_addr(st, kTileBytes, h < RT ? h : 0) + 64 * grp;
+      static_for<KB>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        read_b128x2<256 * kb>(a, qraw[nb][kb][0], qraw[nb][kb][1]);
+        read_b128x2<256 * kb + 32>(a, qraw[nb][kb][2], qraw[nb][kb][3]);
+      });
+    }
+    __builtin_amdgcn_s_barrier();      // every wave's q read before the rows are reused
   }
 
   // q as three int8 limbs per head, and the per-head factors that turn the
@@ -474,6 +499,9 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
       ++kt;
     }
   }
+  // a wave without tiles still has its first tile's loads outstanding (the
+  // empty copies write zeros into its staging buffer, which the merge reuses)
+  vmem_wait<0>();
 
   // per-wave sums: the four lane groups of a head hold partial sums under one max
 #pragma unroll

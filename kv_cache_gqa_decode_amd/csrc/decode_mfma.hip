@@ -126,22 +126,12 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   // q operands, requested first: lane (n, grp) of block (nb, kb) holds dims
   // kb*32 + grp*8 .. +7 of head nb*16 + n.  Unconditional vector loads from a
   // valid head, then a select (a load under a per-lane branch would
-  // serialise into one round trip per element).
-  // With two column blocks (17 to 32 rows) every wave would load all rows
-  // (16 KB at D = 128) while the first tiles go out; instead wave w loads
-  // rows 8w .. 8w + 7 once for the workgroup and stages them in LDS (see
-  // below).  Lane l of staging load i: row 8 w + i * QRPI + l / QLPR, floats
-  // 4 (l % QLPR) .. +3.
+  // serialise into one round trip per element).  With two column blocks the
+  // rows are loaded once per workgroup and staged in LDS (QStage).
   float4 qraw[NB][KB][2];
-  constexpr int QLPR = D / 4, QRPI = 64 / QLPR, QNI = 8 / QRPI;
-  float4 qst[NB == 2 ? QNI : 1];
+  QStage<D> qst;
   if constexpr (NB == 2) {
-#pragma unroll
-    for (int i = 0; i < QNI; ++i) {
-      const int r = 8 * wave + i * QRPI + lane / QLPR;
-      qst[i] = *reinterpret_cast<const float4*>(p.q_rot + query_row(p, b, g, r < RT ? r : 0) * D +
-                                                4 * (lane % QLPR));
-    }
+    qst.load(p, b, g, RT, wave, lane);
   } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -253,44 +243,18 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   }
 
   if constexpr (NB == 2) {
-    // Staged q rows: row r in the second V buffer of wave r / 8 (untouched
-    // until the first tile's successor is requested), rows QS bytes apart
-    // (16 bytes of padding: the 8 lanes of a b128 read pass, rows apart,
-    // fall in different banks).  The LDS accesses are inline assembly for
-    // the reason given at read_vt_tr (the first tile's copies are still in
-    // flight); the barriers carry no memory fence, so they do not wait for
-    // those copies either.
-    constexpr int QS = D * 4 + 16;
-    auto qrow_addr = [&](int r) {
-      return lds_addr(stage) + static_cast<uint32_t>((2 * (r >> 3) + 1) * G::kTileBytes + (r & 7) * QS);
-    };
-#pragma unroll
-    for (int i = 0; i < QNI; ++i) {
-      const uint32_t a = qrow_addr(8 * wave + i * QRPI + lane / QLPR) + 16 * (lane % QLPR);
-      const u32x4 v = __builtin_bit_cast(u32x4, qst[i]);
-      asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
-    }
-    __builtin_amdgcn_s_barrier();
+    const uint32_t st = lds_addr(stage);
+    qst.publish(st, G::kTileBytes, wave, lane);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int h = nb * 16 + n;
-      const uint32_t a = qrow_addr(h < RT ? h : 0) + 32 * grp;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        u32x4 x0, x1;
-        asm volatile(
-            "ds_read_b128 %0, %2 offset:%3\n\t"
-            "ds_read_b128 %1, %2 offset:%4\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(x0), "=&v"(x1)
-            : "v"(a), "i"(128 * kb), "i"(128 * kb + 16)
-            : "memory");
-        qraw[nb][kb][0] = __builtin_bit_cast(float4, x0);
-        qraw[nb][kb][1] = __builtin_bit_cast(float4, x1);
-      }
+      const uint32_t a = QStage<D>::row_addr(st, G::kTileBytes, h < RT ? h : 0) + 32 * grp;
+      static_for<KB>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        read_b128x2<128 * kb>(a, qraw[nb][kb][0], qraw[nb][kb][1]);
+      });
     }
-    // every wave has read its q before any wave's next V copies reuse the rows
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();      // every wave's q read before the rows are reused
   }
 
   // q * scale * log2(e) as bf16 hi + lo (heads >= n_rep get zeros)

@@ -162,6 +162,71 @@ __device__ __forceinline__ bf16x8 read_vt_tr(uint32_t addr) {
 // batched workload, 4.5 per LDS instruction).
 __device__ __forceinline__ constexpr int tile_row(int n) { return 4 * (n & 3) + (n >> 2); }
 
+// Query rows staged once per workgroup, for the kernels with two column
+// blocks (17 to 32 query rows per KV head): there every wave needs all rows
+// (16 KB of fp32 at D = 128), and four waves loading them each while the
+// first tiles go out measured a start-up twice as long (128K MQA: q in
+// registers after 2.8 us, against 1.3 us with no q load at all).  Wave w
+// loads rows 8w .. 8w + 7 (lane l of load i: row 8w + i RPI + l / LPR,
+// floats 4 (l % LPR) .. +3; rows past RT read row 0), and `publish` writes
+// them to the second staging buffer of wave r / 8, which no copy touches
+// before the first tile's successor is requested, rows ROW bytes apart (16
+// bytes of padding: the 8 lanes of a b128 read pass, rows apart, fall in
+// different banks).  The LDS accesses are inline assembly and the barrier
+// carries no memory fence, for the reason given at read_vt_tr: the first
+// tile's HBM -> LDS copies are still in flight.  After reading its rows
+// (read_b128x2), every wave passes a second barrier before any reuse.
+template <int D>
+struct QStage {
+  static constexpr int LPR = D / 4;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int NI = 8 / RPI;
+  static constexpr int ROW = D * 4 + 16;
+  float4 v[NI];
+
+  __device__ __forceinline__ void load(const DecodeParams& p, int b, int g, int RT, int wave,
+                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = 8 * wave + i * RPI + lane / LPR;
+      v[i] = *reinterpret_cast<const float4*>(p.q_rot + query_row(p, b, g, r < RT ? r : 0) * D +
+                                              4 * (lane % LPR));
+    }
+  }
+  // LDS address of staged row r (buffers of `tile_bytes`, two per wave)
+  __device__ __forceinline__ static uint32_t row_addr(uint32_t stage, int tile_bytes, int r) {
+    return stage + static_cast<uint32_t>((2 * (r >> 3) + 1) * tile_bytes + (r & 7) * ROW);
+  }
+  __device__ __forceinline__ void publish(uint32_t stage, int tile_bytes, int wave,
+                                          int lane) const {
+    // the smallest staging buffer: the INT8 kernel's, 4 groups of 16 x D bytes
+    static_assert(8 * ROW <= 4 * D * 16, "eight rows fit a staging buffer");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t a = row_addr(stage, tile_bytes, 8 * wave + i * RPI + lane / LPR) +
+                         16 * (lane % LPR);
+      const u32x4 x = __builtin_bit_cast(u32x4, v[i]);
+      asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(x) : "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+  }
+};
+
+// Two 16-byte LDS reads at addr + kOff and addr + kOff + 16, waited for.
+template <int kOff>
+__device__ __forceinline__ void read_b128x2(uint32_t addr, float4& x0, float4& x1) {
+  u32x4 a, b;
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%3\n\t"
+      "ds_read_b128 %1, %2 offset:%4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "i"(kOff), "i"(kOff + 16)
+      : "memory");
+  x0 = __builtin_bit_cast(float4, a);
+  x1 = __builtin_bit_cast(float4, b);
+}
+
 // f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices).
 template <int N, int I = 0, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
