@@ -292,12 +292,16 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   i32x4 kr0[4][KB], kr1[4][KB];
   int base = t0 + wave * kTT;
   bool vok0 = true, vok1 = true;
-  // issued on every path (a wave without tiles reads its split's last group
-  // of K, in bounds, and copies nothing: empty descriptors), so the
-  // compiler's wait for the q loads stays partial instead of also waiting
-  // for this tile
-  issue_v(base, 0, vb0);
-  issue_k(base, 0, kr0, vok0);
+  // With two column blocks the first tile is requested on every path (a
+  // wave without tiles reads its split's last group of K, in bounds, and
+  // copies nothing: empty descriptors), so the compiler's wait for the q
+  // rows it stages stays partial instead of also waiting for this tile.
+  // With one block the request stays under the branch: issuing it on every
+  // path measured 2-3% slower on a 128K GQA sequence (same box, A/B).
+  if (NB == 2 || base < t1) {
+    issue_v(base, 0, vb0);
+    issue_k(base, 0, kr0, vok0);
+  }
 
   if constexpr (NB == 2) {
     const uint32_t st = lds_addr(stage);
