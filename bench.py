@@ -6,15 +6,26 @@ layer over a batch of synthetic sequences whose inputs are already resident
 in HBM.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
 decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
 
+Timing protocol: before every timed step (and every warm-up step) a 1 GiB
+scratch buffer is written, outside the event bracket, so that no K/V byte
+is left in the 256 MB last-level cache (MALL) or the L2s: every step reads
+its cache cold from HBM, as a decode step of one layer does in a model.
+Each step is bracketed by its own pair of events; the line reports p10 /
+p50 / p90 over the K steps and takes p50 as the headline.  The same
+protocol, in a second pass, times the split-K kernel alone with events the
+library records on its stream around that launch (kvd_options).  A third
+pass times K back-to-back steps without eviction ("warm", reported apart,
+never used for the roofline); --no-warm skips it (profiling runs).
+
 Prints ONE JSON line:
-  value      KV HBM GB/s of the whole step = KV bytes / step time, where
+  value      KV HBM GB/s of the whole step = KV bytes / p50 step time, where
              KV bytes = sum_b L_b * G * D * 2 (K and V) * 2 bytes
-  roofline   the split-K attention kernel alone: KV bytes / its mean
-             duration (HIP events recorded on its stream around every launch
-             in the timed region) against the 8 TB/s HBM peak; `traffic`
-             is the HBM bytes per launch from the committed rocprofv3
-             counter summary of this kernel and workload (null when missing
-             or taken from a different kernel source)
+  roofline   the split-K attention kernel alone: KV bytes / its p50
+             duration against the 8 TB/s HBM peak; `traffic` is the HBM
+             bytes per launch from the committed rocprofv3 counter summary
+             of this kernel and workload (null when missing or taken from a
+             different kernel source); with --read-ceiling also the
+             fraction of the measured streaming-read ceiling
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload, in the same unit (a reported baseline only)
 
@@ -37,7 +48,7 @@ processes B * T tokens.
 Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
                        [--kv-heads G] [--kv native|int8] [--n-query T] [--prefill T]
                        [--kernel auto|valu|mfma] [--split N]
-                       [--no-cpu-baseline] [--flush]
+                       [--no-cpu-baseline] [--no-warm] [--read-ceiling]
 """
 import argparse
 import hashlib
@@ -58,10 +69,10 @@ CSRC = os.path.join(ROOT, "kv_cache_gqa_decode_amd", "csrc")
 # the sources each split-K kernel is built from (a change to any of them
 # invalidates the traffic counters recorded for that kernel)
 KERNEL_SOURCES = {
-    "mfma": ("decode_mfma.hip", "mfma_tile.h", "kvd_internal.h"),
-    "int8": ("decode_i8.hip", "mfma_tile.h", "kvd_internal.h"),
+    "mfma": ("decode_mfma.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
+    "int8": ("decode_i8.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
     "valu": ("decode_valu.hip", "kvd_internal.h"),
-    "prefill": ("prefill_mfma.hip", "mfma_tile.h", "kvd_internal.h"),
+    "prefill": ("prefill_mfma.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
 }
 
 
@@ -113,31 +124,114 @@ def load_traffic(key: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def read_ceiling(dev, kvd, gib: int = 4):
-    """Best streaming-read bandwidth of the read probe over a few launch
-    shapes (GB/s), the practical roof beside the nominal peak."""
+FLUSH_BYTES = 1 << 30      # 4x the 256 MB MALL
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, np.float64), q))
+
+
+def summary(xs):
+    """p10 / p50 / p90 / mean of a list of milliseconds."""
+    return {"p10": round(pct(xs, 10), 5), "p50": round(pct(xs, 50), 5),
+            "p90": round(pct(xs, 90), 5), "mean": round(sum(xs) / len(xs), 5), "n": len(xs)}
+
+
+class Flusher:
+    """Writes a 1 GiB scratch buffer on the current stream: afterwards no
+    K/V byte is left in the MALL or the L2s."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(self.i & 0xFF)
+
+
+def cold_times(run, n, flush):
+    """Milliseconds of n calls of run(), each after a flush, each bracketed
+    by its own events on the current stream (the flush outside)."""
     import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        flush()
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cold_kernel_times(run_with_events, n, flush):
+    """Milliseconds of the main kernel of n calls, each after a flush: the
+    library records the events around that launch (kvd_options)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:            # create the HIP events before the timed loop
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for a, b in evs:
+        flush()
+        run_with_events(a, b)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def warm_ms(run, n):
+    """Mean milliseconds of n back-to-back calls (no eviction)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def read_ceiling(dev, kvd, gib: int = 4):
+    """Best streaming-read bandwidth of the read probe over its load paths
+    (registers or HBM -> LDS copies, default or non-temporal policy) and a
+    few launch shapes (GB/s): the practical roof beside the nominal peak.
+    The 4 GiB buffer is 16x the MALL, so every launch reads from HBM."""
+    import torch
+    from kv_cache_gqa_decode_amd import _binding as B
     buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    names = {0: "registers, grid-stride", B.PROBE_CHUNKED: "registers, chunk per workgroup",
+             B.PROBE_CHUNKED | B.PROBE_NONTEMPORAL: "registers non-temporal, chunk per workgroup",
+             B.PROBE_NONTEMPORAL: "registers non-temporal, grid-stride",
+             B.PROBE_LDS: "HBM->LDS copies, chunk per workgroup",
+             B.PROBE_LDS | B.PROBE_NONTEMPORAL: "HBM->LDS non-temporal copies, chunk per workgroup"}
     best = (0.0, None)
-    for chunked in (False, True):
-        for per_cu in (2, 4, 8, 16):
+    for mode, name in names.items():
+        for per_cu in (1, 2, 4, 8):
             for unroll in (4, 8, 16):
                 nwg = cu * per_cu
-                sink = kvd.read_probe(buf, nwg, unroll, chunked)
+                sink = kvd.read_probe(buf, nwg, unroll, mode)
                 torch.cuda.synchronize()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
                 for _ in range(5):
-                    kvd.read_probe(buf, nwg, unroll, chunked, sink)
+                    kvd.read_probe(buf, nwg, unroll, mode, sink)
                 b.record()
                 torch.cuda.synchronize()
                 gbs = 5 * buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
                 if gbs > best[0]:
-                    best = (gbs, f"{'contiguous chunk per workgroup' if chunked else 'grid-stride'}, "
-                                 f"{per_cu} workgroups/CU x 256 threads, {unroll} x 16 B in flight")
+                    best = (gbs, f"{name}, {per_cu} workgroups/CU x 256 threads, "
+                                 f"{unroll} x 16 B in flight per lane")
     del buf
+    torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
             "shape": best[1], "buffer_gib": gib}
 
@@ -264,30 +358,24 @@ def run_prefill(args, s, dev):
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     max_len = p.max_len
 
-    def step():
+    def step(options=None):
         kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                  t["positions"], table, base=s.rope_base, q_rot=q_rot)
         kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
-                             max_seq_len=max_len, out=out, lse=lse)
+                             max_seq_len=max_len, out=out, lse=lse, options=options)
 
+    flush = Flusher(dev)
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
+    steps = cold_times(step, args.steps, flush)
     t_wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
-    with kvd.kernel_timer(args.steps) as kt:
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
+    kern = cold_kernel_times(lambda a, b: step(kvd.Options(events=(a, b))), args.steps, flush)
+    ms = pct(steps, 50)
     flops = sizing.window_attention_flops(p.seq_lens, T, H, D)
-    kern_ms = kt.mean_ms
+    kern_ms = pct(kern, 50)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     result = {
         "metric": "causal prefill attention TFLOP/s at 1 MI355X",
@@ -305,11 +393,14 @@ def run_prefill(args, s, dev):
                    "arithmetic": "q and P rounded to bf16 on the matrix cores, fp32 accumulate",
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+        "timing": "each step after a 1 GiB cache-evicting write; ms_per_step = p50",
+        "step_ms": summary(steps),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4), "traffic": None,
                      "kernel": "causal prefill attention", "kernel_ms": round(kern_ms, 4),
-                     "launches_timed": kt.count, "algorithmic_flops_per_launch": flops,
+                     "kernel_ms_pct": summary(kern), "launches_timed": len(kern),
+                     "algorithmic_flops_per_launch": flops,
                      "kernel_source_hash": kernel_source_hash("prefill")},
     }
     if not args.no_cpu_baseline:
@@ -345,9 +436,13 @@ def main():
                          "(the kernel-time region stays eager)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--flush", action="store_true",
-                    help="also time each step after evicting the 256 MB MALL")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm (back-to-back, no eviction) pass: every launch of "
+                         "the run is then cold, as a kernel-trace profile should see them")
     ap.add_argument("--read-ceiling", action="store_true",
+                    help="also measure the streaming-read ceiling (the read probe over a "
+                         "4 GiB buffer) and report the kernel against it")
+    ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the streaming-read ceiling and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
@@ -378,7 +473,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
         return
-    if args.read_ceiling:
+    if args.ceiling_only:
         print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd)}))
         return
     s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
@@ -410,24 +505,29 @@ def main():
         t["k_scale"] = W.as_torch(p.k_scale, dev)
         t["v_scale"] = W.as_torch(p.v_scale, dev)
     max_len = p.max_len
-    kvd.set_tuning(None if args.kernel == "auto" else args.kernel, args.split, args.tail_split,
-                   args.tail_span, None if args.order < 0 else args.order)
+    opts = kvd.Options(kernel=None if args.kernel == "auto" else args.kernel,
+                       split_tokens=args.split, tail_split_tokens=args.tail_split,
+                       tail_span_tokens=max(args.tail_span, 0),
+                       dispatch_order=None if args.order < 0 else args.order)
+    if opts == kvd.Options():
+        opts = None          # the automatic plan: the plain entry points
     B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
     lead = (B,) if T == 1 else (B, T)
     q_rot = torch.empty((*lead, H, D), dtype=torch.float32, device=dev)
     out = torch.empty((*lead, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((*lead, H), dtype=torch.float32, device=dev)
-    ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len, n_query=T)
+    ws_bytes = kvd.workspace_size(q_rot, t["k_cache"], table, max_len, n_query=T, options=opts)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T)
+    plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T, options=opts)
     sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
 
-    def step():
+    def step(options=opts):
         if T > 1:
             kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                      t["positions"], table, base=s.rope_base, q_rot=q_rot, **sc)
             kvd.gqa_decode_attn_multi(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
-                                      max_seq_len=max_len, out=out, lse=lse, workspace=ws, **sc)
+                                      max_seq_len=max_len, out=out, lse=lse, workspace=ws,
+                                      options=options, **sc)
             return
         if int8:
             kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
@@ -435,14 +535,16 @@ def main():
                                     base=s.rope_base, q_rot=q_rot)
             kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
                                      t["v_scale"], t["seq_lens"], table, max_seq_len=max_len,
-                                     out=out, lse=lse, workspace=ws)
+                                     out=out, lse=lse, workspace=ws, options=options)
             return
         kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                            t["positions"], table, base=s.rope_base, q_rot=q_rot)
         kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
-                            max_seq_len=max_len, out=out, lse=lse, workspace=ws)
+                            max_seq_len=max_len, out=out, lse=lse, workspace=ws, options=options)
 
+    flush = Flusher(dev)
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     run = step
@@ -457,43 +559,26 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         run = graph.replay
-    # timed region 1: K whole steps, nothing else on the stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # pass 1: K whole steps, each after a cache-evicting write
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        run()
-    ev1.record()
-    torch.cuda.synchronize()
+    steps = cold_times(run, args.steps, flush)
     t_wall = time.perf_counter() - t_wall
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    # timed region 2: the same K steps with HIP events recorded on the stream
-    # around every launch of the split-K attention kernel (the events add a
-    # few microseconds between launches, so the step time comes from region 1)
-    with kvd.kernel_timer(args.steps) as kt:
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
+    # pass 2: the split-K kernel alone, same protocol, events recorded by the
+    # library around its launch (they would add gaps inside pass 1's steps)
+    base_opts = opts if opts is not None else kvd.Options()
+    kern = cold_kernel_times(lambda a, b: step(base_opts.with_events(a, b)), args.steps, flush)
+    # pass 3: back-to-back steps, no eviction (reported apart)
+    warm = None if args.no_warm else warm_ms(run, args.steps)
+    del flush
+    torch.cuda.empty_cache()
+    ms_per_step = pct(steps, 50)
     kv_bytes = sizing.decode_kv_read_bytes(p.seq_lens, G, D, s.elem_bytes)
     aux = sizing.decode_aux_bytes(B, H, G, D, s.elem_bytes,
                                   int(sum(-(-int(L) // s.block_size) for L in p.seq_lens)) if table is not None else 0)
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    kern_ms = kt.mean_ms
+    kern_ms = pct(kern, 50)
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
-
-    flushed = None
-    if args.flush:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        times = []
-        for _ in range(min(args.steps, 20)):
-            scratch.fill_(1)
-            a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(); step(); b2.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b2))
-        flushed = float(np.median(times))
-        del scratch
+    ceiling = read_ceiling(dev, kvd) if args.read_ceiling else None
 
     key = (f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "") +
            (f"_bs{s.block_size}" if s.block_size not in (0, 16) else "") +
@@ -528,17 +613,25 @@ def main():
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "timing": ("each step after a 1 GiB cache-evicting write (MALL and L2 cold); "
+                   "ms_per_step and value from the p50 of the K steps"),
+        "step_ms": summary(steps),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "decode split-K attention",
-                     "kernel_ms": round(kern_ms, 5), "launches_timed": kt.count,
-                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": summary(kern),
+                     "launches_timed": len(kern), "algorithmic_bytes_per_launch": kv_bytes,
                      "kernel_source_hash": src_hash},
     }
-    if flushed is not None:
-        result["mall_flushed_ms_per_step"] = round(flushed, 5)
-        result["mall_flushed_gbs"] = round(kv_bytes / (flushed * 1e-3) / 1e9, 1)
+    if ceiling is not None:
+        result["roofline"]["read_ceiling_gbs"] = ceiling["gbs"]
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
+        result["hbm_read_ceiling"] = ceiling
+    if warm is not None:
+        result["warm"] = {"ms_per_step": round(warm, 5),
+                          "gbs": round(kv_bytes / (warm * 1e-3) / 1e9, 1),
+                          "note": "back-to-back steps, no eviction; not used for the roofline"}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(s, p, args.cpu_budget)

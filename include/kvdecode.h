@@ -31,8 +31,10 @@
  *   block id skips that append; a length above max_seq_len_host is clamped
  *   to it; a block id outside [0, num_blocks) contributes nothing.  Outputs
  *   for such inputs are unspecified.
- * - Calls on different streams are independent; the library keeps only a
- *   per-device property cache and the optional tuning / timing state below.
+ * - The library holds no state between calls apart from a per-device cache
+ *   of the compute-unit count: plan overrides and timing events travel with
+ *   the call (kvd_options).  Calls on different streams are independent as
+ *   long as they do not share a workspace or an output buffer.
  */
 #ifndef KVDECODE_H
 #define KVDECODE_H
@@ -111,6 +113,66 @@ typedef struct kvd_shape {
   int32_t max_blocks_per_seq;
 } kvd_shape;
 
+/* Kernels of the split-K attention (kvd_options.kernel, kvd_get_plan). */
+typedef enum {
+  KVD_KERNEL_AUTO = 0,   /* the planner's choice */
+  KVD_KERNEL_VALU = 1,   /* vector-ALU dot products: fp32 and bf16 caches, one new token */
+  KVD_KERNEL_MFMA = 2,   /* matrix cores: bf16 caches, up to 32 query rows per KV head */
+  KVD_KERNEL_INT8 = 3    /* matrix cores on INT8 codes: INT8 caches (their only kernel) */
+} kvd_kernel;
+
+/* Order in which the (sequence, KV head, split) units of the matrix-core
+ * kernels are dispatched (kvd_options.dispatch_order).  Results do not
+ * depend on it: each unit writes its own partial and the merge reads them
+ * in split order. */
+typedef enum {
+  KVD_ORDER_AUTO = 0,            /* the planner's choice */
+  KVD_ORDER_SPLIT_HEAD_SEQ = 1,  /* split fastest, then KV head, then sequence */
+  KVD_ORDER_HEAD_SEQ_SPLIT = 2,  /* KV head fastest, then sequence, then split */
+  KVD_ORDER_HEAD_SPLIT_SEQ = 3,  /* KV head fastest, then split, then sequence */
+  /* a work list of the (sequence, split) units that hold tokens, built on
+   * the device from seq_lens by a kernel before the split kernel: full
+   * splits sequence by sequence, then the partial last splits longest
+   * first (ignored with a single split) */
+  KVD_ORDER_DEVICE_LIST = 4,
+  /* the same list derived inside the split kernel without the extra launch
+   * (batches of at most 64 sequences; ignored otherwise) */
+  KVD_ORDER_WAVE_LIST = 5
+} kvd_dispatch_order;
+
+/*
+ * Per-call options of the attention calls that take them.  A NULL pointer,
+ * or a zero-initialised struct, means "automatic" for every field.
+ *   kernel           kvd_kernel; a kernel that cannot run this call gives
+ *                    EUNSUPPORTED
+ *   split_tokens     tokens per split: 0 automatic, else a multiple of 16 in
+ *                    [16, 8192]
+ *   tail_split_tokens, tail_span_tokens
+ *                    the last tail_span_tokens positions of the length bound
+ *                    (0: those after the last whole split) are cut into
+ *                    splits of tail_split_tokens (a multiple of 16, at most
+ *                    the split size; 0: none), so that the units dispatched
+ *                    last are short
+ *   dispatch_order   kvd_dispatch_order
+ *   reserved         must be 0
+ *   event_start, event_stop
+ *                    hipEvent_t handles (both or neither) recorded on
+ *                    `stream` immediately before and after the launch of the
+ *                    call's main kernel (the split-K kernel; the prefill
+ *                    kernel), for measuring that kernel alone; NULL: none
+ * Errors: EINVAL for values outside these ranges.
+ */
+typedef struct kvd_options {
+  int32_t kernel;
+  int32_t split_tokens;
+  int32_t tail_split_tokens;
+  int32_t tail_span_tokens;
+  int32_t dispatch_order;
+  int32_t reserved;
+  void* event_start;
+  void* event_stop;
+} kvd_options;
+
 /*
  * rope_append_kv -- RoPE on q and the new k, then the cache append.
  *
@@ -167,8 +229,10 @@ kvd_status rope_append_kv(const kvd_shape* shape, const void* q, const void* k_n
  *   block_table  as in rope_append_kv
  *   max_seq_len_host  host-side upper bound of seq_lens, used to plan the
  *              grid; 0 <= max_seq_len_host <= shape->max_seq_len
- *   scale      softmax scale, normally 1/sqrt(D) ([KVGR] §2.1: d_k is the
- *              per-head dimension; [OPT] §三: the default 1/sqrt(d_k))
+ *   scale      softmax scale, finite; 0 selects the default 1/sqrt(D)
+ *              ([KVGR] §2.1: d_k is the per-head dimension; [OPT] §三: the
+ *              default 1/sqrt(d_k)), computed by the library in double
+ *              precision
  *   out        [B, H, D] fp32 output
  *   lse        [B, H] fp32 output (natural log), or NULL
  *   workspace  device scratch of at least gqa_decode_workspace_size(shape,
@@ -238,7 +302,7 @@ kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace gqa_decode_attn needs for this shape and length bound
- * on the current device under the current tuning (0 when no split merge is
+ * on the current device with the automatic plan (0 when no split merge is
  * needed).  Returns 0 for an invalid shape as well; gqa_decode_attn then
  * reports the shape error. */
 size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host);
@@ -262,7 +326,9 @@ size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_hos
  *   rope_append_kv (bf16 inputs for INT8 caches); every slot P + t must be
  *   below max_seq_len and, when paged, in a block of sequence b's own
  *
- * gqa_decode_attn_multi: with L_b = seq_lens[b] counting the new tokens
+ * gqa_decode_attn_multi (the general form of the attention calls: any
+ * cache dtype, T new tokens, per-call options): with L_b = seq_lens[b]
+ * counting the new tokens
  * (L_b = P + n_query after the append), query t of sequence b attends the
  * tokens j < L_b - n_query + 1 + t, its own and those before it:
  *   out[b, t, h, :], lse[b, t, h] as gqa_decode_attn over those tokens
@@ -270,7 +336,9 @@ size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_hos
  *   q_rot      [B, n_query, H, D] fp32; out [B, n_query, H, D]; lse
  *              [B, n_query, H] or NULL
  *   k_scale, v_scale  as in rope_append_kv_multi
- *   workspace  gqa_decode_workspace_size_multi(shape, n_query, ..) bytes
+ *   workspace  gqa_decode_workspace_size_multi(shape, n_query, .., options)
+ *              bytes (the options change the plan, hence the size)
+ *   options    kvd_options or NULL
  * The matrix-core kernels take the n_query * H / G query rows of a KV head
  * together: at most 32 of them (bf16 and INT8 caches).  fp32 caches take
  * n_query = 1 only.
@@ -291,7 +359,8 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
                                  const float* v_scale, const int32_t* seq_lens,
                                  const int32_t* block_table, int32_t max_seq_len_host,
                                  float scale, float* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream);
 /*
  * gqa_prefill_attn -- causal attention of a prompt, or of one chunk of a
  * prompt appended after a cached history: n_query = T new tokens per
@@ -313,87 +382,61 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
  *              (natural log) or NULL
  *   k_cache, v_cache, seq_lens, block_table, max_seq_len_host, scale
  *              as in gqa_decode_attn
- * Errors: EINVAL, ERANGE as gqa_decode_attn; EUNSUPPORTED for a cache dtype
- * other than bf16 or n_query outside [1, max_seq_len]; EHIP.
+ *   options    NULL, or kvd_options carrying only timing events (every
+ *              other field 0: the prefill kernel has no split plan)
+ * Errors: EINVAL, ERANGE as gqa_decode_attn (EINVAL also for plan fields in
+ * options); EUNSUPPORTED for a cache dtype other than bf16 or n_query
+ * outside [1, max_seq_len]; EHIP.
  */
 kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
-                            float* out, float* lse, void* stream);
+                            float* out, float* lse, const kvd_options* options, void* stream);
 
-/* Workspace bytes of gqa_decode_attn_multi (0 also for an invalid shape). */
+/* Workspace bytes of gqa_decode_attn_multi with these options (NULL:
+ * automatic); 0 also for an invalid shape or invalid options. */
 size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,
-                                       int32_t max_seq_len_host);
+                                       int32_t max_seq_len_host, const kvd_options* options);
 
 /* Static, NUL-terminated description of a status code. */
 const char* kvd_status_string(int32_t status);
 
 /*
- * Plan inspection and tuning (process-wide; set before issuing work).
- *
- * kvd_get_plan reports how gqa_decode_attn would run: plan[0] = tokens per
- * split (a multiple of 16), plan[1] = number of splits, plan[2] = kernel
- * (0 = VALU dot products, 1 = MFMA, 2 = INT8 MFMA), plan[3] = workgroups
- * launched by the split kernel.  `plan` is a host array of 4 int32.
- *
- * kvd_set_tuning overrides the plan: kernel = -1 (automatic), 0 (VALU),
- * 1 (MFMA, bf16 only, up to 32 query heads per KV head) or 2 (INT8 caches,
- * their only kernel); split_tokens = 0
- * (automatic) or a positive multiple of 16.  EUNSUPPORTED if the override
- * cannot run; the override applies to later calls in the whole process.
+ * Plan inspection.  kvd_get_plan reports how gqa_decode_attn would run:
+ * plan[0] = tokens per split (a multiple of 16), plan[1] = number of splits,
+ * plan[2] = the kernel (a kvd_kernel value other than AUTO), plan[3] =
+ * workgroups launched by the split kernel.  `plan` is a host array of 4
+ * int32.  kvd_get_plan_multi does the same for gqa_decode_attn_multi with
+ * n_query new tokens and the given options (NULL: automatic).
+ * Errors: as the attention calls (EUNSUPPORTED when a requested kernel
+ * cannot run the shape).
  */
 kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan);
-/* The plan of gqa_decode_attn_multi with n_query new tokens per sequence. */
 kvd_status kvd_get_plan_multi(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len_host,
-                              int32_t* plan);
-kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens);
-
-/*
- * kvd_set_tuning_ex adds three knobs of the split layout to kvd_set_tuning's
- * two (same meaning): the last tail_span_tokens positions of the length
- * bound are cut into splits of tail_split_tokens (a multiple of 16, at most
- * split_tokens; 0 = no such splits, span -1 = automatic), so the units the
- * hardware dispatches last are short; dispatch_order sets which of (split,
- * KV head, sequence) varies fastest in the MFMA kernels' unit order: 0
- * (split, head, sequence), 1 (head, sequence, split), 2 (head, split,
- * sequence), 3 a work list of the (sequence, split) units that hold
- * tokens, built on the device from seq_lens before the split kernel (full
- * splits sequence by sequence, then the partial last splits longest first;
- * ignored with a single split), 4 the same list derived inside the split
- * kernel, without the launch that builds it (batches of at most 64
- * sequences; ignored otherwise), -1 automatic (order 4 for batches of 2 to
- * 64 sequences with more than one split, order 3 above 64).  EINVAL for
- * values outside these ranges.
- */
-kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
-                             int32_t tail_span_tokens, int32_t dispatch_order);
-
-/*
- * Kernel timing for measurement.  kvd_timer_begin(n) makes the next n calls
- * of the attention functions (gqa_decode_attn and its _int8 / _multi forms,
- * gqa_prefill_attn) record a pair of HIP events on their stream around the
- * launch of their main kernel -- the split-K kernel, the prefill kernel --
- * (n <= 4096).  kvd_timer_end waits for those events
- * and returns the summed kernel time in milliseconds and the number of
- * launches timed, then disables timing.  Host pointers.
- */
-kvd_status kvd_timer_begin(int32_t n_launches);
-kvd_status kvd_timer_end(double* total_ms, int32_t* n_timed);
+                              const kvd_options* options, int32_t* plan);
 
 /*
  * kvd_read_probe -- measurement utility, not part of the decode step: reads
- * `bytes` (a multiple of 16) of the 16-byte-aligned device buffer `buf` with
- * coalesced 16-byte loads (`unroll` in {1, 4, 8, 16} loads in flight per
- * thread, `n_workgroups` workgroups of 256 threads; chunked = 0: the grid
- * strides over the buffer together, chunked = 1: each workgroup streams one
- * contiguous 1/n_workgroups of it) and writes one XOR word per workgroup to
- * `sink` (device, n_workgroups uint32).  Its duration gives the device's
- * practical streaming-read bandwidth, the roof the decode kernels are
- * compared with beside the nominal HBM peak.
+ * `bytes` (a multiple of 16; of 1024 with KVD_PROBE_LDS) of the
+ * 16-byte-aligned device buffer `buf` with coalesced 16-byte loads
+ * (`unroll` in {1, 4, 8, 16} loads in flight per lane, `n_workgroups`
+ * workgroups of 256 threads) and writes one XOR word per workgroup to `sink`
+ * (device, n_workgroups uint32).  `mode` is an OR of
+ *   KVD_PROBE_CHUNKED      each workgroup streams one contiguous
+ *                          1/n_workgroups of the buffer (else the grid
+ *                          strides over it together);
+ *   KVD_PROBE_NONTEMPORAL  loads carry the non-temporal (streaming) hint;
+ *   KVD_PROBE_LDS          the decode kernels' V path: each wave copies 1 KiB
+ *                          pieces HBM -> LDS with buffer loads that bypass
+ *                          the registers (implies chunked; each workgroup's
+ *                          range must stay below 2 GiB).
+ * Its duration gives the device's practical streaming-read bandwidth, the
+ * roof the decode kernels are compared with beside the nominal HBM peak.
  * Errors: EINVAL, EUNSUPPORTED (unroll), EHIP.
  */
+enum { KVD_PROBE_CHUNKED = 1, KVD_PROBE_NONTEMPORAL = 2, KVD_PROBE_LDS = 4 };
 kvd_status kvd_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
-                          int32_t unroll, int32_t chunked, void* stream);
+                          int32_t unroll, int32_t mode, void* stream);
 
 #ifdef __cplusplus
 }

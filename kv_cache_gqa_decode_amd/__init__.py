@@ -10,7 +10,7 @@ __all__ = ["rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8", "gqa_deco
 
 
 def __getattr__(name):
-    if name in __all__ or name in ("set_tuning", "get_plan", "KvdError", "kernel_timer", "read_probe",
+    if name in __all__ or name in ("Options", "get_plan", "KvdError", "read_probe",
                                    "v_cache_shape_int8"):
         from . import _binding
         return getattr(_binding, name)

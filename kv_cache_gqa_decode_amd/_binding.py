@@ -6,11 +6,16 @@ shapes, allocates outputs and the split workspace with torch, passes raw
 pointers and the current HIP stream, and turns status codes into
 exceptions.  There is no fallback: without the built library every call
 raises.
+
+The split workspace, when the caller passes none, is allocated per call
+through torch's caching allocator on the call's stream: calls on different
+streams never share one, and under graph capture the graph's memory pool
+keeps it alive for the graph's lifetime.
 """
 from __future__ import annotations
 
 import ctypes
-import math
+import dataclasses
 import os
 import threading
 from typing import Optional, Tuple
@@ -24,8 +29,9 @@ LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(
 
 KVD_FP32, KVD_BF16, KVD_INT8 = 0, 1, 2
 _STYLES = {"interleaved": 0, "half": 1}
-_KERNELS = {None: -1, "auto": -1, "valu": 0, "mfma": 1, "int8": 2}
-_KERNEL_NAMES = {0: "valu", 1: "mfma", 2: "int8"}
+# kvd_kernel values
+_KERNELS = {None: 0, "auto": 0, "valu": 1, "mfma": 2, "int8": 3}
+_KERNEL_NAMES = {1: "valu", 2: "mfma", 3: "int8"}
 
 
 class KvdError(ValueError):
@@ -42,12 +48,66 @@ class Shape(ctypes.Structure):
         "max_seq_len", "num_blocks", "max_blocks_per_seq")]
 
 
+class _COptions(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("tail_split_tokens", ctypes.c_int32), ("tail_span_tokens", ctypes.c_int32),
+                ("dispatch_order", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("event_start", ctypes.c_void_p), ("event_stop", ctypes.c_void_p)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Options:
+    """Per-call plan overrides and timing events (kvd_options).
+
+    kernel          None / "auto", "valu", "mfma" or "int8"
+    split_tokens    tokens per split (0 automatic; a multiple of 16 up to 8192)
+    tail_split_tokens, tail_span_tokens
+                    shorter splits over the last positions (0: none / automatic)
+    dispatch_order  None (automatic) or the unit order 0-4: 0 split fastest,
+                    1 head-sequence-split, 2 head-split-sequence, 3 device-built
+                    work list, 4 work list derived in the split kernel
+    events          None, or (start, stop) torch.cuda.Event(enable_timing=True)
+                    recorded on the call's stream around its main kernel
+    """
+    kernel: Optional[str] = None
+    split_tokens: int = 0
+    tail_split_tokens: int = 0
+    tail_span_tokens: int = 0
+    dispatch_order: Optional[int] = None
+    events: Optional[Tuple[object, object]] = None
+
+    def with_events(self, start, stop) -> "Options":
+        return dataclasses.replace(self, events=(start, stop))
+
+
+def _event_handle(ev) -> int:
+    """The hipEvent_t behind a torch.cuda.Event (torch creates it lazily on
+    its first record)."""
+    h = ev.cuda_event
+    if not h:
+        ev.record()
+        h = ev.cuda_event
+    return h
+
+
+def _options(opts: Optional[Options]):
+    if opts is None:
+        return None
+    if opts.kernel not in _KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(k for k in _KERNELS if k)}")
+    c = _COptions(_KERNELS[opts.kernel], int(opts.split_tokens), int(opts.tail_split_tokens),
+                  int(opts.tail_span_tokens),
+                  0 if opts.dispatch_order is None else int(opts.dispatch_order) + 1, 0, None, None)
+    if opts.events is not None:
+        c.event_start = _event_handle(opts.events[0])
+        c.event_stop = _event_handle(opts.events[1])
+    return ctypes.byref(c)
+
+
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
             "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
-            "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_set_tuning", "kvd_set_tuning_ex",
-            "kvd_timer_begin",
-            "kvd_timer_end", "kvd_read_probe")
+            "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe")
 
 _lib = None
 _lock = threading.Lock()
@@ -87,26 +147,19 @@ def load_library():
         lib.rope_append_kv_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P, P,
                                              ctypes.c_double, I32, P]
         lib.gqa_decode_attn_multi.restype = I32
+        OP = ctypes.POINTER(_COptions)
         lib.gqa_decode_attn_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_float,
-                                              P, P, P, ctypes.c_size_t, P]
+                                              P, P, P, ctypes.c_size_t, OP, P]
         lib.gqa_prefill_attn.restype = I32
-        lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, P]
+        lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, OP, P]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
-        lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32]
+        lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32, OP]
         lib.kvd_status_string.restype = ctypes.c_char_p
         lib.kvd_status_string.argtypes = [I32]
         lib.kvd_get_plan.restype = I32
         lib.kvd_get_plan.argtypes = [SP, I32, ctypes.POINTER(I32)]
         lib.kvd_get_plan_multi.restype = I32
-        lib.kvd_get_plan_multi.argtypes = [SP, I32, I32, ctypes.POINTER(I32)]
-        lib.kvd_set_tuning.restype = I32
-        lib.kvd_set_tuning.argtypes = [I32, I32]
-        lib.kvd_set_tuning_ex.restype = I32
-        lib.kvd_set_tuning_ex.argtypes = [I32, I32, I32, I32, I32]
-        lib.kvd_timer_begin.restype = I32
-        lib.kvd_timer_begin.argtypes = [I32]
-        lib.kvd_timer_end.restype = I32
-        lib.kvd_timer_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
+        lib.kvd_get_plan_multi.argtypes = [SP, I32, I32, OP, ctypes.POINTER(I32)]
         lib.kvd_read_probe.restype = I32
         lib.kvd_read_probe.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
         _lib = lib
@@ -228,43 +281,80 @@ def rope_append_kv(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.
     return q_rot if q is not None else None
 
 
-_ws_cache = {}
-
-
 def _workspace(dev: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    """A fresh workspace from torch's caching allocator, tied to the current
+    stream (torch's allocator aligns blocks to at least 512 bytes)."""
     if nbytes == 0:
         return None
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
-        _ws_cache[key] = ws
-    return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
 
 def workspace_size(q_rot: torch.Tensor, k_cache: torch.Tensor,
                    block_table: Optional[torch.Tensor] = None,
-                   max_seq_len: Optional[int] = None, n_query: int = 1) -> int:
+                   max_seq_len: Optional[int] = None, n_query: int = 1,
+                   options: Optional[Options] = None) -> int:
     """Workspace bytes of the decode call for q_rot [B, H, D] (n_query 1) or
-    [B, T, H, D] (n_query T)."""
+    [B, T, H, D] (n_query T) with these options."""
     lib = load_library()
     B, H = int(q_rot.shape[0]), int(q_rot.shape[-2])
     shape = make_shape(B, H, k_cache, block_table)
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    return int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), int(n_query), msl))
+    return int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), int(n_query), msl,
+                                                   _options(options)))
+
+
+def _scale_arg(scale: Optional[float]) -> float:
+    """The scale passed to the library: 0 asks it for its default 1/sqrt(D)."""
+    if scale is None:
+        return 0.0
+    if float(scale) == 0.0:
+        raise ValueError("scale must be nonzero (None selects 1/sqrt(head_dim))")
+    return float(scale)
+
+
+def _outputs(lead, H, D, dev, out, lse, want_lse):
+    if out is None:
+        out = torch.empty((*lead, H, D), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (*lead, H, D))
+    if lse is None and want_lse:
+        lse = torch.empty((*lead, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", dev, torch.float32, (*lead, H))
+    return out, lse
+
+
+def _attn_multi(shape, T, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table, msl,
+                scale, out, lse, workspace, options, dev):
+    """gqa_decode_attn_multi through the C ABI, with a per-call workspace
+    unless the caller brings one."""
+    lib = load_library()
+    opts = _options(options)
+    if workspace is None:
+        nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), T, msl, opts))
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_attn_multi(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+                                     _ptr(block_table), msl, _scale_arg(scale), _ptr(out),
+                                     _ptr(lse), _ptr(workspace), wbytes, opts, _stream(dev)))
+
 
 
 def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                     seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
                     scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None,
-                    want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                    options: Optional[Options] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """softmax(q K^T * scale) V per (b, h) over the first seq_lens[b] cached
-    tokens.  Returns (out [B, H, D] float32, lse [B, H] float32 natural log).
+    tokens (fp32 or bf16 cache).  Returns (out [B, H, D] float32, lse [B, H]
+    float32 natural log).
 
     ``max_seq_len`` is the host-side bound on seq_lens used to plan the grid
-    (default: the cache capacity)."""
+    (default: the cache capacity); ``scale`` None lets the library use
+    1/sqrt(D).  With ``options`` the call goes through gqa_decode_attn_multi
+    (one new token), which takes them."""
     lib = load_library()
     dev = k_cache.device
     B, H, D = (int(x) for x in q_rot.shape)
@@ -278,23 +368,19 @@ def gqa_decode_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
     if int(k_cache.shape[3]) != D:
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    _need(out, "out", dev, torch.float32, (B, H, D))
-    if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", dev, torch.float32, (B, H))
-    nbytes = int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+    out, lse = _outputs((B,), H, D, dev, out, lse, want_lse)
+    if options is not None:
+        _attn_multi(shape, 1, q_rot, k_cache, v_cache, None, None, seq_lens, block_table, msl,
+                    scale, out, lse, workspace, options, dev)
+        return out, lse
     if workspace is None:
-        workspace = _workspace(dev, nbytes)
+        workspace = _workspace(dev, int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl)))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gqa_decode_attn(ctypes.byref(shape), _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
-                               _ptr(seq_lens), _ptr(block_table), msl, float(scale), _ptr(out),
-                               _ptr(lse), _ptr(workspace), wbytes, _stream(dev)))
+                               _ptr(seq_lens), _ptr(block_table), msl, _scale_arg(scale),
+                               _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(dev)))
     return out, lse
+
 
 
 def v_cache_shape_int8(k_cache: torch.Tensor, paged: bool) -> Tuple[int, ...]:
@@ -354,8 +440,9 @@ def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                          block_table: Optional[torch.Tensor] = None,
                          scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None,
-                         want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                         workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                         options: Optional[Options] = None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gqa_decode_attn over an INT8 cache (layouts as rope_append_kv_int8)."""
     lib = load_library()
     dev = k_cache.device
@@ -371,24 +458,20 @@ def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     if shape.head_dim != D:
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    _need(out, "out", dev, torch.float32, (B, H, D))
-    if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", dev, torch.float32, (B, H))
-    nbytes = int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl))
+    out, lse = _outputs((B,), H, D, dev, out, lse, want_lse)
+    if options is not None:
+        _attn_multi(shape, 1, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
+                    msl, scale, out, lse, workspace, options, dev)
+        return out, lse
     if workspace is None:
-        workspace = _workspace(dev, nbytes)
+        workspace = _workspace(dev, int(lib.gqa_decode_workspace_size(ctypes.byref(shape), msl)))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gqa_decode_attn_int8(ctypes.byref(shape), _ptr(q_rot), _ptr(k_cache),
                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
-                                    _ptr(block_table), msl, float(scale), _ptr(out), _ptr(lse),
-                                    _ptr(workspace), wbytes, _stream(dev)))
+                                    _ptr(block_table), msl, _scale_arg(scale), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), wbytes, _stream(dev)))
     return out, lse
+
 
 
 def _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, paged):
@@ -450,12 +533,12 @@ def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                           v_scale: Optional[torch.Tensor] = None,
                           scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None,
-                          want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                          workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                          options: Optional[Options] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention of T new tokens per sequence, q_rot [B, T, H, D]: with
     L = seq_lens[b] (the new tokens included), query t attends the tokens
     j < L - T + 1 + t.  Returns (out [B, T, H, D], lse [B, T, H])."""
-    lib = load_library()
     dev = k_cache.device
     B, T, H, D = (int(x) for x in q_rot.shape)
     shape = make_shape(B, H, k_cache, block_table)
@@ -468,35 +551,24 @@ def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     if shape.head_dim != D:
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
-    _need(out, "out", dev, torch.float32, (B, T, H, D))
-    if lse is None and want_lse:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", dev, torch.float32, (B, T, H))
-    nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), T, msl))
-    if workspace is None:
-        workspace = _workspace(dev, nbytes)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gqa_decode_attn_multi(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache),
-                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
-                                     _ptr(block_table), msl, float(scale), _ptr(out), _ptr(lse),
-                                     _ptr(workspace), wbytes, _stream(dev)))
+    out, lse = _outputs((B, T), H, D, dev, out, lse, want_lse)
+    _attn_multi(shape, T, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table, msl,
+                scale, out, lse, workspace, options, dev)
     return out, lse
+
 
 
 def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                     want_lse: bool = True, options: Optional[Options] = None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Causal attention of T new tokens per sequence (a prompt or a chunk of
     one, already appended), q_rot [B, T, H, D], over a bf16 cache; query t
     attends the tokens j < seq_lens[b] - T + 1 + t.  q and P enter the matrix
-    cores as bf16.  Returns (out [B, T, H, D], lse [B, T, H])."""
+    cores as bf16.  ``options`` may carry timing events only.  Returns
+    (out [B, T, H, D], lse [B, T, H])."""
     lib = load_library()
     dev = k_cache.device
     B, T, H, D = (int(x) for x in q_rot.shape)
@@ -510,81 +582,38 @@ def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     if shape.head_dim != D:
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
-    _need(out, "out", dev, torch.float32, (B, T, H, D))
-    if lse is None and want_lse:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", dev, torch.float32, (B, T, H))
+    out, lse = _outputs((B, T), H, D, dev, out, lse, want_lse)
     _check(lib.gqa_prefill_attn(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
-                                _ptr(seq_lens), _ptr(block_table), msl, float(scale), _ptr(out),
-                                _ptr(lse), _stream(dev)))
+                                _ptr(seq_lens), _ptr(block_table), msl, _scale_arg(scale),
+                                _ptr(out), _ptr(lse), _options(options), _stream(dev)))
     return out, lse
-
-
-def set_tuning(kernel: Optional[str] = None, split_tokens: int = 0, tail_split_tokens: int = 0,
-               tail_span_tokens: int = -1, dispatch_order: Optional[int] = None) -> None:
-    """Process-wide override of the kernel ("valu", "mfma", "int8" or None
-    for automatic), the tokens per split (0 = automatic), the shorter splits
-    covering the last ``tail_span_tokens`` positions (0 / -1 = automatic) and
-    the MFMA dispatch order (0-4 or None for automatic)."""
-    _check(load_library().kvd_set_tuning_ex(
-        _KERNELS[kernel], int(split_tokens), int(tail_split_tokens), int(tail_span_tokens),
-        -1 if dispatch_order is None else int(dispatch_order)))
 
 
 def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,
              block_table: Optional[torch.Tensor] = None, max_seq_len: Optional[int] = None,
-             n_query: int = 1):
+             n_query: int = 1, options: Optional[Options] = None):
     """{'split_tokens', 'n_splits', 'kernel', 'workgroups'} the library would use."""
     shape = make_shape(batch, n_heads, k_cache, block_table)
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
     arr = (ctypes.c_int32 * 4)()
-    _check(load_library().kvd_get_plan_multi(ctypes.byref(shape), int(n_query), msl, arr))
+    _check(load_library().kvd_get_plan_multi(ctypes.byref(shape), int(n_query), msl,
+                                             _options(options), arr))
     return {"split_tokens": arr[0], "n_splits": arr[1],
             "kernel": _KERNEL_NAMES[arr[2]], "workgroups": arr[3]}
 
 
-def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8, chunked: bool = False,
+
+PROBE_CHUNKED, PROBE_NONTEMPORAL, PROBE_LDS = 1, 2, 4
+
+
+def read_probe(buf: torch.Tensor, n_workgroups: int, unroll: int = 8, mode: int = 0,
                sink: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Launch the streaming-read probe over all bytes of ``buf`` (measurement
-    only); returns the sink tensor."""
+    only); ``mode`` ORs PROBE_CHUNKED, PROBE_NONTEMPORAL and PROBE_LDS.
+    Returns the sink tensor."""
     if sink is None or sink.numel() < n_workgroups:
         sink = torch.empty(n_workgroups, dtype=torch.int32, device=buf.device)
     nbytes = buf.numel() * buf.element_size()
     _check(load_library().kvd_read_probe(_ptr(buf), nbytes, _ptr(sink), int(n_workgroups),
-                                         int(unroll), int(bool(chunked)), _stream(buf.device)))
+                                         int(unroll), int(mode), _stream(buf.device)))
     return sink
-
-
-class kernel_timer:
-    """Time the split-K attention kernel of the next ``n`` gqa_decode_attn
-    calls with HIP events recorded on their stream around that launch.
-
-        with kernel_timer(100) as t:
-            ...  # 100 calls
-        t.total_ms, t.count, t.mean_ms
-    """
-
-    def __init__(self, n: int):
-        self.n = int(n)
-        self.total_ms = 0.0
-        self.count = 0
-
-    def __enter__(self):
-        _check(load_library().kvd_timer_begin(self.n))
-        return self
-
-    def __exit__(self, *exc):
-        ms = ctypes.c_double(0)
-        cnt = ctypes.c_int32(0)
-        _check(load_library().kvd_timer_end(ctypes.byref(ms), ctypes.byref(cnt)))
-        self.total_ms, self.count = ms.value, cnt.value
-        return False
-
-    @property
-    def mean_ms(self) -> float:
-        return self.total_ms / self.count if self.count else float("nan")

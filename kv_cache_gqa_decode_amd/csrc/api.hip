@@ -8,8 +8,6 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <mutex>
-#include <vector>
 
 #include "kvd_internal.h"
 
@@ -20,31 +18,39 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
 
-std::atomic<int> g_kernel_override{-1};     // -1 auto, 0 VALU, 1 MFMA, 2 INT8 MFMA
-std::atomic<int> g_split_override{0};       // 0 auto
-std::atomic<int> g_tail_split_override{0};  // tokens per split near the end: 0 auto
-std::atomic<int> g_tail_span_override{-1};  // tokens covered by those splits: -1 auto
-std::atomic<int> g_order_override{-1};      // MFMA dispatch order: -1 auto
-
-struct Timer {
-  std::mutex mu;
-  std::vector<hipEvent_t> start, stop;
-  int capacity = 0;
-  int limit = 0;
-  int used = 0;
-  bool active = false;
+// Plan overrides and timing events of one call (kvd_options, resolved):
+// kernel -1 automatic, 0 VALU, 1 MFMA, 2 INT8 MFMA; order -1 automatic or a
+// grid order 0-4 (DecodeParams::grid_order).
+struct Tuning {
+  int kernel = -1;
+  int split = 0;          // tokens per split, 0 automatic
+  int tail_split = 0;     // tokens per split near the end, 0 none
+  int tail_span = -1;     // tokens covered by those splits, -1 automatic
+  int order = -1;
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_stop = nullptr;
 };
-Timer g_timer;
 
-// The next pair of timing events while kvd_timer_begin is active (else the
-// pair stays null): recorded around the one timed kernel of a call.
-void timer_slot(hipEvent_t* start, hipEvent_t* stop) {
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (g_timer.active && g_timer.used < g_timer.limit) {
-    *start = g_timer.start[g_timer.used];
-    *stop = g_timer.stop[g_timer.used];
-    ++g_timer.used;
-  }
+kvd_status read_options(const kvd_options* o, Tuning* t) {
+  *t = Tuning{};
+  if (!o) return KVD_OK;
+  if (o->kernel < KVD_KERNEL_AUTO || o->kernel > KVD_KERNEL_INT8) return KVD_EINVAL;
+  if (o->split_tokens < 0 || o->split_tokens % 16 != 0 || o->split_tokens > kMaxChunk)
+    return KVD_EINVAL;
+  if (o->tail_split_tokens < 0 || o->tail_split_tokens % 16 != 0) return KVD_EINVAL;
+  if (o->tail_span_tokens < 0) return KVD_EINVAL;
+  if (o->dispatch_order < KVD_ORDER_AUTO || o->dispatch_order > KVD_ORDER_WAVE_LIST)
+    return KVD_EINVAL;
+  if (o->reserved != 0) return KVD_EINVAL;
+  if ((o->event_start == nullptr) != (o->event_stop == nullptr)) return KVD_EINVAL;
+  t->kernel = o->kernel - 1;
+  t->split = o->split_tokens;
+  t->tail_split = o->tail_split_tokens;
+  t->tail_span = o->tail_span_tokens > 0 ? o->tail_span_tokens : -1;
+  t->order = o->dispatch_order - 1;
+  t->ev_start = static_cast<hipEvent_t>(o->event_start);
+  t->ev_stop = static_cast<hipEvent_t>(o->event_stop);
+  return KVD_OK;
 }
 
 int device_cu_count(int* cu) {
@@ -103,9 +109,9 @@ int round_up(int64_t x, int64_t m) { return static_cast<int>((x + m - 1) / m * m
 // Splits of [0, max_len): `chunk` tokens each, except that the last
 // `tail span` tokens (tuning; none by default) are cut into splits of
 // `tail` tokens, so that the units dispatched last are short.
-void set_splits(Plan* pl, int chunk, int max_len, bool tail = true) {
-  int t2 = tail ? g_tail_split_override.load() : 0;
-  int span = g_tail_span_override.load();
+void set_splits(Plan* pl, int chunk, int max_len, const Tuning& tu, bool tail = true) {
+  int t2 = tail ? tu.tail_split : 0;
+  int span = tu.tail_span;
   if (t2 <= 0 || t2 > chunk) t2 = chunk;
   if (span < 0 || t2 == chunk) span = 0;
   int n_big = span >= max_len ? 0 : (max_len - span) / chunk;
@@ -118,11 +124,12 @@ void set_splits(Plan* pl, int chunk, int max_len, bool tail = true) {
 
 // T new tokens (queries) per sequence: the matrix-core kernels take the
 // R * T query rows of a KV head as the columns of one tile.
-kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl, int T = 1) {
+kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tuning& tu,
+                     Plan* pl, int T = 1) {
   const int R = s->n_heads / s->n_kv_heads;
   if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
   const int RT = R * T;
-  int kernel = g_kernel_override.load();
+  int kernel = tu.kernel;
   if (s->kv_dtype == KVD_INT8) {
     // INT8 caches: the INT8 matrix-core kernel, up to 32 query rows per KV head
     if (RT > 32) return KVD_EUNSUPPORTED;
@@ -152,7 +159,7 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
     pl->chunk = 16; pl->n_splits = 0; pl->wgs = 0; pl->workspace = 0;
     return KVD_OK;
   }
-  int chunk = g_split_override.load();
+  int chunk = tu.split;
   if (chunk <= 0) {
     // Resident workgroups: two per CU for the MFMA kernel (also with two
     // column blocks, held to 256 registers), four for the VALU kernel, two
@@ -211,11 +218,11 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
   // the split index is a grid dimension: at most 65535 splits
   if ((max_len_host + chunk - 1) / chunk > 65535) chunk = round_up((max_len_host + 65534) / 65535, 16);
   if (chunk > round_up(max_len_host, 16)) chunk = round_up(max_len_host, 16);
-  set_splits(pl, chunk, max_len_host);
+  set_splits(pl, chunk, max_len_host, tu);
   // split is a grid dimension: at most 65535 of them
   if (pl->n_splits > 65535) {
     chunk = round_up((max_len_host + 65534) / 65535, 16);
-    set_splits(pl, chunk, max_len_host, false);
+    set_splits(pl, chunk, max_len_host, tu, false);
   }
   // Dispatch order of the matrix-core kernels.  One sequence: consecutive
   // splits of one head side by side.  Several sequences with more than one
@@ -235,7 +242,7 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
   const bool wave_list_ok = list_ok && s->batch <= 64;
   pl->grid_order = s->batch == 1 ? 0
                  : (wave_list_ok ? 4 : (list_ok ? 3 : (s->block_size != 0 ? 2 : 1)));
-  const int ord = g_order_override.load();
+  const int ord = tu.order;
   if (ord >= 0 && ord <= 2) pl->grid_order = ord;
   if (ord == 3 && list_ok) pl->grid_order = 3;   // a single split (or the VALU kernel): no list
   if (ord == 4 && wave_list_ok) pl->grid_order = 4;
@@ -259,12 +266,48 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, Plan* pl,
 
 }  // namespace
 
+
+namespace {
+
+// The softmax scale of a call: `scale`, or 1/sqrt(head_dim) when it is 0
+// (the default of "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践" §2.1,
+// d_k being the per-head dimension), times log2(e) for the exp2 the kernels use.
+float log2_scale(float scale, int head_dim) {
+  const double s = scale == 0.f ? 1.0 / std::sqrt(static_cast<double>(head_dim))
+                                 : static_cast<double>(scale);
+  return static_cast<float>(s * 1.4426950408889634);
+}
+
+// Report a plan in the C ABI's terms: plan[2] is a kvd_kernel value.
+void export_plan(const Plan& pl, int32_t* plan) {
+  plan[0] = pl.chunk;
+  plan[1] = pl.n_splits;
+  plan[2] = pl.kernel + 1;
+  plan[3] = static_cast<int32_t>(pl.wgs);
+}
+
+kvd_status plan_for(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len_host,
+                    const kvd_options* options, Plan* pl) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (n_query < 1 || n_query > 32) return KVD_EUNSUPPORTED;
+  Tuning tu;
+  st = read_options(options, &tu);
+  if (st != KVD_OK) return st;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  return make_plan(shape, max_seq_len_host, cu, tu, pl, n_query);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kvd_status_string(int32_t status) {
   switch (status) {
     case KVD_OK: return "ok";
-    case KVD_EINVAL: return "invalid argument (null pointer, inconsistent shape or aliasing)";
+    case KVD_EINVAL: return "invalid argument (null pointer, inconsistent shape, options or aliasing)";
     case KVD_EUNSUPPORTED: return "unsupported head_dim, dtype, block_size, rope style or kernel";
     case KVD_ERANGE: return "max_seq_len_host outside [0, max_seq_len]";
     case KVD_EWORKSPACE: return "workspace missing or too small";
@@ -274,59 +317,28 @@ const char* kvd_status_string(int32_t status) {
 }
 
 kvd_status kvd_get_plan(const kvd_shape* shape, int32_t max_seq_len_host, int32_t* plan) {
-  return kvd_get_plan_multi(shape, 1, max_seq_len_host, plan);
-}
-
-kvd_status kvd_set_tuning_ex(int32_t kernel, int32_t split_tokens, int32_t tail_split_tokens,
-                             int32_t tail_span_tokens, int32_t dispatch_order) {
-  if (kernel < -1 || kernel > 2) return KVD_EINVAL;
-  if (split_tokens < 0 || split_tokens % 16 != 0) return KVD_EINVAL;
-  if (tail_split_tokens < 0 || tail_split_tokens % 16 != 0) return KVD_EINVAL;
-  if (tail_span_tokens < -1 || dispatch_order < -1 || dispatch_order > 4) return KVD_EINVAL;
-  g_kernel_override.store(kernel);
-  g_split_override.store(split_tokens);
-  g_tail_split_override.store(tail_split_tokens);
-  g_tail_span_override.store(tail_span_tokens);
-  g_order_override.store(dispatch_order);
-  return KVD_OK;
-}
-
-kvd_status kvd_set_tuning(int32_t kernel, int32_t split_tokens) {
-  return kvd_set_tuning_ex(kernel, split_tokens, 0, -1, -1);
+  return kvd_get_plan_multi(shape, 1, max_seq_len_host, nullptr, plan);
 }
 
 kvd_status kvd_get_plan_multi(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len_host,
-                              int32_t* plan) {
-  kvd_status st = check_shape(shape);
-  if (st != KVD_OK) return st;
+                              const kvd_options* options, int32_t* plan) {
   if (!plan) return KVD_EINVAL;
-  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
-  if (n_query < 1 || n_query > 32) return KVD_EUNSUPPORTED;
-  int cu = 0;
-  if (device_cu_count(&cu) != 0) return KVD_EHIP;
   Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, &pl, n_query);
+  const kvd_status st = plan_for(shape, n_query, max_seq_len_host, options, &pl);
   if (st != KVD_OK) return st;
-  plan[0] = pl.chunk;
-  plan[1] = pl.n_splits;
-  plan[2] = pl.kernel;
-  plan[3] = static_cast<int32_t>(pl.wgs);
+  export_plan(pl, plan);
   return KVD_OK;
 }
 
 size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,
-                                       int32_t max_seq_len_host) {
-  if (check_shape(shape) != KVD_OK) return 0;
-  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return 0;
-  int cu = 0;
-  if (device_cu_count(&cu) != 0) return 0;
+                                       int32_t max_seq_len_host, const kvd_options* options) {
   Plan pl;
-  if (make_plan(shape, max_seq_len_host, cu, &pl, n_query) != KVD_OK) return 0;
+  if (plan_for(shape, n_query, max_seq_len_host, options, &pl) != KVD_OK) return 0;
   return pl.workspace;
 }
 
 size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_host) {
-  return gqa_decode_workspace_size_multi(shape, 1, max_seq_len_host);
+  return gqa_decode_workspace_size_multi(shape, 1, max_seq_len_host, nullptr);
 }
 
 }  // extern "C"
@@ -366,7 +378,8 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
                        const void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* seq_lens, const int32_t* block_table,
                        int32_t max_seq_len_host, float scale, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream, int32_t T = 1);
+                       void* workspace, size_t workspace_bytes, const kvd_options* options,
+                       void* stream, int32_t T = 1);
 
 }  // namespace
 
@@ -401,7 +414,8 @@ kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const voi
                            void* stream) {
   if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;
   return decode_impl(shape, q_rot, k_cache, v_cache, nullptr, nullptr, seq_lens, block_table,
-                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream);
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, nullptr,
+                     stream);
 }
 
 kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
@@ -414,7 +428,8 @@ kvd_status gqa_decode_attn_int8(const kvd_shape* shape, const float* q_rot,
   if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
   if (!k_scale || !v_scale) return KVD_EINVAL;
   return decode_impl(shape, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
-                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream);
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, nullptr,
+                     stream);
 }
 
 kvd_status rope_append_kv_multi(const kvd_shape* shape, int32_t n_query, const void* q,
@@ -436,19 +451,20 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
                                  const float* v_scale, const int32_t* seq_lens,
                                  const int32_t* block_table, int32_t max_seq_len_host,
                                  float scale, float* out, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream) {
   if (!shape) return KVD_EINVAL;
   const bool i8 = shape->kv_dtype == KVD_INT8;
   if (i8 != (k_scale != nullptr) || i8 != (v_scale != nullptr)) return KVD_EINVAL;
   return decode_impl(shape, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table,
-                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, stream,
-                     n_query);
+                     max_seq_len_host, scale, out, lse, workspace, workspace_bytes, options,
+                     stream, n_query);
 }
 
 kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
-                            float* out, float* lse, void* stream) {
+                            float* out, float* lse, const kvd_options* options, void* stream) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (shape->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
@@ -461,6 +477,12 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
   const bool paged = shape->block_size != 0;
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  Tuning tu;
+  st = read_options(options, &tu);
+  if (st != KVD_OK) return st;
+  // the prefill kernel has no split plan: only the timing events apply
+  if (tu.kernel >= 0 || tu.split != 0 || tu.tail_split != 0 || tu.tail_span >= 0 || tu.order >= 0)
+    return KVD_EINVAL;
   if (shape->batch == 0) return KVD_OK;
   DecodeParams p{};
   p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
@@ -470,13 +492,11 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
   p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
-  p.qscale = scale * 1.4426950408889634f;
+  p.qscale = log2_scale(scale, shape->head_dim);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
-  timer_slot(&ev_start, &ev_stop);
-  if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
+  if (tu.ev_start && hipEventRecord(tu.ev_start, s) != hipSuccess) return KVD_EHIP;
   if (launch_prefill_mfma(p, paged, s) != hipSuccess) return KVD_EHIP;
-  if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
+  if (tu.ev_stop && hipEventRecord(tu.ev_stop, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;
 }
 
@@ -488,7 +508,8 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
                        const void* v_cache, const float* k_scale, const float* v_scale,
                        const int32_t* seq_lens, const int32_t* block_table,
                        int32_t max_seq_len_host, float scale, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream, int32_t T) {
+                       void* workspace, size_t workspace_bytes, const kvd_options* options,
+                       void* stream, int32_t T) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
@@ -500,11 +521,14 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
   if (T < 1 || T > 32) return KVD_EUNSUPPORTED;
+  Tuning tu;
+  st = read_options(options, &tu);
+  if (st != KVD_OK) return st;
   if (shape->batch == 0) return KVD_OK;
   int cu = 0;
   if (device_cu_count(&cu) != 0) return KVD_EHIP;
   Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, &pl, T);
+  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, T);
   if (st != KVD_OK) return st;
   if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
   if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
@@ -521,7 +545,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
   p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
-  p.qscale = scale * 1.4426950408889634f;
+  p.qscale = log2_scale(scale, shape->head_dim);
   p.direct = pl.n_splits <= 1 ? 1 : 0;
   p.grid_order = pl.grid_order;
   p.units = nullptr; p.n_units = nullptr;
@@ -545,55 +569,15 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
     return launch_lse_reduce(p, s) == hipSuccess ? KVD_OK : KVD_EHIP;
   }
 
-  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
-  timer_slot(&ev_start, &ev_stop);
   if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
-  if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return KVD_EHIP;
+  if (tu.ev_start && hipEventRecord(tu.ev_start, s) != hipSuccess) return KVD_EHIP;
   const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)
                      : pl.kernel == 2 ? launch_decode_i8(p, paged, s)
                                       : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
   if (e != hipSuccess) return KVD_EHIP;
-  if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess) return KVD_EHIP;
+  if (tu.ev_stop && hipEventRecord(tu.ev_stop, s) != hipSuccess) return KVD_EHIP;
   if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;
 }
 
 }  // namespace
-
-extern "C" {
-
-kvd_status kvd_timer_begin(int32_t n_launches) {
-  if (n_launches < 1 || n_launches > 4096) return KVD_EINVAL;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  while (g_timer.capacity < n_launches) {
-    hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess) return KVD_EHIP;
-    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return KVD_EHIP; }
-    g_timer.start.push_back(a);
-    g_timer.stop.push_back(b);
-    ++g_timer.capacity;
-  }
-  g_timer.used = 0;
-  g_timer.limit = n_launches;
-  g_timer.active = true;
-  return KVD_OK;
-}
-
-kvd_status kvd_timer_end(double* total_ms, int32_t* n_timed) {
-  if (!total_ms || !n_timed) return KVD_EINVAL;
-  std::lock_guard<std::mutex> lk(g_timer.mu);
-  double sum = 0.0;
-  for (int i = 0; i < g_timer.used; ++i) {
-    if (hipEventSynchronize(g_timer.stop[i]) != hipSuccess) return KVD_EHIP;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess) return KVD_EHIP;
-    sum += ms;
-  }
-  *total_ms = sum;
-  *n_timed = g_timer.used;
-  g_timer.active = false;
-  g_timer.used = 0;
-  return KVD_OK;
-}
-
-}  // extern "C"

@@ -8,6 +8,7 @@
 #include <type_traits>
 
 #include "kvd_internal.h"
+#include "uniform_join.h"
 
 namespace kvd {
 namespace mt {
@@ -51,13 +52,12 @@ __device__ __forceinline__ void vmem_wait() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// A 64-bit value made wave-uniform (readfirstlane of both halves).  The
-// builtin returns a signed int: each half goes back through uint32_t so the
-// low half is zero-extended, not sign-extended, when the halves are joined.
+// A 64-bit value made wave-uniform (readfirstlane of both halves, joined
+// without sign-extending the low half: uniform_join.h).
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  return join_uniform_halves(v, [](uint32_t x) {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(x));
+  });
 }
 
 // Raw buffer descriptor over `bytes` bytes from `base` (stride 0: byte

@@ -31,21 +31,31 @@ def upload(p: W.Problem, dev):
     return t
 
 
-def gpu_step(t, s: W.Spec, max_len: int, style="interleaved", scale=None, sync=True):
+def opts(kernel=None, split=0, tail=(0, -1), order=None, events=None):
+    """Per-call options of the attention calls (None when all automatic)."""
+    if kernel is None and split == 0 and tail[0] == 0 and order is None and events is None:
+        return None
+    return kvd.Options(kernel=kernel, split_tokens=split, tail_split_tokens=tail[0],
+                       tail_span_tokens=max(tail[1], 0), dispatch_order=order, events=events)
+
+
+def gpu_step(t, s: W.Spec, max_len: int, style="interleaved", scale=None, sync=True,
+             options=None):
     if s.dtype == "i8":
         q_rot = kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"],
                                         t["v_cache"], t["k_scale"], t["v_scale"], t["positions"],
                                         t["block_table"], base=s.rope_base, style=style)
         out, lse = kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
                                             t["v_scale"], t["seq_lens"], t["block_table"],
-                                            scale=scale, max_seq_len=max_len)
+                                            scale=scale, max_seq_len=max_len, options=options)
         if sync:
             torch.cuda.synchronize()
         return q_rot, out, lse
     q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                t["positions"], t["block_table"], base=s.rope_base, style=style)
     out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
-                                   t["block_table"], scale=scale, max_seq_len=max_len)
+                                   t["block_table"], scale=scale, max_seq_len=max_len,
+                                   options=options)
     if sync:
         torch.cuda.synchronize()
     return q_rot, out, lse
@@ -70,13 +80,16 @@ def oracle_step(p: W.Problem, style="interleaved", units=None, scale=None):
 
 
 def appended_rows(p: W.Problem):
-    """Index tuples of the B * G appended (row, head) slots in the cache array."""
+    """Index tuples (leading two indices) of the appended token rows in the
+    bf16 / fp32 cache arrays: (b, position) when contiguous, (block, row in
+    block) in a paged pool of p.spec.block_size-token blocks."""
     s = p.spec
     rows = []
     for b in range(s.batch):
         pos = int(p.positions[b])
         if s.block_size:
-            rows.append((int(p.block_table[b, pos // 16]), pos % 16))
+            bs = s.block_size
+            rows.append((int(p.block_table[b, pos // bs]), pos % bs))
         else:
             rows.append((b, pos))
     return rows

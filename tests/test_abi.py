@@ -144,10 +144,11 @@ def rope_m(lib, sh, T, ks=None, vs=None):
                                     10000.0, 0, None)
 
 
-def attn_m(lib, sh, T, ks=None, vs=None, msl=32):
+def attn_m(lib, sh, T, ks=None, vs=None, msl=32, opts=None, scale=0.125):
     return lib.gqa_decode_attn_multi(ctypes.byref(sh) if sh is not None else None, T, FAKE, FAKE,
-                                     FAKE, ks, vs, FAKE, None, msl, 0.125,
-                                     ctypes.c_void_p(0x2000), None, None, 0, None)
+                                     FAKE, ks, vs, FAKE, None, msl, scale,
+                                     ctypes.c_void_p(0x2000), None, None, 0,
+                                     None if opts is None else ctypes.byref(opts), None)
 
 
 def test_multi_calls_validate(lib):
@@ -165,12 +166,14 @@ def test_multi_calls_validate(lib):
     assert rope_m(lib, shape(batch=0), 5) == OK
     assert attn_m(lib, shape(batch=0), 5) == OK
     assert attn_m(lib, shape(kv_dtype=2, batch=0), 5, ks=FAKE, vs=FAKE) == OK
-    assert lib.gqa_decode_workspace_size_multi(ctypes.byref(bf), 0, 10) == 0
+    assert lib.gqa_decode_workspace_size_multi(ctypes.byref(bf), 0, 10, None) == 0
 
 
-def prefill(lib, sh, T, q=FAKE, lens=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000)):
+def prefill(lib, sh, T, q=FAKE, lens=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000),
+            opts=None):
     return lib.gqa_prefill_attn(ctypes.byref(sh) if sh is not None else None, T, q, FAKE, FAKE,
-                                lens, table, msl, 0.125, out, None, None)
+                                lens, table, msl, 0.125, out, None,
+                                None if opts is None else ctypes.byref(opts), None)
 
 
 def test_prefill_validates(lib):
@@ -185,22 +188,44 @@ def test_prefill_validates(lib):
     assert prefill(lib, shape(), 4, table=FAKE) == EINVAL
     assert prefill(lib, shape(), 4, msl=65) == ERANGE
     assert prefill(lib, shape(batch=0), 64) == OK
+    # options: timing events only (both or neither); no plan fields
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions()) == OK
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(split_tokens=64)) == EINVAL
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(kernel=2)) == EINVAL
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(event_start=0x10)) == EINVAL
 
 
-def test_tuning_and_timer_validation(lib):
-    assert lib.kvd_set_tuning(-2, 0) == EINVAL
-    assert lib.kvd_set_tuning(3, 0) == EINVAL
-    assert lib.kvd_set_tuning(0, 24) == EINVAL           # not a multiple of 16
-    assert lib.kvd_set_tuning(0, -16) == EINVAL
-    assert lib.kvd_set_tuning(-1, 0) == OK
-    # dispatch orders 0-4 (4: the work list derived inside the split kernel)
-    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, 5) == EINVAL
-    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, -2) == EINVAL
-    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, 4) == OK
-    assert lib.kvd_set_tuning_ex(-1, 0, 0, -1, -1) == OK
-    assert lib.kvd_timer_begin(0) == EINVAL
-    assert lib.kvd_timer_begin(5000) == EINVAL
-    assert lib.kvd_timer_end(None, None) == EINVAL
+def test_options_validation(lib):
+    """kvd_options travel with the call; bad values are refused before any
+    HIP call (batch 0: a valid call does nothing)."""
+    O = B._COptions
+    empty = shape(batch=0)
+    assert attn_m(lib, empty, 1, opts=O()) == OK                       # zeros: automatic
+    for bad in (O(kernel=-1), O(kernel=4), O(split_tokens=24), O(split_tokens=-16),
+                O(split_tokens=8192 + 16), O(tail_split_tokens=8), O(tail_span_tokens=-1),
+                O(dispatch_order=-1), O(dispatch_order=6), O(reserved=1),
+                O(event_start=0x10), O(event_stop=0x10)):
+        assert attn_m(lib, empty, 1, opts=bad) == EINVAL
+        assert lib.gqa_decode_workspace_size_multi(ctypes.byref(shape()), 1, 32,
+                                                   ctypes.byref(bad)) == 0
+    for good in (O(kernel=1), O(kernel=2, split_tokens=8192), O(split_tokens=16),
+                 O(dispatch_order=5), O(tail_split_tokens=32, tail_span_tokens=64)):
+        assert attn_m(lib, empty, 1, opts=good) == OK
+    plan = (ctypes.c_int32 * 4)()
+    assert lib.kvd_get_plan_multi(ctypes.byref(shape()), 1, 32, ctypes.byref(O(kernel=9)),
+                                  plan) == EINVAL
+
+
+def test_scale_zero_selects_the_default(lib):
+    """0 asks the library for 1/sqrt(head_dim); infinities and NaN are refused."""
+    empty = shape(batch=0)
+    assert attn_m(lib, empty, 1, scale=0.0) == OK
+    assert attn(lib, empty, scale=0.0) == OK
+    assert attn_m(lib, shape(), 1, scale=float("inf")) == EINVAL
+    assert attn_m(lib, shape(), 1, scale=float("-inf")) == EINVAL
+
+
+def test_plan_validation(lib):
     plan = (ctypes.c_int32 * 4)()
     assert lib.kvd_get_plan(None, 0, plan) == EINVAL
     assert lib.kvd_get_plan(ctypes.byref(shape()), 100, plan) == ERANGE
@@ -214,6 +239,19 @@ def test_binding_raises_without_compute(lib):
         B._dtype_code(torch.float16)
     with pytest.raises(ValueError):
         B.make_shape(2, 8, torch.zeros((2, 64, 2)), None)
-    with pytest.raises(KeyError):
-        B.set_tuning("triton")
+    with pytest.raises(ValueError):
+        B._options(B.Options(kernel="triton"))
+    with pytest.raises(ValueError):
+        B._scale_arg(0.0)
+    assert B._scale_arg(None) == 0.0
     assert cpu.shape == (2, 8, 64)
+
+
+def test_read_probe_validates(lib):
+    sink = ctypes.c_void_p(0x2000)
+    assert lib.kvd_read_probe(FAKE, 4096, sink, 4, 8, 8, None) == EINVAL        # unknown mode bit
+    assert lib.kvd_read_probe(FAKE, 4096 + 16, sink, 4, 8, 4, None) == EINVAL   # LDS: whole KiB
+    assert lib.kvd_read_probe(FAKE, 4100, sink, 4, 8, 0, None) == EINVAL        # 16-byte words
+    assert lib.kvd_read_probe(FAKE, 4096, sink, 4, 3, 0, None) == EUNSUPPORTED  # unroll
+    assert lib.kvd_read_probe(ctypes.c_void_p(0x1008), 4096, sink, 4, 8, 0, None) == EINVAL
+    assert lib.kvd_read_probe(FAKE, 4096, sink, 0, 8, 0, None) == EINVAL

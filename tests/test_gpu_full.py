@@ -1,15 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark uses (automatic plan).
 
-The oracle recomputes sampled (b, h) rows one by one; every appended cache
-row is compared bit for bit, and the rest of each cache is checked unchanged
-on the device against the host copy.
+Every (b, h) output row and its lse are compared with the oracle, which
+computes the whole batch (fp64, all host threads); every appended cache row
+is compared bit for bit, and the rest of each cache is checked unchanged on
+the device against the host copy.
 """
 import numpy as np
 import pytest
 import torch
 
-import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
 from tests.gpu_helpers import appended_rows, bits, device, gpu_step, oracle_step, upload
@@ -17,28 +17,16 @@ from tests.gpu_helpers import appended_rows, bits, device, gpu_step, oracle_step
 pytestmark = pytest.mark.gpu
 
 
-def sample_units(s: W.Spec, n: int, seed: int):
-    rng = np.random.default_rng(seed)
-    units = {(0, 0), (s.batch - 1, s.n_heads - 1)}
-    while len(units) < min(n, s.batch * s.n_heads):
-        units.add((int(rng.integers(s.batch)), int(rng.integers(s.n_heads))))
-    return sorted(units)
-
-
-def run_full(s: W.Spec, n_units: int):
+def run_full(s: W.Spec):
     dev = device()
-    kvd.set_tuning(None, 0)
     p = W.make_problem(s)
     print(f"[full] {s.name} G={s.n_kv_heads} B={s.batch} max_len={p.max_len}", flush=True)
     t = upload(p, dev)
     q_rot, out, lse = gpu_step(t, s, p.max_len)
-    units = sample_units(s, n_units, seed=s.cfg_id)
-    oq, oo, ol, okc, ovc = oracle_step(p, units=units)
-    ub = [u[0] for u in units]
-    uh = [u[1] for u in units]
-    got = out.cpu().numpy()[ub, uh]
-    gates.assert_out(got, oo, s.dtype, f"{s.name} sampled")
-    gates.assert_lse(lse.cpu().numpy()[ub, uh], ol, s.dtype, f"{s.name} sampled lse")
+    oq, oo, ol, okc, ovc = oracle_step(p)
+    e = gates.assert_out(out.cpu().numpy(), oo, s.dtype, f"{s.name} all rows")
+    gates.assert_lse(lse.cpu().numpy(), ol, s.dtype, f"{s.name} all rows lse")
+    print(f"[full] {s.name} G={s.n_kv_heads}: {e}", flush=True)
     # appended rows, bit for bit
     kc = t["k_cache"]
     vc = t["v_cache"]
@@ -56,18 +44,19 @@ def run_full(s: W.Spec, n_units: int):
 
 
 def test_c3_batched_varlen_full():
-    run_full(W.spec("c3"), 48)
+    run_full(W.spec("c3"))
 
 
 def test_c4_paged_full():
-    run_full(W.spec("c4"), 32)
+    run_full(W.spec("c4"))
 
 
 @pytest.mark.parametrize("G", [32, 8, 1])
 def test_c5_long_context_full(G):
-    run_full(W.spec("c5", n_kv_heads=G), 12)
+    run_full(W.spec("c5", n_kv_heads=G))
 
 
-@pytest.mark.parametrize("q_gain", [32.0])
-def test_c5_gqa_peaked(q_gain):
-    run_full(W.spec("c5", n_kv_heads=8, q_gain=q_gain), 8)
+@pytest.mark.parametrize("G", [8, 1])
+def test_c5_peaked(G):
+    """q x 32: score spread ~2.8, so the running max moves and rescales."""
+    run_full(W.spec("c5", n_kv_heads=G, q_gain=32.0))

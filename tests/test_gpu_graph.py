@@ -46,7 +46,6 @@ def _step_fn(t, s, max_len, bufs):
                                         ("c4", "bf16")])
 def test_graph_replays_equal_eager(name, dtype):
     dev = device()
-    kvd.set_tuning(None, 0)
     if name == "c2":
         s = W.spec("c2")
     elif name == "c3":

@@ -5,8 +5,7 @@ seeded codes and scales.
 The stored codes must be bit-exact (both sides quantise the exact rotated
 key and v_new with an fp64 quotient, ties to even); outputs pass the bf16
 gates (both sides dequantise the same codes, so only arithmetic differs).
-Small cases compare every element; the full workload sizes compare sampled
-(b, h) rows plus both caches in full.
+Every case compares every output row and lse, and both caches in full.
 """
 import numpy as np
 import pytest
@@ -15,20 +14,12 @@ import torch
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import device, gpu_step, oracle_step, upload
-from tests.test_gpu_full import sample_units
+from tests.gpu_helpers import device, gpu_step, opts, oracle_step, upload
 from tests.test_gpu_parity import shared_prefix
 
 pytestmark = pytest.mark.gpu
 
 RAGGED = np.array([1, 2, 15, 16, 17, 63, 64, 65, 300, 1000, 1023, 1024], np.int32)
-
-
-@pytest.fixture(autouse=True)
-def _reset_tuning():
-    kvd.set_tuning(None, 0)
-    yield
-    kvd.set_tuning(None, 0)
 
 
 def i8(name, **kw):
@@ -38,9 +29,9 @@ def i8(name, **kw):
 def check_full(p: W.Problem, split=0, style="interleaved", what="", tail=(0, -1), order=None):
     dev = device()
     s = p.spec
-    kvd.set_tuning(None, split, tail[0], tail[1], order)
     t = upload(p, dev)
-    q_rot, out, lse = gpu_step(t, s, p.max_len, style=style)
+    q_rot, out, lse = gpu_step(t, s, p.max_len, style=style,
+                               options=opts(None, split, tail, order))
     oq, oo, ol, okc, ovc = oracle_step(p, style=style)
     assert np.array_equal(W.from_torch(t["k_cache"]), okc), f"{what}: K codes differ"
     assert np.array_equal(W.from_torch(t["v_cache"]), ovc), f"{what}: V codes differ"
@@ -102,7 +93,6 @@ def test_gqa_ratios(D, n_rep):
 @pytest.mark.parametrize("block_size", [16, 32])
 def test_paged_equals_contiguous_bitwise(split, block_size):
     dev = device()
-    kvd.set_tuning(None, split)
     L = np.array([5, 16, 333, 1024, 700], np.int32)
     sp = i8("c4", batch=5, num_blocks=8000 // block_size, max_blocks_per_seq=1024 // block_size,
             block_size=block_size)
@@ -111,9 +101,29 @@ def test_paged_equals_contiguous_bitwise(split, block_size):
     for s in (sp, sc):
         p = W.make_problem(s, lengths=L)
         t = upload(p, dev)
-        res.append([x.cpu() for x in gpu_step(t, s, 1024)])
+        res.append([x.cpu() for x in gpu_step(t, s, 1024, options=opts(None, split))])
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("split", [6144, 8192])
+def test_paged_long_splits(block_size, split):
+    """Splits above 4096 tokens (the block ids of a wave in a second register)."""
+    L = np.array([8192, 7001, 6150, 4097, 300], np.int32)
+    s = i8("c4", batch=L.size, num_blocks=48000 // block_size,
+           max_blocks_per_seq=8192 // block_size, block_size=block_size, q_gain=8.0)
+    check_full(W.make_problem(s, lengths=L), split=split,
+               what=f"int8 paged{block_size} split={split}")
+
+
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("split", [0, 64])
+def test_block_ids_outside_the_pool(block_size, split):
+    from tests.test_gpu_parity import run_bad_table
+    s = i8("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+           max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
+    run_bad_table(W.make_problem(s, lengths=RAGGED), opts(None, split))
 
 
 def test_split_counts_agree():
@@ -166,28 +176,23 @@ def test_plan_reports_the_int8_kernel():
     k = torch.empty((4, 4, 8, 16, 128), dtype=torch.int8, device=dev)    # [B, S/16, G, 16, D]
     assert kvd.get_plan(4, 32, k)["kernel"] == "int8"
     with pytest.raises(kvd.KvdError):
-        kvd.set_tuning("mfma", 0)
-        kvd.get_plan(4, 32, k)
-    kvd.set_tuning(None, 0)
+        kvd.get_plan(4, 32, k, options=kvd.Options(kernel="mfma"))
     with pytest.raises(kvd.KvdError):
         kvd.get_plan(1, 64, torch.empty((1, 4, 1, 16, 128), dtype=torch.int8, device=dev))  # n_rep 64
 
 
 # ------------------------------------------------------------- full sizes
 
-def run_full_i8(s: W.Spec, n_units: int):
+def run_full_i8(s: W.Spec):
     dev = device()
-    kvd.set_tuning(None, 0)
     p = W.make_problem(s)
     print(f"[full int8] {s.name} G={s.n_kv_heads} B={s.batch} max_len={p.max_len}", flush=True)
     t = upload(p, dev)
     q_rot, out, lse = gpu_step(t, s, p.max_len)
-    units = sample_units(s, n_units, seed=s.cfg_id)
-    oq, oo, ol, okc, ovc = oracle_step(p, units=units)
-    ub = [u[0] for u in units]
-    uh = [u[1] for u in units]
-    gates.assert_out(out.cpu().numpy()[ub, uh], oo, "i8", f"int8 {s.name} sampled")
-    gates.assert_lse(lse.cpu().numpy()[ub, uh], ol, "i8", f"int8 {s.name} sampled lse")
+    oq, oo, ol, okc, ovc = oracle_step(p)
+    e = gates.assert_out(out.cpu().numpy(), oo, "i8", f"int8 {s.name} all rows")
+    gates.assert_lse(lse.cpu().numpy(), ol, "i8", f"int8 {s.name} all rows lse")
+    print(f"[full int8] {s.name} G={s.n_kv_heads}: {e}", flush=True)
     # both caches in full (the appended codes and everything else unchanged)
     assert torch.equal(t["k_cache"], torch.from_numpy(okc).to(dev))
     assert torch.equal(t["v_cache"], torch.from_numpy(ovc).to(dev))
@@ -196,13 +201,13 @@ def run_full_i8(s: W.Spec, n_units: int):
 
 
 def test_c3_int8_full():
-    run_full_i8(i8("c3"), 48)
+    run_full_i8(i8("c3"))
 
 
 def test_c4_int8_full():
-    run_full_i8(i8("c4"), 32)
+    run_full_i8(i8("c4"))
 
 
 @pytest.mark.parametrize("G", [32, 8, 1])
 def test_c5_int8_full(G):
-    run_full_i8(i8("c5", n_kv_heads=G), 12)
+    run_full_i8(i8("c5", n_kv_heads=G))

@@ -16,16 +16,9 @@ import torch
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import (appended_rows, bits, device, gpu_step, oracle_step, upload)
+from tests.gpu_helpers import (appended_rows, bits, device, gpu_step, opts, oracle_step, upload)
 
 pytestmark = pytest.mark.gpu
-
-
-@pytest.fixture(autouse=True)
-def _reset_tuning():
-    kvd.set_tuning(None, 0)
-    yield
-    kvd.set_tuning(None, 0)
 
 
 def check_full(p: W.Problem, kernel=None, split=0, style="interleaved", what="", tail=(0, -1),
@@ -33,9 +26,9 @@ def check_full(p: W.Problem, kernel=None, split=0, style="interleaved", what="",
     """Every output element and every cache element against the oracle."""
     dev = device()
     s = p.spec
-    kvd.set_tuning(kernel, split, tail[0], tail[1], order)
     t = upload(p, dev)
-    q_rot, out, lse = gpu_step(t, s, p.max_len, style=style)
+    q_rot, out, lse = gpu_step(t, s, p.max_len, style=style,
+                               options=opts(kernel, split, tail, order))
     oq, oo, ol, okc, ovc = oracle_step(p, style=style)
     kc, vc = W.from_torch(t["k_cache"]), W.from_torch(t["v_cache"])
     assert np.array_equal(bits(kc), bits(okc)), f"{what}: K cache differs from the oracle's"
@@ -119,8 +112,7 @@ def test_auto_plan_picks_matrix_cores_for_bf16():
     k32 = torch.empty((4, 64, 8, 128), dtype=torch.float32, device=dev)
     assert kvd.get_plan(4, 32, k32)["kernel"] == "valu"
     with pytest.raises(kvd.KvdError):
-        kvd.set_tuning("mfma", 0)
-        kvd.get_plan(4, 32, k32)
+        kvd.get_plan(4, 32, k32, options=kvd.Options(kernel="mfma"))
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
@@ -129,7 +121,6 @@ def test_auto_plan_picks_matrix_cores_for_bf16():
 def test_paged_equals_contiguous_bitwise(kernel, split, block_size):
     """The same logical cache, paged or contiguous, gives identical bits."""
     dev = device()
-    kvd.set_tuning(kernel, split)
     L = np.array([5, 16, 333, 1024, 700], np.int32)
     sp = W.spec("c4", batch=5, num_blocks=8000 // block_size, max_blocks_per_seq=1024 // block_size,
                 block_size=block_size)
@@ -138,7 +129,7 @@ def test_paged_equals_contiguous_bitwise(kernel, split, block_size):
     for s in (sp, sc):
         p = W.make_problem(s, lengths=L)
         t = upload(p, dev)
-        q_rot, out, lse = gpu_step(t, s, 1024)
+        q_rot, out, lse = gpu_step(t, s, 1024, options=opts(kernel, split))
         res.append((q_rot.cpu(), out.cpu(), lse.cpu()))
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
@@ -205,15 +196,16 @@ def test_workspace_too_small_is_reported():
     s = W.spec("c3", batch=2, max_seq_len=2048)
     p = W.make_problem(s, lengths=np.array([2048, 100], np.int32))
     t = upload(p, dev)
-    kvd.set_tuning(None, 64)
+    o = kvd.Options(split_tokens=64)
     q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                t["positions"])
-    need = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=2048)
-    assert need > 0
+    need = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=2048, options=o)
+    assert need > kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=2048,
+                                     options=kvd.Options(split_tokens=1024)) > 0
     small = torch.empty(need - 256, dtype=torch.uint8, device=dev)
     with pytest.raises(kvd.KvdError) as ei:
         kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], max_seq_len=2048,
-                            workspace=small)
+                            workspace=small, options=o)
     assert ei.value.status == 4
 
 
@@ -269,12 +261,12 @@ def test_empty_sequences_with_several_splits(kernel, order):
     dev = device()
     s = W.spec("c3", batch=5, max_seq_len=1024, q_gain=8.0)
     p = W.make_problem(s, lengths=np.array([1, 300, 1, 1024, 17], np.int32))
-    kvd.set_tuning(kernel, 64, 0, -1, order)
     t = upload(p, dev)
     q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                t["positions"])
     lens = torch.tensor([0, 300, 0, 1024, 17], dtype=torch.int32, device=dev)
-    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens, max_seq_len=1024)
+    out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens, max_seq_len=1024,
+                                   options=opts(kernel, 64, order=order))
     torch.cuda.synchronize()
     assert (out[0] == 0).all() and (out[2] == 0).all()
     assert torch.isinf(lse[0]).all() and torch.isinf(lse[2]).all()
@@ -313,16 +305,16 @@ def test_work_list_derived_in_kernel(dtype, batch):
     lens_t = torch.tensor(run_lens, dtype=torch.int32, device=dev)
     results = []
     for order in (3, 4):
-        kvd.set_tuning(None, 128, 0, -1, order)
-        nbytes = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=1024)
+        o = kvd.Options(split_tokens=128, dispatch_order=order)
+        nbytes = kvd.workspace_size(q_rot, t["k_cache"], max_seq_len=1024, options=o)
         ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev)
         if dtype == "i8":
             out, lse = kvd.gqa_decode_attn_int8(q_rot, t["k_cache"], t["v_cache"], t["k_scale"],
                                                 t["v_scale"], lens_t, max_seq_len=1024,
-                                                workspace=ws)
+                                                workspace=ws, options=o)
         else:
             out, lse = kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], lens_t,
-                                           max_seq_len=1024, workspace=ws)
+                                           max_seq_len=1024, workspace=ws, options=o)
         torch.cuda.synchronize()
         results.append((out.clone(), lse.clone()))
     assert torch.equal(results[0][0], results[1][0]), "orders 3 and 4 differ"
@@ -334,3 +326,117 @@ def test_work_list_derived_in_kernel(dtype, batch):
     keep = np.flatnonzero(run_lens > 0)
     gates.assert_out(out[keep], oo[keep], dtype, f"work list order 4, B={batch}")
     gates.assert_lse(lse[keep], ol[keep], dtype, f"work list order 4, B={batch}")
+
+
+# --------------------------- reachable paths: long splits, bad table entries
+
+LONG = np.array([8192, 7001, 6150, 4097, 300], np.int32)
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("split", [6144, 8192])
+def test_paged_long_splits(kernel, block_size, split):
+    """Splits above 4096 tokens: a wave of the matrix-core kernel then holds
+    the ids of the blocks it visits in a second register."""
+    s = W.spec("c4", batch=LONG.size, num_blocks=48000 // block_size,
+               max_blocks_per_seq=8192 // block_size, block_size=block_size, q_gain=8.0)
+    p = W.make_problem(s, lengths=LONG)
+    check_full(p, kernel=kernel, split=split, what=f"paged{block_size} {kernel} split={split}")
+
+
+def bad_table(p: W.Problem):
+    """The problem's table with entries outside the pool: two inside the
+    history of sequence 9, the appended block of sequences 10 and 4 (their
+    appends must be skipped) and the first block of sequence 10.  Returns
+    (table, the sequences left intact)."""
+    s = p.spec
+    bs = s.block_size
+    t = p.block_table.copy()
+    t[9, 5] = -1
+    t[9, 20] = s.num_blocks + 7
+    for b, v in ((10, -5), (4, s.num_blocks)):
+        t[b, int(p.positions[b]) // bs] = v
+    t[10, 0] = 2 ** 31 - 1
+    intact = [b for b in range(s.batch) if b not in (4, 9, 10)]
+    return t, intact
+
+
+def run_bad_table(p: W.Problem, options):
+    """GPU step on a table with out-of-pool entries: the intact sequences
+    equal the oracle, every output is finite or (no valid token) 0 / -inf,
+    and the caches equal the oracle's after appending only the intact
+    sequences (no write through a bad id)."""
+    dev = device()
+    s = p.spec
+    table, intact = bad_table(p)
+    t = upload(p, dev)
+    t["block_table"] = W.as_torch(table, dev)
+    q_rot, out, lse = gpu_step(t, s, p.max_len, options=options)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(out).all()
+    assert not np.isnan(lse).any()
+    sub = dataclasses.replace(
+        p, spec=s.replace(batch=len(intact)), q=p.q[intact], k_new=p.k_new[intact],
+        v_new=p.v_new[intact], positions=p.positions[intact], seq_lens=p.seq_lens[intact],
+        block_table=p.block_table[intact])
+    _, oo, ol, okc, ovc = oracle_step(sub)
+    gates.assert_out(out[intact], oo, s.dtype, "intact sequences")
+    gates.assert_lse(lse[intact], ol, s.dtype, "intact sequences")
+    assert np.array_equal(bits(W.from_torch(t["k_cache"])), bits(okc)), "K pool written"
+    assert np.array_equal(bits(W.from_torch(t["v_cache"])), bits(ovc)), "V pool written"
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("split", [0, 48])
+def test_block_ids_outside_the_pool(kernel, block_size, split):
+    s = W.spec("c4", batch=RAGGED.size, num_blocks=16000 // block_size,
+               max_blocks_per_seq=1024 // block_size, block_size=block_size, q_gain=8.0)
+    run_bad_table(W.make_problem(s, lengths=RAGGED), opts(kernel, split))
+
+
+# ------------------------------------------------- streams and timing events
+
+def test_two_streams_concurrently():
+    """Two decode steps enqueued on two streams at once, each with the
+    workspace the binding allocates per call on its stream: both equal the
+    oracle (a workspace shared across streams would mix their partials)."""
+    dev = device()
+    probs = []
+    for i, (B, L) in enumerate([(16, 4096), (24, 2048)]):
+        s = W.spec("c3", batch=B, max_seq_len=L, len_lo=L // 4, len_hi=L, q_gain=8.0)
+        s = s.replace(cfg_id=s.cfg_id + 100 * (i + 1))
+        p = W.make_problem(s)
+        probs.append((s, p, upload(p, dev)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    res = [None, None]
+    for _ in range(4):
+        for i, ((s, p, t), st) in enumerate(zip(probs, streams)):
+            st.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(st):
+                res[i] = gpu_step(t, s, p.max_len, sync=False)
+    torch.cuda.synchronize()
+    for (s, p, t), (q_rot, out, lse) in zip(probs, res):
+        _, oo, ol, _, _ = oracle_step(p)
+        gates.assert_out(out.cpu().numpy(), oo, s.dtype, f"stream B={s.batch}")
+        gates.assert_lse(lse.cpu().numpy(), ol, s.dtype, f"stream B={s.batch}")
+
+
+def test_option_events_bracket_the_split_kernel():
+    """Events passed in the options are recorded around the split kernel:
+    their interval is positive and inside the whole call's."""
+    dev = device()
+    s = W.spec("c3", batch=8, max_seq_len=4096, len_lo=2048, len_hi=4096)
+    p = W.make_problem(s)
+    t = upload(p, dev)
+    q_rot = gpu_step(t, s, p.max_len)[0]
+    e0, e1, a, b = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    a.record()
+    kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], max_seq_len=p.max_len,
+                        options=kvd.Options(events=(e0, e1)))
+    b.record()
+    torch.cuda.synchronize()
+    k_ms, all_ms = e0.elapsed_time(e1), a.elapsed_time(b)
+    assert 0 < k_ms <= all_ms

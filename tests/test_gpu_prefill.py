@@ -7,8 +7,9 @@ prompt is the same window after a cached history.  Query t attends the
 tokens j < L_b - T + 1 + t ([KVGR] §5.1 b.v inside the window; the tiled
 attention of [KVGR] §4.2).  The caches must match bit for bit; outputs and
 lse pass the prefill gates (bf16 q and probabilities on the matrix cores:
-max abs <= 1e-2, normwise <= 1e-2, lse <= 5e-3 relative).  Small cases
-compare every element; long prompts compare sampled (b, t, h) rows.
+max abs <= 1e-2, normwise <= 1e-2, lse <= 5e-3 relative).  Every case up to
+a 2048-token prompt compares every element; the 8192-token prompt compares
+4096 sampled (b, t, h) rows (the oracle takes each row's causal bound).
 """
 import numpy as np
 import pytest
@@ -145,13 +146,24 @@ def test_zero_and_short_lengths():
     assert np.isfinite(l[1, 6:]).all() and np.isfinite(o[2]).all()
 
 
+def test_prompt_2048_every_row():
+    """A 2048-token prompt at the 128K workload's head shape (H 32, G 8,
+    D 128): every output row and lse against the oracle, caches in full."""
+    T = 2048
+    s = W.spec("c5", max_seq_len=T, q_gain=2.0)
+    p = W.make_window(s, T, lengths=np.array([T], np.int32))
+    check_prefill(p, what="prompt 2048, all rows")
+
+
 def test_long_prompt_sampled():
-    """An 8192-token prompt at the 128K workload's head shape (H 32, G 8,
-    D 128): sampled rows against the oracle, caches in full."""
+    """An 8192-token prompt at the same head shape: 4096 sampled rows (the
+    first and last tokens of every 128-row query tile among them) against the
+    oracle, caches in full."""
     T = 8192
     s = W.spec("c5", max_seq_len=T, q_gain=2.0)
     p = W.make_window(s, T, lengths=np.array([T], np.int32))
     rng = np.random.default_rng(71)
-    ts = np.r_[0, 1, 31, 32, 127, 128, T - 1, rng.integers(0, T, 25)]
+    edges = np.r_[np.arange(0, T, 128), np.arange(127, T, 128)]
+    ts = np.r_[edges, rng.integers(0, T, 4096 - edges.size)]
     units = [(0, int(t), int(h)) for t, h in zip(ts, rng.integers(0, s.n_heads, ts.size))]
-    check_prefill(p, units=units, what="prompt 8192")
+    check_prefill(p, units=units, what="prompt 8192, 4096 rows")
