@@ -7,13 +7,15 @@ in HBM.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
 decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
 
 Timing protocol: before every timed step (and every warm-up step) a 1 GiB
-scratch buffer is written, outside the event bracket, so that no K/V byte
-is left in the 256 MB last-level cache (MALL) or the L2s: every step reads
-its cache cold from HBM, as a decode step of one layer does in a model.
+scratch buffer is streamed through the caches, outside the event bracket,
+so that no K/V byte is left in the 256 MB last-level cache (MALL) or the
+L2s: every step reads its cache cold from HBM, as a decode step of one
+layer does in a model (--flush write fills the buffer instead).
 Each step is bracketed by its own pair of events; the line reports p10 /
 p50 / p90 over the K steps and takes p50 as the headline.  The same
 protocol, in a second pass, times the split-K kernel alone with events the
-library records on its stream around that launch (kvd_options).  A third
+library ties to that kernel's dispatch (kvd_options; hipExtLaunchKernel
+takes the kernel's own start and end times).  A third
 pass times K back-to-back steps without eviction ("warm", reported apart,
 never used for the roofline); --no-warm skips it (profiling runs).
 
@@ -139,17 +141,36 @@ def summary(xs):
 
 
 class Flusher:
-    """Writes a 1 GiB scratch buffer on the current stream: afterwards no
-    K/V byte is left in the MALL or the L2s."""
+    """Evicts the K/V bytes of the previous step from the 256 MB MALL and the
+    L2s before a timed step, on the current stream.
 
-    def __init__(self, dev):
+    "read" (default): streams a 1 GiB scratch buffer with plain loads (the
+    read probe, default cache policy, so its lines allocate in every cache
+    level), which leaves the caches full of clean, unrelated lines -- the
+    state an attention call meets in a model, where the layers in between
+    stream their own caches and weights.  "write": fills the 1 GiB buffer
+    instead, which also evicts but leaves up to the MALL's size of dirty
+    lines that the timed step then pays to write back.  "none": no eviction."""
+
+    def __init__(self, dev, mode="read"):
         import torch
-        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.mode = mode
         self.i = 0
+        if mode != "none":
+            self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+            self.buf.fill_(1)
+            cu = torch.cuda.get_device_properties(dev).multi_processor_count
+            self.nwg = 4 * cu
+            self.sink = torch.empty(self.nwg, dtype=torch.int32, device=dev)
 
     def __call__(self):
         self.i += 1
-        self.buf.fill_(self.i & 0xFF)
+        if self.mode == "write":
+            self.buf.fill_(self.i & 0xFF)
+        elif self.mode == "read":
+            import kv_cache_gqa_decode_amd as kvd
+            from kv_cache_gqa_decode_amd import _binding as B
+            kvd.read_probe(self.buf, self.nwg, 8, B.PROBE_CHUNKED, self.sink)
 
 
 def cold_times(run, n, flush):
@@ -170,7 +191,7 @@ def cold_times(run, n, flush):
 
 def cold_kernel_times(run_with_events, n, flush):
     """Milliseconds of the main kernel of n calls, each after a flush: the
-    library records the events around that launch (kvd_options)."""
+    library ties the events to that kernel's dispatch (kvd_options)."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
@@ -364,7 +385,7 @@ def run_prefill(args, s, dev):
         kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
                              max_seq_len=max_len, out=out, lse=lse, options=options)
 
-    flush = Flusher(dev)
+    flush = Flusher(dev, args.flush)
     for _ in range(args.warmup):
         flush()
         step()
@@ -393,7 +414,7 @@ def run_prefill(args, s, dev):
                    "arithmetic": "q and P rounded to bf16 on the matrix cores, fp32 accumulate",
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-        "timing": "each step after a 1 GiB cache-evicting write; ms_per_step = p50",
+        "timing": f"each step after a 1 GiB cache-evicting {args.flush}; ms_per_step = p50",
         "step_ms": summary(steps),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 2500.0,
@@ -436,6 +457,9 @@ def main():
                          "(the kernel-time region stays eager)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
+                    help="how the caches are evicted before each timed step (default: a "
+                         "1 GiB streaming read; 'write' fills 1 GiB, leaving dirty lines)")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm (back-to-back, no eviction) pass: every launch of "
                          "the run is then cold, as a kernel-trace profile should see them")
@@ -542,7 +566,7 @@ def main():
         kvd.gqa_decode_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
                             max_seq_len=max_len, out=out, lse=lse, workspace=ws, options=options)
 
-    flush = Flusher(dev)
+    flush = Flusher(dev, args.flush)
     for _ in range(args.warmup):
         flush()
         step()
@@ -563,8 +587,8 @@ def main():
     t_wall = time.perf_counter()
     steps = cold_times(run, args.steps, flush)
     t_wall = time.perf_counter() - t_wall
-    # pass 2: the split-K kernel alone, same protocol, events recorded by the
-    # library around its launch (they would add gaps inside pass 1's steps)
+    # pass 2: the split-K kernel alone, same protocol, events the library
+    # ties to its dispatch (kept out of pass 1, whose steps they would change)
     base_opts = opts if opts is not None else kvd.Options()
     kern = cold_kernel_times(lambda a, b: step(base_opts.with_events(a, b)), args.steps, flush)
     # pass 3: back-to-back steps, no eviction (reported apart)
@@ -613,8 +637,10 @@ def main():
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "timing": ("each step after a 1 GiB cache-evicting write (MALL and L2 cold); "
-                   "ms_per_step and value from the p50 of the K steps"),
+        "timing": (f"each step after a 1 GiB cache-evicting {args.flush} (MALL and L2 cold); "
+                   "ms_per_step and value from the p50 of the K steps"
+                   if args.flush != "none" else
+                   "no eviction between steps; ms_per_step and value from the p50"),
         "step_ms": summary(steps),
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

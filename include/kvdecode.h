@@ -156,10 +156,12 @@ typedef enum {
  *   dispatch_order   kvd_dispatch_order
  *   reserved         must be 0
  *   event_start, event_stop
- *                    hipEvent_t handles (both or neither) recorded on
- *                    `stream` immediately before and after the launch of the
- *                    call's main kernel (the split-K kernel; the prefill
- *                    kernel), for measuring that kernel alone; NULL: none
+ *                    hipEvent_t handles (both or neither, created by the
+ *                    caller with timing enabled) tied to the dispatch of the
+ *                    call's main kernel -- the split-K kernel, the prefill
+ *                    kernel -- through hipExtLaunchKernel: they take that
+ *                    kernel's own start and end times, so their interval is
+ *                    its execution; NULL: none
  * Errors: EINVAL for values outside these ranges.
  */
 typedef struct kvd_options {

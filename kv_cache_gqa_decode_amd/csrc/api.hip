@@ -493,11 +493,8 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.qscale = log2_scale(scale, shape->head_dim);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (tu.ev_start && hipEventRecord(tu.ev_start, s) != hipSuccess) return KVD_EHIP;
-  if (launch_prefill_mfma(p, paged, s) != hipSuccess) return KVD_EHIP;
-  if (tu.ev_stop && hipEventRecord(tu.ev_stop, s) != hipSuccess) return KVD_EHIP;
-  return KVD_OK;
+  const Launch l{static_cast<hipStream_t>(stream), tu.ev_start, tu.ev_stop};
+  return launch_prefill_mfma(p, paged, l) == hipSuccess ? KVD_OK : KVD_EHIP;
 }
 
 }  // extern "C"
@@ -570,12 +567,11 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   }
 
   if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
-  if (tu.ev_start && hipEventRecord(tu.ev_start, s) != hipSuccess) return KVD_EHIP;
-  const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, s)
-                     : pl.kernel == 2 ? launch_decode_i8(p, paged, s)
-                                      : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, s);
+  const Launch l{s, tu.ev_start, tu.ev_stop};
+  const hipError_t e = pl.kernel == 1 ? launch_decode_mfma(p, paged, l)
+                     : pl.kernel == 2 ? launch_decode_i8(p, paged, l)
+                                      : launch_decode_valu(p, shape->kv_dtype, paged, pl.rb, l);
   if (e != hipSuccess) return KVD_EHIP;
-  if (tu.ev_stop && hipEventRecord(tu.ev_stop, s) != hipSuccess) return KVD_EHIP;
   if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;
 }

@@ -457,30 +457,25 @@ void decode_mfma_kernel_wide(DecodeParams p) {
 }
 
 template <int D, int NB>
-hipError_t launch_nb(const DecodeParams& p, bool paged, hipStream_t s) {
-  const dim3 grid = split_grid(p);
-  if (NB == 1) {
-    if (paged) decode_mfma_kernel<D, true><<<grid, 256, 0, s>>>(p);
-    else decode_mfma_kernel<D, false><<<grid, 256, 0, s>>>(p);
-  } else {
-    if (paged) decode_mfma_kernel_wide<D, true><<<grid, 256, 0, s>>>(p);
-    else decode_mfma_kernel_wide<D, false><<<grid, 256, 0, s>>>(p);
-  }
-  return hipGetLastError();
+hipError_t launch_nb(const DecodeParams& p, bool paged, const Launch& l) {
+  void (*k)(DecodeParams) = NB == 1 ? (paged ? decode_mfma_kernel<D, true> : decode_mfma_kernel<D, false>)
+                                    : (paged ? decode_mfma_kernel_wide<D, true>
+                                             : decode_mfma_kernel_wide<D, false>);
+  return launch_kernel(k, split_grid(p), dim3(256), l, p);
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams& p, bool paged, hipStream_t s) {
-  return p.R * p.T <= 16 ? launch_nb<D, 1>(p, paged, s) : launch_nb<D, 2>(p, paged, s);
+hipError_t launch_d(const DecodeParams& p, bool paged, const Launch& l) {
+  return p.R * p.T <= 16 ? launch_nb<D, 1>(p, paged, l) : launch_nb<D, 2>(p, paged, l);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l) {
   if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32)
     return hipErrorInvalidValue;
-  return p.D == 64 ? launch_d<64>(p, paged, s) : launch_d<128>(p, paged, s);
+  return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }
 
 }  // namespace kvd

@@ -258,20 +258,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
 }
 
 template <typename T, int D, bool PAGED>
-hipError_t launch_t(const DecodeParams& p, int rb, hipStream_t s) {
+hipError_t launch_t(const DecodeParams& p, int rb, const Launch& l) {
   const dim3 grid(p.B, p.G * p.head_groups, p.n_splits);
-  switch (rb) {
-    case 1: decode_valu_kernel<T, D, 1, PAGED><<<grid, 256, 0, s>>>(p); break;
-    case 2: decode_valu_kernel<T, D, 2, PAGED><<<grid, 256, 0, s>>>(p); break;
-    case 4: decode_valu_kernel<T, D, 4, PAGED><<<grid, 256, 0, s>>>(p); break;
-    default: decode_valu_kernel<T, D, 8, PAGED><<<grid, 256, 0, s>>>(p); break;
-  }
-  return hipGetLastError();
+  void (*k)(DecodeParams) = rb == 1 ? decode_valu_kernel<T, D, 1, PAGED>
+                          : rb == 2 ? decode_valu_kernel<T, D, 2, PAGED>
+                          : rb == 4 ? decode_valu_kernel<T, D, 4, PAGED>
+                                    : decode_valu_kernel<T, D, 8, PAGED>;
+  return launch_kernel(k, grid, dim3(256), l, p);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const DecodeParams& p, bool paged, int rb, hipStream_t s) {
-  return paged ? launch_t<T, D, true>(p, rb, s) : launch_t<T, D, false>(p, rb, s);
+hipError_t launch_d(const DecodeParams& p, bool paged, int rb, const Launch& l) {
+  return paged ? launch_t<T, D, true>(p, rb, l) : launch_t<T, D, false>(p, rb, l);
 }
 
 }  // namespace
@@ -284,13 +282,13 @@ int valu_heads_per_pass(int n_rep) {
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged, int rb,
-                              hipStream_t s) {
+                              const Launch& l) {
   if (p.T != 1) return hipErrorInvalidValue;    // one new token per sequence
   if (kv_dtype == KVD_FP32) {
-    return p.D == 64 ? launch_d<float, 64>(p, paged, rb, s) : launch_d<float, 128>(p, paged, rb, s);
+    return p.D == 64 ? launch_d<float, 64>(p, paged, rb, l) : launch_d<float, 128>(p, paged, rb, l);
   }
-  return p.D == 64 ? launch_d<uint16_t, 64>(p, paged, rb, s)
-                   : launch_d<uint16_t, 128>(p, paged, rb, s);
+  return p.D == 64 ? launch_d<uint16_t, 64>(p, paged, rb, l)
+                   : launch_d<uint16_t, 128>(p, paged, rb, l);
 }
 
 }  // namespace kvd

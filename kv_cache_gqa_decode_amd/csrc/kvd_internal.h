@@ -2,6 +2,7 @@
 // Nothing here is part of the C ABI (include/kvdecode.h is).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,15 +69,38 @@ struct RopeParams {
   int32_t block_shift;      // paged: log2(block_size / 16), 0 or 1
 };
 
+// Where a main kernel goes: its stream and, for measurement, a pair of
+// events tied to the dispatch itself (hipExtLaunchKernel records them at
+// the kernel's own start and end, so their interval is the kernel's
+// execution as a profiler's kernel trace sees it, without the gap between
+// a separately recorded event and the dispatch).
+struct Launch {
+  hipStream_t stream = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// kernel<<<grid, block, 0, l.stream>>>(p), with l's events when it has them.
+template <typename P>
+inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, const Launch& l, P p) {
+  if (l.start || l.stop) {
+    void* args[] = {&p};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0,
+                              l.stream, l.start, l.stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, l.stream, p);
+  return hipGetLastError();
+}
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
-                              int rb, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
-hipError_t launch_decode_i8(const DecodeParams& p, bool paged, hipStream_t stream);
+                              int rb, const Launch& l);
+hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l);
+hipError_t launch_decode_i8(const DecodeParams& p, bool paged, const Launch& l);
 // causal prefill of p.T new tokens per sequence (p.qscale, no splits)
-hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, hipStream_t stream);
+hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, const Launch& l);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_build_units(const DecodeParams& p, hipStream_t stream);
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).

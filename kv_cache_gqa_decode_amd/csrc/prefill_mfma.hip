@@ -391,21 +391,16 @@ void prefill_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, hipStream_t s) {
+hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, const Launch& l) {
   if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
   const int64_t ncols = static_cast<int64_t>(p.T) * p.R;
   const int64_t nqt = (ncols + kPfRows - 1) / kPfRows;
   const int64_t wgs = nqt * p.B * p.G;
   if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs));
-  if (p.D == 64) {
-    if (paged) prefill_kernel<64, true><<<grid, 256, 0, s>>>(p);
-    else prefill_kernel<64, false><<<grid, 256, 0, s>>>(p);
-  } else {
-    if (paged) prefill_kernel<128, true><<<grid, 256, 0, s>>>(p);
-    else prefill_kernel<128, false><<<grid, 256, 0, s>>>(p);
-  }
-  return hipGetLastError();
+  void (*k)(DecodeParams) = p.D == 64 ? (paged ? prefill_kernel<64, true> : prefill_kernel<64, false>)
+                                      : (paged ? prefill_kernel<128, true> : prefill_kernel<128, false>);
+  return launch_kernel(k, grid, dim3(256), l, p);
 }
 
 }  // namespace kvd

@@ -95,6 +95,25 @@ def appended_rows(p: W.Problem):
     return rows
 
 
+def assert_q_rot(got, ref, what=""):
+    """q_rot against the oracle's fp64 rotation.  Both sides rotate in fp64
+    and round once to fp32, so they agree to 1 ulp -- except where the
+    rotated value nearly cancels (|a cos - c sin| << |a|): there the fp64
+    rounding of the angle itself (P * theta, up to ~1e-11 rad at positions
+    near 131072, and the 1-ulp freedom of libm's pow / sin / cos) is no
+    longer small against the result.  Such elements must still agree to
+    1e-9 of their row's largest element, far below any effect on the
+    attention and far above a wrong angle or pair."""
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float64)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - ref.astype(np.float32).view(np.int32))
+    near = np.abs(got.astype(np.float64) - ref) <= 1e-9 * np.abs(ref).max(axis=-1, keepdims=True)
+    ok = (ulp <= 1) | near
+    assert ok.all(), (f"{what}: q_rot differs at {(~ok).sum()} elements "
+                      f"(max {ulp[~ok].max()} ulp)")
+    return int((ulp > 1).sum())
+
+
 def bits(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.int8:
         return a

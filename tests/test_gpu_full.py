@@ -12,7 +12,8 @@ import torch
 
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import appended_rows, bits, device, gpu_step, oracle_step, upload
+from tests.gpu_helpers import (appended_rows, assert_q_rot, bits, device, gpu_step, oracle_step,
+                               upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +25,7 @@ def run_full(s: W.Spec):
     t = upload(p, dev)
     q_rot, out, lse = gpu_step(t, s, p.max_len)
     oq, oo, ol, okc, ovc = oracle_step(p)
+    assert_q_rot(q_rot.cpu().numpy(), oq, f"{s.name} q_rot")
     e = gates.assert_out(out.cpu().numpy(), oo, s.dtype, f"{s.name} all rows")
     gates.assert_lse(lse.cpu().numpy(), ol, s.dtype, f"{s.name} all rows lse")
     print(f"[full] {s.name} G={s.n_kv_heads}: {e}", flush=True)

@@ -14,7 +14,7 @@ import torch
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import device, gpu_step, opts, oracle_step, upload
+from tests.gpu_helpers import assert_q_rot, device, gpu_step, opts, oracle_step, upload
 from tests.test_gpu_parity import shared_prefix
 
 pytestmark = pytest.mark.gpu
@@ -36,8 +36,7 @@ def check_full(p: W.Problem, split=0, style="interleaved", what="", tail=(0, -1)
     assert np.array_equal(W.from_torch(t["k_cache"]), okc), f"{what}: K codes differ"
     assert np.array_equal(W.from_torch(t["v_cache"]), ovc), f"{what}: V codes differ"
     qr = q_rot.cpu().numpy()
-    ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
-    assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+    assert_q_rot(qr, oq, what)
     e = gates.assert_out(out.cpu().numpy(), oo, "i8", what)
     gates.assert_lse(lse.cpu().numpy(), ol, "i8", what)
     return e
@@ -190,6 +189,7 @@ def run_full_i8(s: W.Spec):
     t = upload(p, dev)
     q_rot, out, lse = gpu_step(t, s, p.max_len)
     oq, oo, ol, okc, ovc = oracle_step(p)
+    assert_q_rot(q_rot.cpu().numpy(), oq, f"int8 {s.name} q_rot")
     e = gates.assert_out(out.cpu().numpy(), oo, "i8", f"int8 {s.name} all rows")
     gates.assert_lse(lse.cpu().numpy(), ol, "i8", f"int8 {s.name} all rows lse")
     print(f"[full int8] {s.name} G={s.n_kv_heads}: {e}", flush=True)

@@ -5,7 +5,7 @@ against the oracle's multi-token step on the same seeded inputs.
 "Transformer架构优化实战2026" §五: the target model checks the gamma draft
 tokens of speculative decoding in one forward (gamma = 4 there, T = 5); each
 of the T queries attends the cache and the new tokens up to its own position
-([KVGR] §5.1 b.v).  Caches must match bit for bit, q_rot to 1 ulp, outputs
+([KVGR] §5.1 b.v).  Caches must match bit for bit, q_rot to 1 ulp (gpu_helpers.assert_q_rot), outputs
 and lse within the bf16 gates (INT8 caches use them too: both sides read the
 same codes).  Every case compares every output row and lse, and the caches
 in full.
@@ -18,7 +18,7 @@ import oracle
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import device, geom, opts, upload
+from tests.gpu_helpers import assert_q_rot, device, geom, opts, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -74,8 +74,7 @@ def check_window(p: W.Problem, split=0, style="interleaved", what=""):
     assert np.array_equal(W.from_torch(t["k_cache"]), okc), f"{what}: K cache differs"
     assert np.array_equal(W.from_torch(t["v_cache"]), ovc), f"{what}: V cache differs"
     qr = q_rot.cpu().numpy()
-    ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
-    assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+    assert_q_rot(qr, oq, what)
     gd = "i8" if s.dtype == "i8" else "bf16"
     gates.assert_out(out.cpu().numpy(), oo, gd, what)
     gates.assert_lse(lse.cpu().numpy(), ol, gd, what)

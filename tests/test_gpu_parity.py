@@ -16,7 +16,8 @@ import torch
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import (appended_rows, bits, device, gpu_step, opts, oracle_step, upload)
+from tests.gpu_helpers import (appended_rows, assert_q_rot, bits, device, gpu_step, opts,
+                               oracle_step, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +35,7 @@ def check_full(p: W.Problem, kernel=None, split=0, style="interleaved", what="",
     assert np.array_equal(bits(kc), bits(okc)), f"{what}: K cache differs from the oracle's"
     assert np.array_equal(bits(vc), bits(ovc)), f"{what}: V cache differs from the oracle's"
     qr = q_rot.cpu().numpy()
-    ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
-    assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+    assert_q_rot(qr, oq, what)
     e = gates.assert_out(out.cpu().numpy(), oo, s.dtype, what)
     gates.assert_lse(lse.cpu().numpy(), ol, s.dtype, what)
     return e
@@ -349,7 +349,7 @@ def bad_table(p: W.Problem):
     """The problem's table with entries outside the pool: two inside the
     history of sequence 9, the appended block of sequences 10 and 4 (their
     appends must be skipped) and the first block of sequence 10.  Returns
-    (table, the sequences left intact)."""
+    (table, the sequences left intact, the sequences whose append lands)."""
     s = p.spec
     bs = s.block_size
     t = p.block_table.copy()
@@ -359,32 +359,38 @@ def bad_table(p: W.Problem):
         t[b, int(p.positions[b]) // bs] = v
     t[10, 0] = 2 ** 31 - 1
     intact = [b for b in range(s.batch) if b not in (4, 9, 10)]
-    return t, intact
+    appended = [b for b in range(s.batch) if b not in (4, 10)]
+    return t, intact, appended
+
+
+def _subset(p: W.Problem, rows):
+    s = p.spec
+    return dataclasses.replace(
+        p, spec=s.replace(batch=len(rows)), q=p.q[rows], k_new=p.k_new[rows],
+        v_new=p.v_new[rows], positions=p.positions[rows], seq_lens=p.seq_lens[rows],
+        block_table=p.block_table[rows])
 
 
 def run_bad_table(p: W.Problem, options):
     """GPU step on a table with out-of-pool entries: the intact sequences
     equal the oracle, every output is finite or (no valid token) 0 / -inf,
-    and the caches equal the oracle's after appending only the intact
-    sequences (no write through a bad id)."""
+    and the caches equal the oracle's after the appends whose block is in
+    the pool (no write through a bad id)."""
     dev = device()
     s = p.spec
-    table, intact = bad_table(p)
+    table, intact, appended = bad_table(p)
     t = upload(p, dev)
     t["block_table"] = W.as_torch(table, dev)
     q_rot, out, lse = gpu_step(t, s, p.max_len, options=options)
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(out).all()
     assert not np.isnan(lse).any()
-    sub = dataclasses.replace(
-        p, spec=s.replace(batch=len(intact)), q=p.q[intact], k_new=p.k_new[intact],
-        v_new=p.v_new[intact], positions=p.positions[intact], seq_lens=p.seq_lens[intact],
-        block_table=p.block_table[intact])
-    _, oo, ol, okc, ovc = oracle_step(sub)
+    _, oo, ol, _, _ = oracle_step(_subset(p, intact))
     gates.assert_out(out[intact], oo, s.dtype, "intact sequences")
     gates.assert_lse(lse[intact], ol, s.dtype, "intact sequences")
-    assert np.array_equal(bits(W.from_torch(t["k_cache"])), bits(okc)), "K pool written"
-    assert np.array_equal(bits(W.from_torch(t["v_cache"])), bits(ovc)), "V pool written"
+    _, _, _, okc, ovc = oracle_step(_subset(p, appended))
+    assert np.array_equal(bits(W.from_torch(t["k_cache"])), bits(okc)), "K pool differs"
+    assert np.array_equal(bits(W.from_torch(t["v_cache"])), bits(ovc)), "V pool differs"
 
 
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])

@@ -18,7 +18,7 @@ import torch
 import kv_cache_gqa_decode_amd as kvd
 from kv_cache_gqa_decode_amd import workloads as W
 from tests import gates
-from tests.gpu_helpers import device, upload
+from tests.gpu_helpers import assert_q_rot, device, upload
 from tests.test_gpu_multi import oracle_window, _bits
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,7 @@ def check_prefill(p: W.Problem, what="", units=None, style="interleaved"):
         go, gl = go[ub, ut, uh], gl[ub, ut, uh]
     else:
         qr = q_rot.cpu().numpy()
-        ulp = np.abs(qr.view(np.int32).astype(np.int64) - oq.astype(np.float32).view(np.int32))
-        assert ulp.max() <= 1, f"{what}: q_rot differs by {ulp.max()} ulp"
+        assert_q_rot(qr, oq, what)
     e = gates.assert_out(go, oo, "prefill", what)
     gates.assert_lse(gl, ol, "prefill", what)
     print(f"[prefill] {what}: {e}", flush=True)
