@@ -395,6 +395,31 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
                             float* out, float* lse, const kvd_options* options, void* stream);
 
+/*
+ * gqa_decode_attn_multi_noalloc -- gqa_decode_attn_multi without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The split partials and the work list go to a library-owned
+ * device array of KVD_NOALLOC_SCRATCH_BYTES (32 MiB), one per device, held
+ * until the process ends (looked up with hipGetSymbolAddress on the first
+ * call on each device).  The call allocates and frees nothing.
+ *   Arguments, results and errors as gqa_decode_attn_multi, and in
+ *   addition EWORKSPACE when gqa_decode_workspace_size_multi(shape,
+ *   n_query, max_seq_len_host, options) exceeds KVD_NOALLOC_SCRATCH_BYTES
+ *   (nothing enqueued).
+ *   Calls that may run at the same time on one device (other streams,
+ *   other host threads) share the array and race: serialise them.  No
+ *   part of the array needs clearing between calls.
+ */
+#define KVD_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query,
+                                         const float* q_rot, const void* k_cache,
+                                         const void* v_cache, const float* k_scale,
+                                         const float* v_scale, const int32_t* seq_lens,
+                                         const int32_t* block_table, int32_t max_seq_len_host,
+                                         float scale, float* out, float* lse,
+                                         const kvd_options* options, void* stream);
+
 /* Workspace bytes of gqa_decode_attn_multi with these options (NULL:
  * automatic); 0 also for an invalid shape or invalid options. */
 size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,

@@ -107,7 +107,9 @@ def _options(opts: Optional[Options]):
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
             "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
-            "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe")
+            "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
+            "gqa_decode_attn_multi_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 _lock = threading.Lock()
@@ -150,6 +152,9 @@ def load_library():
         OP = ctypes.POINTER(_COptions)
         lib.gqa_decode_attn_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_float,
                                               P, P, P, ctypes.c_size_t, OP, P]
+        lib.gqa_decode_attn_multi_noalloc.restype = I32
+        lib.gqa_decode_attn_multi_noalloc.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
+                                                      ctypes.c_float, P, P, OP, P]
         lib.gqa_prefill_attn.restype = I32
         lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, OP, P]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
@@ -556,6 +561,40 @@ def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                 scale, out, lse, workspace, options, dev)
     return out, lse
 
+
+
+def gqa_decode_attn_noalloc(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                            k_scale: Optional[torch.Tensor] = None,
+                            v_scale: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                            out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                            options: Optional[Options] = None
+                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gqa_decode_attn_multi through gqa_decode_attn_multi_noalloc: the split
+    partials live in the library's own device array (at most
+    NOALLOC_SCRATCH_BYTES), so with ``out`` (and ``lse``) given nothing is
+    allocated.  q_rot [B, T, H, D]; calls overlapping on one device race."""
+    lib = load_library()
+    dev = k_cache.device
+    B, T, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, T, H, D))
+    _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, shape.n_kv_heads, dev,
+                        block_table is not None)
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if shape.head_dim != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    out, lse = _outputs((B, T), H, D, dev, out, lse, want_lse)
+    _check(lib.gqa_decode_attn_multi_noalloc(
+        ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(seq_lens), _ptr(block_table), msl, _scale_arg(scale), _ptr(out),
+        _ptr(lse), _options(options), _stream(dev)))
+    return out, lse
 
 
 def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
