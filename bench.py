@@ -26,8 +26,9 @@ Prints ONE JSON line:
              duration against the 8 TB/s HBM peak; `traffic` is the HBM
              bytes per launch from the committed rocprofv3 counter summary
              of this kernel and workload (null when missing or taken from a
-             different kernel source); with --read-ceiling also the
-             fraction of the measured streaming-read ceiling
+             different kernel source); `frac_of_read_ceiling` compares it
+             with a plain cold streaming read of the same byte count (the
+             read probe, same eviction and event timing)
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload, in the same unit (a reported baseline only)
 
@@ -50,7 +51,7 @@ processes B * T tokens.
 Usage: python bench.py [--steps K] [--warmup W] [--config c3|c4|c5|c2|c1]
                        [--kv-heads G] [--kv native|int8] [--n-query T] [--prefill T]
                        [--kernel auto|valu|mfma] [--split N]
-                       [--no-cpu-baseline] [--no-warm] [--read-ceiling]
+                       [--no-cpu-baseline] [--no-warm] [--no-read-ceiling]
 """
 import argparse
 import hashlib
@@ -219,42 +220,40 @@ def warm_ms(run, n):
     return a.elapsed_time(b) / n
 
 
-def read_ceiling(dev, kvd, gib: int = 4):
-    """Best streaming-read bandwidth of the read probe over its load paths
-    (registers or HBM -> LDS copies, default or non-temporal policy) and a
-    few launch shapes (GB/s): the practical roof beside the nominal peak.
-    The 4 GiB buffer is 16x the MALL, so every launch reads from HBM."""
+def read_ceiling(dev, kvd, nbytes: int, flush):
+    """The practical roof for reading `nbytes` once, cold: the read probe over
+    a buffer of exactly that size, after the same cache eviction as the
+    timed steps, timed with events like the kernel, best median over its load
+    paths (registers or HBM -> LDS copies, non-temporal) and launch shapes
+    (GB/s).  At small sizes this is far below the nominal peak: the launch,
+    the first requests' latency and the tail are not hidden by a long stream."""
     import torch
     from kv_cache_gqa_decode_amd import _binding as B
-    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    nbytes = (nbytes + 1023) // 1024 * 1024
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    names = {0: "registers, grid-stride", B.PROBE_CHUNKED: "registers, chunk per workgroup",
-             B.PROBE_CHUNKED | B.PROBE_NONTEMPORAL: "registers non-temporal, chunk per workgroup",
-             B.PROBE_NONTEMPORAL: "registers non-temporal, grid-stride",
-             B.PROBE_LDS: "HBM->LDS copies, chunk per workgroup",
-             B.PROBE_LDS | B.PROBE_NONTEMPORAL: "HBM->LDS non-temporal copies, chunk per workgroup"}
+    names = {B.PROBE_CHUNKED | B.PROBE_NONTEMPORAL: "registers, non-temporal",
+             B.PROBE_CHUNKED: "registers",
+             B.PROBE_LDS | B.PROBE_NONTEMPORAL: "HBM->LDS copies, non-temporal"}
     best = (0.0, None)
     for mode, name in names.items():
-        for per_cu in (1, 2, 4, 8):
-            for unroll in (4, 8, 16):
+        for per_cu in (1, 2, 4):
+            for unroll in (8, 16):
                 nwg = cu * per_cu
+                if mode & B.PROBE_LDS and nbytes // nwg >= (1 << 31):
+                    continue
                 sink = kvd.read_probe(buf, nwg, unroll, mode)
-                torch.cuda.synchronize()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                for _ in range(5):
-                    kvd.read_probe(buf, nwg, unroll, mode, sink)
-                b.record()
-                torch.cuda.synchronize()
-                gbs = 5 * buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+                times = cold_times(lambda: kvd.read_probe(buf, nwg, unroll, mode, sink), 9, flush)
+                gbs = nbytes / (pct(times, 50) * 1e-3) / 1e9
                 if gbs > best[0]:
-                    best = (gbs, f"{name}, {per_cu} workgroups/CU x 256 threads, "
-                                 f"{unroll} x 16 B in flight per lane")
+                    best = (gbs, f"{name}, one contiguous chunk per workgroup, {per_cu} "
+                                 f"workgroups/CU x 256 threads, {unroll} x 16 B in flight per lane")
     del buf
     torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
-            "shape": best[1], "buffer_gib": gib}
+            "shape": best[1], "bytes": nbytes,
+            "protocol": "read probe over the kernel's byte count, cold, p50 of 9 event-timed launches"}
 
 
 def cpu_baseline(s, p, budget_s: float):
@@ -463,11 +462,11 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm (back-to-back, no eviction) pass: every launch of "
                          "the run is then cold, as a kernel-trace profile should see them")
-    ap.add_argument("--read-ceiling", action="store_true",
-                    help="also measure the streaming-read ceiling (the read probe over a "
-                         "4 GiB buffer) and report the kernel against it")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the cold streaming-read ceiling at the kernel's byte count (the "
+                         "read probe, measured by default) that the kernel is reported against")
     ap.add_argument("--ceiling-only", action="store_true",
-                    help="only measure the streaming-read ceiling and print it")
+                    help="only measure the cold streaming-read ceiling over 4 GiB and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times "
                          "(reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -498,7 +497,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
         return
     if args.ceiling_only:
-        print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd)}))
+        print(json.dumps({"hbm_read_ceiling": read_ceiling(dev, kvd, 4 << 30, Flusher(dev))}))
         return
     s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False)
     if args.block_size is not None:
@@ -602,7 +601,8 @@ def main():
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kern_ms = pct(kern, 50)
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
-    ceiling = read_ceiling(dev, kvd) if args.read_ceiling else None
+    ceiling = (None if args.no_read_ceiling else
+               read_ceiling(dev, kvd, kv_bytes, Flusher(dev, args.flush)))
 
     key = (f"{s.name}" + (f"_g{G}" if s.name == "c5" else "") + ("_i8" if int8 else "") +
            (f"_bs{s.block_size}" if s.block_size not in (0, 16) else "") +

@@ -227,8 +227,8 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   lds_char* const stage = (lds_char*)(smem);
   lds_char* vbuf[2] = {stage + (2 * wave) * G::kTileBytes, stage + (2 * wave + 1) * G::kTileBytes};
   // this lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
-  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + G::at(tile_row(4 * grp + n / 4), 8 * (n % 4)),
-                           lds_addr(vbuf[1]) + G::at(tile_row(4 * grp + n / 4), 8 * (n % 4))};
+  const uint32_t vrd_off = G::at(tile_row(4 * grp + n / 4), 8 * (n % 4));
+  const uint32_t vrd[2] = {lds_addr(vbuf[0]) + vrd_off, lds_addr(vbuf[1]) + vrd_off};
   constexpr int kVHalf = (16 / RPI) * G::BLOCK;     // rows r -> r + 16
   uint4 kr[2][KB];
   int blk_cur[2];
@@ -287,29 +287,9 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One tile (the wave's kt-th): `kr` holds its K rows, buffer `cur` its V
-  // rows (being copied), `blk` its block ids.  The next tile's V copies go
-  // out first, into the other buffer; its K rows go out right after this
-  // tile's score MFMAs have consumed `kr`.  `more` (a constant at each call)
-  // says whether there is a next tile: the loads are then issued on every
-  // path, so the compiler's own wait for `kr` counts them and stays partial.
-  auto compute = [&](int kt, int tbase, int (&blk)[2], int cur, const bool more) {
-    const int nbase = tbase + kWaves * TT;
-    int blk_next[2];
-    tile_blocks(kt + 1, blk_next);
-    const TileSrc ns = tile_src(nbase, blk_next);
-    if (more) {
-      issue_v(ns, vbuf[cur ^ 1]);
-      // keep the copies ahead of the score MFMAs, whose wait for `kr` may
-      // then leave them outstanding
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const bool full = tbase + TT <= t1;
-    const bool ok0 = !PAGED || blk[0] >= 0;
-    const bool ok1 = !PAGED || blk[1] >= 0;
-    const bool masked = !full || !ok0 || !ok1 || tbase + TT > win;      // wave-uniform
-    // scores of the two 16-token halves
-    f32x4 s[NB][2];
+  // The pieces of one tile's work.  Scores of the two 16-token halves from
+  // the K registers:
+  auto scores = [&](const uint4 (&k)[2][KB], f32x4 (&sc)[NB][2]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -317,22 +297,25 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, kr[h2][kb]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, k[h2][kb]);
           c = mfma(a, qh[nb][kb], c);
           c = mfma(a, ql[nb][kb], c);
         }
-        s[nb][h2] = c;
+        sc[nb][h2] = c;
       }
-    if (more) issue_k(ns, kr);          // K rows of the next tile, into the same registers
-
-    bf16x8 ph[NB], pl[NB];
+  };
+  // Online softmax of a tile's scores (tokens at or past the end, in a bad
+  // block, or past a column's bound excluded when `masked`): moves the
+  // running max when needed and returns the probabilities as bf16 hi + lo.
+  auto softmax = [&](f32x4 (&sc)[NB][2], int tbase, bool masked, bool ok0, bool ok1,
+                     bf16x8 (&ph)[NB], bf16x8 (&pl)[NB]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float sv[8];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j];
+        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = sc[nb][h2][j];
       if (masked) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -371,48 +354,82 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       ph[nb] = __builtin_bit_cast(bf16x8, hi);
       pl[nb] = __builtin_bit_cast(bf16x8, lo);
     }
-
-    // this tile's V copies have landed: only the next tile's loads (V copies,
-    // then K rows) may still be outstanding
-    if (more) vmem_wait<G::NLOADS>();
-    else vmem_wait<0>();
-    if (masked) {                        // rows past the end or in a bad block become zeros
-      const uint32_t vt = lds_addr(vbuf[cur]);
+  };
+  // Staged V rows past the end or in a bad block become zeros (after the
+  // tile's copies have landed; stale LDS may hold NaN and 0 * NaN is NaN).
+  auto zero_rows = [&](uint32_t vt, int tbase, bool ok0, bool ok1) {
 #pragma unroll
-      for (int jj = 0; jj < NVL; ++jj) {
-        const int r = jj * RPI + lane / LPR;
-        const bool ok = (jj * RPI) / 16 == 0 ? ok0 : ok1;
-        if (!(tbase + r < t1 && ok)) lds_zero16(vt + jj * G::BLOCK + lane * 16);
-      }
+    for (int jj = 0; jj < NVL; ++jj) {
+      const int r = jj * RPI + lane / LPR;
+      const bool ok = (jj * RPI) / 16 == 0 ? ok0 : ok1;
+      if (!(tbase + r < t1 && ok)) lds_zero16(vt + jj * G::BLOCK + lane * 16);
     }
-
-    // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens
-    // 16*(j/4) + tile_row(4*grp + j%4)
-    // (transposing LDS reads)
+  };
+  // O^T[d][h] += V^T[d][t] P^T[t][h]; A row = dim 16*cb + n, tokens
+  // 16*(j/4) + tile_row(4*grp + j%4) (transposing LDS reads at `vaddr`,
+  // this lane's read address in the staged tile)
+  auto pv = [&](uint32_t vaddr, const bf16x8 (&ph)[NB], const bf16x8 (&pl)[NB]) {
     static_for<CB>([&](auto cbc) {
       constexpr int cb = decltype(cbc)::value;
-      const bf16x8 av = read_vt_tr<32 * cb, kVHalf>(vrd[cur]);
+      const bf16x8 av = read_vt_tr<32 * cb, kVHalf>(vaddr);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         acc[nb][cb] = mfma(av, ph[nb], acc[nb][cb]);
         acc[nb][cb] = mfma(av, pl[nb], acc[nb][cb]);
       }
     });
-    blk[0] = blk_next[0];
-    blk[1] = blk_next[1];
   };
 
-  // the two V buffers alternate; K lives in one register set; the wave's
-  // last tile is peeled off (no next tile to request)
-  if (base < t1) {
-    int kt = 0, cur = 0;
-    while (base + kWaves * TT < t1) {
-      compute(kt, base, blk_cur, cur, true);
-      base += kWaves * TT;
-      ++kt;
-      cur ^= 1;
+  {
+    // One tile (the wave's kt-th): `kr` holds its K rows, buffer `cur` its V
+    // rows (being copied), `blk` its block ids.  The next tile's V copies go
+    // out first, into the other buffer; its K rows go out right after this
+    // tile's score MFMAs have consumed `kr`.  `more` (a constant at each
+    // call) says whether there is a next tile: the loads are then issued on
+    // every path, so the compiler's own wait for `kr` counts them and stays
+    // partial.
+    auto compute = [&](int kt, int tbase, int (&blk)[2], int cur, const bool more) {
+      const int nbase = tbase + kWaves * TT;
+      int blk_next[2];
+      tile_blocks(kt + 1, blk_next);
+      const TileSrc ns = tile_src(nbase, blk_next);
+      if (more) {
+        issue_v(ns, vbuf[cur ^ 1]);
+        // keep the copies ahead of the score MFMAs, whose wait for `kr` may
+        // then leave them outstanding
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool full = tbase + TT <= t1;
+      const bool ok0 = !PAGED || blk[0] >= 0;
+      const bool ok1 = !PAGED || blk[1] >= 0;
+      const bool masked = !full || !ok0 || !ok1 || tbase + TT > win;      // wave-uniform
+      f32x4 sc[NB][2];
+      scores(kr, sc);
+      if (more) issue_k(ns, kr);          // K rows of the next tile, into the same registers
+      bf16x8 ph[NB], pl[NB];
+      softmax(sc, tbase, masked, ok0, ok1, ph, pl);
+      // this tile's V copies have landed: only the next tile's loads (V
+      // copies, then K rows) may still be outstanding
+      if (more) vmem_wait<G::NLOADS>();
+      else vmem_wait<0>();
+      if (masked) zero_rows(lds_addr(vbuf[cur]), tbase, ok0, ok1);
+      pv(vrd[cur], ph, pl);
+      blk[0] = blk_next[0];
+      blk[1] = blk_next[1];
+    };
+
+    // the two V buffers alternate; K lives in one register set; the wave's
+    // last tile is peeled off (no next tile to request)
+    if (base < t1) {
+      int kt = 0, cur = 0;
+      while (base + kWaves * TT < t1) {
+        compute(kt, base, blk_cur, cur, true);
+        base += kWaves * TT;
+        ++kt;
+        cur ^= 1;
+      }
+      compute(kt, base, blk_cur, cur, false);
     }
-    compute(kt, base, blk_cur, cur, false);
   }
   // a wave without tiles still has its (empty) copies outstanding: they
   // write zeros into its staging buffers, which the merge below reuses
