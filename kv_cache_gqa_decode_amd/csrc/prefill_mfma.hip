@@ -23,14 +23,14 @@
 //    V layout) by the transposing LDS reads of gfx950.
 //
 // Arithmetic: q (times scale * log2 e) and the probabilities enter the
-// matrix cores rounded once to bf16, accumulation is fp32.  Two running
-// sums are kept: of the rounded probabilities, which normalises the output
-// (an exact convex combination of V rows, weights accurate to bf16), and of
-// the fp32 ones, which gives the log-sum-exp (off by the score rounding
-// only).  This is the precision of FlashAttention-2 in bf16; the decode
-// kernels carry q and P as bf16 hi + lo pairs instead, at twice the
-// matrix-core work, which the bandwidth-bound decode step does not notice
-// but the compute-bound prefill would.
+// matrix cores rounded once to bf16, accumulation is fp32.  One running sum
+// of the fp32 probabilities normalises the output and gives the
+// log-sum-exp (the weights P V uses are those probabilities rounded to
+// bf16, so the output is off by their rounding, 2^-9 relative at most).
+// This is the precision of FlashAttention-2 in bf16; the decode kernels
+// carry q and P as bf16 hi + lo pairs instead, at twice the matrix-core
+// work, which the bandwidth-bound decode step does not notice but the
+// compute-bound prefill would.
 #include "mfma_tile.h"
 
 namespace kvd {
@@ -248,10 +248,10 @@ void prefill_kernel(DecodeParams p) {
   constexpr int kVHalf = (16 / VG::RPI) * VG::BLOCK;     // rows r -> r + 16
 
   f32x4 acc[NB][CB];
-  float m[NB], l[NB], lx[NB];
+  float m[NB], lx[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = kNegInf; l[nb] = 0.f; lx[nb] = 0.f;
+    m[nb] = kNegInf; lx[nb] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -325,7 +325,6 @@ void prefill_kernel(DecodeParams p) {
       if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
         const float mn = fmaxf(m[nb], mt);
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
-        l[nb] *= alpha;
         lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
@@ -333,7 +332,7 @@ void prefill_kernel(DecodeParams p) {
       }
       const float ref = m[nb] == kNegInf ? 0.f : m[nb];
       float e[8];
-      float ps = 0.f, px = 0.f;
+      float px = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
@@ -341,12 +340,7 @@ void prefill_kernel(DecodeParams p) {
       }
       u32x4 h;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] = pack_bf16(e[2 * j], e[2 * j + 1]);
-        // the sum of the weights P V uses
-        ps += __uint_as_float(h[j] << 16) + __uint_as_float(h[j] & 0xffff0000u);
-      }
-      l[nb] += ps;
+      for (int j = 0; j < 4; ++j) h[j] = pack_bf16(e[2 * j], e[2 * j + 1]);
       lx[nb] += px;
       pb[nb] = __builtin_bit_cast(bf16x8, h);
     }
@@ -371,15 +365,13 @@ void prefill_kernel(DecodeParams p) {
   // the four lane groups of a column hold partial sums under one max
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    l[nb] += __shfl_xor(l[nb], 16);
-    l[nb] += __shfl_xor(l[nb], 32);
     lx[nb] += __shfl_xor(lx[nb], 16);
     lx[nb] += __shfl_xor(lx[nb], 32);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (!real[nb]) continue;
-    const float inv = l[nb] > 0.f ? 1.f / l[nb] : 0.f;
+    const float inv = lx[nb] > 0.f ? 1.f / lx[nb] : 0.f;
     float* dst = p.out + qrow[nb] * D + 4 * grp;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)

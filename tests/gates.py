@@ -13,13 +13,14 @@
 * Causal prefill (gqa_prefill_attn, dtype "prefill"): q * scale and the
   probabilities enter the matrix cores rounded once to bf16, as in
   FlashAttention-2 in bf16.  Rounding each weight to bf16 perturbs it by up
-  to 2^-9 relative (1.1e-3 rms), and since the weights are normalised by
-  their own sum the output error is that perturbation averaged over V:
-  about 1e-3 relative per element.  lse comes from the sum of the unrounded
-  probabilities, so only the rounding of q moves it.  An fp64 emulation of
-  exactly these roundings (rows of 2 to 2000 tokens, q gain 1 to 32) gave
-  normwise output errors of 1.5e-3 to 3.0e-3 and lse errors up to 1.5e-3 *
-  max(1, |lse|) (2 tokens at q gain 32; 3e-4 otherwise).  Gates: max abs
+  to 2^-9 relative (1.1e-3 rms); the output is normalised by the sum of the
+  unrounded weights, so its error is that perturbation averaged over V:
+  about 1e-3 relative per element.  lse comes from the same sum, so only
+  the rounding of q moves it.  An fp64 emulation of exactly these roundings
+  (rows of 2 to 2000 tokens, q gain 1 to 32) gave normwise output errors of
+  1.5e-3 to 3.0e-3 and lse errors up to 1.5e-3 * max(1, |lse|) (2 tokens at
+  q gain 32; 3e-4 otherwise); normalising by the sum of the rounded weights
+  instead gives the same errors to within the spread of the trials.  Gates: max abs
   <= 1e-2 (the bf16 gate), normwise <= 1e-2, lse <= 5e-3 * max(1, |r|).
 * lse (natural log): |g - r| <= tol_lse * max(1, |r|).
 * Cache append and block-table indexing: bit-exact.
