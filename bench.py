@@ -377,12 +377,19 @@ def run_prefill(args, s, dev):
     out = torch.empty_like(q_rot)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     max_len = p.max_len
+    base_opts = kvd.Options(dispatch_order=args.order if args.order >= 0 else None,
+                            split_tokens=args.split)
+    # the key-split workspace, allocated before the timed region
+    ws_bytes = kvd.prefill_workspace_size(B, H, T, t["k_cache"], table, max_len, base_opts)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step(options=None):
         kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                  t["positions"], table, base=s.rope_base, q_rot=q_rot)
         kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
-                             max_seq_len=max_len, out=out, lse=lse, options=options)
+                             max_seq_len=max_len, out=out, lse=lse,
+                             options=options if options is not None else base_opts,
+                             workspace=ws)
 
     flush = Flusher(dev, args.flush)
     for _ in range(args.warmup):
@@ -392,7 +399,7 @@ def run_prefill(args, s, dev):
     t_wall = time.perf_counter()
     steps = cold_times(step, args.steps, flush)
     t_wall = time.perf_counter() - t_wall
-    kern = cold_kernel_times(lambda a, b: step(kvd.Options(events=(a, b))), args.steps, flush)
+    kern = cold_kernel_times(lambda a, b: step(base_opts.with_events(a, b)), args.steps, flush)
     ms = pct(steps, 50)
     flops = sizing.window_attention_flops(p.seq_lens, T, H, D)
     kern_ms = pct(kern, 50)
@@ -410,6 +417,7 @@ def run_prefill(args, s, dev):
                    "new_tokens_per_seq": T, "total_context_tokens": int(p.seq_lens.sum()),
                    "attended_keys": sizing.window_key_count(p.seq_lens, T),
                    "flops_per_step": flops, "block_size": s.block_size,
+                   "key_split_workspace_bytes": ws_bytes,
                    "arithmetic": "q and P rounded to bf16 on the matrix cores, fp32 accumulate",
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
@@ -450,7 +458,8 @@ def main():
     ap.add_argument("--tail-split", type=int, default=0,
                     help="tokens per split over the last --tail-span positions (0 = automatic)")
     ap.add_argument("--tail-span", type=int, default=-1)
-    ap.add_argument("--order", type=int, default=-1, help="MFMA dispatch order 0-4 (-1 automatic)")
+    ap.add_argument("--order", type=int, default=-1,
+                    help="dispatch order (-1 automatic): decode 0-4, prefill 5-7")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph in the timed region "
                          "(the kernel-time region stays eager)")

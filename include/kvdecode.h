@@ -122,9 +122,12 @@ typedef enum {
 } kvd_kernel;
 
 /* Order in which the (sequence, KV head, split) units of the matrix-core
- * kernels are dispatched (kvd_options.dispatch_order).  Results do not
- * depend on it: each unit writes its own partial and the merge reads them
- * in split order. */
+ * decode kernels, or the (sequence, KV head, query tile) workgroups of the
+ * prefill kernel, are dispatched (kvd_options.dispatch_order).  Results do
+ * not depend on it: each unit writes its own partial and the merge reads
+ * them in split order; each prefill workgroup writes its own rows.  Values
+ * 1-5 apply to the decode calls, 6-8 to gqa_prefill_attn; the other kind
+ * gives EINVAL. */
 typedef enum {
   KVD_ORDER_AUTO = 0,            /* the planner's choice */
   KVD_ORDER_SPLIT_HEAD_SEQ = 1,  /* split fastest, then KV head, then sequence */
@@ -137,7 +140,17 @@ typedef enum {
   KVD_ORDER_DEVICE_LIST = 4,
   /* the same list derived inside the split kernel without the extra launch
    * (batches of at most 64 sequences; ignored otherwise) */
-  KVD_ORDER_WAVE_LIST = 5
+  KVD_ORDER_WAVE_LIST = 5,
+  /* prefill: (sequence, KV head) pair fastest, the query tiles with the
+   * most keys first */
+  KVD_ORDER_PREFILL_PAIRS_FASTEST = 6,
+  /* prefill: the query tiles of one pair consecutive (most keys first),
+   * pairs in order */
+  KVD_ORDER_PREFILL_TILES_FASTEST = 7,
+  /* prefill: the order of 7, but each XCD (the device hands consecutive
+   * workgroups to its XCDs in turn) takes a contiguous run of it, so the
+   * query tiles that read one pair's keys share that XCD's L2 */
+  KVD_ORDER_PREFILL_XCD_RUNS = 8
 } kvd_dispatch_order;
 
 /*
@@ -374,26 +387,50 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
  * [KVGR] §4.2, here on the matrix cores).
  *
  * Arithmetic: q * scale and the softmax probabilities are rounded once to
- * bf16 for the matrix cores, accumulation is fp32, and each row's weights
- * are normalised by their own sum (the precision of FlashAttention-2 in
- * bf16: about 1e-3 relative per output element, where gqa_decode_attn_multi
- * keeps q and P to ~2^-17).  No workspace: each query row's output is
- * finished by one workgroup.
+ * bf16 for the matrix cores, accumulation is fp32, and each row is
+ * normalised by the fp32 sum of its probabilities (the precision of
+ * FlashAttention-2 in bf16: about 1e-3 relative per output element, where
+ * gqa_decode_attn_multi keeps q and P to ~2^-17).
+ *
+ * Key splits: a workgroup owns 128 query rows of one (sequence, KV head)
+ * pair.  When those workgroups are too few to fill the device (a short
+ * chunk after a long history), each row's keys [0, bound) are cut into
+ * splits of split_tokens (whole 32-token tiles); every split writes its
+ * normalised output and log2-sum-exp to the workspace, and the splits are
+ * merged by their log-sum-exp weights as in gqa_decode_attn (the same
+ * blockwise softmax algebra, [KVGR] §4.2).
  *
  *   q_rot      [B, T, H, D] fp32; out [B, T, H, D] fp32; lse [B, T, H] fp32
  *              (natural log) or NULL
  *   k_cache, v_cache, seq_lens, block_table, max_seq_len_host, scale
  *              as in gqa_decode_attn
- *   options    NULL, or kvd_options carrying only timing events (every
- *              other field 0: the prefill kernel has no split plan)
- * Errors: EINVAL, ERANGE as gqa_decode_attn (EINVAL also for plan fields in
- * options); EUNSUPPORTED for a cache dtype other than bf16 or n_query
- * outside [1, max_seq_len]; EHIP.
+ *   workspace  NULL (no key split unless options ask for one), or device
+ *              memory of gqa_prefill_workspace_size(shape, n_query,
+ *              max_seq_len_host, options) bytes, 256-byte aligned, owned by
+ *              the caller and not read before it is written; one workspace
+ *              per call in flight
+ *   options    NULL, or kvd_options with split_tokens (0 automatic, else a
+ *              multiple of 32; one split when it covers max_seq_len_host),
+ *              a prefill dispatch_order (6-8) and timing events; kernel and
+ *              the tail fields must be 0
+ * Errors: EINVAL, ERANGE as gqa_decode_attn (EINVAL also for decode plan
+ * fields in options); EWORKSPACE when the plan needs a workspace that is
+ * missing, smaller than the size above or misaligned; EUNSUPPORTED for a
+ * cache dtype other than bf16 or n_query outside [1, max_seq_len]; EHIP.
  */
 kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
-                            float* out, float* lse, const kvd_options* options, void* stream);
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            const kvd_options* options, void* stream);
+
+/*
+ * gqa_prefill_workspace_size -- bytes of workspace gqa_prefill_attn needs
+ * for these arguments with a non-NULL workspace: 0 when the plan has no
+ * key split, or when an argument is invalid (the call itself says which).
+ */
+size_t gqa_prefill_workspace_size(const kvd_shape* shape, int32_t n_query,
+                                  int32_t max_seq_len_host, const kvd_options* options);
 
 /*
  * gqa_decode_attn_multi_noalloc -- gqa_decode_attn_multi without a

@@ -11,7 +11,9 @@ __all__ = ["rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8", "gqa_deco
 
 def __getattr__(name):
     if name in __all__ or name in ("Options", "get_plan", "KvdError", "read_probe",
-                                   "v_cache_shape_int8", "gqa_decode_attn_noalloc"):
+                                   "v_cache_shape_int8", "gqa_decode_attn_noalloc",
+                                   "PREFILL_PAIRS_FASTEST", "PREFILL_TILES_FASTEST",
+                                   "PREFILL_XCD_RUNS", "prefill_workspace_size"):
         from . import _binding
         return getattr(_binding, name)
     raise AttributeError(name)

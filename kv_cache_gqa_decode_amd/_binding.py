@@ -55,6 +55,10 @@ class _COptions(ctypes.Structure):
                 ("event_start", ctypes.c_void_p), ("event_stop", ctypes.c_void_p)]
 
 
+# prefill dispatch orders (Options.dispatch_order of gqa_prefill_attn)
+PREFILL_PAIRS_FASTEST, PREFILL_TILES_FASTEST, PREFILL_XCD_RUNS = 5, 6, 7
+
+
 @dataclasses.dataclass(frozen=True)
 class Options:
     """Per-call plan overrides and timing events (kvd_options).
@@ -63,9 +67,11 @@ class Options:
     split_tokens    tokens per split (0 automatic; a multiple of 16 up to 8192)
     tail_split_tokens, tail_span_tokens
                     shorter splits over the last positions (0: none / automatic)
-    dispatch_order  None (automatic) or the unit order 0-4: 0 split fastest,
-                    1 head-sequence-split, 2 head-split-sequence, 3 device-built
-                    work list, 4 work list derived in the split kernel
+    dispatch_order  None (automatic), a decode unit order 0-4: 0 split
+                    fastest, 1 head-sequence-split, 2 head-split-sequence,
+                    3 device-built work list, 4 work list derived in the split
+                    kernel; or a prefill order: PREFILL_PAIRS_FASTEST,
+                    PREFILL_TILES_FASTEST, PREFILL_XCD_RUNS
     events          None, or (start, stop) torch.cuda.Event(enable_timing=True)
                     recorded on the call's stream around its main kernel
     """
@@ -107,6 +113,7 @@ def _options(opts: Optional[Options]):
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
             "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
+            "gqa_prefill_workspace_size",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
             "gqa_decode_attn_multi_noalloc")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
@@ -156,7 +163,10 @@ def load_library():
         lib.gqa_decode_attn_multi_noalloc.argtypes = [SP, I32, P, P, P, P, P, P, P, I32,
                                                       ctypes.c_float, P, P, OP, P]
         lib.gqa_prefill_attn.restype = I32
-        lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, OP, P]
+        lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, P,
+                                         ctypes.c_size_t, OP, P]
+        lib.gqa_prefill_workspace_size.restype = ctypes.c_size_t
+        lib.gqa_prefill_workspace_size.argtypes = [SP, I32, I32, OP]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32, OP]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -601,13 +611,16 @@ def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                      seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     want_lse: bool = True, options: Optional[Options] = None
+                     want_lse: bool = True, options: Optional[Options] = None,
+                     workspace: Optional[torch.Tensor] = None
                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Causal attention of T new tokens per sequence (a prompt or a chunk of
     one, already appended), q_rot [B, T, H, D], over a bf16 cache; query t
     attends the tokens j < seq_lens[b] - T + 1 + t.  q and P enter the matrix
-    cores as bf16.  ``options`` may carry timing events only.  Returns
-    (out [B, T, H, D], lse [B, T, H])."""
+    cores as bf16.  ``options`` may carry split_tokens (a multiple of 32), a
+    prefill dispatch order and timing events.  The key-split partials go to
+    ``workspace`` or to a per-call allocation of the size the library asks
+    for.  Returns (out [B, T, H, D], lse [B, T, H])."""
     lib = load_library()
     dev = k_cache.device
     B, T, H, D = (int(x) for x in q_rot.shape)
@@ -622,10 +635,27 @@ def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         raise ValueError("head_dim of q_rot and cache differ")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
     out, lse = _outputs((B, T), H, D, dev, out, lse, want_lse)
+    opts = _options(options)
+    if workspace is None:
+        nbytes = int(lib.gqa_prefill_workspace_size(ctypes.byref(shape), T, msl, opts))
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gqa_prefill_attn(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(seq_lens), _ptr(block_table), msl, _scale_arg(scale),
-                                _ptr(out), _ptr(lse), _options(options), _stream(dev)))
+                                _ptr(out), _ptr(lse), _ptr(workspace), wbytes, opts,
+                                _stream(dev)))
     return out, lse
+
+
+def prefill_workspace_size(batch: int, n_heads: int, n_query: int, k_cache: torch.Tensor,
+                           block_table: Optional[torch.Tensor] = None,
+                           max_seq_len: Optional[int] = None,
+                           options: Optional[Options] = None) -> int:
+    """Bytes of key-split workspace gqa_prefill_attn would take (0: no split)."""
+    shape = make_shape(batch, n_heads, k_cache, block_table)
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    return int(load_library().gqa_prefill_workspace_size(ctypes.byref(shape), int(n_query), msl,
+                                                         _options(options)))
 
 
 def get_plan(batch: int, n_heads: int, k_cache: torch.Tensor,

@@ -17,10 +17,12 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not yet queried
+std::atomic<int> g_xcc_count[kMaxDevices];  // 0 = not yet queried
 
 // Plan overrides and timing events of one call (kvd_options, resolved):
-// kernel -1 automatic, 0 VALU, 1 MFMA, 2 INT8 MFMA; order -1 automatic or a
-// grid order 0-4 (DecodeParams::grid_order).
+// kernel -1 automatic, 0 VALU, 1 MFMA, 2 INT8 MFMA; order -1 automatic, a
+// decode grid order 0-4 or a prefill grid order 5-7 (DecodeParams::grid_order
+// 0-2 of the prefill kernel).
 struct Tuning {
   int kernel = -1;
   int split = 0;          // tokens per split, 0 automatic
@@ -31,15 +33,22 @@ struct Tuning {
   hipEvent_t ev_stop = nullptr;
 };
 
-kvd_status read_options(const kvd_options* o, Tuning* t) {
+// prefill: the options of gqa_prefill_attn (its own dispatch orders; key
+// splits of whole 32-token tiles, any length)
+kvd_status read_options(const kvd_options* o, Tuning* t, bool prefill = false) {
   *t = Tuning{};
   if (!o) return KVD_OK;
   if (o->kernel < KVD_KERNEL_AUTO || o->kernel > KVD_KERNEL_INT8) return KVD_EINVAL;
-  if (o->split_tokens < 0 || o->split_tokens % 16 != 0 || o->split_tokens > kMaxChunk)
+  if (o->split_tokens < 0) return KVD_EINVAL;
+  if (prefill ? o->split_tokens % kPrefillTile != 0
+              : (o->split_tokens % 16 != 0 || o->split_tokens > kMaxChunk))
     return KVD_EINVAL;
   if (o->tail_split_tokens < 0 || o->tail_split_tokens % 16 != 0) return KVD_EINVAL;
   if (o->tail_span_tokens < 0) return KVD_EINVAL;
-  if (o->dispatch_order < KVD_ORDER_AUTO || o->dispatch_order > KVD_ORDER_WAVE_LIST)
+  if (o->dispatch_order < KVD_ORDER_AUTO || o->dispatch_order > KVD_ORDER_PREFILL_XCD_RUNS)
+    return KVD_EINVAL;
+  if (o->dispatch_order != KVD_ORDER_AUTO &&
+      (o->dispatch_order >= KVD_ORDER_PREFILL_PAIRS_FASTEST) != prefill)
     return KVD_EINVAL;
   if (o->reserved != 0) return KVD_EINVAL;
   if ((o->event_start == nullptr) != (o->event_stop == nullptr)) return KVD_EINVAL;
@@ -65,6 +74,19 @@ int device_cu_count(int* cu) {
   }
   *cu = v;
   return 0;
+}
+
+// XCDs of the current device (1 where the runtime does not say)
+int device_xcc_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+  int v = g_xcc_count[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || v <= 0)
+      v = 1;
+    g_xcc_count[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -300,6 +322,66 @@ kvd_status plan_for(const kvd_shape* shape, int32_t n_query, int32_t max_seq_len
   return make_plan(shape, max_seq_len_host, cu, tu, pl, n_query);
 }
 
+// Key splits of a prefill call.  Each workgroup owns 128 query rows of one
+// (sequence, KV head) pair and walks their keys; when those workgroups
+// would not fill two rounds of the device (three per CU), each row tile's
+// keys are cut into splits of whole tiles, at least 2048 keys each (so that
+// a workgroup's start and its partial write stay small beside its tiles),
+// written to the workspace as (o, log2 lse) and merged by lse_reduce.
+constexpr int kPrefillMinSplit = 2048;
+
+struct PfPlan {
+  int n_splits = 1;     // 1: no split, out and lse written directly
+  int chunk = 0;        // keys per split
+  size_t lse_offset = 0;
+  size_t workspace = 0;
+};
+
+// Validation shared by gqa_prefill_attn and its workspace size, and the plan
+// (may_split: a workspace is or will be given).
+kvd_status prefill_setup(const kvd_shape* s, int32_t T, int32_t max_len, const kvd_options* options,
+                         bool may_split, Tuning* tu, PfPlan* pl) {
+  *pl = PfPlan{};
+  kvd_status st = check_shape(s);
+  if (st != KVD_OK) return st;
+  if (s->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+  if (T < 1 || T > s->max_seq_len) return KVD_EUNSUPPORTED;
+  if (max_len < 0 || max_len > s->max_seq_len) return KVD_ERANGE;
+  st = read_options(options, tu, true);
+  if (st != KVD_OK) return st;
+  // the prefill kernel has no kernel choice and no tail splits
+  if (tu->kernel >= 0 || tu->tail_split != 0 || tu->tail_span >= 0) return KVD_EINVAL;
+  const int64_t R = s->n_heads / s->n_kv_heads;
+  const int64_t nqt = (static_cast<int64_t>(T) * R + kPrefillRows - 1) / kPrefillRows;
+  const int64_t wgs = nqt * s->batch * s->n_kv_heads;
+  const int64_t rows = static_cast<int64_t>(s->batch) * T * s->n_heads;
+  if (wgs > 0x7fffffff || rows > 0x7fffffff) return KVD_EUNSUPPORTED;
+  int64_t chunk = 0;
+  if (tu->split > 0) {
+    chunk = tu->split;
+  } else if (may_split && wgs > 0 && max_len > kPrefillMinSplit) {
+    int cu = 0;
+    if (device_cu_count(&cu) != 0) return KVD_EHIP;
+    const int64_t target = 2 * 3 * static_cast<int64_t>(cu);
+    if (wgs < target) {
+      const int64_t n = (target + wgs - 1) / wgs;
+      chunk = (max_len + n - 1) / n;
+      if (chunk < kPrefillMinSplit) chunk = kPrefillMinSplit;
+      chunk = (chunk + kPrefillTile - 1) / kPrefillTile * kPrefillTile;
+    }
+  }
+  if (chunk > 0 && max_len > chunk) {
+    const int64_t n = (max_len + chunk - 1) / chunk;
+    if (wgs * n > 0x7fffffff) return KVD_EUNSUPPORTED;
+    pl->n_splits = static_cast<int>(n);
+    pl->chunk = static_cast<int>(chunk);
+    const size_t parts = static_cast<size_t>(rows) * pl->n_splits;
+    pl->lse_offset = (parts * s->head_dim * sizeof(float) + 255) / 256 * 256;
+    pl->workspace = pl->lse_offset + (parts * sizeof(float) + 255) / 256 * 256;
+  }
+  return KVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -461,28 +543,33 @@ kvd_status gqa_decode_attn_multi(const kvd_shape* shape, int32_t n_query, const 
                      stream, n_query);
 }
 
+size_t gqa_prefill_workspace_size(const kvd_shape* shape, int32_t n_query,
+                                  int32_t max_seq_len_host, const kvd_options* options) {
+  Tuning tu;
+  PfPlan pl;
+  if (prefill_setup(shape, n_query, max_seq_len_host, options, true, &tu, &pl) != KVD_OK) return 0;
+  return pl.workspace;
+}
+
 kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float* q_rot,
                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
-                            float* out, float* lse, const kvd_options* options, void* stream) {
-  kvd_status st = check_shape(shape);
-  if (st != KVD_OK) return st;
-  if (shape->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
-  if (n_query < 1 || n_query > shape->max_seq_len) return KVD_EUNSUPPORTED;
+                            float* out, float* lse, void* workspace, size_t workspace_bytes,
+                            const kvd_options* options, void* stream) {
   if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
   if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return KVD_EINVAL;
   if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
   if (!std::isfinite(scale)) return KVD_EINVAL;
-  const bool paged = shape->block_size != 0;
-  if (paged != (block_table != nullptr)) return KVD_EINVAL;
-  if (max_seq_len_host < 0 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  if (shape && (shape->block_size != 0) != (block_table != nullptr)) return KVD_EINVAL;
   Tuning tu;
-  st = read_options(options, &tu);
+  PfPlan pl;
+  kvd_status st = prefill_setup(shape, n_query, max_seq_len_host, options, workspace != nullptr,
+                                &tu, &pl);
   if (st != KVD_OK) return st;
-  // the prefill kernel has no split plan: only the timing events apply
-  if (tu.kernel >= 0 || tu.split != 0 || tu.tail_split != 0 || tu.tail_span >= 0 || tu.order >= 0)
-    return KVD_EINVAL;
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace ||
+                           (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return KVD_EWORKSPACE;
   if (shape->batch == 0) return KVD_OK;
   DecodeParams p{};
   p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
@@ -493,8 +580,23 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.qscale = log2_scale(scale, shape->head_dim);
-  const Launch l{static_cast<hipStream_t>(stream), tu.ev_start, tu.ev_stop};
-  return launch_prefill_mfma(p, paged, l) == hipSuccess ? KVD_OK : KVD_EHIP;
+  p.n_xcd = device_xcc_count();
+  // -1: the launcher's choice
+  p.grid_order = tu.order >= 0 ? tu.order - (KVD_ORDER_PREFILL_PAIRS_FASTEST - 1) : -1;
+  p.n_splits = pl.n_splits;
+  p.direct = pl.n_splits == 1 ? 1 : 0;
+  if (!p.direct) {
+    // uniform splits (n_big = n_splits), as the merge counts them
+    p.chunk = p.chunk2 = pl.chunk;
+    p.n_big = pl.n_splits;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lse_offset);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch l{s, tu.ev_start, tu.ev_stop};
+  if (launch_prefill_mfma(p, shape->block_size != 0, l) != hipSuccess) return KVD_EHIP;
+  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
+  return KVD_OK;
 }
 
 }  // extern "C"

@@ -46,6 +46,7 @@ struct DecodeParams {
                             // 4 the same list derived by each wave (B <= 64)
   int32_t* units;           // work list (grid_order 3): b | split << 16, in the workspace
   int32_t* n_units;         // its length
+  int32_t n_xcd;            // prefill, grid_order 2: XCDs the workgroups are dealt to
 };
 
 struct RopeParams {
@@ -100,6 +101,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool page
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l);
 hipError_t launch_decode_i8(const DecodeParams& p, bool paged, const Launch& l);
 // causal prefill of p.T new tokens per sequence (p.qscale, no splits)
+// n_splits 1: out and lse directly; more: (o, log2 lse) per key split into
+// part_o / part_lse, merged by launch_lse_reduce
 hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, const Launch& l);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_build_units(const DecodeParams& p, hipStream_t stream);
@@ -110,6 +113,8 @@ constexpr int kMfmaWaves = 4;
 constexpr int kMfmaTileTokens = 32;   // tokens per wave per iteration
 constexpr int kI8TileTokens = 64;     // INT8 kernel: tokens per wave per iteration
 constexpr int kMaxChunk = 8192;       // tokens per split, upper bound
+constexpr int kPrefillRows = 128;     // prefill: query rows per workgroup
+constexpr int kPrefillTile = 32;      // prefill: keys per tile (key splits are whole tiles)
 constexpr int kMfmaMaxChunk = kMaxChunk;
 
 // ------------------------------------------------------------ device helpers

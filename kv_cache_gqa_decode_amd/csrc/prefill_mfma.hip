@@ -42,6 +42,7 @@ constexpr int kPfWaves = 4;
 constexpr int kPfCols = 32;                      // query rows per wave (two column blocks)
 constexpr int kPfRows = kPfWaves * kPfCols;      // query rows per workgroup
 constexpr int kPfTT = 32;                        // key tokens per tile
+static_assert(kPfRows == kPrefillRows && kPfTT == kPrefillTile, "the host plans with these");
 
 template <int D>
 struct PfGeo {
@@ -93,9 +94,14 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
   k[1] = __builtin_bit_cast(bf16x8, r1);
 }
 
-// Workgroup x: query-row tile nqt - 1 - x / (B G) (the tiles with the most
-// keys first), sequence and KV head from x mod B G.  Held to 168 registers,
-// three workgroups share a CU (measured 18% faster than two).
+// Workgroup x owns one query-row tile of one unit -- a (sequence, KV head)
+// pair, or with key splits a (pair, split) -- whose tiles go most keys
+// first.  U units in all.  grid_order 0: unit x mod U, tile nqt - 1 - x / U.
+// 1: unit x / nqt, tile nqt - 1 - x mod nqt (a unit's tiles together).
+// 2: the order of 1 cut into n_xcd contiguous runs, run k taken by the
+// workgroups x = k mod n_xcd, which the device sends to one XCD, so that a
+// unit's tiles, which all read its keys, share one L2.  Held to 168
+// registers, three workgroups share a CU (measured 18% faster than two).
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_kernel(DecodeParams p) {
@@ -107,8 +113,17 @@ void prefill_kernel(DecodeParams p) {
   const int R = p.R, T = p.T;
   const int64_t ncols = static_cast<int64_t>(T) * R;
   const int nqt = static_cast<int>((ncols + kPfRows - 1) / kPfRows);
-  const int bg = static_cast<int>(blockIdx.x % (p.B * p.G));
-  const int qt = nqt - 1 - static_cast<int>(blockIdx.x / (p.B * p.G));
+  const int nsplit = p.n_splits;                   // 1: no key split
+  const int64_t units = static_cast<int64_t>(p.B) * p.G * nsplit;
+  int64_t lin = blockIdx.x;
+  if (p.grid_order == 2) {
+    const int64_t nx = p.n_xcd, nwg = gridDim.x;
+    const int64_t k = lin % nx, per = nwg / nx, rem = nwg % nx;
+    lin = k * per + (k < rem ? k : rem) + lin / nx;
+  }
+  const int unit = static_cast<int>(p.grid_order == 0 ? lin % units : lin / nqt);
+  const int qt = nqt - 1 - static_cast<int>(p.grid_order == 0 ? lin / units : lin % nqt);
+  const int bg = unit / nsplit, split = unit - bg * nsplit;
   const int g = bg % p.G, b = bg / p.G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -124,6 +139,16 @@ void prefill_kernel(DecodeParams p) {
   kmax = kmax < L ? kmax : L;
   const int64_t cw = c0 + wave * kPfCols;
   const int wbound = win + static_cast<int>((cw < ncols ? cw : c_last) / R);
+  // this workgroup's keys [k_lo, k_hi): a split's whole tiles.  A split at
+  // or past the sequence's end writes nothing (the merge reads only the
+  // splits that hold its tokens); one below it writes every row, empty
+  // ones as (0, -inf).
+  int k_lo = 0, k_hi = kmax;
+  if (nsplit > 1) {
+    if (split >= (L + p.chunk - 1) / p.chunk) return;
+    k_lo = split * p.chunk;
+    k_hi = k_lo + p.chunk < kmax ? k_lo + p.chunk : kmax;
+  }
 
   // the lane's query rows: column nb*16 + n of the wave
   int cbound[NB];
@@ -256,11 +281,13 @@ void prefill_kernel(DecodeParams p) {
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int nkt = kmax > 0 ? (kmax + kPfTT - 1) / kPfTT : 0;
+  // key tiles [kt_lo, nkt)
+  const int nkt = k_hi > k_lo ? (k_hi + kPfTT - 1) / kPfTT : 0;
+  const int kt_lo = k_lo / kPfTT;
   TileSrc cur;
-  if (nkt > 0) {
-    cur = tile_src(0);
-    issue(cur, 0);
+  if (nkt > kt_lo) {
+    cur = tile_src(kt_lo * kPfTT);
+    issue(cur, kt_lo & 1);
   }
   // One key tile: wait for its copies, request the next tile's, then scores,
   // online softmax and P V.  MASK (a constant at each call) says whether the
@@ -358,7 +385,7 @@ void prefill_kernel(DecodeParams p) {
   // rest, at most two per wave, take the masked body.
   const int wg_bound = win + static_cast<int>(c0 / R);
   const int n_full = wg_bound >= kPfTT ? (wg_bound / kPfTT < nkt ? wg_bound / kPfTT : nkt) : 0;
-  int kt = 0;
+  int kt = kt_lo;
   for (; kt < n_full; ++kt) tile(kt, std::false_type{});
   for (; kt < nkt; ++kt) tile(kt, std::true_type{});
 
@@ -372,22 +399,49 @@ void prefill_kernel(DecodeParams p) {
   for (int nb = 0; nb < NB; ++nb) {
     if (!real[nb]) continue;
     const float inv = lx[nb] > 0.f ? 1.f / lx[nb] : 0.f;
-    float* dst = p.out + qrow[nb] * D + 4 * grp;
+    const float lse2 = lx[nb] > 0.f ? m[nb] + log2f(lx[nb]) : kNegInf;
+    if (nsplit == 1) {
+      float* dst = p.out + qrow[nb] * D + 4 * grp;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
-    if (grp == 0 && p.lse)
-      p.lse[qrow[nb]] = lx[nb] > 0.f ? (m[nb] + log2f(lx[nb])) * 0.69314718055994531f : kNegInf;
+      for (int cb = 0; cb < CB; ++cb)
+        *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
+      if (grp == 0 && p.lse) p.lse[qrow[nb]] = lse2 * 0.69314718055994531f;
+    } else {
+      // the split's partial: normalised output and log2-sum-exp
+      const int64_t slot = qrow[nb] * nsplit + split;
+      float* dst = p.part_o + slot * D + 4 * grp;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
+      if (grp == 0) p.part_lse[slot] = lse2;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, const Launch& l) {
+// grid_order -1 chooses.  Fewer (sequence, KV head) pairs than XCDs: pairs
+// fastest, which deals every pair's tiles over the XCDs.  Otherwise a pair's
+// query tiles go together: with few of them (short chunks) round-robin over
+// the XCDs, every XCD taking an equal share of every pair, since the pairs'
+// lengths differ; with many, in contiguous runs per XCD, so that a pair's
+// keys are fetched into one L2 instead of eight.  Measured on 64 ragged
+// sequences with 8 KV heads: 512-token chunks 3.80 / 3.05 / 3.25 ms (orders
+// 0 / 1 / 2), 2048-token chunks 12.6 / 10.5 / 11.0 ms, 8192-token chunks
+// 54.9 / 49.5 / 42.6 ms; a 32K prompt with 32 KV heads 81.0 / 84.1 / 76.2 ms.
+hipError_t launch_prefill_mfma(const DecodeParams& p_in, bool paged, const Launch& l) {
+  DecodeParams p = p_in;
   if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
+  if (p.n_xcd < 1 || p.grid_order < -1 || p.grid_order > 2 || p.n_splits < 1) return hipErrorInvalidValue;
+  if (p.n_splits > 1 && (p.chunk < kPfTT || p.chunk % kPfTT != 0 || !p.part_o || !p.part_lse))
+    return hipErrorInvalidValue;
   const int64_t ncols = static_cast<int64_t>(p.T) * p.R;
   const int64_t nqt = (ncols + kPfRows - 1) / kPfRows;
-  const int64_t wgs = nqt * p.B * p.G;
+  const int64_t units = static_cast<int64_t>(p.B) * p.G * p.n_splits;
+  // with key splits the units hold equal key counts: runs per XCD
+  if (p.grid_order < 0)
+    p.grid_order = units < p.n_xcd ? 0 : (p.n_splits > 1 || nqt > 64 ? 2 : 1);
+  const int64_t wgs = nqt * units;
   if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs));
   void (*k)(DecodeParams) = p.D == 64 ? (paged ? prefill_kernel<64, true> : prefill_kernel<64, false>)

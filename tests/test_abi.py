@@ -170,9 +170,9 @@ def test_multi_calls_validate(lib):
 
 
 def prefill(lib, sh, T, q=FAKE, lens=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000),
-            opts=None):
+            opts=None, ws=None, ws_bytes=0):
     return lib.gqa_prefill_attn(ctypes.byref(sh) if sh is not None else None, T, q, FAKE, FAKE,
-                                lens, table, msl, 0.125, out, None,
+                                lens, table, msl, 0.125, out, None, ws, ws_bytes,
                                 None if opts is None else ctypes.byref(opts), None)
 
 
@@ -188,11 +188,48 @@ def test_prefill_validates(lib):
     assert prefill(lib, shape(), 4, table=FAKE) == EINVAL
     assert prefill(lib, shape(), 4, msl=65) == ERANGE
     assert prefill(lib, shape(batch=0), 64) == OK
-    # options: timing events only (both or neither); no plan fields
+    # options: key splits of whole 32-token tiles, a prefill dispatch order
+    # (6-8) and timing events (both or neither); no kernel or tail fields,
+    # no decode order
     assert prefill(lib, shape(batch=0), 4, opts=B._COptions()) == OK
-    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(split_tokens=64)) == EINVAL
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(split_tokens=64)) == OK
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(split_tokens=16)) == EINVAL
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(split_tokens=-32)) == EINVAL
+    assert prefill(lib, shape(batch=0), 4, opts=B._COptions(tail_split_tokens=32)) == EINVAL
     assert prefill(lib, shape(batch=0), 4, opts=B._COptions(kernel=2)) == EINVAL
     assert prefill(lib, shape(batch=0), 4, opts=B._COptions(event_start=0x10)) == EINVAL
+    for order in (6, 7, 8):
+        assert prefill(lib, shape(batch=0), 4, opts=B._COptions(dispatch_order=order)) == OK
+    for order in (1, 2, 3, 4, 5, 9, -1):
+        assert prefill(lib, shape(batch=0), 4, opts=B._COptions(dispatch_order=order)) == EINVAL
+
+
+def test_prefill_key_split_workspace(lib):
+    """A requested key split sizes its partials, (o[D], log2 lse) per query
+    row and split, each array 256-byte aligned; without that workspace the
+    call is refused before anything is enqueued."""
+    O = B._COptions
+    sh = shape(batch=2, n_heads=8, n_kv_heads=2, head_dim=64, max_seq_len=256)
+    T = 4
+    rows = 2 * T * 8
+    up = lambda x: (x + 255) // 256 * 256
+    for split, msl, n in ((64, 256, 4), (96, 256, 3), (32, 33, 2)):
+        size = lib.gqa_prefill_workspace_size(ctypes.byref(sh), T, msl,
+                                              ctypes.byref(O(split_tokens=split)))
+        assert size == up(rows * n * 64 * 4) + up(rows * n * 4), (split, msl)
+        assert prefill(lib, sh, T, msl=msl, opts=O(split_tokens=split)) == EWORKSPACE
+        assert prefill(lib, sh, T, msl=msl, opts=O(split_tokens=split), ws=FAKE,
+                       ws_bytes=size - 1) == EWORKSPACE
+        assert prefill(lib, sh, T, msl=msl, opts=O(split_tokens=split),
+                       ws=ctypes.c_void_p(0x1010), ws_bytes=size) == EWORKSPACE   # misaligned
+    # one split covers the window: no workspace
+    assert lib.gqa_prefill_workspace_size(ctypes.byref(sh), T, 64,
+                                          ctypes.byref(O(split_tokens=64))) == 0
+    # invalid arguments report 0
+    assert lib.gqa_prefill_workspace_size(ctypes.byref(sh), T, 64,
+                                          ctypes.byref(O(split_tokens=48))) == 0
+    assert lib.gqa_prefill_workspace_size(ctypes.byref(sh), T, 257, None) == 0
+    assert lib.gqa_prefill_workspace_size(None, T, 64, None) == 0
 
 
 def test_options_validation(lib):
@@ -203,7 +240,8 @@ def test_options_validation(lib):
     assert attn_m(lib, empty, 1, opts=O()) == OK                       # zeros: automatic
     for bad in (O(kernel=-1), O(kernel=4), O(split_tokens=24), O(split_tokens=-16),
                 O(split_tokens=8192 + 16), O(tail_split_tokens=8), O(tail_span_tokens=-1),
-                O(dispatch_order=-1), O(dispatch_order=6), O(reserved=1),
+                O(dispatch_order=-1), O(dispatch_order=6), O(dispatch_order=8),
+                O(dispatch_order=9), O(reserved=1),
                 O(event_start=0x10), O(event_stop=0x10)):
         assert attn_m(lib, empty, 1, opts=bad) == EINVAL
         assert lib.gqa_decode_workspace_size_multi(ctypes.byref(shape()), 1, 32,

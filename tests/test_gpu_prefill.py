@@ -24,22 +24,22 @@ from tests.test_gpu_multi import oracle_window, _bits
 pytestmark = pytest.mark.gpu
 
 
-def gpu_prefill(t, s: W.Spec, max_len: int, style="interleaved"):
+def gpu_prefill(t, s: W.Spec, max_len: int, style="interleaved", options=None):
     q_rot = kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                      t["positions"], t["block_table"], base=s.rope_base,
                                      style=style)
     out, lse = kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
-                                    t["block_table"], max_seq_len=max_len)
+                                    t["block_table"], max_seq_len=max_len, options=options)
     torch.cuda.synchronize()
     return q_rot, out, lse
 
 
-def check_prefill(p: W.Problem, what="", units=None, style="interleaved"):
+def check_prefill(p: W.Problem, what="", units=None, style="interleaved", options=None):
     dev = device()
     s = p.spec
     print(f"[prefill] {what}", flush=True)
     t = upload(p, dev)
-    q_rot, out, lse = gpu_prefill(t, s, p.max_len, style=style)
+    q_rot, out, lse = gpu_prefill(t, s, p.max_len, style=style, options=options)
     oq, oo, ol, okc, ovc = oracle_window(p, style=style, units=units)
     assert torch.equal(_bits(t["k_cache"]), _bits(W.as_torch(okc, dev))), f"{what}: K cache"
     assert torch.equal(_bits(t["v_cache"]), _bits(W.as_torch(ovc, dev))), f"{what}: V cache"
@@ -93,6 +93,67 @@ def test_gqa_ratios(n_rep):
     s = _spec(2, H, H // n_rep, 128, 640)
     p = W.make_window(s, 150, lengths=np.array([150, 600], np.int32))
     check_prefill(p, what=f"n_rep={n_rep}")
+
+
+ORDERS = [kvd.PREFILL_PAIRS_FASTEST, kvd.PREFILL_TILES_FASTEST, kvd.PREFILL_XCD_RUNS]
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("order", ORDERS)
+@pytest.mark.parametrize("B,G,T,paged", [(3, 3, 300, False), (1, 1, 300, True),
+                                         (1, 2, 40, False), (5, 8, 64, True)])
+def test_dispatch_orders(order, B, G, T, paged, split):
+    """Every workgroup order computes the same rows, with and without key
+    splits: unit counts that are not a multiple of the XCD count, one pair,
+    fewer workgroups than XCDs."""
+    H = 4 * G
+    lens = np.array([T + 37 * i for i in range(B)], np.int32)
+    s = _spec(B, H, G, 128, 512, paged)
+    p = W.make_window(s, T, lengths=lens)
+    check_prefill(p, what=f"order {order} split {split} B={B} G={G} T={T} paged={paged}",
+                  options=kvd.Options(dispatch_order=order, split_tokens=split))
+
+
+@pytest.mark.parametrize("split", [32, 96, 2048])
+@pytest.mark.parametrize("paged,block_size", [(False, 16), (True, 32)])
+def test_key_split_forced(split, paged, block_size):
+    """Key splits of `split` tokens merged by their log-sum-exp: rows whose
+    bound lies before a split's start (empty partials), sequences that end
+    before the longest (splits past their end are never read), a sequence
+    with no history, split boundaries inside the window."""
+    T = 100
+    lens = np.array([T, T + 31, T + 500, 1024, 1200], np.int32)
+    s = _spec(lens.size, 32, 8, 128, 1280, paged, block_size)
+    p = W.make_window(s, T, lengths=lens)
+    check_prefill(p, what=f"split {split} paged={paged}/{block_size}",
+                  options=kvd.Options(split_tokens=split))
+
+
+def test_key_split_automatic_long_history():
+    """A 64-token chunk after a 20K history, one sequence and two KV heads:
+    four query tiles cannot fill the device, so the library splits the keys
+    (it asks for a workspace); every row against the oracle."""
+    T, L = 64, 20480
+    s = _spec(1, 8, 2, 128, L)
+    p = W.make_window(s, T, lengths=np.array([L], np.int32))
+    k = torch.empty((1, L, 2, 128), dtype=torch.bfloat16, device=device())
+    assert kvd.prefill_workspace_size(1, 8, T, k, max_seq_len=L) > 0
+    check_prefill(p, what="chunk 64 after 20K, automatic split")
+
+
+def test_key_split_128k_history_sampled():
+    """A 512-token chunk after a 128K history at the 128K workload's head
+    shape (H 32, G 8, D 128), split automatically: 1024 sampled rows (the
+    first and last tokens of every query tile among them) against the
+    oracle, caches in full."""
+    s = W.spec("c5", q_gain=2.0)
+    T, L = 512, s.max_seq_len
+    p = W.make_window(s, T, lengths=np.array([L], np.int32))
+    rng = np.random.default_rng(72)
+    edges = np.r_[np.arange(0, T, 128 // 4), np.arange(31, T, 128 // 4)]
+    ts = np.r_[edges, rng.integers(0, T, 1024 - edges.size)]
+    units = [(0, int(t), int(h)) for t, h in zip(ts, rng.integers(0, s.n_heads, ts.size))]
+    check_prefill(p, units=units, what="chunk 512 after 128K, 1024 rows")
 
 
 @pytest.mark.parametrize("q_gain", [1.0, 8.0, 32.0])
