@@ -25,6 +25,15 @@ saturating); attention reads scale * code.  Tokens are grouped by 16 and
 each group holds, per KV head, the 16 K rows and the V block transposed
 (``Geometry.cache_shape`` / ``Geometry.v_cache_shape``).
 
+Mixed precision ([KVGR] §4.3 names caches that keep the most recent tokens at
+high precision and quantise the older history): the W newest tokens of each
+sequence sit in bf16 rings ``k_recent`` / ``v_recent`` [B, W, G, D] (token p
+in row p mod W), every older token in an INT8 cache as above.  The append of
+the token at position P first moves token P - W (when P >= W) from its ring
+row into the INT8 cache as codes of its bf16 values, then writes the new
+token into that row (``rope_append_mixed``); attention reads the last W of
+the L attended tokens from the rings (``decode_attn_mixed``).
+
 Arrays: bf16 data are passed as ``uint16`` bit patterns; fp32 as ``float32``;
 fp64 as ``float64``.  Pages cited by title:
   [KVGR] "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践"
@@ -97,6 +106,14 @@ def _load():
         lib.kvo_decode_attn_units_mq.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P,
                                                  P, P, P, P, ctypes.c_double, P, P,
                                                  ctypes.c_int64, P, P, ctypes.c_int]
+        lib.kvo_rope_append_mixed.restype = ctypes.c_int
+        lib.kvo_rope_append_mixed.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P, P,
+                                              P, P, P, P, P, P, P, P, ctypes.c_double,
+                                              ctypes.c_int]
+        lib.kvo_decode_attn_mixed.restype = ctypes.c_int
+        lib.kvo_decode_attn_mixed.argtypes = [ctypes.POINTER(_Shape), ctypes.c_int, P, P, P, P,
+                                              P, P, P, P, P, ctypes.c_double, P, P,
+                                              ctypes.c_int64, P, P, ctypes.c_int]
         lib.kvo_decode_attn.restype = ctypes.c_int
         lib.kvo_decode_attn.argtypes = [ctypes.POINTER(_Shape), P, P, P, P, P,
                                         ctypes.c_double, P, P, P, ctypes.c_int]
@@ -363,6 +380,87 @@ def decode_attn_units(geom: Geometry, q_rot, k_cache, v_cache, seq_lens, units,
                                           _ptr(block_table), float(scale), _ptr(ub), _ptr(uh),
                                           n, _ptr(out), _ptr(lse),
                                           n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("a referenced cache slot does not exist")
+    return out, lse
+
+
+def recent_shape(geom: Geometry, window: int):
+    """Shape of a bf16 ring of the ``window`` newest tokens: [B, W, G, D]."""
+    return (geom.batch, int(window), geom.n_kv_heads, geom.head_dim)
+
+
+def rope_append_mixed(geom: Geometry, window, q, k_new, v_new, k_cache, v_cache, k_recent,
+                      v_recent, positions, block_table=None, base=10000.0,
+                      style="interleaved", k_scale=None, v_scale=None):
+    """The append into a mixed-precision cache (module docstring): geom
+    describes the INT8 cache; k_recent / v_recent are uint16 bf16 rings
+    [B, W, G, D].  Everything is modified in place; returns q_rot [B, H, D]
+    fp64.  Raises ValueError if a position or a block id does not exist."""
+    if geom.dtype != "i8":
+        raise ValueError("the history of a mixed cache is INT8")
+    B, H, G, D = geom.batch, geom.n_heads, geom.n_kv_heads, geom.head_dim
+    if q is not None:
+        _need(q, np.uint16, "q", (B, H, D))
+    _need(k_new, np.uint16, "k_new", (B, G, D))
+    _need(v_new, np.uint16, "v_new", (B, G, D))
+    _need(k_cache, np.int8, "k_cache", geom.cache_shape())
+    _need(v_cache, np.int8, "v_cache", geom.v_cache_shape())
+    _need(k_recent, np.uint16, "k_recent", recent_shape(geom, window))
+    _need(v_recent, np.uint16, "v_recent", recent_shape(geom, window))
+    _need(positions, np.int32, "positions", (B,))
+    if geom.block_size:
+        _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    ks, vs = _scales(geom, k_scale, v_scale)
+    q_rot = np.zeros((B, H, D), np.float64)
+    rc = _load().kvo_rope_append_mixed(ctypes.byref(geom._c()), int(window), _ptr(q),
+                                       _ptr(k_new), _ptr(v_new), _ptr(q_rot), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(ks), _ptr(vs), _ptr(k_recent),
+                                       _ptr(v_recent), _ptr(positions), _ptr(block_table),
+                                       float(base), _STYLE_CODE[style])
+    if rc != 0:
+        raise ValueError("position or block id out of range")
+    return q_rot
+
+
+def decode_attn_mixed(geom: Geometry, window, q_rot, k_cache, v_cache, k_recent, v_recent,
+                      seq_lens, block_table=None, scale=None, k_scale=None, v_scale=None,
+                      units=None, n_threads=None):
+    """fp64 attention over a mixed-precision cache: every (b, h), or the
+    listed (b, h) pairs; returns (out, lse) of shape [B, H, D], [B, H] or
+    [n, D], [n]."""
+    if geom.dtype != "i8":
+        raise ValueError("the history of a mixed cache is INT8")
+    B, H, D = geom.batch, geom.n_heads, geom.head_dim
+    _need(q_rot, np.float64, "q_rot", (B, H, D))
+    _need(k_cache, np.int8, "k_cache", geom.cache_shape())
+    _need(v_cache, np.int8, "v_cache", geom.v_cache_shape())
+    _need(k_recent, np.uint16, "k_recent", recent_shape(geom, window))
+    _need(v_recent, np.uint16, "v_recent", recent_shape(geom, window))
+    _need(seq_lens, np.int32, "seq_lens", (B,))
+    if geom.block_size:
+        _need(block_table, np.int32, "block_table", (B, geom.max_blocks_per_seq))
+    ks, vs = _scales(geom, k_scale, v_scale)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ub = uh = None
+    if units is None:
+        n = B * H
+        out = np.zeros((B, H, D), np.float64)
+        lse = np.zeros((B, H), np.float64)
+    else:
+        u = np.asarray(units, dtype=np.int32).reshape(-1, 2)
+        if ((u[:, 0] < 0) | (u[:, 0] >= B) | (u[:, 1] < 0) | (u[:, 1] >= H)).any():
+            raise ValueError("unit out of range")
+        ub, uh = np.ascontiguousarray(u[:, 0]), np.ascontiguousarray(u[:, 1])
+        n = u.shape[0]
+        out = np.zeros((n, D), np.float64)
+        lse = np.zeros((n,), np.float64)
+    rc = _load().kvo_decode_attn_mixed(ctypes.byref(geom._c()), int(window), _ptr(q_rot),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(ks), _ptr(vs),
+                                       _ptr(k_recent), _ptr(v_recent), _ptr(seq_lens),
+                                       _ptr(block_table), float(scale), _ptr(ub), _ptr(uh), n,
+                                       _ptr(out), _ptr(lse), n_threads or default_threads())
     if rc != 0:
         raise ValueError("a referenced cache slot does not exist")
     return out, lse

@@ -56,6 +56,18 @@
  * ([G][16][D]: element (pos, g, d) at ((r * G + g) * 16 + pos % 16) * D + d)
  * and the V block transposed ([G][D][16]: at ((r * G + g) * D + d) * 16 +
  * pos % 16).
+ *
+ * Mixed precision (the *_mixed functions): [KVGR] §4.3 also names caches that
+ * keep the most recent tokens at high precision and quantise the older
+ * history.  Here the W newest tokens of each sequence sit in a bf16 ring
+ * [B, W, G, D] (token p in row p mod W) and every older token in an INT8
+ * cache as above, at its own position.  Appending the token at position P
+ * (one per sequence): when P >= W, token P - W leaves the ring -- its stored
+ * bf16 K and V values become codes (nearest to value / scale, as for a new
+ * INT8 element) at position P - W of the INT8 cache -- and then the rotated k
+ * (one rounding to bf16) and v_new take ring row P mod W.  Attention over L
+ * tokens reads token j from the ring when j >= L - W, else from the INT8
+ * cache.
  */
 #include <math.h>
 #include <pthread.h>
@@ -295,6 +307,64 @@ int kvo_rope_append_mq(const kvo_shape* sh, int T, const void* q, const void* k_
                           positions, block_table, base, style);
 }
 
+/* The mixed-precision append (file header): sh describes the INT8 cache,
+ * k_recent / v_recent the bf16 rings [B, window, G, D] (bit patterns).
+ * Returns 0, or -1 when a position is outside [0, max_seq_len) (that
+ * sequence's cache update is skipped) or the INT8 slot of a leaving token
+ * does not exist (that token's codes are not written; the ring row is still
+ * overwritten). */
+int kvo_rope_append_mixed(const kvo_shape* sh, int window, const void* q, const void* k_new,
+                          const void* v_new, double* q_rot, int8_t* k_cache, int8_t* v_cache,
+                          const float* k_scale, const float* v_scale, uint16_t* k_recent,
+                          uint16_t* v_recent, const int32_t* positions,
+                          const int32_t* block_table, double base, int style) {
+  if (sh->dtype != KVO_I8 || window < 1) return -2;
+  const int H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
+  int rc = 0;
+  double* x = (double*)malloc(sizeof(double) * D);
+  double* y = (double*)malloc(sizeof(double) * D);
+  for (int b = 0; b < sh->batch; ++b) {
+    const int64_t P = positions[b];
+    if (q != NULL) {
+      for (int h = 0; h < H; ++h) {
+        int64_t base_i = ((int64_t)b * H + h) * D;
+        for (int d = 0; d < D; ++d) x[d] = load_elem(q, KVO_BF16, base_i + d);
+        kvo_rope_rotate(x, y, D, (double)P, base, style);
+        for (int d = 0; d < D; ++d) q_rot[base_i + d] = y[d];
+      }
+    }
+    if (P < 0 || P >= sh->max_seq_len) { rc = -1; continue; }
+    for (int g = 0; g < G; ++g) {
+      const int64_t ring = (((int64_t)b * window + P % window) * G + g) * D;
+      if (P >= window) {
+        /* token P - window leaves the ring for the INT8 cache */
+        const int64_t old = P - window;
+        int64_t row = cache_row(sh, block_table, b, old, g);
+        if (row < 0) {
+          rc = -1;
+        } else {
+          for (int d = 0; d < D; ++d) {
+            k_cache[kq_index(sh, b, old, g, d, row)] =
+                (int8_t)kvo_quantize_i8(bf16_bits_to_double(k_recent[ring + d]), k_scale[g]);
+            v_cache[vt_index(sh, b, old, g, d, row)] =
+                (int8_t)kvo_quantize_i8(bf16_bits_to_double(v_recent[ring + d]), v_scale[g]);
+          }
+        }
+      }
+      int64_t src = ((int64_t)b * G + g) * D;
+      for (int d = 0; d < D; ++d) x[d] = load_elem(k_new, KVO_BF16, src + d);
+      kvo_rope_rotate(x, y, D, (double)P, base, style);
+      for (int d = 0; d < D; ++d) {
+        k_recent[ring + d] = kvo_bf16_bits(y[d]);
+        v_recent[ring + d] = ((const uint16_t*)v_new)[src + d];
+      }
+    }
+  }
+  free(x);
+  free(y);
+  return rc;
+}
+
 /* ------------------------------------------------------------- attention */
 
 typedef struct {
@@ -308,6 +378,9 @@ typedef struct {
   const float* k_scale;    /* INT8 caches: [G] per-head scales */
   const float* v_scale;
   int n_query;             /* T new tokens (queries) per sequence */
+  int window;              /* mixed precision: W > 0, the bf16 rings below */
+  const uint16_t* k_recent;
+  const uint16_t* v_recent;
   const int32_t* unit_b;   /* NULL: unit u is (u / (T H), u % (T H)) */
   const int32_t* unit_h;   /* query row t * H + h of its sequence */
   int64_t n_units;
@@ -337,6 +410,18 @@ static double value_at(const attn_job* job, int b, int64_t j, int64_t row, int g
   return load_elem(job->v_cache, sh->dtype, row * sh->head_dim + d);
 }
 
+/* Mixed precision: token j of sequence b is in the ring when it is among the
+ * W newest of the L attended (j >= L - W). */
+static int in_ring(const attn_job* job, int64_t L, int64_t j) {
+  return job->window > 0 && j >= L - job->window;
+}
+
+static double ring_at(const attn_job* job, const uint16_t* ring, int b, int64_t j, int g, int d) {
+  const kvo_shape* sh = job->sh;
+  return bf16_bits_to_double(
+      ring[(((int64_t)b * job->window + j % job->window) * sh->n_kv_heads + g) * sh->head_dim + d]);
+}
+
 static void attn_unit(attn_job* job, int64_t u, double* s) {
   const kvo_shape* sh = job->sh;
   const int H = sh->n_heads, G = sh->n_kv_heads, D = sh->head_dim;
@@ -359,9 +444,15 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
   /* pass 1: scores and their maximum */
   double m = -INFINITY;
   for (int64_t j = 0; j < L; ++j) {
+    double dot = 0.0;
+    if (in_ring(job, L, j)) {
+      for (int d = 0; d < D; ++d) dot += q[d] * ring_at(job, job->k_recent, b, j, g, d);
+      s[j] = job->scale * dot;
+      if (s[j] > m) m = s[j];
+      continue;
+    }
     int64_t row = cache_row(sh, job->table, b, j, g);
     if (row < 0) { job->bad = 1; s[j] = -INFINITY; continue; }
-    double dot = 0.0;
     for (int d = 0; d < D; ++d) dot += q[d] * key_at(job, b, j, row, g, d);
     s[j] = job->scale * dot;
     if (s[j] > m) m = s[j];
@@ -376,6 +467,10 @@ static void attn_unit(attn_job* job, int64_t u, double* s) {
   for (int64_t j = 0; j < L; ++j) {
     double p = s[j] / l;
     if (job->probs) job->probs[u * sh->max_seq_len + j] = p;
+    if (in_ring(job, L, j)) {
+      for (int d = 0; d < D; ++d) o[d] += p * ring_at(job, job->v_recent, b, j, g, d);
+      continue;
+    }
     int64_t row = cache_row(sh, job->table, b, j, g);
     if (row < 0) continue;
     for (int d = 0; d < D; ++d) o[d] += p * value_at(job, b, j, row, g, d);
@@ -488,4 +583,27 @@ int kvo_decode_attn_units(const kvo_shape* sh, const double* q_rot,
   return kvo_decode_attn_units_i8(sh, q_rot, k_cache, v_cache, NULL, NULL, seq_lens,
                                   block_table, scale, unit_b, unit_h, n_units, out, lse,
                                   n_threads);
+}
+
+/* Attention over a mixed-precision cache (file header): every (b, h), or
+ * only the listed units when unit_b is not NULL; one new token per
+ * sequence. */
+int kvo_decode_attn_mixed(const kvo_shape* sh, int window, const double* q_rot,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const uint16_t* k_recent,
+                          const uint16_t* v_recent, const int32_t* seq_lens,
+                          const int32_t* block_table, double scale, const int32_t* unit_b,
+                          const int32_t* unit_h, int64_t n_units, double* out, double* lse,
+                          int n_threads) {
+  if (sh->dtype != KVO_I8 || window < 1 || !k_scale || !v_scale) return -2;
+  attn_job job;
+  memset(&job, 0, sizeof job);
+  job.sh = sh; job.q_rot = q_rot; job.k_cache = k_cache; job.v_cache = v_cache;
+  job.k_scale = k_scale; job.v_scale = v_scale; job.n_query = 1;
+  job.window = window; job.k_recent = k_recent; job.v_recent = v_recent;
+  job.seq_lens = seq_lens; job.table = block_table; job.scale = scale;
+  job.unit_b = unit_b; job.unit_h = unit_h;
+  job.n_units = unit_b ? n_units : (int64_t)sh->batch * sh->n_heads;
+  job.out = out; job.lse = lse;
+  return run_attn(&job, n_threads);
 }
