@@ -433,6 +433,66 @@ size_t gqa_prefill_workspace_size(const kvd_shape* shape, int32_t n_query,
                                   int32_t max_seq_len_host, const kvd_options* options);
 
 /*
+ * Mixed-precision cache ([KVGR] §4.3 names caches that keep the most recent
+ * tokens at high precision and quantise the older history): the `window`
+ * (W) newest tokens of each sequence are kept in bf16 rings k_recent /
+ * v_recent [B, W, G, D] (token p in row p mod W, the bf16 cache's row
+ * layout), every older token in an INT8 cache described by `shape`
+ * (kv_dtype KVD_INT8, contiguous or paged, layout and scales as for
+ * rope_append_kv_int8), at its own position.  One new token per sequence.
+ *
+ * rope_append_kv_mixed -- RoPE of q and k as in rope_append_kv; then for
+ * every sequence b with P = positions[b] in [0, max_seq_len):
+ *   if P >= W, token P - W leaves the ring: its stored bf16 K and V values
+ *   are quantised (the code nearest to value / scale[g], ties to even,
+ *   saturating at +-127) into the INT8 cache at position P - W (skipped if
+ *   that slot's block id is outside the pool);
+ *   ring row P mod W then receives the rotated k, rounded once to bf16, and
+ *   v_new (bits).
+ * A position outside [0, max_seq_len) changes nothing for its sequence.
+ *   window     W, 1 <= W <= max_seq_len; k_recent / v_recent bf16
+ *              [B, W, G, D], modified in place at row P mod W only
+ *   other arguments as rope_append_kv_int8 (q, k_new, v_new bf16)
+ * Errors: EINVAL, EUNSUPPORTED (shape not INT8, bad style), ERANGE (window),
+ * EHIP.
+ */
+kvd_status rope_append_kv_mixed(const kvd_shape* shape, int32_t window, const void* q,
+                                const void* k_new, const void* v_new, float* q_rot,
+                                void* k_cache, void* v_cache, const float* k_scale,
+                                const float* v_scale, void* k_recent, void* v_recent,
+                                const int32_t* positions, const int32_t* block_table,
+                                double rope_base, int32_t rope_style, void* stream);
+
+/*
+ * gqa_decode_attn_mixed -- gqa_decode_attn over a mixed-precision cache:
+ * with L = seq_lens[b] (clamped to [0, max_seq_len_host]), query (b, h)
+ * attends its L tokens, token j read from the rings when j >= L - W and
+ * dequantised (scale[g] * code) from the INT8 cache otherwise.  The history
+ * runs on the INT8 kernel and the ring on the bf16 kernels (the ring's
+ * rows read in ring order: a softmax does not depend on the order of its
+ * keys); both write split partials to the workspace and one log-sum-exp
+ * merge combines them.  Options: split_tokens and dispatch_order apply to
+ * both parts; kernel and the tail fields must be 0 (EINVAL); the timing
+ * events bracket both split kernels.
+ *   workspace  gqa_decode_workspace_size_mixed(shape, window,
+ *              max_seq_len_host, options) bytes, 256-byte aligned
+ *   other arguments as gqa_decode_attn_int8; k_recent / v_recent as above
+ * Errors: as gqa_decode_attn_multi, and ERANGE for the window.
+ */
+kvd_status gqa_decode_attn_mixed(const kvd_shape* shape, int32_t window, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const void* k_recent,
+                                 const void* v_recent, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream);
+
+/* Workspace bytes of gqa_decode_attn_mixed (0 for invalid arguments). */
+size_t gqa_decode_workspace_size_mixed(const kvd_shape* shape, int32_t window,
+                                       int32_t max_seq_len_host, const kvd_options* options);
+
+/*
  * gqa_decode_attn_multi_noalloc -- gqa_decode_attn_multi without a
  * workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

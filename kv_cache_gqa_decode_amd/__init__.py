@@ -13,7 +13,9 @@ def __getattr__(name):
     if name in __all__ or name in ("Options", "get_plan", "KvdError", "read_probe",
                                    "v_cache_shape_int8", "gqa_decode_attn_noalloc",
                                    "PREFILL_PAIRS_FASTEST", "PREFILL_TILES_FASTEST",
-                                   "PREFILL_XCD_RUNS", "prefill_workspace_size"):
+                                   "PREFILL_XCD_RUNS", "prefill_workspace_size",
+                                   "rope_append_kv_mixed", "gqa_decode_attn_mixed",
+                                   "workspace_size_mixed"):
         from . import _binding
         return getattr(_binding, name)
     raise AttributeError(name)

@@ -113,7 +113,8 @@ def _options(opts: Optional[Options]):
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
             "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
-            "gqa_prefill_workspace_size",
+            "gqa_prefill_workspace_size", "rope_append_kv_mixed", "gqa_decode_attn_mixed",
+            "gqa_decode_workspace_size_mixed",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
             "gqa_decode_attn_multi_noalloc")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
@@ -167,6 +168,14 @@ def load_library():
                                          ctypes.c_size_t, OP, P]
         lib.gqa_prefill_workspace_size.restype = ctypes.c_size_t
         lib.gqa_prefill_workspace_size.argtypes = [SP, I32, I32, OP]
+        lib.rope_append_kv_mixed.restype = I32
+        lib.rope_append_kv_mixed.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P, P, P, P,
+                                             ctypes.c_double, I32, P]
+        lib.gqa_decode_attn_mixed.restype = I32
+        lib.gqa_decode_attn_mixed.argtypes = [SP, I32, P, P, P, P, P, P, P, P, P, I32,
+                                              ctypes.c_float, P, P, P, ctypes.c_size_t, OP, P]
+        lib.gqa_decode_workspace_size_mixed.restype = ctypes.c_size_t
+        lib.gqa_decode_workspace_size_mixed.argtypes = [SP, I32, I32, OP]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32, OP]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -487,6 +496,107 @@ def gqa_decode_attn_int8(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                                     _ptr(lse), _ptr(workspace), wbytes, _stream(dev)))
     return out, lse
 
+
+
+def _check_rings(k_recent, v_recent, B, G, D, dev):
+    """The bf16 rings [B, W, G, D] of a mixed-precision cache; returns W."""
+    _need(k_recent, "k_recent", dev, torch.bfloat16)
+    if k_recent.dim() != 4 or tuple(k_recent.shape[::2]) != (B, G) or int(k_recent.shape[3]) != D:
+        raise ValueError(f"k_recent: expected [B={B}, W, G={G}, D={D}], got {tuple(k_recent.shape)}")
+    _need(v_recent, "v_recent", dev, torch.bfloat16, tuple(k_recent.shape))
+    return int(k_recent.shape[1])
+
+
+def rope_append_kv_mixed(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                         v_scale: torch.Tensor, k_recent: torch.Tensor, v_recent: torch.Tensor,
+                         positions: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                         base: float = 10000.0, style: str = "interleaved",
+                         q_rot: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """rope_append_kv into a mixed-precision cache: the W newest tokens in the
+    bf16 rings k_recent / v_recent [B, W, G, D] (token p in row p mod W), the
+    older ones in the INT8 cache (layouts and scales as rope_append_kv_int8).
+    The token that leaves the ring is quantised into the INT8 cache."""
+    lib = load_library()
+    dev = k_cache.device
+    B, G, D = int(k_new.shape[0]), int(k_new.shape[1]), int(k_new.shape[2])
+    H = int(q.shape[1]) if q is not None else G
+    shape = make_shape(B, H, k_cache, block_table)
+    if q is not None:
+        _need(q, "q", dev, torch.bfloat16, (B, H, D))
+    _need(k_new, "k_new", dev, torch.bfloat16, (B, G, D))
+    _need(v_new, "v_new", dev, torch.bfloat16, (B, G, D))
+    _need(k_cache, "k_cache", dev, torch.int8)
+    _need(v_cache, "v_cache", dev, torch.int8, v_cache_shape_int8(k_cache, block_table is not None))
+    _check_scales(k_scale, v_scale, G, dev)
+    window = _check_rings(k_recent, v_recent, B, G, D, dev)
+    _need(positions, "positions", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if style not in _STYLES:
+        raise ValueError(f"style must be one of {sorted(_STYLES)}")
+    if q is not None and q_rot is None:
+        q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _check(lib.rope_append_kv_mixed(ctypes.byref(shape), window, _ptr(q), _ptr(k_new),
+                                    _ptr(v_new), _ptr(q_rot) if q is not None else None,
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(k_recent), _ptr(v_recent), _ptr(positions),
+                                    _ptr(block_table), float(base), _STYLES[style], _stream(dev)))
+    return q_rot if q is not None else None
+
+
+def gqa_decode_attn_mixed(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          k_scale: torch.Tensor, v_scale: torch.Tensor, k_recent: torch.Tensor,
+                          v_recent: torch.Tensor, seq_lens: torch.Tensor,
+                          block_table: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                          options: Optional[Options] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gqa_decode_attn over a mixed-precision cache (rope_append_kv_mixed):
+    the last W of each sequence's tokens from the bf16 rings, the rest from
+    the INT8 cache."""
+    lib = load_library()
+    dev = k_cache.device
+    B, H, D = (int(x) for x in q_rot.shape)
+    shape = make_shape(B, H, k_cache, block_table)
+    _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    _need(k_cache, "k_cache", dev, torch.int8)
+    _need(v_cache, "v_cache", dev, torch.int8, v_cache_shape_int8(k_cache, block_table is not None))
+    _check_scales(k_scale, v_scale, shape.n_kv_heads, dev)
+    window = _check_rings(k_recent, v_recent, B, shape.n_kv_heads, D, dev)
+    _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if shape.head_dim != D:
+        raise ValueError("head_dim of q_rot and cache differ")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    out, lse = _outputs((B,), H, D, dev, out, lse, want_lse)
+    opts = _options(options)
+    if workspace is None:
+        workspace = _workspace(dev, int(lib.gqa_decode_workspace_size_mixed(
+            ctypes.byref(shape), window, msl, opts)))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_attn_mixed(ctypes.byref(shape), window, _ptr(q_rot), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                     _ptr(k_recent), _ptr(v_recent), _ptr(seq_lens),
+                                     _ptr(block_table), msl, _scale_arg(scale), _ptr(out),
+                                     _ptr(lse), _ptr(workspace), wbytes, opts, _stream(dev)))
+    return out, lse
+
+
+def workspace_size_mixed(batch: int, n_heads: int, k_cache: torch.Tensor, window: int,
+                         block_table: Optional[torch.Tensor] = None,
+                         max_seq_len: Optional[int] = None,
+                         options: Optional[Options] = None) -> int:
+    """Workspace bytes gqa_decode_attn_mixed takes."""
+    shape = make_shape(batch, n_heads, k_cache, block_table)
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    return int(load_library().gqa_decode_workspace_size_mixed(ctypes.byref(shape), int(window),
+                                                              msl, _options(options)))
 
 
 def _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, paged):

@@ -427,11 +427,14 @@ size_t gqa_decode_workspace_size(const kvd_shape* shape, int32_t max_seq_len_hos
 
 namespace {
 
+// window > 0: the append into a mixed-precision cache (k_recent / v_recent
+// the bf16 rings of the `window` newest tokens, shape the INT8 history)
 kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
                        const void* v_new, float* q_rot, void* k_cache, void* v_cache,
                        const float* k_scale, const float* v_scale, const int32_t* positions,
                        const int32_t* block_table, double rope_base, int32_t rope_style,
-                       void* stream, int32_t T = 1) {
+                       void* stream, int32_t T = 1, void* k_recent = nullptr,
+                       void* v_recent = nullptr, int32_t window = 0) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   if (T < 1 || T > shape->max_seq_len) return KVD_EUNSUPPORTED;
@@ -443,7 +446,7 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
   const bool paged = shape->block_size != 0;
   if (paged != (block_table != nullptr)) return KVD_EINVAL;
   if (shape->batch == 0) return KVD_OK;
-  RopeParams p;
+  RopeParams p{};
   p.q = q; p.k_new = k_new; p.v_new = v_new; p.q_rot = q ? q_rot : nullptr;
   p.k_cache = k_cache; p.v_cache = v_cache; p.k_scale = k_scale; p.v_scale = v_scale;
   p.positions = positions; p.table = block_table;
@@ -451,9 +454,11 @@ kvd_status append_impl(const kvd_shape* shape, const void* q, const void* k_new,
   p.D = shape->head_dim; p.T = T; p.style = rope_style; p.max_seq_len = shape->max_seq_len;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
-  if (launch_rope_append(p, shape->kv_dtype, paged, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return KVD_EHIP;
-  return KVD_OK;
+  p.k_recent = k_recent; p.v_recent = v_recent; p.window = window;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = window > 0 ? launch_rope_append_mixed(p, paged, s)
+                                  : launch_rope_append(p, shape->kv_dtype, paged, s);
+  return e == hipSuccess ? KVD_OK : KVD_EHIP;
 }
 
 kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k_cache,
@@ -633,7 +638,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  DecodeParams p;
+  DecodeParams p{};
   p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
   p.k_scale = k_scale; p.v_scale = v_scale;
   p.out = out; p.lse = lse;
@@ -644,6 +649,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
   p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
+  p.part_stride = pl.n_splits;
   p.qscale = log2_scale(scale, shape->head_dim);
   p.direct = pl.n_splits <= 1 ? 1 : 0;
   p.grid_order = pl.grid_order;
@@ -678,4 +684,197 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   return KVD_OK;
 }
 
+// Attention over a mixed-precision cache: the history (tokens older than
+// the window) on the INT8 kernel, the rings (the window's tokens) on the
+// bf16 kernels, read as a contiguous cache of `window` rows in ring order
+// (a softmax does not depend on the order of its keys).  Both write their
+// split partials side by side in one workspace -- the history's in slots
+// [0, n1), the rings' in [n1, n1 + n2) -- and one merge combines them.
+struct MixedPlan {
+  Plan hist, ring;
+  kvd_shape ring_shape;
+  int n1 = 0, n2 = 0;
+  size_t lse_offset = 0, units1 = 0, units2 = 0, workspace = 0;
+};
+
+kvd_status mixed_plan(const kvd_shape* s, int32_t window, int32_t max_len,
+                      const kvd_options* options, Tuning* tu, MixedPlan* mp) {
+  *mp = MixedPlan{};
+  kvd_status st = check_shape(s);
+  if (st != KVD_OK) return st;
+  // the INT8 kernel takes up to 32 query rows per KV head
+  if (s->kv_dtype != KVD_INT8 || s->n_heads / s->n_kv_heads > 32) return KVD_EUNSUPPORTED;
+  if (window < 1 || window > s->max_seq_len) return KVD_ERANGE;
+  if (max_len < 0 || max_len > s->max_seq_len) return KVD_ERANGE;
+  st = read_options(options, tu);
+  if (st != KVD_OK) return st;
+  // each part takes its own kernel; the two-level tail split is not offered
+  if (tu->kernel >= 0 || tu->tail_split != 0 || tu->tail_span >= 0) return KVD_EINVAL;
+  mp->ring_shape = *s;
+  mp->ring_shape.kv_dtype = KVD_BF16;
+  mp->ring_shape.block_size = 0;
+  mp->ring_shape.max_seq_len = window;
+  mp->ring_shape.num_blocks = 0;
+  mp->ring_shape.max_blocks_per_seq = 0;
+  if (s->batch == 0) return KVD_OK;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  const int hist_bound = max_len > window ? max_len - window : 0;
+  const int ring_bound = max_len < window ? max_len : window;
+  if (hist_bound > 0) {
+    st = make_plan(s, hist_bound, cu, *tu, &mp->hist, 1);
+    if (st != KVD_OK) return st;
+    mp->n1 = mp->hist.n_splits;
+  }
+  if (ring_bound > 0) {
+    st = make_plan(&mp->ring_shape, ring_bound, cu, *tu, &mp->ring, 1);
+    if (st != KVD_OK) return st;
+    mp->n2 = mp->ring.n_splits;
+  }
+  const size_t parts = static_cast<size_t>(s->batch) * s->n_heads * (mp->n1 + mp->n2);
+  mp->lse_offset = (parts * s->head_dim * sizeof(float) + 255) / 256 * 256;
+  size_t off = mp->lse_offset + (parts * sizeof(float) + 255) / 256 * 256;
+  // work lists ([count][entries]) of the parts that dispatch from one
+  const auto list_bytes = [&](int n) {
+    return ((static_cast<size_t>(s->batch) * n + 64) * sizeof(int32_t) + 255) / 256 * 256;
+  };
+  if (mp->n1 > 0 && mp->hist.grid_order == 3) { mp->units1 = off; off += list_bytes(mp->n1); }
+  if (mp->n2 > 0 && mp->ring.grid_order == 3) { mp->units2 = off; off += list_bytes(mp->n2); }
+  mp->workspace = parts > 0 ? off : 0;
+  return KVD_OK;
+}
+
+kvd_status mixed_impl(const kvd_shape* shape, int32_t window, const float* q_rot,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const void* k_recent, const void* v_recent,
+                      const int32_t* seq_lens, const int32_t* block_table,
+                      int32_t max_seq_len_host, float scale, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, const kvd_options* options,
+                      void* stream) {
+  if (!shape) return KVD_EINVAL;
+  if (!q_rot || !k_cache || !v_cache || !k_scale || !v_scale || !k_recent || !v_recent ||
+      !seq_lens || !out)
+    return KVD_EINVAL;
+  if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(k_recent) || !aligned16(v_recent))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
+  if (!std::isfinite(scale)) return KVD_EINVAL;
+  const bool paged = shape->block_size != 0;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  Tuning tu;
+  MixedPlan mp;
+  kvd_status st = mixed_plan(shape, window, max_seq_len_host, options, &tu, &mp);
+  if (st != KVD_OK) return st;
+  if (shape->batch == 0) return KVD_OK;
+  if (mp.workspace > 0 && (!workspace || workspace_bytes < mp.workspace ||
+                           (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return KVD_EWORKSPACE;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  DecodeParams p{};
+  p.q_rot = q_rot; p.seq_lens = seq_lens;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G; p.T = 1;
+  p.max_len_host = max_seq_len_host;
+  p.qscale = log2_scale(scale, shape->head_dim);
+  p.window = window;
+  p.direct = 0;
+  p.part_stride = mp.n1 + mp.n2;
+  if (mp.n1 + mp.n2 > 0) {
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + mp.lse_offset);
+  }
+  // the timing events bracket both parts: start at the first, stop at the last
+  const bool two = mp.n1 > 0 && mp.n2 > 0;
+  if (mp.n1 > 0) {
+    DecodeParams h = p;
+    h.k = k_cache; h.v = v_cache; h.k_scale = k_scale; h.v_scale = v_scale; h.table = block_table;
+    h.max_seq_len = shape->max_seq_len;
+    h.num_blocks = shape->num_blocks; h.max_blocks_per_seq = shape->max_blocks_per_seq;
+    h.block_shift = shape->block_size == 32 ? 1 : 0;
+    h.chunk = mp.hist.chunk; h.chunk2 = mp.hist.chunk2; h.n_big = mp.hist.n_big;
+    h.n_splits = mp.n1; h.head_groups = mp.hist.head_groups; h.grid_order = mp.hist.grid_order;
+    h.len_mode = 1; h.split_base = 0;
+    if (h.grid_order == 3) {
+      h.n_units = reinterpret_cast<int32_t*>(ws + mp.units1);
+      h.units = h.n_units + 64;
+      if (launch_build_units(h, s) != hipSuccess) return KVD_EHIP;
+    }
+    const Launch l{s, tu.ev_start, two ? nullptr : tu.ev_stop};
+    if (launch_decode_i8(h, paged, l) != hipSuccess) return KVD_EHIP;
+  }
+  if (mp.n2 > 0) {
+    DecodeParams r = p;
+    r.k = k_recent; r.v = v_recent; r.table = nullptr;
+    r.max_seq_len = window;
+    r.chunk = mp.ring.chunk; r.chunk2 = mp.ring.chunk2; r.n_big = mp.ring.n_big;
+    r.n_splits = mp.n2; r.head_groups = mp.ring.head_groups; r.grid_order = mp.ring.grid_order;
+    r.len_mode = 2; r.split_base = mp.n1;
+    if (r.grid_order == 3) {
+      r.n_units = reinterpret_cast<int32_t*>(ws + mp.units2);
+      r.units = r.n_units + 64;
+      if (launch_build_units(r, s) != hipSuccess) return KVD_EHIP;
+    }
+    const Launch l{s, two ? nullptr : tu.ev_start, tu.ev_stop};
+    const hipError_t e = mp.ring.kernel == 1 ? launch_decode_mfma(r, false, l)
+                                             : launch_decode_valu(r, KVD_BF16, false, mp.ring.rb, l);
+    if (e != hipSuccess) return KVD_EHIP;
+  }
+  // the merge: history slots under the history's split layout, ring slots
+  // in splits of the ring's (uniform) size; no part at all (a zero bound):
+  // zeros and -inf
+  p.len_mode = 3;
+  p.n_splits = mp.n1 + mp.n2;
+  p.seg2_base = mp.n1;
+  p.seg2_chunk = mp.n2 > 0 ? mp.ring.chunk : 16;
+  p.chunk = mp.n1 > 0 ? mp.hist.chunk : 16;
+  p.chunk2 = mp.n1 > 0 ? mp.hist.chunk2 : 16;
+  p.n_big = mp.n1 > 0 ? mp.hist.n_big : 1;
+  if (p.n_splits == 0) p.n_splits = 1;
+  return launch_lse_reduce(p, s) == hipSuccess ? KVD_OK : KVD_EHIP;
+}
+
 }  // namespace
+
+extern "C" {
+
+kvd_status rope_append_kv_mixed(const kvd_shape* shape, int32_t window, const void* q,
+                                const void* k_new, const void* v_new, float* q_rot,
+                                void* k_cache, void* v_cache, const float* k_scale,
+                                const float* v_scale, void* k_recent, void* v_recent,
+                                const int32_t* positions, const int32_t* block_table,
+                                double rope_base, int32_t rope_style, void* stream) {
+  if (!shape) return KVD_EINVAL;
+  if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
+  if (window < 1 || window > shape->max_seq_len) return KVD_ERANGE;
+  if (!k_scale || !v_scale || !k_recent || !v_recent) return KVD_EINVAL;
+  return append_impl(shape, q, k_new, v_new, q_rot, k_cache, v_cache, k_scale, v_scale,
+                     positions, block_table, rope_base, rope_style, stream, 1, k_recent,
+                     v_recent, window);
+}
+
+kvd_status gqa_decode_attn_mixed(const kvd_shape* shape, int32_t window, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const void* k_recent,
+                                 const void* v_recent, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream) {
+  return mixed_impl(shape, window, q_rot, k_cache, v_cache, k_scale, v_scale, k_recent,
+                    v_recent, seq_lens, block_table, max_seq_len_host, scale, out, lse,
+                    workspace, workspace_bytes, options, stream);
+}
+
+size_t gqa_decode_workspace_size_mixed(const kvd_shape* shape, int32_t window,
+                                       int32_t max_seq_len_host, const kvd_options* options) {
+  Tuning tu;
+  MixedPlan mp;
+  if (mixed_plan(shape, window, max_seq_len_host, options, &tu, &mp) != KVD_OK) return 0;
+  return mp.workspace;
+}
+
+}  // extern "C"

@@ -154,8 +154,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   static_assert(NB >= 1 && NB <= 2 && (D == 64 || D == 128), "tile shape");
   const int R = p.R;
   const int RT = R * p.T;             // tile columns: the query rows of this KV head
-  int L = scalar_load_i32(p.seq_lens + b);
-  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int L = attended_len(p, scalar_load_i32(p.seq_lens + b));
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf

@@ -90,8 +90,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int g = blockIdx.y / p.head_groups;
   const int hg = blockIdx.y - g * p.head_groups;
   const int split = blockIdx.z;
-  int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
-  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int L = attended_len(p, __builtin_amdgcn_readfirstlane(p.seq_lens[b]));
   const int h0 = g * p.R + hg * RB;
   const int nh = min(RB, p.R - hg * RB);
   const int t0 = split_start(p, split);
@@ -250,7 +249,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       p.out[(static_cast<int64_t>(b) * p.H + h) * D + d] = val;
       if (d == 0 && p.lse) p.lse[static_cast<int64_t>(b) * p.H + h] = lse2 * 0.69314718055994531f;
     } else {
-      const int64_t pr = (static_cast<int64_t>(b) * p.H + h) * p.n_splits + split;
+      const int64_t pr = (static_cast<int64_t>(b) * p.H + h) * p.part_stride + p.split_base + split;
       p.part_o[pr * D + d] = val;
       if (d == 0) p.part_lse[pr] = lse2;
     }

@@ -47,6 +47,20 @@ struct DecodeParams {
   int32_t* units;           // work list (grid_order 3): b | split << 16, in the workspace
   int32_t* n_units;         // its length
   int32_t n_xcd;            // prefill, grid_order 2: XCDs the workgroups are dealt to
+  // Partial slots: row h's split s goes to slot h * part_stride + split_base
+  // + s (one launch's splits inside a wider set, for the mixed-precision
+  // cache; else part_stride = n_splits, split_base = 0).
+  int32_t part_stride;
+  int32_t split_base;
+  // Tokens a launch covers of a cache whose `window` newest tokens are kept
+  // apart (mixed precision): len_mode 0 all, 1 the older ones, 2 the newest
+  // ones (see attended_len); 3 (the merge only): split slots [0, seg2_base)
+  // are those of mode 1 under chunk / chunk2 / n_big, slots seg2_base + s
+  // those of mode 2 in splits of seg2_chunk tokens.
+  int32_t len_mode;
+  int32_t window;
+  int32_t seg2_base;
+  int32_t seg2_chunk;
 };
 
 struct RopeParams {
@@ -68,6 +82,11 @@ struct RopeParams {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t block_shift;      // paged: log2(block_size / 16), 0 or 1
+  // mixed precision: the bf16 rings [B, window, G, D] of the newest tokens
+  // (window 0: a plain cache)
+  void* k_recent;
+  void* v_recent;
+  int32_t window;
 };
 
 // Where a main kernel goes: its stream and, for measurement, a pair of
@@ -96,6 +115,8 @@ inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, const 
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
                               hipStream_t stream);
+// the append into a mixed-precision cache (INT8 history, bf16 rings)
+hipError_t launch_rope_append_mixed(const RopeParams& p, bool paged, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int32_t kv_dtype, bool paged,
                               int rb, const Launch& l);
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l);
@@ -127,6 +148,15 @@ __host__ __device__ __forceinline__ int split_size(const DecodeParams& p, int s)
   return s < p.n_big ? p.chunk : p.chunk2;
 }
 // splits holding at least one of L tokens
+// The tokens of sequence b a launch attends, from its stored length: clamped
+// to [0, max_len_host], then all of them (len_mode 0), the ones older than
+// the `window` newest (1), or the newest ones (2).
+__host__ __device__ __forceinline__ int attended_len(const DecodeParams& p, int L) {
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  return p.len_mode == 1 ? (L > p.window ? L - p.window : 0)
+       : p.len_mode == 2 ? (L < p.window ? L : p.window) : L;
+}
+
 __host__ __device__ __forceinline__ int split_count(const DecodeParams& p, int L) {
   const int big = p.n_big * p.chunk;
   return L <= big ? (L + p.chunk - 1) / p.chunk : p.n_big + (L - big + p.chunk2 - 1) / p.chunk2;

@@ -7,7 +7,10 @@
 // algebra behind the tiled attention of "Transformer推理核心：KV Cache、GQA与
 // RoPE原理与工程实践" §4.2 applied across workgroups.
 //
-// Only the splits that hold tokens of the sequence contribute.  The kernel
+// Only the splits that hold tokens of the sequence contribute: the first
+// split_count(L) slots, or for a mixed-precision cache (len_mode 3) the
+// history's splits in slots [0, seg2_base) and the recent tokens' splits
+// from seg2_base on, each counted from its own share of L.  The kernel
 // is a handful of microseconds of memory latency around a few MB of
 // partials, so it is written to wait for memory once: the sequence length
 // and every partial a thread merges are requested together (all reads stay
@@ -63,12 +66,17 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
       o[u] = *reinterpret_cast<const float4*>(po + static_cast<int64_t>(sc) * D);
     }
   };
-  // fold the landed batch s0 into (m, wsum, acc); ns = splits holding tokens
-  auto fold = [&](int s0, int ns) {
+  // fold the landed batch s0 into (m, wsum, acc); slot s holds tokens when
+  // s < ns, or with two segments when s < ns (the first) or s - seg2_base <
+  // ns2 (the second)
+  auto fold = [&](int s0, int ns, int ns2) {
     float mt = m;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + u * SL >= ns) ls[u] = kNegInf;       // never weighs in, even if NaN was read
+      const int s = s0 + u * SL;
+      const bool held = p.len_mode == 3 ? (s < p.seg2_base ? s < ns : s - p.seg2_base < ns2)
+                                        : s < ns;
+      if (!held) ls[u] = kNegInf;                   // never weighs in, even if NaN was read
       mt = fmaxf(mt, ls[u]);
     }
     if (mt == kNegInf) return;
@@ -91,11 +99,18 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
     request(sl);
     // the splits holding tokens (the length clamped as in the split kernels)
     const int Lc = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
-    const int ns = split_count(p, Lc);
-    fold(sl, ns);
+    int ns, ns2 = 0;
+    if (p.len_mode == 3) {
+      const int lh = Lc > p.window ? Lc - p.window : 0, lr = Lc < p.window ? Lc : p.window;
+      ns = p.seg2_base > 0 ? split_count(p, lh) : 0;
+      ns2 = (lr + p.seg2_chunk - 1) / p.seg2_chunk;
+    } else {
+      ns = split_count(p, Lc);
+    }
+    fold(sl, ns, ns2);
     for (int s0 = sl + SL * U; s0 < n_splits; s0 += SL * U) {
       request(s0);
-      fold(s0, ns);
+      fold(s0, ns, ns2);
     }
   }
   // Combine the split lanes: the workgroup's maximum (wave shuffles, then

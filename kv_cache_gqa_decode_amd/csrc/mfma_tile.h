@@ -274,8 +274,7 @@ __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u
   const int lane = threadIdx.x & 63;
   const int id = static_cast<int>(blockIdx.x);
   const int k = id / p.G;
-  int L = lane < p.B ? p.seq_lens[lane] : 0;
-  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int L = lane < p.B ? attended_len(p, p.seq_lens[lane]) : 0;
   const int n = split_count(p, L);
   int full = 0, part = 0;
   if (n > 0) {
@@ -428,7 +427,7 @@ __device__ __forceinline__ void merge_waves(const DecodeParams& p, char* smem, i
     dst = p.out + h * D;
     if (c == 0 && p.lse) p.lse[h] = lse2 * 0.69314718055994531f;
   } else {
-    const int64_t pr = h * p.n_splits + split;
+    const int64_t pr = h * p.part_stride + p.split_base + split;
     dst = p.part_o + pr * D;
     if (c == 0) p.part_lse[pr] = lse2;
   }

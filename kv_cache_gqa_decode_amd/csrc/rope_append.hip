@@ -21,6 +21,15 @@
 // holding per KV head its 16 K rows and its V block transposed: K element
 // (pos, g, d) at ((r * G + g) * 16 + pos % 16) * D + d, V element at
 // ((r * G + g) * D + d) * 16 + pos % 16.
+//
+// Mixed precision (the same §4.3 names caches that keep the most recent
+// tokens at high precision and quantise the older history): the W newest
+// tokens of a sequence sit in bf16 rings [B, W, G, D], token p in row p mod
+// W, the older ones in an INT8 cache as above.  The append of the token at
+// position P first moves token P - W (when P >= W) out of row P mod W into
+// the INT8 cache, as codes of its stored bf16 values, then writes the
+// rotated k (rounded once to bf16) and v_new there.  Each thread reads and
+// rewrites only its own ring elements, so the move needs no ordering.
 #include <type_traits>
 
 #include "kvd_internal.h"
@@ -115,8 +124,9 @@ __device__ __forceinline__ int64_t i8_krow(const RopeParams& p, int b, int pos, 
   return (i8_group<PAGED>(p, b, pos, row) * p.G + g) * 16 + (pos & 15);
 }
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, bool MIXED = false>
 __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
+  static_assert(!MIXED || std::is_same<T, int8_t>::value, "a mixed cache's history is INT8");
   // workgroup (new token bt = b * T + t, slices y, y + gridDim.y, .. of 256
   // items): the D/2 rotation factors of the token's position are computed
   // once per workgroup (fp64) and shared by its threads through LDS
@@ -151,6 +161,24 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
       if (is_q) {
         p.q_rot[src + ia] = static_cast<float>(ra);
         p.q_rot[src + ib] = static_cast<float>(rb);
+      } else if constexpr (MIXED) {
+        if (pos >= 0 && pos < p.max_seq_len) {
+          uint16_t* kr = static_cast<uint16_t*>(p.k_recent) +
+                         ((static_cast<int64_t>(b) * p.window + pos % p.window) * p.G + head) * p.D;
+          if (pos >= p.window) {
+            // token pos - window leaves the ring for the INT8 history
+            const int old = pos - p.window;
+            const int64_t row = slot_row<PAGED>(p, b, old, head);
+            if (row >= 0) {
+              int8_t* kc = static_cast<int8_t*>(p.k_cache) + i8_krow<PAGED>(p, b, old, head, row) * p.D;
+              const float ks = p.k_scale[head];
+              kc[ia] = quantize_i8(load_d<uint16_t>(kr, ia), ks);
+              kc[ib] = quantize_i8(load_d<uint16_t>(kr, ib), ks);
+            }
+          }
+          kr[ia] = double_to_bf16_rne(ra);
+          kr[ib] = double_to_bf16_rne(rb);
+        }
       } else {
         const int64_t row = slot_row<PAGED>(p, b, pos, head);
         if (row >= 0) {
@@ -164,6 +192,22 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeParams p) {
             store_rounded<T>(p.k_cache, row * p.D + ib, rb);
           }
         }
+      }
+    } else if constexpr (MIXED) {
+      const int j = i - nq - nk;
+      const int g = j / p.D, d = j - g * p.D;
+      if (pos >= 0 && pos < p.max_seq_len) {
+        uint16_t* vr = static_cast<uint16_t*>(p.v_recent) +
+                       ((static_cast<int64_t>(b) * p.window + pos % p.window) * p.G + g) * p.D + d;
+        if (pos >= p.window) {
+          const int old = pos - p.window;
+          const int64_t row = slot_row<PAGED>(p, b, old, g);
+          if (row >= 0) {
+            const int64_t vi = ((i8_group<PAGED>(p, b, old, row) * p.G + g) * p.D + d) * 16 + (old & 15);
+            static_cast<int8_t*>(p.v_cache)[vi] = quantize_i8(load_d<uint16_t>(vr, 0), p.v_scale[g]);
+          }
+        }
+        *vr = static_cast<const uint16_t*>(p.v_new)[(static_cast<int64_t>(bt) * p.G + g) * p.D + d];
       }
     } else {
       const int j = i - nq - nk;
@@ -204,6 +248,15 @@ hipError_t launch_rope_append(const RopeParams& p, int32_t kv_dtype, bool paged,
     if (paged) rope_append_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(p);
     else rope_append_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append_mixed(const RopeParams& p, bool paged, hipStream_t stream) {
+  if (p.T != 1 || p.window < 1 || !p.k_recent || !p.v_recent) return hipErrorInvalidValue;
+  const int work = (p.q ? p.H : 0) * (p.D / 2) + p.G * (p.D / 2) + p.G * p.D;
+  const dim3 grid(static_cast<unsigned>(p.B), (work + 255) / 256);
+  if (paged) rope_append_kernel<int8_t, true, true><<<grid, 256, 0, stream>>>(p);
+  else rope_append_kernel<int8_t, false, true><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

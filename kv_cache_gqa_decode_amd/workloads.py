@@ -130,6 +130,9 @@ class Problem:
     k_scale: Optional[np.ndarray] = None   # INT8 caches: [G] float32
     v_scale: Optional[np.ndarray] = None
     n_query: int = 1                       # new tokens per sequence (make_window)
+    window: int = 0                        # mixed precision (make_mixed): ring rows W
+    k_recent: Optional[np.ndarray] = None  # [B, W, G, D] bf16 bits, token p in row p mod W
+    v_recent: Optional[np.ndarray] = None
 
     @property
     def max_len(self) -> int:
@@ -303,6 +306,57 @@ def make_window(s: Spec, n_query: int, lengths: Optional[np.ndarray] = None) -> 
     return dataclasses.replace(p, q=_to_storage(q, idt), k_new=_to_storage(k_new, idt),
                                v_new=_to_storage(v_new, idt), positions=(L - T).astype(np.int32),
                                seq_lens=L, n_query=T)
+
+
+def _i8_slot(p: Problem, b: int, pos: int):
+    """Index tuples of token pos of sequence b in an INT8 K and V cache."""
+    s = p.spec
+    if s.block_size:
+        blk = int(p.block_table[b, pos // s.block_size])
+        r = pos % s.block_size
+        if s.block_size == 16:
+            return (blk, slice(None), r % 16), (blk, slice(None), slice(None), r % 16)
+        return ((blk, r // 16, slice(None), r % 16),
+                (blk, r // 16, slice(None), slice(None), r % 16))
+    return (b, pos // 16, slice(None), pos % 16), (b, pos // 16, slice(None), slice(None), pos % 16)
+
+
+def make_mixed(s: Spec, window: int, lengths: Optional[np.ndarray] = None) -> Problem:
+    """A decode step on a mixed-precision cache: the ``window`` = W newest
+    cached tokens of a sequence in bf16 rings (token p in row p mod W), the
+    older ones in the INT8 cache of ``s`` (dtype "i8").  Before the step
+    sequence b holds P = L_b - 1 tokens: the INT8 cache has codes (drawn as
+    by ``make_problem``) for positions [0, P - W), and the rings hold the
+    tokens [max(0, P - W), P), drawn from stream 2000 + b with the bf16
+    distribution (N(0, 1) * value_scale).  Every INT8 slot from P - W on and
+    every ring row past P (a short sequence) is poisoned."""
+    if s.dtype != "i8":
+        raise ValueError("the history of a mixed cache is INT8")
+    W = int(window)
+    if W < 1:
+        raise ValueError("window must be >= 1")
+    p = make_problem(s, lengths=lengths)
+    B, G, D = s.batch, s.n_kv_heads, s.head_dim
+    fill = _fill_value(s)
+    kr = np.full((B, W, G, D), BF16_NAN if s.poison else np.uint16(0), np.uint16)
+    vr = kr.copy()
+    k_cache, v_cache = p.k_cache, p.v_cache
+    for b in range(B):
+        P = int(p.positions[b])
+        lo = max(0, P - W)
+        for pos in range(lo, P):                     # in the ring, not in the INT8 cache
+            ki, vi = _i8_slot(p, b, pos)
+            k_cache[ki] = fill
+            v_cache[vi] = fill
+        if P > lo:
+            rng = _rng(s, 2000 + b)
+            shape = (P - lo, G, D)
+            kh = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
+            vh = rng.standard_normal(shape, dtype=np.float32) * np.float32(s.value_scale)
+            rows = np.arange(lo, P) % W
+            kr[b, rows] = _to_storage(kh, "bf16")
+            vr[b, rows] = _to_storage(vh, "bf16")
+    return dataclasses.replace(p, window=W, k_recent=kr, v_recent=vr)
 
 
 def as_torch(a: np.ndarray, device=None):

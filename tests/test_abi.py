@@ -232,6 +232,40 @@ def test_prefill_key_split_workspace(lib):
     assert lib.gqa_prefill_workspace_size(None, T, 64, None) == 0
 
 
+def test_mixed_validates(lib):
+    """Mixed-precision calls: an INT8 history, a window in [1, max_seq_len],
+    both rings; no kernel or tail options; batch 0 does nothing."""
+    O = B._COptions
+    i8 = shape(kv_dtype=2)
+
+    def app(sh, window, kr=FAKE, vr=FAKE, ks=FAKE):
+        return lib.rope_append_kv_mixed(ctypes.byref(sh), window, FAKE, FAKE, FAKE,
+                                        ctypes.c_void_p(0x3000), FAKE, FAKE, ks, FAKE, kr, vr,
+                                        FAKE, None, 10000.0, 0, None)
+
+    def att(sh, window, kr=FAKE, opts=None, msl=32, ws=None, ws_bytes=0):
+        return lib.gqa_decode_attn_mixed(ctypes.byref(sh), window, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         kr, FAKE, FAKE, None, msl, 0.0, ctypes.c_void_p(0x2000),
+                                         None, ws, ws_bytes,
+                                         None if opts is None else ctypes.byref(opts), None)
+
+    assert app(shape(), 16) == EUNSUPPORTED                 # bf16 shape
+    assert app(i8, 0) == ERANGE and app(i8, 65) == ERANGE
+    assert app(i8, 16, kr=None) == EINVAL and app(i8, 16, ks=None) == EINVAL
+    assert app(shape(kv_dtype=2, batch=0), 16) == OK
+    assert att(shape(), 16) == EUNSUPPORTED
+    assert att(i8, 0) == ERANGE and att(i8, 65) == ERANGE
+    assert att(i8, 16, kr=None) == EINVAL
+    assert att(i8, 16, msl=65) == ERANGE
+    for bad in (O(kernel=2), O(tail_split_tokens=32), O(dispatch_order=7)):
+        assert att(i8, 16, opts=bad) == EINVAL
+    empty = shape(kv_dtype=2, batch=0)
+    assert att(empty, 16) == OK and att(empty, 16, opts=O(split_tokens=64)) == OK
+    assert lib.gqa_decode_workspace_size_mixed(ctypes.byref(empty), 16, 32, None) == 0
+    assert lib.gqa_decode_workspace_size_mixed(ctypes.byref(i8), 0, 32, None) == 0
+    assert lib.gqa_decode_workspace_size_mixed(ctypes.byref(shape()), 16, 32, None) == 0
+
+
 def test_options_validation(lib):
     """kvd_options travel with the call; bad values are refused before any
     HIP call (batch 0: a valid call does nothing)."""
