@@ -437,6 +437,98 @@ def run_prefill(args, s, dev):
     print(json.dumps(result), flush=True)
 
 
+def run_mixed(args, s, dev):
+    """Decode step on a mixed-precision cache: the --window newest tokens of
+    each sequence in bf16 rings, the older ones INT8.  KV bytes are the INT8
+    history's plus the rings' (bf16) tokens attended; the kernel time spans
+    both split kernels (the library ties the events to the first and the
+    last)."""
+    import numpy as np
+    import torch
+    import kv_cache_gqa_decode_amd as kvd
+    from kv_cache_gqa_decode_amd import workloads as W
+    Wn = int(args.window)
+    t_gen = time.perf_counter()
+    p = W.make_mixed(s, Wn)
+    print(f"# generated {s.name} mixed inputs in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    t = {k: W.as_torch(getattr(p, k), dev) for k in
+         ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens", "k_scale",
+          "v_scale", "k_recent", "v_recent")}
+    table = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
+    max_len = p.max_len
+    opts = kvd.Options(split_tokens=args.split,
+                       dispatch_order=None if args.order < 0 else args.order)
+    q_rot = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q_rot)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws_bytes = kvd.workspace_size_mixed(B, H, t["k_cache"], Wn, table, max_len, opts)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(options=opts):
+        kvd.rope_append_kv_mixed(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                 t["k_scale"], t["v_scale"], t["k_recent"], t["v_recent"],
+                                 t["positions"], table, base=s.rope_base, q_rot=q_rot)
+        kvd.gqa_decode_attn_mixed(q_rot, t["k_cache"], t["v_cache"], t["k_scale"], t["v_scale"],
+                                  t["k_recent"], t["v_recent"], t["seq_lens"], table,
+                                  max_seq_len=max_len, out=out, lse=lse, workspace=ws,
+                                  options=options)
+
+    flush = Flusher(dev, args.flush)
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    steps = cold_times(step, args.steps, flush)
+    kern = cold_kernel_times(lambda a, b: step(opts.with_events(a, b)), args.steps, flush)
+    warm = None if args.no_warm else warm_ms(step, args.steps)
+    del flush
+    torch.cuda.empty_cache()
+    L = p.seq_lens.astype(np.int64)
+    hist = int(np.maximum(L - Wn, 0).sum())
+    ring = int(np.minimum(L, Wn).sum())
+    kv_bytes = 2 * G * D * (hist + 2 * ring)
+    ms = pct(steps, 50)
+    kern_ms = pct(kern, 50)
+    achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    ceiling = (None if args.no_read_ceiling else
+               read_ceiling(dev, kvd, kv_bytes, Flusher(dev, args.flush)))
+    result = {
+        "metric": "decode-attention KV HBM GB/s (% of peak) and seq-steps/sec at 1 MI355X",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8+bf16",
+        "data": ("synthetic (seeded INT8 codes ~ clipped N(0, 40^2) and per-head scales for the "
+                 "history, seeded N(0,1)/sqrt(128) bf16 rings, seeded lengths; no datasets or "
+                 "weights)"),
+        "config": {"workload": workload_name(s).replace("INT8-KV", f"mixed-KV (last {Wn} bf16, "
+                                                         "older INT8)", 1),
+                   "batch": B, "n_heads": H, "n_kv_heads": G, "head_dim": D,
+                   "window": Wn, "history_tokens": hist, "ring_tokens": ring,
+                   "kv_bytes_per_step": kv_bytes, "block_size": s.block_size,
+                   "max_context": max_len, "workspace_bytes": ws_bytes,
+                   "parallelism": "single GPU"},
+        "seq_steps_per_s": round(B / (ms * 1e-3), 1),
+        "timing": (f"each step after a 1 GiB cache-evicting {args.flush}; ms_per_step and value "
+                   "from the p50 of the K steps"),
+        "step_ms": summary(steps),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode split-K attention, INT8 history + bf16 ring kernels",
+                     "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": summary(kern),
+                     "launches_timed": len(kern), "algorithmic_bytes_per_launch": kv_bytes},
+    }
+    if ceiling is not None:
+        result["roofline"]["read_ceiling_gbs"] = ceiling["gbs"]
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
+    if warm is not None:
+        result["warm"] = {"ms_per_step": round(warm, 5),
+                          "gbs": round(kv_bytes / (warm * 1e-3) / 1e9, 1)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,8 +538,11 @@ def main():
     ap.add_argument("--kv-heads", type=int, default=None)
     ap.add_argument("--block-size", type=int, default=None, choices=[16, 32],
                     help="paged workload (c4) with 16- or 32-token blocks (same pool bytes)")
-    ap.add_argument("--kv", default="native", choices=["native", "int8"],
-                    help="cache dtype: the workload's own (bf16 / fp32) or INT8 with per-head scales")
+    ap.add_argument("--kv", default="native", choices=["native", "int8", "mixed"],
+                    help="cache dtype: the workload's own (bf16 / fp32), INT8 with per-head "
+                         "scales, or mixed (the --window newest tokens bf16, the rest INT8)")
+    ap.add_argument("--window", type=int, default=1024,
+                    help="--kv mixed: tokens per sequence kept in bf16")
     ap.add_argument("--n-query", type=int, default=1,
                     help="new tokens per sequence (T > 1: the multi-token verification step)")
     ap.add_argument("--prefill", type=int, default=0,
@@ -516,11 +611,17 @@ def main():
         s = W.spec(args.config, n_kv_heads=args.kv_heads, poison=False, block_size=args.block_size,
                    num_blocks=s.num_blocks * s.block_size // args.block_size,
                    max_blocks_per_seq=s.max_blocks_per_seq * s.block_size // args.block_size)
-    if args.kv == "int8":
+    if args.kv in ("int8", "mixed"):
         if s.dtype != "bf16":
-            print("--kv int8 applies to the bf16 workloads (c2..c5)", file=sys.stderr)
+            print(f"--kv {args.kv} applies to the bf16 workloads (c2..c5)", file=sys.stderr)
             sys.exit(2)
         s = s.replace(dtype="i8")
+    if args.kv == "mixed":
+        if args.prefill > 0 or args.n_query != 1 or args.graph:
+            print("--kv mixed times the one-token decode step", file=sys.stderr)
+            sys.exit(2)
+        run_mixed(args, s, dev)
+        return
     if args.prefill > 0:
         run_prefill(args, s, dev)
         return
