@@ -73,9 +73,11 @@ CSRC = os.path.join(ROOT, "kv_cache_gqa_decode_amd", "csrc")
 # invalidates the traffic counters recorded for that kernel)
 KERNEL_SOURCES = {
     "mfma": ("decode_mfma.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
-    "int8": ("decode_i8.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
+    "int8": ("decode_i8.hip", "i8_codes.h", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
     "valu": ("decode_valu.hip", "kvd_internal.h"),
     "prefill": ("prefill_mfma.hip", "mfma_tile.h", "kvd_internal.h", "uniform_join.h"),
+    "prefill_i8": ("prefill_i8.hip", "i8_codes.h", "mfma_tile.h", "kvd_internal.h",
+                   "uniform_join.h"),
 }
 
 
@@ -324,8 +326,9 @@ def prefill_cpu_baseline(s, p, T, budget_s: float):
                         max_seq_len=s.max_seq_len, block_size=s.block_size,
                         num_blocks=s.num_blocks, max_blocks_per_seq=s.max_blocks_per_seq)
     kc, vc = p.k_cache.copy(), p.v_cache.copy()
+    sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if s.dtype == "i8" else {}
     q_rot = oracle.rope_append(g, p.q, p.k_new, p.v_new, kc, vc, p.positions, p.block_table,
-                               base=s.rope_base, n_query=T)
+                               base=s.rope_base, n_query=T, **sc)
     rng = np.random.default_rng(97)
     threads = oracle.default_threads()
 
@@ -337,7 +340,7 @@ def prefill_cpu_baseline(s, p, T, budget_s: float):
                    for b, t, _ in units)
         t0 = time.perf_counter()
         oracle.decode_attn_units(g, q_rot, kc, vc, p.seq_lens, units, p.block_table,
-                                 n_query=T, n_threads=threads)
+                                 n_query=T, n_threads=threads, **sc)
         return time.perf_counter() - t0, 4 * s.head_dim * keys
 
     n = 8
@@ -359,9 +362,10 @@ def run_prefill(args, s, dev):
     from kv_cache_gqa_decode_amd import sizing
     from kv_cache_gqa_decode_amd import workloads as W
     T = args.prefill
-    if s.dtype != "bf16":
-        print("--prefill runs on the bf16 workloads (c2..c5)", file=sys.stderr)
+    if s.dtype not in ("bf16", "i8"):
+        print("--prefill runs on the bf16 workloads (c2..c5) or their INT8 form", file=sys.stderr)
         sys.exit(2)
+    i8 = s.dtype == "i8"
     if T > s.max_seq_len:
         print(f"--prefill {T} exceeds the cache capacity {s.max_seq_len}", file=sys.stderr)
         sys.exit(2)
@@ -372,6 +376,7 @@ def run_prefill(args, s, dev):
     t = {k: W.as_torch(getattr(p, k), dev) for k in
          ("q", "k_new", "v_new", "k_cache", "v_cache", "positions", "seq_lens")}
     table = None if p.block_table is None else W.as_torch(p.block_table, dev)
+    sc = dict(k_scale=W.as_torch(p.k_scale, dev), v_scale=W.as_torch(p.v_scale, dev)) if i8 else {}
     B, H, G, D = s.batch, s.n_heads, s.n_kv_heads, s.head_dim
     q_rot = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
     out = torch.empty_like(q_rot)
@@ -385,11 +390,11 @@ def run_prefill(args, s, dev):
 
     def step(options=None):
         kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
-                                 t["positions"], table, base=s.rope_base, q_rot=q_rot)
+                                 t["positions"], table, base=s.rope_base, q_rot=q_rot, **sc)
         kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"], table,
                              max_seq_len=max_len, out=out, lse=lse,
                              options=options if options is not None else base_opts,
-                             workspace=ws)
+                             workspace=ws, **sc)
 
     flush = Flusher(dev, args.flush)
     for _ in range(args.warmup):
@@ -410,7 +415,7 @@ def run_prefill(args, s, dev):
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "vs_baseline": None, "dtype": "i8 codes, f16 matrix cores" if i8 else "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(128) values and lengths; no datasets or weights)",
         "config": {"workload": workload_name(s) + f", prefill of {T} new tokens per sequence",
                    "batch": B, "n_heads": H, "n_kv_heads": G, "head_dim": D,
@@ -418,7 +423,9 @@ def run_prefill(args, s, dev):
                    "attended_keys": sizing.window_key_count(p.seq_lens, T),
                    "flops_per_step": flops, "block_size": s.block_size,
                    "key_split_workspace_bytes": ws_bytes,
-                   "arithmetic": "q and P rounded to bf16 on the matrix cores, fp32 accumulate",
+                   "arithmetic": ("codes converted to exact fp16 per tile, q and P rounded to "
+                                  "fp16, fp32 accumulate" if i8 else
+                                  "q and P rounded to bf16 on the matrix cores, fp32 accumulate"),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "timing": f"each step after a 1 GiB cache-evicting {args.flush}; ms_per_step = p50",
@@ -429,7 +436,7 @@ def run_prefill(args, s, dev):
                      "kernel": "causal prefill attention", "kernel_ms": round(kern_ms, 4),
                      "kernel_ms_pct": summary(kern), "launches_timed": len(kern),
                      "algorithmic_flops_per_launch": flops,
-                     "kernel_source_hash": kernel_source_hash("prefill")},
+                     "kernel_source_hash": kernel_source_hash("prefill_i8" if i8 else "prefill")},
     }
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)

@@ -425,9 +425,29 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
                             const kvd_options* options, void* stream);
 
 /*
- * gqa_prefill_workspace_size -- bytes of workspace gqa_prefill_attn needs
- * for these arguments with a non-NULL workspace: 0 when the plan has no
- * key split, or when an argument is invalid (the call itself says which).
+ * gqa_prefill_attn_int8 -- gqa_prefill_attn over an INT8 cache (layout and
+ * per-head scales as in gqa_decode_attn_int8; [KVGR] §4.3).  Each key tile's
+ * codes are converted once per workgroup to exact fp16 values; q * scale and
+ * the probabilities are rounded once to fp16 for the matrix cores, fp32
+ * accumulation; the scores are q . code times k_scale[g], the output is
+ * scaled by v_scale[g].  Key splits, options and workspace as in
+ * gqa_prefill_attn (gqa_prefill_workspace_size takes INT8 shapes too).
+ * Errors: as gqa_prefill_attn; EINVAL also for missing scales; EUNSUPPORTED
+ * for a cache dtype other than INT8.
+ */
+kvd_status gqa_prefill_attn_int8(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream);
+
+/*
+ * gqa_prefill_workspace_size -- bytes of workspace gqa_prefill_attn (bf16
+ * shapes) or gqa_prefill_attn_int8 (INT8 shapes) needs for these arguments
+ * with a non-NULL workspace: 0 when the plan has no key split, or when an
+ * argument is invalid (the call itself says which).
  */
 size_t gqa_prefill_workspace_size(const kvd_shape* shape, int32_t n_query,
                                   int32_t max_seq_len_host, const kvd_options* options);

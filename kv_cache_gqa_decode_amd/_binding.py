@@ -113,7 +113,8 @@ def _options(opts: Optional[Options]):
 EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_int8", "gqa_decode_workspace_size", "rope_append_kv_multi",
             "gqa_decode_attn_multi", "gqa_decode_workspace_size_multi", "gqa_prefill_attn",
-            "gqa_prefill_workspace_size", "rope_append_kv_mixed", "gqa_decode_attn_mixed",
+            "gqa_prefill_workspace_size", "gqa_prefill_attn_int8", "rope_append_kv_mixed",
+            "gqa_decode_attn_mixed",
             "gqa_decode_workspace_size_mixed",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
             "gqa_decode_attn_multi_noalloc")
@@ -166,6 +167,9 @@ def load_library():
         lib.gqa_prefill_attn.restype = I32
         lib.gqa_prefill_attn.argtypes = [SP, I32, P, P, P, P, P, I32, ctypes.c_float, P, P, P,
                                          ctypes.c_size_t, OP, P]
+        lib.gqa_prefill_attn_int8.restype = I32
+        lib.gqa_prefill_attn_int8.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_float,
+                                              P, P, P, ctypes.c_size_t, OP, P]
         lib.gqa_prefill_workspace_size.restype = ctypes.c_size_t
         lib.gqa_prefill_workspace_size.argtypes = [SP, I32, I32, OP]
         lib.rope_append_kv_mixed.restype = I32
@@ -722,22 +726,33 @@ def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                      scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      want_lse: bool = True, options: Optional[Options] = None,
-                     workspace: Optional[torch.Tensor] = None
+                     workspace: Optional[torch.Tensor] = None,
+                     k_scale: Optional[torch.Tensor] = None,
+                     v_scale: Optional[torch.Tensor] = None
                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Causal attention of T new tokens per sequence (a prompt or a chunk of
-    one, already appended), q_rot [B, T, H, D], over a bf16 cache; query t
-    attends the tokens j < seq_lens[b] - T + 1 + t.  q and P enter the matrix
-    cores as bf16.  ``options`` may carry split_tokens (a multiple of 32), a
-    prefill dispatch order and timing events.  The key-split partials go to
-    ``workspace`` or to a per-call allocation of the size the library asks
-    for.  Returns (out [B, T, H, D], lse [B, T, H])."""
+    one, already appended), q_rot [B, T, H, D], over a bf16 cache, or an
+    INT8 cache with its per-head ``k_scale`` / ``v_scale``; query t attends
+    the tokens j < seq_lens[b] - T + 1 + t.  q and P enter the matrix cores
+    as bf16 (fp16 on an INT8 cache).  ``options`` may carry split_tokens (a
+    multiple of 32), a prefill dispatch order and timing events.  The
+    key-split partials go to ``workspace`` or to a per-call allocation of the
+    size the library asks for.  Returns (out [B, T, H, D], lse [B, T, H])."""
     lib = load_library()
     dev = k_cache.device
     B, T, H, D = (int(x) for x in q_rot.shape)
     shape = make_shape(B, H, k_cache, block_table)
     _need(q_rot, "q_rot", dev, torch.float32, (B, T, H, D))
-    _need(k_cache, "k_cache", dev, torch.bfloat16)
-    _need(v_cache, "v_cache", dev, torch.bfloat16, tuple(k_cache.shape))
+    i8 = k_cache.dtype == torch.int8
+    if i8:
+        _need(v_cache, "v_cache", dev, torch.int8,
+              v_cache_shape_int8(k_cache, block_table is not None))
+        _check_scales(k_scale, v_scale, shape.n_kv_heads, dev)
+    else:
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("scales are only for INT8 caches")
+        _need(k_cache, "k_cache", dev, torch.bfloat16)
+        _need(v_cache, "v_cache", dev, torch.bfloat16, tuple(k_cache.shape))
     _need(seq_lens, "seq_lens", dev, torch.int32, (B,))
     if block_table is not None:
         _need(block_table, "block_table", dev, torch.int32)
@@ -750,6 +765,13 @@ def gqa_prefill_attn(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         nbytes = int(lib.gqa_prefill_workspace_size(ctypes.byref(shape), T, msl, opts))
         workspace = _workspace(dev, nbytes)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if i8:
+        _check(lib.gqa_prefill_attn_int8(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache),
+                                         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                         _ptr(seq_lens), _ptr(block_table), msl,
+                                         _scale_arg(scale), _ptr(out), _ptr(lse),
+                                         _ptr(workspace), wbytes, opts, _stream(dev)))
+        return out, lse
     _check(lib.gqa_prefill_attn(ctypes.byref(shape), T, _ptr(q_rot), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(seq_lens), _ptr(block_table), msl, _scale_arg(scale),
                                 _ptr(out), _ptr(lse), _ptr(workspace), wbytes, opts,

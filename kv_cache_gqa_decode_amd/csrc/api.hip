@@ -337,14 +337,16 @@ struct PfPlan {
   size_t workspace = 0;
 };
 
-// Validation shared by gqa_prefill_attn and its workspace size, and the plan
-// (may_split: a workspace is or will be given).
+// Validation shared by the prefill calls and their workspace size, and the
+// plan (may_split: a workspace is or will be given; dtype: the cache dtype
+// the call takes, -1 for either of bf16 and INT8).
 kvd_status prefill_setup(const kvd_shape* s, int32_t T, int32_t max_len, const kvd_options* options,
-                         bool may_split, Tuning* tu, PfPlan* pl) {
+                         bool may_split, Tuning* tu, PfPlan* pl, int dtype = KVD_BF16) {
   *pl = PfPlan{};
   kvd_status st = check_shape(s);
   if (st != KVD_OK) return st;
-  if (s->kv_dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+  if (dtype < 0 ? (s->kv_dtype != KVD_BF16 && s->kv_dtype != KVD_INT8) : s->kv_dtype != dtype)
+    return KVD_EUNSUPPORTED;
   if (T < 1 || T > s->max_seq_len) return KVD_EUNSUPPORTED;
   if (max_len < 0 || max_len > s->max_seq_len) return KVD_ERANGE;
   st = read_options(options, tu, true);
@@ -379,6 +381,61 @@ kvd_status prefill_setup(const kvd_shape* s, int32_t T, int32_t max_len, const k
     pl->lse_offset = (parts * s->head_dim * sizeof(float) + 255) / 256 * 256;
     pl->workspace = pl->lse_offset + (parts * sizeof(float) + 255) / 256 * 256;
   }
+  return KVD_OK;
+}
+
+// The prefill calls: a bf16 cache (no scales) or an INT8 cache (scales).
+kvd_status prefill_impl(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                        const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* seq_lens,
+                        const int32_t* block_table, int32_t max_seq_len_host, float scale,
+                        float* out, float* lse, void* workspace, size_t workspace_bytes,
+                        const kvd_options* options, void* stream) {
+  const bool i8 = k_scale != nullptr;
+  if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
+  if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
+  if (!std::isfinite(scale)) return KVD_EINVAL;
+  if (shape && (shape->block_size != 0) != (block_table != nullptr)) return KVD_EINVAL;
+  Tuning tu;
+  PfPlan pl;
+  kvd_status st = prefill_setup(shape, n_query, max_seq_len_host, options, workspace != nullptr,
+                                &tu, &pl, i8 ? KVD_INT8 : KVD_BF16);
+  if (st != KVD_OK) return st;
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace ||
+                           (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return KVD_EWORKSPACE;
+  if (shape->batch == 0) return KVD_OK;
+  DecodeParams p{};
+  p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
+  p.k_scale = k_scale; p.v_scale = v_scale;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G; p.T = n_query;
+  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
+  p.qscale = log2_scale(scale, shape->head_dim);
+  p.n_xcd = device_xcc_count();
+  // -1: the launcher's choice
+  p.grid_order = tu.order >= 0 ? tu.order - (KVD_ORDER_PREFILL_PAIRS_FASTEST - 1) : -1;
+  p.n_splits = pl.n_splits;
+  p.part_stride = pl.n_splits;
+  p.direct = pl.n_splits == 1 ? 1 : 0;
+  if (!p.direct) {
+    // uniform splits (n_big = n_splits), as the merge counts them
+    p.chunk = p.chunk2 = pl.chunk;
+    p.n_big = pl.n_splits;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lse_offset);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch l{s, tu.ev_start, tu.ev_stop};
+  const bool paged = shape->block_size != 0;
+  const hipError_t e = i8 ? launch_prefill_i8(p, paged, l) : launch_prefill_mfma(p, paged, l);
+  if (e != hipSuccess) return KVD_EHIP;
+  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
   return KVD_OK;
 }
 
@@ -552,7 +609,8 @@ size_t gqa_prefill_workspace_size(const kvd_shape* shape, int32_t n_query,
                                   int32_t max_seq_len_host, const kvd_options* options) {
   Tuning tu;
   PfPlan pl;
-  if (prefill_setup(shape, n_query, max_seq_len_host, options, true, &tu, &pl) != KVD_OK) return 0;
+  if (prefill_setup(shape, n_query, max_seq_len_host, options, true, &tu, &pl, -1) != KVD_OK)
+    return 0;
   return pl.workspace;
 }
 
@@ -561,47 +619,22 @@ kvd_status gqa_prefill_attn(const kvd_shape* shape, int32_t n_query, const float
                             const int32_t* block_table, int32_t max_seq_len_host, float scale,
                             float* out, float* lse, void* workspace, size_t workspace_bytes,
                             const kvd_options* options, void* stream) {
-  if (!q_rot || !k_cache || !v_cache || !seq_lens || !out) return KVD_EINVAL;
-  if (!aligned16(q_rot) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return KVD_EINVAL;
-  if (static_cast<const void*>(out) == static_cast<const void*>(q_rot)) return KVD_EINVAL;
-  if (!std::isfinite(scale)) return KVD_EINVAL;
-  if (shape && (shape->block_size != 0) != (block_table != nullptr)) return KVD_EINVAL;
-  Tuning tu;
-  PfPlan pl;
-  kvd_status st = prefill_setup(shape, n_query, max_seq_len_host, options, workspace != nullptr,
-                                &tu, &pl);
-  if (st != KVD_OK) return st;
-  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace ||
-                           (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
-    return KVD_EWORKSPACE;
-  if (shape->batch == 0) return KVD_OK;
-  DecodeParams p{};
-  p.q_rot = q_rot; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens; p.table = block_table;
-  p.out = out; p.lse = lse;
-  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
-  p.R = p.H / p.G; p.T = n_query;
-  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
-  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
-  p.block_shift = shape->block_size == 32 ? 1 : 0;
-  p.qscale = log2_scale(scale, shape->head_dim);
-  p.n_xcd = device_xcc_count();
-  // -1: the launcher's choice
-  p.grid_order = tu.order >= 0 ? tu.order - (KVD_ORDER_PREFILL_PAIRS_FASTEST - 1) : -1;
-  p.n_splits = pl.n_splits;
-  p.direct = pl.n_splits == 1 ? 1 : 0;
-  if (!p.direct) {
-    // uniform splits (n_big = n_splits), as the merge counts them
-    p.chunk = p.chunk2 = pl.chunk;
-    p.n_big = pl.n_splits;
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lse_offset);
-  }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Launch l{s, tu.ev_start, tu.ev_stop};
-  if (launch_prefill_mfma(p, shape->block_size != 0, l) != hipSuccess) return KVD_EHIP;
-  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
-  return KVD_OK;
+  return prefill_impl(shape, n_query, q_rot, k_cache, v_cache, nullptr, nullptr, seq_lens,
+                      block_table, max_seq_len_host, scale, out, lse, workspace,
+                      workspace_bytes, options, stream);
+}
+
+kvd_status gqa_prefill_attn_int8(const kvd_shape* shape, int32_t n_query, const float* q_rot,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* seq_lens,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 float scale, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, const kvd_options* options,
+                                 void* stream) {
+  if (!k_scale || !v_scale) return KVD_EINVAL;
+  return prefill_impl(shape, n_query, q_rot, k_cache, v_cache, k_scale, v_scale, seq_lens,
+                      block_table, max_seq_len_host, scale, out, lse, workspace,
+                      workspace_bytes, options, stream);
 }
 
 }  // extern "C"

@@ -49,7 +49,7 @@
 // past it, or of an invalid block, are read out of range (zeros, no memory
 // traffic).  Masked tokens get probability 0, and codes are finite, so they
 // contribute exactly zero.
-#include "mfma_tile.h"
+#include "i8_codes.h"
 
 namespace kvd {
 namespace {
@@ -57,8 +57,6 @@ namespace {
 using namespace mt;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTT = kI8TileTokens;     // tokens per wave-tile
 constexpr int kLimbs = 3;
@@ -68,22 +66,6 @@ constexpr int kBlkRegsI8 = (kMaxChunk / 16 / kMfmaWaves + 63) / 64;
 __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// Eight codes (two words, token order) -> eight exact fp16 values.
-__device__ __forceinline__ f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
-  constexpr uint32_t kExp = 0x64646464u;            // fp16 exponent byte of 1024
-  const f16x2 off = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
-  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;   // c + 128, unsigned
-  const f16x2 h0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x0, 0x04010400u)) + off;
-  const f16x2 h1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x0, 0x04030402u)) + off;
-  const f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x1, 0x04010400u)) + off;
-  const f16x2 h3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp, x1, 0x04030402u)) + off;
-  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
 // fp16 hi + lo of two floats (hi truncated, lo the exact remainder truncated:
 // hi + lo within 2^-21 of x).
 __device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32_t& lo) {

@@ -125,6 +125,8 @@ hipError_t launch_decode_i8(const DecodeParams& p, bool paged, const Launch& l);
 // n_splits 1: out and lse directly; more: (o, log2 lse) per key split into
 // part_o / part_lse, merged by launch_lse_reduce
 hipError_t launch_prefill_mfma(const DecodeParams& p, bool paged, const Launch& l);
+// the same on an INT8 cache (k_scale / v_scale set)
+hipError_t launch_prefill_i8(const DecodeParams& p, bool paged, const Launch& l);
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_build_units(const DecodeParams& p, hipStream_t stream);
 // Heads per pass of the VALU kernel for a given n_rep (1, 2, 4 or 8).

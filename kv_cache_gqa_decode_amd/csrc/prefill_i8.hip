@@ -1,0 +1,436 @@
+// Causal prefill attention over an INT8 cache on the fp16 matrix cores.
+//
+// "Transformer推理核心：KV Cache、GQA与RoPE原理与工程实践" §4.3: K and V held as
+// 8-bit codes with per-head scales (value = scale[g] * code); §4.2: the tiled
+// attention with an online softmax across key blocks; §5.1 b.v: the causal
+// mask.  Query t of sequence b attends the tokens j < L_b - T + 1 + t, as in
+// the bf16 prefill kernel, whose organisation this kernel keeps: a
+// workgroup owns 128 query rows of one KV head (each wave 32), walks the
+// 32-token key tiles below their bounds, and computes S^T = K Q^T and
+// O^T = V^T P^T so that each row's softmax lives in one lane column.
+//
+// What differs is the cache: the INT8 layout groups tokens by 16, each group
+// holding per KV head its 16 K rows [16][D] and its V block transposed
+// [D][16].  Per tile:
+//   * the two groups' K rows and V^T blocks (half the bytes of a bf16 tile)
+//     are copied HBM -> LDS by the four waves;
+//   * after a barrier the workgroup converts them once, cooperatively, into
+//     an fp16 tile: every code is exact in fp16 (codes_to_f16), K rows go
+//     to the bf16 kernel's swizzled row layout, and the V^T rows keep their
+//     transposed form with the tokens reordered so that the 8 tokens a lane
+//     feeds to the P V matrix op are contiguous -- no transposing read;
+//   * after a second barrier the next tile's copies go out and the waves
+//     compute on the fp16 tile.
+// Converting once per workgroup costs each wave a quarter of a tile's codes;
+// converting operands as each wave reads them would cost all four waves the
+// whole tile.
+//
+// Arithmetic: q * scale * log2 e and the probabilities enter the matrix
+// cores rounded once to fp16 (finer than the bf16 prefill's rounding),
+// accumulation is fp32.  The raw scores q . code are multiplied by k_scale[g]
+// before the softmax, the output by v_scale[g]; one fp32 running sum of the
+// probabilities normalises the output and gives the log-sum-exp.  Key splits
+// and dispatch orders are those of the bf16 prefill kernel.
+#include "i8_codes.h"
+
+namespace kvd {
+namespace {
+
+using namespace mt;
+
+constexpr int kWaves = 4;
+constexpr int kCols = 32;                        // query rows per wave
+constexpr int kRows = kWaves * kCols;            // query rows per workgroup
+constexpr int kTT = 32;                          // key tokens per tile
+static_assert(kRows == kPrefillRows && kTT == kPrefillTile, "the host plans with these");
+
+template <int D>
+struct I8PfGeo {
+  static constexpr int KB = D / 32;              // 32-dim blocks of the score contraction
+  static constexpr int CB = D / 16;              // 16-dim blocks of the output
+  static constexpr int NDC = D / 8;              // 8-dim (16-byte fp16) chunks of a K row
+  static constexpr int kGroup = 16 * D;          // bytes of one head's group: K rows or V^T
+  static constexpr int kStage = 4 * kGroup;      // staged codes: K of 2 groups, then V^T
+  static constexpr int NCI = kStage / 1024;      // copy instructions per tile
+  static constexpr int kKBytes = kTT * 2 * D;    // fp16 K tile
+  static constexpr int kVRow = kTT * 2 + 16;     // fp16 V^T row: 32 tokens, 16 bytes of pad
+  static constexpr int kVBytes = D * kVRow;
+  static constexpr int kLds = kStage + kKBytes + kVBytes;
+  static_assert(NCI % kWaves == 0, "copies split over the waves");
+  // K rows as in the bf16 prefill kernel: chunk dc of row t at slot dc ^ swz(t)
+  __device__ __forceinline__ static int swz(int t) {
+    return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
+  }
+  // Position of token t in a V^T row: the lane that feeds tokens 4m + r
+  // (m = 0..7) to the P V matrix op reads them at r * 8 + m.
+  __device__ __forceinline__ static int vpos(int t) { return (t & 3) * 8 + (t >> 2); }
+};
+
+// Four 16-byte LDS reads, waited for together (inline, for the reason given
+// at read_vt_tr: a compiler-visible LDS read would first wait for the next
+// tile's copies).
+__device__ __forceinline__ void lds_read4(const uint32_t (&a)[4], u32x4 (&r)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+__device__ __forceinline__ void lds_read2(const uint32_t (&a)[2], u32x4 (&r)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a[0]), "v"(a[1]));
+}
+template <int N>
+__device__ __forceinline__ void lds_read(const uint32_t (&a)[N], u32x4 (&r)[N]) {
+  if constexpr (N == 4) {
+    lds_read4(a, r);
+  } else {
+    static_assert(N == 2, "two or four operands");
+    lds_read2(a, r);
+  }
+}
+
+// Unit and dispatch order as in the bf16 prefill kernel (grid_order 0: unit
+// x mod U; 1: unit x / nqt, a unit's tiles together; 2: the order of 1 cut
+// into per-XCD contiguous runs).  Held to 168 registers: three workgroups
+// per CU.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_i8_kernel(DecodeParams p) {
+  using PG = I8PfGeo<D>;
+  constexpr int KB = PG::KB, CB = PG::CB, NB = kCols / 16;
+  __shared__ __align__(16) char smem[PG::kLds];
+
+  const int R = p.R, T = p.T;
+  const int64_t ncols = static_cast<int64_t>(T) * R;
+  const int nqt = static_cast<int>((ncols + kRows - 1) / kRows);
+  const int nsplit = p.n_splits;
+  const int64_t units = static_cast<int64_t>(p.B) * p.G * nsplit;
+  int64_t lin = blockIdx.x;
+  if (p.grid_order == 2) {
+    const int64_t nx = p.n_xcd, nwg = gridDim.x;
+    const int64_t k = lin % nx, per = nwg / nx, rem = nwg % nx;
+    lin = k * per + (k < rem ? k : rem) + lin / nx;
+  }
+  const int unit = static_cast<int>(p.grid_order == 0 ? lin % units : lin / nqt);
+  const int qt = nqt - 1 - static_cast<int>(p.grid_order == 0 ? lin / units : lin % nqt);
+  const int bg = unit / nsplit, split = unit - bg * nsplit;
+  const int g = bg % p.G, b = bg / p.G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+
+  int L = scalar_load_i32(p.seq_lens + b);
+  L = L < 0 ? 0 : (L > p.max_len_host ? p.max_len_host : L);
+  const int win = L - T + 1;                      // query t sees the tokens j < win + t
+  const int64_t c0 = static_cast<int64_t>(qt) * kRows;
+  const int64_t c_last = (c0 + kRows < ncols ? c0 + kRows : ncols) - 1;
+  int kmax = win + static_cast<int>(c_last / R);
+  kmax = kmax < L ? kmax : L;
+  const int64_t cw = c0 + wave * kCols;
+  const int wbound = win + static_cast<int>((cw < ncols ? cw : c_last) / R);
+  int k_lo = 0, k_hi = kmax;
+  if (nsplit > 1) {
+    if (split >= (L + p.chunk - 1) / p.chunk) return;
+    k_lo = split * p.chunk;
+    k_hi = k_lo + p.chunk < kmax ? k_lo + p.chunk : kmax;
+  }
+
+  int cbound[NB];
+  int64_t qrow[NB];
+  bool real[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t c = cw + nb * 16 + n;
+    real[nb] = c < ncols;
+    const int t = static_cast<int>((real[nb] ? c : 0) / R);
+    const int r = static_cast<int>((real[nb] ? c : 0) - static_cast<int64_t>(t) * R);
+    cbound[nb] = real[nb] ? win + t : 0;
+    qrow[nb] = (static_cast<int64_t>(b) * T + t) * p.H + g * R + r;
+  }
+  // q * scale * log2(e) rounded to fp16: lane (n, grp) of block (nb, kb)
+  // holds dims kb*32 + grp*8 .. +7 of its row
+  f16x8 qv[NB][KB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float* src = p.q_rot + qrow[nb] * D + grp * 8;
+    const float qs = real[nb] ? p.qscale : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const float4 x0 = *reinterpret_cast<const float4*>(src + kb * 32);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + kb * 32 + 4);
+      const u32x4 h = {pack_f16(x0.x * qs, x0.y * qs), pack_f16(x0.z * qs, x0.w * qs),
+                       pack_f16(x1.x * qs, x1.y * qs), pack_f16(x1.z * qs, x1.w * qs)};
+      qv[nb][kb] = __builtin_bit_cast(f16x8, h);
+    }
+  }
+  const float ksc = p.k_scale[g], vsc = p.v_scale[g];
+
+  // The head's 16-token groups: group j16 of the sequence (contiguous: b's
+  // row of S_max/16 groups; paged: the pool group the table gives, -1 when
+  // its block id is outside the pool).
+  const int64_t gstride = static_cast<int64_t>(p.G) * PG::kGroup;   // bytes per group
+  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * PG::kGroup;
+  const char* vbase = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * PG::kGroup;
+  // One descriptor per half-tile group and operand: K spans the rows below
+  // kmax (the others read as zeros), V^T the whole block of a valid group
+  // (its tokens past kmax are masked, and codes are finite, so they add 0);
+  // an invalid group reads as zeros without touching memory.
+  struct TileSrc { rsrc_t k[2], v[2]; bool ok[2]; };
+  auto tile_src = [&](int j0) {
+    TileSrc ts;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lo = j0 + 16 * h;
+      int rows = kmax - lo;
+      rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+      int64_t grp16;
+      ts.ok[h] = true;
+      if (PAGED) {
+        const int gi = rows > 0 ? paged_group(p, b, lo >> 4) : 0;
+        if (gi < 0) { rows = 0; ts.ok[h] = false; }
+        grp16 = gi < 0 ? 0 : gi;
+      } else {
+        grp16 = static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (lo >> 4);
+      }
+      rows = __builtin_amdgcn_readfirstlane(rows);
+      ts.k[h] = make_rsrc(kbase + grp16 * gstride, static_cast<uint32_t>(rows) * D);
+      ts.v[h] = make_rsrc(vbase + grp16 * gstride, rows > 0 ? PG::kGroup : 0u);
+    }
+    return ts;
+  };
+  lds_char* const stage = (lds_char*)(smem);
+  // this wave's copies: instructions wave + 4 i, each 1 KiB of one part
+  // (K group 0, K group 1, V^T group 0, V^T group 1)
+  auto issue = [&](const TileSrc& ts) {
+#pragma unroll
+    for (int i = 0; i < PG::NCI / kWaves; ++i) {
+      const int jj = wave + kWaves * i;
+      const int part = jj / (PG::kGroup / 1024);
+      const uint32_t off = static_cast<uint32_t>((jj % (PG::kGroup / 1024)) * 1024 + lane * 16);
+      const rsrc_t r = part == 0 ? ts.k[0] : part == 1 ? ts.k[1] : part == 2 ? ts.v[0] : ts.v[1];
+      copy16_to_lds(r, stage + jj * 1024, off);
+    }
+  };
+  // Convert the staged codes into the fp16 tile (all 256 threads).
+  char* const kt16 = smem + PG::kStage;
+  char* const vt16 = kt16 + PG::kKBytes;
+  auto convert = [&]() {
+    // K: chunk (t, dc) = 8 codes -> 16 bytes at row t, slot dc ^ swz(t)
+#pragma unroll
+    for (int i = 0; i < kTT * PG::NDC / 256; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      const int t = u / PG::NDC, dc = u % PG::NDC;
+      const uint2 w = *reinterpret_cast<const uint2*>(smem + (t >> 4) * PG::kGroup +
+                                                      (t & 15) * D + dc * 8);
+      *reinterpret_cast<f16x8*>(kt16 + t * 2 * D + 16 * (dc ^ PG::swz(t))) =
+          codes_to_f16(w.x, w.y);
+    }
+    // V^T: (dimension d, group h) = 16 codes; tokens 16h + 4m + r (m = 0..3)
+    // go to positions r * 8 + 4h + m
+    for (int u = threadIdx.x; u < 2 * D; u += 256) {
+      const int d = u % D, h = u / D;
+      const uint4 w = *reinterpret_cast<const uint4*>(smem + 2 * PG::kGroup + h * PG::kGroup + d * 16);
+      const f16x8 lo = codes_to_f16(w.x, w.y), hi = codes_to_f16(w.z, w.w);   // tokens 0-7, 8-15
+      const uint32_t a0 = __builtin_bit_cast(u32x4, lo)[0], a1 = __builtin_bit_cast(u32x4, lo)[1];
+      const uint32_t a2 = __builtin_bit_cast(u32x4, lo)[2], a3 = __builtin_bit_cast(u32x4, lo)[3];
+      const uint32_t b0 = __builtin_bit_cast(u32x4, hi)[0], b1 = __builtin_bit_cast(u32x4, hi)[1];
+      const uint32_t b2 = __builtin_bit_cast(u32x4, hi)[2], b3 = __builtin_bit_cast(u32x4, hi)[3];
+      // word k of lo holds tokens 2k, 2k+1; of hi tokens 8 + 2k, 9 + 2k.
+      // r = 0: tokens 0, 4, 8, 12; r = 1: 1, 5, 9, 13; r = 2: 2, 6, 10, 14; r = 3: 3, 7, 11, 15
+      const uint32_t lo16 = 0x05040100u, hi16 = 0x07060302u;   // low / high halves of two words
+      char* row = vt16 + d * PG::kVRow + 8 * h;
+      *reinterpret_cast<uint2*>(row + 0) =
+          make_uint2(__builtin_amdgcn_perm(a2, a0, lo16), __builtin_amdgcn_perm(b2, b0, lo16));
+      *reinterpret_cast<uint2*>(row + 16) =
+          make_uint2(__builtin_amdgcn_perm(a2, a0, hi16), __builtin_amdgcn_perm(b2, b0, hi16));
+      *reinterpret_cast<uint2*>(row + 32) =
+          make_uint2(__builtin_amdgcn_perm(a3, a1, lo16), __builtin_amdgcn_perm(b3, b1, lo16));
+      *reinterpret_cast<uint2*>(row + 48) =
+          make_uint2(__builtin_amdgcn_perm(a3, a1, hi16), __builtin_amdgcn_perm(b3, b1, hi16));
+    }
+  };
+
+  // LDS read addresses: K operand rows 16 h2 + tile_row(n), chunk kb*4 + grp;
+  // V^T operand dimension 16 cb + n, tokens grp*8 .. +7
+  const uint32_t kaddr = lds_addr((lds_char*)(kt16));
+  uint32_t koff[2][KB];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int t = 16 * h2 + tile_row(n);
+      koff[h2][kb] = kaddr + static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
+    }
+  const uint32_t vaddr = lds_addr((lds_char*)(vt16)) + static_cast<uint32_t>(n * PG::kVRow + grp * 16);
+
+  f32x4 acc[NB][CB];
+  float m[NB], lx[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf; lx[nb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nkt = k_hi > k_lo ? (k_hi + kTT - 1) / kTT : 0;
+  const int kt_lo = k_lo / kTT;
+  TileSrc cur;
+  if (nkt > kt_lo) {
+    cur = tile_src(kt_lo * kTT);
+    issue(cur);
+  }
+  auto tile = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int j0 = kt * kTT;
+    vmem_wait<0>();                    // this wave's copies of tile kt have landed
+    __syncthreads();                   // every wave's copies; the fp16 tile no longer read
+    convert();
+    __syncthreads();                   // the fp16 tile complete; the staged codes no longer read
+    const TileSrc now = cur;
+    if (kt + 1 < nkt) {
+      cur = tile_src(j0 + kTT);
+      issue(cur);
+    }
+    const bool masked = (MASK && j0 + kTT > wbound) || (PAGED && !(now.ok[0] && now.ok[1]));
+
+    // S^T (raw, times k_scale below): token rows 16 h2 + 4 grp + j
+    f32x4 s[NB][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 kr[KB];
+      lds_read<KB>(koff[h2], kr);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          c = mfma_f16(__builtin_bit_cast(f16x8, kr[kb]), qv[nb][kb], c);
+        s[nb][h2] = c;
+      }
+    }
+
+    f16x8 pb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j] * ksc;
+      if (masked) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = j0 + 16 * h2 + tile_row(4 * grp + j);
+            if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
+          }
+      }
+      float mt = sv[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
+        const float mn = fmaxf(m[nb], mt);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        lx[nb] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
+        m[nb] = mn;
+      }
+      const float ref = m[nb] == kNegInf ? 0.f : m[nb];
+      float e[8];
+      float px = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+        px += e[j];
+      }
+      const u32x4 h = {pack_f16(e[0], e[1]), pack_f16(e[2], e[3]), pack_f16(e[4], e[5]),
+                       pack_f16(e[6], e[7])};
+      lx[nb] += px;
+      pb[nb] = __builtin_bit_cast(f16x8, h);
+    }
+
+    // O^T[d][row] += V^T[d][t] P^T[t][row], four output blocks per read
+#pragma unroll
+    for (int c4 = 0; c4 < CB; c4 += 4) {
+      constexpr int NR = CB < 4 ? CB : 4;
+      uint32_t va[NR];
+      u32x4 vr[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) va[i] = vaddr + static_cast<uint32_t>((c4 + i) * 16 * PG::kVRow);
+      lds_read<NR>(va, vr);
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb][c4 + i] = mfma_f16(__builtin_bit_cast(f16x8, vr[i]), pb[nb], acc[nb][c4 + i]);
+    }
+  };
+
+  const int wg_bound = win + static_cast<int>(c0 / R);
+  const int n_full = wg_bound >= kTT ? (wg_bound / kTT < nkt ? wg_bound / kTT : nkt) : 0;
+  int kt = kt_lo;
+  for (; kt < n_full; ++kt) tile(kt, std::false_type{});
+  for (; kt < nkt; ++kt) tile(kt, std::true_type{});
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    lx[nb] += __shfl_xor(lx[nb], 16);
+    lx[nb] += __shfl_xor(lx[nb], 32);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (!real[nb]) continue;
+    const float inv = lx[nb] > 0.f ? vsc / lx[nb] : 0.f;
+    const float lse2 = lx[nb] > 0.f ? m[nb] + log2f(lx[nb]) : kNegInf;
+    float* dst;
+    if (nsplit == 1) {
+      dst = p.out + qrow[nb] * D + 4 * grp;
+      if (grp == 0 && p.lse) p.lse[qrow[nb]] = lse2 * 0.69314718055994531f;
+    } else {
+      const int64_t slot = qrow[nb] * nsplit + split;
+      dst = p.part_o + slot * D + 4 * grp;
+      if (grp == 0) p.part_lse[slot] = lse2;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      *reinterpret_cast<f32x4*>(dst + 16 * cb) = acc[nb][cb] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_i8(const DecodeParams& p_in, bool paged, const Launch& l) {
+  DecodeParams p = p_in;
+  if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128) || !p.k_scale || !p.v_scale)
+    return hipErrorInvalidValue;
+  if (!paged && p.max_seq_len % 16 != 0) return hipErrorInvalidValue;
+  if (p.n_xcd < 1 || p.grid_order < -1 || p.grid_order > 2 || p.n_splits < 1)
+    return hipErrorInvalidValue;
+  if (p.n_splits > 1 && (p.chunk < kTT || p.chunk % kTT != 0 || !p.part_o || !p.part_lse))
+    return hipErrorInvalidValue;
+  const int64_t ncols = static_cast<int64_t>(p.T) * p.R;
+  const int64_t nqt = (ncols + kRows - 1) / kRows;
+  const int64_t units = static_cast<int64_t>(p.B) * p.G * p.n_splits;
+  if (p.grid_order < 0)
+    p.grid_order = units < p.n_xcd ? 0 : (p.n_splits > 1 || nqt > 64 ? 2 : 1);
+  const int64_t wgs = nqt * units;
+  if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  void (*k)(DecodeParams) = p.D == 64 ? (paged ? prefill_i8_kernel<64, true> : prefill_i8_kernel<64, false>)
+                                      : (paged ? prefill_i8_kernel<128, true> : prefill_i8_kernel<128, false>);
+  return launch_kernel(k, grid, dim3(256), l, p);
+}
+
+}  // namespace kvd

@@ -204,6 +204,30 @@ def test_prefill_validates(lib):
         assert prefill(lib, shape(batch=0), 4, opts=B._COptions(dispatch_order=order)) == EINVAL
 
 
+def test_prefill_int8_validates(lib):
+    """The INT8 prefill takes INT8 shapes and both scales; the bf16 one
+    refuses INT8 shapes; the workspace size serves both."""
+    O = B._COptions
+
+    def pf8(sh, ks=FAKE, vs=FAKE, opts=None, msl=32):
+        return lib.gqa_prefill_attn_int8(ctypes.byref(sh), 4, FAKE, FAKE, FAKE, ks, vs, FAKE,
+                                         None, msl, 0.0, ctypes.c_void_p(0x2000), None, None, 0,
+                                         None if opts is None else ctypes.byref(opts), None)
+
+    i8 = shape(kv_dtype=2)
+    assert pf8(shape()) == EUNSUPPORTED                         # bf16 shape
+    assert pf8(i8, ks=None) == EINVAL and pf8(i8, vs=None) == EINVAL
+    assert pf8(shape(kv_dtype=2, batch=0)) == OK
+    assert pf8(i8, opts=O(kernel=3)) == EINVAL
+    assert pf8(i8, opts=O(split_tokens=16)) == EINVAL          # whole 32-token tiles
+    assert pf8(i8, opts=O(split_tokens=32), msl=64) == EWORKSPACE   # two splits, no workspace
+    assert prefill(lib, i8, 4) == EUNSUPPORTED
+    sh = shape(kv_dtype=2, max_seq_len=256)
+    n = lib.gqa_prefill_workspace_size(ctypes.byref(sh), 4, 256, ctypes.byref(O(split_tokens=64)))
+    assert n == lib.gqa_prefill_workspace_size(ctypes.byref(shape(max_seq_len=256)), 4, 256,
+                                               ctypes.byref(O(split_tokens=64))) > 0
+
+
 def test_prefill_key_split_workspace(lib):
     """A requested key split sizes its partials, (o[D], log2 lse) per query
     row and split, each array 256-byte aligned; without that workspace the

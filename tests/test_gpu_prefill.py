@@ -25,11 +25,12 @@ pytestmark = pytest.mark.gpu
 
 
 def gpu_prefill(t, s: W.Spec, max_len: int, style="interleaved", options=None):
+    sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if s.dtype == "i8" else {}
     q_rot = kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                      t["positions"], t["block_table"], base=s.rope_base,
-                                     style=style)
+                                     style=style, **sc)
     out, lse = kvd.gqa_prefill_attn(q_rot, t["k_cache"], t["v_cache"], t["seq_lens"],
-                                    t["block_table"], max_seq_len=max_len, options=options)
+                                    t["block_table"], max_seq_len=max_len, options=options, **sc)
     torch.cuda.synchronize()
     return q_rot, out, lse
 
@@ -56,14 +57,14 @@ def check_prefill(p: W.Problem, what="", units=None, style="interleaved", option
     return e
 
 
-def _spec(B, H, G, D, S, paged=False, block_size=16, q_gain=2.0):
+def _spec(B, H, G, D, S, paged=False, block_size=16, q_gain=2.0, dtype="bf16"):
     if paged:
         s = W.spec("c4", batch=B, n_heads=H, n_kv_heads=G, head_dim=D,
                    num_blocks=B * (S // block_size) + 8, max_blocks_per_seq=S // block_size,
-                   block_size=block_size, q_gain=q_gain)
+                   block_size=block_size, q_gain=q_gain, dtype=dtype)
     else:
         s = W.spec("c3", batch=B, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=S,
-                   q_gain=q_gain)
+                   q_gain=q_gain, dtype=dtype)
     return s
 
 
@@ -227,3 +228,57 @@ def test_long_prompt_sampled():
     ts = np.r_[edges, rng.integers(0, T, 4096 - edges.size)]
     units = [(0, int(t), int(h)) for t, h in zip(ts, rng.integers(0, s.n_heads, ts.size))]
     check_prefill(p, units=units, what="prompt 8192, 4096 rows")
+
+
+# INT8 caches ([KVGR] §4.3): codes with per-head scales, converted once per
+# tile to exact fp16; q and P rounded to fp16 (finer than the bf16 prefill's
+# bf16), so the prefill gates apply.  The caches (codes of the appended
+# window) must match bit for bit.
+
+@pytest.mark.parametrize("D,T", [(64, 1), (64, 100), (128, 33), (128, 257)])
+def test_int8_prompt_from_empty(D, T):
+    s = _spec(2, 8, 2, D, 512, dtype="i8")
+    p = W.make_window(s, T, lengths=np.array([T, T], np.int32))
+    check_prefill(p, what=f"INT8 prompt D={D} T={T}")
+
+
+@pytest.mark.parametrize("paged,block_size", [(False, 16), (True, 16), (True, 32)])
+@pytest.mark.parametrize("split", [0, 64])
+def test_int8_chunk_after_history(paged, block_size, split):
+    T = 100
+    lens = np.array([T, T + 1, T + 15, T + 300, 900, 1024], np.int32)
+    s = _spec(lens.size, 32, 8, 128, 1024, paged, block_size, dtype="i8")
+    p = W.make_window(s, T, lengths=lens)
+    check_prefill(p, what=f"INT8 chunk paged={paged}/{block_size} split={split}",
+                  options=kvd.Options(split_tokens=split))
+
+
+@pytest.mark.parametrize("n_rep", [1, 4, 32])
+def test_int8_gqa_ratios_and_orders(n_rep):
+    H = 32
+    s = _spec(2, H, H // n_rep, 128, 640, dtype="i8")
+    p = W.make_window(s, 150, lengths=np.array([150, 600], np.int32))
+    for order in ORDERS:
+        check_prefill(p, what=f"INT8 n_rep={n_rep} order {order}",
+                      options=kvd.Options(dispatch_order=order))
+
+
+def test_int8_peaked_scores():
+    s = _spec(2, 32, 8, 128, 1024, q_gain=16.0, dtype="i8")
+    p = W.make_window(s, 200, lengths=np.array([400, 1024], np.int32))
+    check_prefill(p, what="INT8 peaked")
+
+
+def test_int8_prompt_2048_every_row():
+    T = 2048
+    s = W.spec("c5", max_seq_len=T, q_gain=2.0, dtype="i8")
+    p = W.make_window(s, T, lengths=np.array([T], np.int32))
+    check_prefill(p, what="INT8 prompt 2048, all rows")
+
+
+def test_int8_key_split_after_long_history():
+    """A 64-token chunk after a 20K history: split automatically."""
+    T, L = 64, 20480
+    s = _spec(1, 8, 2, 128, L, dtype="i8")
+    p = W.make_window(s, T, lengths=np.array([L], np.int32))
+    check_prefill(p, what="INT8 chunk 64 after 20K, automatic split")
