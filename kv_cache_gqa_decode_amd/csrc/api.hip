@@ -121,6 +121,7 @@ struct Plan {
   int grid_order = 0;   // matrix-core dispatch order (DecodeParams::grid_order)
   size_t units_offset = 0;   // work list in the workspace (grid_order 3)
   int head_groups = 1;  // VALU: query-head groups per KV head
+  int row_groups = 1;   // INT8: workgroups of 16 query rows per KV head (DecodeParams)
   int rb = 1;           // VALU: heads per pass
   int64_t wgs = 0;
   size_t workspace = 0;
@@ -166,6 +167,21 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
     if (kernel == 0 && T > 1) return KVD_EUNSUPPORTED;
   }
   pl->kernel = kernel;
+  // The INT8 kernel with 17 to 32 query rows per KV head holds one
+  // workgroup per CU (its registers); when the KV bytes at the bound fit in
+  // half of the 256 MB memory-side cache, two workgroups of 16 rows each
+  // (two per CU) read each tile instead, the second read served from that
+  // cache.  Measured on larger caches, where it is not (5 new tokens on the
+  // batched workload), the same split was slower: 151 against 130 us; on a
+  // 1024-token sequence with 5 new tokens (8 KV heads) the kernel went from
+  // 12.2 to 9.4 us.  Its units are sized for one round at one workgroup per
+  // CU: longer units amortise each workgroup's start (a 128K MQA sequence:
+  // 1024-token splits 16.1 us, 512 18.3, 256 24.7, 2048 20.9).
+  pl->row_groups = 1;
+  if (kernel == 2 && RT > 16 &&
+      static_cast<int64_t>(s->batch) * s->n_kv_heads * max_len_host * 2 * s->head_dim <=
+          (int64_t{128} << 20))
+    pl->row_groups = 2;
   if (kernel >= 1) {
     pl->rb = R;
     pl->head_groups = 1;
@@ -213,11 +229,13 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
     // 321 us against 328 us at 1024; the batch of contexts up to 8K, 1024
     // tokens 179 us against 180 us at 2048; one 128K sequence, 512 tokens
     // 79 us against 81 at 1024 and 83 at 256).
+    const bool one_per_cu = RT > 16 && pl->row_groups == 1;
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
-                         static_cast<int64_t>(max_len_host);
-    const int64_t slots = static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (RT > 16 ? 1 : 2));
+                         pl->row_groups * static_cast<int64_t>(max_len_host);
+    const int64_t slots =
+        static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (one_per_cu || pl->row_groups > 1 ? 1 : 2));
     const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : (s->batch > 1 ? 8 : 4));
-    const int cap = kernel == 2 && RT > 16 ? 4096 : 2048;
+    const int cap = kernel == 2 && one_per_cu ? 4096 : 2048;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
     // Short units pay the workgroup's fixed cost (q loads, merge, partial
@@ -256,7 +274,8 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
   // 10% (paged) faster than without the list.  Grid
   // orders 1 (contiguous) and 2 (paged) without the list: heads fastest,
   // then sequences, splits slowest (resp. sequences slowest).
-  const int64_t list_wgs = static_cast<int64_t>(s->n_kv_heads) * s->batch * pl->n_splits;
+  const int64_t list_wgs =
+      static_cast<int64_t>(s->n_kv_heads) * pl->row_groups * s->batch * pl->n_splits;
   const bool list_ok = kernel >= 1 && pl->n_splits > 1 && list_wgs <= 0x7fffffff;
   // Up to 64 sequences the split kernel's waves derive the list themselves
   // from the lengths (order 4, one sequence per lane): the same order
@@ -268,7 +287,8 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
   if (ord >= 0 && ord <= 2) pl->grid_order = ord;
   if (ord == 3 && list_ok) pl->grid_order = 3;   // a single split (or the VALU kernel): no list
   if (ord == 4 && wave_list_ok) pl->grid_order = 4;
-  pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups * s->batch;
+  pl->wgs = static_cast<int64_t>(pl->n_splits) * s->n_kv_heads * pl->head_groups *
+            pl->row_groups * s->batch;
   if (pl->n_splits > 1) {
     const size_t rows = static_cast<size_t>(s->batch) * T * s->n_heads * pl->n_splits;
     size_t o_bytes = rows * s->head_dim * sizeof(float);
@@ -681,7 +701,7 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
   p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
-  p.n_splits = pl.n_splits; p.head_groups = pl.head_groups;
+  p.n_splits = pl.n_splits; p.head_groups = pl.head_groups; p.row_groups = pl.row_groups;
   p.part_stride = pl.n_splits;
   p.qscale = log2_scale(scale, shape->head_dim);
   p.direct = pl.n_splits <= 1 ? 1 : 0;
@@ -830,6 +850,7 @@ kvd_status mixed_impl(const kvd_shape* shape, int32_t window, const float* q_rot
     h.block_shift = shape->block_size == 32 ? 1 : 0;
     h.chunk = mp.hist.chunk; h.chunk2 = mp.hist.chunk2; h.n_big = mp.hist.n_big;
     h.n_splits = mp.n1; h.head_groups = mp.hist.head_groups; h.grid_order = mp.hist.grid_order;
+    h.row_groups = mp.hist.row_groups;
     h.len_mode = 1; h.split_base = 0;
     if (h.grid_order == 3) {
       h.n_units = reinterpret_cast<int32_t*>(ws + mp.units1);

@@ -122,10 +122,12 @@ constexpr int smem_bytes_i8() {
   return stage > merge ? stage : merge;
 }
 
-// One (sequence b, KV head g, split) unit computed by the whole workgroup.
+// One (sequence b, KV head g, split) unit computed by the whole workgroup:
+// query rows rb .. rb + 16 NB - 1 of the KV head (rb > 0 when the rows are
+// split over row groups).
 template <int D, int NB, bool PAGED>
 __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, int b, int g,
-                                             int split) {
+                                             int split, int rb) {
   constexpr int KB = D / 64;          // 64-dim blocks of the score contraction
   constexpr int CB = D / 16;          // 16-dim blocks of the output
   constexpr int kWaves = kMfmaWaves;
@@ -140,9 +142,10 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
-      for (int idx = threadIdx.x; idx < RT * D; idx += 256) {
+      const int nr = min(16 * NB, RT - rb);
+      for (int idx = threadIdx.x; idx < nr * D; idx += 256) {
         const int r = idx / D, d = idx - r * D;
-        const int64_t row = query_row(p, b, g, r);
+        const int64_t row = query_row(p, b, g, rb + r);
         p.out[row * D + d] = 0.f;
         if (d == 0 && p.lse) p.lse[row] = kNegInf;
       }
@@ -156,7 +159,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   int cbound[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int c = nb * 16 + (threadIdx.x & 15);
+    const int c = rb + nb * 16 + (threadIdx.x & 15);
     cbound[nb] = c < RT ? win + c / R : L;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,7 +185,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int h = nb * 16 + n;
+      const int h = rb + nb * 16 + n;
       const float* src = p.q_rot + query_row(p, b, g, h < RT ? h : 0) * D + grp * 16;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -307,7 +310,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   const float kscale = p.k_scale[g];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const bool real = nb * 16 + n < RT;
+    const bool real = rb + nb * 16 + n < RT;
     float amax = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -501,9 +504,9 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   const float vscale = p.v_scale[g];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int nh = min(16, RT - nb * 16);
+    const int nh = min(16, RT - rb - nb * 16);
     if (nh <= 0) break;
-    merge_waves<D>(p, smem, b, g, split, nb * 16, nh, acc[nb],
+    merge_waves<D>(p, smem, b, g, split, rb + nb * 16, nh, acc[nb],
                    m[nb] == kNegInf ? kNegInf : m[nb] - kPBias, lsum[nb], vscale);
   }
 }
@@ -516,7 +519,9 @@ void decode_i8_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
   Unit u;
   if (!unit_at(p, u)) return;
-  run_split_i8<D, 1, PAGED>(p, smem, u.b, u.g, u.split);
+  // with row groups the unit's head index is (KV head, row group)
+  const int rg = p.row_groups > 1 ? p.row_groups : 1;
+  run_split_i8<D, 1, PAGED>(p, smem, u.b, u.g / rg, u.split, 16 * (u.g % rg));
 }
 // 17 to 32 query rows per KV head (two column blocks): at D = 128 the q
 // limbs, scores and accumulators of the second block do not fit beside the
@@ -527,7 +532,7 @@ __global__ __launch_bounds__(256) void decode_i8_kernel_wide(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
   Unit u;
   if (!unit_at(p, u)) return;
-  run_split_i8<D, 2, PAGED>(p, smem, u.b, u.g, u.split);
+  run_split_i8<D, 2, PAGED>(p, smem, u.b, u.g, u.split, 0);
 }
 
 template <int D, int NB>
@@ -538,9 +543,12 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, const Launch& l) {
   return launch_kernel(k, split_grid(p), dim3(256), l, p);
 }
 
+// Up to 16 rows per workgroup: the one-block kernel (with row groups, each
+// takes 16 of the head's rows); 17 to 32 in one workgroup: the wide kernel.
 template <int D>
 hipError_t launch_d(const DecodeParams& p, bool paged, const Launch& l) {
-  return p.R * p.T <= 16 ? launch_nb<D, 1>(p, paged, l) : launch_nb<D, 2>(p, paged, l);
+  return p.R * p.T <= 16 || p.row_groups > 1 ? launch_nb<D, 1>(p, paged, l)
+                                             : launch_nb<D, 2>(p, paged, l);
 }
 
 }  // namespace
@@ -550,6 +558,8 @@ hipError_t launch_decode_i8(const DecodeParams& p, bool paged, const Launch& l) 
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
       !p.k_scale || !p.v_scale || (!paged && p.max_seq_len % 16 != 0))
     return hipErrorInvalidValue;
+  // row groups of 16 rows must cover the head's rows exactly
+  if (p.row_groups > 1 && (p.row_groups != 2 || p.R * p.T <= 16)) return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }
 

@@ -489,7 +489,8 @@ hipError_t launch_d(const DecodeParams& p, bool paged, const Launch& l) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l) {
   if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
-      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32)
+      p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
+      p.row_groups > 1)
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }

@@ -61,7 +61,16 @@ struct DecodeParams {
   int32_t window;
   int32_t seg2_base;
   int32_t seg2_chunk;
+  // INT8 kernel: the query rows of a KV head split over row_groups
+  // workgroups of 16 rows each (0 or 1: one workgroup takes all); units then
+  // run over G * row_groups (KV head, row group) pairs
+  int32_t row_groups;
 };
+
+// (KV head, row group) pairs the units of a split kernel run over
+__host__ __device__ __forceinline__ int unit_heads(const DecodeParams& p) {
+  return p.row_groups > 1 ? p.G * p.row_groups : p.G;
+}
 
 struct RopeParams {
   const void* q;            // [B, H, D] or null

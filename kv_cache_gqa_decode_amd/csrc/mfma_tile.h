@@ -273,7 +273,7 @@ __device__ __forceinline__ Unit unit_of(const DecodeParams& p, int x, int y, int
 __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u) {
   const int lane = threadIdx.x & 63;
   const int id = static_cast<int>(blockIdx.x);
-  const int k = id / p.G;
+  const int k = id / unit_heads(p);
   const int L = lane < p.B ? attended_len(p, p.seq_lens[lane]) : 0;
   const int n = split_count(p, L);
   int full = 0, part = 0;
@@ -314,7 +314,8 @@ __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u
     b = __builtin_ctzll(cand);
     split = __builtin_amdgcn_readlane(full, b);
   }
-  u = Unit{b, (id - k * p.G + (k >> 4)) % p.G, split};
+  const int uh = unit_heads(p);
+  u = Unit{b, (id - k * uh + (k >> 4)) % uh, split};
   return true;
 }
 
@@ -333,10 +334,11 @@ __device__ __forceinline__ bool unit_at(const DecodeParams& p, Unit& u) {
   if (p.grid_order == 4) return unit_from_lengths(p, u);
   if (p.grid_order == 3) {
     const int id = static_cast<int>(blockIdx.x);
-    const int k = id / p.G;
+    const int uh = unit_heads(p);
+    const int k = id / uh;
     if (k >= scalar_load_i32(p.n_units)) return false;
     const uint32_t e = static_cast<uint32_t>(scalar_load_i32(p.units + k));
-    u = Unit{static_cast<int>(e & 0xffffu), (id - k * p.G + (k >> 4)) % p.G,
+    u = Unit{static_cast<int>(e & 0xffffu), (id - k * uh + (k >> 4)) % uh,
              static_cast<int>(e >> 16)};
     return true;
   }
@@ -346,10 +348,10 @@ __device__ __forceinline__ bool unit_at(const DecodeParams& p, Unit& u) {
 // The split kernels' grid for the dispatch order.
 inline dim3 split_grid(const DecodeParams& p) {
   switch (p.grid_order) {
-    case 0: return dim3(p.n_splits, p.G, p.B);
-    case 1: return dim3(p.G, p.B, p.n_splits);
-    case 2: return dim3(p.G, p.n_splits, p.B);
-    default: return dim3(static_cast<unsigned>(p.G) * p.B * p.n_splits);   // orders 3, 4
+    case 0: return dim3(p.n_splits, unit_heads(p), p.B);
+    case 1: return dim3(unit_heads(p), p.B, p.n_splits);
+    case 2: return dim3(unit_heads(p), p.n_splits, p.B);
+    default: return dim3(static_cast<unsigned>(unit_heads(p)) * p.B * p.n_splits);   // orders 3, 4
   }
 }
 
