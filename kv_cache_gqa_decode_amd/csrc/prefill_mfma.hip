@@ -67,29 +67,31 @@ struct PfGeo {
 // Four (D = 128) or two (D = 64) 16-byte K operands from LDS, waiting for
 // their own reads.  Inline assembly for the reason given at read_vt_tr: a
 // compiler-visible LDS read would first wait for the next tile's copies.
+template <int kOff>
 __device__ __forceinline__ void read_k(const uint32_t (&a)[4], bf16x8 (&k)[4]) {
   u32x4 r0, r1, r2, r3;
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kOff));
   k[0] = __builtin_bit_cast(bf16x8, r0);
   k[1] = __builtin_bit_cast(bf16x8, r1);
   k[2] = __builtin_bit_cast(bf16x8, r2);
   k[3] = __builtin_bit_cast(bf16x8, r3);
 }
+template <int kOff>
 __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
   u32x4 r0, r1;
   asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
+      "ds_read_b128 %0, %2 offset:%4\n\t"
+      "ds_read_b128 %1, %3 offset:%4\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1)
-      : "v"(a[0]), "v"(a[1]));
+      : "v"(a[0]), "v"(a[1]), "i"(kOff));
   k[0] = __builtin_bit_cast(bf16x8, r0);
   k[1] = __builtin_bit_cast(bf16x8, r1);
 }
@@ -186,8 +188,11 @@ void prefill_kernel(DecodeParams p) {
   const int64_t rs = static_cast<int64_t>(p.G) * (2 * D);
   const int64_t head0 = (PAGED ? 0 : static_cast<int64_t>(b) * p.max_seq_len * rs) +
                         static_cast<int64_t>(g) * (2 * D);
-  const char* kbase = static_cast<const char*>(p.k) + head0;
-  const char* vbase = static_cast<const char*>(p.v) + head0;
+  // wave-uniform, so that the per-tile descriptor arithmetic stays scalar
+  const char* kbase = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<uint64_t>(static_cast<const char*>(p.k) + head0)));
+  const char* vbase = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<uint64_t>(static_cast<const char*>(p.v) + head0)));
 
   // One descriptor per 16-token half of a tile and operand, spanning the
   // valid rows (below kmax, in a valid block): other rows read as zeros
@@ -198,7 +203,7 @@ void prefill_kernel(DecodeParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int lo = j0 + 16 * h;
-      int rows = kmax - lo;
+      int rows = __builtin_amdgcn_readfirstlane(kmax - lo);
       rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
       int64_t off;
       ts.ok[h] = true;
@@ -266,7 +271,8 @@ void prefill_kernel(DecodeParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int t = 16 * h2 + tile_row(n);
-      koff[h2][kb] = static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
+      koff[h2][kb] = lds_addr(buf0) +
+                     static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
     }
   // the lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
   const uint32_t vrd = static_cast<uint32_t>(VG::at(tile_row(4 * grp + n / 4), 8 * (n % 4)));
@@ -304,8 +310,8 @@ void prefill_kernel(DecodeParams p) {
       cur = tile_src(j0 + kPfTT);
       issue(cur, sel ^ 1);
     }
-    const uint32_t kaddr = lds_addr(buf0 + sel * PG::kBufBytes);
-    const uint32_t vaddr = kaddr + PG::kKBytes + vrd;
+    const uint32_t kaddr = static_cast<uint32_t>(sel * PG::kBufBytes);
+    const uint32_t vaddr = lds_addr(buf0) + kaddr + PG::kKBytes + vrd;
     // wave-uniform; an invalid block (paged) masks its tokens on either path
     const bool masked = (MASK && j0 + kPfTT > wbound) || (PAGED && !(now.ok[0] && now.ok[1]));
 
@@ -317,7 +323,7 @@ void prefill_kernel(DecodeParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) a[kb] = kaddr + koff[h2][kb];
       bf16x8 ka[KB];
-      read_k(a, ka);
+      read_k<0>(a, ka);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
