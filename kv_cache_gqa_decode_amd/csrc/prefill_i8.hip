@@ -177,8 +177,11 @@ void prefill_i8_kernel(DecodeParams p) {
   // row of S_max/16 groups; paged: the pool group the table gives, -1 when
   // its block id is outside the pool).
   const int64_t gstride = static_cast<int64_t>(p.G) * PG::kGroup;   // bytes per group
-  const char* kbase = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * PG::kGroup;
-  const char* vbase = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * PG::kGroup;
+  // wave-uniform, so that the per-tile descriptor arithmetic stays scalar
+  const char* kbase = reinterpret_cast<const char*>(uniform_u64(reinterpret_cast<uint64_t>(
+      static_cast<const char*>(p.k) + static_cast<int64_t>(g) * PG::kGroup)));
+  const char* vbase = reinterpret_cast<const char*>(uniform_u64(reinterpret_cast<uint64_t>(
+      static_cast<const char*>(p.v) + static_cast<int64_t>(g) * PG::kGroup)));
   // One descriptor per half-tile group and operand: K spans the rows below
   // kmax (the others read as zeros), V^T the whole block of a valid group
   // (its tokens past kmax are masked, and codes are finite, so they add 0);
@@ -189,7 +192,7 @@ void prefill_i8_kernel(DecodeParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int lo = j0 + 16 * h;
-      int rows = kmax - lo;
+      int rows = __builtin_amdgcn_readfirstlane(kmax - lo);
       rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
       int64_t grp16;
       ts.ok[h] = true;
