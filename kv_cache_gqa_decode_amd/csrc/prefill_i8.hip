@@ -61,9 +61,6 @@ struct I8PfGeo {
   __device__ __forceinline__ static int swz(int t) {
     return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
   }
-  // Position of token t in a V^T row: the lane that feeds tokens 4m + r
-  // (m = 0..7) to the P V matrix op reads them at r * 8 + m.
-  __device__ __forceinline__ static int vpos(int t) { return (t & 3) * 8 + (t >> 2); }
 };
 
 // Four 16-byte LDS reads, waited for together (inline, for the reason given
@@ -236,8 +233,10 @@ void prefill_i8_kernel(DecodeParams p) {
       *reinterpret_cast<f16x8*>(kt16 + t * 2 * D + 16 * (dc ^ PG::swz(t))) =
           codes_to_f16(w.x, w.y);
     }
-    // V^T: (dimension d, group h) = 16 codes; tokens 16h + 4m + r (m = 0..3)
-    // go to positions r * 8 + 4h + m
+    // V^T: (dimension d, group h) = 16 codes.  Token t sits at position
+    // 8 (t mod 4) + t div 4 of its row, so that the lane feeding tokens
+    // 4m + r (m = 0..7) to the P V matrix op reads them at r * 8 + m: tokens
+    // 16h + 4m + r (m = 0..3) of the group go to positions r * 8 + 4h + m
     for (int u = threadIdx.x; u < 2 * D; u += 256) {
       const int d = u % D, h = u / D;
       const uint4 w = *reinterpret_cast<const uint4*>(smem + 2 * PG::kGroup + h * PG::kGroup + d * 16);
