@@ -42,6 +42,8 @@ constexpr int kWaves = 4;
 constexpr int kCols = 32;                        // query rows per wave
 constexpr int kRows = kWaves * kCols;            // query rows per workgroup
 constexpr int kTT = 32;                          // key tokens per tile
+constexpr float kRescaleBound = 256.f;           // 2^kRescaleSlack
+static_assert(kRescaleSlack == 8.f, "kRescaleBound is 2^kRescaleSlack");
 static_assert(kRows == kPrefillRows && kTT == kPrefillTile, "the host plans with these");
 
 template <int D>
@@ -336,26 +338,38 @@ void prefill_i8_kernel(DecodeParams p) {
             if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
           }
       }
-      float mt = sv[0];
+      // weights against the lazily kept running max; the tile's max only
+      // when a lane's sum passes 2^slack or the row has no max yet (as in the
+      // bf16 prefill kernel)
+      float e[8];
+      float px = 0.f;
+      {
+        const float ref = m[nb] == kNegInf ? 0.f : m[nb];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          px += e[j];
+        }
+      }
+      if (__builtin_expect(__any(!(px <= kRescaleBound) || m[nb] == kNegInf), 0)) {
+        float mt = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = fmaxf(m[nb], mt);
-        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        const float alpha = m[nb] == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
         m[nb] = mn;
-      }
-      const float ref = m[nb] == kNegInf ? 0.f : m[nb];
-      float e[8];
-      float px = 0.f;
+        const float ref = mn == kNegInf ? 0.f : mn;
+        px = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
-        px += e[j];
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          px += e[j];
+        }
       }
       const u32x4 h = {pack_f16(e[0], e[1]), pack_f16(e[2], e[3]), pack_f16(e[4], e[5]),
                        pack_f16(e[6], e[7])};

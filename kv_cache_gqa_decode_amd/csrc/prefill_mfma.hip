@@ -42,6 +42,8 @@ constexpr int kPfWaves = 4;
 constexpr int kPfCols = 32;                      // query rows per wave (two column blocks)
 constexpr int kPfRows = kPfWaves * kPfCols;      // query rows per workgroup
 constexpr int kPfTT = 32;                        // key tokens per tile
+constexpr float kRescaleBound = 256.f;           // 2^kRescaleSlack
+static_assert(kRescaleSlack == 8.f, "kRescaleBound is 2^kRescaleSlack");
 static_assert(kPfRows == kPrefillRows && kPfTT == kPrefillTile, "the host plans with these");
 
 template <int D>
@@ -350,26 +352,41 @@ void prefill_kernel(DecodeParams p) {
             if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
           }
       }
-      float mt = sv[0];
+      // Probabilities against the running max (lazily kept: it moves only
+      // when a score passes it by more than kRescaleSlack).  A lane's sum of
+      // its 8 weights bounds each of them, so the tile's max is needed only
+      // when that sum passes 2^slack (or is not finite), or while the row has
+      // no max yet: then the max moves to the tile's, the state is rescaled
+      // and the weights are taken again.
+      float e[8];
+      float px = 0.f;
+      {
+        const float ref = m[nb] == kNegInf ? 0.f : m[nb];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__builtin_expect(__any(mt > m[nb] + kRescaleSlack), 0)) {   // a running max moves
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          px += e[j];
+        }
+      }
+      if (__builtin_expect(__any(!(px <= kRescaleBound) || m[nb] == kNegInf), 0)) {
+        float mt = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = fmaxf(m[nb], mt);
-        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        const float alpha = m[nb] == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
         m[nb] = mn;
-      }
-      const float ref = m[nb] == kNegInf ? 0.f : m[nb];
-      float e[8];
-      float px = 0.f;
+        const float ref = mn == kNegInf ? 0.f : mn;
+        px = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
-        px += e[j];
+        for (int j = 0; j < 8; ++j) {
+          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          px += e[j];
+        }
       }
       u32x4 h;
 #pragma unroll
