@@ -20,7 +20,8 @@
 //    each query row's scores and accumulators live in one lane column and
 //    the online softmax needs only two cross-lane shuffles;
 //  * O^T = V^T P^T with V^T read from the staged tile (the decode kernel's
-//    V layout) by the transposing LDS reads of gfx950.
+//    blocks, rows split in halves at D = 128) by the transposing LDS reads of
+//    gfx950.
 //
 // Arithmetic: q (times scale * log2 e) and the probabilities enter the
 // matrix cores rounded once to bf16, accumulation is fp32.  One running sum
@@ -54,15 +55,39 @@ struct PfGeo {
   static constexpr int kKBytes = kPfTT * 2 * D;  // staged K tile
   static constexpr int NKI = kKBytes / 1024;     // K copy instructions per tile
   static constexpr int TPI = 64 / NDC;           // K rows per copy instruction
-  using VG = Geo<D>;                             // V tile: the decode kernel's layout
+  using VG = Geo<D>;                             // V copy blocks as in the decode kernel
   static constexpr int kVBytes = VG::kTileBytes;
   static constexpr int kBufBytes = kKBytes + kVBytes;
   static_assert(NKI % kPfWaves == 0 && VG::NVL % kPfWaves == 0, "copies split over the waves");
-  // Chunk dc of K row t is stored at slot dc ^ swz(t) of the row: the 16
-  // rows one A-operand read touches then fall into 16 different bank
-  // groups (row t's chunk at t * 2D + 16 (dc ^ swz(t)) bytes).
+  // Chunk dc of K row t is stored at slot dc ^ swz(t) (at t * 2D +
+  // 16 (dc ^ swz(t)) bytes).  A 16-byte LDS read serves lanes 0-7 together
+  // with lanes 16-23 (8-15 with 24-31, and so on), 256 bytes per pass: a
+  // swizzle that spread lanes 0-15 over the 64 banks left a 2-way conflict on
+  // every K read (SQ_LDS_BANK_CONFLICT), this one none.  Such a pass reads
+  // chunks 4 kb + grp, grp in {2i, 2i + 1}, of eight rows tile_row(n); swz
+  // sends those rows to eight distinct even slots (D = 128), or to four per
+  // 128-byte half of the banks (D = 64), and grp's low bit fills the odd ones.
   __device__ __forceinline__ static int swz(int t) {
-    return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
+    return D == 128 ? (((t << 1) & 2) | (t & 12)) : ((t >> 1) & 6);
+  }
+  // Staged V: blocks of one copy instruction each (RPI rows, 32 bytes of
+  // padding after every block, so blocks start 8 banks apart).  At D = 128 a
+  // block holds the first 128 bytes of its four rows, then their second 128
+  // bytes.  The transposing reads of lanes 0-31 (lane groups 0 and 1) go out
+  // together and address rows 4 m + grp of four blocks: with whole 256-byte
+  // rows, group 1's rows sat on the same 32 banks as group 0's (a 2-way
+  // conflict on every V^T read); with split rows they are 128 bytes apart and
+  // the eight rows cover all 64 banks.
+  static constexpr bool kVSplit = D == 128;
+  __device__ __forceinline__ static constexpr int vat(int r, int c) {
+    return kVSplit ? (r / VG::RPI) * VG::BLOCK + (c >> 7) * 512 + (r % VG::RPI) * 128 + (c & 127)
+                   : VG::at(r, c);
+  }
+  // row (within its block) and byte (within its row) copied by lane l of a
+  // V copy instruction, which lands 16 bytes at block + 16 l
+  __device__ __forceinline__ static int vrow_of(int l) { return kVSplit ? (l >> 3) & 3 : l / VG::LPR; }
+  __device__ __forceinline__ static int vbyte_of(int l) {
+    return kVSplit ? (l >> 5) * 128 + (l & 7) * 16 : (l % VG::LPR) * 16;
   }
 };
 
@@ -225,7 +250,7 @@ void prefill_kernel(DecodeParams p) {
   };
   // this wave's quarter of a tile's copies: K instructions wave + 4 i (each
   // 64 16-byte chunks, rows jj * TPI ..), V instructions likewise (rows
-  // jj * RPI .., the decode kernel's layout)
+  // jj * RPI .., placed by vrow_of / vbyte_of)
   uint32_t koffc[PG::NKI / kPfWaves];
 #pragma unroll
   for (int i = 0; i < PG::NKI / kPfWaves; ++i) {
@@ -235,7 +260,7 @@ void prefill_kernel(DecodeParams p) {
     const int dc = slot ^ PG::swz(t);
     koffc[i] = static_cast<uint32_t>((t & 15) * rs + dc * 16);
   }
-  const uint32_t vlane = static_cast<uint32_t>((lane / VG::LPR) * rs + (lane % VG::LPR) * 16);
+  const uint32_t vlane = static_cast<uint32_t>(PG::vrow_of(lane) * rs + PG::vbyte_of(lane));
   lds_char* const buf0 = (lds_char*)(smem);
   auto issue = [&](const TileSrc& ts, int sel) {
     lds_char* kb_ = buf0 + sel * PG::kBufBytes;
@@ -260,7 +285,7 @@ void prefill_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < VG::NVL / kPfWaves; ++i) {
       const int jj = wave + kPfWaves * i;
-      const int r = jj * VG::RPI + lane / VG::LPR;
+      const int r = jj * VG::RPI + PG::vrow_of(lane);
       const bool ok = (jj * VG::RPI) >> 4 == 0 ? ts.ok[0] : ts.ok[1];
       if (!(j0 + r < kmax && ok)) lds_zero16(vb + jj * VG::BLOCK + lane * 16);
     }
@@ -277,7 +302,7 @@ void prefill_kernel(DecodeParams p) {
                      static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
     }
   // the lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
-  const uint32_t vrd = static_cast<uint32_t>(VG::at(tile_row(4 * grp + n / 4), 8 * (n % 4)));
+  const uint32_t vrd = static_cast<uint32_t>(PG::vat(tile_row(4 * grp + n / 4), 8 * (n % 4)));
   constexpr int kVHalf = (16 / VG::RPI) * VG::BLOCK;     // rows r -> r + 16
 
   f32x4 acc[NB][CB];
@@ -398,7 +423,7 @@ void prefill_kernel(DecodeParams p) {
     // O^T[d][row] += V^T[d][t] P^T[t][row]
     static_for<CB>([&](auto cbc) {
       constexpr int cb = decltype(cbc)::value;
-      const bf16x8 av = read_vt_tr<32 * cb, kVHalf>(vaddr);
+      const bf16x8 av = read_vt_tr<PG::vat(0, 32 * cb), kVHalf>(vaddr);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb][cb] = mfma(av, pb[nb], acc[nb][cb]);
     });
