@@ -55,13 +55,36 @@ struct I8PfGeo {
   static constexpr int kStage = 4 * kGroup;      // staged codes: K of 2 groups, then V^T
   static constexpr int NCI = kStage / 1024;      // copy instructions per tile
   static constexpr int kKBytes = kTT * 2 * D;    // fp16 K tile
-  static constexpr int kVRow = kTT * 2 + 16;     // fp16 V^T row: 32 tokens, 16 bytes of pad
+  // fp16 V^T row: 32 tokens and 32 bytes of padding.  96 bytes = 6 slots of
+  // 16: the eight rows n = 0..7 a 16-byte read pass takes (lanes 0-7 and
+  // 16-23, see swz) start on even slots 6 n mod 16, and the two lane groups
+  // of the pass read slots 0 and 1 of them: all 16 slots, no conflict.
+  static constexpr int kVRow = kTT * 2 + 32;
   static constexpr int kVBytes = D * kVRow;
   static constexpr int kLds = kStage + kKBytes + kVBytes;
   static_assert(NCI % kWaves == 0, "copies split over the waves");
-  // K rows as in the bf16 prefill kernel: chunk dc of row t at slot dc ^ swz(t)
+  // K rows: chunk dc of row t at slot dc ^ swz(t).  The score matrix op
+  // takes K row 16 h2 + n in lane n (tokens in their own order, unlike the
+  // bf16 kernel, whose transposing V^T reads want another).  A 16-byte LDS
+  // read serves lanes 0-7 with 16-23 (8-15 with 24-31, ...) in one 256-byte
+  // pass, an 8-byte one lanes 0-31, a 16-byte write 8 lanes; swz sends the
+  // eight rows of an operand read's pass to distinct even slots (D = 128) or
+  // four per 128-byte half (D = 64), and the lane group's low bit fills the
+  // odd ones.
   __device__ __forceinline__ static int swz(int t) {
-    return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
+    return D == 128 ? (t & 7) << 1 : t & 6;
+  }
+  // the K chunk thread u converts: lanes 0-7 / 16-23 of each 32 take chunks
+  // 0-7 / 8-15 of one row, lanes 8-15 / 24-31 those of the next (D = 128);
+  // at D = 64 the four lane octets take chunks 0-7 of four rows.  Every
+  // 16-byte write (8 lanes) then fills distinct slots of one row, and every
+  // 8-byte read pass reads 256 contiguous bytes.
+  __device__ __forceinline__ static int kconv_row(int u) {
+    return D == 128 ? (u >> 5) * 2 + ((u >> 3) & 1)
+                    : 4 * (u >> 5) + ((u >> 4) & 1) + 2 * ((u >> 3) & 1);
+  }
+  __device__ __forceinline__ static int kconv_chunk(int u) {
+    return D == 128 ? (u & 7) | (((u >> 4) & 1) << 3) : u & 7;
   }
 };
 
@@ -229,40 +252,52 @@ void prefill_i8_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kTT * PG::NDC / 256; ++i) {
       const int u = threadIdx.x + 256 * i;
-      const int t = u / PG::NDC, dc = u % PG::NDC;
+      const int t = PG::kconv_row(u), dc = PG::kconv_chunk(u);
       const uint2 w = *reinterpret_cast<const uint2*>(smem + (t >> 4) * PG::kGroup +
                                                       (t & 15) * D + dc * 8);
       *reinterpret_cast<f16x8*>(kt16 + t * 2 * D + 16 * (dc ^ PG::swz(t))) =
           codes_to_f16(w.x, w.y);
     }
-    // V^T: (dimension d, group h) = 16 codes.  Token t sits at position
-    // 8 (t mod 4) + t div 4 of its row, so that the lane feeding tokens
-    // 4m + r (m = 0..7) to the P V matrix op reads them at r * 8 + m: tokens
-    // 16h + 4m + r (m = 0..3) of the group go to positions r * 8 + 4h + m
-    for (int u = threadIdx.x; u < 2 * D; u += 256) {
-      const int d = u % D, h = u / D;
-      const uint4 w = *reinterpret_cast<const uint4*>(smem + 2 * PG::kGroup + h * PG::kGroup + d * 16);
-      const f16x8 lo = codes_to_f16(w.x, w.y), hi = codes_to_f16(w.z, w.w);   // tokens 0-7, 8-15
-      const uint32_t a0 = __builtin_bit_cast(u32x4, lo)[0], a1 = __builtin_bit_cast(u32x4, lo)[1];
-      const uint32_t a2 = __builtin_bit_cast(u32x4, lo)[2], a3 = __builtin_bit_cast(u32x4, lo)[3];
-      const uint32_t b0 = __builtin_bit_cast(u32x4, hi)[0], b1 = __builtin_bit_cast(u32x4, hi)[1];
-      const uint32_t b2 = __builtin_bit_cast(u32x4, hi)[2], b3 = __builtin_bit_cast(u32x4, hi)[3];
-      // word k of lo holds tokens 2k, 2k+1; of hi tokens 8 + 2k, 9 + 2k.
-      // r = 0: tokens 0, 4, 8, 12; r = 1: 1, 5, 9, 13; r = 2: 2, 6, 10, 14; r = 3: 3, 7, 11, 15
-      const uint32_t lo16 = 0x05040100u, hi16 = 0x07060302u;   // low / high halves of two words
-      char* row = vt16 + d * PG::kVRow + 8 * h;
-      *reinterpret_cast<uint2*>(row + 0) =
-          make_uint2(__builtin_amdgcn_perm(a2, a0, lo16), __builtin_amdgcn_perm(b2, b0, lo16));
-      *reinterpret_cast<uint2*>(row + 16) =
-          make_uint2(__builtin_amdgcn_perm(a2, a0, hi16), __builtin_amdgcn_perm(b2, b0, hi16));
-      *reinterpret_cast<uint2*>(row + 32) =
-          make_uint2(__builtin_amdgcn_perm(a3, a1, lo16), __builtin_amdgcn_perm(b3, b1, lo16));
-      *reinterpret_cast<uint2*>(row + 48) =
-          make_uint2(__builtin_amdgcn_perm(a3, a1, hi16), __builtin_amdgcn_perm(b3, b1, hi16));
+    // V^T: dimension d of group h holds 16 codes, tokens 16 h + 0..15, as
+    // four words of 4.  The fp16 row of d keeps them by class: class c (bytes
+    // 16 c .. 16 c + 15) = word c of group 0, then word c of group 1, i.e.
+    // tokens 4c .. 4c + 3 and 16 + 4c .. 16 + 4c + 3: the 8 tokens that lane
+    // group c feeds to the P V matrix op, one 16-byte read.  codes_to_f16 of
+    // (group 0 word c, group 1 word c) is class c as it stands.
+    // Thread (wave wv, lane l) converts classes 2q, 2q + 1 of dimension d,
+    // q = bit 2 of l, d = 32 wv + the other lane bits (l & 3, then bits 4, 3,
+    // 5), and writes class 2q + q first.  16-byte writes are served 8 lanes
+    // (128 bytes) at a time: lanes 0-7 hold dimensions 4 k .. 4 k + 3, whose
+    // rows start 6 d mod 8 slots apart, each with q = 0 and 1, which write
+    // slots of opposite parity.  The 16 lanes of a 16-byte read pass and the
+    // 32 of an 8-byte one (the staged codes) also meet distinct banks.
+    // Measured on a 32K prompt: no bank-conflict cycles (1.9e9 with the
+    // dimensions in lane order).
+    const int cl = threadIdx.x & 63, cw = threadIdx.x >> 6;
+    const int d = 32 * cw + ((cl & 3) | (((cl >> 4) & 1) << 2) | (((cl >> 3) & 1) << 3) |
+                             ((cl >> 5) << 4)),
+              q = (cl >> 2) & 1;
+    if (d < D) {
+      lds_char* src = stage + 2 * PG::kGroup + d * 16 + 8 * q;   // group 0, words 2q, 2q + 1
+      typedef const __attribute__((address_space(3))) uint64_t lds_u64;
+      const uint64_t g0 = *reinterpret_cast<lds_u64*>(src);
+      // opaque, so that the two reads are not fused into one two-address
+      // read, which is served like a 16-byte read
+      asm volatile("" : "+v"(src));
+      const uint64_t g1 = *reinterpret_cast<lds_u64*>(src + PG::kGroup);   // group 1
+      const uint32_t g0x = static_cast<uint32_t>(g0), g0y = static_cast<uint32_t>(g0 >> 32);
+      const uint32_t g1x = static_cast<uint32_t>(g1), g1y = static_cast<uint32_t>(g1 >> 32);
+      const uint32_t f0 = q ? g0y : g0x, f1 = q ? g1y : g1x;          // class 2q + q
+      const uint32_t s0 = q ? g0x : g0y, s1 = q ? g1x : g1y;          // class 2q + 1 - q
+      lds_char* const row = (lds_char*)(vt16) + d * PG::kVRow;
+      *reinterpret_cast<__attribute__((address_space(3))) f16x8*>(row + 48 * q) =
+          codes_to_f16(f0, f1);
+      *reinterpret_cast<__attribute__((address_space(3))) f16x8*>(row + 16 + 16 * q) =
+          codes_to_f16(s0, s1);
     }
   };
 
-  // LDS read addresses: K operand rows 16 h2 + tile_row(n), chunk kb*4 + grp;
+  // LDS read addresses: K operand rows 16 h2 + n, chunk kb*4 + grp;
   // V^T operand dimension 16 cb + n, tokens grp*8 .. +7
   const uint32_t kaddr = lds_addr((lds_char*)(kt16));
   uint32_t koff[2][KB];
@@ -270,7 +305,7 @@ void prefill_i8_kernel(DecodeParams p) {
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int t = 16 * h2 + tile_row(n);
+      const int t = 16 * h2 + n;
       koff[h2][kb] = kaddr + static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
     }
   const uint32_t vaddr = lds_addr((lds_char*)(vt16)) + static_cast<uint32_t>(n * PG::kVRow + grp * 16);
@@ -334,7 +369,7 @@ void prefill_i8_kernel(DecodeParams p) {
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int t = j0 + 16 * h2 + tile_row(4 * grp + j);
+            const int t = j0 + 16 * h2 + 4 * grp + j;
             if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
           }
       }
