@@ -52,23 +52,34 @@ struct PfGeo {
   static constexpr int KB = D / 32;              // 32-dim blocks of the score contraction
   static constexpr int CB = D / 16;              // 16-dim blocks of the output
   static constexpr int NDC = D / 8;              // 16-byte chunks of a K row
-  static constexpr int kKBytes = kPfTT * 2 * D;  // staged K tile
-  static constexpr int NKI = kKBytes / 1024;     // K copy instructions per tile
+  static constexpr int NKI = kPfTT * 2 * D / 1024;  // K copy instructions per tile
+  // one K copy instruction's block (TPI rows), padded by 64 bytes at D = 128
+  static constexpr bool kKPad = D == 128;
+  static constexpr int kKBlock = kKPad ? 1024 + 64 : 1024;
+  static constexpr int kKBytes = NKI * kKBlock;  // staged K tile
   static constexpr int TPI = 64 / NDC;           // K rows per copy instruction
   using VG = Geo<D>;                             // V copy blocks as in the decode kernel
   static constexpr int kVBytes = VG::kTileBytes;
   static constexpr int kBufBytes = kKBytes + kVBytes;
   static_assert(NKI % kPfWaves == 0 && VG::NVL % kPfWaves == 0, "copies split over the waves");
-  // Chunk dc of K row t is stored at slot dc ^ swz(t) (at t * 2D +
-  // 16 (dc ^ swz(t)) bytes).  A 16-byte LDS read serves lanes 0-7 together
-  // with lanes 16-23 (8-15 with 24-31, and so on), 256 bytes per pass: a
-  // swizzle that spread lanes 0-15 over the 64 banks left a 2-way conflict on
-  // every K read (SQ_LDS_BANK_CONFLICT), this one none.  Such a pass reads
-  // chunks 4 kb + grp, grp in {2i, 2i + 1}, of eight rows tile_row(n); swz
-  // sends those rows to eight distinct even slots (D = 128), or to four per
-  // 128-byte half of the banks (D = 64), and grp's low bit fills the odd ones.
+  // Chunk dc of K row t is stored at slot dc ^ swz(t) of the row, at byte
+  // kat(t, dc).  A 16-byte LDS read serves lanes 0-7 together with lanes
+  // 16-23 (8-15 with 24-31, and so on), 256 bytes per pass: a swizzle that
+  // spread lanes 0-15 over the 64 banks left a 2-way conflict on every K
+  // read (SQ_LDS_BANK_CONFLICT).  Such a pass reads chunks 4 kb + grp, grp in
+  // {2i, 2i + 1}, of the eight rows tile_row(n), n < 8 (or n >= 8).  At
+  // D = 128 those rows are 4 m + r, m = 0..3, r in {0, 1} (or {2, 3}): the
+  // 64-byte block padding puts the four m on four different 64-byte quarters
+  // of the banks, and swz = 2 (t & 1) with grp's low bit gives the four
+  // slots of a quarter.  swz leaves bits 2-3 of the chunk alone, so chunk
+  // 4 kb + grp of a row lies 64 kb bytes after chunk grp: one address and
+  // immediate offsets serve a lane's reads.  At D = 64 (128-byte rows, no
+  // padding) swz sends the rows to four slots per 128-byte half.
   __device__ __forceinline__ static int swz(int t) {
-    return D == 128 ? (((t << 1) & 2) | (t & 12)) : ((t >> 1) & 6);
+    return D == 128 ? (t & 1) << 1 : ((t >> 1) & 6);
+  }
+  __device__ __forceinline__ static int kat(int t, int dc) {
+    return (t / TPI) * kKBlock + (t % TPI) * (2 * D) + 16 * (dc ^ swz(t));
   }
   // Staged V: blocks of one copy instruction each (RPI rows, 32 bytes of
   // padding after every block, so blocks start 8 banks apart).  At D = 128 a
@@ -105,6 +116,23 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[4], bf16x8 (&k)[4]) {
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kOff));
+  k[0] = __builtin_bit_cast(bf16x8, r0);
+  k[1] = __builtin_bit_cast(bf16x8, r1);
+  k[2] = __builtin_bit_cast(bf16x8, r2);
+  k[3] = __builtin_bit_cast(bf16x8, r3);
+}
+// The same four reads from one address, 64 bytes apart (D = 128).
+template <int kOff>
+__device__ __forceinline__ void read_k(uint32_t a, bf16x8 (&k)[4]) {
+  u32x4 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a), "i"(kOff), "i"(kOff + 64), "i"(kOff + 128), "i"(kOff + 192));
   k[0] = __builtin_bit_cast(bf16x8, r0);
   k[1] = __builtin_bit_cast(bf16x8, r1);
   k[2] = __builtin_bit_cast(bf16x8, r2);
@@ -268,7 +296,7 @@ void prefill_kernel(DecodeParams p) {
     for (int i = 0; i < PG::NKI / kPfWaves; ++i) {
       const int jj = wave + kPfWaves * i;
       const int h = (jj * PG::TPI) >> 4;
-      copy16_to_lds(h == 0 ? ts.k[0] : ts.k[1], kb_ + jj * 1024, koffc[i]);
+      copy16_to_lds(h == 0 ? ts.k[0] : ts.k[1], kb_ + jj * PG::kKBlock, koffc[i]);
     }
 #pragma unroll
     for (int i = 0; i < VG::NVL / kPfWaves; ++i) {
@@ -291,16 +319,15 @@ void prefill_kernel(DecodeParams p) {
     }
   };
 
-  // LDS read offsets of the lane's K operands: row 16 h2 + tile_row(n), chunk kb*4 + grp
-  uint32_t koff[2][KB];
+  // LDS read offsets of the lane's K operands: row 16 h2 + tile_row(n), chunk
+  // kb*4 + grp; at D = 128 one offset, the rest 4 kKBlock h2 + 64 kb further
+  constexpr int NKO = PG::kKPad ? 1 : 2 * KB;
+  uint32_t koff[NKO];
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int t = 16 * h2 + tile_row(n);
-      koff[h2][kb] = lds_addr(buf0) +
-                     static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
-    }
+  for (int i = 0; i < NKO; ++i) {
+    const int h2 = i / KB, kb = i % KB;
+    koff[i] = lds_addr(buf0) + static_cast<uint32_t>(PG::kat(16 * h2 + tile_row(n), kb * 4 + grp));
+  }
   // the lane's address for read_vt_tr: row tile_row(4 grp + n / 4), dims 4 (n % 4) ..
   const uint32_t vrd = static_cast<uint32_t>(PG::vat(tile_row(4 * grp + n / 4), 8 * (n % 4)));
   constexpr int kVHalf = (16 / VG::RPI) * VG::BLOCK;     // rows r -> r + 16
@@ -344,13 +371,17 @@ void prefill_kernel(DecodeParams p) {
 
     // S^T: token rows 16 h2 + 4 grp + j, lane column n of block nb
     f32x4 s[NB][2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      uint32_t a[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) a[kb] = kaddr + koff[h2][kb];
+    static_for<2>([&](auto h2c) {
+      constexpr int h2 = decltype(h2c)::value;
       bf16x8 ka[KB];
-      read_k<0>(a, ka);
+      if constexpr (PG::kKPad) {
+        read_k<h2 * 4 * PG::kKBlock>(kaddr + koff[0], ka);
+      } else {
+        uint32_t a[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) a[kb] = kaddr + koff[h2 * KB + kb];
+        read_k<0>(a, ka);
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -358,7 +389,7 @@ void prefill_kernel(DecodeParams p) {
         for (int kb = 0; kb < KB; ++kb) c = mfma(ka[kb], qv[nb][kb], c);
         s[nb][h2] = c;
       }
-    }
+    });
 
     bf16x8 pb[NB];
 #pragma unroll
