@@ -334,9 +334,14 @@ void prefill_kernel(DecodeParams p) {
 
   f32x4 acc[NB][CB];
   float m[NB], lx[NB];
+  // minus the reference the weights are taken against (the running max, 0
+  // while there is none), in all four lanes of a score accumulator: the
+  // score MFMAs start from it and leave s - ref
+  f32x4 nref[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m[nb] = kNegInf; lx[nb] = 0.f;
+    nref[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -369,7 +374,7 @@ void prefill_kernel(DecodeParams p) {
     // wave-uniform; an invalid block (paged) masks its tokens on either path
     const bool masked = (MASK && j0 + kPfTT > wbound) || (PAGED && !(now.ok[0] && now.ok[1]));
 
-    // S^T: token rows 16 h2 + 4 grp + j, lane column n of block nb
+    // S^T - ref: token rows 16 h2 + 4 grp + j, lane column n of block nb
     f32x4 s[NB][2];
     static_for<2>([&](auto h2c) {
       constexpr int h2 = decltype(h2c)::value;
@@ -384,7 +389,7 @@ void prefill_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        f32x4 c = nref[nb];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) c = mfma(ka[kb], qv[nb][kb], c);
         s[nb][h2] = c;
@@ -409,38 +414,38 @@ void prefill_kernel(DecodeParams p) {
           }
       }
       // Probabilities against the running max (lazily kept: it moves only
-      // when a score passes it by more than kRescaleSlack).  A lane's sum of
-      // its 8 weights bounds each of them, so the tile's max is needed only
-      // when that sum passes 2^slack (or is not finite), or while the row has
-      // no max yet: then the max moves to the tile's, the state is rescaled
-      // and the weights are taken again.
+      // when a score passes it by more than kRescaleSlack); sv already holds
+      // score - ref.  A lane's sum of its 8 weights bounds each of them, so
+      // the tile's max is needed only when that sum passes 2^slack (or is not
+      // finite), or while the row has no max yet: then the max moves to the
+      // tile's, the state is rescaled and the weights are taken again.
       float e[8];
       float px = 0.f;
-      {
-        const float ref = m[nb] == kNegInf ? 0.f : m[nb];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
-          px += e[j];
-        }
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(sv[j]);
+        px += e[j];
       }
       if (__builtin_expect(__any(!(px <= kRescaleBound) || m[nb] == kNegInf), 0)) {
+        const float ref = -nref[nb][0];
         float mt = sv[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m[nb], mt);
+        const float mn = fmaxf(m[nb], mt + ref);
         const float alpha = m[nb] == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
         m[nb] = mn;
-        const float ref = mn == kNegInf ? 0.f : mn;
+        const float ref2 = mn == kNegInf ? 0.f : mn;
+        const float shift = ref - ref2;            // score - ref2 = sv + shift
+        nref[nb] = f32x4{-ref2, -ref2, -ref2, -ref2};
         px = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          e[j] = __builtin_amdgcn_exp2f(sv[j] + shift);
           px += e[j];
         }
       }
