@@ -54,7 +54,10 @@ struct I8PfGeo {
   static constexpr int kGroup = 16 * D;          // bytes of one head's group: K rows or V^T
   static constexpr int kStage = 4 * kGroup;      // staged codes: K of 2 groups, then V^T
   static constexpr int NCI = kStage / 1024;      // copy instructions per tile
-  static constexpr int kKBytes = kTT * 2 * D;    // fp16 K tile
+  // fp16 K row: 2D bytes and 32 of padding, so that row t starts 2t slots
+  // (of 16 bytes) further round the banks than row 0
+  static constexpr int kKRow = 2 * D + 32;
+  static constexpr int kKBytes = kTT * kKRow;    // fp16 K tile
   // fp16 V^T row: 32 tokens and 32 bytes of padding.  96 bytes = 6 slots of
   // 16: the eight rows n = 0..7 a 16-byte read pass takes (lanes 0-7 and
   // 16-23, see swz) start on even slots 6 n mod 16, and the two lane groups
@@ -63,17 +66,17 @@ struct I8PfGeo {
   static constexpr int kVBytes = D * kVRow;
   static constexpr int kLds = kStage + kKBytes + kVBytes;
   static_assert(NCI % kWaves == 0, "copies split over the waves");
-  // K rows: chunk dc of row t at slot dc ^ swz(t).  The score matrix op
-  // takes K row 16 h2 + n in lane n (tokens in their own order, unlike the
-  // bf16 kernel, whose transposing V^T reads want another).  A 16-byte LDS
-  // read serves lanes 0-7 with 16-23 (8-15 with 24-31, ...) in one 256-byte
-  // pass, an 8-byte one lanes 0-31, a 16-byte write 8 lanes; swz sends the
-  // eight rows of an operand read's pass to distinct even slots (D = 128) or
-  // four per 128-byte half (D = 64), and the lane group's low bit fills the
-  // odd ones.
-  __device__ __forceinline__ static int swz(int t) {
-    return D == 128 ? (t & 7) << 1 : t & 6;
-  }
+  // K rows: chunk dc of row t at kat(t, dc), in plain order within its
+  // padded row.  The score matrix op takes K row 16 h2 + n in lane n (tokens
+  // in their own order, unlike the bf16 kernel, whose transposing V^T reads
+  // want another).  A 16-byte LDS read serves lanes 0-7 with 16-23 (8-15
+  // with 24-31, ...) in one 256-byte pass, an 8-byte one lanes 0-31, a
+  // 16-byte write 8 lanes.  An operand read's pass takes chunk 4 kb + grp,
+  // grp in {2i, 2i + 1}, of eight rows t: the rows start on the even slots
+  // 2t (D = 128) or 10t (D = 64) mod 16, all distinct, and grp's low bit
+  // fills the odd ones.  Chunk 4 kb + grp lies 64 kb bytes after chunk grp,
+  // so a lane's reads take one address and immediate offsets.
+  __device__ __forceinline__ static constexpr int kat(int t, int dc) { return t * kKRow + 16 * dc; }
   // the K chunk thread u converts: lanes 0-7 / 16-23 of each 32 take chunks
   // 0-7 / 8-15 of one row, lanes 8-15 / 24-31 those of the next (D = 128);
   // at D = 64 the four lane octets take chunks 0-7 of four rows.  Every
@@ -88,34 +91,29 @@ struct I8PfGeo {
   }
 };
 
-// Four 16-byte LDS reads, waited for together (inline, for the reason given
-// at read_vt_tr: a compiler-visible LDS read would first wait for the next
-// tile's copies).
-__device__ __forceinline__ void lds_read4(const uint32_t (&a)[4], u32x4 (&r)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-}
-__device__ __forceinline__ void lds_read2(const uint32_t (&a)[2], u32x4 (&r)[2]) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1])
-      : "v"(a[0]), "v"(a[1]));
-}
-template <int N>
-__device__ __forceinline__ void lds_read(const uint32_t (&a)[N], u32x4 (&r)[N]) {
+// N (4 or 2) 16-byte LDS reads at a + kOff + i kStride, waited for together
+// (inline, for the reason given at read_vt_tr: a compiler-visible LDS read
+// would first wait for the next tile's copies).
+template <int N, int kOff, int kStride>
+__device__ __forceinline__ void lds_read(uint32_t a, u32x4 (&r)[N]) {
   if constexpr (N == 4) {
-    lds_read4(a, r);
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a), "i"(kOff), "i"(kOff + kStride), "i"(kOff + 2 * kStride),
+          "i"(kOff + 3 * kStride));
   } else {
     static_assert(N == 2, "two or four operands");
-    lds_read2(a, r);
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a), "i"(kOff), "i"(kOff + kStride));
   }
 }
 
@@ -177,13 +175,18 @@ void prefill_i8_kernel(DecodeParams p) {
     cbound[nb] = real[nb] ? win + t : 0;
     qrow[nb] = (static_cast<int64_t>(b) * T + t) * p.H + g * R + r;
   }
-  // q * scale * log2(e) rounded to fp16: lane (n, grp) of block (nb, kb)
-  // holds dims kb*32 + grp*8 .. +7 of its row
+  // q * scale * log2(e) * k_scale[g] rounded to fp16: lane (n, grp) of
+  // block (nb, kb) holds dims kb*32 + grp*8 .. +7 of its row.  With the
+  // K scale folded in, q . codes is the score itself.  An fp16 rounding
+  // error is at most 2^-12 relative or 2^-25 absolute (below the normal
+  // range), so the score is off by at most 2^-25 * 127 * D beyond the
+  // relative part, whatever the scale.
+  const float ksc = p.k_scale[g], vsc = p.v_scale[g];
   f16x8 qv[NB][KB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float* src = p.q_rot + qrow[nb] * D + grp * 8;
-    const float qs = real[nb] ? p.qscale : 0.f;
+    const float qs = real[nb] ? p.qscale * ksc : 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const float4 x0 = *reinterpret_cast<const float4*>(src + kb * 32);
@@ -193,7 +196,6 @@ void prefill_i8_kernel(DecodeParams p) {
       qv[nb][kb] = __builtin_bit_cast(f16x8, h);
     }
   }
-  const float ksc = p.k_scale[g], vsc = p.v_scale[g];
 
   // The head's 16-token groups: group j16 of the sequence (contiguous: b's
   // row of S_max/16 groups; paged: the pool group the table gives, -1 when
@@ -248,14 +250,14 @@ void prefill_i8_kernel(DecodeParams p) {
   char* const kt16 = smem + PG::kStage;
   char* const vt16 = kt16 + PG::kKBytes;
   auto convert = [&]() {
-    // K: chunk (t, dc) = 8 codes -> 16 bytes at row t, slot dc ^ swz(t)
+    // K: chunk (t, dc) = 8 codes -> 16 bytes at kat(t, dc)
 #pragma unroll
     for (int i = 0; i < kTT * PG::NDC / 256; ++i) {
       const int u = threadIdx.x + 256 * i;
       const int t = PG::kconv_row(u), dc = PG::kconv_chunk(u);
       const uint2 w = *reinterpret_cast<const uint2*>(smem + (t >> 4) * PG::kGroup +
                                                       (t & 15) * D + dc * 8);
-      *reinterpret_cast<f16x8*>(kt16 + t * 2 * D + 16 * (dc ^ PG::swz(t))) =
+      *reinterpret_cast<f16x8*>(kt16 + PG::kat(t, dc)) =
           codes_to_f16(w.x, w.y);
     }
     // V^T: dimension d of group h holds 16 codes, tokens 16 h + 0..15, as
@@ -297,24 +299,24 @@ void prefill_i8_kernel(DecodeParams p) {
     }
   };
 
-  // LDS read addresses: K operand rows 16 h2 + n, chunk kb*4 + grp;
-  // V^T operand dimension 16 cb + n, tokens grp*8 .. +7
-  const uint32_t kaddr = lds_addr((lds_char*)(kt16));
-  uint32_t koff[2][KB];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int t = 16 * h2 + n;
-      koff[h2][kb] = kaddr + static_cast<uint32_t>((t * PG::NDC + ((kb * 4 + grp) ^ PG::swz(t))) * 16);
-    }
+  // LDS read addresses, one per operand kind (the rest are immediate
+  // offsets): K operand row 16 h2 + n, chunk kb*4 + grp at kaddr +
+  // 16 h2 kKRow + 64 kb; V^T operand dimension 16 cb + n, tokens grp*8 .. +7
+  // (class grp) at vaddr + 16 cb kVRow
+  const uint32_t kaddr = lds_addr((lds_char*)(kt16)) + static_cast<uint32_t>(PG::kat(n, grp));
   const uint32_t vaddr = lds_addr((lds_char*)(vt16)) + static_cast<uint32_t>(n * PG::kVRow + grp * 16);
+  static_assert(16 * PG::kKRow + 3 * 64 + 16 <= 65536 && (CB - 1) * 16 * PG::kVRow < 65536,
+                "LDS read offsets fit the 16-bit offset field");
 
   f32x4 acc[NB][CB];
   float m[NB], lx[NB];
+  // minus the reference the weights are taken against (the running max, 0
+  // while there is none): the score MFMAs start from it and leave s - ref
+  f32x4 nref[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m[nb] = kNegInf; lx[nb] = 0.f;
+    nref[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -342,19 +344,19 @@ void prefill_i8_kernel(DecodeParams p) {
 
     // S^T (raw, times k_scale below): token rows 16 h2 + 4 grp + j
     f32x4 s[NB][2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    static_for<2>([&](auto h2c) {
+      constexpr int h2 = decltype(h2c)::value;
       u32x4 kr[KB];
-      lds_read<KB>(koff[h2], kr);
+      lds_read<KB, 16 * h2 * PG::kKRow, 64>(kaddr, kr);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        f32x4 c = nref[nb];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
           c = mfma_f16(__builtin_bit_cast(f16x8, kr[kb]), qv[nb][kb], c);
         s[nb][h2] = c;
       }
-    }
+    });
 
     f16x8 pb[NB];
 #pragma unroll
@@ -363,7 +365,7 @@ void prefill_i8_kernel(DecodeParams p) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j] * ksc;
+        for (int j = 0; j < 4; ++j) sv[h2 * 4 + j] = s[nb][h2][j];
       if (masked) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -373,36 +375,36 @@ void prefill_i8_kernel(DecodeParams p) {
             if (!(t < cbound[nb] && now.ok[h2])) sv[h2 * 4 + j] = kNegInf;
           }
       }
-      // weights against the lazily kept running max; the tile's max only
-      // when a lane's sum passes 2^slack or the row has no max yet (as in the
-      // bf16 prefill kernel)
+      // weights against the lazily kept running max (sv holds score - ref);
+      // the tile's max only when a lane's sum passes 2^slack or the row has
+      // no max yet (as in the bf16 prefill kernel)
       float e[8];
       float px = 0.f;
-      {
-        const float ref = m[nb] == kNegInf ? 0.f : m[nb];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
-          px += e[j];
-        }
+      for (int j = 0; j < 8; ++j) {
+        e[j] = __builtin_amdgcn_exp2f(sv[j]);
+        px += e[j];
       }
       if (__builtin_expect(__any(!(px <= kRescaleBound) || m[nb] == kNegInf), 0)) {
+        const float ref = -nref[nb][0];
         float mt = sv[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m[nb], mt);
+        const float mn = fmaxf(m[nb], mt + ref);
         const float alpha = m[nb] == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[nb] - mn);
         lx[nb] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[nb][cb] *= alpha;
         m[nb] = mn;
-        const float ref = mn == kNegInf ? 0.f : mn;
+        const float ref2 = mn == kNegInf ? 0.f : mn;
+        const float shift = ref - ref2;            // score - ref2 = sv + shift
+        nref[nb] = f32x4{-ref2, -ref2, -ref2, -ref2};
         px = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(sv[j] - ref);
+          e[j] = __builtin_amdgcn_exp2f(sv[j] + shift);
           px += e[j];
         }
       }
@@ -413,20 +415,17 @@ void prefill_i8_kernel(DecodeParams p) {
     }
 
     // O^T[d][row] += V^T[d][t] P^T[t][row], four output blocks per read
-#pragma unroll
-    for (int c4 = 0; c4 < CB; c4 += 4) {
-      constexpr int NR = CB < 4 ? CB : 4;
-      uint32_t va[NR];
+    constexpr int NR = CB < 4 ? CB : 4;
+    static_for<CB / NR>([&](auto c4c) {
+      constexpr int c4 = NR * decltype(c4c)::value;
       u32x4 vr[NR];
-#pragma unroll
-      for (int i = 0; i < NR; ++i) va[i] = vaddr + static_cast<uint32_t>((c4 + i) * 16 * PG::kVRow);
-      lds_read<NR>(va, vr);
+      lds_read<NR, c4 * 16 * PG::kVRow, 16 * PG::kVRow>(vaddr, vr);
 #pragma unroll
       for (int i = 0; i < NR; ++i)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb][c4 + i] = mfma_f16(__builtin_bit_cast(f16x8, vr[i]), pb[nb], acc[nb][c4 + i]);
-    }
+    });
   };
 
   const int wg_bound = win + static_cast<int>(c0 / R);
