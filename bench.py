@@ -585,7 +585,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step "
               "shards across GPUs by batch, heads or sequence with no change to the kernels, "
-              "but this build measures one GPU.", file=sys.stderr)
+              "but this benchmark times one GPU.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
