@@ -506,13 +506,13 @@ void prefill_kernel(DecodeParams p) {
 
 // grid_order -1 chooses.  Fewer (sequence, KV head) pairs than XCDs: pairs
 // fastest, which deals every pair's tiles over the XCDs.  Otherwise a pair's
-// query tiles go together: with few of them (short chunks) round-robin over
-// the XCDs, every XCD taking an equal share of every pair, since the pairs'
-// lengths differ; with many, in contiguous runs per XCD, so that a pair's
-// keys are fetched into one L2 instead of eight.  Measured on 64 ragged
-// sequences with 8 KV heads: 512-token chunks 3.80 / 3.05 / 3.25 ms (orders
-// 0 / 1 / 2), 2048-token chunks 12.6 / 10.5 / 11.0 ms, 8192-token chunks
-// 54.9 / 49.5 / 42.6 ms; a 32K prompt with 32 KV heads 81.0 / 84.1 / 76.2 ms.
+// query tiles go together in contiguous runs per XCD, so that a pair's keys
+// are fetched into one L2 instead of eight.  Measured on 64 ragged sequences
+// with 8 KV heads (orders 0 / 1 / 2): 512-token chunks 3.63 / 2.87 / 2.37 ms,
+// 2048-token chunks 12.2 / 8.79 / 8.57 ms, 8192-token chunks 54.0 / 40.2 /
+// 34.3 ms; a 32K prompt with 32 KV heads 63.3 / 68.9 / 59.5 ms.  (With the
+// earlier, slower tile loop, order 1 was the faster one for short chunks:
+// 3.80 / 3.05 / 3.25 ms at 512 tokens.)
 hipError_t launch_prefill_mfma(const DecodeParams& p_in, bool paged, const Launch& l) {
   DecodeParams p = p_in;
   if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;
@@ -524,7 +524,7 @@ hipError_t launch_prefill_mfma(const DecodeParams& p_in, bool paged, const Launc
   const int64_t units = static_cast<int64_t>(p.B) * p.G * p.n_splits;
   // with key splits the units hold equal key counts: runs per XCD
   if (p.grid_order < 0)
-    p.grid_order = units < p.n_xcd ? 0 : (p.n_splits > 1 || nqt > 64 ? 2 : 1);
+    p.grid_order = units < p.n_xcd ? 0 : 2;
   const int64_t wgs = nqt * units;
   if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs));
