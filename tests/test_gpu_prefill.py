@@ -130,6 +130,20 @@ def test_key_split_forced(split, paged, block_size):
                   options=kvd.Options(split_tokens=split))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("paged,block_size,split", [(False, 16, 64), (True, 16, 0), (True, 32, 96)])
+def test_head_dim_64_chunks(dtype, paged, block_size, split):
+    """D = 64 (its own LDS layouts: 128-byte rows, another swizzle) on chunks
+    after ragged histories, contiguous and paged, with and without key
+    splits, on both cache dtypes."""
+    T = 100
+    lens = np.array([T, T + 17, T + 400, 1000], np.int32)
+    s = _spec(lens.size, 16, 4, 64, 1024, paged, block_size, dtype=dtype)
+    p = W.make_window(s, T, lengths=lens)
+    check_prefill(p, what=f"D=64 {dtype} paged={paged}/{block_size} split={split}",
+                  options=kvd.Options(split_tokens=split))
+
+
 def test_key_split_automatic_long_history():
     """A 64-token chunk after a 20K history, one sequence and two KV heads:
     four query tiles cannot fill the device, so the library splits the keys
