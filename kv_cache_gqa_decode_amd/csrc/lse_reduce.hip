@@ -23,24 +23,30 @@ namespace kvd {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+// rows from which each row's merge is one wave (four rows per workgroup):
+// enough waves to occupy every CU, and no barrier or LDS round in the merge
+constexpr int64_t kMergeWaveRows = 1024;
 
 // Workgroup (b*T*H + t*H + h, dim group): 256 threads = SL split lanes x
 // DT/4 float4 columns merge DT output dims of one query row; split lane sl
 // takes splits sl, sl + SL, ... in batches of U whose loads are issued
 // together.  With few splits one workgroup takes all D dims; with many,
-// D/DT workgroups share a row.
-template <int D, int DT, int U>
+// D/DT workgroups share a row.  kWaveRow: each of the 4 waves merges a row
+// of its own (all D dims, 64 / (D/4) split lanes), rows 4x + wave.
+template <int D, int DT, int U, bool kWaveRow = false>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   constexpr int C4 = DT / 4;          // float4 columns
-  constexpr int SL = 256 / C4;        // split lanes
-  static_assert(C4 <= 32 && SL * C4 == 256, "columns within a wave");
+  constexpr int SL = (kWaveRow ? 64 : 256) / C4;   // split lanes
+  static_assert(C4 <= 32 && SL * C4 == (kWaveRow ? 64 : 256), "columns within a wave");
+  static_assert(!kWaveRow || DT == D, "a wave merges whole rows");
   __shared__ float4 sm_acc[4][C4];
   __shared__ float sm_m[4], sm_w[4];
 
-  const int bh = blockIdx.x;
+  const int bh = kWaveRow ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
+  if (kWaveRow && bh >= p.B * p.H * p.T) return;   // the whole wave: no barrier follows
   const int d0 = blockIdx.y * DT;
   const int b = bh / (p.H * p.T);       // rows b * T * H + t * H + h
-  const int tid = threadIdx.x;
+  const int tid = kWaveRow ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
   const int sl = tid / C4, c4 = tid - sl * C4;
   // no workspace: no sequence can hold a token (the host planned no split)
   const int n_splits = p.part_lse ? p.n_splits : 0;
@@ -113,18 +119,21 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
       fold(s0, ns, ns2);
     }
   }
-  // Combine the split lanes: the workgroup's maximum (wave shuffles, then
-  // the 4 waves through LDS), each lane's sums rescaled to it, then summed
-  // over the split lanes of a column -- shuffles inside a wave (the lanes
-  // C4 apart hold the same column), the 4 waves through LDS.
+  // Combine the split lanes: the row's maximum (wave shuffles, then the 4
+  // waves through LDS unless the wave holds the whole row), each lane's sums
+  // rescaled to it, then summed over the split lanes of a column -- shuffles
+  // inside a wave (the lanes C4 apart hold the same column), then the 4
+  // waves through LDS.
   constexpr int kW = 4;
   const int lane = tid & 63, wave = tid >> 6;
   float M = m;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) sm_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  if constexpr (!kWaveRow) {
+    if (lane == 0) sm_m[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  }
   const float sc = m == kNegInf ? 0.f : exp2f(m - M);   // a lane without tokens adds 0
   float4 a = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
   float ws = wsum * sc;
@@ -134,19 +143,23 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
     a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
     ws += __shfl_xor(ws, off);
   }
-  if (lane < C4) {
-    sm_acc[wave][lane] = a;
-    if (lane == 0) sm_w[wave] = ws;
-  }
-  __syncthreads();
-  if (tid >= C4) return;
-  a = sm_acc[0][tid];
-  ws = sm_w[0];
+  if constexpr (kWaveRow) {
+    if (tid >= C4) return;
+  } else {
+    if (lane < C4) {
+      sm_acc[wave][lane] = a;
+      if (lane == 0) sm_w[wave] = ws;
+    }
+    __syncthreads();
+    if (tid >= C4) return;
+    a = sm_acc[0][tid];
+    ws = sm_w[0];
 #pragma unroll
-  for (int w = 1; w < kW; ++w) {
-    const float4 x = sm_acc[w][tid];
-    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-    ws += sm_w[w];
+    for (int w = 1; w < kW; ++w) {
+      const float4 x = sm_acc[w][tid];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      ws += sm_w[w];
+    }
   }
   // no split saw a valid token (an empty sequence, or every block invalid):
   // an empty softmax, out = 0 and lse = -inf
@@ -160,12 +173,34 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream) {
-  // up to 8 splits: one workgroup per row, 8 split lanes x 32 columns; up to
-  // 64: 32-dim groups, 32 split lanes x 8 columns; more: 16-dim groups,
-  // 64 split lanes x 4 columns, 4 splits per lane per batch of loads
+  // Many rows (a batch, several new tokens, a prefill's key splits): a wave
+  // per row, all D columns (D/4 float4 lanes) x 64/(D/4) split lanes, each
+  // lane taking up to 8 splits per batch of loads.  Fewer rows: a workgroup
+  // per row -- up to 8 splits all D columns x 256/(D/4) split lanes; more
+  // splits (one long sequence) the row's dims over several workgroups, up to
+  // 64 splits 32-dim groups (32 split lanes x 8 columns, 2 splits per lane
+  // per batch), more 16-dim groups (64 split lanes x 4 columns, 4 per batch).
   const int ns = p.n_splits;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.T;
+  if (rows >= kMergeWaveRows) {
+    const dim3 grid(static_cast<unsigned>((rows + 3) / 4), 1);
+    const int sl = 64 / (p.D / 4);
+    const int u = ns <= sl ? 1 : ns <= 2 * sl ? 2 : ns <= 4 * sl ? 4 : 8;
+    if (p.D == 64) {
+      if (u == 1) lse_reduce_kernel<64, 64, 1, true><<<grid, 256, 0, stream>>>(p);
+      else if (u == 2) lse_reduce_kernel<64, 64, 2, true><<<grid, 256, 0, stream>>>(p);
+      else if (u == 4) lse_reduce_kernel<64, 64, 4, true><<<grid, 256, 0, stream>>>(p);
+      else lse_reduce_kernel<64, 64, 8, true><<<grid, 256, 0, stream>>>(p);
+    } else {
+      if (u == 1) lse_reduce_kernel<128, 128, 1, true><<<grid, 256, 0, stream>>>(p);
+      else if (u == 2) lse_reduce_kernel<128, 128, 2, true><<<grid, 256, 0, stream>>>(p);
+      else if (u == 4) lse_reduce_kernel<128, 128, 4, true><<<grid, 256, 0, stream>>>(p);
+      else lse_reduce_kernel<128, 128, 8, true><<<grid, 256, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   const int groups = ns <= 8 ? 1 : (ns <= 64 ? p.D / 32 : p.D / 16);
-  const dim3 grid(p.B * p.H * p.T, groups);
+  const dim3 grid(static_cast<unsigned>(rows), groups);
   if (p.D == 64) {
     if (ns <= 8) lse_reduce_kernel<64, 64, 1><<<grid, 256, 0, stream>>>(p);
     else if (ns <= 64) lse_reduce_kernel<64, 32, 2><<<grid, 256, 0, stream>>>(p);

@@ -328,6 +328,22 @@ def test_work_list_derived_in_kernel(dtype, batch):
     gates.assert_lse(lse[keep], ol[keep], dtype, f"work list order 4, B={batch}")
 
 
+@pytest.mark.parametrize("dtype,kernel", KERNELS)
+@pytest.mark.parametrize("D,batch,split", [(128, 1027, 16), (64, 1025, 16), (128, 1027, 128)])
+def test_merge_of_many_rows(dtype, kernel, D, batch, split):
+    """Over a thousand query rows (one head per sequence, a row count that is
+    not a multiple of 4) with 1 to 64 splits per sequence: the merge takes
+    a wave per row, four rows to a workgroup, the last workgroup partly
+    empty, and split lanes that run several batches of loads."""
+    rng = np.random.default_rng(batch + D + split)
+    L = rng.integers(1, 1025, batch).astype(np.int32)
+    L[:5] = [1, 1024, 16, 17, 1023]
+    s = W.spec("c3", batch=batch, n_heads=1, n_kv_heads=1, head_dim=D, max_seq_len=1024,
+               dtype=dtype, q_gain=4.0, value_scale=D ** -0.5 if dtype == "bf16" else 1.0)
+    p = W.make_problem(s, lengths=L)
+    check_full(p, kernel=kernel, split=split, what=f"{dtype} {kernel} D={D} B={batch} split={split}")
+
+
 # --------------------------- reachable paths: long splits, bad table entries
 
 LONG = np.array([8192, 7001, 6150, 4097, 300], np.int32)
