@@ -96,6 +96,10 @@ struct RopeParams {
   void* k_recent;
   void* v_recent;
   int32_t window;
+  // set by the launcher: workgroup slices y < rot_slices of a token take its
+  // q and k items (which need the rotation factors), the others its v items;
+  // rot_slices = gridDim.y: every slice takes items of both kinds
+  int32_t rot_slices;
 };
 
 // Where a main kernel goes: its stream and, for measurement, a pair of
