@@ -100,6 +100,34 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* p) {
   return *reinterpret_cast<const_i32*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
 }
 
+// Prefill dispatch order 2 with the batch a multiple of n_xcd (at most 64
+// sequences): the sequence that slot `slot` of the unit list holds.  The
+// list's n_xcd contiguous runs, one per XCD, then hold B / n_xcd whole
+// sequences each; run x takes the sequences of length ranks x, 2 n_xcd - 1 -
+// x, 2 n_xcd + x, .. (longest first, ties by index, dealt back and forth),
+// so that the runs' summed lengths -- each XCD's share of the work -- come
+// out nearly equal whatever order the lengths arrive in.  Every lane of the
+// wave takes part; the result is wave-uniform.
+__device__ __forceinline__ int balanced_run_seq(const DecodeParams& p, int slot) {
+  const int per = p.B / p.n_xcd;
+  const int x = slot / per, j = slot - x * per;
+  const int r = j * p.n_xcd + ((j & 1) ? p.n_xcd - 1 - x : x);
+  const int l = static_cast<int>(threadIdx.x & 63);
+  int len = -1;
+  if (l < p.B) {
+    const int v = p.seq_lens[l];
+    len = v < 0 ? 0 : (v > p.max_len_host ? p.max_len_host : v);
+  }
+  int rank = 0;                              // sequences ahead of lane l's
+  for (int m = 0; m < p.B; ++m) {
+    const int lm = __builtin_amdgcn_readlane(len, m);
+    rank += (lm > len || (lm == len && m < l)) ? 1 : 0;
+  }
+  // the ranks of lanes 0..B-1 are a permutation of 0..B-1, and r < B
+  const uint64_t hit = __ballot(l < p.B && rank == r);
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }

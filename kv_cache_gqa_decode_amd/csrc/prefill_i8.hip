@@ -142,7 +142,9 @@ void prefill_i8_kernel(DecodeParams p) {
   const int unit = static_cast<int>(p.grid_order == 0 ? lin % units : lin / nqt);
   const int qt = nqt - 1 - static_cast<int>(p.grid_order == 0 ? lin / units : lin % nqt);
   const int bg = unit / nsplit, split = unit - bg * nsplit;
-  const int g = bg % p.G, b = bg / p.G;
+  const int g = bg % p.G;
+  const int b = p.grid_order == 2 && p.B <= 64 && p.B % p.n_xcd == 0 ? balanced_run_seq(p, bg / p.G)
+                                                                      : bg / p.G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -473,13 +475,18 @@ hipError_t launch_prefill_i8(const DecodeParams& p_in, bool paged, const Launch&
   const int64_t ncols = static_cast<int64_t>(p.T) * p.R;
   const int64_t nqt = (ncols + kRows - 1) / kRows;
   const int64_t units = static_cast<int64_t>(p.B) * p.G * p.n_splits;
-  // grid_order -1 chooses: pairs fastest below n_xcd units; a pair's tiles
-  // together, round-robin over the XCDs, for up to 64 tiles per pair; else
-  // contiguous runs per XCD.  Unlike the bf16 kernel, short chunks run best
-  // round-robin: 64 ragged sequences with 512-token chunks 2.73 / 2.50 /
-  // 2.75 ms (orders 0 / 1 / 2); a 32K prompt 58.8 / 63.8 / 58.8 ms.
+  // grid_order -1 chooses: pairs fastest below n_xcd units; contiguous runs
+  // per XCD when the runs are balanced by length (up to 64 sequences, a
+  // multiple of n_xcd), or with key splits or more than 64 tiles per pair;
+  // otherwise a pair's tiles together, round-robin over the XCDs, which
+  // shares every pair's work evenly where unbalanced runs would not.  64
+  // ragged sequences with 512-token chunks: 2.73 / 2.50 / 2.75 ms (orders
+  // 0 / 1 / 2, runs not balanced), 2.54 (order 1) against 2.34 ms (balanced
+  // runs); 2048-token chunks 9.13 against 8.09 ms.  A 32K prompt 58.8 / 63.8
+  // / 58.8 ms.
+  const bool balanced = p.B <= 64 && p.B % p.n_xcd == 0;
   if (p.grid_order < 0)
-    p.grid_order = units < p.n_xcd ? 0 : (p.n_splits > 1 || nqt > 64 ? 2 : 1);
+    p.grid_order = units < p.n_xcd ? 0 : (balanced || p.n_splits > 1 || nqt > 64 ? 2 : 1);
   const int64_t wgs = nqt * units;
   if (wgs <= 0 || wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(wgs));

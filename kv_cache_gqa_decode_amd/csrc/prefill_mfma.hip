@@ -157,7 +157,9 @@ __device__ __forceinline__ void read_k(const uint32_t (&a)[2], bf16x8 (&k)[2]) {
 // 1: unit x / nqt, tile nqt - 1 - x mod nqt (a unit's tiles together).
 // 2: the order of 1 cut into n_xcd contiguous runs, run k taken by the
 // workgroups x = k mod n_xcd, which the device sends to one XCD, so that a
-// unit's tiles, which all read its keys, share one L2.  Held to 168
+// unit's tiles, which all read its keys, share one L2; with up to 64
+// sequences, a multiple of n_xcd, the list's sequences are ordered so that
+// the runs hold equal shares of the work (balanced_run_seq).  Held to 168
 // registers, three workgroups share a CU (measured 18% faster than two).
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
@@ -181,7 +183,9 @@ void prefill_kernel(DecodeParams p) {
   const int unit = static_cast<int>(p.grid_order == 0 ? lin % units : lin / nqt);
   const int qt = nqt - 1 - static_cast<int>(p.grid_order == 0 ? lin / units : lin % nqt);
   const int bg = unit / nsplit, split = unit - bg * nsplit;
-  const int g = bg % p.G, b = bg / p.G;
+  const int g = bg % p.G;
+  const int b = p.grid_order == 2 && p.B <= 64 && p.B % p.n_xcd == 0 ? balanced_run_seq(p, bg / p.G)
+                                                                      : bg / p.G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -508,11 +512,12 @@ void prefill_kernel(DecodeParams p) {
 // fastest, which deals every pair's tiles over the XCDs.  Otherwise a pair's
 // query tiles go together in contiguous runs per XCD, so that a pair's keys
 // are fetched into one L2 instead of eight.  Measured on 64 ragged sequences
-// with 8 KV heads (orders 0 / 1 / 2): 512-token chunks 3.63 / 2.87 / 2.37 ms,
-// 2048-token chunks 12.2 / 8.79 / 8.57 ms, 8192-token chunks 54.0 / 40.2 /
-// 34.3 ms; a 32K prompt with 32 KV heads 63.3 / 68.9 / 59.5 ms.  (With the
-// earlier, slower tile loop, order 1 was the faster one for short chunks:
-// 3.80 / 3.05 / 3.25 ms at 512 tokens.)
+// with 8 KV heads (orders 0 / 1 / 2, runs in batch order): 512-token chunks
+// 3.63 / 2.87 / 2.37 ms, 2048-token chunks 12.2 / 8.79 / 8.57 ms, 8192-token
+// chunks 54.0 / 40.2 / 34.3 ms; a 32K prompt with 32 KV heads 63.3 / 68.9 /
+// 59.5 ms.  Runs in batch order left one XCD a fifth more work than the
+// mean on that batch; balanced by length (balanced_run_seq) the 512-token
+// chunks take 2.08 ms (order 1: 2.88), the 2048-token chunks 7.35 ms.
 hipError_t launch_prefill_mfma(const DecodeParams& p_in, bool paged, const Launch& l) {
   DecodeParams p = p_in;
   if (p.T < 1 || p.R < 1 || (p.D != 64 && p.D != 128)) return hipErrorInvalidValue;

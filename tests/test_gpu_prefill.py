@@ -115,6 +115,36 @@ def test_dispatch_orders(order, B, G, T, paged, split):
                   options=kvd.Options(dispatch_order=order, split_tokens=split))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("B", [8, 64])
+def test_xcd_runs_balanced_by_length(dtype, split, B):
+    """Contiguous runs per XCD with the batch a multiple of the XCD count:
+    the unit list takes the sequences in an order dealt by length, so the
+    runs carry equal work.  Lengths in no particular order, with ties and
+    chunks on an empty history; every row against the oracle, and the same
+    bits as the order that deals a pair's tiles round-robin."""
+    T = 40
+    rng = np.random.default_rng(B + split)
+    lens = rng.integers(T, 400, B).astype(np.int32)
+    lens[: B // 4] = lens[B // 4: B // 2]
+    lens[-1] = T
+    rng.shuffle(lens)
+    s = _spec(B, 8, 2, 128, 512, dtype=dtype)
+    p = W.make_window(s, T, lengths=lens)
+    what = f"{dtype} B={B} split {split}"
+    check_prefill(p, what=f"XCD runs {what}",
+                  options=kvd.Options(dispatch_order=kvd.PREFILL_XCD_RUNS, split_tokens=split))
+    dev = device()
+    res = []
+    for order in (kvd.PREFILL_TILES_FASTEST, kvd.PREFILL_XCD_RUNS):
+        t = upload(p, dev)
+        _, out, lse = gpu_prefill(t, s, p.max_len,
+                                  options=kvd.Options(dispatch_order=order, split_tokens=split))
+        res.append((out.cpu(), lse.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), what
+
+
 @pytest.mark.parametrize("split", [32, 96, 2048])
 @pytest.mark.parametrize("paged,block_size", [(False, 16), (True, 32)])
 def test_key_split_forced(split, paged, block_size):
