@@ -92,11 +92,20 @@ def test_decode_step_both_kernels(dtype, block_size, style, D):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
-@pytest.mark.parametrize("B,T,S", [(17, 8, 256), (1, 4096, 4096)])
-def test_several_tokens_both_kernels(dtype, B, T, S):
-    s = W.spec("c3", dtype=dtype, batch=B, n_heads=8, n_kv_heads=2, head_dim=64,
-               max_seq_len=S)
-    lens = np.resize(np.array([T, T + 100, S], np.int32), B)
+@pytest.mark.parametrize("B,T,S", [(17, 8, 256), (9, 40, 256), (1, 4096, 4096)])
+@pytest.mark.parametrize("block_size", [0, 32])
+def test_several_tokens_both_kernels(dtype, B, T, S, block_size):
+    """From 16 tokens per sequence INT8 caches take v by 16-token groups:
+    chunks that start and end inside a group (byte stores) and whole groups
+    (16-byte stores); 8 tokens keep the per-token v items."""
+    if block_size:
+        nb = S // block_size
+        s = W.spec("c4", dtype=dtype, batch=B, n_heads=8, n_kv_heads=2, head_dim=64,
+                   num_blocks=B * nb + 3, max_blocks_per_seq=nb, block_size=block_size)
+    else:
+        s = W.spec("c3", dtype=dtype, batch=B, n_heads=8, n_kv_heads=2, head_dim=64,
+                   max_seq_len=S)
+    lens = np.resize(np.array([T, T + 100, S, T + 7], np.int32), B)
     p = W.make_window(s, T, lengths=lens)
     qa, ka, va = _both(p, "half", multi=True)
     g = geom(s)
@@ -106,7 +115,7 @@ def test_several_tokens_both_kernels(dtype, B, T, S):
                             base=s.rope_base, style="half", n_query=T, **sc)
     assert np.array_equal(bits(ka), bits(kc)), "K cache differs from the oracle's"
     assert np.array_equal(bits(va), bits(vc)), "V cache differs from the oracle's"
-    assert_q_rot(qa, oq, f"{dtype} B={B} T={T}")
+    assert_q_rot(qa, oq, f"{dtype} B={B} T={T} block {block_size}")
 
 
 @pytest.mark.parametrize("block_size", [0, 16])
