@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   __shared__ float sm_m[4], sm_w[4];
 
   const int bh = kWaveRow ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
-  if (kWaveRow && bh >= p.B * p.H * p.T) return;   // the whole wave: no barrier follows
+  if (kWaveRow && bh >= static_cast<int64_t>(p.B) * p.H * p.T) return;   // the whole wave: no barrier follows
   const int d0 = blockIdx.y * DT;
   const int b = bh / (p.H * p.T);       // rows b * T * H + t * H + h
   const int tid = kWaveRow ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
@@ -182,6 +182,7 @@ hipError_t launch_lse_reduce(const DecodeParams& p, hipStream_t stream) {
   // per batch), more 16-dim groups (64 split lanes x 4 columns, 4 per batch).
   const int ns = p.n_splits;
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.T;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;   // rows index the grid
   if (rows >= kMergeWaveRows) {
     const dim3 grid(static_cast<unsigned>((rows + 3) / 4), 1);
     const int sl = 64 / (p.D / 4);
