@@ -224,17 +224,19 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
     // the bound overstates the work: lengths spread over [0, bound] average
     // about half of it.  The MFMA kernel with up to 8 rows therefore aims
     // for eight rounds of the bound with several sequences (about four of
-    // the real work) and four with one, up to 2048 tokens per split
-    // (measured: the paged batch of contexts up to 32K, 2048-token splits
-    // 321 us against 328 us at 1024; the batch of contexts up to 8K, 1024
-    // tokens 179 us against 180 us at 2048; one 128K sequence, 512 tokens
-    // 79 us against 81 at 1024 and 83 at 256).
+    // the real work) and two with one, up to 2048 tokens per split
+    // (measured with the caches evicted before each step: the paged batch
+    // of contexts up to 32K, 2048-token splits 321 us against 328 us at
+    // 1024; the batch of contexts up to 8K, 1024 tokens 179 us against 180
+    // us at 2048; one 128K sequence with 8 KV heads, 1024 tokens 87.7 us
+    // against 89.6 at 512, 87.4 at 896, 90.5 at 2048 and 92.9 at 384, with
+    // 4 KV heads 47.6 against 48.6 us at 512).
     const bool one_per_cu = RT > 16 && pl->row_groups == 1;
     const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads * pl->head_groups *
                          pl->row_groups * static_cast<int64_t>(max_len_host);
     const int64_t slots =
         static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (one_per_cu || pl->row_groups > 1 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : (s->batch > 1 ? 8 : 4));
+    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : (s->batch > 1 ? 8 : 2));
     const int cap = kernel == 2 && one_per_cu ? 4096 : 2048;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
