@@ -216,6 +216,9 @@ typedef struct kvd_options {
  *              sequence alone
  *   rope_base  > 0 (10000 in the pages; some models use 1e6)
  *   rope_style kvd_rope_style
+ * Buffers need only their element alignment.  When q, k_new, v_new, q_rot
+ * and the caches are all 16-byte aligned and the call appends 128 tokens or
+ * more, a vector form of the kernel runs; it writes the same bits.
  * Errors: EINVAL (null pointer, H % G != 0, B < 0, table given for a
  * contiguous cache or missing for a paged one, q_rot == q, base <= 0),
  * EUNSUPPORTED (head_dim, kv_dtype, block_size, rope_style), EHIP.
