@@ -218,7 +218,14 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
     // keep two 64-token tiles in flight per wave from the first tile on,
     // and each one pays a full memory latency before its first tile, so
     // fewer, longer units measured faster (a 128K sequence: 2048-token
-    // splits 46 us, 512-token splits 63 us).
+    // splits 46 us, 512-token splits 63 us).  A batch with up to 16 rows
+    // takes eight rounds of the bound instead (about four of the real
+    // work), as the MFMA kernel does: the batch of contexts up to 8K went
+    // from 2048- to 1024-token splits, 106.7 -> 101.3 us (its mixed-cache
+    // history kernel 119.6 -> 114.1 us), while the paged batch up to 32K
+    // stays at 2048 (1024: 186.5 against 171.4 us).  The 17-32-row kernel
+    // keeps one round: 5 new tokens on the 8K batch, 2048-token splits
+    // took 150 against 131 us at 4096.
     //
     // The rounds are counted over the host bound on lengths.  For a batch
     // the bound overstates the work: lengths spread over [0, bound] average
@@ -236,7 +243,9 @@ kvd_status make_plan(const kvd_shape* s, int32_t max_len_host, int cu, const Tun
                          pl->row_groups * static_cast<int64_t>(max_len_host);
     const int64_t slots =
         static_cast<int64_t>(cu) * (kernel == 0 ? 4 : (one_per_cu || pl->row_groups > 1 ? 1 : 2));
-    const int64_t rounds = kernel == 0 ? 2 : (kernel == 2 || RT > 8 ? 1 : (s->batch > 1 ? 8 : 2));
+    const int64_t rounds = kernel == 0 ? 2
+                         : kernel == 2 ? (s->batch > 1 && RT <= 16 ? 8 : 1)
+                         : (RT > 8 ? 1 : (s->batch > 1 ? 8 : 2));
     const int cap = kernel == 2 && one_per_cu ? 4096 : 2048;
     chunk = round_up((rows + slots * rounds - 1) / (slots * rounds), granule);
     if (chunk < granule) chunk = granule;
