@@ -1,9 +1,11 @@
 """Decode-step benchmark on one MI355X.
 
-One step = rope_append_kv + gqa_decode_attn (RoPE on q and the new k, the
-KV-cache append, split-K GQA attention and the cross-split merge) for one
-layer over a batch of synthetic sequences whose inputs are already resident
-in HBM.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
+One step = RoPE on q and the new k, the KV-cache append, split-K GQA
+attention and the cross-split merge, for one layer over a batch of synthetic
+sequences whose inputs are already resident in HBM: gqa_decode_step (the
+split kernel rotates q and appends the new token itself, then the merge)
+on bf16 caches with one new token and up to 16 query heads per KV head,
+rope_append_kv + gqa_decode_attn otherwise or with --two-calls.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
 decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
 
 Timing protocol: before every timed step (and every warm-up step) a 1 GiB
@@ -22,7 +24,8 @@ never used for the roofline); --no-warm skips it (profiling runs).
 Prints ONE JSON line:
   value      KV HBM GB/s of the whole step = KV bytes / p50 step time, where
              KV bytes = sum_b L_b * G * D * 2 (K and V) * 2 bytes
-  roofline   the split-K attention kernel alone: KV bytes / its p50
+  roofline   the split-K attention kernel alone (with the fused step: its
+             RoPE and append included): KV bytes / its p50
              duration against the 8 TB/s HBM peak; `traffic` is the HBM
              bytes per launch from the committed rocprofv3 counter summary
              of this kernel and workload (null when missing or taken from a
@@ -562,6 +565,10 @@ def main():
     ap.add_argument("--tail-span", type=int, default=-1)
     ap.add_argument("--order", type=int, default=-1,
                     help="dispatch order (-1 automatic): decode 0-4, prefill 5-7")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="time rope_append_kv + gqa_decode_attn where gqa_decode_step (the step "
+                         "in one launch plus the merge) would otherwise run: bf16 caches, one "
+                         "new token, up to 16 query heads per KV head")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph in the timed region "
                          "(the kernel-time region stays eager)")
@@ -660,8 +667,16 @@ def main():
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T, options=opts)
     sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
+    # the decode step in one call where the library offers it
+    fused = (not args.two_calls and T == 1 and s.dtype == "bf16" and H // G <= 16 and
+             args.kernel in ("auto", "mfma"))
 
     def step(options=opts):
+        if fused:
+            kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                t["positions"], table, base=s.rope_base, max_seq_len=max_len,
+                                out=out, lse=lse, workspace=ws, options=options)
+            return
         if T > 1:
             kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                      t["positions"], table, base=s.rope_base, q_rot=q_rot, **sc)
@@ -750,6 +765,8 @@ def main():
                    "aux_bytes_per_step": aux, "split_tokens": plan["split_tokens"],
                    "n_splits": plan["n_splits"], "kernel": plan["kernel"],
                    "launch": "hip graph replay" if args.graph else "eager launches",
+                   "step": ("gqa_decode_step: RoPE, append and attention in the split kernel, "
+                            "then the merge" if fused else "rope_append_kv, then the attention call"),
                    "parallelism": "single GPU"},
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
@@ -762,7 +779,9 @@ def main():
         "wall_ms_per_step": round(t_wall * 1e3 / args.steps, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode split-K attention",
+                     "traffic": traffic,
+                     "kernel": ("decode split-K attention with RoPE and append fused" if fused
+                                else "decode split-K attention"),
                      "kernel_ms": round(kern_ms, 5), "kernel_ms_pct": summary(kern),
                      "launches_timed": len(kern), "algorithmic_bytes_per_launch": kv_bytes,
                      "kernel_source_hash": src_hash},

@@ -540,6 +540,36 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
                                          float scale, float* out, float* lse,
                                          const kvd_options* options, void* stream);
 
+/*
+ * gqa_decode_step -- the whole decode step in one launch (plus the merge):
+ * rope_append_kv followed by gqa_decode_attn_multi with n_query = 1 and
+ * seq_lens[b] = positions[b] + 1 ([KVGR] §3 and §5.1 b.ii-vi; [SA4] §4.5),
+ * for bf16 caches with up to 16 query heads per KV head.  The split kernel
+ * rotates q itself, and for each (sequence, KV head) the workgroup of the
+ * last split writes the rotated key and the value into the cache slot
+ * before it reads any tile; the results are those of the two calls.
+ *   q, k_new, v_new, k_cache, v_cache, positions, block_table, rope_base,
+ *              rope_style   as in rope_append_kv (bf16 inputs); q and the
+ *              caches 16-byte aligned
+ *   max_seq_len_host  a host bound on positions[b] + 1, in [1, max_seq_len];
+ *              attention covers min(positions[b] + 1, max_seq_len_host)
+ *              tokens (none for a negative position)
+ *   scale, out, lse, workspace, options   as in gqa_decode_attn_multi with
+ *              n_query = 1 (the same workspace size); options may not ask
+ *              for the VALU kernel
+ *   q_rot      [B, H, D] fp32 output of the rotated q, or NULL; written for
+ *              every sequence with a non-negative position
+ * Errors: as rope_append_kv and gqa_decode_attn_multi; EUNSUPPORTED for a
+ * cache that is not bf16 or more than 16 query heads per KV head (use the
+ * two calls); ERANGE for max_seq_len_host < 1.
+ */
+kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* positions, const int32_t* block_table,
+                           int32_t max_seq_len_host, double rope_base, int32_t rope_style,
+                           float scale, float* q_rot, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, const kvd_options* options, void* stream);
+
 /* Workspace bytes of gqa_decode_attn_multi with these options (NULL:
  * automatic); 0 also for an invalid shape or invalid options. */
 size_t gqa_decode_workspace_size_multi(const kvd_shape* shape, int32_t n_query,

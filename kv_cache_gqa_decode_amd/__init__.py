@@ -5,8 +5,8 @@ The compute entry points are imported lazily from ``_binding`` so that the
 workload generators and the sizing helpers import without the native library.
 """
 __all__ = ["rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8", "gqa_decode_attn_int8",
-           "rope_append_kv_multi", "gqa_decode_attn_multi", "gqa_prefill_attn", "workspace_size",
-           "library_path"]
+           "rope_append_kv_multi", "gqa_decode_attn_multi", "gqa_decode_step", "gqa_prefill_attn",
+           "workspace_size", "library_path"]
 
 
 def __getattr__(name):

@@ -117,7 +117,7 @@ EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_mixed",
             "gqa_decode_workspace_size_mixed",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
-            "gqa_decode_attn_multi_noalloc")
+            "gqa_decode_attn_multi_noalloc", "gqa_decode_step")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -180,6 +180,9 @@ def load_library():
                                               ctypes.c_float, P, P, P, ctypes.c_size_t, OP, P]
         lib.gqa_decode_workspace_size_mixed.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_mixed.argtypes = [SP, I32, I32, OP]
+        lib.gqa_decode_step.restype = I32
+        lib.gqa_decode_step.argtypes = [SP, P, P, P, P, P, P, P, I32, ctypes.c_double, I32,
+                                        ctypes.c_float, P, P, P, P, ctypes.c_size_t, OP, P]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32, OP]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -685,6 +688,52 @@ def gqa_decode_attn_multi(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                 scale, out, lse, workspace, options, dev)
     return out, lse
 
+
+
+def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+                    block_table: Optional[torch.Tensor] = None, base: float = 10000.0,
+                    style: str = "interleaved", scale: Optional[float] = None,
+                    max_seq_len: Optional[int] = None, q_rot: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
+                    options: Optional[Options] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The decode step in one call (gqa_decode_step): rope_append_kv, then
+    attention over positions[b] + 1 tokens, for a bf16 cache with up to 16
+    query heads per KV head.  q [B, H, D], k_new / v_new [B, G, D] bf16;
+    ``q_rot`` (optional, [B, H, D] float32) receives the rotated q.
+    Returns (out [B, H, D], lse [B, H])."""
+    lib = load_library()
+    dev = k_cache.device
+    B, H, D = (int(x) for x in q.shape)
+    G = int(k_new.shape[1])
+    shape = make_shape(B, H, k_cache, block_table)
+    dt = k_cache.dtype
+    _need(q, "q", dev, dt, (B, H, D))
+    _need(k_new, "k_new", dev, dt, (B, G, D))
+    _need(v_new, "v_new", dev, dt, (B, G, D))
+    _need(k_cache, "k_cache", dev, dt)
+    _need(v_cache, "v_cache", dev, dt, tuple(k_cache.shape))
+    _need(positions, "positions", dev, torch.int32, (B,))
+    if block_table is not None:
+        _need(block_table, "block_table", dev, torch.int32)
+    if q_rot is not None:
+        _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+    if style not in _STYLES:
+        raise ValueError(f"style must be one of {sorted(_STYLES)}")
+    msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
+    out, lse = _outputs((B,), H, D, dev, out, lse, want_lse)
+    opts = _options(options)
+    if workspace is None:
+        nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), 1, msl, opts))
+        workspace = _workspace(dev, nbytes)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                               _ptr(k_cache), _ptr(v_cache), _ptr(positions), _ptr(block_table),
+                               msl, float(base), _STYLES[style], _scale_arg(scale), _ptr(q_rot),
+                               _ptr(out), _ptr(lse), _ptr(workspace), wbytes, opts, _stream(dev)))
+    return out, lse
 
 
 def gqa_decode_attn_noalloc(q_rot: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

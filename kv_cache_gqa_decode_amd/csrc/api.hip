@@ -582,6 +582,79 @@ kvd_status rope_append_kv_int8(const kvd_shape* shape, const void* q, const void
                      positions, block_table, rope_base, rope_style, stream);
 }
 
+kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* positions, const int32_t* block_table,
+                           int32_t max_seq_len_host, double rope_base, int32_t rope_style,
+                           float scale, float* q_rot, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, const kvd_options* options, void* stream) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  if (shape->kv_dtype != KVD_BF16 || shape->n_heads / shape->n_kv_heads > 16)
+    return KVD_EUNSUPPORTED;
+  if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (q_rot && !aligned16(q_rot)))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == q || (q_rot && static_cast<const void*>(q_rot) == q) ||
+      (q_rot && q_rot == out))
+    return KVD_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base) || !std::isfinite(scale)) return KVD_EINVAL;
+  const bool paged = shape->block_size != 0;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  if (max_seq_len_host < 1 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  Tuning tu;
+  st = read_options(options, &tu);
+  if (st != KVD_OK) return st;
+  if (tu.kernel >= 0 && tu.kernel != 1) return KVD_EINVAL;
+  if (shape->batch == 0) return KVD_OK;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  Plan pl;
+  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, 1);
+  if (st != KVD_OK) return st;
+  if (pl.kernel != 1 || pl.n_splits < 1) return KVD_EUNSUPPORTED;
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
+  if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeParams p{};
+  // lengths: positions[b] + 1
+  p.seq_lens = positions; p.len_bias = 1;
+  p.q_in = q; p.k_new = k_new; p.v_new = v_new; p.q_rot_out = q_rot;
+  p.rope_base = rope_base; p.rope_style = rope_style;
+  p.q_rot = nullptr; p.k = k_cache; p.v = v_cache; p.table = block_table;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G; p.T = 1;
+  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
+  p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
+  p.n_splits = pl.n_splits; p.head_groups = pl.head_groups; p.row_groups = pl.row_groups;
+  p.part_stride = pl.n_splits;
+  p.qscale = log2_scale(scale, shape->head_dim);
+  p.direct = pl.n_splits <= 1 ? 1 : 0;
+  p.grid_order = pl.grid_order;
+  if (pl.n_splits > 1) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
+    const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
+    if (pl.grid_order == 3) {
+      p.n_units = reinterpret_cast<int32_t*>(ws + pl.units_offset);
+      p.units = p.n_units + 64;
+    }
+  }
+  if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
+  const Launch l{s, tu.ev_start, tu.ev_stop};
+  if (launch_decode_mfma(p, paged, l) != hipSuccess) return KVD_EHIP;
+  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
+  return KVD_OK;
+}
+
 kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const void* k_cache,
                            const void* v_cache, const int32_t* seq_lens,
                            const int32_t* block_table, int32_t max_seq_len_host, float scale,

@@ -76,19 +76,27 @@ constexpr int smem_bytes() {
   return stage > merge ? stage : merge;
 }
 
+// LDS of the fused step's rotation factors: wave 0's second V buffer, free
+// until that wave requests its second tile (after a barrier)
+typedef __attribute__((address_space(3))) double lds_f64;
+
 // One (sequence b, KV head g, split) unit computed by the whole workgroup:
 // the waves take interleaved tiles of the split, merge through LDS and
 // write the split's normalised output and log-sum-exp (or the final output
-// when there is a single split).
-template <int D, int NB, bool PAGED>
+// when there is a single split).  FUSED (the decode step in one launch, one
+// new token, NB = 1): q is rotated here from the raw q, and the workgroup
+// of the sequence's last split appends the token's k and v first.
+template <int D, int NB, bool PAGED, bool FUSED = false>
 __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int b, int g, int split) {
   using G = Geo<D>;
   constexpr int KB = G::KB, CB = G::CB, TT = G::TT, LPR = G::LPR, RPI = G::RPI, NVL = G::NVL;
   constexpr int kWaves = kMfmaWaves;
   static_assert(TT == 32 && NB >= 1 && NB <= 2, "tile shape");
+  static_assert(!FUSED || NB == 1, "the fused step takes up to 16 query rows");
   const int R = p.R;
   const int RT = R * p.T;             // tile columns: the query rows of this KV head
-  const int L = attended_len(p, scalar_load_i32(p.seq_lens + b));
+  const int raw_len = scalar_load_i32(p.seq_lens + b);   // FUSED: the new token's position
+  const int L = attended_len(p, len_of(p, raw_len));
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
@@ -129,8 +137,16 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   // rows are loaded once per workgroup and staged in LDS (QStage).
   float4 qraw[NB][KB][2];
   QStage<D> qst;
+  // FUSED: the raw q (bf16), rotated once the factors are in LDS
+  uint4 qin[FUSED ? KB : 1];
   if constexpr (NB == 2) {
     qst.load(p, b, g, RT, wave, lane);
+  } else if constexpr (FUSED) {
+    const int h = n;
+    const uint16_t* src = static_cast<const uint16_t*>(p.q_in) +
+                          (static_cast<int64_t>(b) * p.H + g * R + (h < RT ? h : 0)) * D + grp * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qin[kb] = *reinterpret_cast<const uint4*>(src + kb * 32);
   } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -233,12 +249,119 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   int blk_cur[2];
   int base = t0 + wave * TT;
   tile_blocks(0, blk_cur);
-  {
+  // FUSED: the workgroup of the last split appends the new token (wave-
+  // uniform), and must not request its first tile before that
+  const bool appender = FUSED && split == split_count(p, L) - 1;
+  if (!appender) {
     // issued on every path (a wave without tiles gets empty descriptors and
     // reads nothing), so the wait for the q loads above stays partial
     const TileSrc ts = tile_src(base, blk_cur);
     issue_k(ts, kr);
     issue_v(ts, vbuf[0]);
+  }
+  if constexpr (FUSED) {
+    // RoPE factors of the new token's position, in fp64 as the append
+    // kernel computes them, into LDS
+    const int P = raw_len;
+    lds_f64* const fcos = reinterpret_cast<lds_f64*>(stage + G::kTileBytes);
+    lds_f64* const fsin = fcos + D / 2;
+    if (wave == 0 && lane < D / 2) {
+      const double theta = pow(p.rope_base, -2.0 * lane / D);
+      double sv, cv;
+      sincos(static_cast<double>(P) * theta, &sv, &cv);
+      fcos[lane] = cv;
+      fsin[lane] = sv;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool inter = p.rope_style != KVD_ROPE_HALF;
+    if (appender) {
+      // k_new rotated and rounded once to bf16, v_new copied, into the
+      // cache slot of position P (skipped outside the cache); the stores
+      // land before any wave requests a tile, and the tile that holds P
+      // reads them
+      if (P >= 0 && P < p.max_seq_len) {
+        int64_t row = -1;
+        if (PAGED) {
+          const int grp16 = paged_group(p, b, P >> 4);
+          if (grp16 >= 0) row = (static_cast<int64_t>(grp16) * 16 + (P & 15)) * p.G + g;
+        } else {
+          row = (static_cast<int64_t>(b) * p.max_seq_len + P) * p.G + g;
+        }
+        if (row >= 0) {
+          const int64_t src = (static_cast<int64_t>(b) * p.G + g) * D;
+          const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + src;
+          uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(p.k)) + row * D;
+          const int i = threadIdx.x;
+          if (i < D / 2) {
+            const int ia = inter ? 2 * i : i, ib = inter ? 2 * i + 1 : i + D / 2;
+            const double a = bf16_to_float(kn[ia]), c = bf16_to_float(kn[ib]);
+            const double cf = fcos[i], sf = fsin[i];
+            kc[ia] = double_to_bf16_rne(a * cf - c * sf);
+            kc[ib] = double_to_bf16_rne(a * sf + c * cf);
+          } else if (i < D / 2 + D) {
+            const int d = i - D / 2;
+            static_cast<uint16_t*>(const_cast<void*>(p.v))[row * D + d] =
+                static_cast<const uint16_t*>(p.v_new)[src + d];
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const TileSrc ts = tile_src(base, blk_cur);
+      issue_k(ts, kr);
+      issue_v(ts, vbuf[0]);
+    }
+    // rotate this lane's q dims (pairs 2i, 2i+1, or i and i + D/2 held in
+    // blocks kb and kb + KB/2), fp64, rounded once to fp32 as q_rot
+    float qv[KB][8];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t w[4] = {qin[kb].x, qin[kb].y, qin[kb].z, qin[kb].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qv[kb][2 * j] = bf16lo(w[j]);
+        qv[kb][2 * j + 1] = bf16hi(w[j]);
+      }
+    }
+    if (inter) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int f = kb * 16 + grp * 4 + j;
+          const double a = qv[kb][2 * j], c = qv[kb][2 * j + 1];
+          const double cf = fcos[f], sf = fsin[f];
+          qv[kb][2 * j] = static_cast<float>(a * cf - c * sf);
+          qv[kb][2 * j + 1] = static_cast<float>(a * sf + c * cf);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB / 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int f = kb * 32 + grp * 8 + e;
+          const double a = qv[kb][e], c = qv[kb + KB / 2][e];
+          const double cf = fcos[f], sf = fsin[f];
+          qv[kb][e] = static_cast<float>(a * cf - c * sf);
+          qv[kb + KB / 2][e] = static_cast<float>(a * sf + c * cf);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qraw[0][kb][0] = make_float4(qv[kb][0], qv[kb][1], qv[kb][2], qv[kb][3]);
+      qraw[0][kb][1] = make_float4(qv[kb][4], qv[kb][5], qv[kb][6], qv[kb][7]);
+    }
+    // q_rot for the caller, written once per (sequence, KV head)
+    if (p.q_rot_out && split == 0 && n < RT) {
+      float* dst = p.q_rot_out + (static_cast<int64_t>(b) * p.H + g * R + n) * D + grp * 8;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        *reinterpret_cast<float4*>(dst + kb * 32) = qraw[0][kb][0];
+        *reinterpret_cast<float4*>(dst + kb * 32 + 4) = qraw[0][kb][1];
+      }
+    }
+    // every wave has read the factors before wave 0 copies its second tile
+    // over them
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if constexpr (NB == 2) {
@@ -452,12 +575,12 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 
 // One workgroup per unit, dispatched by the hardware in the planner's order.
 // Up to 16 query rows per KV head:
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes<D>()];
   Unit u;
   if (!unit_at(p, u)) return;
-  run_split<D, 1, PAGED>(p, smem, u.b, u.g, u.split);
+  run_split<D, 1, PAGED, FUSED>(p, smem, u.b, u.g, u.split);
 }
 // 17 to 32 query rows per KV head (two column blocks): left to itself the
 // compiler splits the accumulators into AGPRs and needs 295 registers per
@@ -474,9 +597,10 @@ void decode_mfma_kernel_wide(DecodeParams p) {
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, const Launch& l) {
-  void (*k)(DecodeParams) = NB == 1 ? (paged ? decode_mfma_kernel<D, true> : decode_mfma_kernel<D, false>)
-                                    : (paged ? decode_mfma_kernel_wide<D, true>
-                                             : decode_mfma_kernel_wide<D, false>);
+  void (*k)(DecodeParams) =
+      NB == 1 ? (p.len_bias ? (paged ? decode_mfma_kernel<D, true, true> : decode_mfma_kernel<D, false, true>)
+                            : (paged ? decode_mfma_kernel<D, true, false> : decode_mfma_kernel<D, false, false>))
+              : (paged ? decode_mfma_kernel_wide<D, true> : decode_mfma_kernel_wide<D, false>);
   return launch_kernel(k, split_grid(p), dim3(256), l, p);
 }
 
@@ -491,6 +615,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l
   if (p.chunk > kMfmaMaxChunk || p.chunk % 16 != 0 || p.chunk2 > p.chunk || p.chunk2 < 16 ||
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
       p.row_groups > 1)
+    return hipErrorInvalidValue;
+  // the fused step: one new token, up to 16 query rows, its inputs given
+  if (p.len_bias && (p.len_bias != 1 || p.T != 1 || p.R > 16 || !p.q_in || !p.k_new || !p.v_new))
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }

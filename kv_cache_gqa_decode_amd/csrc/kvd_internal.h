@@ -65,7 +65,26 @@ struct DecodeParams {
   // workgroups of 16 rows each (0 or 1: one workgroup takes all); units then
   // run over G * row_groups (KV head, row group) pairs
   int32_t row_groups;
+  // Fused decode step (gqa_decode_step, one new token, the MFMA kernel):
+  // seq_lens points at the positions and len_bias is 1, so sequence b
+  // attends positions[b] + 1 tokens; the split kernel rotates q_in itself,
+  // and the workgroup of each (sequence, KV head)'s last split appends the
+  // new token's rotated k and v before it requests any tile.  len_bias 0:
+  // the plain calls.
+  int32_t len_bias;
+  int32_t rope_style;
+  double rope_base;
+  const void* q_in;         // [B, H, D] bf16, not rotated
+  const void* k_new;        // [B, G, D] bf16, not rotated
+  const void* v_new;        // [B, G, D] bf16
+  float* q_rot_out;         // [B, H, D] fp32, or null
 };
+
+// Tokens sequence b holds, from its entry in seq_lens (plus len_bias;
+// saturating, so that a position of INT32_MAX stays positive).
+__host__ __device__ __forceinline__ int len_of(const DecodeParams& p, int raw) {
+  return raw > 0x7fffffff - p.len_bias ? 0x7fffffff : raw + p.len_bias;
+}
 
 // (KV head, row group) pairs the units of a split kernel run over
 __host__ __device__ __forceinline__ int unit_heads(const DecodeParams& p) {
@@ -198,6 +217,38 @@ __host__ __device__ __forceinline__ int64_t query_row(const DecodeParams& p, int
 // bf16 pair in a 32-bit word -> two floats (exact).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Nearest-even bf16 of a double, in one rounding (no detour through fp32,
+// which would round twice).  Works on the binary64 fields directly.
+__device__ __forceinline__ uint16_t double_to_bf16_rne(double x) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
+  const int e = static_cast<int>((u >> 52) & 0x7ff);
+  const uint64_t frac = u & ((1ull << 52) - 1);
+  if (e == 0x7ff) return static_cast<uint16_t>(sign | (frac ? 0x7fc0u : 0x7f80u));
+  if (e == 0) return static_cast<uint16_t>(sign);          // |x| < 2^-1022 rounds to 0
+  int E = e - 1023;
+  if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
+  const uint64_t sig = (1ull << 52) | frac;                 // 53-bit significand
+  if (E >= -126) {                                          // bf16 normal range
+    uint64_t keep = sig >> 45;                              // 8 significant bits
+    const uint64_t rem = sig & ((1ull << 45) - 1);
+    const uint64_t halfway = 1ull << 44;
+    if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
+    if (keep == 256) { keep = 128; ++E; }
+    if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
+    return static_cast<uint16_t>(sign | (static_cast<uint32_t>(E + 127) << 7) |
+                                 static_cast<uint32_t>(keep & 0x7f));
+  }
+  // bf16 subnormal: value = sig * 2^(E-52), unit 2^-133 -> sig >> (-(E + 81))
+  const int shift = -(E + 81);                              // > 45 here
+  if (shift > 54) return static_cast<uint16_t>(sign);       // below half a unit
+  uint64_t keep = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t halfway = 1ull << (shift - 1);
+  if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
+  return static_cast<uint16_t>(sign | static_cast<uint32_t>(keep));  // 128 -> min normal
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }

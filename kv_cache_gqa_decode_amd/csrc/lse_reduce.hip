@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   // be waited for before the partials below are requested
   const __amdgpu_buffer_rsrc_t lens = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(p.seq_lens), 0, p.B * static_cast<int>(sizeof(int32_t)), 0x00020000);
-  const int L = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens, b * 4, 0, 0));
+  const int L = len_of(p, static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens, b * 4, 0, 0)));
   float m = kNegInf, wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float ls[U];

@@ -302,7 +302,7 @@ __device__ __forceinline__ bool unit_from_lengths(const DecodeParams& p, Unit& u
   const int lane = threadIdx.x & 63;
   const int id = static_cast<int>(blockIdx.x);
   const int k = id / unit_heads(p);
-  const int L = lane < p.B ? attended_len(p, p.seq_lens[lane]) : 0;
+  const int L = lane < p.B ? attended_len(p, len_of(p, p.seq_lens[lane])) : 0;
   const int n = split_count(p, L);
   int full = 0, part = 0;
   if (n > 0) {

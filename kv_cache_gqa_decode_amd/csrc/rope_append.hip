@@ -39,38 +39,6 @@
 namespace kvd {
 namespace {
 
-// Nearest-even bf16 of a double, in one rounding (no detour through fp32,
-// which would round twice).  Works on the binary64 fields directly.
-__device__ uint16_t double_to_bf16_rne(double x) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-  const uint32_t sign = static_cast<uint32_t>(u >> 63) << 15;
-  const int e = static_cast<int>((u >> 52) & 0x7ff);
-  const uint64_t frac = u & ((1ull << 52) - 1);
-  if (e == 0x7ff) return static_cast<uint16_t>(sign | (frac ? 0x7fc0u : 0x7f80u));
-  if (e == 0) return static_cast<uint16_t>(sign);          // |x| < 2^-1022 rounds to 0
-  int E = e - 1023;
-  if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
-  const uint64_t sig = (1ull << 52) | frac;                 // 53-bit significand
-  if (E >= -126) {                                          // bf16 normal range
-    uint64_t keep = sig >> 45;                              // 8 significant bits
-    const uint64_t rem = sig & ((1ull << 45) - 1);
-    const uint64_t halfway = 1ull << 44;
-    if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
-    if (keep == 256) { keep = 128; ++E; }
-    if (E > 127) return static_cast<uint16_t>(sign | 0x7f80u);
-    return static_cast<uint16_t>(sign | (static_cast<uint32_t>(E + 127) << 7) |
-                                 static_cast<uint32_t>(keep & 0x7f));
-  }
-  // bf16 subnormal: value = sig * 2^(E-52), unit 2^-133 -> sig >> (-(E + 81))
-  const int shift = -(E + 81);                              // > 45 here
-  if (shift > 54) return static_cast<uint16_t>(sign);       // below half a unit
-  uint64_t keep = sig >> shift;
-  const uint64_t rem = sig & ((1ull << shift) - 1);
-  const uint64_t halfway = 1ull << (shift - 1);
-  if (rem > halfway || (rem == halfway && (keep & 1))) ++keep;
-  return static_cast<uint16_t>(sign | static_cast<uint32_t>(keep));  // 128 -> min normal
-}
-
 // INT8 code of x under scale s: nearest integer to the fp64 quotient, ties
 // to even (v_rndne_f64), saturating at +-127; a NaN quotient gives 0.
 __device__ __forceinline__ int8_t quantize_i8(double x, float s) {

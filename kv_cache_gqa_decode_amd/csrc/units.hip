@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void build_units_kernel(DecodeParams p) {
   // full units of sequence b (all splits but the last, plus the last one when
   // it is full-size) and the tokens of its partial last split (0 if none)
   auto counts = [&](int b, int& full, int& last_tokens) {
-    const int L = attended_len(p, p.seq_lens[b]);
+    const int L = attended_len(p, len_of(p, p.seq_lens[b]));
     const int n = split_count(p, L);
     full = 0;
     last_tokens = 0;

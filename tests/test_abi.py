@@ -92,6 +92,36 @@ def test_attn_rejects_bad_arguments(lib):
     assert attn(lib, shape(batch=0)) == OK                               # nothing to do
 
 
+def step(lib, sh, q=FAKE, k=FAKE, pos=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000),
+         qr=None, base=10000.0, style=0, scale=0.125, opts=None):
+    return lib.gqa_decode_step(ctypes.byref(sh) if sh is not None else None, q, FAKE, FAKE, k, k,
+                               pos, table, msl, base, style, scale, qr, out, None, None, 0, opts,
+                               None)
+
+
+def test_step_rejects_bad_arguments(lib):
+    assert step(lib, None) == EINVAL
+    assert step(lib, shape(kv_dtype=2)) == EUNSUPPORTED                 # INT8: two calls
+    assert step(lib, shape(kv_dtype=0)) == EUNSUPPORTED                 # fp32: two calls
+    assert step(lib, shape(n_heads=64, n_kv_heads=2)) == EUNSUPPORTED   # 32 heads per KV head
+    assert step(lib, shape(head_dim=96)) == EUNSUPPORTED
+    assert step(lib, shape(), style=2) == EUNSUPPORTED
+    assert step(lib, shape(), q=None) == EINVAL
+    assert step(lib, shape(), pos=None) == EINVAL
+    assert step(lib, shape(), out=None) == EINVAL
+    assert step(lib, shape(), out=FAKE) == EINVAL                       # out aliases q
+    assert step(lib, shape(), qr=ctypes.c_void_p(0x2000)) == EINVAL     # q_rot aliases out
+    assert step(lib, shape(), q=ctypes.c_void_p(0x1008)) == EINVAL      # misaligned
+    assert step(lib, shape(), base=0.0) == EINVAL
+    assert step(lib, shape(), scale=float("inf")) == EINVAL
+    assert step(lib, shape(), table=FAKE) == EINVAL                     # table for contiguous
+    assert step(lib, shape(), msl=0) == ERANGE                          # the step attends a token
+    assert step(lib, shape(), msl=65) == ERANGE
+    vopt = B._COptions(1, 0, 0, 0, 0, 0, None, None)                     # VALU kernel asked for
+    assert step(lib, shape(), opts=ctypes.byref(vopt)) == EINVAL
+    assert step(lib, shape(batch=0)) == OK                              # nothing to do
+
+
 def test_rope_rejects_bad_arguments(lib):
     assert rope(lib, None) == EINVAL
     assert rope(lib, shape(head_dim=80)) == EUNSUPPORTED

@@ -1,0 +1,145 @@
+"""The decode step in one call (gqa_decode_step) against the two calls it
+stands for (rope_append_kv, then gqa_decode_attn_multi over positions + 1
+tokens) and against the oracle.
+
+The fused split kernel rotates q with the same fp64 arithmetic as the append
+kernel, and its last split's workgroup writes the new key and value before
+it reads any tile, so the two paths must agree bit for bit: q_rot, both
+caches, out and lse.  The oracle holds the fused step to the same gates as
+the two calls (caches bit for bit, q_rot to 1 ulp, outputs to the bf16
+gates).  Cases: head dims 64 and 128, n_rep 1-16, both RoPE styles,
+contiguous and paged (16- and 32-token blocks) caches, one and many splits
+(the direct write and the merge), every decode dispatch order, positions 0
+and at split and tile boundaries, a negative position, and the c3 batch at
+full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_gqa_decode_amd as kvd
+from kv_cache_gqa_decode_amd import workloads as W
+from tests import gates
+from tests.gpu_helpers import assert_q_rot, bits, device, oracle_step, upload
+
+pytestmark = pytest.mark.gpu
+
+LENS = np.array([1, 2, 16, 17, 32, 33, 128, 129, 300, 511, 512, 1000], np.int32)
+
+
+def _spec(B, H, G, D, S, block_size=0, q_gain=2.0):
+    if block_size:
+        nb = S // block_size
+        return W.spec("c4", batch=B, n_heads=H, n_kv_heads=G, head_dim=D,
+                      num_blocks=B * nb + 5, max_blocks_per_seq=nb, block_size=block_size,
+                      q_gain=q_gain)
+    return W.spec("c3", batch=B, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=S,
+                  q_gain=q_gain)
+
+
+def two_calls(p: W.Problem, style, options, positions=None):
+    dev = device()
+    t = upload(p, dev)
+    pos = t["positions"] if positions is None else positions
+    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], pos,
+                               t["block_table"], base=p.spec.rope_base, style=style)
+    lens = (pos + 1).contiguous()
+    out, lse = kvd.gqa_decode_attn_multi(q_rot[:, None], t["k_cache"], t["v_cache"], lens,
+                                         t["block_table"], max_seq_len=p.max_len,
+                                         options=options)
+    torch.cuda.synchronize()
+    return q_rot, out[:, 0], lse[:, 0], t
+
+
+def fused(p: W.Problem, style, options, positions=None):
+    dev = device()
+    t = upload(p, dev)
+    pos = t["positions"] if positions is None else positions
+    q_rot = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device=dev)
+    out, lse = kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                   pos, t["block_table"], base=p.spec.rope_base, style=style,
+                                   max_seq_len=p.max_len, q_rot=q_rot, options=options)
+    torch.cuda.synchronize()
+    return q_rot, out, lse, t
+
+
+def same(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.int32 if a.element_size() == 4 else torch.int16),
+                       b.contiguous().view(torch.int32 if b.element_size() == 4 else torch.int16))
+
+
+def check(p: W.Problem, style="interleaved", options=None, what=""):
+    print(f"[step] {what}", flush=True)
+    qa, oa, la, ta = two_calls(p, style, options)
+    qb, ob, lb, tb = fused(p, style, options)
+    assert same(qa, qb), f"{what}: q_rot differs from the two calls"
+    assert same(ta["k_cache"], tb["k_cache"]), f"{what}: K cache differs from the two calls"
+    assert same(ta["v_cache"], tb["v_cache"]), f"{what}: V cache differs from the two calls"
+    assert same(oa, ob), f"{what}: out differs from the two calls"
+    assert same(la, lb), f"{what}: lse differs from the two calls"
+    oq, oo, ol, okc, ovc = oracle_step(p, style=style)
+    assert np.array_equal(bits(W.from_torch(tb["k_cache"])), bits(okc)), f"{what}: K cache"
+    assert np.array_equal(bits(W.from_torch(tb["v_cache"])), bits(ovc)), f"{what}: V cache"
+    assert_q_rot(qb.cpu().numpy(), oq, what)
+    gates.assert_out(ob.cpu().numpy(), oo, "bf16", what)
+    gates.assert_lse(lb.cpu().numpy(), ol, "bf16", what)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16])
+def test_head_shapes(D, n_rep):
+    G = 2
+    s = _spec(LENS.size, G * n_rep, G, D, 1024)
+    check(W.make_problem(s, lengths=LENS), what=f"D={D} n_rep={n_rep}")
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("block_size", [0, 16, 32])
+@pytest.mark.parametrize("split", [0, 16, 64, 256])
+def test_layouts_and_splits(style, block_size, split):
+    s = _spec(LENS.size, 8, 2, 128, 1024, block_size)
+    opts = kvd.Options(split_tokens=split) if split else None
+    check(W.make_problem(s, lengths=LENS), style=style, options=opts,
+          what=f"{style} block {block_size} split {split}")
+
+
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
+def test_dispatch_orders(order):
+    s = _spec(LENS.size, 16, 4, 128, 1024, q_gain=8.0)
+    check(W.make_problem(s, lengths=LENS), options=kvd.Options(split_tokens=64, dispatch_order=order),
+          what=f"order {order}")
+
+
+def test_many_sequences_and_a_negative_position():
+    """65 sequences (the work list built by its own launch, dispatch order
+    3) with the positions given by hand: sequence 3 has none (position -1:
+    no append, out = 0, lse = -inf), the others match the two calls."""
+    B = 65
+    lens = np.resize(LENS, B)
+    s = _spec(B, 8, 2, 64, 1024)
+    p = W.make_problem(s, lengths=lens)
+    dev = device()
+    pos = torch.tensor(lens - 1, dtype=torch.int32, device=dev)
+    pos[3] = -1
+    qa, oa, la, ta = two_calls(p, "interleaved", None, positions=pos)
+    qb, ob, lb, tb = fused(p, "interleaved", None, positions=pos)
+    keep = [b for b in range(B) if b != 3]
+    assert same(qa[keep], qb[keep])
+    assert same(ta["k_cache"], tb["k_cache"]) and same(ta["v_cache"], tb["v_cache"])
+    assert same(oa, ob) and same(la, lb)
+    assert (ob[3] == 0).all() and torch.isinf(lb[3]).all()
+
+
+def test_c3_full_size():
+    """The batched workload (64 sequences up to 8K tokens): the two paths
+    bit for bit, every row against the oracle."""
+    check(W.make_problem(W.spec("c3")), what="c3 full")
+
+
+def test_unsupported_caches_raise():
+    s = _spec(2, 8, 2, 64, 64).replace(dtype="i8")
+    p = W.make_problem(s, lengths=np.array([3, 64], np.int32))
+    t = upload(p, device())
+    with pytest.raises((kvd.KvdError, ValueError)):
+        kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                            t["positions"])
