@@ -4,8 +4,8 @@ One step = RoPE on q and the new k, the KV-cache append, split-K GQA
 attention and the cross-split merge, for one layer over a batch of synthetic
 sequences whose inputs are already resident in HBM: gqa_decode_step (the
 split kernel rotates q and appends the new token itself, then the merge)
-on bf16 caches with one new token and up to 16 query heads per KV head,
-rope_append_kv + gqa_decode_attn otherwise or with --two-calls.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
+on bf16 and INT8 caches with one new token and up to 16 query heads per
+KV head, rope_append_kv + gqa_decode_attn otherwise or with --two-calls.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
 decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
 
 Timing protocol: before every timed step (and every warm-up step) a 1 GiB
@@ -567,8 +567,8 @@ def main():
                     help="dispatch order (-1 automatic): decode 0-4, prefill 5-7")
     ap.add_argument("--two-calls", action="store_true",
                     help="time rope_append_kv + gqa_decode_attn where gqa_decode_step (the step "
-                         "in one launch plus the merge) would otherwise run: bf16 caches, one "
-                         "new token, up to 16 query heads per KV head")
+                         "in one launch plus the merge) would otherwise run: bf16 and INT8 "
+                         "caches, one new token, up to 16 query heads per KV head")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph in the timed region "
                          "(the kernel-time region stays eager)")
@@ -668,14 +668,14 @@ def main():
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T, options=opts)
     sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
     # the decode step in one call where the library offers it
-    fused = (not args.two_calls and T == 1 and s.dtype == "bf16" and H // G <= 16 and
+    fused = (not args.two_calls and T == 1 and s.dtype in ("bf16", "i8") and H // G <= 16 and
              args.kernel in ("auto", "mfma"))
 
     def step(options=opts):
         if fused:
             kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                 t["positions"], table, base=s.rope_base, max_seq_len=max_len,
-                                out=out, lse=lse, workspace=ws, options=options)
+                                out=out, lse=lse, workspace=ws, options=options, **sc)
             return
         if T > 1:
             kvd.rope_append_kv_multi(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],

@@ -544,7 +544,7 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  * gqa_decode_step -- the whole decode step in one launch (plus the merge):
  * rope_append_kv followed by gqa_decode_attn_multi with n_query = 1 and
  * seq_lens[b] = positions[b] + 1 ([KVGR] §3 and §5.1 b.ii-vi; [SA4] §4.5),
- * for bf16 caches with up to 16 query heads per KV head.  The split kernel
+ * for bf16 (and, below, INT8) caches with up to 16 query heads per KV head.  The split kernel
  * rotates q itself, and for each (sequence, KV head) the workgroup of the
  * last split writes the rotated key and the value into the cache slot
  * before it reads any tile; the results are those of the two calls.
@@ -560,8 +560,12 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  *   q_rot      [B, H, D] fp32 output of the rotated q, or NULL; written for
  *              every sequence with a non-negative position
  * Errors: as rope_append_kv and gqa_decode_attn_multi; EUNSUPPORTED for a
- * cache that is not bf16 or more than 16 query heads per KV head (use the
- * two calls); ERANGE for max_seq_len_host < 1.
+ * cache that is not bf16 (INT8: gqa_decode_step_int8) or more than 16 query
+ * heads per KV head (use the two calls); ERANGE for max_seq_len_host < 1.
+ *
+ * gqa_decode_step_int8: the same on an INT8 cache with per-head scales
+ * k_scale, v_scale [G] (rope_append_kv_int8 then gqa_decode_attn_multi);
+ * the new token's codes are those rope_append_kv_int8 writes.
  */
 kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_new,
                            const void* v_new, void* k_cache, void* v_cache,
@@ -569,6 +573,14 @@ kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_
                            int32_t max_seq_len_host, double rope_base, int32_t rope_style,
                            float scale, float* q_rot, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, const kvd_options* options, void* stream);
+kvd_status gqa_decode_step_int8(const kvd_shape* shape, const void* q, const void* k_new,
+                                const void* v_new, int8_t* k_cache, int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t max_seq_len_host, double rope_base, int32_t rope_style,
+                                float scale, float* q_rot, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                const kvd_options* options, void* stream);
 
 /* Workspace bytes of gqa_decode_attn_multi with these options (NULL:
  * automatic); 0 also for an invalid shape or invalid options. */

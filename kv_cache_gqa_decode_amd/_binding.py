@@ -117,7 +117,7 @@ EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_mixed",
             "gqa_decode_workspace_size_mixed",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
-            "gqa_decode_attn_multi_noalloc", "gqa_decode_step")
+            "gqa_decode_attn_multi_noalloc", "gqa_decode_step", "gqa_decode_step_int8")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -180,6 +180,10 @@ def load_library():
                                               ctypes.c_float, P, P, P, ctypes.c_size_t, OP, P]
         lib.gqa_decode_workspace_size_mixed.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_mixed.argtypes = [SP, I32, I32, OP]
+        lib.gqa_decode_step_int8.restype = I32
+        lib.gqa_decode_step_int8.argtypes = [SP, P, P, P, P, P, P, P, P, P, I32, ctypes.c_double,
+                                             I32, ctypes.c_float, P, P, P, P, ctypes.c_size_t, OP,
+                                             P]
         lib.gqa_decode_step.restype = I32
         lib.gqa_decode_step.argtypes = [SP, P, P, P, P, P, P, P, I32, ctypes.c_double, I32,
                                         ctypes.c_float, P, P, P, P, ctypes.c_size_t, OP, P]
@@ -697,10 +701,12 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     max_seq_len: Optional[int] = None, q_rot: Optional[torch.Tensor] = None,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, want_lse: bool = True,
-                    options: Optional[Options] = None
+                    options: Optional[Options] = None, k_scale: Optional[torch.Tensor] = None,
+                    v_scale: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The decode step in one call (gqa_decode_step): rope_append_kv, then
-    attention over positions[b] + 1 tokens, for a bf16 cache with up to 16
+    attention over positions[b] + 1 tokens, for a bf16 cache (or an INT8
+    cache with ``k_scale`` / ``v_scale``: gqa_decode_step_int8) with up to 16
     query heads per KV head.  q [B, H, D], k_new / v_new [B, G, D] bf16;
     ``q_rot`` (optional, [B, H, D] float32) receives the rotated q.
     Returns (out [B, H, D], lse [B, H])."""
@@ -709,12 +715,11 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     B, H, D = (int(x) for x in q.shape)
     G = int(k_new.shape[1])
     shape = make_shape(B, H, k_cache, block_table)
-    dt = k_cache.dtype
+    int8 = k_cache.dtype == torch.int8
+    dt = _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, block_table is not None)
     _need(q, "q", dev, dt, (B, H, D))
     _need(k_new, "k_new", dev, dt, (B, G, D))
     _need(v_new, "v_new", dev, dt, (B, G, D))
-    _need(k_cache, "k_cache", dev, dt)
-    _need(v_cache, "v_cache", dev, dt, tuple(k_cache.shape))
     _need(positions, "positions", dev, torch.int32, (B,))
     if block_table is not None:
         _need(block_table, "block_table", dev, torch.int32)
@@ -729,10 +734,18 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), 1, msl, opts))
         workspace = _workspace(dev, nbytes)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gqa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
-                               _ptr(k_cache), _ptr(v_cache), _ptr(positions), _ptr(block_table),
-                               msl, float(base), _STYLES[style], _scale_arg(scale), _ptr(q_rot),
-                               _ptr(out), _ptr(lse), _ptr(workspace), wbytes, opts, _stream(dev)))
+    if int8:
+        _check(lib.gqa_decode_step_int8(
+            ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale), _ptr(v_scale), _ptr(positions), _ptr(block_table), msl, float(base),
+            _STYLES[style], _scale_arg(scale), _ptr(q_rot), _ptr(out), _ptr(lse),
+            _ptr(workspace), wbytes, opts, _stream(dev)))
+    else:
+        _check(lib.gqa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(positions),
+                                   _ptr(block_table), msl, float(base), _STYLES[style],
+                                   _scale_arg(scale), _ptr(q_rot), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), wbytes, opts, _stream(dev)))
     return out, lse
 
 

@@ -556,6 +556,84 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
                        void* workspace, size_t workspace_bytes, const kvd_options* options,
                        void* stream, int32_t T = 1);
 
+// The decode step in one launch (gqa_decode_step / _int8): scales given
+// for an INT8 cache, NULL for bf16.
+kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                     const int32_t* positions, const int32_t* block_table,
+                     int32_t max_seq_len_host, double rope_base, int32_t rope_style, float scale,
+                     float* q_rot, float* out, float* lse, void* workspace,
+                     size_t workspace_bytes, const kvd_options* options, void* stream) {
+  kvd_status st = check_shape(shape);
+  if (st != KVD_OK) return st;
+  const bool i8 = k_scale != nullptr;
+  if (shape->kv_dtype != (i8 ? KVD_INT8 : KVD_BF16) || shape->n_heads / shape->n_kv_heads > 16)
+    return KVD_EUNSUPPORTED;
+  if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (q_rot && !aligned16(q_rot)))
+    return KVD_EINVAL;
+  if (static_cast<const void*>(out) == q || (q_rot && static_cast<const void*>(q_rot) == q) ||
+      (q_rot && q_rot == out))
+    return KVD_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base) || !std::isfinite(scale)) return KVD_EINVAL;
+  const bool paged = shape->block_size != 0;
+  if (paged != (block_table != nullptr)) return KVD_EINVAL;
+  if (max_seq_len_host < 1 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
+  Tuning tu;
+  st = read_options(options, &tu);
+  if (st != KVD_OK) return st;
+  if (tu.kernel >= 0 && tu.kernel != (i8 ? 2 : 1)) return KVD_EINVAL;
+  if (shape->batch == 0) return KVD_OK;
+  int cu = 0;
+  if (device_cu_count(&cu) != 0) return KVD_EHIP;
+  Plan pl;
+  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, 1);
+  if (st != KVD_OK) return st;
+  if (pl.kernel != (i8 ? 2 : 1) || pl.row_groups > 1 || pl.n_splits < 1) return KVD_EUNSUPPORTED;
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
+  if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeParams p{};
+  // lengths: positions[b] + 1
+  p.seq_lens = positions; p.len_bias = 1;
+  p.q_in = q; p.k_new = k_new; p.v_new = v_new; p.q_rot_out = q_rot;
+  p.rope_base = rope_base; p.rope_style = rope_style;
+  p.q_rot = nullptr; p.k = k_cache; p.v = v_cache; p.table = block_table;
+  p.k_scale = k_scale; p.v_scale = v_scale;
+  p.out = out; p.lse = lse;
+  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
+  p.R = p.H / p.G; p.T = 1;
+  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
+  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
+  p.block_shift = shape->block_size == 32 ? 1 : 0;
+  p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
+  p.n_splits = pl.n_splits; p.head_groups = pl.head_groups; p.row_groups = pl.row_groups;
+  p.part_stride = pl.n_splits;
+  p.qscale = log2_scale(scale, shape->head_dim);
+  p.direct = pl.n_splits <= 1 ? 1 : 0;
+  p.grid_order = pl.grid_order;
+  if (pl.n_splits > 1) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
+    const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
+    if (pl.grid_order == 3) {
+      p.n_units = reinterpret_cast<int32_t*>(ws + pl.units_offset);
+      p.units = p.n_units + 64;
+    }
+  }
+  if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
+  const Launch l{s, tu.ev_start, tu.ev_stop};
+  if ((i8 ? launch_decode_i8(p, paged, l) : launch_decode_mfma(p, paged, l)) != hipSuccess)
+    return KVD_EHIP;
+  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
+  return KVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -588,71 +666,26 @@ kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_
                            int32_t max_seq_len_host, double rope_base, int32_t rope_style,
                            float scale, float* q_rot, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, const kvd_options* options, void* stream) {
-  kvd_status st = check_shape(shape);
-  if (st != KVD_OK) return st;
-  if (shape->kv_dtype != KVD_BF16 || shape->n_heads / shape->n_kv_heads > 16)
-    return KVD_EUNSUPPORTED;
-  if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      (q_rot && !aligned16(q_rot)))
-    return KVD_EINVAL;
-  if (static_cast<const void*>(out) == q || (q_rot && static_cast<const void*>(q_rot) == q) ||
-      (q_rot && q_rot == out))
-    return KVD_EINVAL;
-  if (!(rope_base > 0.0) || !std::isfinite(rope_base) || !std::isfinite(scale)) return KVD_EINVAL;
-  const bool paged = shape->block_size != 0;
-  if (paged != (block_table != nullptr)) return KVD_EINVAL;
-  if (max_seq_len_host < 1 || max_seq_len_host > shape->max_seq_len) return KVD_ERANGE;
-  Tuning tu;
-  st = read_options(options, &tu);
-  if (st != KVD_OK) return st;
-  if (tu.kernel >= 0 && tu.kernel != 1) return KVD_EINVAL;
-  if (shape->batch == 0) return KVD_OK;
-  int cu = 0;
-  if (device_cu_count(&cu) != 0) return KVD_EHIP;
-  Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, 1);
-  if (st != KVD_OK) return st;
-  if (pl.kernel != 1 || pl.n_splits < 1) return KVD_EUNSUPPORTED;
-  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
-  if (pl.workspace > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVD_EWORKSPACE;
+  if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;   // gqa_decode_step_int8
+  return step_impl(shape, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, positions,
+                   block_table, max_seq_len_host, rope_base, rope_style, scale, q_rot, out, lse,
+                   workspace, workspace_bytes, options, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  DecodeParams p{};
-  // lengths: positions[b] + 1
-  p.seq_lens = positions; p.len_bias = 1;
-  p.q_in = q; p.k_new = k_new; p.v_new = v_new; p.q_rot_out = q_rot;
-  p.rope_base = rope_base; p.rope_style = rope_style;
-  p.q_rot = nullptr; p.k = k_cache; p.v = v_cache; p.table = block_table;
-  p.out = out; p.lse = lse;
-  p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
-  p.R = p.H / p.G; p.T = 1;
-  p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
-  p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
-  p.block_shift = shape->block_size == 32 ? 1 : 0;
-  p.chunk = pl.chunk; p.chunk2 = pl.chunk2; p.n_big = pl.n_big;
-  p.n_splits = pl.n_splits; p.head_groups = pl.head_groups; p.row_groups = pl.row_groups;
-  p.part_stride = pl.n_splits;
-  p.qscale = log2_scale(scale, shape->head_dim);
-  p.direct = pl.n_splits <= 1 ? 1 : 0;
-  p.grid_order = pl.grid_order;
-  if (pl.n_splits > 1) {
-    char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
-    const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
-    p.part_o = reinterpret_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
-    if (pl.grid_order == 3) {
-      p.n_units = reinterpret_cast<int32_t*>(ws + pl.units_offset);
-      p.units = p.n_units + 64;
-    }
-  }
-  if (p.grid_order == 3 && launch_build_units(p, s) != hipSuccess) return KVD_EHIP;
-  const Launch l{s, tu.ev_start, tu.ev_stop};
-  if (launch_decode_mfma(p, paged, l) != hipSuccess) return KVD_EHIP;
-  if (!p.direct && launch_lse_reduce(p, s) != hipSuccess) return KVD_EHIP;
-  return KVD_OK;
+kvd_status gqa_decode_step_int8(const kvd_shape* shape, const void* q, const void* k_new,
+                                const void* v_new, int8_t* k_cache, int8_t* v_cache,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t max_seq_len_host, double rope_base, int32_t rope_style,
+                                float scale, float* q_rot, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                const kvd_options* options, void* stream) {
+  if (!shape) return KVD_EINVAL;
+  if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
+  if (!k_scale || !v_scale) return KVD_EINVAL;
+  return step_impl(shape, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions,
+                   block_table, max_seq_len_host, rope_base, rope_style, scale, q_rot, out, lse,
+                   workspace, workspace_bytes, options, stream);
 }
 
 kvd_status gqa_decode_attn(const kvd_shape* shape, const float* q_rot, const void* k_cache,

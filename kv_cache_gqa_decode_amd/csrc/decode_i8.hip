@@ -125,7 +125,12 @@ constexpr int smem_bytes_i8() {
 // One (sequence b, KV head g, split) unit computed by the whole workgroup:
 // query rows rb .. rb + 16 NB - 1 of the KV head (rb > 0 when the rows are
 // split over row groups).
-template <int D, int NB, bool PAGED>
+typedef __attribute__((address_space(3))) double lds_f64;
+
+// FUSED (the decode step in one launch, one new token, NB = 1, no row
+// groups): q is rotated here from the raw q, and the workgroup of the
+// sequence's last split quantises and appends the token's k and v first.
+template <int D, int NB, bool PAGED, bool FUSED = false>
 __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, int b, int g,
                                              int split, int rb) {
   constexpr int KB = D / 64;          // 64-dim blocks of the score contraction
@@ -136,9 +141,11 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   constexpr int NK = 4 * KB;          // K loads per tile
   constexpr int NV = kTileBytes / 1024;   // V^T copy instructions per tile
   static_assert(NB >= 1 && NB <= 2 && (D == 64 || D == 128), "tile shape");
+  static_assert(!FUSED || NB == 1, "the fused step takes up to 16 query rows");
   const int R = p.R;
   const int RT = R * p.T;             // tile columns: the query rows of this KV head
-  const int L = attended_len(p, scalar_load_i32(p.seq_lens + b));
+  const int raw_len = scalar_load_i32(p.seq_lens + b);   // FUSED: the new token's position
+  const int L = attended_len(p, len_of(p, raw_len));
   const int t0 = split_start(p, split);
   if (t0 >= L) {
     if (p.direct && split == 0) {     // empty sequence: out = 0, lse = -inf
@@ -180,8 +187,18 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   // rows are loaded once per workgroup and staged in LDS (QStage).
   float4 qraw[NB][KB][4];
   QStage<D> qst;
+  // FUSED: the raw q (bf16), rotated once the factors are in LDS
+  uint4 qin[FUSED ? 2 * KB : 1];
   if constexpr (NB == 2) {
     qst.load(p, b, g, RT, wave, lane);
+  } else if constexpr (FUSED) {
+    const uint16_t* src = static_cast<const uint16_t*>(p.q_in) +
+                          (static_cast<int64_t>(b) * p.H + g * R + (n < RT ? n : 0)) * D + grp * 16;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qin[2 * kb] = *reinterpret_cast<const uint4*>(src + kb * 64);
+      qin[2 * kb + 1] = *reinterpret_cast<const uint4*>(src + kb * 64 + 8);
+    }
   } else {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -282,9 +299,131 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
   // rows it stages stays partial instead of also waiting for this tile.
   // With one block the request stays under the branch: issuing it on every
   // path measured 2-3% slower on a 128K GQA sequence (same box, A/B).
-  if (NB == 2 || base < t1) {
+  // FUSED: the workgroup of the last split appends the new token (wave-
+  // uniform), and must not request its first tile before that
+  const bool appender = FUSED && split == split_count(p, L) - 1;
+  if (!appender && (NB == 2 || base < t1)) {
     issue_v(base, 0, vb0);
     issue_k(base, 0, kr0, vok0);
+  }
+  if constexpr (FUSED) {
+    // RoPE factors of the new token's position, fp64 as the append kernel
+    // computes them, into wave 0's second V buffer (free until its second
+    // tile)
+    const int P = raw_len;
+    lds_f64* const fcos = reinterpret_cast<lds_f64*>(stage + kTileBytes);
+    lds_f64* const fsin = fcos + D / 2;
+    if (wave == 0 && lane < D / 2) {
+      const double theta = pow(p.rope_base, -2.0 * lane / D);
+      double sv, cv;
+      sincos(static_cast<double>(P) * theta, &sv, &cv);
+      fcos[lane] = cv;
+      fsin[lane] = sv;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool inter = p.rope_style != KVD_ROPE_HALF;
+    if (appender) {
+      // the codes of the rotated k_new and of v_new in the token's slot of
+      // its 16-token group (skipped outside the cache); the stores land
+      // before any wave requests a tile, and the tile that holds P reads
+      // them
+      if (P >= 0 && P < p.max_seq_len) {
+        const int64_t grp16 = PAGED ? paged_group(p, b, P >> 4)
+                                    : static_cast<int64_t>(b) * (p.max_seq_len >> 4) + (P >> 4);
+        if (grp16 >= 0) {
+          const int64_t src = (static_cast<int64_t>(b) * p.G + g) * D;
+          const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + src;
+          int8_t* kc = static_cast<int8_t*>(const_cast<void*>(p.k)) +
+                       ((grp16 * p.G + g) * 16 + (P & 15)) * D;
+          const int i = threadIdx.x;
+          if (i < D / 2) {
+            const int ia = inter ? 2 * i : i, ib = inter ? 2 * i + 1 : i + D / 2;
+            const double a = bf16_to_float(kn[ia]), c = bf16_to_float(kn[ib]);
+            const double cf = fcos[i], sf = fsin[i];
+            const float ks = p.k_scale[g];
+            kc[ia] = quantize_i8(a * cf - c * sf, ks);
+            kc[ib] = quantize_i8(a * sf + c * cf, ks);
+          } else if (i < D / 2 + D) {
+            const int d = i - D / 2;
+            int8_t* vc = static_cast<int8_t*>(const_cast<void*>(p.v));
+            vc[((grp16 * p.G + g) * D + d) * 16 + (P & 15)] =
+                quantize_i8(bf16_to_float(static_cast<const uint16_t*>(p.v_new)[src + d]),
+                            p.v_scale[g]);
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (base < t1) {
+        issue_v(base, 0, vb0);
+        issue_k(base, 0, kr0, vok0);
+      }
+    }
+    // rotate this lane's 16 dims per 64-dim block, fp64, rounded once to
+    // fp32 as q_rot: interleaved pairs sit in the lane's dims; half pairs
+    // in blocks kb and kb + KB/2 (D = 128) or in the lane 32 apart (D = 64)
+    float qv[KB][16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t w[8] = {qin[2 * kb].x, qin[2 * kb].y, qin[2 * kb].z, qin[2 * kb].w,
+                             qin[2 * kb + 1].x, qin[2 * kb + 1].y, qin[2 * kb + 1].z,
+                             qin[2 * kb + 1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qv[kb][2 * j] = bf16lo(w[j]);
+        qv[kb][2 * j + 1] = bf16hi(w[j]);
+      }
+    }
+    if (inter) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int f = kb * 32 + grp * 8 + j;
+          const double a = qv[kb][2 * j], c = qv[kb][2 * j + 1];
+          const double cf = fcos[f], sf = fsin[f];
+          qv[kb][2 * j] = static_cast<float>(a * cf - c * sf);
+          qv[kb][2 * j + 1] = static_cast<float>(a * sf + c * cf);
+        }
+    } else if constexpr (KB == 2) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int f = grp * 16 + e;
+        const double a = qv[0][e], c = qv[1][e];
+        const double cf = fcos[f], sf = fsin[f];
+        qv[0][e] = static_cast<float>(a * cf - c * sf);
+        qv[1][e] = static_cast<float>(a * sf + c * cf);
+      }
+    } else {
+      // D = 64: dims grp*16 + e; the partner of dim d < 32 is d + 32, held
+      // by the lane with grp + 2 (lane ^ 32)
+      const bool low = grp < 2;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float other = __shfl_xor(qv[0][e], 32);
+        const int f = (grp & 1) * 16 + e;
+        const double own = qv[0][e], par = other;
+        const double cf = fcos[f], sf = fsin[f];
+        qv[0][e] = low ? static_cast<float>(own * cf - par * sf)
+                       : static_cast<float>(par * sf + own * cf);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qraw[0][kb][j] = make_float4(qv[kb][4 * j], qv[kb][4 * j + 1], qv[kb][4 * j + 2],
+                                     qv[kb][4 * j + 3]);
+    // q_rot for the caller, written once per (sequence, KV head)
+    if (p.q_rot_out && split == 0 && n < RT) {
+      float* dst = p.q_rot_out + (static_cast<int64_t>(b) * p.H + g * R + n) * D + grp * 16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(dst + kb * 64 + 4 * j) = qraw[0][kb][j];
+    }
+    // every wave has read the factors before wave 0 copies its second tile
+    // over them
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if constexpr (NB == 2) {
@@ -513,7 +652,7 @@ __device__ __forceinline__ void run_split_i8(const DecodeParams& p, char* smem, 
 
 // Up to 16 query heads per KV head: two workgroups per CU fit only if the
 // registers stay within 256 per lane, which the compiler is told to aim for.
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_i8_kernel(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes_i8<D>()];
@@ -521,7 +660,7 @@ void decode_i8_kernel(DecodeParams p) {
   if (!unit_at(p, u)) return;
   // with row groups the unit's head index is (KV head, row group)
   const int rg = p.row_groups > 1 ? p.row_groups : 1;
-  run_split_i8<D, 1, PAGED>(p, smem, u.b, u.g / rg, u.split, 16 * (u.g % rg));
+  run_split_i8<D, 1, PAGED, FUSED>(p, smem, u.b, u.g / rg, u.split, 16 * (u.g % rg));
 }
 // 17 to 32 query rows per KV head (two column blocks): at D = 128 the q
 // limbs, scores and accumulators of the second block do not fit beside the
@@ -537,9 +676,10 @@ __global__ __launch_bounds__(256) void decode_i8_kernel_wide(DecodeParams p) {
 
 template <int D, int NB>
 hipError_t launch_nb(const DecodeParams& p, bool paged, const Launch& l) {
-  void (*k)(DecodeParams) = NB == 1 ? (paged ? decode_i8_kernel<D, true> : decode_i8_kernel<D, false>)
-                                    : (paged ? decode_i8_kernel_wide<D, true>
-                                             : decode_i8_kernel_wide<D, false>);
+  void (*k)(DecodeParams) =
+      NB == 1 ? (p.len_bias ? (paged ? decode_i8_kernel<D, true, true> : decode_i8_kernel<D, false, true>)
+                            : (paged ? decode_i8_kernel<D, true, false> : decode_i8_kernel<D, false, false>))
+              : (paged ? decode_i8_kernel_wide<D, true> : decode_i8_kernel_wide<D, false>);
   return launch_kernel(k, split_grid(p), dim3(256), l, p);
 }
 
@@ -560,6 +700,10 @@ hipError_t launch_decode_i8(const DecodeParams& p, bool paged, const Launch& l) 
     return hipErrorInvalidValue;
   // row groups of 16 rows must cover the head's rows exactly
   if (p.row_groups > 1 && (p.row_groups != 2 || p.R * p.T <= 16)) return hipErrorInvalidValue;
+  // the fused step: one new token, up to 16 query rows in one workgroup
+  if (p.len_bias && (p.len_bias != 1 || p.T != 1 || p.R > 16 || p.row_groups > 1 || !p.q_in ||
+                     !p.k_new || !p.v_new))
+    return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }
 

@@ -249,6 +249,16 @@ __device__ __forceinline__ uint16_t double_to_bf16_rne(double x) {
   return static_cast<uint16_t>(sign | static_cast<uint32_t>(keep));  // 128 -> min normal
 }
 
+// INT8 code of x under scale s: nearest integer to the fp64 quotient, ties
+// to even (v_rndne_f64), saturating at +-127; a NaN quotient gives 0.
+__device__ __forceinline__ int8_t quantize_i8(double x, float s) {
+  const double q = x / static_cast<double>(s);
+  if (q != q) return 0;
+  if (q >= 127.0) return 127;
+  if (q <= -127.0) return -127;
+  return static_cast<int8_t>(static_cast<int>(__builtin_rint(q)));
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }

@@ -39,16 +39,6 @@
 namespace kvd {
 namespace {
 
-// INT8 code of x under scale s: nearest integer to the fp64 quotient, ties
-// to even (v_rndne_f64), saturating at +-127; a NaN quotient gives 0.
-__device__ __forceinline__ int8_t quantize_i8(double x, float s) {
-  const double q = x / static_cast<double>(s);
-  if (q != q) return 0;
-  if (q >= 127.0) return 127;
-  if (q <= -127.0) return -127;
-  return static_cast<int8_t>(static_cast<int>(__builtin_rint(q)));
-}
-
 // T = cache element type; int8_t stands for an INT8 cache fed with bf16
 template <typename T> __device__ __forceinline__ double load_d(const void* p, int64_t i);
 template <> __device__ __forceinline__ double load_d<float>(const void* p, int64_t i) {

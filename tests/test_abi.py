@@ -101,7 +101,7 @@ def step(lib, sh, q=FAKE, k=FAKE, pos=FAKE, table=None, msl=32, out=ctypes.c_voi
 
 def test_step_rejects_bad_arguments(lib):
     assert step(lib, None) == EINVAL
-    assert step(lib, shape(kv_dtype=2)) == EUNSUPPORTED                 # INT8: two calls
+    assert step(lib, shape(kv_dtype=2)) == EUNSUPPORTED                 # INT8: its own call
     assert step(lib, shape(kv_dtype=0)) == EUNSUPPORTED                 # fp32: two calls
     assert step(lib, shape(n_heads=64, n_kv_heads=2)) == EUNSUPPORTED   # 32 heads per KV head
     assert step(lib, shape(head_dim=96)) == EUNSUPPORTED
@@ -120,6 +120,21 @@ def test_step_rejects_bad_arguments(lib):
     vopt = B._COptions(1, 0, 0, 0, 0, 0, None, None)                     # VALU kernel asked for
     assert step(lib, shape(), opts=ctypes.byref(vopt)) == EINVAL
     assert step(lib, shape(batch=0)) == OK                              # nothing to do
+
+
+def step8(lib, sh, ks=FAKE, vs=FAKE, msl=32):
+    return lib.gqa_decode_step_int8(ctypes.byref(sh) if sh is not None else None, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, ks, vs, FAKE, None, msl, 10000.0, 0, 0.125,
+                                    None, ctypes.c_void_p(0x2000), None, None, 0, None, None)
+
+
+def test_step_int8_validates(lib):
+    assert step8(lib, None) == EINVAL
+    assert step8(lib, shape()) == EUNSUPPORTED                          # a bf16 shape
+    assert step8(lib, shape(kv_dtype=2), ks=None) == EINVAL             # scales missing
+    assert step8(lib, shape(kv_dtype=2, n_heads=64, n_kv_heads=2)) == EUNSUPPORTED
+    assert step8(lib, shape(kv_dtype=2), msl=0) == ERANGE
+    assert step8(lib, shape(kv_dtype=2, batch=0)) == OK
 
 
 def test_rope_rejects_bad_arguments(lib):

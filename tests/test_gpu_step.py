@@ -37,16 +37,25 @@ def _spec(B, H, G, D, S, block_size=0, q_gain=2.0):
                   q_gain=q_gain)
 
 
+def _scales(t, s):
+    return dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if s.dtype == "i8" else {}
+
+
 def two_calls(p: W.Problem, style, options, positions=None):
     dev = device()
     t = upload(p, dev)
     pos = t["positions"] if positions is None else positions
-    q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], pos,
-                               t["block_table"], base=p.spec.rope_base, style=style)
+    if p.spec.dtype == "i8":
+        q_rot = kvd.rope_append_kv_int8(t["q"], t["k_new"], t["v_new"], t["k_cache"],
+                                        t["v_cache"], t["k_scale"], t["v_scale"], pos,
+                                        t["block_table"], base=p.spec.rope_base, style=style)
+    else:
+        q_rot = kvd.rope_append_kv(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                   pos, t["block_table"], base=p.spec.rope_base, style=style)
     lens = (pos + 1).contiguous()
     out, lse = kvd.gqa_decode_attn_multi(q_rot[:, None], t["k_cache"], t["v_cache"], lens,
                                          t["block_table"], max_seq_len=p.max_len,
-                                         options=options)
+                                         options=options, **_scales(t, p.spec))
     torch.cuda.synchronize()
     return q_rot, out[:, 0], lse[:, 0], t
 
@@ -58,7 +67,8 @@ def fused(p: W.Problem, style, options, positions=None):
     q_rot = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device=dev)
     out, lse = kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                    pos, t["block_table"], base=p.spec.rope_base, style=style,
-                                   max_seq_len=p.max_len, q_rot=q_rot, options=options)
+                                   max_seq_len=p.max_len, q_rot=q_rot, options=options,
+                                   **_scales(t, p.spec))
     torch.cuda.synchronize()
     return q_rot, out, lse, t
 
@@ -81,8 +91,8 @@ def check(p: W.Problem, style="interleaved", options=None, what=""):
     assert np.array_equal(bits(W.from_torch(tb["k_cache"])), bits(okc)), f"{what}: K cache"
     assert np.array_equal(bits(W.from_torch(tb["v_cache"])), bits(ovc)), f"{what}: V cache"
     assert_q_rot(qb.cpu().numpy(), oq, what)
-    gates.assert_out(ob.cpu().numpy(), oo, "bf16", what)
-    gates.assert_lse(lb.cpu().numpy(), ol, "bf16", what)
+    gates.assert_out(ob.cpu().numpy(), oo, p.spec.dtype, what)
+    gates.assert_lse(lb.cpu().numpy(), ol, p.spec.dtype, what)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -136,10 +146,28 @@ def test_c3_full_size():
     check(W.make_problem(W.spec("c3")), what="c3 full")
 
 
-def test_unsupported_caches_raise():
-    s = _spec(2, 8, 2, 64, 64).replace(dtype="i8")
-    p = W.make_problem(s, lengths=np.array([3, 64], np.int32))
-    t = upload(p, device())
-    with pytest.raises((kvd.KvdError, ValueError)):
-        kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
-                            t["positions"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("block_size,split", [(0, 0), (0, 64), (16, 0), (32, 128)])
+def test_int8_cache(D, style, block_size, split):
+    """gqa_decode_step_int8: the quantising append inside the INT8 split
+    kernel, against rope_append_kv_int8 + the attention call."""
+    s = _spec(LENS.size, 8, 2, D, 1024, block_size).replace(dtype="i8")
+    opts = kvd.Options(split_tokens=split) if split else None
+    check(W.make_problem(s, lengths=LENS), style=style, options=opts,
+          what=f"INT8 D={D} {style} block {block_size} split {split}")
+
+
+def test_int8_c3_full_size():
+    check(W.make_problem(W.spec("c3").replace(dtype="i8")), what="INT8 c3 full")
+
+
+def test_unsupported_shapes_raise():
+    """More than 16 query heads per KV head, or an fp32 cache: the two
+    calls, not this one."""
+    for s in (_spec(2, 64, 2, 64, 64), _spec(2, 8, 2, 64, 64).replace(dtype="f32")):
+        p = W.make_problem(s, lengths=np.array([3, 64], np.int32))
+        t = upload(p, device())
+        with pytest.raises((kvd.KvdError, ValueError)):
+            kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                t["positions"])
