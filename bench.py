@@ -668,8 +668,8 @@ def main():
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T, options=opts)
     sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
     # the decode step in one call where the library offers it
-    fused = (not args.two_calls and T == 1 and s.dtype in ("bf16", "i8") and H // G <= 16 and
-             args.kernel in ("auto", "mfma"))
+    fused = (not args.two_calls and T == 1 and args.kernel in ("auto", "mfma") and
+             (s.dtype == "bf16" and H // G <= 32 or s.dtype == "i8" and H // G <= 16))
 
     def step(options=opts):
         if fused:

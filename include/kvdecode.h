@@ -544,7 +544,8 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  * gqa_decode_step -- the whole decode step in one launch (plus the merge):
  * rope_append_kv followed by gqa_decode_attn_multi with n_query = 1 and
  * seq_lens[b] = positions[b] + 1 ([KVGR] §3 and §5.1 b.ii-vi; [SA4] §4.5),
- * for bf16 (and, below, INT8) caches with up to 16 query heads per KV head.  The split kernel
+ * for bf16 caches with up to 32 query heads per KV head (and, below, INT8
+ * caches with up to 16).  The split kernel
  * rotates q itself, and for each (sequence, KV head) the workgroup of the
  * last split writes the rotated key and the value into the cache slot
  * before it reads any tile; the results are those of the two calls.
@@ -560,8 +561,9 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  *   q_rot      [B, H, D] fp32 output of the rotated q, or NULL; written for
  *              every sequence with a non-negative position
  * Errors: as rope_append_kv and gqa_decode_attn_multi; EUNSUPPORTED for a
- * cache that is not bf16 (INT8: gqa_decode_step_int8) or more than 16 query
- * heads per KV head (use the two calls); ERANGE for max_seq_len_host < 1.
+ * cache that is not bf16 (INT8: gqa_decode_step_int8) or more query heads
+ * per KV head than above (use the two calls); ERANGE for max_seq_len_host
+ * < 1.
  *
  * gqa_decode_step_int8: the same on an INT8 cache with per-head scales
  * k_scale, v_scale [G] (rope_append_kv_int8 then gqa_decode_attn_multi);

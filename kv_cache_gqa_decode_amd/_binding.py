@@ -706,8 +706,8 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The decode step in one call (gqa_decode_step): rope_append_kv, then
     attention over positions[b] + 1 tokens, for a bf16 cache (or an INT8
-    cache with ``k_scale`` / ``v_scale``: gqa_decode_step_int8) with up to 16
-    query heads per KV head.  q [B, H, D], k_new / v_new [B, G, D] bf16;
+    cache with ``k_scale`` / ``v_scale``: gqa_decode_step_int8) with up to 32
+    (INT8: 16) query heads per KV head.  q [B, H, D], k_new / v_new [B, G, D] bf16;
     ``q_rot`` (optional, [B, H, D] float32) receives the rotated q.
     Returns (out [B, H, D], lse [B, H])."""
     lib = load_library()

@@ -567,7 +567,10 @@ kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, c
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   const bool i8 = k_scale != nullptr;
-  if (shape->kv_dtype != (i8 ? KVD_INT8 : KVD_BF16) || shape->n_heads / shape->n_kv_heads > 16)
+  // query heads per KV head: up to 32 on bf16 caches (one or two column
+  // blocks), up to 16 on INT8 ones (the one-block kernel)
+  if (shape->kv_dtype != (i8 ? KVD_INT8 : KVD_BF16) ||
+      shape->n_heads / shape->n_kv_heads > (i8 ? 16 : 32))
     return KVD_EUNSUPPORTED;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;

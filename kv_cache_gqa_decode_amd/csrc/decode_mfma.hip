@@ -84,15 +84,14 @@ typedef __attribute__((address_space(3))) double lds_f64;
 // the waves take interleaved tiles of the split, merge through LDS and
 // write the split's normalised output and log-sum-exp (or the final output
 // when there is a single split).  FUSED (the decode step in one launch, one
-// new token, NB = 1): q is rotated here from the raw q, and the workgroup
-// of the sequence's last split appends the token's k and v first.
+// new token): q is rotated here from the raw q, and the workgroup of the
+// sequence's last split appends the token's k and v first.
 template <int D, int NB, bool PAGED, bool FUSED = false>
 __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int b, int g, int split) {
   using G = Geo<D>;
   constexpr int KB = G::KB, CB = G::CB, TT = G::TT, LPR = G::LPR, RPI = G::RPI, NVL = G::NVL;
   constexpr int kWaves = kMfmaWaves;
   static_assert(TT == 32 && NB >= 1 && NB <= 2, "tile shape");
-  static_assert(!FUSED || NB == 1, "the fused step takes up to 16 query rows");
   const int R = p.R;
   const int RT = R * p.T;             // tile columns: the query rows of this KV head
   const int raw_len = scalar_load_i32(p.seq_lens + b);   // FUSED: the new token's position
@@ -137,9 +136,20 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   // rows are loaded once per workgroup and staged in LDS (QStage).
   float4 qraw[NB][KB][2];
   QStage<D> qst;
-  // FUSED: the raw q (bf16), rotated once the factors are in LDS
-  uint4 qin[FUSED ? KB : 1];
-  if constexpr (NB == 2) {
+  // FUSED: the raw q (bf16), rotated once the factors are in LDS; with two
+  // column blocks in QStage's layout (4 dims of rows 8w + i RPI + lane/LPR)
+  using QS = QStage<D>;
+  uint4 qin[FUSED && NB == 1 ? KB : 1];
+  uint2 qin2[FUSED && NB == 2 ? QS::NI : 1];
+  if constexpr (NB == 2 && FUSED) {
+#pragma unroll
+    for (int i = 0; i < QS::NI; ++i) {
+      const int r = 8 * wave + i * QS::RPI + lane / QS::LPR;
+      qin2[i] = *reinterpret_cast<const uint2*>(
+          static_cast<const uint16_t*>(p.q_in) +
+          (static_cast<int64_t>(b) * p.H + g * R + (r < RT ? r : 0)) * D + 4 * (lane % QS::LPR));
+    }
+  } else if constexpr (NB == 2) {
     qst.load(p, b, g, RT, wave, lane);
   } else if constexpr (FUSED) {
     const int h = n;
@@ -263,7 +273,9 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     // RoPE factors of the new token's position, in fp64 as the append
     // kernel computes them, into LDS
     const int P = raw_len;
-    lds_f64* const fcos = reinterpret_cast<lds_f64*>(stage + G::kTileBytes);
+    // (past the 8 q rows QStage keeps there with two column blocks)
+    static_assert(8 * QS::ROW + D * 8 <= G::kTileBytes, "factors beside the staged q rows");
+    lds_f64* const fcos = reinterpret_cast<lds_f64*>(stage + G::kTileBytes + (NB == 2 ? 8 * QS::ROW : 0));
     lds_f64* const fsin = fcos + D / 2;
     if (wave == 0 && lane < D / 2) {
       const double theta = pow(p.rope_base, -2.0 * lane / D);
@@ -310,6 +322,42 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       issue_k(ts, kr);
       issue_v(ts, vbuf[0]);
     }
+    if constexpr (NB == 2) {
+      // rotate this lane's 4 dims (4c .. 4c+3, c = lane % LPR) of each of
+      // its rows: interleaved pairs sit in them; the half pair of dim d <
+      // D/2 is d + D/2, held by the lane LPR/2 apart in the same row
+      const int c = lane % QS::LPR;
+#pragma unroll
+      for (int i = 0; i < QS::NI; ++i) {
+        float x[4] = {bf16lo(qin2[i].x), bf16hi(qin2[i].x), bf16lo(qin2[i].y), bf16hi(qin2[i].y)};
+        if (inter) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int f = 2 * c + j;
+            const double a = x[2 * j], cc = x[2 * j + 1];
+            const double cf = fcos[f], sf = fsin[f];
+            x[2 * j] = static_cast<float>(a * cf - cc * sf);
+            x[2 * j + 1] = static_cast<float>(a * sf + cc * cf);
+          }
+        } else {
+          const bool low = c < QS::LPR / 2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float other = __shfl_xor(x[e], QS::LPR / 2);
+            const int f = 4 * (c % (QS::LPR / 2)) + e;
+            const double own = x[e], par = other;
+            const double cf = fcos[f], sf = fsin[f];
+            x[e] = low ? static_cast<float>(own * cf - par * sf)
+                       : static_cast<float>(par * sf + own * cf);
+          }
+        }
+        qst.v[i] = make_float4(x[0], x[1], x[2], x[3]);
+        const int r = 8 * wave + i * QS::RPI + lane / QS::LPR;
+        if (p.q_rot_out && split == 0 && r < RT)
+          *reinterpret_cast<float4*>(p.q_rot_out + (static_cast<int64_t>(b) * p.H + g * R + r) * D +
+                                     4 * c) = qst.v[i];
+      }
+    } else {
     // rotate this lane's q dims (pairs 2i, 2i+1, or i and i + D/2 held in
     // blocks kb and kb + KB/2), fp64, rounded once to fp32 as q_rot
     float qv[KB][8];
@@ -359,8 +407,10 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
         *reinterpret_cast<float4*>(dst + kb * 32 + 4) = qraw[0][kb][1];
       }
     }
+    }
     // every wave has read the factors before wave 0 copies its second tile
-    // over them
+    // over them (with two column blocks also before QStage's rows are
+    // written beside them)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
@@ -586,13 +636,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
 // compiler splits the accumulators into AGPRs and needs 295 registers per
 // lane at D = 128, one workgroup per CU; held to 256 it fits them in VGPRs
 // without spilling, and two workgroups share a CU.
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mfma_kernel_wide(DecodeParams p) {
   __shared__ __align__(16) char smem[smem_bytes<D>()];
   Unit u;
   if (!unit_at(p, u)) return;
-  run_split<D, 2, PAGED>(p, smem, u.b, u.g, u.split);
+  run_split<D, 2, PAGED, FUSED>(p, smem, u.b, u.g, u.split);
 }
 
 template <int D, int NB>
@@ -600,7 +650,10 @@ hipError_t launch_nb(const DecodeParams& p, bool paged, const Launch& l) {
   void (*k)(DecodeParams) =
       NB == 1 ? (p.len_bias ? (paged ? decode_mfma_kernel<D, true, true> : decode_mfma_kernel<D, false, true>)
                             : (paged ? decode_mfma_kernel<D, true, false> : decode_mfma_kernel<D, false, false>))
-              : (paged ? decode_mfma_kernel_wide<D, true> : decode_mfma_kernel_wide<D, false>);
+              : (p.len_bias ? (paged ? decode_mfma_kernel_wide<D, true, true>
+                                     : decode_mfma_kernel_wide<D, false, true>)
+                            : (paged ? decode_mfma_kernel_wide<D, true, false>
+                                     : decode_mfma_kernel_wide<D, false, false>));
   return launch_kernel(k, split_grid(p), dim3(256), l, p);
 }
 
@@ -616,8 +669,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
       p.row_groups > 1)
     return hipErrorInvalidValue;
-  // the fused step: one new token, up to 16 query rows, its inputs given
-  if (p.len_bias && (p.len_bias != 1 || p.T != 1 || p.R > 16 || !p.q_in || !p.k_new || !p.v_new))
+  // the fused step: one new token, its inputs given
+  if (p.len_bias && (p.len_bias != 1 || p.T != 1 || !p.q_in || !p.k_new || !p.v_new))
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }

@@ -103,7 +103,7 @@ def test_step_rejects_bad_arguments(lib):
     assert step(lib, None) == EINVAL
     assert step(lib, shape(kv_dtype=2)) == EUNSUPPORTED                 # INT8: its own call
     assert step(lib, shape(kv_dtype=0)) == EUNSUPPORTED                 # fp32: two calls
-    assert step(lib, shape(n_heads=64, n_kv_heads=2)) == EUNSUPPORTED   # 32 heads per KV head
+    assert step(lib, shape(n_heads=128, n_kv_heads=2)) == EUNSUPPORTED  # 64 heads per KV head
     assert step(lib, shape(head_dim=96)) == EUNSUPPORTED
     assert step(lib, shape(), style=2) == EUNSUPPORTED
     assert step(lib, shape(), q=None) == EINVAL

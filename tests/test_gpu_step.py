@@ -96,7 +96,7 @@ def check(p: W.Problem, style="interleaved", options=None, what=""):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16, 20, 32])
 def test_head_shapes(D, n_rep):
     G = 2
     s = _spec(LENS.size, G * n_rep, G, D, 1024)
@@ -162,10 +162,28 @@ def test_int8_c3_full_size():
     check(W.make_problem(W.spec("c3").replace(dtype="i8")), what="INT8 c3 full")
 
 
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("block_size", [0, 32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_two_column_blocks(style, block_size, D):
+    """17-32 query heads per KV head (the kernel with two column blocks,
+    its q rows staged through LDS): MQA with 32 heads and a 24-head group."""
+    for H, G in ((32, 1), (48, 2)):
+        s = _spec(LENS.size, H, G, D, 1024, block_size, q_gain=4.0)
+        check(W.make_problem(s, lengths=LENS), style=style, options=kvd.Options(split_tokens=64),
+              what=f"two blocks H={H} G={G} D={D} {style} block {block_size}")
+
+
+def test_mqa_128k():
+    """The 128K MQA sequence at full size (32 heads on one KV head)."""
+    check(W.make_problem(W.spec("c5", n_kv_heads=1)), what="c5 MQA full")
+
+
 def test_unsupported_shapes_raise():
-    """More than 16 query heads per KV head, or an fp32 cache: the two
-    calls, not this one."""
-    for s in (_spec(2, 64, 2, 64, 64), _spec(2, 8, 2, 64, 64).replace(dtype="f32")):
+    """More query heads per KV head than the kernels take (64, or 32 on an
+    INT8 cache), or an fp32 cache: the two calls, not this one."""
+    for s in (_spec(2, 128, 2, 64, 64), _spec(2, 8, 2, 64, 64).replace(dtype="f32"),
+              _spec(2, 64, 2, 64, 64).replace(dtype="i8")):
         p = W.make_problem(s, lengths=np.array([3, 64], np.int32))
         t = upload(p, device())
         with pytest.raises((kvd.KvdError, ValueError)):
