@@ -3,9 +3,11 @@
 One step = RoPE on q and the new k, the KV-cache append, split-K GQA
 attention and the cross-split merge, for one layer over a batch of synthetic
 sequences whose inputs are already resident in HBM: gqa_decode_step (the
-split kernel rotates q and appends the new token itself, then the merge)
-on bf16 and INT8 caches with one new token and up to 16 query heads per
-KV head, rope_append_kv + gqa_decode_attn otherwise or with --two-calls.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
+split kernel rotates q and appends the new tokens itself, then the merge)
+on bf16 caches with up to 16 new tokens and up to 32 query rows (new tokens
+x query heads) per KV head and on INT8 caches with one new token and up to
+16 query heads per KV head; rope_append_kv(_multi) + gqa_decode_attn(_multi)
+otherwise or with --two-calls.  Default workload: c3, the batched variable-length Llama-3-8B-shaped
 decode (B 64, H 32, G 8, D 128, bf16 KV, contexts uniform in [512, 8192]).
 
 Timing protocol: before every timed step (and every warm-up step) a 1 GiB
@@ -566,9 +568,9 @@ def main():
     ap.add_argument("--order", type=int, default=-1,
                     help="dispatch order (-1 automatic): decode 0-4, prefill 5-7")
     ap.add_argument("--two-calls", action="store_true",
-                    help="time rope_append_kv + gqa_decode_attn where gqa_decode_step (the step "
-                         "in one launch plus the merge) would otherwise run: bf16 and INT8 "
-                         "caches, one new token, up to 16 query heads per KV head")
+                    help="time rope_append_kv(_multi) + gqa_decode_attn(_multi) where "
+                         "gqa_decode_step (the step in one launch plus the merge) would "
+                         "otherwise run")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as one captured HIP graph in the timed region "
                          "(the kernel-time region stays eager)")
@@ -668,8 +670,9 @@ def main():
     plan = kvd.get_plan(B, H, t["k_cache"], table, max_len, n_query=T, options=opts)
     sc = dict(k_scale=t["k_scale"], v_scale=t["v_scale"]) if int8 else {}
     # the decode step in one call where the library offers it
-    fused = (not args.two_calls and T == 1 and args.kernel in ("auto", "mfma") and
-             (s.dtype == "bf16" and H // G <= 32 or s.dtype == "i8" and H // G <= 16))
+    fused = (not args.two_calls and args.kernel in ("auto", "mfma") and
+             (T == 1 and (s.dtype == "bf16" and H // G <= 32 or s.dtype == "i8" and H // G <= 16)
+              or s.dtype == "bf16" and T <= 16 and T * (H // G) <= 32))
 
     def step(options=opts):
         if fused:
@@ -766,7 +769,8 @@ def main():
                    "n_splits": plan["n_splits"], "kernel": plan["kernel"],
                    "launch": "hip graph replay" if args.graph else "eager launches",
                    "step": ("gqa_decode_step: RoPE, append and attention in the split kernel, "
-                            "then the merge" if fused else "rope_append_kv, then the attention call"),
+                            "then the merge" if fused else "rope_append_kv, then the attention call"
+                            if T == 1 else "rope_append_kv_multi, then the attention call"),
                    "parallelism": "single GPU"},
         "seq_steps_per_s": round(B / (ms_per_step * 1e-3), 1),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),

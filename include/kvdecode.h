@@ -565,6 +565,14 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  * per KV head than above (use the two calls); ERANGE for max_seq_len_host
  * < 1.
  *
+ * gqa_decode_step_multi: n_query = T new tokens per sequence (1 <= T <= 16,
+ * T x query heads per KV head <= 32), bf16 caches: rope_append_kv_multi
+ * then gqa_decode_attn_multi with seq_lens[b] = positions[b] + T; q, q_rot,
+ * out [B, T, H, D], k_new, v_new [B, T, G, D], lse [B, T, H]; workspace
+ * gqa_decode_workspace_size_multi(shape, T, ..).  Each split's workgroup
+ * appends the window tokens its split holds (the last one also those past
+ * max_seq_len_host).
+ *
  * gqa_decode_step_int8: the same on an INT8 cache with per-head scales
  * k_scale, v_scale [G] (rope_append_kv_int8 then gqa_decode_attn_multi);
  * the new token's codes are those rope_append_kv_int8 writes.
@@ -575,6 +583,13 @@ kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_
                            int32_t max_seq_len_host, double rope_base, int32_t rope_style,
                            float scale, float* q_rot, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, const kvd_options* options, void* stream);
+kvd_status gqa_decode_step_multi(const kvd_shape* shape, int32_t n_query, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* positions,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 double rope_base, int32_t rope_style, float scale, float* q_rot,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 const kvd_options* options, void* stream);
 kvd_status gqa_decode_step_int8(const kvd_shape* shape, const void* q, const void* k_new,
                                 const void* v_new, int8_t* k_cache, int8_t* v_cache,
                                 const float* k_scale, const float* v_scale,

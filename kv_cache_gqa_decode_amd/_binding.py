@@ -117,7 +117,8 @@ EXPORTED = ("rope_append_kv", "gqa_decode_attn", "rope_append_kv_int8",
             "gqa_decode_attn_mixed",
             "gqa_decode_workspace_size_mixed",
             "kvd_status_string", "kvd_get_plan", "kvd_get_plan_multi", "kvd_read_probe",
-            "gqa_decode_attn_multi_noalloc", "gqa_decode_step", "gqa_decode_step_int8")
+            "gqa_decode_attn_multi_noalloc", "gqa_decode_step", "gqa_decode_step_int8",
+            "gqa_decode_step_multi")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # KVD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -187,6 +188,10 @@ def load_library():
         lib.gqa_decode_step.restype = I32
         lib.gqa_decode_step.argtypes = [SP, P, P, P, P, P, P, P, I32, ctypes.c_double, I32,
                                         ctypes.c_float, P, P, P, P, ctypes.c_size_t, OP, P]
+        lib.gqa_decode_step_multi.restype = I32
+        lib.gqa_decode_step_multi.argtypes = [SP, I32, P, P, P, P, P, P, P, I32, ctypes.c_double,
+                                              I32, ctypes.c_float, P, P, P, P, ctypes.c_size_t,
+                                              OP, P]
         lib.gqa_decode_workspace_size_multi.restype = ctypes.c_size_t
         lib.gqa_decode_workspace_size_multi.argtypes = [SP, I32, I32, OP]
         lib.kvd_status_string.restype = ctypes.c_char_p
@@ -709,32 +714,51 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     cache with ``k_scale`` / ``v_scale``: gqa_decode_step_int8) with up to 32
     (INT8: 16) query heads per KV head.  q [B, H, D], k_new / v_new [B, G, D] bf16;
     ``q_rot`` (optional, [B, H, D] float32) receives the rotated q.
-    Returns (out [B, H, D], lse [B, H])."""
+    Returns (out [B, H, D], lse [B, H]).
+
+    With q [B, T, H, D] and k_new / v_new [B, T, G, D] (bf16 cache, T <= 16
+    new tokens, T x query heads per KV head <= 32): gqa_decode_step_multi,
+    rope_append_kv_multi then attention over positions[b] + T tokens;
+    q_rot, out [B, T, H, D], lse [B, T, H]."""
     lib = load_library()
     dev = k_cache.device
-    B, H, D = (int(x) for x in q.shape)
-    G = int(k_new.shape[1])
+    multi = q.dim() == 4
+    if multi:
+        B, T, H, D = (int(x) for x in q.shape)
+        G = int(k_new.shape[2])
+    else:
+        B, H, D = (int(x) for x in q.shape)
+        T, G = 1, int(k_new.shape[1])
+    lead = (B, T) if multi else (B,)
     shape = make_shape(B, H, k_cache, block_table)
     int8 = k_cache.dtype == torch.int8
+    if multi and int8:
+        raise ValueError("several new tokens per sequence need a bf16 cache")
     dt = _multi_cache_checks(k_cache, v_cache, k_scale, v_scale, G, dev, block_table is not None)
-    _need(q, "q", dev, dt, (B, H, D))
-    _need(k_new, "k_new", dev, dt, (B, G, D))
-    _need(v_new, "v_new", dev, dt, (B, G, D))
+    _need(q, "q", dev, dt, lead + (H, D))
+    _need(k_new, "k_new", dev, dt, lead + (G, D))
+    _need(v_new, "v_new", dev, dt, lead + (G, D))
     _need(positions, "positions", dev, torch.int32, (B,))
     if block_table is not None:
         _need(block_table, "block_table", dev, torch.int32)
     if q_rot is not None:
-        _need(q_rot, "q_rot", dev, torch.float32, (B, H, D))
+        _need(q_rot, "q_rot", dev, torch.float32, lead + (H, D))
     if style not in _STYLES:
         raise ValueError(f"style must be one of {sorted(_STYLES)}")
     msl = shape.max_seq_len if max_seq_len is None else int(max_seq_len)
-    out, lse = _outputs((B,), H, D, dev, out, lse, want_lse)
+    out, lse = _outputs(lead, H, D, dev, out, lse, want_lse)
     opts = _options(options)
     if workspace is None:
-        nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), 1, msl, opts))
+        nbytes = int(lib.gqa_decode_workspace_size_multi(ctypes.byref(shape), T, msl, opts))
         workspace = _workspace(dev, nbytes)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if int8:
+    if multi:
+        _check(lib.gqa_decode_step_multi(
+            ctypes.byref(shape), T, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+            _ptr(v_cache), _ptr(positions), _ptr(block_table), msl, float(base), _STYLES[style],
+            _scale_arg(scale), _ptr(q_rot), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, opts,
+            _stream(dev)))
+    elif int8:
         _check(lib.gqa_decode_step_int8(
             ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
             _ptr(k_scale), _ptr(v_scale), _ptr(positions), _ptr(block_table), msl, float(base),

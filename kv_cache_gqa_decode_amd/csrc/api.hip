@@ -558,19 +558,21 @@ kvd_status decode_impl(const kvd_shape* shape, const float* q_rot, const void* k
 
 // The decode step in one launch (gqa_decode_step / _int8): scales given
 // for an INT8 cache, NULL for bf16.
-kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, const void* v_new,
-                     void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
-                     const int32_t* positions, const int32_t* block_table,
+kvd_status step_impl(const kvd_shape* shape, int32_t T, const void* q, const void* k_new,
+                     const void* v_new, void* k_cache, void* v_cache, const float* k_scale,
+                     const float* v_scale, const int32_t* positions, const int32_t* block_table,
                      int32_t max_seq_len_host, double rope_base, int32_t rope_style, float scale,
                      float* q_rot, float* out, float* lse, void* workspace,
                      size_t workspace_bytes, const kvd_options* options, void* stream) {
   kvd_status st = check_shape(shape);
   if (st != KVD_OK) return st;
   const bool i8 = k_scale != nullptr;
+  // new tokens: up to 16 on bf16 caches (the INT8 kernel's fused form takes one)
+  if (T < 1 || T > (i8 ? 1 : 16) || T > shape->max_seq_len) return KVD_EUNSUPPORTED;
   // query heads per KV head: up to 32 on bf16 caches (one or two column
   // blocks), up to 16 on INT8 ones (the one-block kernel)
   if (shape->kv_dtype != (i8 ? KVD_INT8 : KVD_BF16) ||
-      shape->n_heads / shape->n_kv_heads > (i8 ? 16 : 32))
+      shape->n_heads / shape->n_kv_heads * T > (i8 ? 16 : 32))
     return KVD_EUNSUPPORTED;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;
@@ -592,7 +594,7 @@ kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, c
   int cu = 0;
   if (device_cu_count(&cu) != 0) return KVD_EHIP;
   Plan pl;
-  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, 1);
+  st = make_plan(shape, max_seq_len_host, cu, tu, &pl, T);
   if (st != KVD_OK) return st;
   if (pl.kernel != (i8 ? 2 : 1) || pl.row_groups > 1 || pl.n_splits < 1) return KVD_EUNSUPPORTED;
   if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return KVD_EWORKSPACE;
@@ -600,15 +602,15 @@ kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, c
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeParams p{};
-  // lengths: positions[b] + 1
-  p.seq_lens = positions; p.len_bias = 1;
+  // lengths: positions[b] + T
+  p.seq_lens = positions; p.len_bias = T;
   p.q_in = q; p.k_new = k_new; p.v_new = v_new; p.q_rot_out = q_rot;
   p.rope_base = rope_base; p.rope_style = rope_style;
   p.q_rot = nullptr; p.k = k_cache; p.v = v_cache; p.table = block_table;
   p.k_scale = k_scale; p.v_scale = v_scale;
   p.out = out; p.lse = lse;
   p.B = shape->batch; p.H = shape->n_heads; p.G = shape->n_kv_heads; p.D = shape->head_dim;
-  p.R = p.H / p.G; p.T = 1;
+  p.R = p.H / p.G; p.T = T;
   p.max_seq_len = shape->max_seq_len; p.max_len_host = max_seq_len_host;
   p.num_blocks = shape->num_blocks; p.max_blocks_per_seq = shape->max_blocks_per_seq;
   p.block_shift = shape->block_size == 32 ? 1 : 0;
@@ -620,7 +622,7 @@ kvd_status step_impl(const kvd_shape* shape, const void* q, const void* k_new, c
   p.grid_order = pl.grid_order;
   if (pl.n_splits > 1) {
     char* ws = static_cast<char*>(workspace);
-    const size_t rows = static_cast<size_t>(p.B) * p.H * p.n_splits;
+    const size_t rows = static_cast<size_t>(p.B) * p.T * p.H * p.n_splits;
     const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
     p.part_o = reinterpret_cast<float*>(ws);
     p.part_lse = reinterpret_cast<float*>(ws + o_bytes);
@@ -670,9 +672,22 @@ kvd_status gqa_decode_step(const kvd_shape* shape, const void* q, const void* k_
                            float scale, float* q_rot, float* out, float* lse, void* workspace,
                            size_t workspace_bytes, const kvd_options* options, void* stream) {
   if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;   // gqa_decode_step_int8
-  return step_impl(shape, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, positions,
+  return step_impl(shape, 1, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr, positions,
                    block_table, max_seq_len_host, rope_base, rope_style, scale, q_rot, out, lse,
                    workspace, workspace_bytes, options, stream);
+}
+
+kvd_status gqa_decode_step_multi(const kvd_shape* shape, int32_t n_query, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* positions,
+                                 const int32_t* block_table, int32_t max_seq_len_host,
+                                 double rope_base, int32_t rope_style, float scale, float* q_rot,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 const kvd_options* options, void* stream) {
+  if (shape && shape->kv_dtype == KVD_INT8) return KVD_EUNSUPPORTED;
+  return step_impl(shape, n_query, q, k_new, v_new, k_cache, v_cache, nullptr, nullptr,
+                   positions, block_table, max_seq_len_host, rope_base, rope_style, scale, q_rot,
+                   out, lse, workspace, workspace_bytes, options, stream);
 }
 
 kvd_status gqa_decode_step_int8(const kvd_shape* shape, const void* q, const void* k_new,
@@ -686,7 +701,7 @@ kvd_status gqa_decode_step_int8(const kvd_shape* shape, const void* q, const voi
   if (!shape) return KVD_EINVAL;
   if (shape->kv_dtype != KVD_INT8) return KVD_EUNSUPPORTED;
   if (!k_scale || !v_scale) return KVD_EINVAL;
-  return step_impl(shape, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions,
+  return step_impl(shape, 1, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, positions,
                    block_table, max_seq_len_host, rope_base, rope_style, scale, q_rot, out, lse,
                    workspace, workspace_bytes, options, stream);
 }

@@ -83,9 +83,10 @@ typedef __attribute__((address_space(3))) double lds_f64;
 // One (sequence b, KV head g, split) unit computed by the whole workgroup:
 // the waves take interleaved tiles of the split, merge through LDS and
 // write the split's normalised output and log-sum-exp (or the final output
-// when there is a single split).  FUSED (the decode step in one launch, one
-// new token): q is rotated here from the raw q, and the workgroup of the
-// sequence's last split appends the token's k and v first.
+// when there is a single split).  FUSED (the decode step in one launch, T
+// new tokens at positions P .. P + T - 1): q is rotated here from the raw
+// q, and each workgroup whose split holds window tokens (the last split
+// also those past the host bound) appends their k and v first.
 template <int D, int NB, bool PAGED, bool FUSED = false>
 __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int b, int g, int split) {
   using G = Geo<D>;
@@ -94,7 +95,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   static_assert(TT == 32 && NB >= 1 && NB <= 2, "tile shape");
   const int R = p.R;
   const int RT = R * p.T;             // tile columns: the query rows of this KV head
-  const int raw_len = scalar_load_i32(p.seq_lens + b);   // FUSED: the new token's position
+  const int raw_len = scalar_load_i32(p.seq_lens + b);   // FUSED: the first new token's position
   const int L = attended_len(p, len_of(p, raw_len));
   const int t0 = split_start(p, split);
   if (t0 >= L) {
@@ -145,16 +146,16 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
 #pragma unroll
     for (int i = 0; i < QS::NI; ++i) {
       const int r = 8 * wave + i * QS::RPI + lane / QS::LPR;
-      qin2[i] = *reinterpret_cast<const uint2*>(
-          static_cast<const uint16_t*>(p.q_in) +
-          (static_cast<int64_t>(b) * p.H + g * R + (r < RT ? r : 0)) * D + 4 * (lane % QS::LPR));
+      qin2[i] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.q_in) +
+                                                query_row(p, b, g, r < RT ? r : 0) * D +
+                                                4 * (lane % QS::LPR));
     }
   } else if constexpr (NB == 2) {
     qst.load(p, b, g, RT, wave, lane);
   } else if constexpr (FUSED) {
     const int h = n;
-    const uint16_t* src = static_cast<const uint16_t*>(p.q_in) +
-                          (static_cast<int64_t>(b) * p.H + g * R + (h < RT ? h : 0)) * D + grp * 8;
+    const uint16_t* src =
+        static_cast<const uint16_t*>(p.q_in) + query_row(p, b, g, h < RT ? h : 0) * D + grp * 8;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qin[kb] = *reinterpret_cast<const uint4*>(src + kb * 32);
   } else {
@@ -259,9 +260,16 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
   int blk_cur[2];
   int base = t0 + wave * TT;
   tile_blocks(0, blk_cur);
-  // FUSED: the workgroup of the last split appends the new token (wave-
-  // uniform), and must not request its first tile before that
-  const bool appender = FUSED && split == split_count(p, L) - 1;
+  // FUSED: a workgroup whose split holds window tokens appends them (the
+  // last split also those at or past the host bound), and must not request
+  // its first tile before that; wave-uniform
+  const int P0 = raw_len;
+  const bool last_split = split == split_count(p, L) - 1;
+  const int app_lo = P0 > t0 ? P0 : t0;
+  const int64_t win_end = static_cast<int64_t>(P0) + p.T;
+  const int64_t split_end = static_cast<int64_t>(t0) + split_size(p, split);
+  const int app_hi = static_cast<int>(last_split || win_end < split_end ? win_end : split_end);
+  const bool appender = FUSED && app_lo < app_hi;
   if (!appender) {
     // issued on every path (a wave without tiles gets empty descriptors and
     // reads nothing), so the wait for the q loads above stays partial
@@ -270,51 +278,56 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     issue_v(ts, vbuf[0]);
   }
   if constexpr (FUSED) {
-    // RoPE factors of the new token's position, in fp64 as the append
-    // kernel computes them, into LDS
-    const int P = raw_len;
-    // (past the 8 q rows QStage keeps there with two column blocks)
-    static_assert(8 * QS::ROW + D * 8 <= G::kTileBytes, "factors beside the staged q rows");
-    lds_f64* const fcos = reinterpret_cast<lds_f64*>(stage + G::kTileBytes + (NB == 2 ? 8 * QS::ROW : 0));
-    lds_f64* const fsin = fcos + D / 2;
-    if (wave == 0 && lane < D / 2) {
-      const double theta = pow(p.rope_base, -2.0 * lane / D);
+    // RoPE factors of each new token's position (token t at P0 + t), in
+    // fp64 as the append kernel computes them, into LDS: token t's table in
+    // wave t % 4's second V buffer (past the 8 q rows QStage keeps there
+    // with two column blocks), t / 4 tables in (up to 16 tokens)
+    static_assert((NB == 2 ? 8 * QS::ROW : 0) + 4 * D * 8 <= G::kTileBytes,
+                  "four factor tables beside the staged q rows");
+    auto fac = [&](int t) {
+      return reinterpret_cast<lds_f64*>(stage + (2 * (t & 3) + 1) * G::kTileBytes +
+                                        (NB == 2 ? 8 * QS::ROW : 0) + (t >> 2) * D * 8);
+    };
+    for (int idx = threadIdx.x; idx < p.T * (D / 2); idx += 256) {
+      const int t = idx / (D / 2), i = idx - t * (D / 2);
+      const double theta = pow(p.rope_base, -2.0 * i / D);
       double sv, cv;
-      sincos(static_cast<double>(P) * theta, &sv, &cv);
-      fcos[lane] = cv;
-      fsin[lane] = sv;
+      sincos(static_cast<double>(static_cast<int64_t>(P0) + t) * theta, &sv, &cv);
+      fac(t)[i] = cv;
+      fac(t)[D / 2 + i] = sv;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool inter = p.rope_style != KVD_ROPE_HALF;
     if (appender) {
-      // k_new rotated and rounded once to bf16, v_new copied, into the
-      // cache slot of position P (skipped outside the cache); the stores
-      // land before any wave requests a tile, and the tile that holds P
-      // reads them
-      if (P >= 0 && P < p.max_seq_len) {
+      // each of its window tokens: k_new rotated and rounded once to bf16,
+      // v_new copied, into the token's cache slot (skipped outside the
+      // cache); the stores land before any wave requests a tile, and the
+      // tiles that hold the tokens read them
+      constexpr int kItems = D / 2 + D;   // pairs of k, elements of v
+      for (int idx = threadIdx.x; idx < (app_hi - app_lo) * kItems; idx += 256) {
+        const int pos = app_lo + idx / kItems, it = idx % kItems, t = pos - P0;
+        if (pos < 0 || pos >= p.max_seq_len) continue;
         int64_t row = -1;
         if (PAGED) {
-          const int grp16 = paged_group(p, b, P >> 4);
-          if (grp16 >= 0) row = (static_cast<int64_t>(grp16) * 16 + (P & 15)) * p.G + g;
+          const int grp16 = paged_group(p, b, pos >> 4);
+          if (grp16 >= 0) row = (static_cast<int64_t>(grp16) * 16 + (pos & 15)) * p.G + g;
         } else {
-          row = (static_cast<int64_t>(b) * p.max_seq_len + P) * p.G + g;
+          row = (static_cast<int64_t>(b) * p.max_seq_len + pos) * p.G + g;
         }
-        if (row >= 0) {
-          const int64_t src = (static_cast<int64_t>(b) * p.G + g) * D;
+        if (row < 0) continue;
+        const int64_t src = ((static_cast<int64_t>(b) * p.T + t) * p.G + g) * D;
+        if (it < D / 2) {
           const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + src;
           uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(p.k)) + row * D;
-          const int i = threadIdx.x;
-          if (i < D / 2) {
-            const int ia = inter ? 2 * i : i, ib = inter ? 2 * i + 1 : i + D / 2;
-            const double a = bf16_to_float(kn[ia]), c = bf16_to_float(kn[ib]);
-            const double cf = fcos[i], sf = fsin[i];
-            kc[ia] = double_to_bf16_rne(a * cf - c * sf);
-            kc[ib] = double_to_bf16_rne(a * sf + c * cf);
-          } else if (i < D / 2 + D) {
-            const int d = i - D / 2;
-            static_cast<uint16_t*>(const_cast<void*>(p.v))[row * D + d] =
-                static_cast<const uint16_t*>(p.v_new)[src + d];
-          }
+          const int ia = inter ? 2 * it : it, ib = inter ? 2 * it + 1 : it + D / 2;
+          const double a = bf16_to_float(kn[ia]), c = bf16_to_float(kn[ib]);
+          const double cf = fac(t)[it], sf = fac(t)[D / 2 + it];
+          kc[ia] = double_to_bf16_rne(a * cf - c * sf);
+          kc[ib] = double_to_bf16_rne(a * sf + c * cf);
+        } else {
+          const int d = it - D / 2;
+          static_cast<uint16_t*>(const_cast<void*>(p.v))[row * D + d] =
+              static_cast<const uint16_t*>(p.v_new)[src + d];
         }
       }
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -329,6 +342,9 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       const int c = lane % QS::LPR;
 #pragma unroll
       for (int i = 0; i < QS::NI; ++i) {
+        const int r = 8 * wave + i * QS::RPI + lane / QS::LPR;
+        const lds_f64* const fcos = fac((r < RT ? r : 0) / R);
+        const lds_f64* const fsin = fcos + D / 2;
         float x[4] = {bf16lo(qin2[i].x), bf16hi(qin2[i].x), bf16lo(qin2[i].y), bf16hi(qin2[i].y)};
         if (inter) {
 #pragma unroll
@@ -352,14 +368,15 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
           }
         }
         qst.v[i] = make_float4(x[0], x[1], x[2], x[3]);
-        const int r = 8 * wave + i * QS::RPI + lane / QS::LPR;
         if (p.q_rot_out && split == 0 && r < RT)
-          *reinterpret_cast<float4*>(p.q_rot_out + (static_cast<int64_t>(b) * p.H + g * R + r) * D +
-                                     4 * c) = qst.v[i];
+          *reinterpret_cast<float4*>(p.q_rot_out + query_row(p, b, g, r) * D + 4 * c) = qst.v[i];
       }
     } else {
     // rotate this lane's q dims (pairs 2i, 2i+1, or i and i + D/2 held in
-    // blocks kb and kb + KB/2), fp64, rounded once to fp32 as q_rot
+    // blocks kb and kb + KB/2), fp64, rounded once to fp32 as q_rot; the
+    // lane's row n is token n / R
+    const lds_f64* const fcos = fac((n < RT ? n : 0) / R);
+    const lds_f64* const fsin = fcos + D / 2;
     float qv[KB][8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -400,7 +417,7 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
     }
     // q_rot for the caller, written once per (sequence, KV head)
     if (p.q_rot_out && split == 0 && n < RT) {
-      float* dst = p.q_rot_out + (static_cast<int64_t>(b) * p.H + g * R + n) * D + grp * 8;
+      float* dst = p.q_rot_out + query_row(p, b, g, n) * D + grp * 8;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         *reinterpret_cast<float4*>(dst + kb * 32) = qraw[0][kb][0];
@@ -669,8 +686,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, bool paged, const Launch& l
       p.chunk2 % 16 != 0 || p.n_big < 0 || p.n_big > p.n_splits || p.T < 1 || p.R * p.T > 32 ||
       p.row_groups > 1)
     return hipErrorInvalidValue;
-  // the fused step: one new token, its inputs given
-  if (p.len_bias && (p.len_bias != 1 || p.T != 1 || !p.q_in || !p.k_new || !p.v_new))
+  // the fused step: lengths positions + T, up to 16 new tokens (four factor
+  // tables per wave buffer), its inputs given
+  if (p.len_bias && (p.len_bias != p.T || p.T > 16 || !p.q_in || !p.k_new || !p.v_new))
     return hipErrorInvalidValue;
   return p.D == 64 ? launch_d<64>(p, paged, l) : launch_d<128>(p, paged, l);
 }

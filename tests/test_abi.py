@@ -137,6 +137,22 @@ def test_step_int8_validates(lib):
     assert step8(lib, shape(kv_dtype=2, batch=0)) == OK
 
 
+def stepm(lib, sh, T, msl=32):
+    return lib.gqa_decode_step_multi(ctypes.byref(sh) if sh is not None else None, T, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, None, msl, 10000.0, 0, 0.125, None,
+                                     ctypes.c_void_p(0x2000), None, None, 0, None, None)
+
+
+def test_step_multi_validates(lib):
+    assert stepm(lib, None, 2) == EINVAL
+    for T in (0, -1, 17):                                               # 1 to 16 new tokens
+        assert stepm(lib, shape(), T) == EUNSUPPORTED
+    assert stepm(lib, shape(n_heads=8, n_kv_heads=2), 9) == EUNSUPPORTED   # 36 rows per KV head
+    assert stepm(lib, shape(kv_dtype=2), 2) == EUNSUPPORTED             # bf16 caches only
+    assert stepm(lib, shape(), 2, msl=0) == ERANGE
+    assert stepm(lib, shape(batch=0, n_heads=2, n_kv_heads=2), 16) == OK
+
+
 def test_rope_rejects_bad_arguments(lib):
     assert rope(lib, None) == EINVAL
     assert rope(lib, shape(head_dim=80)) == EUNSUPPORTED

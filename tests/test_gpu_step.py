@@ -189,3 +189,105 @@ def test_unsupported_shapes_raise():
         with pytest.raises((kvd.KvdError, ValueError)):
             kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                 t["positions"])
+
+
+# ---- several new tokens per sequence (gqa_decode_step_multi) ----
+
+def _window_spec(B, H, G, D, S, block_size=0):
+    if block_size:
+        nb = S // block_size
+        return W.spec("c4", batch=B, n_heads=H, n_kv_heads=G, head_dim=D,
+                      num_blocks=B * nb + 5, max_blocks_per_seq=nb, block_size=block_size,
+                      q_gain=4.0)
+    return W.spec("c3", batch=B, n_heads=H, n_kv_heads=G, head_dim=D, max_seq_len=S, q_gain=4.0)
+
+
+def check_window_step(p: W.Problem, style="interleaved", options=None, what="", max_len=None):
+    """rope_append_kv_multi + gqa_decode_attn_multi against the fused step
+    bit for bit, then the fused step against the oracle's window step (its
+    caches only when a host bound ``max_len`` below the lengths cuts the
+    attention)."""
+    from tests.test_gpu_multi import oracle_window
+    print(f"[step T] {what}", flush=True)
+    dev = device()
+    msl = p.max_len if max_len is None else max_len
+    ta = upload(p, dev)
+    qa = kvd.rope_append_kv_multi(ta["q"], ta["k_new"], ta["v_new"], ta["k_cache"],
+                                  ta["v_cache"], ta["positions"], ta["block_table"],
+                                  base=p.spec.rope_base, style=style)
+    oa, la = kvd.gqa_decode_attn_multi(qa, ta["k_cache"], ta["v_cache"],
+                                       (ta["positions"] + p.n_query).contiguous(),
+                                       ta["block_table"], max_seq_len=msl, options=options)
+    tb = upload(p, dev)
+    qb = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device=dev)
+    ob, lb = kvd.gqa_decode_step(tb["q"], tb["k_new"], tb["v_new"], tb["k_cache"],
+                                 tb["v_cache"], tb["positions"], tb["block_table"],
+                                 base=p.spec.rope_base, style=style, max_seq_len=msl,
+                                 q_rot=qb, options=options)
+    torch.cuda.synchronize()
+    assert ob.shape == oa.shape and lb.shape == la.shape
+    assert same(qa, qb), f"{what}: q_rot differs from the two calls"
+    assert same(ta["k_cache"], tb["k_cache"]), f"{what}: K cache differs from the two calls"
+    assert same(ta["v_cache"], tb["v_cache"]), f"{what}: V cache differs from the two calls"
+    assert same(oa, ob), f"{what}: out differs from the two calls"
+    assert same(la, lb), f"{what}: lse differs from the two calls"
+    oq, oo, ol, okc, ovc = oracle_window(p, style=style)
+    assert np.array_equal(bits(W.from_torch(tb["k_cache"])), bits(okc)), f"{what}: K cache"
+    assert np.array_equal(bits(W.from_torch(tb["v_cache"])), bits(ovc)), f"{what}: V cache"
+    assert_q_rot(qb.cpu().numpy(), oq, what)
+    if msl < p.max_len:
+        return
+    gates.assert_out(ob.cpu().numpy(), oo, "bf16", what)
+    gates.assert_lse(lb.cpu().numpy(), ol, "bf16", what)
+
+
+@pytest.mark.parametrize("T,H,G", [(2, 8, 2), (5, 8, 2), (8, 8, 2), (16, 2, 2), (5, 24, 4),
+                                   (8, 32, 8), (16, 4, 2)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_several_tokens_head_shapes(T, H, G, D):
+    """T new tokens with T x n_rep query rows from 2 to 32 (one and two
+    column blocks), windows that straddle 16- and 64-token splits."""
+    s = _window_spec(LENS.size, H, G, D, 1024)
+    p = W.make_window(s, T, lengths=np.maximum(LENS, T))
+    check_window_step(p, options=kvd.Options(split_tokens=64),
+                      what=f"T={T} H={H} G={G} D={D}")
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("block_size", [0, 16, 32])
+@pytest.mark.parametrize("split", [0, 16, 48])
+def test_several_tokens_layouts(style, block_size, split):
+    s = _window_spec(LENS.size, 8, 2, 128, 1024, block_size)
+    p = W.make_window(s, 5, lengths=np.maximum(LENS, 5))
+    opts = kvd.Options(split_tokens=split) if split else None
+    check_window_step(p, style=style, options=opts,
+                      what=f"T=5 {style} block {block_size} split {split}")
+
+
+def test_several_tokens_past_the_host_bound():
+    """max_seq_len below the window's end: the tokens past it are still
+    appended (by the last split's workgroup) and not attended."""
+    s = _window_spec(3, 8, 2, 64, 256)
+    p = W.make_window(s, 6, lengths=np.array([6, 153, 200], np.int32))
+    check_window_step(p, options=kvd.Options(split_tokens=32), what="T=6 host bound 150",
+                      max_len=150)
+
+
+def test_several_tokens_c3_full_size():
+    """The batched workload (64 sequences up to 8K tokens, 32 heads on 8 KV
+    heads) verifying 5 draft tokens: 20 query rows per KV head."""
+    s = W.spec("c3")
+    p = W.make_window(s, 5)
+    check_window_step(p, what="c3 T=5 full")
+
+
+def test_several_tokens_unsupported():
+    """More than 16 new tokens, more than 32 query rows per KV head, or an
+    INT8 cache: the two calls, not this one."""
+    for (T, H, G, dt) in ((17, 2, 2, "bf16"), (9, 8, 2, "bf16"), (2, 8, 2, "i8")):
+        s = _window_spec(2, H, G, 64, 64).replace(dtype=dt)
+        p = W.make_window(s, T, lengths=np.array([T, 64], np.int32))
+        t = upload(p, device())
+        with pytest.raises((kvd.KvdError, ValueError)):
+            kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
+                                t["positions"], t["block_table"])
