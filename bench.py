@@ -119,9 +119,10 @@ def workload_name(s) -> str:
     return name
 
 
-def load_traffic(key: str, src_hash: str):
+def load_traffic(key: str, src_hash: str, fused: bool):
     """HBM traffic per launch from profiles/<key>.json when it was measured
-    on the current kernel sources."""
+    on the current kernel sources and on the same kernel form (the split
+    kernel with the RoPE and append fused, or the plain one)."""
     path = os.path.join(PROFILE_DIR, f"traffic_{key}.json")
     if not os.path.exists(path):
         return None
@@ -130,6 +131,8 @@ def load_traffic(key: str, src_hash: str):
     except (OSError, ValueError):
         return None
     if d.get("kernel_source_hash") != src_hash:
+        return None
+    if d.get("kernel_match", "").replace(" ", "").endswith(",true>") != fused:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -743,7 +746,7 @@ def main():
            (f"_bs{s.block_size}" if s.block_size not in (0, 16) else "") +
            (f"_t{T}" if T > 1 else ""))
     src_hash = kernel_source_hash(plan["kernel"])
-    traffic = load_traffic(key, src_hash)
+    traffic = load_traffic(key, src_hash, fused)
     result = {
         "metric": "decode-attention KV HBM GB/s (% of peak) and seq-steps/sec at 1 MI355X",
         "value": round(gbs, 1),

@@ -550,8 +550,8 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  * last split writes the rotated key and the value into the cache slot
  * before it reads any tile; the results are those of the two calls.
  *   q, k_new, v_new, k_cache, v_cache, positions, block_table, rope_base,
- *              rope_style   as in rope_append_kv (bf16 inputs); q and the
- *              caches 16-byte aligned
+ *              rope_style   as in rope_append_kv (bf16 inputs); q, k_new,
+ *              v_new and the caches 16-byte aligned (EINVAL otherwise)
  *   max_seq_len_host  a host bound on positions[b] + 1, in [1, max_seq_len];
  *              attention covers min(positions[b] + 1, max_seq_len_host)
  *              tokens (none for a negative position)
@@ -571,7 +571,8 @@ kvd_status gqa_decode_attn_multi_noalloc(const kvd_shape* shape, int32_t n_query
  * out [B, T, H, D], k_new, v_new [B, T, G, D], lse [B, T, H]; workspace
  * gqa_decode_workspace_size_multi(shape, T, ..).  Each split's workgroup
  * appends the window tokens its split holds (the last one also those past
- * max_seq_len_host).
+ * max_seq_len_host).  EUNSUPPORTED for T outside [1, 16], more than 32
+ * query rows per KV head, or a cache that is not bf16.
  *
  * gqa_decode_step_int8: the same on an INT8 cache with per-head scales
  * k_scale, v_scale [G] (rope_append_kv_int8 then gqa_decode_attn_multi);

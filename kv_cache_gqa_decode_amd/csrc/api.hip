@@ -576,8 +576,8 @@ kvd_status step_impl(const kvd_shape* shape, int32_t T, const void* q, const voi
     return KVD_EUNSUPPORTED;
   if (rope_style != KVD_ROPE_INTERLEAVED && rope_style != KVD_ROPE_HALF) return KVD_EUNSUPPORTED;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !positions || !out) return KVD_EINVAL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      (q_rot && !aligned16(q_rot)))
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || (q_rot && !aligned16(q_rot)))
     return KVD_EINVAL;
   if (static_cast<const void*>(out) == q || (q_rot && static_cast<const void*>(q_rot) == q) ||
       (q_rot && q_rot == out))

@@ -288,13 +288,16 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       return reinterpret_cast<lds_f64*>(stage + (2 * (t & 3) + 1) * G::kTileBytes +
                                         (NB == 2 ? 8 * QS::ROW : 0) + (t >> 2) * D * 8);
     };
-    for (int idx = threadIdx.x; idx < p.T * (D / 2); idx += 256) {
-      const int t = idx / (D / 2), i = idx - t * (D / 2);
+    {
+      // thread (t, i): theta_i once, then tokens t, t + 256 / (D/2), ...
+      const int i = threadIdx.x % (D / 2);
       const double theta = pow(p.rope_base, -2.0 * i / D);
-      double sv, cv;
-      sincos(static_cast<double>(static_cast<int64_t>(P0) + t) * theta, &sv, &cv);
-      fac(t)[i] = cv;
-      fac(t)[D / 2 + i] = sv;
+      for (int t = threadIdx.x / (D / 2); t < p.T; t += 256 / (D / 2)) {
+        double sv, cv;
+        sincos(static_cast<double>(static_cast<int64_t>(P0) + t) * theta, &sv, &cv);
+        fac(t)[i] = cv;
+        fac(t)[D / 2 + i] = sv;
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool inter = p.rope_style != KVD_ROPE_HALF;
@@ -302,10 +305,13 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
       // each of its window tokens: k_new rotated and rounded once to bf16,
       // v_new copied, into the token's cache slot (skipped outside the
       // cache); the stores land before any wave requests a tile, and the
-      // tiles that hold the tokens read them
-      constexpr int kItems = D / 2 + D;   // pairs of k, elements of v
-      for (int idx = threadIdx.x; idx < (app_hi - app_lo) * kItems; idx += 256) {
-        const int pos = app_lo + idx / kItems, it = idx % kItems, t = pos - P0;
+      // tiles that hold the tokens read them.  Item c < D/8 of a token
+      // rotates 4 pairs of k: elements 8c .. 8c+7 (interleaved) or
+      // 4c .. 4c+3 with 4c+D/2 .. (half), pair k using factor 4c + k; item
+      // D/8 + c copies v elements 8c .. 8c+7 (16-byte accesses)
+      constexpr int N8 = D / 8;
+      for (int idx = threadIdx.x; idx < (app_hi - app_lo) * 2 * N8; idx += 256) {
+        const int pos = app_lo + idx / (2 * N8), it = idx % (2 * N8), t = pos - P0;
         if (pos < 0 || pos >= p.max_seq_len) continue;
         int64_t row = -1;
         if (PAGED) {
@@ -316,18 +322,47 @@ __device__ __forceinline__ void run_split(const DecodeParams& p, char* smem, int
         }
         if (row < 0) continue;
         const int64_t src = ((static_cast<int64_t>(b) * p.T + t) * p.G + g) * D;
-        if (it < D / 2) {
+        if (it < N8) {
           const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + src;
           uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(p.k)) + row * D;
-          const int ia = inter ? 2 * it : it, ib = inter ? 2 * it + 1 : it + D / 2;
-          const double a = bf16_to_float(kn[ia]), c = bf16_to_float(kn[ib]);
-          const double cf = fac(t)[it], sf = fac(t)[D / 2 + it];
-          kc[ia] = double_to_bf16_rne(a * cf - c * sf);
-          kc[ib] = double_to_bf16_rne(a * sf + c * cf);
+          const lds_f64* const fc = fac(t);
+          // the 4 pairs as (a, c) -> (a cos - c sin, a sin + c cos)
+          auto rot = [&](float a, float c, int f, uint16_t& ra, uint16_t& rc) {
+            const double cf = fc[f], sf = fc[D / 2 + f];
+            ra = double_to_bf16_rne(static_cast<double>(a) * cf - static_cast<double>(c) * sf);
+            rc = double_to_bf16_rne(static_cast<double>(a) * sf + static_cast<double>(c) * cf);
+          };
+          if (inter) {
+            const uint4 w = *reinterpret_cast<const uint4*>(kn + 8 * it);
+            const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+            uint32_t wo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              uint16_t ra, rc;
+              rot(bf16lo(wi[k]), bf16hi(wi[k]), 4 * it + k, ra, rc);
+              wo[k] = static_cast<uint32_t>(ra) | (static_cast<uint32_t>(rc) << 16);
+            }
+            *reinterpret_cast<uint4*>(kc + 8 * it) = make_uint4(wo[0], wo[1], wo[2], wo[3]);
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(kn + 4 * it);
+            const uint2 y = *reinterpret_cast<const uint2*>(kn + 4 * it + D / 2);
+            const float xa[4] = {bf16lo(x.x), bf16hi(x.x), bf16lo(x.y), bf16hi(x.y)};
+            const float ya[4] = {bf16lo(y.x), bf16hi(y.x), bf16lo(y.y), bf16hi(y.y)};
+            uint16_t ra[4], rc[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rot(xa[k], ya[k], 4 * it + k, ra[k], rc[k]);
+            *reinterpret_cast<uint2*>(kc + 4 * it) =
+                make_uint2(ra[0] | (static_cast<uint32_t>(ra[1]) << 16),
+                           ra[2] | (static_cast<uint32_t>(ra[3]) << 16));
+            *reinterpret_cast<uint2*>(kc + 4 * it + D / 2) =
+                make_uint2(rc[0] | (static_cast<uint32_t>(rc[1]) << 16),
+                           rc[2] | (static_cast<uint32_t>(rc[3]) << 16));
+          }
         } else {
-          const int d = it - D / 2;
-          static_cast<uint16_t*>(const_cast<void*>(p.v))[row * D + d] =
-              static_cast<const uint16_t*>(p.v_new)[src + d];
+          const int c = it - N8;
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(p.v)) + row * D +
+                                    8 * c) =
+              *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_new) + src + 8 * c);
         }
       }
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");

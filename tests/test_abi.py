@@ -93,8 +93,8 @@ def test_attn_rejects_bad_arguments(lib):
 
 
 def step(lib, sh, q=FAKE, k=FAKE, pos=FAKE, table=None, msl=32, out=ctypes.c_void_p(0x2000),
-         qr=None, base=10000.0, style=0, scale=0.125, opts=None):
-    return lib.gqa_decode_step(ctypes.byref(sh) if sh is not None else None, q, FAKE, FAKE, k, k,
+         qr=None, base=10000.0, style=0, scale=0.125, opts=None, kn=FAKE):
+    return lib.gqa_decode_step(ctypes.byref(sh) if sh is not None else None, q, kn, FAKE, k, k,
                                pos, table, msl, base, style, scale, qr, out, None, None, 0, opts,
                                None)
 
@@ -112,6 +112,7 @@ def test_step_rejects_bad_arguments(lib):
     assert step(lib, shape(), out=FAKE) == EINVAL                       # out aliases q
     assert step(lib, shape(), qr=ctypes.c_void_p(0x2000)) == EINVAL     # q_rot aliases out
     assert step(lib, shape(), q=ctypes.c_void_p(0x1008)) == EINVAL      # misaligned
+    assert step(lib, shape(), kn=ctypes.c_void_p(0x1008)) == EINVAL     # k_new misaligned
     assert step(lib, shape(), base=0.0) == EINVAL
     assert step(lib, shape(), scale=float("inf")) == EINVAL
     assert step(lib, shape(), table=FAKE) == EINVAL                     # table for contiguous
