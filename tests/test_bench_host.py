@@ -29,3 +29,22 @@ def test_code_edits_change_the_hash():
 def test_code_text_strips_comments_only():
     src = "int a = 1; // one\n/* two\n three */ int b = 2;\n"
     assert bench.code_text(src) == "int a = 1; int b = 2;"
+
+
+def test_traffic_needs_the_same_kernel_form(tmp_path, monkeypatch):
+    """A traffic record counts only for the kernel source and the kernel
+    form (RoPE and append fused into the split kernel, or not) it was
+    taken on."""
+    import json
+    rec = {"kernel_match": "decode_mfma_kernel<128, false, true>", "kernel_source_hash": "abc",
+           "hbm_bytes_per_launch": 123}
+    (tmp_path / "traffic_w.json").write_text(json.dumps(rec))
+    rec2 = dict(rec, kernel_match="decode_i8_kernel_wide<128, false>")
+    (tmp_path / "traffic_v.json").write_text(json.dumps(rec2))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.load_traffic("w", "abc", True) == 123
+    assert bench.load_traffic("w", "abc", False) is None
+    assert bench.load_traffic("w", "abd", True) is None
+    assert bench.load_traffic("v", "abc", False) == 123
+    assert bench.load_traffic("v", "abc", True) is None
+    assert bench.load_traffic("missing", "abc", False) is None
