@@ -291,3 +291,21 @@ def test_several_tokens_unsupported():
         with pytest.raises((kvd.KvdError, ValueError)):
             kvd.gqa_decode_step(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"],
                                 t["positions"], t["block_table"])
+
+
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
+def test_several_tokens_dispatch_orders(order):
+    """Every decode dispatch order with T = 5: the work lists (orders 3 and
+    4) read the lengths as positions + T."""
+    s = _window_spec(LENS.size, 16, 4, 128, 1024)
+    p = W.make_window(s, 5, lengths=np.maximum(LENS, 5))
+    check_window_step(p, options=kvd.Options(split_tokens=64, dispatch_order=order),
+                      what=f"T=5 order {order}")
+
+
+def test_several_tokens_many_sequences():
+    """65 sequences (the work list built by its own launch) with 3 new
+    tokens each, on a paged cache."""
+    lens = np.maximum(np.resize(LENS, 65), 3)
+    s = _window_spec(65, 8, 2, 64, 1024, block_size=16)
+    check_window_step(W.make_window(s, 3, lengths=lens), what="T=3 B=65 paged")
