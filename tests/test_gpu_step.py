@@ -12,6 +12,12 @@ contiguous and paged (16- and 32-token blocks) caches, one and many splits
 (the direct write and the merge), every decode dispatch order, positions 0
 and at split and tile boundaries, a negative position, and the c3 batch at
 full size.
+
+Several new tokens (gqa_decode_step_multi, bf16): against
+rope_append_kv_multi + gqa_decode_attn_multi bit for bit and the oracle's
+window step, for T = 2-16 with 2-32 query rows per KV head, both RoPE
+styles, paged caches, windows that straddle splits, a host bound inside the
+window, every dispatch order, 65 sequences, and c3 with T = 5 at full size.
 """
 import numpy as np
 import pytest
